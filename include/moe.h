@@ -1,0 +1,193 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) mixture-of-experts expert path.
+ *
+ * One MoE layer on one GPU, as four asynchronous calls on one HIP stream:
+ *
+ *   moe_router_logits -> moe_route -> moe_dispatch -> moe_expert_ffn -> moe_combine
+ *
+ * plus moe_pack_weights (one-time weight re-layout) and moe_check_error.
+ *
+ * Sources of the operations (cited by page title and section):
+ *   - MoE sparse-activation page ("大模型MoE稀疏激活原理与硬件适配实战"):
+ *     §2.2 the three levels (route, load the chosen experts' weights, compute
+ *     locally); §2.3 per-expert load / capacity; §3.1 router row of the table
+ *     (logits in, top-k indices out); §3.2 stage 2 (rank the logits, take the
+ *     top k); §5.3 scenario 3 (router kept in fp32).
+ *   - NCCL EP page ("NCCL EP架构解析"): §1 long-lived group resources vs a
+ *     per-batch handle (here: caller-owned workspace vs the dispatch plan that
+ *     moe_combine reuses); §2.1 LL combine (weighted sum over the k experts);
+ *     §2.2 layout table (compact expert-major rows); §5.1 error codes
+ *     (invalid top-k index, runtime error).
+ *   - DWDP page ("DWDP: 在NVL72上的高性能分布式权重数据并行"): key
+ *     optimisations -- one grouped GEMM over all local experts with the row
+ *     gather and SwiGLU fused, then a second grouped GEMM; W3/W1 packed as one
+ *     first-layer operand; the operator takes the selected experts [T x k] and
+ *     their final scales [T x k].
+ *   - ThunderEP page (PCIe all-to-all scheduling on consumer GPUs): §2.1 pack
+ *     every row bound for one owner into one contiguous buffer; §4.4 MoE
+ *     tensors must be contiguous (misaligned addresses fault).
+ *   - MegaMoE comparison page ("细粒度专家并行方案对比"): core differences §1,
+ *     the single fused kernel with a wave pipeline (moe_forward_fused).
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer argument is a device pointer owned by the caller (the
+ *     library never allocates or frees on these paths), unless stated.
+ *     Every pointer must be 16-byte aligned; tensors are dense row-major.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Calls only enqueue work and return after host-side validation; the
+ *     only call that waits is moe_check_error.
+ *   - Validation failures return an error code and enqueue nothing.
+ *     MOE_ERR_HIP means a launch failed; moe_last_hip_error() gives the code.
+ *   - Element types: MOE_F32 (fp32 everywhere) or MOE_BF16 (bf16 storage,
+ *     fp32 accumulation).  Router logits and gates are always fp32.
+ *   - Results are bitwise reproducible run to run: no floating-point atomics
+ *     are used anywhere; integer atomics only where order cannot matter.
+ *   - Calls on one stream that share a workspace must not overlap in time
+ *     with calls on other streams using the same workspace.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,   /* a size, range or pointer argument is invalid        */
+  MOE_ERR_INVALID_TOPK = 2,  /* k < 1, k > E, k > MOE_MAX_K, or (device-detected)
+                                an expert index outside [0, E) or repeated in a row */
+  MOE_ERR_UNSUPPORTED = 3,   /* a dtype / shape combination this build does not run */
+  MOE_ERR_MISALIGNED = 4,    /* a pointer is not 16-byte aligned                    */
+  MOE_ERR_WORKSPACE = 5,     /* workspace NULL or smaller than moe_workspace_bytes  */
+  MOE_ERR_HIP = 6            /* a HIP launch or runtime call failed                 */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+typedef enum {
+  /* softmax over all experts, keep the top k, renormalise over the k; equal to
+     a softmax over the k chosen logits (sparse-activation page §3.2 stage 2) */
+  MOE_GATE_SOFTMAX_TOPK_RENORM = 0,
+  /* sigmoid of each chosen logit, normalised to sum to 1 over the k chosen   */
+  MOE_GATE_SIGMOID_TOPK_NORM = 1
+} moe_gate;
+
+#define MOE_MAX_K 8     /* largest top-k supported                          */
+#define MOE_MAX_E 1024  /* largest number of (global) experts supported     */
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* moe_status_string(int status);
+
+/* hipError_t code of the last failed HIP call made by this library on the
+ * calling host thread (0 if none). */
+int moe_last_hip_error(void);
+
+/* Bytes of workspace needed by moe_dispatch and moe_expert_ffn (and the
+ * device error word read by moe_check_error) for T tokens, E global experts,
+ * top-k k and E_loc local experts.  Returns 0 if the sizes are invalid.
+ * The workspace must be zero-filled once before its first use; the library
+ * keeps it consistent afterwards. */
+size_t moe_workspace_bytes(int T, int E, int k, int E_loc);
+
+/* Per-expert capacity C = ceil(cf * T * k / E) for a capacity factor given as
+ * the exact fraction cf = cf_num / cf_den (MoE sparse-activation page §2.3:
+ * per-expert load (Batch x SeqLen x K) / E, scaled by the capacity factor).
+ * Returns -1 (no limit) if cf_num < 0, and -2 if an argument is invalid. */
+int64_t moe_capacity(int T, int k, int E, int64_t cf_num, int64_t cf_den);
+
+/* Number of rows that x_perm / h / y_perm must provide: min(T*k, E_loc*C)
+ * when capacity C >= 0, else T*k. */
+int64_t moe_max_rows(int T, int k, int E_loc, int capacity);
+
+/* One-time re-layout of expert weights from the logical x.W layout
+ *   w1, w3: [E_loc][d][f]      w2: [E_loc][f][d]
+ * into the K-contiguous packed layout used by moe_expert_ffn:
+ *   w13_packed: [E_loc][2f][d]  (rows 0..f-1: W1 transposed; f..2f-1: W3 transposed)
+ *   w2_packed:  [E_loc][d][f]   (W2 transposed)
+ * (DWDP page, key optimisations: W3 and W1 form one fused first-layer
+ * operand; sparse-activation page §4.2 layer 2: each expert's weights
+ * contiguous, re-ordered once at load.)  Outputs must not alias inputs. */
+moe_status moe_pack_weights(const void* w1, const void* w3, const void* w2, int E_loc, int d,
+                            int f, moe_dtype dtype, void* w13_packed, void* w2_packed,
+                            void* stream);
+
+/* Router logits (sparse-activation page §3.1 router row, §5.3 fp32 router):
+ *   logits[t][e] = sum_i x[t][i] * w_gate[i][e]
+ * x: [T][d] bf16; w_gate: [d][E] fp32; logits: [T][E] fp32 (output).
+ * fp32 products and accumulation.  Requires d % 8 == 0, 1 <= E <= 64. */
+moe_status moe_router_logits(const void* x, const float* w_gate, int T, int d, int E,
+                             float* logits, void* stream);
+
+/* Top-k routing and gates (sparse-activation page §3.2 stage 2).
+ * logits: [T][E] fp32, finite.  Outputs topk_idx [T][k] int32 (best first,
+ * equal logits ordered by lower expert index, -0.0 == +0.0) and topk_w [T][k]
+ * fp32 gate weights per `gate`.  Selection compares the fp32 logits exactly. */
+moe_status moe_route(const float* logits, int T, int E, int k, int gate, int32_t* topk_idx,
+                     float* topk_w, void* stream);
+
+/* Dispatch plan and permutation (ThunderEP page §2.1/§2.2: rows packed per
+ * owner, per-expert index lists; NCCL EP page §2.2: compact expert-major
+ * layout; sparse-activation page §2.3: capacity).
+ * Pair p = t*k + j is token t's j-th choice e = topk_idx[t][j].  Its position
+ * pos(p) is the number of tokens t' < t that chose e.  It is kept iff
+ * capacity < 0 or pos(p) < capacity, and local iff e_begin <= e < e_end.
+ * Outputs (int32, device):
+ *   counts[E]            pairs per expert before any drop
+ *   offsets[E_loc + 1]   exclusive scan of min(counts, capacity) over local experts
+ *   sorted_pair[rows]    sorted_pair[offsets[e - e_begin] + pos(p)] = p for kept local p
+ *                        (entries past n_kept are left untouched)
+ *   pair_pos[T*k]        that row, -1 if dropped, -2 if kept but not local
+ *   n_kept[1]            offsets[E_loc]
+ *   x_perm[rows][d]      x_perm[row] = x[sorted_pair[row] / k] (skipped if x == NULL)
+ * x / x_perm hold `dtype` elements; rows = moe_max_rows(T, k, E_loc, capacity).
+ * An index outside [0, E) or repeated within a row sets the device error word
+ * (see moe_check_error); such pairs are ignored. */
+moe_status moe_dispatch(const int32_t* topk_idx, int T, int E, int k, int capacity,
+                        int e_begin, int e_end, const void* x, int d, moe_dtype dtype,
+                        int32_t* counts, int32_t* offsets, int32_t* sorted_pair,
+                        int32_t* pair_pos, int32_t* n_kept, void* x_perm, void* ws,
+                        size_t ws_bytes, void* stream);
+
+/* Per-expert SwiGLU FFN as two grouped GEMMs over the expert-major rows
+ * (DWDP page key optimisations: gather + grouped GEMM + SwiGLU, then grouped
+ * GEMM; MegaMoE comparison page §1: two linear layers and SwiGLU):
+ *   h[r]      = silu(x_perm[r] . W1_e) * (x_perm[r] . W3_e)   silu(a) = a*sigmoid(a)
+ *   y_perm[r] = h[r] . W2_e          for rows r in [offsets[i], offsets[i+1]), e = local i
+ * x_perm: [rows][d]; h: [rows][f] (output, scratch for the second GEMM);
+ * y_perm: [rows][d] (output, not yet weighted); weights packed by
+ * moe_pack_weights.  max_rows bounds offsets[E_loc] (moe_max_rows).
+ * Requires d % 64 == 0 and f % 64 == 0 (bf16) or d % 4 == 0, f % 4 == 0 (f32).
+ * Row counts are read on the device; nothing is synchronised with the host.
+ * moe_ffn_up and moe_ffn_down are the two halves of moe_expert_ffn. */
+moe_status moe_expert_ffn(const void* x_perm, const int32_t* offsets, int E_loc,
+                          int64_t max_rows, int d, int f, moe_dtype dtype,
+                          const void* w13_packed, const void* w2_packed, void* h, void* y_perm,
+                          void* ws, size_t ws_bytes, void* stream);
+moe_status moe_ffn_up(const void* x_perm, const int32_t* offsets, int E_loc, int64_t max_rows,
+                      int d, int f, moe_dtype dtype, const void* w13_packed, void* h,
+                      void* ws, size_t ws_bytes, void* stream);
+moe_status moe_ffn_down(const void* h, const int32_t* offsets, int E_loc, int64_t max_rows,
+                        int d, int f, moe_dtype dtype, const void* w2_packed, void* y_perm,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/* Weighted combine (NCCL EP page §2.1, LL combine):
+ *   y[t] = sum_{j=0..k-1, pair_pos[t*k+j] >= 0} topk_w[t][j] * y_perm[pair_pos[t*k+j]]
+ * accumulated in fp32 in ascending j, rounded once to `dtype`; tokens with no
+ * local kept pair get zero rows.  y: [T][d] (output). */
+moe_status moe_combine(const void* y_perm, const int32_t* pair_pos, const float* topk_w, int T,
+                       int k, int d, moe_dtype dtype, void* y, void* stream);
+
+/* Waits for `stream`, then returns MOE_ERR_INVALID_TOPK if a kernel since the
+ * last check saw an invalid expert index (and clears the flag), MOE_ERR_HIP
+ * if the stream reported an error, else MOE_OK. */
+moe_status moe_check_error(void* ws, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,11 @@
+"""MI355X (gfx950) MoE expert path: route -> dispatch -> grouped SwiGLU FFN -> combine.
+
+The computation lives in hand-written HIP kernels behind the C ABI of
+include/moe.h (libmoe_mi355x.so, built in-tree by `build.py`).  This package
+only marshals torch tensors and streams into that library.
+"""
+from ._lib import LIB_PATH, MoEError, lib  # noqa: F401
+from .layer import MoELayer  # noqa: F401
+from .ops import (alloc_plan, alloc_workspace, moe_check_error, moe_combine, moe_dispatch,  # noqa: F401
+                  moe_capacity, moe_expert_ffn, moe_ffn_down, moe_ffn_up, moe_max_rows, moe_pack_weights,
+                  moe_route, moe_router_logits, moe_workspace_bytes)

@@ -1,0 +1,260 @@
+// C ABI of the MoE expert path: argument validation and launch.
+//
+// Validation is pure host code that makes no HIP call, so every invalid
+// argument is rejected (and can be tested) without touching a GPU.  Only
+// after validation do the entry points call the launchers.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+
+#include "launch.h"
+#include "moe.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline moe_status hip_status(int e) {
+  if (e != 0) {
+    g_last_hip_error = e;
+    return MOE_ERR_HIP;
+  }
+  return MOE_OK;
+}
+
+inline bool elem_ok(int dtype) { return dtype == MOE_F32 || dtype == MOE_BF16; }
+inline int elem_bytes(int dtype) { return dtype == MOE_F32 ? 4 : 2; }
+
+moe_status check_topk(int E, int k) {
+  if (E < 1 || E > MOE_MAX_E) return MOE_ERR_INVALID_ARG;
+  if (k < 1 || k > E || k > MOE_MAX_K) return MOE_ERR_INVALID_TOPK;
+  return MOE_OK;
+}
+
+// FFN shape rules shared by moe_expert_ffn and its halves
+moe_status check_ffn(const void* a, const int32_t* offsets, int E_loc, int64_t max_rows, int d,
+                     int f, int dtype, const void* w, const void* out) {
+  if (!elem_ok(dtype)) return MOE_ERR_UNSUPPORTED;
+  if (E_loc < 1 || E_loc > MOE_MAX_E || max_rows < 0 || d < 1 || f < 1)
+    return MOE_ERR_INVALID_ARG;
+  if (max_rows > INT32_MAX) return MOE_ERR_INVALID_ARG;
+  if (!offsets || !w) return MOE_ERR_INVALID_ARG;
+  if (max_rows > 0 && (!a || !out)) return MOE_ERR_INVALID_ARG;
+  if (dtype == MOE_BF16 && (d % 64 != 0 || f % 64 != 0)) return MOE_ERR_UNSUPPORTED;
+  if (dtype == MOE_F32 && (d % 4 != 0 || f % 4 != 0)) return MOE_ERR_UNSUPPORTED;
+  if (!aligned16(a) || !aligned16(offsets) || !aligned16(w) || !aligned16(out))
+    return MOE_ERR_MISALIGNED;
+  return MOE_OK;
+}
+
+}  // namespace
+
+namespace moe {
+
+int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+int check_error(void* ws, void* stream, int* device_flags) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return static_cast<int>(e);
+  int flags = 0;
+  e = hipMemcpy(&flags, ws, sizeof(int), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return static_cast<int>(e);
+  if (flags != 0) {
+    e = hipMemset(ws, 0, sizeof(int));
+    if (e != hipSuccess) return static_cast<int>(e);
+  }
+  *device_flags = flags;
+  return 0;
+}
+
+}  // namespace moe
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: invalid size, range or pointer";
+    case MOE_ERR_INVALID_TOPK: return "MOE_ERR_INVALID_TOPK: top-k out of range or invalid expert index";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: dtype or shape not supported";
+    case MOE_ERR_MISALIGNED: return "MOE_ERR_MISALIGNED: pointer not 16-byte aligned";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing or too small";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: HIP runtime error";
+    default: return "unknown moe_status";
+  }
+}
+
+int moe_last_hip_error(void) { return g_last_hip_error; }
+
+size_t moe_workspace_bytes(int T, int E, int k, int E_loc) {
+  if (T < 0 || E < 1 || E > MOE_MAX_E || k < 1 || k > MOE_MAX_K || k > E || E_loc < 1 || E_loc > E)
+    return 0;
+  return moe::dispatch_ws_bytes(T, E);
+}
+
+int64_t moe_capacity(int T, int k, int E, int64_t cf_num, int64_t cf_den) {
+  if (cf_num < 0) return -1;
+  if (T < 0 || k < 1 || E < 1 || cf_den < 1) return -2;
+  const int64_t num = cf_num * static_cast<int64_t>(T) * k;  // callers keep cf_num small
+  const int64_t den = cf_den * static_cast<int64_t>(E);
+  return (num + den - 1) / den;
+}
+
+int64_t moe_max_rows(int T, int k, int E_loc, int capacity) {
+  const int64_t all = static_cast<int64_t>(T) * k;
+  if (capacity < 0) return all;
+  const int64_t cap = static_cast<int64_t>(E_loc) * capacity;
+  return cap < all ? cap : all;
+}
+
+moe_status moe_pack_weights(const void* w1, const void* w3, const void* w2, int E_loc, int d,
+                            int f, moe_dtype dtype, void* w13_packed, void* w2_packed,
+                            void* stream) {
+  if (!elem_ok(dtype)) return MOE_ERR_UNSUPPORTED;
+  if (E_loc < 1 || E_loc > MOE_MAX_E || d < 1 || f < 1) return MOE_ERR_INVALID_ARG;
+  if (!w1 || !w3 || !w2 || !w13_packed || !w2_packed) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(w1) || !aligned16(w3) || !aligned16(w2) || !aligned16(w13_packed) ||
+      !aligned16(w2_packed))
+    return MOE_ERR_MISALIGNED;
+  return hip_status(moe::launch_pack(w1, w3, w2, E_loc, d, f, elem_bytes(dtype), w13_packed,
+                                     w2_packed, stream));
+}
+
+moe_status moe_router_logits(const void* x, const float* w_gate, int T, int d, int E,
+                             float* logits, void* stream) {
+  if (T < 0 || d < 1 || E < 1 || E > 64) return MOE_ERR_INVALID_ARG;
+  if (d % 8 != 0) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!x || !w_gate || !logits) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w_gate) || !aligned16(logits)) return MOE_ERR_MISALIGNED;
+  return hip_status(moe::launch_router_logits(x, w_gate, T, d, E, logits, stream));
+}
+
+moe_status moe_route(const float* logits, int T, int E, int k, int gate, int32_t* topk_idx,
+                     float* topk_w, void* stream) {
+  if (T < 0) return MOE_ERR_INVALID_ARG;
+  moe_status st = check_topk(E, k);
+  if (st != MOE_OK) return st;
+  if (gate != MOE_GATE_SOFTMAX_TOPK_RENORM && gate != MOE_GATE_SIGMOID_TOPK_NORM)
+    return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!logits || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(logits) || !aligned16(topk_idx) || !aligned16(topk_w)) return MOE_ERR_MISALIGNED;
+  return hip_status(moe::launch_route(logits, T, E, k, gate, topk_idx, topk_w, stream));
+}
+
+moe_status moe_dispatch(const int32_t* topk_idx, int T, int E, int k, int capacity,
+                        int e_begin, int e_end, const void* x, int d, moe_dtype dtype,
+                        int32_t* counts, int32_t* offsets, int32_t* sorted_pair,
+                        int32_t* pair_pos, int32_t* n_kept, void* x_perm, void* ws,
+                        size_t ws_bytes, void* stream) {
+  if (T < 0) return MOE_ERR_INVALID_ARG;
+  moe_status st = check_topk(E, k);
+  if (st != MOE_OK) return st;
+  if (!(0 <= e_begin && e_begin < e_end && e_end <= E)) return MOE_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(T) * k > INT32_MAX) return MOE_ERR_INVALID_ARG;
+  if (!elem_ok(dtype)) return MOE_ERR_UNSUPPORTED;
+  if (x) {
+    if (d < 1) return MOE_ERR_INVALID_ARG;
+    if ((static_cast<int64_t>(d) * elem_bytes(dtype)) % 16 != 0) return MOE_ERR_UNSUPPORTED;
+    if (!x_perm) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(x_perm)) return MOE_ERR_MISALIGNED;
+  }
+  if (!counts || !offsets || !pair_pos || !n_kept || !ws) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && !sorted_pair) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(topk_idx) || !aligned16(counts) || !aligned16(offsets) ||
+      !aligned16(sorted_pair) || !aligned16(pair_pos) || !aligned16(n_kept) || !aligned16(ws))
+    return MOE_ERR_MISALIGNED;
+  if (ws_bytes < moe::dispatch_ws_bytes(T, E)) return MOE_ERR_WORKSPACE;
+  if (T > 0 && !topk_idx) return MOE_ERR_INVALID_ARG;
+  const moe::DispatchWs w = moe::dispatch_ws(ws, T, E);
+  return hip_status(moe::launch_dispatch(topk_idx, T, E, k, capacity, e_begin, e_end, x, d,
+                                         elem_bytes(dtype), counts, offsets, sorted_pair,
+                                         pair_pos, n_kept, x_perm, w, stream));
+}
+
+moe_status moe_ffn_up(const void* x_perm, const int32_t* offsets, int E_loc, int64_t max_rows,
+                      int d, int f, moe_dtype dtype, const void* w13_packed, void* h,
+                      void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  moe_status st = check_ffn(x_perm, offsets, E_loc, max_rows, d, f, dtype, w13_packed, h);
+  if (st != MOE_OK) return st;
+  if (dtype == MOE_BF16)
+    return hip_status(moe::launch_ffn_up_bf16(x_perm, offsets, E_loc, max_rows, d, f, w13_packed,
+                                              h, stream));
+  return hip_status(moe::launch_ffn_up_f32(static_cast<const float*>(x_perm), offsets, E_loc,
+                                           max_rows, d, f, static_cast<const float*>(w13_packed),
+                                           static_cast<float*>(h), stream));
+}
+
+moe_status moe_ffn_down(const void* h, const int32_t* offsets, int E_loc, int64_t max_rows,
+                        int d, int f, moe_dtype dtype, const void* w2_packed, void* y_perm,
+                        void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  moe_status st = check_ffn(h, offsets, E_loc, max_rows, d, f, dtype, w2_packed, y_perm);
+  if (st != MOE_OK) return st;
+  if (dtype == MOE_BF16)
+    return hip_status(moe::launch_ffn_down_bf16(h, offsets, E_loc, max_rows, d, f, w2_packed,
+                                                y_perm, stream));
+  return hip_status(moe::launch_ffn_down_f32(static_cast<const float*>(h), offsets, E_loc,
+                                             max_rows, d, f, static_cast<const float*>(w2_packed),
+                                             static_cast<float*>(y_perm), stream));
+}
+
+moe_status moe_expert_ffn(const void* x_perm, const int32_t* offsets, int E_loc,
+                          int64_t max_rows, int d, int f, moe_dtype dtype,
+                          const void* w13_packed, const void* w2_packed, void* h, void* y_perm,
+                          void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = check_ffn(x_perm, offsets, E_loc, max_rows, d, f, dtype, w13_packed, h);
+  if (st != MOE_OK) return st;
+  st = check_ffn(h, offsets, E_loc, max_rows, d, f, dtype, w2_packed, y_perm);
+  if (st != MOE_OK) return st;
+  st = moe_ffn_up(x_perm, offsets, E_loc, max_rows, d, f, dtype, w13_packed, h, ws, ws_bytes,
+                  stream);
+  if (st != MOE_OK) return st;
+  return moe_ffn_down(h, offsets, E_loc, max_rows, d, f, dtype, w2_packed, y_perm, ws, ws_bytes,
+                      stream);
+}
+
+moe_status moe_combine(const void* y_perm, const int32_t* pair_pos, const float* topk_w, int T,
+                       int k, int d, moe_dtype dtype, void* y, void* stream) {
+  if (T < 0 || d < 1 || k < 1 || k > MOE_MAX_K) return MOE_ERR_INVALID_ARG;
+  if (!elem_ok(dtype)) return MOE_ERR_UNSUPPORTED;
+  if ((static_cast<int64_t>(d) * elem_bytes(dtype)) % 16 != 0) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!pair_pos || !topk_w || !y) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(y_perm) || !aligned16(pair_pos) || !aligned16(topk_w) || !aligned16(y))
+    return MOE_ERR_MISALIGNED;
+  return hip_status(moe::launch_combine(y_perm, pair_pos, topk_w, T, k, d, dtype == MOE_BF16, y,
+                                        stream));
+}
+
+moe_status moe_check_error(void* ws, void* stream) {
+  if (!ws) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(ws)) return MOE_ERR_MISALIGNED;
+  int flags = 0;
+  int e = moe::check_error(ws, stream, &flags);
+  if (e != 0) return hip_status(e);
+  if (flags & (1 << MOE_ERR_INVALID_TOPK)) return MOE_ERR_INVALID_TOPK;
+  if (flags != 0) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+}  // extern "C"

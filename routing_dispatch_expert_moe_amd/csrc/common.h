@@ -1,0 +1,75 @@
+// Shared device helpers for the gfx950 kernels: bf16 conversion, vector
+// types, wave-level reductions.  CDNA4: 64-lane wavefronts.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// bf16 bit pattern -> fp32 (exact)
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// fp32 -> bf16 bit pattern, round to nearest, ties to even (NaN kept quiet)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// unpack 8 bf16 held in a uint4 into fp32
+__device__ __forceinline__ void unpack8(const uint4& v, float* o) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o[2 * i] = __uint_as_float(w[i] << 16);
+    o[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+__device__ __forceinline__ uint4 pack8(const float* f) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    w[i] = static_cast<uint32_t>(f32_to_bf16(f[2 * i])) |
+           (static_cast<uint32_t>(f32_to_bf16(f[2 * i + 1])) << 16);
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), off, kWave);
+    uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), off, kWave);
+    uint64_t o = (static_cast<uint64_t>(hi) << 32) | lo;
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+// butterfly sum: every lane ends with the same value, same order on every lane
+__device__ __forceinline__ float wave_sum_f32(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+// Set the device error word (bitwise OR; order does not matter).
+__device__ __forceinline__ void raise_error(int* err, int code) {
+  if (err) atomicOr(err, 1 << code);
+}
+
+}  // namespace moe

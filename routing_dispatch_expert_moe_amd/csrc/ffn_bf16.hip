@@ -1,0 +1,246 @@
+// Grouped expert GEMMs in bf16 on gfx950 MFMA (v_mfma_f32_32x32x16_bf16),
+// fp32 accumulation.
+//
+// DWDP page, key optimisations: the first grouped GEMM runs every local
+// expert's rows against that expert's fused [W1 | W3] operand with SwiGLU in
+// the epilogue; the second grouped GEMM applies W2.  MegaMoE comparison page,
+// core differences §1: two linear layers with SwiGLU between them.
+//
+//   up   : h[r, n] = silu(sum_k A[r,k] W1t[n,k]) * (sum_k A[r,k] W3t[n,k])
+//   down : y[r, n] = sum_k h[r,k] W2t[n,k]
+//
+// Weights are packed K-contiguous ("NT" GEMM), so both MFMA operands are
+// 16-byte runs along K in LDS.  Rows of each expert are the segment
+// [offsets[e], offsets[e+1]) of the expert-major activations; segment sizes
+// live only on the device.
+//
+// Scheduling (persistent per-expert tile scheduler): a fixed grid of
+// workgroups walks a linear tile space.  Each workgroup first scans the
+// expert segment sizes into an LDS prefix of M-tiles, then maps a tile id to
+// (expert, n-tile, m-tile) with m fastest, so consecutive tiles reuse one
+// weight tile.  Workgroup ids are remapped so that each XCD (ids are dealt
+// round-robin over the 8 XCDs) owns contiguous tile ranges and the tiles that
+// share a weight tile meet in the same L2.
+#include "common.h"
+#include "launch.h"
+#include "tile_sched.h"
+
+namespace moe {
+
+struct TileCfg {
+  int BM, BN, BK, WM, WN;
+};
+
+__device__ __forceinline__ float silu_f(float a) { return a / (1.f + __expf(-a)); }
+
+template <int BM, int BN, int BK, int WM, int WN, bool SWIGLU>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(
+    const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets, int E_loc,
+    const uint16_t* __restrict__ W, uint16_t* __restrict__ C, int N, int K) {
+  constexpr int NTHR = WM * WN * 64;
+  constexpr int BNW = SWIGLU ? 2 * BN : BN;  // weight rows per tile
+  constexpr int KC = BK / 8;                 // 16-byte chunks per tile row
+  constexpr int TM = BM / WM, TN = BN / WN;  // wave tile
+  constexpr int FM = TM / 32, FN = TN / 32;  // 32x32 MFMA tiles per wave
+  constexpr int CA = BM * KC / NTHR;         // A chunks per thread per stage
+  constexpr int CB = BNW * KC / NTHR;        // B chunks per thread per stage
+  static_assert(BM * KC % NTHR == 0 && BNW * KC % NTHR == 0, "tile / thread mismatch");
+  static_assert(TM % 32 == 0 && TN % 32 == 0 && BK % 16 == 0, "MFMA tiling");
+
+  extern __shared__ uint4 lds[];
+  uint4* As = lds;                      // [2][BM * KC]
+  uint4* Bs = lds + 2 * BM * KC;        // [2][BNW * KC]
+  __shared__ int prefix[MOE_MAX_E + 1];
+
+  mtile_prefix<BM>(offsets, E_loc, prefix);
+  const int NT = (N + BN - 1) / BN;
+  const int total = prefix[E_loc] * NT;
+  const int G = gridDim.x;
+  // XCD-aware remap of the workgroup id (ids are dealt round-robin over 8 XCDs)
+  int vb = blockIdx.x;
+  if ((G & 7) == 0) vb = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int wm = wave / WN, wn = wave % WN;
+  const int KT = K / BK;
+  const size_t wstride = static_cast<size_t>(SWIGLU ? 2 * N : N) * K;
+
+  for (int tile = vb; tile < total; tile += G) {
+    const int mt = tile / NT;  // global M-tile index ... expert from prefix
+    const int e = find_expert(prefix, E_loc, mt);
+    const int mt_e = prefix[e + 1] - prefix[e];
+    const int local = tile - prefix[e] * NT;
+    const int nt = local / mt_e;
+    const int mti = local % mt_e;
+    const int seg0 = offsets[e], seg1 = offsets[e + 1];
+    const int m0 = seg0 + mti * BM;
+    const int n0 = nt * BN;
+    const uint16_t* We = W + e * wstride;
+
+    // per-thread load descriptors
+    const uint16_t* a_src[CA];
+    bool a_ok[CA];
+    int a_dst[CA];
+#pragma unroll
+    for (int i = 0; i < CA; ++i) {
+      const int c = tid + i * NTHR;
+      const int r = c / KC, kc = c % KC;
+      const int row = m0 + r;
+      a_ok[i] = row < seg1;
+      a_src[i] = A + static_cast<size_t>(a_ok[i] ? row : seg0) * K + kc * 8;
+      a_dst[i] = r * KC + (kc ^ ((r >> 1) & (KC - 1)));
+    }
+    const uint16_t* b_src[CB];
+    bool b_ok[CB];
+    int b_dst[CB];
+#pragma unroll
+    for (int i = 0; i < CB; ++i) {
+      const int c = tid + i * NTHR;
+      const int r = c / KC, kc = c % KC;
+      const int half = SWIGLU ? (r / BN) : 0;
+      const int n = n0 + (r % BN);
+      b_ok[i] = n < N;
+      b_src[i] = We + (static_cast<size_t>(half) * N + (b_ok[i] ? n : 0)) * K + kc * 8;
+      b_dst[i] = r * KC + (kc ^ ((r >> 1) & (KC - 1)));
+    }
+
+    f32x16_t acc[FM][FN];
+    f32x16_t accg[SWIGLU ? FM : 1][SWIGLU ? FN : 1];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        acc[i][j] = f32x16_t{};
+        if constexpr (SWIGLU) accg[i][j] = f32x16_t{};
+      }
+
+    uint4 ra[CA], rb[CB];
+    auto gload = [&](int kt) {
+      const int koff = kt * BK;
+#pragma unroll
+      for (int i = 0; i < CA; ++i)
+        ra[i] = a_ok[i] ? *reinterpret_cast<const uint4*>(a_src[i] + koff) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < CB; ++i)
+        rb[i] = b_ok[i] ? *reinterpret_cast<const uint4*>(b_src[i] + koff) : make_uint4(0, 0, 0, 0);
+    };
+    auto sstore = [&](int buf) {
+#pragma unroll
+      for (int i = 0; i < CA; ++i) As[buf * BM * KC + a_dst[i]] = ra[i];
+#pragma unroll
+      for (int i = 0; i < CB; ++i) Bs[buf * BNW * KC + b_dst[i]] = rb[i];
+    };
+
+    gload(0);
+    sstore(0);
+    __syncthreads();
+    for (int kt = 0; kt < KT; ++kt) {
+      const int buf = kt & 1;
+      if (kt + 1 < KT) gload(kt + 1);
+      const uint4* Ab = As + buf * BM * KC;
+      const uint4* Bb = Bs + buf * BNW * KC;
+#pragma unroll
+      for (int ks = 0; ks < BK / 16; ++ks) {
+        const int ch = ks * 2 + (lane >> 5);
+        bf16x8_t af[FM], bf[FN], gf[SWIGLU ? FN : 1];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          const int r = wm * TM + i * 32 + (lane & 31);
+          af[i] = __builtin_bit_cast(bf16x8_t, Ab[r * KC + (ch ^ ((r >> 1) & (KC - 1)))]);
+        }
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int r = wn * TN + j * 32 + (lane & 31);
+          bf[j] = __builtin_bit_cast(bf16x8_t, Bb[r * KC + (ch ^ ((r >> 1) & (KC - 1)))]);
+          if constexpr (SWIGLU) {
+            const int r2 = BN + r;
+            gf[j] = __builtin_bit_cast(bf16x8_t, Bb[r2 * KC + (ch ^ ((r2 >> 1) & (KC - 1)))]);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+            if constexpr (SWIGLU)
+              accg[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], gf[j], accg[i][j], 0, 0, 0);
+          }
+      }
+      if (kt + 1 < KT) sstore(buf ^ 1);
+      __syncthreads();
+    }
+
+    // epilogue: D[m][n] of a 32x32 tile sits in lane (n + 32 * ((m / 4) % 2)),
+    // register 4 * (m / 8) + m % 4
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int col = n0 + wn * TN + j * 32 + (lane & 31);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          const int row = m0 + wm * TM + i * 32 + m;
+          float v = acc[i][j][r];
+          if constexpr (SWIGLU) v = silu_f(v) * accg[i][j][r];
+          if (row < seg1 && col < N) C[static_cast<size_t>(row) * N + col] = f32_to_bf16(v);
+        }
+      }
+  }
+}
+
+template <int BM, int BN, int BK, int WM, int WN, bool SWIGLU>
+static int launch_gemm(const void* A, const int32_t* offsets, int E_loc, int64_t max_rows,
+                       const void* W, void* C, int N, int K, hipStream_t s) {
+  constexpr int BNW = SWIGLU ? 2 * BN : BN;
+  const size_t lds = static_cast<size_t>(2) * (BM + BNW) * BK * sizeof(uint16_t);
+  auto kern = gemm_bf16_kernel<BM, BN, BK, WM, WN, SWIGLU>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       static_cast<int>(lds));
+    if (e != hipSuccess) return static_cast<int>(e);
+    attr_set = true;
+  }
+  const int64_t NT = (N + BN - 1) / BN;
+  const int64_t tiles_ub = (max_rows / BM + E_loc) * NT;
+  int occ = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(kern),
+                                                             WM * WN * 64, lds);
+  if (e != hipSuccess) return static_cast<int>(e);
+  if (occ < 1) occ = 1;
+  int64_t grid = static_cast<int64_t>(device_cu_count()) * occ;
+  if (grid > tiles_ub) grid = tiles_ub;
+  if (grid >= 8) grid &= ~static_cast<int64_t>(7);
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(WM * WN * 64), lds, s,
+                     static_cast<const uint16_t*>(A), offsets, E_loc,
+                     static_cast<const uint16_t*>(W), static_cast<uint16_t*>(C), N, K);
+  return static_cast<int>(hipGetLastError());
+}
+
+// Rows per expert on average decide the tile shape: weight-streaming (few
+// rows) or MFMA-bound (many rows).
+int launch_ffn_up_bf16(const void* x_perm, const int32_t* offsets, int E_loc, int64_t max_rows,
+                       int d, int f, const void* w13, void* h, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (max_rows == 0) return 0;
+  const int64_t avg = max_rows / E_loc;
+  if (avg <= 48)
+    return launch_gemm<32, 128, 64, 1, 4, true>(x_perm, offsets, E_loc, max_rows, w13, h, f, d, s);
+  return launch_gemm<128, 128, 64, 2, 2, true>(x_perm, offsets, E_loc, max_rows, w13, h, f, d, s);
+}
+
+int launch_ffn_down_bf16(const void* h, const int32_t* offsets, int E_loc, int64_t max_rows,
+                         int d, int f, const void* w2, void* y, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (max_rows == 0) return 0;
+  const int64_t avg = max_rows / E_loc;
+  if (avg <= 48)
+    return launch_gemm<32, 128, 64, 1, 4, false>(h, offsets, E_loc, max_rows, w2, y, d, f, s);
+  return launch_gemm<128, 128, 64, 2, 2, false>(h, offsets, E_loc, max_rows, w2, y, d, f, s);
+}
+
+}  // namespace moe

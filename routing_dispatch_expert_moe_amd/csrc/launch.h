@@ -1,0 +1,47 @@
+// Internal launchers (C++ linkage, not exported).  Each returns a hipError_t
+// as int (0 = success).  Arguments are already validated by the C ABI layer.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// device error word lives at the start of the workspace
+constexpr size_t kWsHeader = 256;
+constexpr int kDispatchTokensPerBlock = 256;
+
+struct DispatchWs {
+  int* err;           // [1]
+  int* block_counts;  // [nb * E]
+  int* block_base;    // [nb * E]
+};
+
+size_t dispatch_ws_bytes(int T, int E);
+DispatchWs dispatch_ws(void* ws, int T, int E);
+
+int launch_router_logits(const void* x, const float* wg, int T, int d, int E, float* logits,
+                         void* stream);
+int launch_route(const float* logits, int T, int E, int k, int gate, int32_t* idx, float* w,
+                 void* stream);
+int launch_dispatch(const int32_t* idx, int T, int E, int k, int capacity, int e_begin,
+                    int e_end, const void* x, int d, int elem_bytes, int32_t* counts,
+                    int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos, int32_t* n_kept,
+                    void* x_perm, const DispatchWs& ws, void* stream);
+int launch_ffn_up_bf16(const void* x_perm, const int32_t* offsets, int E_loc, int64_t max_rows,
+                       int d, int f, const void* w13, void* h, void* stream);
+int launch_ffn_down_bf16(const void* h, const int32_t* offsets, int E_loc, int64_t max_rows,
+                         int d, int f, const void* w2, void* y, void* stream);
+int launch_ffn_up_f32(const float* x_perm, const int32_t* offsets, int E_loc, int64_t max_rows,
+                      int d, int f, const float* w13, float* h, void* stream);
+int launch_ffn_down_f32(const float* h, const int32_t* offsets, int E_loc, int64_t max_rows,
+                        int d, int f, const float* w2, float* y, void* stream);
+int launch_combine(const void* y_perm, const int32_t* pair_pos, const float* w, int T, int k,
+                   int d, int bf16, void* y, void* stream);
+int launch_pack(const void* w1, const void* w3, const void* w2, int E_loc, int d, int f,
+                int elem_bytes, void* w13, void* w2p, void* stream);
+int check_error(void* ws, void* stream, int* device_flags);
+
+int device_cu_count();
+
+}  // namespace moe

@@ -1,0 +1,83 @@
+"""One MoE layer on one GPU through the C ABI, with every buffer preallocated.
+
+forward() enqueues, on the current HIP stream:
+  [moe_router_logits] -> moe_route -> moe_dispatch -> moe_ffn_up -> moe_ffn_down -> moe_combine
+and never synchronises with the host (row counts stay on the device).
+"""
+from __future__ import annotations
+
+from typing import Dict, Optional
+
+import torch
+
+from . import ops
+
+
+class MoELayer:
+    def __init__(self, w13_packed: torch.Tensor, w2_packed: torch.Tensor, *, E: int, k: int,
+                 gate, T: int, capacity: int = -1, e_begin: int = 0, e_end: Optional[int] = None):
+        self.w13, self.w2 = w13_packed, w2_packed
+        self.E, self.k, self.gate, self.T = E, k, gate, T
+        self.capacity = capacity
+        self.e_begin = e_begin
+        self.e_end = E if e_end is None else e_end
+        self.E_loc = self.e_end - self.e_begin
+        self.d = w13_packed.shape[2]
+        self.f = w13_packed.shape[1] // 2
+        self.dtype = w13_packed.dtype
+        dev = w13_packed.device
+        if w13_packed.shape[0] != self.E_loc:
+            raise ValueError("packed weights must hold exactly the local experts")
+        self.ws = ops.alloc_workspace(T, E, k, self.E_loc, dev)
+        self.plan = ops.alloc_plan(T, E, k, self.E_loc, capacity, self.d, self.dtype, dev)
+        rows = max(self.plan.max_rows, 1)
+        self.logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+        self.topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+        self.topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+        self.h = torch.empty((rows, self.f), dtype=self.dtype, device=dev)
+        self.y_perm = torch.empty((rows, self.d), dtype=self.dtype, device=dev)
+        self.y = torch.empty((T, self.d), dtype=self.dtype, device=dev)
+
+    # individual steps (the benchmark brackets each with events)
+    def router(self, x, w_gate):
+        return ops.moe_router_logits(x, w_gate, self.logits)
+
+    def route(self, logits):
+        return ops.moe_route(logits, self.k, self.gate, self.topk_idx, self.topk_w)
+
+    def dispatch(self, x):
+        return ops.moe_dispatch(self.topk_idx, self.E, self.capacity, self.e_begin, self.e_end, x,
+                                self.ws, self.plan)
+
+    def ffn_up(self):
+        return ops.moe_ffn_up(self.plan.x_perm, self.plan.offsets, self.E_loc, self.plan.max_rows,
+                              self.w13, self.h, self.ws)
+
+    def ffn_down(self):
+        return ops.moe_ffn_down(self.h, self.plan.offsets, self.E_loc, self.plan.max_rows, self.w2,
+                                self.y_perm, self.ws)
+
+    def combine(self):
+        return ops.moe_combine(self.y_perm, self.plan.pair_pos, self.topk_w, self.y)
+
+    def forward(self, x: torch.Tensor, logits: Optional[torch.Tensor] = None,
+                w_gate: Optional[torch.Tensor] = None) -> torch.Tensor:
+        if x.shape[0] != self.T:
+            raise ValueError(f"layer was sized for T={self.T}, got {x.shape[0]}")
+        if logits is None:
+            if w_gate is None:
+                raise ValueError("need logits or a gate matrix")
+            logits = self.router(x, w_gate)
+        self.route(logits)
+        self.dispatch(x)
+        self.ffn_up()
+        self.ffn_down()
+        self.combine()
+        return self.y
+
+    def outputs(self) -> Dict[str, torch.Tensor]:
+        p = self.plan
+        return dict(logits=self.logits, topk_idx=self.topk_idx, topk_w=self.topk_w,
+                    counts=p.counts, offsets=p.offsets, sorted_pair=p.sorted_pair,
+                    pair_pos=p.pair_pos, n_kept=p.n_kept, x_perm=p.x_perm, h=self.h,
+                    y_perm=self.y_perm, y=self.y)

@@ -1,0 +1,210 @@
+"""Thin PyTorch binding of the C ABI: same names as include/moe.h.
+
+Each function checks tensor placement, dtype and contiguity, allocates the
+outputs the caller did not pass (torch is the allocator), and calls the
+library on torch's current HIP stream.  No step of the MoE path runs here:
+every computation happens in the library's kernels.
+"""
+from __future__ import annotations
+
+import dataclasses
+from fractions import Fraction
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib as L
+from ._lib import check, lib
+
+GATES = {
+    "softmax_topk_renorm": L.MOE_GATE_SOFTMAX_TOPK_RENORM,
+    "sigmoid_topk_norm": L.MOE_GATE_SIGMOID_TOPK_NORM,
+}
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return L.MOE_F32
+    if t == torch.bfloat16:
+        return L.MOE_BF16
+    raise TypeError(f"unsupported dtype {t}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr() if t.numel() else None
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _gate_code(gate) -> int:
+    return GATES[gate] if isinstance(gate, str) else int(gate)
+
+
+def moe_workspace_bytes(T: int, E: int, k: int, E_loc: int) -> int:
+    return int(lib().moe_workspace_bytes(T, E, k, E_loc))
+
+
+def moe_capacity(T: int, k: int, E: int, capacity_factor) -> int:
+    """Per-expert capacity for a capacity factor (None = no limit -> -1)."""
+    if capacity_factor is None:
+        return -1
+    q = Fraction(str(capacity_factor))
+    c = int(lib().moe_capacity(T, k, E, q.numerator, q.denominator))
+    if c < -1:
+        raise ValueError("invalid capacity arguments")
+    return c
+
+
+def moe_max_rows(T: int, k: int, E_loc: int, capacity: int) -> int:
+    return int(lib().moe_max_rows(T, k, E_loc, capacity))
+
+
+def alloc_workspace(T: int, E: int, k: int, E_loc: int, device="cuda") -> torch.Tensor:
+    n = moe_workspace_bytes(T, E, k, E_loc)
+    if n == 0:
+        raise ValueError("invalid sizes for the workspace")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def moe_pack_weights(w1: torch.Tensor, w3: torch.Tensor, w2: torch.Tensor,
+                     w13_packed: Optional[torch.Tensor] = None,
+                     w2_packed: Optional[torch.Tensor] = None, stream=None):
+    """w1, w3 [E_loc, d, f], w2 [E_loc, f, d] -> (w13 [E_loc, 2f, d], w2p [E_loc, d, f])."""
+    E_loc, d, f = w1.shape
+    if w13_packed is None:
+        w13_packed = torch.empty((E_loc, 2 * f, d), dtype=w1.dtype, device=w1.device)
+    if w2_packed is None:
+        w2_packed = torch.empty((E_loc, d, f), dtype=w1.dtype, device=w1.device)
+    check(lib().moe_pack_weights(_ptr(w1), _ptr(w3), _ptr(w2), E_loc, d, f, _dtype_code(w1.dtype),
+                                 _ptr(w13_packed), _ptr(w2_packed), _stream(stream)),
+          "moe_pack_weights")
+    return w13_packed, w2_packed
+
+
+def moe_router_logits(x: torch.Tensor, w_gate: torch.Tensor,
+                      logits: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    T, d = x.shape
+    E = w_gate.shape[1]
+    if x.dtype != torch.bfloat16 or w_gate.dtype != torch.float32:
+        raise TypeError("router logits take bf16 x and an fp32 gate matrix")
+    if logits is None:
+        logits = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    check(lib().moe_router_logits(_ptr(x), _ptr(w_gate), T, d, E, _ptr(logits), _stream(stream)),
+          "moe_router_logits")
+    return logits
+
+
+def moe_route(logits: torch.Tensor, k: int, gate, topk_idx: Optional[torch.Tensor] = None,
+              topk_w: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    T, E = logits.shape
+    if logits.dtype != torch.float32:
+        raise TypeError("logits must be fp32")
+    if topk_idx is None:
+        topk_idx = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+    if topk_w is None:
+        topk_w = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    check(lib().moe_route(_ptr(logits), T, E, k, _gate_code(gate), _ptr(topk_idx), _ptr(topk_w),
+                          _stream(stream)), "moe_route")
+    return topk_idx, topk_w
+
+
+@dataclasses.dataclass
+class DispatchPlan:
+    """The per-batch routing plan (reused by the combine)."""
+    counts: torch.Tensor
+    offsets: torch.Tensor
+    sorted_pair: torch.Tensor
+    pair_pos: torch.Tensor
+    n_kept: torch.Tensor
+    x_perm: Optional[torch.Tensor]
+    max_rows: int
+
+
+def alloc_plan(T: int, E: int, k: int, E_loc: int, capacity: int, d: int, dtype,
+               device="cuda") -> DispatchPlan:
+    rows = moe_max_rows(T, k, E_loc, capacity)
+    i32 = dict(dtype=torch.int32, device=device)
+    return DispatchPlan(counts=torch.empty(E, **i32), offsets=torch.empty(E_loc + 1, **i32),
+                        sorted_pair=torch.empty(max(rows, 1), **i32),
+                        pair_pos=torch.empty(max(T * k, 1), **i32), n_kept=torch.empty(4, **i32),
+                        x_perm=torch.empty((max(rows, 1), d), dtype=dtype, device=device),
+                        max_rows=rows)
+
+
+def moe_dispatch(topk_idx: torch.Tensor, E: int, capacity: int, e_begin: int, e_end: int,
+                 x: Optional[torch.Tensor], ws: torch.Tensor, plan: Optional[DispatchPlan] = None,
+                 d: Optional[int] = None, dtype=None, stream=None) -> DispatchPlan:
+    T, k = topk_idx.shape
+    if x is not None:
+        d, dtype = x.shape[1], x.dtype
+    d = d or 8
+    dtype = dtype or torch.bfloat16
+    if plan is None:
+        plan = alloc_plan(T, E, k, e_end - e_begin, capacity, d, dtype, topk_idx.device)
+    check(lib().moe_dispatch(_ptr(topk_idx), T, E, k, capacity, e_begin, e_end, _ptr(x), d,
+                             _dtype_code(dtype), _ptr(plan.counts), _ptr(plan.offsets),
+                             _ptr(plan.sorted_pair), _ptr(plan.pair_pos), _ptr(plan.n_kept),
+                             _ptr(plan.x_perm) if x is not None else None, _ptr(ws), ws.numel(),
+                             _stream(stream)), "moe_dispatch")
+    return plan
+
+
+def moe_ffn_up(x_perm, offsets, E_loc, max_rows, w13_packed, h=None, ws=None, stream=None):
+    d = x_perm.shape[1]
+    f = w13_packed.shape[1] // 2
+    if h is None:
+        h = torch.empty((max(max_rows, 1), f), dtype=x_perm.dtype, device=x_perm.device)
+    check(lib().moe_ffn_up(_ptr(x_perm), _ptr(offsets), E_loc, max_rows, d, f,
+                           _dtype_code(x_perm.dtype), _ptr(w13_packed), _ptr(h), _ptr(ws),
+                           ws.numel() if ws is not None else 0, _stream(stream)), "moe_ffn_up")
+    return h
+
+
+def moe_ffn_down(h, offsets, E_loc, max_rows, w2_packed, y_perm=None, ws=None, stream=None):
+    f = h.shape[1]
+    d = w2_packed.shape[1]
+    if y_perm is None:
+        y_perm = torch.empty((max(max_rows, 1), d), dtype=h.dtype, device=h.device)
+    check(lib().moe_ffn_down(_ptr(h), _ptr(offsets), E_loc, max_rows, d, f, _dtype_code(h.dtype),
+                             _ptr(w2_packed), _ptr(y_perm), _ptr(ws),
+                             ws.numel() if ws is not None else 0, _stream(stream)), "moe_ffn_down")
+    return y_perm
+
+
+def moe_expert_ffn(x_perm, offsets, E_loc, max_rows, w13_packed, w2_packed, h=None, y_perm=None,
+                   ws=None, stream=None):
+    d = x_perm.shape[1]
+    f = w13_packed.shape[1] // 2
+    if h is None:
+        h = torch.empty((max(max_rows, 1), f), dtype=x_perm.dtype, device=x_perm.device)
+    if y_perm is None:
+        y_perm = torch.empty((max(max_rows, 1), d), dtype=x_perm.dtype, device=x_perm.device)
+    check(lib().moe_expert_ffn(_ptr(x_perm), _ptr(offsets), E_loc, max_rows, d, f,
+                               _dtype_code(x_perm.dtype), _ptr(w13_packed), _ptr(w2_packed),
+                               _ptr(h), _ptr(y_perm), _ptr(ws), ws.numel() if ws is not None else 0,
+                               _stream(stream)), "moe_expert_ffn")
+    return h, y_perm
+
+
+def moe_combine(y_perm, pair_pos, topk_w, y=None, stream=None):
+    T, k = topk_w.shape
+    d = y_perm.shape[1]
+    if y is None:
+        y = torch.empty((T, d), dtype=y_perm.dtype, device=y_perm.device)
+    check(lib().moe_combine(_ptr(y_perm), _ptr(pair_pos), _ptr(topk_w), T, k, d,
+                            _dtype_code(y_perm.dtype), _ptr(y), _stream(stream)), "moe_combine")
+    return y
+
+
+def moe_check_error(ws, stream=None) -> int:
+    """Synchronise and return the device-side status (0 = OK) without raising."""
+    return int(lib().moe_check_error(_ptr(ws), _stream(stream)))

@@ -1,0 +1,84 @@
+"""Helpers for the GPU parity tests: move seeded workloads onto the GPU, run the
+library through its C ABI, bring results back as numpy.  (No arithmetic of
+the method lives here.)"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import routing_dispatch_expert_moe_amd as M
+from oracle import moe_oracle as O
+
+DEV = torch.device("cuda:0")
+
+
+def log(msg: str) -> None:
+    print(f"[gpu-test] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def t_in(arr: np.ndarray, dtype: str) -> torch.Tensor:
+    """Host array (fp32 values or bf16 bits) -> device tensor of the matching torch dtype."""
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).to(DEV)
+    return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).to(DEV)
+
+
+def t_out(t: torch.Tensor) -> np.ndarray:
+    """Device tensor -> host numpy (bf16 as uint16 bits, others as is)."""
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def as64(t: torch.Tensor, dtype: str) -> np.ndarray:
+    return O.widen(t_out(t), dtype)
+
+
+def packed_weights(wl, chunk: int = 16, keep_host: bool = False):
+    """Generate the workload's local experts, upload and pack them chunk by chunk.
+
+    Returns (w13 [E_loc, 2f, d], w2p [E_loc, d, f], host) where host is the list
+    of per-expert (W1, W3, W2) host arrays if keep_host else None.
+    """
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    w13 = torch.empty((wl.E_loc, 2 * wl.f, wl.d), dtype=tdt, device=DEV)
+    w2p = torch.empty((wl.E_loc, wl.d, wl.f), dtype=tdt, device=DEV)
+    host = [] if keep_host else None
+    for c0 in range(0, wl.E_loc, chunk):
+        ids = list(range(wl.e_begin + c0, wl.e_begin + min(wl.E_loc, c0 + chunk)))
+        a, b, c = wl.stacked_weights(ids)
+        if keep_host:
+            host.extend(zip(a, b, c))
+        n = len(ids)
+        M.moe_pack_weights(t_in(a, wl.dtype), t_in(b, wl.dtype), t_in(c, wl.dtype),
+                           w13[c0:c0 + n], w2p[c0:c0 + n])
+    torch.cuda.synchronize()
+    return w13, w2p, host
+
+
+def weights_fn(wl, host=None):
+    """Float64 weights of local expert i for the oracle (from the host copy, else regenerated)."""
+    def get(i):
+        if host is not None:
+            w1, w3, w2 = host[i]
+        else:
+            w1, w3, w2 = wl.expert_weights(wl.e_begin + i)
+        return O.widen(w1, wl.dtype), O.widen(w3, wl.dtype), O.widen(w2, wl.dtype)
+    return get
+
+
+def capacity_of(wl) -> int:
+    """The library's capacity for the workload, checked against the oracle's rule."""
+    c = M.moe_capacity(wl.T, wl.k, wl.E, wl.capacity_factor)
+    assert c == O.capacity(wl.T, wl.k, wl.E, wl.capacity_factor)
+    return c
+
+
+def layer_for(wl, w13, w2p, capacity=None) -> M.MoELayer:
+    C = capacity_of(wl) if capacity is None else capacity
+    return M.MoELayer(w13, w2p, E=wl.E, k=wl.k, gate=wl.gate, T=wl.T, capacity=C,
+                      e_begin=wl.e_begin, e_end=wl.e_end)

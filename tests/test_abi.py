@@ -1,0 +1,140 @@
+"""The C-ABI library without a GPU: it loads, exports every symbol the header
+declares, and rejects invalid arguments on the host before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import routing_dispatch_expert_moe_amd as M
+from routing_dispatch_expert_moe_amd import _lib as L
+from oracle import moe_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        from routing_dispatch_expert_moe_amd import build
+        build.build()
+    return M.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_path():
+    names = declared_functions()
+    for n in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_router_logits",
+              "moe_pack_weights", "moe_check_error", "moe_ffn_up", "moe_ffn_down"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    raw = ctypes.CDLL(L.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(raw, name), name
+        assert name in L.SIGNATURES, f"binding lacks {name}"
+
+
+def test_status_strings(lib):
+    for s in range(7):
+        assert lib.moe_status_string(s).decode().startswith("MOE_")
+    assert b"unknown" in lib.moe_status_string(99)
+
+
+def test_capacity_matches_oracle_rule(lib):
+    for T, k, E, cf in [(16384, 2, 128, 1.25), (32 * 2048, 2, 128, 1.0), (100, 2, 8, 0.1),
+                        (30, 1, 10, 0.3), (7, 3, 5, 2.0), (1, 1, 1, 1.0), (0, 2, 4, 1.0)]:
+        assert M.moe_capacity(T, k, E, cf) == O.capacity(T, k, E, cf)
+    assert M.moe_capacity(10, 1, 1, None) == -1
+
+
+def test_max_rows_and_workspace(lib):
+    assert M.moe_max_rows(16384, 2, 32, 320) == 32 * 320
+    assert M.moe_max_rows(128, 8, 256, -1) == 1024
+    assert M.moe_max_rows(10, 2, 4, 100) == 20
+    assert M.moe_workspace_bytes(4096, 8, 2, 8) >= 256 + 2 * 16 * 8 * 4
+    assert M.moe_workspace_bytes(10, 8, 9, 8) == 0      # k > MOE_MAX_K
+    assert M.moe_workspace_bytes(10, 8, 2, 9) == 0      # E_loc > E
+
+
+FAKE = 4096      # aligned, never dereferenced: every call below fails validation first
+MIS = 4098       # not 16-byte aligned
+
+
+def test_route_validation(lib):
+    r = lib.moe_route
+    assert r(FAKE, 10, 8, 0, 0, FAKE, FAKE, None) == L.MOE_ERR_INVALID_TOPK
+    assert r(FAKE, 10, 8, 9, 0, FAKE, FAKE, None) == L.MOE_ERR_INVALID_TOPK
+    assert r(FAKE, 10, 4, 5, 0, FAKE, FAKE, None) == L.MOE_ERR_INVALID_TOPK
+    assert r(FAKE, 10, 2000, 2, 0, FAKE, FAKE, None) == L.MOE_ERR_INVALID_ARG
+    assert r(FAKE, 10, 8, 2, 7, FAKE, FAKE, None) == L.MOE_ERR_INVALID_ARG
+    assert r(None, 10, 8, 2, 0, FAKE, FAKE, None) == L.MOE_ERR_INVALID_ARG
+    assert r(MIS, 10, 8, 2, 0, FAKE, FAKE, None) == L.MOE_ERR_MISALIGNED
+    assert r(FAKE, -1, 8, 2, 0, FAKE, FAKE, None) == L.MOE_ERR_INVALID_ARG
+    assert r(None, 0, 8, 2, 0, None, None, None) == L.MOE_OK   # empty batch: nothing to do
+
+
+def test_dispatch_validation(lib):
+    d = lib.moe_dispatch
+    ok = dict(idx=FAKE, T=10, E=8, k=2, cap=-1, e0=0, e1=8, x=FAKE, d=64, dt=L.MOE_BF16,
+              counts=FAKE, off=FAKE, sp=FAKE, pp=FAKE, nk=FAKE, xp=FAKE, ws=FAKE, wsb=0)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return d(a["idx"], a["T"], a["E"], a["k"], a["cap"], a["e0"], a["e1"], a["x"], a["d"],
+                 a["dt"], a["counts"], a["off"], a["sp"], a["pp"], a["nk"], a["xp"], a["ws"],
+                 a["wsb"], None)
+
+    assert call() == L.MOE_ERR_WORKSPACE
+    assert call(wsb=M.moe_workspace_bytes(10, 8, 2, 8) - 1) == L.MOE_ERR_WORKSPACE
+    assert call(k=9) == L.MOE_ERR_INVALID_TOPK
+    assert call(e0=3, e1=3) == L.MOE_ERR_INVALID_ARG
+    assert call(e1=9) == L.MOE_ERR_INVALID_ARG
+    assert call(d=12) == L.MOE_ERR_UNSUPPORTED      # bf16 rows of 24 bytes
+    assert call(dt=5) == L.MOE_ERR_UNSUPPORTED
+    assert call(xp=None) == L.MOE_ERR_INVALID_ARG
+    assert call(pp=MIS) == L.MOE_ERR_MISALIGNED
+    assert call(ws=None) == L.MOE_ERR_INVALID_ARG
+
+
+def test_ffn_validation(lib):
+    f = lib.moe_expert_ffn
+    args = [FAKE, FAKE, 8, 100, 4096, 14336, L.MOE_BF16, FAKE, FAKE, FAKE, FAKE, None, 0, None]
+    bad_d = list(args); bad_d[4] = 4000
+    assert f(*bad_d) == L.MOE_ERR_UNSUPPORTED
+    bad_e = list(args); bad_e[2] = 0
+    assert f(*bad_e) == L.MOE_ERR_INVALID_ARG
+    mis = list(args); mis[7] = MIS
+    assert f(*mis) == L.MOE_ERR_MISALIGNED
+    nul = list(args); nul[1] = None
+    assert f(*nul) == L.MOE_ERR_INVALID_ARG
+    f32 = list(args); f32[6] = L.MOE_F32; f32[4] = 6
+    assert f(*f32) == L.MOE_ERR_UNSUPPORTED
+    up = lib.moe_ffn_up
+    assert up(FAKE, FAKE, 8, -1, 64, 64, L.MOE_BF16, FAKE, FAKE, None, 0, None) == L.MOE_ERR_INVALID_ARG
+
+
+def test_combine_router_pack_validation(lib):
+    assert lib.moe_combine(FAKE, FAKE, FAKE, 10, 9, 64, L.MOE_BF16, FAKE, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_combine(FAKE, FAKE, FAKE, 10, 2, 6, L.MOE_F32, FAKE, None) == L.MOE_ERR_UNSUPPORTED
+    assert lib.moe_combine(FAKE, FAKE, MIS, 10, 2, 64, L.MOE_BF16, FAKE, None) == L.MOE_ERR_MISALIGNED
+    assert lib.moe_router_logits(FAKE, FAKE, 10, 4096, 65, FAKE, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_router_logits(FAKE, FAKE, 10, 4092, 8, FAKE, None) == L.MOE_ERR_UNSUPPORTED
+    assert lib.moe_pack_weights(FAKE, FAKE, FAKE, 0, 64, 64, L.MOE_BF16, FAKE, FAKE, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_pack_weights(FAKE, MIS, FAKE, 2, 64, 64, L.MOE_BF16, FAKE, FAKE, None) == L.MOE_ERR_MISALIGNED
+    assert lib.moe_check_error(None, None) == L.MOE_ERR_INVALID_ARG
+
+
+def test_package_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(L, "_lib", None)
+    with pytest.raises(RuntimeError, match="no CPU fallback"):
+        L.lib()

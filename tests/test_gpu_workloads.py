@@ -1,0 +1,137 @@
+"""GPU parity on the five named workloads at their full sizes, in the same
+launch configuration the benchmark times (MoELayer.forward).
+
+Routing, counts, offsets, sorted pairs, pair positions and the permuted rows
+are compared bit-exactly over the whole layer; expert outputs y are compared
+on sampled tokens that the oracle computes one at a time from the layer's
+definition (max|err|/max|ref| <= 1e-2 bf16, 1e-5 fp32).
+"""
+import numpy as np
+import pytest
+import torch
+
+import routing_dispatch_expert_moe_amd as M
+from oracle import moe_oracle as O
+from workloads import make
+
+from gpu_util import (DEV, as64, capacity_of, layer_for, log, packed_weights, t_in, t_out,
+                      weights_fn)
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 1e-2}
+_WEIGHTS = {}
+
+
+def weights(wl):
+    key = (wl.E_loc, wl.e_begin, wl.d, wl.f, wl.seed, wl.dtype)
+    if key not in _WEIGHTS:
+        _WEIGHTS.clear()
+        torch.cuda.empty_cache()
+        log(f"generating + packing {wl.E_loc} experts d={wl.d} f={wl.f}")
+        _WEIGHTS[key] = packed_weights(wl, keep_host=True)
+    return _WEIGHTS[key]
+
+
+def check_plan(out, ref, T, k):
+    n = ref["n_kept"]
+    assert int(t_out(out["n_kept"])[0]) == n
+    assert np.array_equal(t_out(out["counts"]), ref["counts"])
+    assert np.array_equal(t_out(out["offsets"]), ref["offsets"])
+    assert np.array_equal(t_out(out["sorted_pair"])[:n], ref["sorted_pair"])
+    assert np.array_equal(t_out(out["pair_pos"])[:T * k], ref["pair_pos"])
+
+
+def sampled_tokens(T, pair_pos, k, n=24, seed=0):
+    rng = np.random.default_rng(seed)
+    cand = sorted(set([0, T - 1] + rng.choice(T, size=min(n, T), replace=False).tolist()))
+    return cand
+
+
+def check_outputs(wl, host, y, idx, w, pair_pos, tokens):
+    x64 = O.widen(wl.x[tokens], wl.dtype)
+    wfn = weights_fn(wl, host)
+    ref = O.token_outputs(tokens, x64, idx, w, pair_pos, wl.e_begin,
+                          lambda e: wfn(e - wl.e_begin))
+    got = as64(y, wl.dtype)[tokens]
+    err = O.rel_err(got, ref)
+    log(f"{wl.name}: sampled {len(tokens)} tokens rel err {err:.3e}")
+    assert err <= TOL[wl.dtype]
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", ["tiny_fp32", "ep_rank_share", "dsv3_decode", "dsv3_prefill_zipf"])
+def test_workload_with_given_logits(name):
+    wl = make(name)
+    log(f"workload {name}: T={wl.T} d={wl.d} f={wl.f} E={wl.E} k={wl.k} local=[{wl.e_begin},{wl.e_end})")
+    w13, w2p, host = weights(wl)
+    layer = layer_for(wl, w13, w2p)
+    x = t_in(wl.x, wl.dtype)
+    y = layer.forward(x, logits=t_in(wl.logits, "f32"))
+    assert M.moe_check_error(layer.ws) == 0
+    out = layer.outputs()
+    idx, w = O.route(wl.logits, wl.k, wl.gate)
+    assert np.array_equal(t_out(out["topk_idx"]), idx)
+    assert O.rel_err(t_out(out["topk_w"]), w) <= 1e-6
+    ref = O.dispatch(idx, wl.E, capacity_of(wl), wl.e_begin, wl.e_end)
+    check_plan(out, ref, wl.T, wl.k)
+    n = ref["n_kept"]
+    counts = ref["counts"][wl.e_begin:wl.e_end]
+    log(f"{name}: n_kept={n} per-expert counts min={counts.min()} max={counts.max()} "
+        f"dropped={(ref['pair_pos'] == O.DROPPED).sum()} remote={(ref['pair_pos'] == O.REMOTE).sum()}")
+    assert np.array_equal(t_out(out["x_perm"])[:n], O.permute(wl.x, ref["sorted_pair"], wl.k))
+    if name == "tiny_fp32":
+        full = O.moe_layer(wl.x, wl.dtype, wl.logits, wl.k, wl.gate, weights_fn(wl, host), wl.E)
+        assert O.rel_err(as64(y, wl.dtype), full["y"]) <= TOL["f32"]
+    else:
+        toks = sampled_tokens(wl.T, ref["pair_pos"], wl.k, n=12 if wl.E >= 256 else 24)
+        check_outputs(wl, host, y, idx, w, ref["pair_pos"], toks)
+    # a second pass is bitwise identical
+    y1 = t_out(y).copy()
+    layer.forward(x, logits=t_in(wl.logits, "f32"))
+    assert np.array_equal(t_out(layer.y), y1)
+
+
+@pytest.mark.timeout(600)
+def test_mixtral_prefill_with_router():
+    """Router logits on the GPU, then the whole path; the oracle routes on its own
+    float64 logits rounded to fp32."""
+    wl = make("mixtral_prefill")
+    log(f"workload mixtral_prefill: T={wl.T} d={wl.d} f={wl.f} E={wl.E}")
+    w13, w2p, host = weights(wl)
+    layer = layer_for(wl, w13, w2p)
+    x = t_in(wl.x, "bf16")
+    wg = t_in(wl.w_gate, "f32")
+    y = layer.forward(x, w_gate=wg)
+    assert M.moe_check_error(layer.ws) == 0
+    out = layer.outputs()
+    l64 = O.router_logits(O.widen(wl.x, "bf16"), wl.w_gate.astype(np.float64))
+    gl = t_out(out["logits"])
+    err = O.rel_err(gl, l64)
+    log(f"router logits rel err {err:.3e}")
+    assert err <= 1e-5
+    l32 = O.round_to_f32(l64)
+    idx, w = O.route(l32, wl.k, wl.gate)
+    gidx = t_out(out["topk_idx"])
+    # tokens whose routing differs must be near-ties within the router's error
+    diff = np.nonzero((gidx != idx).any(axis=1))[0]
+    bound = 2e-5 * np.abs(l64).max()
+    for t in diff:
+        chosen = set(gidx[t].tolist())
+        lo = min(l64[t, e] for e in chosen)
+        hi = max(l64[t, e] for e in range(wl.E) if e not in chosen)
+        assert hi - lo <= bound, f"token {t}: routing differs beyond a near-tie"
+    log(f"mixtral_prefill: {len(diff)} tokens routed differently (near-ties)")
+    # routing step alone on the oracle's fp32 logits: bit-exact
+    gi2, gw2 = M.moe_route(t_in(l32, "f32"), wl.k, wl.gate)
+    assert np.array_equal(t_out(gi2), idx)
+    assert O.rel_err(t_out(gw2), w) <= 1e-6
+    ref = O.dispatch(idx, wl.E)
+    if len(diff) == 0:
+        check_plan(out, ref, wl.T, wl.k)
+        n = ref["n_kept"]
+        assert np.array_equal(t_out(out["x_perm"])[:n], O.permute(wl.x, ref["sorted_pair"], wl.k))
+    # sampled outputs: tokens routed identically on both sides, all oracle inputs
+    skip = set(diff.tolist())
+    toks = [t for t in sampled_tokens(wl.T, ref["pair_pos"], wl.k, n=32) if t not in skip]
+    check_outputs(wl, host, y, idx, w, ref["pair_pos"], toks)
