@@ -27,11 +27,7 @@
 
 namespace moe {
 
-struct TileCfg {
-  int BM, BN, BK, WM, WN;
-};
-
-__device__ __forceinline__ float silu_f(float a) { return a / (1.f + __expf(-a)); }
+__device__ __forceinline__ float silu_f(float a) { return a * __builtin_amdgcn_rcpf(1.f + __expf(-a)); }
 
 template <int BM, int BN, int BK, int WM, int WN, bool SWIGLU>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(
@@ -221,6 +217,7 @@ static int launch_gemm(const void* A, const int32_t* offsets, int E_loc, int64_t
   return static_cast<int>(hipGetLastError());
 }
 
+
 // Rows per expert on average decide the tile shape: weight-streaming (few
 // rows) or MFMA-bound (many rows).
 int launch_ffn_up_bf16(const void* x_perm, const int32_t* offsets, int E_loc, int64_t max_rows,
@@ -228,9 +225,12 @@ int launch_ffn_up_bf16(const void* x_perm, const int32_t* offsets, int E_loc, in
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (max_rows == 0) return 0;
   const int64_t avg = max_rows / E_loc;
-  if (avg <= 48)
+  // the large-tile kernel addresses operands with 32-bit byte offsets
+  const bool fits32 = static_cast<double>(max_rows) * d * 2 < 4294967296.0 &&
+                      static_cast<double>(2) * f * d * 2 < 4294967296.0;
+  if (avg <= 48 || !fits32)
     return launch_gemm<32, 128, 64, 1, 4, true>(x_perm, offsets, E_loc, max_rows, w13, h, f, d, s);
-  return launch_gemm<128, 128, 64, 2, 2, true>(x_perm, offsets, E_loc, max_rows, w13, h, f, d, s);
+  return launch_gemm_big_bf16(true, x_perm, offsets, E_loc, max_rows, w13, h, f, d, stream);
 }
 
 int launch_ffn_down_bf16(const void* h, const int32_t* offsets, int E_loc, int64_t max_rows,
@@ -238,9 +238,11 @@ int launch_ffn_down_bf16(const void* h, const int32_t* offsets, int E_loc, int64
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (max_rows == 0) return 0;
   const int64_t avg = max_rows / E_loc;
-  if (avg <= 48)
+  const bool fits32 = static_cast<double>(max_rows) * f * 2 < 4294967296.0 &&
+                      static_cast<double>(d) * f * 2 < 4294967296.0;
+  if (avg <= 48 || !fits32)
     return launch_gemm<32, 128, 64, 1, 4, false>(h, offsets, E_loc, max_rows, w2, y, d, f, s);
-  return launch_gemm<128, 128, 64, 2, 2, false>(h, offsets, E_loc, max_rows, w2, y, d, f, s);
+  return launch_gemm_big_bf16(false, h, offsets, E_loc, max_rows, w2, y, d, f, stream);
 }
 
 }  // namespace moe

@@ -1,0 +1,309 @@
+// Large-tile grouped GEMM for experts with many rows (MFMA-bound), bf16 in,
+// fp32 accumulation, v_mfma_f32_32x32x16_bf16.
+//
+// DWDP page, key optimisations: the first grouped GEMM takes every local
+// expert's rows against its fused [W1 | W3] operand with SwiGLU in the
+// epilogue; the second grouped GEMM applies W2.
+//
+// Tile: 256 activation rows x 256 weight rows (SwiGLU: 128 W1 rows + the
+// matching 128 W3 rows -> 128 h columns).  4 waves split the tile 2 x 2;
+// each wave owns 128 x 128 (4 x 4 MFMA tiles, 256 fp32 accumulators).
+//
+// Memory pipeline: operands go HBM/L2 -> LDS directly (global_load_lds_dwordx4,
+// no staging registers) in K-steps of 32, through 4 LDS stages of 32 KB, so
+// loads run three steps ahead of the MFMAs.  A step's loads are spread over
+// the MFMAs of the step before; MFMA operands are double buffered in
+// registers (the next 16-deep substep's LDS reads overlap the current
+// substep's MFMAs), and each step's barrier sits under the last substep's
+// MFMAs.  The load stream runs across tile boundaries, so the next tile's
+// operands are in flight during the current tile's epilogue.  Rows are 64
+// bytes (4 chunks of 16 B); chunk c of row r sits at chunk c ^ ((r >> 2) & 3),
+// so each 16-lane phase of a ds_read_b128 touches 16 distinct bank groups;
+// the direct loads realise this by choosing which global chunk each lane
+// fetches.
+//
+// Scheduling: persistent grid (one workgroup per CU); tiles in expert order,
+// M-tiles fastest so consecutive tiles share a weight tile; workgroup ids
+// remapped so each XCD (ids dealt round-robin over 8 XCDs) owns contiguous
+// tile ranges and shares weight tiles in its own L2.
+#include "common.h"
+#include "launch.h"
+#include "tile_sched.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kBM = 256, kBNW = 256;
+// pipeline step depth along K and LDS stages (loads run kStages - 1 steps ahead)
+constexpr int kBK = 32, kStages = 4;
+
+__device__ __forceinline__ float silu_fast(float a) {
+  return a * __builtin_amdgcn_rcpf(1.f + __expf(-a));
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  else if constexpr (N == 24) asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+  else if constexpr (N == 32) asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
+  else static_assert(N == 0, "unsupported vmcnt");
+}
+
+struct Tile {
+  int e, m0, seg1, n0;
+};
+
+template <int BN>
+__device__ __forceinline__ Tile decode_tile(int t, int NT, const int* prefix, const int* segs,
+                                            int E_loc) {
+  Tile r;
+  r.e = find_expert(prefix, E_loc, t / NT);
+  const int mt_e = prefix[r.e + 1] - prefix[r.e];
+  const int local = t - prefix[r.e] * NT;
+  const int nt = local / mt_e, mti = local % mt_e;
+  r.m0 = segs[r.e] + mti * kBM;
+  r.seg1 = segs[r.e + 1];
+  r.n0 = nt * BN;
+  // the tile is the same for the whole wave: keep its fields in scalar registers
+  r.e = __builtin_amdgcn_readfirstlane(r.e);
+  r.m0 = __builtin_amdgcn_readfirstlane(r.m0);
+  r.seg1 = __builtin_amdgcn_readfirstlane(r.seg1);
+  r.n0 = __builtin_amdgcn_readfirstlane(r.n0);
+  return r;
+}
+
+}  // namespace
+
+// BK: K depth of one pipeline step (32 or 64); STAGES: LDS buffers (loads run
+// STAGES - 1 steps ahead of the MFMAs).
+template <bool SWIGLU, int BK, int STAGES, int VS>
+__global__ __launch_bounds__(256, 1) void gemm_bf16_big(const uint16_t* __restrict__ A,
+                                                        const int32_t* __restrict__ offsets,
+                                                        int E_loc,
+                                                        const uint16_t* __restrict__ W,
+                                                        uint16_t* __restrict__ C, int N, int K) {
+  constexpr int BN = SWIGLU ? 128 : 256;  // output columns per tile
+  constexpr int KC = BK / 8;              // 16-byte chunks per row
+  constexpr int RPI = 64 / KC;            // rows covered by one 64-lane 16-byte load
+  constexpr int LPM = kBM / RPI / 4;      // loads per wave per matrix per step
+  constexpr int STAGE_U4 = (kBM + kBNW) * KC;
+  constexpr int SUB = BK / 16;            // MFMA K-substeps per step
+  static_assert(VS == SUB && (2 * LPM / SUB) % 4 == 0, "loads must split evenly over the substeps");
+  extern __shared__ uint4 lds[];
+  __shared__ int prefix[MOE_MAX_E + 1];
+  __shared__ int segs[MOE_MAX_E + 1];
+
+  for (int i = threadIdx.x; i <= E_loc; i += blockDim.x) segs[i] = offsets[i];
+  mtile_prefix<kBM>(offsets, E_loc, prefix);  // ends with a barrier
+  const int NT = (N + BN - 1) / BN;
+  const int total = prefix[E_loc] * NT;
+  const int G = gridDim.x;
+  int vb = blockIdx.x;
+  if ((G & 7) == 0) vb = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+  if (vb >= total) return;
+  const int ntiles = (total - vb + G - 1) / G;
+  const int KT = K / BK;
+  const int S = ntiles * KT;  // this workgroup's K-steps over all its tiles
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const size_t wstride = static_cast<size_t>(SWIGLU ? 2 * N : N) * K;
+  // LDS swizzle: chunk c of row r is stored at c ^ swz(r); swz spreads the 16
+  // rows read by one 16-lane ds_read_b128 phase over all bank groups
+  auto swz = [](int r) { return KC == 8 ? ((r >> 1) & 7) : ((r >> 2) & 3); };
+  // the chunk this lane fetches in each row group it loads (row = g * RPI + lane / KC;
+  // g = i * 4 + wave, so swz depends only on the lane and the wave)
+  const int lrow0 = (lane / KC) + RPI * wave;
+  const int lkc = (lane % KC) ^ swz(lrow0);
+  const char* Ab = reinterpret_cast<const char*>(A);
+
+  // ---- issue side: the tile whose operands are being fetched
+  int it_tile = -1;
+  const char* iWb = nullptr;
+  uint32_t aoff[LPM], boff[LPM];
+  auto set_issue_tile = [&](int j) {
+    const Tile t = decode_tile<BN>(vb + j * G, NT, prefix, segs, E_loc);
+    iWb = reinterpret_cast<const char*>(W + t.e * wstride);
+#pragma unroll
+    for (int i = 0; i < LPM; ++i) {
+      const int rt = (i * 4 + wave) * RPI + lane / KC;  // row within the tile
+      const int arow = min(t.m0 + rt, t.seg1 - 1);
+      aoff[i] = (static_cast<uint32_t>(arow) * K + lkc * 8) * 2u;
+      int wrow;
+      if (SWIGLU) wrow = (rt >> 7) * N + min(t.n0 + (rt & 127), N - 1);
+      else wrow = min(t.n0 + rt, N - 1);
+      boff[i] = (static_cast<uint32_t>(wrow) * K + lkc * 8) * 2u;
+    }
+    it_tile = j;
+  };
+  // loads [p * LPM / VS, (p + 1) * LPM / VS) of A and of B into buffer buf
+  auto issue_part = [&](int p, int buf, uint32_t koff) {
+    uint4* As = lds + buf * STAGE_U4;
+    uint4* Bs = As + kBM * KC;
+#pragma unroll
+    for (int i = p * (LPM / VS); i < (p + 1) * (LPM / VS); ++i) {
+      const int g = i * 4 + wave;
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(Ab + (aoff[i] + koff)),
+          (__attribute__((address_space(3))) void*)(As + g * 64), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(iWb + (boff[i] + koff)),
+          (__attribute__((address_space(3))) void*)(Bs + g * 64), 16, 0, 0);
+    }
+  };
+  // byte offset along K of step p's operands, switching the issue tile when p
+  // starts a new one; steps past the end re-fetch the last step (valid
+  // addresses, result unused)
+  auto issue_koff = [&](int p) -> uint32_t {
+    if (p >= S) p = S - 1;
+    const int j = p / KT, kt = p - j * KT;
+    if (j != it_tile) set_issue_tile(j);
+    return static_cast<uint32_t>(kt) * BK * 2u;
+  };
+
+  // LDS fragments of substep ks of the step held in buffer `buf`
+  bf16x8_t fa[2][4], fb[2][4];
+  auto load_frags = [&](int buf, int ks, int slot) {
+    const uint4* As = lds + buf * STAGE_U4;
+    const uint4* Bs = As + kBM * KC;
+    const int ch = ks * 2 + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = wm * 128 + i * 32 + (lane & 31);
+      fa[slot][i] = __builtin_bit_cast(bf16x8_t, As[r * KC + (ch ^ swz(r))]);
+      const int q = SWIGLU ? ((i >> 1) * 128 + wn * 64 + (i & 1) * 32 + (lane & 31))
+                           : (wn * 128 + i * 32 + (lane & 31));
+      fb[slot][i] = __builtin_bit_cast(bf16x8_t, Bs[q * KC + (ch ^ swz(q))]);
+    }
+  };
+  // Step p becomes readable: this wave's loads of step p are done once at most
+  // the (STAGES - 2) younger steps' loads are outstanding (loads complete in
+  // order) and its own LDS reads of the step before are done; the barrier then
+  // publishes every wave's step-p data and frees the buffer of step p - 1,
+  // which immediately receives the loads of step p + STAGES - 1.
+  // The loads of step p + STAGES - 1 go out in SUB parts: part 0 right after
+  // this barrier, parts 1 .. SUB - 1 during the first substeps of step p
+  // (pk / pb hold the pending step's K offset and buffer meanwhile).
+  uint32_t pk = 0u;
+  int pb = 0;
+  auto sync_and_issue = [&](int p) {
+    wait_vmcnt<(STAGES - 2) * 2 * LPM>();
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    pk = issue_koff(p + STAGES - 1);
+    pb = (p + STAGES - 1) % STAGES;
+    issue_part(0, pb, pk);
+  };
+
+  // ---- prologue: steps 0 .. STAGES - 2 in flight, step 0 made readable
+  for (int p = 0; p < STAGES - 1; ++p) {
+    const uint32_t ko = issue_koff(p);
+#pragma unroll
+    for (int q = 0; q < VS; ++q) issue_part(q, p % STAGES, ko);
+  }
+  sync_and_issue(0);
+
+  for (int j = 0; j < ntiles; ++j) {
+    const Tile ct = decode_tile<BN>(vb + j * G, NT, prefix, segs, E_loc);
+    const int valid = min(kBM, ct.seg1 - ct.m0);
+    f32x16_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[i][q] = f32x16_t{};
+    load_frags((j * KT) % STAGES, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+
+    for (int kt = 0; kt < KT; ++kt) {
+      const int s = j * KT + kt;
+      const int buf = s % STAGES;
+#pragma unroll
+      for (int ks = 0; ks < SUB; ++ks) {
+        const int cur = ks & 1;  // SUB is even: substep 0 of every step uses slot 0
+        const bool last = ks + 1 == SUB;
+        if (!last) {
+          load_frags(buf, ks + 1, cur ^ 1);
+          issue_part(ks + 1, pb, pk);
+        } else if (s + 1 < S) {
+          // the next step's barrier sits under this substep's MFMAs; within
+          // the tile its first fragments are fetched right behind it
+          sync_and_issue(s + 1);
+          if (kt + 1 < KT) load_frags((s + 1) % STAGES, 0, cur ^ 1);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            acc[i][q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][q], acc[i][q], 0, 0, 0);
+        // 8 LDS reads and the 2 * LPM / SUB global loads spread between 16 MFMAs
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (g % 2 == 1) __builtin_amdgcn_sched_group_barrier(0x020, 2 * LPM / SUB / 4, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+
+    // epilogue (registers -> global); D[m][n] of a 32x32 MFMA tile is in lane
+    // n + 32 * ((m / 4) % 2), register 4 * (m / 8) + m % 4
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (wm * 128 + i * 32 >= valid) continue;
+#pragma unroll
+      for (int q = 0; q < (SWIGLU ? 2 : 4); ++q) {
+        const int col = ct.n0 + (SWIGLU ? wn * 64 : wn * 128) + q * 32 + (lane & 31);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          const int row = ct.m0 + wm * 128 + i * 32 + m;
+          float v = acc[i][q][r];
+          if constexpr (SWIGLU) v = silu_fast(v) * acc[i][q + 2][r];
+          if (row < ct.seg1 && col < N) C[static_cast<size_t>(row) * N + col] = f32_to_bf16(v);
+        }
+      }
+    }
+  }
+  wait_vmcnt<0>();  // redundant tail loads must land before the LDS is released
+}
+
+template <bool SWIGLU, int BK, int STAGES, int VS>
+static int launch_big(const void* A, const int32_t* offsets, int E_loc, int64_t max_rows,
+                      const void* W, void* C, int N, int K, hipStream_t s) {
+  const size_t lds = static_cast<size_t>(STAGES) * (kBM + kBNW) * BK * sizeof(uint16_t);
+  auto kern = gemm_bf16_big<SWIGLU, BK, STAGES, VS>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       static_cast<int>(lds));
+    if (e != hipSuccess) return static_cast<int>(e);
+    attr_set = true;
+  }
+  const int BN = SWIGLU ? 128 : 256;
+  const int64_t NT = (N + BN - 1) / BN;
+  const int64_t tiles_ub = (max_rows / kBM + E_loc) * NT;
+  int64_t grid = device_cu_count();
+  if (grid > tiles_ub) grid = tiles_ub;
+  if (grid >= 8) grid &= ~static_cast<int64_t>(7);
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(256), lds, s,
+                     static_cast<const uint16_t*>(A), offsets, E_loc,
+                     static_cast<const uint16_t*>(W), static_cast<uint16_t*>(C), N, K);
+  return static_cast<int>(hipGetLastError());
+}
+
+int launch_gemm_big_bf16(bool swiglu, const void* A, const int32_t* offsets, int E_loc,
+                         int64_t max_rows, const void* W, void* C, int N, int K, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (swiglu)
+    return launch_big<true, kBK, kStages, kBK / 16>(A, offsets, E_loc, max_rows, W, C, N, K, s);
+  return launch_big<false, kBK, kStages, kBK / 16>(A, offsets, E_loc, max_rows, W, C, N, K, s);
+}
+
+}  // namespace moe

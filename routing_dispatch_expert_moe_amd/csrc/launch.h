@@ -32,6 +32,8 @@ int launch_ffn_up_bf16(const void* x_perm, const int32_t* offsets, int E_loc, in
                        int d, int f, const void* w13, void* h, void* stream);
 int launch_ffn_down_bf16(const void* h, const int32_t* offsets, int E_loc, int64_t max_rows,
                          int d, int f, const void* w2, void* y, void* stream);
+int launch_gemm_big_bf16(bool swiglu, const void* A, const int32_t* offsets, int E_loc,
+                         int64_t max_rows, const void* W, void* C, int N, int K, void* stream);
 int launch_ffn_up_f32(const float* x_perm, const int32_t* offsets, int E_loc, int64_t max_rows,
                       int d, int f, const float* w13, float* h, void* stream);
 int launch_ffn_down_f32(const float* h, const int32_t* offsets, int E_loc, int64_t max_rows,
