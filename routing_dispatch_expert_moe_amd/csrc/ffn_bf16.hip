@@ -29,7 +29,7 @@ namespace moe {
 
 __device__ __forceinline__ float silu_f(float a) { return a * __builtin_amdgcn_rcpf(1.f + __expf(-a)); }
 
-template <int BM, int BN, int BK, int WM, int WN, bool SWIGLU>
+template <int BM, int BN, int BK, int WM, int WN, bool SWIGLU, int CLASS>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets, int E_loc,
     const uint16_t* __restrict__ W, uint16_t* __restrict__ C, int N, int K) {
@@ -48,7 +48,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(
   uint4* Bs = lds + 2 * BM * KC;        // [2][BNW * KC]
   __shared__ int prefix[MOE_MAX_E + 1];
 
-  mtile_prefix<BM>(offsets, E_loc, prefix);
+  mtile_prefix<BM, CLASS>(offsets, E_loc, prefix);
   const int NT = (N + BN - 1) / BN;
   const int total = prefix[E_loc] * NT;
   const int G = gridDim.x;
@@ -69,7 +69,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(
     const int local = tile - prefix[e] * NT;
     const int nt = local / mt_e;
     const int mti = local % mt_e;
-    const int seg0 = offsets[e], seg1 = offsets[e + 1];
+    int first, count;
+    class_rows<CLASS>(offsets[e + 1] - offsets[e], first, count);
+    const int seg0 = offsets[e] + first, seg1 = seg0 + count;
     const int m0 = seg0 + mti * BM;
     const int n0 = nt * BN;
     const uint16_t* We = W + e * wstride;
@@ -111,6 +113,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(
         if constexpr (SWIGLU) accg[i][j] = f32x16_t{};
       }
 
+    const bool wave_active = m0 + wm * TM < seg1;
     uint4 ra[CA], rb[CB];
     auto gload = [&](int kt) {
       const int koff = kt * BK;
@@ -138,6 +141,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(
       const uint4* Bb = Bs + buf * BNW * KC;
 #pragma unroll
       for (int ks = 0; ks < BK / 16; ++ks) {
+        // a wave whose rows all lie past the segment has nothing to compute
+        if (!wave_active) break;
         const int ch = ks * 2 + (lane >> 5);
         bf16x8_t af[FM], bf[FN], gf[SWIGLU ? FN : 1];
 #pragma unroll
@@ -186,12 +191,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(
   }
 }
 
-template <int BM, int BN, int BK, int WM, int WN, bool SWIGLU>
+template <int BM, int BN, int BK, int WM, int WN, bool SWIGLU, int CLASS>
 static int launch_gemm(const void* A, const int32_t* offsets, int E_loc, int64_t max_rows,
                        const void* W, void* C, int N, int K, hipStream_t s) {
   constexpr int BNW = SWIGLU ? 2 * BN : BN;
   const size_t lds = static_cast<size_t>(2) * (BM + BNW) * BK * sizeof(uint16_t);
-  auto kern = gemm_bf16_kernel<BM, BN, BK, WM, WN, SWIGLU>;
+  auto kern = gemm_bf16_kernel<BM, BN, BK, WM, WN, SWIGLU, CLASS>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -201,7 +206,8 @@ static int launch_gemm(const void* A, const int32_t* offsets, int E_loc, int64_t
     attr_set = true;
   }
   const int64_t NT = (N + BN - 1) / BN;
-  const int64_t tiles_ub = (max_rows / BM + E_loc) * NT;
+  int64_t tiles_ub = (max_rows / BM + E_loc) * NT;
+  if (CLASS == ROWS_TAIL) tiles_ub = static_cast<int64_t>(E_loc) * ((kTailMax + BM - 1) / BM) * NT;
   int occ = 0;
   hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(kern),
                                                              WM * WN * 64, lds);
@@ -218,8 +224,11 @@ static int launch_gemm(const void* A, const int32_t* offsets, int E_loc, int64_t
 }
 
 
-// Rows per expert on average decide the tile shape: weight-streaming (few
-// rows) or MFMA-bound (many rows).
+// Rows per expert on average decide the kernels: with few rows per expert the
+// FFN is weight streaming and one small-tile kernel takes every row; otherwise
+// the large-tile kernel takes the full 256-row blocks and a small-tile kernel
+// the short remainders (ROWS_BIG / ROWS_TAIL), both reading the row counts on
+// the device.
 int launch_ffn_up_bf16(const void* x_perm, const int32_t* offsets, int E_loc, int64_t max_rows,
                        int d, int f, const void* w13, void* h, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -229,8 +238,10 @@ int launch_ffn_up_bf16(const void* x_perm, const int32_t* offsets, int E_loc, in
   const bool fits32 = static_cast<double>(max_rows) * d * 2 < 4294967296.0 &&
                       static_cast<double>(2) * f * d * 2 < 4294967296.0;
   if (avg <= 48 || !fits32)
-    return launch_gemm<32, 128, 64, 1, 4, true>(x_perm, offsets, E_loc, max_rows, w13, h, f, d, s);
-  return launch_gemm_big_bf16(true, x_perm, offsets, E_loc, max_rows, w13, h, f, d, stream);
+    return launch_gemm<32, 128, 64, 1, 4, true, ROWS_ALL>(x_perm, offsets, E_loc, max_rows, w13, h, f, d, s);
+  int e = launch_gemm_big_bf16(true, x_perm, offsets, E_loc, max_rows, w13, h, f, d, stream);
+  if (e != 0) return e;
+  return launch_gemm<128, 128, 64, 4, 1, true, ROWS_TAIL>(x_perm, offsets, E_loc, max_rows, w13, h, f, d, s);
 }
 
 int launch_ffn_down_bf16(const void* h, const int32_t* offsets, int E_loc, int64_t max_rows,
@@ -241,8 +252,10 @@ int launch_ffn_down_bf16(const void* h, const int32_t* offsets, int E_loc, int64
   const bool fits32 = static_cast<double>(max_rows) * f * 2 < 4294967296.0 &&
                       static_cast<double>(d) * f * 2 < 4294967296.0;
   if (avg <= 48 || !fits32)
-    return launch_gemm<32, 128, 64, 1, 4, false>(h, offsets, E_loc, max_rows, w2, y, d, f, s);
-  return launch_gemm_big_bf16(false, h, offsets, E_loc, max_rows, w2, y, d, f, stream);
+    return launch_gemm<32, 128, 64, 1, 4, false, ROWS_ALL>(h, offsets, E_loc, max_rows, w2, y, d, f, s);
+  int e = launch_gemm_big_bf16(false, h, offsets, E_loc, max_rows, w2, y, d, f, stream);
+  if (e != 0) return e;
+  return launch_gemm<128, 128, 64, 4, 1, false, ROWS_TAIL>(h, offsets, E_loc, max_rows, w2, y, d, f, s);
 }
 
 }  // namespace moe

@@ -22,6 +22,9 @@
 // the direct loads realise this by choosing which global chunk each lane
 // fetches.
 //
+// Rows: only each expert's ROWS_BIG rows (full 256-row blocks and a last block
+// at least half full); the small-tile kernel takes the rest.
+//
 // Scheduling: persistent grid (one workgroup per CU); tiles in expert order,
 // M-tiles fastest so consecutive tiles share a weight tile; workgroup ids
 // remapped so each XCD (ids dealt round-robin over 8 XCDs) owns contiguous
@@ -64,8 +67,10 @@ __device__ __forceinline__ Tile decode_tile(int t, int NT, const int* prefix, co
   const int mt_e = prefix[r.e + 1] - prefix[r.e];
   const int local = t - prefix[r.e] * NT;
   const int nt = local / mt_e, mti = local % mt_e;
-  r.m0 = segs[r.e] + mti * kBM;
-  r.seg1 = segs[r.e + 1];
+  int first, count;
+  class_rows<ROWS_BIG>(segs[r.e + 1] - segs[r.e], first, count);
+  r.m0 = segs[r.e] + first + mti * kBM;
+  r.seg1 = segs[r.e] + first + count;
   r.n0 = nt * BN;
   // the tile is the same for the whole wave: keep its fields in scalar registers
   r.e = __builtin_amdgcn_readfirstlane(r.e);
@@ -97,7 +102,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big(const uint16_t* __restri
   __shared__ int segs[MOE_MAX_E + 1];
 
   for (int i = threadIdx.x; i <= E_loc; i += blockDim.x) segs[i] = offsets[i];
-  mtile_prefix<kBM>(offsets, E_loc, prefix);  // ends with a barrier
+  mtile_prefix<kBM, ROWS_BIG>(offsets, E_loc, prefix);  // ends with a barrier
   const int NT = (N + BN - 1) / BN;
   const int total = prefix[E_loc] * NT;
   const int G = gridDim.x;

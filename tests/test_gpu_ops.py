@@ -106,6 +106,8 @@ def test_dispatch_flags_invalid_index():
 @pytest.mark.parametrize("dtype,d,f,rows", [
     ("bf16", 64, 64, [1]), ("bf16", 128, 192, [0, 5, 130, 0, 257]), ("bf16", 256, 512, [300, 31, 64]),
     ("bf16", 192, 128, [40] * 8), ("bf16", 128, 128, [3, 2, 7, 0, 1, 11, 4, 5, 6, 9]),
+    # large/small tile split boundaries: 256-row blocks, remainders of 127/128, empty experts
+    ("bf16", 128, 192, [1024, 1152, 1100, 128, 127, 255, 256, 0, 384, 513]),
     ("f32", 128, 256, [17, 0, 111]), ("f32", 32, 48, [5, 70, 1]), ("f32", 12, 20, [3, 64, 65])])
 def test_expert_ffn(dtype, d, f, rows):
     log(f"ffn {dtype} d={d} f={f} rows={rows}")
