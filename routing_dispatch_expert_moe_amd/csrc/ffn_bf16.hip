@@ -224,6 +224,12 @@ static int launch_gemm(const void* A, const int32_t* offsets, int E_loc, int64_t
 }
 
 
+#ifndef MOE_DECODE_SMALL_TILES
+#define MOE_DECODE_SMALL_TILES 1
+#endif
+constexpr bool kDecodeSmallTiles = MOE_DECODE_SMALL_TILES != 0;
+constexpr int64_t kStreamRows = 48;
+
 // Rows per expert on average decide the kernels: with few rows per expert the
 // FFN is weight streaming and one small-tile kernel takes every row; otherwise
 // the large-tile kernel takes the full 256-row blocks and a small-tile kernel
@@ -237,11 +243,16 @@ int launch_ffn_up_bf16(const void* x_perm, const int32_t* offsets, int E_loc, in
   // the large-tile kernel addresses operands with 32-bit byte offsets
   const bool fits32 = static_cast<double>(max_rows) * d * 2 < 4294967296.0 &&
                       static_cast<double>(2) * f * d * 2 < 4294967296.0;
-  if (avg <= 48 || !fits32)
+  if (!fits32)
     return launch_gemm<32, 128, 64, 1, 4, true, ROWS_ALL>(x_perm, offsets, E_loc, max_rows, w13, h, f, d, s);
-  int e = launch_gemm_big_bf16(true, x_perm, offsets, E_loc, max_rows, w13, h, f, d, stream);
+  if (avg <= kStreamRows) {
+    if (kDecodeSmallTiles)
+      return launch_gemm<32, 128, 64, 1, 4, true, ROWS_ALL>(x_perm, offsets, E_loc, max_rows, w13, h, f, d, s);
+    return launch_gemm_pipe_bf16(PipeRows::kAllRows, true, x_perm, offsets, E_loc, max_rows, w13, h, f, d, stream);
+  }
+  int e = launch_gemm_pipe_bf16(PipeRows::kBigTiles, true, x_perm, offsets, E_loc, max_rows, w13, h, f, d, stream);
   if (e != 0) return e;
-  return launch_gemm<128, 128, 64, 4, 1, true, ROWS_TAIL>(x_perm, offsets, E_loc, max_rows, w13, h, f, d, s);
+  return launch_gemm_pipe_bf16(PipeRows::kTailTiles, true, x_perm, offsets, E_loc, max_rows, w13, h, f, d, stream);
 }
 
 int launch_ffn_down_bf16(const void* h, const int32_t* offsets, int E_loc, int64_t max_rows,
@@ -251,11 +262,16 @@ int launch_ffn_down_bf16(const void* h, const int32_t* offsets, int E_loc, int64
   const int64_t avg = max_rows / E_loc;
   const bool fits32 = static_cast<double>(max_rows) * f * 2 < 4294967296.0 &&
                       static_cast<double>(d) * f * 2 < 4294967296.0;
-  if (avg <= 48 || !fits32)
+  if (!fits32)
     return launch_gemm<32, 128, 64, 1, 4, false, ROWS_ALL>(h, offsets, E_loc, max_rows, w2, y, d, f, s);
-  int e = launch_gemm_big_bf16(false, h, offsets, E_loc, max_rows, w2, y, d, f, stream);
+  if (avg <= kStreamRows) {
+    if (kDecodeSmallTiles)
+      return launch_gemm<32, 128, 64, 1, 4, false, ROWS_ALL>(h, offsets, E_loc, max_rows, w2, y, d, f, s);
+    return launch_gemm_pipe_bf16(PipeRows::kAllRows, false, h, offsets, E_loc, max_rows, w2, y, d, f, stream);
+  }
+  int e = launch_gemm_pipe_bf16(PipeRows::kBigTiles, false, h, offsets, E_loc, max_rows, w2, y, d, f, stream);
   if (e != 0) return e;
-  return launch_gemm<128, 128, 64, 4, 1, false, ROWS_TAIL>(h, offsets, E_loc, max_rows, w2, y, d, f, s);
+  return launch_gemm_pipe_bf16(PipeRows::kTailTiles, false, h, offsets, E_loc, max_rows, w2, y, d, f, stream);
 }
 
 }  // namespace moe

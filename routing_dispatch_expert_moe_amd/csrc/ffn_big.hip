@@ -1,29 +1,30 @@
-// Large-tile grouped GEMM for experts with many rows (MFMA-bound), bf16 in,
-// fp32 accumulation, v_mfma_f32_32x32x16_bf16.
+// Pipelined grouped GEMM (bf16 in, fp32 accumulation, v_mfma_f32_32x32x16_bf16)
+// for the expert FFN halves.
 //
 // DWDP page, key optimisations: the first grouped GEMM takes every local
 // expert's rows against its fused [W1 | W3] operand with SwiGLU in the
 // epilogue; the second grouped GEMM applies W2.
 //
-// Tile: 256 activation rows x 256 weight rows (SwiGLU: 128 W1 rows + the
-// matching 128 W3 rows -> 128 h columns).  4 waves split the tile 2 x 2;
-// each wave owns 128 x 128 (4 x 4 MFMA tiles, 256 fp32 accumulators).
+// Tile: BM activation rows x 256 weight rows (SwiGLU: 128 W1 rows + the
+// matching 128 W3 rows -> 128 h columns).  4 waves split the tile 2 x 2; each
+// wave owns (BM / 2) x 128, i.e. BM / 64 x 4 MFMA tiles of 32 x 32.
+//   BM = 256  experts with many rows (MFMA-bound; 256 accumulators per lane);
+//   BM = 128 / 64  experts with few rows, where the weights stream from HBM
+//             and the smaller A tile leaves LDS for a deeper pipeline.
 //
 // Memory pipeline: operands go HBM/L2 -> LDS directly (global_load_lds_dwordx4,
-// no staging registers) in K-steps of 32, through 4 LDS stages of 32 KB, so
-// loads run three steps ahead of the MFMAs.  A step's loads are spread over
-// the MFMAs of the step before; MFMA operands are double buffered in
-// registers (the next 16-deep substep's LDS reads overlap the current
-// substep's MFMAs), and each step's barrier sits under the last substep's
-// MFMAs.  The load stream runs across tile boundaries, so the next tile's
-// operands are in flight during the current tile's epilogue.  Rows are 64
-// bytes (4 chunks of 16 B); chunk c of row r sits at chunk c ^ ((r >> 2) & 3),
-// so each 16-lane phase of a ds_read_b128 touches 16 distinct bank groups;
-// the direct loads realise this by choosing which global chunk each lane
-// fetches.
+// no staging registers) in K-steps of 32 through STAGES LDS buffers, so loads
+// run STAGES - 1 steps ahead of the MFMAs.  A step's loads are spread over the
+// MFMAs of the step before; MFMA operands are double buffered in registers
+// (the next 16-deep substep's LDS reads overlap the current substep's MFMAs),
+// and each step's barrier sits under the last substep's MFMAs.  The load
+// stream runs across tile boundaries, so the next tile's operands are in
+// flight during the current tile's epilogue.  Rows are 64 bytes (4 chunks of
+// 16 B); chunk c of row r sits at chunk c ^ ((r >> 2) & 3), so each 16-lane
+// phase of a ds_read_b128 touches 16 distinct bank groups; the direct loads
+// realise this by choosing which global chunk each lane fetches.
 //
-// Rows: only each expert's ROWS_BIG rows (full 256-row blocks and a last block
-// at least half full); the small-tile kernel takes the rest.
+// Rows: the rows of row class CLASS of each expert (tile_sched.h).
 //
 // Scheduling: persistent grid (one workgroup per CU); tiles in expert order,
 // M-tiles fastest so consecutive tiles share a weight tile; workgroup ids
@@ -37,29 +38,43 @@ namespace moe {
 
 namespace {
 
-constexpr int kBM = 256, kBNW = 256;
-// pipeline step depth along K and LDS stages (loads run kStages - 1 steps ahead)
-constexpr int kBK = 32, kStages = 4;
+constexpr int kBNW = 256;        // weight rows per tile
+constexpr int kBK = 32;          // K depth of one pipeline step
+constexpr int kKC = kBK / 8;     // 16-byte chunks per 64-byte row
+constexpr int kRPI = 64 / kKC;   // rows covered by one 64-lane 16-byte load (16)
+constexpr int kSUB = kBK / 16;   // MFMA K-substeps per step (2)
 
 __device__ __forceinline__ float silu_fast(float a) {
   return a * __builtin_amdgcn_rcpf(1.f + __expf(-a));
 }
 
+// s_waitcnt vmcnt(N) (N < 64) with the other counters left alone
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
-  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-  else if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-  else if constexpr (N == 24) asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
-  else if constexpr (N == 32) asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
-  else static_assert(N == 0, "unsupported vmcnt");
+  static_assert(N >= 0 && N < 64, "vmcnt out of range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// scheduling groups of one substep: MFMA g is preceded by its share of the NDS
+// LDS reads (evenly spread, first one before MFMA 0) and followed by its share
+// of the NVM global loads (evenly spread, none after the last MFMA)
+template <int G, int NMF, int NDS, int NVM>
+__device__ __forceinline__ void interleave() {
+  if constexpr (G < NMF) {
+    constexpr int nds = ((G + 1) * NDS + NMF - 1) / NMF - (G * NDS + NMF - 1) / NMF;
+    constexpr int nvm = ((G + 2) * NVM) / NMF - ((G + 1) * NVM) / NMF;
+    if constexpr (nds > 0) __builtin_amdgcn_sched_group_barrier(0x100, nds, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (nvm > 0) __builtin_amdgcn_sched_group_barrier(0x020, nvm, 0);
+    interleave<G + 1, NMF, NDS, NVM>();
+  }
 }
 
 struct Tile {
   int e, m0, seg1, n0;
 };
 
-template <int BN>
+template <int BM, int BN, int CLASS>
 __device__ __forceinline__ Tile decode_tile(int t, int NT, const int* prefix, const int* segs,
                                             int E_loc) {
   Tile r;
@@ -68,8 +83,8 @@ __device__ __forceinline__ Tile decode_tile(int t, int NT, const int* prefix, co
   const int local = t - prefix[r.e] * NT;
   const int nt = local / mt_e, mti = local % mt_e;
   int first, count;
-  class_rows<ROWS_BIG>(segs[r.e + 1] - segs[r.e], first, count);
-  r.m0 = segs[r.e] + first + mti * kBM;
+  class_rows<CLASS>(segs[r.e + 1] - segs[r.e], first, count);
+  r.m0 = segs[r.e] + first + mti * BM;
   r.seg1 = segs[r.e] + first + count;
   r.n0 = nt * BN;
   // the tile is the same for the whole wave: keep its fields in scalar registers
@@ -82,27 +97,25 @@ __device__ __forceinline__ Tile decode_tile(int t, int NT, const int* prefix, co
 
 }  // namespace
 
-// BK: K depth of one pipeline step (32 or 64); STAGES: LDS buffers (loads run
-// STAGES - 1 steps ahead of the MFMAs).
-template <bool SWIGLU, int BK, int STAGES, int VS>
-__global__ __launch_bounds__(256, 1) void gemm_bf16_big(const uint16_t* __restrict__ A,
-                                                        const int32_t* __restrict__ offsets,
-                                                        int E_loc,
-                                                        const uint16_t* __restrict__ W,
-                                                        uint16_t* __restrict__ C, int N, int K) {
-  constexpr int BN = SWIGLU ? 128 : 256;  // output columns per tile
-  constexpr int KC = BK / 8;              // 16-byte chunks per row
-  constexpr int RPI = 64 / KC;            // rows covered by one 64-lane 16-byte load
-  constexpr int LPM = kBM / RPI / 4;      // loads per wave per matrix per step
-  constexpr int STAGE_U4 = (kBM + kBNW) * KC;
-  constexpr int SUB = BK / 16;            // MFMA K-substeps per step
-  static_assert(VS == SUB && (2 * LPM / SUB) % 4 == 0, "loads must split evenly over the substeps");
+template <bool SWIGLU, int BM, int STAGES, int CLASS>
+__global__ __launch_bounds__(256, 1) void gemm_bf16_pipe(const uint16_t* __restrict__ A,
+                                                         const int32_t* __restrict__ offsets,
+                                                         int E_loc,
+                                                         const uint16_t* __restrict__ W,
+                                                         uint16_t* __restrict__ C, int N, int K) {
+  constexpr int BN = SWIGLU ? 128 : 256;   // output columns per tile
+  constexpr int FM = BM / 64;              // 32-row MFMA blocks per wave
+  constexpr int LA = BM / kRPI / 4;        // A loads per wave per step
+  constexpr int LB = kBNW / kRPI / 4;      // B loads per wave per step (4)
+  constexpr int LSTEP = LA + LB;
+  constexpr int STAGE_U4 = (BM + kBNW) * kKC;
+  static_assert(FM >= 1 && LB % kSUB == 0, "unsupported tile");
   extern __shared__ uint4 lds[];
   __shared__ int prefix[MOE_MAX_E + 1];
   __shared__ int segs[MOE_MAX_E + 1];
 
   for (int i = threadIdx.x; i <= E_loc; i += blockDim.x) segs[i] = offsets[i];
-  mtile_prefix<kBM, ROWS_BIG>(offsets, E_loc, prefix);  // ends with a barrier
+  mtile_prefix<BM, CLASS>(offsets, E_loc, prefix);  // ends with a barrier
   const int NT = (N + BN - 1) / BN;
   const int total = prefix[E_loc] * NT;
   const int G = gridDim.x;
@@ -110,7 +123,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big(const uint16_t* __restri
   if ((G & 7) == 0) vb = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
   if (vb >= total) return;
   const int ntiles = (total - vb + G - 1) / G;
-  const int KT = K / BK;
+  const int KT = K / kBK;
   const int S = ntiles * KT;  // this workgroup's K-steps over all its tiles
 
   const int tid = threadIdx.x;
@@ -119,25 +132,28 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big(const uint16_t* __restri
   const size_t wstride = static_cast<size_t>(SWIGLU ? 2 * N : N) * K;
   // LDS swizzle: chunk c of row r is stored at c ^ swz(r); swz spreads the 16
   // rows read by one 16-lane ds_read_b128 phase over all bank groups
-  auto swz = [](int r) { return KC == 8 ? ((r >> 1) & 7) : ((r >> 2) & 3); };
-  // the chunk this lane fetches in each row group it loads (row = g * RPI + lane / KC;
-  // g = i * 4 + wave, so swz depends only on the lane and the wave)
-  const int lrow0 = (lane / KC) + RPI * wave;
-  const int lkc = (lane % KC) ^ swz(lrow0);
+  auto swz = [](int r) { return (r >> 2) & 3; };
+  // the chunk this lane fetches in every 16-row group it loads (row = g * 16 +
+  // lane / 4, so swz(row) depends only on the lane)
+  const int lkc = (lane % kKC) ^ swz(lane / kKC);
   const char* Ab = reinterpret_cast<const char*>(A);
 
   // ---- issue side: the tile whose operands are being fetched
   int it_tile = -1;
   const char* iWb = nullptr;
-  uint32_t aoff[LPM], boff[LPM];
+  uint32_t aoff[LA], boff[LB];
   auto set_issue_tile = [&](int j) {
-    const Tile t = decode_tile<BN>(vb + j * G, NT, prefix, segs, E_loc);
+    const Tile t = decode_tile<BM, BN, CLASS>(vb + j * G, NT, prefix, segs, E_loc);
     iWb = reinterpret_cast<const char*>(W + t.e * wstride);
 #pragma unroll
-    for (int i = 0; i < LPM; ++i) {
-      const int rt = (i * 4 + wave) * RPI + lane / KC;  // row within the tile
+    for (int i = 0; i < LA; ++i) {
+      const int rt = (i * 4 + wave) * kRPI + lane / kKC;  // row within the tile
       const int arow = min(t.m0 + rt, t.seg1 - 1);
       aoff[i] = (static_cast<uint32_t>(arow) * K + lkc * 8) * 2u;
+    }
+#pragma unroll
+    for (int i = 0; i < LB; ++i) {
+      const int rt = (i * 4 + wave) * kRPI + lane / kKC;
       int wrow;
       if (SWIGLU) wrow = (rt >> 7) * N + min(t.n0 + (rt & 127), N - 1);
       else wrow = min(t.n0 + rt, N - 1);
@@ -145,20 +161,20 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big(const uint16_t* __restri
     }
     it_tile = j;
   };
-  // loads [p * LPM / VS, (p + 1) * LPM / VS) of A and of B into buffer buf
+  // part p (of kSUB) of a step's loads into buffer buf
   auto issue_part = [&](int p, int buf, uint32_t koff) {
     uint4* As = lds + buf * STAGE_U4;
-    uint4* Bs = As + kBM * KC;
+    uint4* Bs = As + BM * kKC;
 #pragma unroll
-    for (int i = p * (LPM / VS); i < (p + 1) * (LPM / VS); ++i) {
-      const int g = i * 4 + wave;
+    for (int i = p * LA / kSUB; i < (p + 1) * LA / kSUB; ++i)
       __builtin_amdgcn_global_load_lds(
           (const __attribute__((address_space(1))) void*)(Ab + (aoff[i] + koff)),
-          (__attribute__((address_space(3))) void*)(As + g * 64), 16, 0, 0);
+          (__attribute__((address_space(3))) void*)(As + (i * 4 + wave) * 64), 16, 0, 0);
+#pragma unroll
+    for (int i = p * LB / kSUB; i < (p + 1) * LB / kSUB; ++i)
       __builtin_amdgcn_global_load_lds(
           (const __attribute__((address_space(1))) void*)(iWb + (boff[i] + koff)),
-          (__attribute__((address_space(3))) void*)(Bs + g * 64), 16, 0, 0);
-    }
+          (__attribute__((address_space(3))) void*)(Bs + (i * 4 + wave) * 64), 16, 0, 0);
   };
   // byte offset along K of step p's operands, switching the issue tile when p
   // starts a new one; steps past the end re-fetch the last step (valid
@@ -167,36 +183,37 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big(const uint16_t* __restri
     if (p >= S) p = S - 1;
     const int j = p / KT, kt = p - j * KT;
     if (j != it_tile) set_issue_tile(j);
-    return static_cast<uint32_t>(kt) * BK * 2u;
+    return static_cast<uint32_t>(kt) * kBK * 2u;
   };
 
   // LDS fragments of substep ks of the step held in buffer `buf`
-  bf16x8_t fa[2][4], fb[2][4];
+  bf16x8_t fa[2][FM], fb[2][4];
   auto load_frags = [&](int buf, int ks, int slot) {
     const uint4* As = lds + buf * STAGE_U4;
-    const uint4* Bs = As + kBM * KC;
+    const uint4* Bs = As + BM * kKC;
     const int ch = ks * 2 + (lane >> 5);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = wm * 128 + i * 32 + (lane & 31);
-      fa[slot][i] = __builtin_bit_cast(bf16x8_t, As[r * KC + (ch ^ swz(r))]);
+      if (i < FM) {
+        const int r = wm * (BM / 2) + i * 32 + (lane & 31);
+        fa[slot][i] = __builtin_bit_cast(bf16x8_t, As[r * kKC + (ch ^ swz(r))]);
+      }
       const int q = SWIGLU ? ((i >> 1) * 128 + wn * 64 + (i & 1) * 32 + (lane & 31))
                            : (wn * 128 + i * 32 + (lane & 31));
-      fb[slot][i] = __builtin_bit_cast(bf16x8_t, Bs[q * KC + (ch ^ swz(q))]);
+      fb[slot][i] = __builtin_bit_cast(bf16x8_t, Bs[q * kKC + (ch ^ swz(q))]);
     }
   };
   // Step p becomes readable: this wave's loads of step p are done once at most
   // the (STAGES - 2) younger steps' loads are outstanding (loads complete in
   // order) and its own LDS reads of the step before are done; the barrier then
-  // publishes every wave's step-p data and frees the buffer of step p - 1,
-  // which immediately receives the loads of step p + STAGES - 1.
-  // The loads of step p + STAGES - 1 go out in SUB parts: part 0 right after
-  // this barrier, parts 1 .. SUB - 1 during the first substeps of step p
+  // publishes every wave's step-p data and frees the buffer of step p - 1.
+  // The loads of step p + STAGES - 1 go into that buffer in kSUB parts: part 0
+  // right after the barrier, the others during the first substeps of step p
   // (pk / pb hold the pending step's K offset and buffer meanwhile).
   uint32_t pk = 0u;
   int pb = 0;
   auto sync_and_issue = [&](int p) {
-    wait_vmcnt<(STAGES - 2) * 2 * LPM>();
+    wait_vmcnt<(STAGES - 2) * LSTEP>();
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     pk = issue_koff(p + STAGES - 1);
     pb = (p + STAGES - 1) % STAGES;
@@ -207,16 +224,20 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big(const uint16_t* __restri
   for (int p = 0; p < STAGES - 1; ++p) {
     const uint32_t ko = issue_koff(p);
 #pragma unroll
-    for (int q = 0; q < VS; ++q) issue_part(q, p % STAGES, ko);
+    for (int q = 0; q < kSUB; ++q) issue_part(q, p % STAGES, ko);
   }
   sync_and_issue(0);
 
+  // instruction interleave of one substep: FM * 4 MFMAs with the FM + 4 LDS
+  // reads of the next substep and about LSTEP / kSUB global loads between them
+  constexpr int NMF = FM * 4, NDS = FM + 4, NVM = (LSTEP + kSUB - 1) / kSUB;
+
   for (int j = 0; j < ntiles; ++j) {
-    const Tile ct = decode_tile<BN>(vb + j * G, NT, prefix, segs, E_loc);
-    const int valid = min(kBM, ct.seg1 - ct.m0);
-    f32x16_t acc[4][4];
+    const Tile ct = decode_tile<BM, BN, CLASS>(vb + j * G, NT, prefix, segs, E_loc);
+    const int valid = min(BM, ct.seg1 - ct.m0);
+    f32x16_t acc[FM][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int q = 0; q < 4; ++q) acc[i][q] = f32x16_t{};
     load_frags((j * KT) % STAGES, 0, 0);
@@ -226,10 +247,9 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big(const uint16_t* __restri
       const int s = j * KT + kt;
       const int buf = s % STAGES;
 #pragma unroll
-      for (int ks = 0; ks < SUB; ++ks) {
-        const int cur = ks & 1;  // SUB is even: substep 0 of every step uses slot 0
-        const bool last = ks + 1 == SUB;
-        if (!last) {
+      for (int ks = 0; ks < kSUB; ++ks) {
+        const int cur = ks & 1;  // kSUB is even: substep 0 of every step uses slot 0
+        if (ks + 1 < kSUB) {
           load_frags(buf, ks + 1, cur ^ 1);
           issue_part(ks + 1, pb, pk);
         } else if (s + 1 < S) {
@@ -239,18 +259,11 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big(const uint16_t* __restri
           if (kt + 1 < KT) load_frags((s + 1) % STAGES, 0, cur ^ 1);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < FM; ++i)
 #pragma unroll
           for (int q = 0; q < 4; ++q)
             acc[i][q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][q], acc[i][q], 0, 0, 0);
-        // 8 LDS reads and the 2 * LPM / SUB global loads spread between 16 MFMAs
-#pragma unroll
-        for (int g = 0; g < 8; ++g) {
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          if (g % 2 == 1) __builtin_amdgcn_sched_group_barrier(0x020, 2 * LPM / SUB / 4, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        }
+        interleave<0, NMF, NDS, NVM>();
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -258,15 +271,15 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big(const uint16_t* __restri
     // epilogue (registers -> global); D[m][n] of a 32x32 MFMA tile is in lane
     // n + 32 * ((m / 4) % 2), register 4 * (m / 8) + m % 4
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (wm * 128 + i * 32 >= valid) continue;
+    for (int i = 0; i < FM; ++i) {
+      if (wm * (BM / 2) + i * 32 >= valid) continue;
 #pragma unroll
       for (int q = 0; q < (SWIGLU ? 2 : 4); ++q) {
         const int col = ct.n0 + (SWIGLU ? wn * 64 : wn * 128) + q * 32 + (lane & 31);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int m = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          const int row = ct.m0 + wm * 128 + i * 32 + m;
+          const int row = ct.m0 + wm * (BM / 2) + i * 32 + m;
           float v = acc[i][q][r];
           if constexpr (SWIGLU) v = silu_fast(v) * acc[i][q + 2][r];
           if (row < ct.seg1 && col < N) C[static_cast<size_t>(row) * N + col] = f32_to_bf16(v);
@@ -277,11 +290,15 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big(const uint16_t* __restri
   wait_vmcnt<0>();  // redundant tail loads must land before the LDS is released
 }
 
-template <bool SWIGLU, int BK, int STAGES, int VS>
-static int launch_big(const void* A, const int32_t* offsets, int E_loc, int64_t max_rows,
-                      const void* W, void* C, int N, int K, hipStream_t s) {
-  const size_t lds = static_cast<size_t>(STAGES) * (kBM + kBNW) * BK * sizeof(uint16_t);
-  auto kern = gemm_bf16_big<SWIGLU, BK, STAGES, VS>;
+namespace {
+
+template <bool SWIGLU, int BM, int STAGES, int CLASS>
+int launch_pipe(const void* A, const int32_t* offsets, int E_loc, int64_t max_rows, const void* W,
+                void* C, int N, int K, hipStream_t s) {
+  const size_t lds = static_cast<size_t>(STAGES) * (BM + kBNW) * kBK * sizeof(uint16_t);
+  static_assert(static_cast<size_t>(STAGES) * (BM + kBNW) * kBK * 2 + 2 * (MOE_MAX_E + 1) * 4 <=
+                    160 * 1024, "LDS budget");
+  auto kern = gemm_bf16_pipe<SWIGLU, BM, STAGES, CLASS>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -292,7 +309,8 @@ static int launch_big(const void* A, const int32_t* offsets, int E_loc, int64_t 
   }
   const int BN = SWIGLU ? 128 : 256;
   const int64_t NT = (N + BN - 1) / BN;
-  const int64_t tiles_ub = (max_rows / kBM + E_loc) * NT;
+  int64_t tiles_ub = (max_rows / BM + E_loc) * NT;
+  if (CLASS == ROWS_TAIL) tiles_ub = static_cast<int64_t>(E_loc) * ((kTailMax + BM - 1) / BM) * NT;
   int64_t grid = device_cu_count();
   if (grid > tiles_ub) grid = tiles_ub;
   if (grid >= 8) grid &= ~static_cast<int64_t>(7);
@@ -303,12 +321,35 @@ static int launch_big(const void* A, const int32_t* offsets, int E_loc, int64_t 
   return static_cast<int>(hipGetLastError());
 }
 
-int launch_gemm_big_bf16(bool swiglu, const void* A, const int32_t* offsets, int E_loc,
-                         int64_t max_rows, const void* W, void* C, int N, int K, void* stream) {
+#ifndef MOE_SMALL_BM
+#define MOE_SMALL_BM 128
+#endif
+#ifndef MOE_SMALL_STAGES
+#define MOE_SMALL_STAGES 6
+#endif
+
+template <bool SWIGLU>
+int launch_kind(PipeRows rows, const void* A, const int32_t* offsets, int E_loc, int64_t max_rows,
+                const void* W, void* C, int N, int K, hipStream_t s) {
+  constexpr int SB = MOE_SMALL_BM, SS = MOE_SMALL_STAGES;
+  switch (rows) {
+    case PipeRows::kBigTiles:
+      return launch_pipe<SWIGLU, 256, 4, ROWS_BIG>(A, offsets, E_loc, max_rows, W, C, N, K, s);
+    case PipeRows::kTailTiles:
+      return launch_pipe<SWIGLU, SB, SS, ROWS_TAIL>(A, offsets, E_loc, max_rows, W, C, N, K, s);
+    default:
+      return launch_pipe<SWIGLU, SB, SS, ROWS_ALL>(A, offsets, E_loc, max_rows, W, C, N, K, s);
+  }
+}
+
+}  // namespace
+
+int launch_gemm_pipe_bf16(PipeRows rows, bool swiglu, const void* A, const int32_t* offsets,
+                          int E_loc, int64_t max_rows, const void* W, void* C, int N, int K,
+                          void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (swiglu)
-    return launch_big<true, kBK, kStages, kBK / 16>(A, offsets, E_loc, max_rows, W, C, N, K, s);
-  return launch_big<false, kBK, kStages, kBK / 16>(A, offsets, E_loc, max_rows, W, C, N, K, s);
+  if (swiglu) return launch_kind<true>(rows, A, offsets, E_loc, max_rows, W, C, N, K, s);
+  return launch_kind<false>(rows, A, offsets, E_loc, max_rows, W, C, N, K, s);
 }
 
 }  // namespace moe

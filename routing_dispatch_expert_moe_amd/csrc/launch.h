@@ -32,8 +32,13 @@ int launch_ffn_up_bf16(const void* x_perm, const int32_t* offsets, int E_loc, in
                        int d, int f, const void* w13, void* h, void* stream);
 int launch_ffn_down_bf16(const void* h, const int32_t* offsets, int E_loc, int64_t max_rows,
                          int d, int f, const void* w2, void* y, void* stream);
-int launch_gemm_big_bf16(bool swiglu, const void* A, const int32_t* offsets, int E_loc,
-                         int64_t max_rows, const void* W, void* C, int N, int K, void* stream);
+// Pipelined direct-to-LDS grouped GEMM over one row class: 256-row tiles over
+// each expert's full blocks, smaller tiles over the short remainders, or
+// smaller tiles over every row.
+enum class PipeRows { kBigTiles, kTailTiles, kAllRows };
+int launch_gemm_pipe_bf16(PipeRows rows, bool swiglu, const void* A, const int32_t* offsets,
+                          int E_loc, int64_t max_rows, const void* W, void* C, int N, int K,
+                          void* stream);
 int launch_ffn_up_f32(const float* x_perm, const int32_t* offsets, int E_loc, int64_t max_rows,
                       int d, int f, const float* w13, float* h, void* stream);
 int launch_ffn_down_f32(const float* h, const int32_t* offsets, int E_loc, int64_t max_rows,
