@@ -45,8 +45,120 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-tokens", type=int, default=256)
     p.add_argument("--traffic", default=None,
-                   help="JSON file with counter-derived HBM bytes per launch of the dominant kernel")
+                   help="JSON file with counter-derived HBM bytes per launch of the dominant "
+                        "kernel (default: profiles/traffic_<workload>.json if present)")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain 1 GiB device copy (the counter calibration kernel)")
+    p.add_argument("--traffic-from", default=None, metavar="DIR",
+                   help="turn rocprofv3 --pmc databases under DIR/{fetch,write,copy_fetch,"
+                        "copy_write} into profiles/traffic_<workload>.json and exit")
     return p.parse_args()
+
+
+# ---- HBM traffic of the dominant kernel from hardware counters -------------
+#
+# FETCH_SIZE and WRITE_SIZE (KiB per dispatch, summed over the channels) are
+# taken in two rocprofv3 --pmc passes over a short bench run, and in two passes
+# over a plain device copy of known size; the copy's counted bytes over its
+# true bytes is the scale applied to the kernel's counts.  The result records a
+# hash of the kernel's sources: once they change, the stored traffic is stale
+# and the bench reports null.
+
+DOMINANT = "moe_ffn_up"                         # one GEMM1 + SwiGLU pass over all local rows
+DOMINANT_KERNELS = ("gemm_bf16_pipe<true",)     # the kernels that pass launches (demangled prefix)
+DOMINANT_SOURCES = ("routing_dispatch_expert_moe_amd/csrc/ffn_big.hip",
+                    "routing_dispatch_expert_moe_amd/csrc/ffn_bf16.hip",
+                    "routing_dispatch_expert_moe_amd/csrc/tile_sched.h",
+                    "routing_dispatch_expert_moe_amd/csrc/common.h")
+COPY_BYTES = 1 << 30
+
+
+def sources_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in DOMINANT_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def copy_calibration():
+    import torch
+    src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "launches": 3}))
+
+
+def _pmc_per_dispatch(path, counter):
+    """{dispatch_id: (kernel_name, value summed over dimensions)} from rocprofv3 databases."""
+    import glob
+    import sqlite3
+    out = {}
+    files = glob.glob(os.path.join(path, "**", "*.db"), recursive=True)
+    if not files:
+        raise SystemExit(f"no rocprofv3 database under {path}")
+    for f in files:
+        con = sqlite3.connect(f)
+        for did, kname, cname, val in con.execute(
+                "select dispatch_id, kernel_name, counter_name, value from counters_collection"):
+            if cname != counter:
+                continue
+            k = (f, did)
+            name, v = out.get(k, (kname, 0.0))
+            out[k] = (name, v + float(val))
+    return out
+
+
+def traffic_from(args):
+    d = args.traffic_from
+    res = {}
+    for ctr, sub in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
+        copy = [v for n, v in _pmc_per_dispatch(os.path.join(d, "copy_" + sub), ctr).values()
+                if "copy" in n.lower() or "elementwise" in n.lower()]
+        kern = [v for n, v in _pmc_per_dispatch(os.path.join(d, sub), ctr).values()
+                if any(p in n for p in DOMINANT_KERNELS)]
+        if not copy or not kern:
+            raise SystemExit(f"{ctr}: found {len(copy)} copy and {len(kern)} kernel dispatches")
+        copy_kib = float(np.median(copy))
+        scale = (COPY_BYTES / 1024.0) / copy_kib   # true KiB per counted KiB
+        res[ctr] = {"copy_counted_kib": copy_kib, "scale": scale,
+                    "kernel_dispatches": len(kern),
+                    "kernel_counted_kib_per_dispatch": float(np.mean(kern))}
+    # the dominant pass launches len(DOMINANT_KERNELS)-many kernels per call at most;
+    # bytes per call = sum over its kernels of their mean counted KiB, scaled
+    per_call = {}
+    for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+        groups = {}
+        sub = "fetch" if ctr == "FETCH_SIZE" else "write"
+        for n, v in _pmc_per_dispatch(os.path.join(d, sub), ctr).values():
+            if any(p in n for p in DOMINANT_KERNELS):
+                groups.setdefault(n.split("(")[0], []).append(v)
+        per_call[ctr] = sum(float(np.mean(v)) for v in groups.values()) * 1024.0 * res[ctr]["scale"]
+        res[ctr]["kernels"] = {k: float(np.mean(v)) for k, v in groups.items()}
+    out = {DOMINANT: {"fetch_bytes": per_call["FETCH_SIZE"], "write_bytes": per_call["WRITE_SIZE"],
+                      "bytes": per_call["FETCH_SIZE"] + per_call["WRITE_SIZE"]},
+           "workload": args.workload, "sources_sha256_16": sources_hash(), "counters": res}
+    path = args.traffic or os.path.join(ROOT, "profiles", f"traffic_{args.workload}.json")
+    with open(path, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out[DOMINANT]))
+
+
+def load_traffic(args):
+    path = args.traffic or os.path.join(ROOT, "profiles", f"traffic_{args.workload}.json")
+    if not os.path.exists(path):
+        return None, "no counter file"
+    with open(path) as fh:
+        t = json.load(fh)
+    if t.get("workload") != args.workload:
+        return None, "counter file is for another workload"
+    if t.get("sources_sha256_16") != sources_hash():
+        return None, "kernel sources changed since the counters were taken"
+    return t[DOMINANT]["bytes"], "rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by a 1 GiB copy"
 
 
 def log(msg):
@@ -75,7 +187,16 @@ def work_model(wl, n, touched, T_read):
 
 
 def cpu_baseline(wl, host_w, n_tok):
-    """The CPU oracle (float64) on the first n_tok tokens of the workload."""
+    """The CPU oracle (float64) on the first n_tok tokens of the workload, grown once
+    so that the timed sample takes roughly 10-30 s."""
+    rate, dt = _cpu_oracle(wl, host_w, n_tok)
+    if dt < 8.0 and n_tok < wl.T:
+        n_tok = min(wl.T, int(n_tok * 15.0 / max(dt, 1e-3)))
+        rate, dt = _cpu_oracle(wl, host_w, n_tok)
+    return rate, dt, n_tok
+
+
+def _cpu_oracle(wl, host_w, n_tok):
     from oracle import moe_oracle as O
     x = wl.x[:n_tok]
     t0 = time.perf_counter()
@@ -95,6 +216,12 @@ def cpu_baseline(wl, host_w, n_tok):
 
 def main():
     args = parse()
+    if args.traffic_from:
+        traffic_from(args)
+        return
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; "
                                    f"--gpus {args.gpus} is not supported (the path is single-GPU)"}))
@@ -177,6 +304,28 @@ def main():
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
 
+    # the same layer as one fused persistent launch (router logits stay a separate call)
+    fev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+
+    def fused_step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        lg = layer.router(x, wg) if wg is not None else logits
+        layer.forward_fused(x, lg)
+        if ev is not None:
+            ev[1].record()
+
+    for _ in range(args.warmup):
+        fused_step()
+    torch.cuda.synchronize()
+    for s in range(args.steps):
+        fused_step(fev[s])
+    torch.cuda.synchronize()
+    if M.moe_check_error(layer.ws) != 0:
+        raise RuntimeError("device error in the fused layer")
+    fused_ms = float(np.median([e[0].elapsed_time(e[1]) for e in fev]))
+    unfused_ms = float(np.median([events[s][0].elapsed_time(events[s][6]) for s in range(args.steps)]))
+
     per = {}
     model = work_model(wl, n, touched, T_read)
     for i, name in enumerate(STEPS):
@@ -194,22 +343,23 @@ def main():
     dom_ms = per[dom]["ms"]
     dom_fl = model[dom][0]
     achieved = dom_fl / (dom_ms * 1e-3) / 1e12
-    traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        with open(args.traffic) as fh:
-            traffic = json.load(fh).get(dom)
-    roofline = {"bound": "mfma", "kernel": "gemm_bf16_kernel<SwiGLU> (moe_ffn_up)",
+    traffic, traffic_note = load_traffic(args)
+    roofline = {"bound": "mfma", "kernel": f"{DOMINANT}: gemm_bf16_pipe<SwiGLU> over each "
+                                           "expert's 256-row blocks + its remainder tiles",
                 "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                "algorithmic_flops_per_launch": dom_fl, "avg_launch_ms": dom_ms}
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": round(traffic) if traffic is not None else None,
+                "traffic_note": traffic_note,
+                "algorithmic_flops_per_launch": dom_fl,
+                "algorithmic_bytes_per_launch": model[dom][1], "avg_launch_ms": dom_ms}
 
     cpu = None
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle on {args.cpu_sample_tokens} tokens")
-        rate, dt = cpu_baseline(wl, host_w, args.cpu_sample_tokens)
+        rate, dt, n_tok = cpu_baseline(wl, host_w, args.cpu_sample_tokens)
         cpu = {"value": round(rate, 2), "unit": "tokens/s", "cores": _CORES, "kind": "oracle",
-               "sample": f"first {args.cpu_sample_tokens} of {wl.T} tokens of {wl.name}, whole "
-                         f"layer in float64 (router..combine), {dt:.1f} s"}
+               "sample": f"first {n_tok} of {wl.T} tokens of {wl.name} (capacity rule applied "
+                         f"to the sample), whole layer in float64 (router..combine), {dt:.1f} s"}
 
     line = {
         "metric": METRIC, "value": round(wl.T / (ms_step * 1e-3), 1), "unit": "tokens/s",
@@ -222,6 +372,10 @@ def main():
         "layer_tflops": round(tflops, 2), "layer_mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
         "layer_hbm_gbs": round(gbs, 1), "layer_hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
         "per_step": per, "roofline": roofline, "cpu_baseline": cpu,
+        "fused": {"entry": "moe_forward_fused", "ms_per_step_median": round(fused_ms, 4),
+                  "tokens_per_s": round(wl.T / (fused_ms * 1e-3), 1),
+                  "unfused_ms_per_step_median": round(unfused_ms, 4),
+                  "speedup_vs_unfused": round(unfused_ms / fused_ms, 3)},
     }
     print(json.dumps(line), flush=True)
 

@@ -5,7 +5,8 @@
  *
  *   moe_router_logits -> moe_route -> moe_dispatch -> moe_expert_ffn -> moe_combine
  *
- * plus moe_pack_weights (one-time weight re-layout) and moe_check_error.
+ * plus moe_pack_weights (one-time weight re-layout) and moe_check_error, and
+ * moe_forward_fused: route -> dispatch -> expert FFN -> combine in one launch.
  *
  * Sources of the operations (cited by page title and section):
  *   - MoE sparse-activation page ("大模型MoE稀疏激活原理与硬件适配实战"):
@@ -182,9 +183,37 @@ moe_status moe_combine(const void* y_perm, const int32_t* pair_pos, const float*
                        int k, int d, moe_dtype dtype, void* y, void* stream);
 
 /* Waits for `stream`, then returns MOE_ERR_INVALID_TOPK if a kernel since the
- * last check saw an invalid expert index (and clears the flag), MOE_ERR_HIP
- * if the stream reported an error, else MOE_OK. */
+ * last check saw an invalid expert index, MOE_ERR_HIP if the stream reported
+ * an error or a moe_forward_fused barrier timed out, else MOE_OK.  Clears the
+ * device flags it reports (and re-arms the fused barrier after a time-out). */
 moe_status moe_check_error(void* ws, void* stream);
+
+/* The whole layer -- moe_route, moe_dispatch, moe_expert_ffn, moe_combine --
+ * as ONE persistent cooperative launch (MegaMoE comparison page, core
+ * differences §1 and summary: one fused kernel for the MoE layer instead of a
+ * chain of kernels; sparse-activation page §4.2 layer 1: router, top-k and
+ * expert compute fused).  Every argument means what it means in those four
+ * calls, and every output (topk_idx, topk_w, counts, offsets, sorted_pair,
+ * pair_pos, n_kept, h, y_perm, y) is written with the same bits the four
+ * calls produce.  No permuted copy of x is made: the first GEMM reads each row
+ * of x in place through sorted_pair (DWDP page, key optimisations: the row
+ * gather fused into the grouped GEMM), so there is no x_perm argument.
+ * logits: [T][E] fp32 (moe_router_logits stays a separate call).  d, f and
+ * the pointers obey the union of the four calls' rules; bf16 additionally
+ * needs max(max_rows, T) * max(d, f) * 2 and 4 * f * d below 2^32 (else
+ * MOE_ERR_UNSUPPORTED).  One workgroup per CU at most; phases are
+ * separated by device-wide barriers whose words live in the workspace header
+ * (zero-filled once, as for every call), so two fused calls that share a
+ * workspace must not run concurrently.  A barrier that does not complete
+ * within seconds sets the device error word (see moe_check_error) instead of
+ * hanging the GPU. */
+moe_status moe_forward_fused(const float* logits, const void* x, int T, int E, int k, int gate,
+                             int capacity, int e_begin, int e_end, int d, int f, moe_dtype dtype,
+                             const void* w13_packed, const void* w2_packed, int32_t* topk_idx,
+                             float* topk_w, int32_t* counts, int32_t* offsets,
+                             int32_t* sorted_pair, int32_t* pair_pos, int32_t* n_kept,
+                             void* h, void* y_perm, void* y, void* ws, size_t ws_bytes,
+                             void* stream);
 
 #ifdef __cplusplus
 }

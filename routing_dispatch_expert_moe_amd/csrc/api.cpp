@@ -75,7 +75,9 @@ int check_error(void* ws, void* stream, int* device_flags) {
   e = hipMemcpy(&flags, ws, sizeof(int), hipMemcpyDeviceToHost);
   if (e != hipSuccess) return static_cast<int>(e);
   if (flags != 0) {
-    e = hipMemset(ws, 0, sizeof(int));
+    // clear the error word; after a barrier time-out also re-arm the fused
+    // layer's barrier words (the whole header)
+    e = hipMemset(ws, 0, (flags & (1 << MOE_ERR_HIP)) ? kWsHeader : sizeof(int));
     if (e != hipSuccess) return static_cast<int>(e);
   }
   *device_flags = flags;
@@ -253,8 +255,77 @@ moe_status moe_check_error(void* ws, void* stream) {
   int e = moe::check_error(ws, stream, &flags);
   if (e != 0) return hip_status(e);
   if (flags & (1 << MOE_ERR_INVALID_TOPK)) return MOE_ERR_INVALID_TOPK;
+  if (flags & (1 << MOE_ERR_HIP)) return MOE_ERR_HIP;
   if (flags != 0) return MOE_ERR_INVALID_ARG;
   return MOE_OK;
+}
+
+moe_status moe_forward_fused(const float* logits, const void* x, int T, int E, int k, int gate,
+                             int capacity, int e_begin, int e_end, int d, int f, moe_dtype dtype,
+                             const void* w13_packed, const void* w2_packed, int32_t* topk_idx,
+                             float* topk_w, int32_t* counts, int32_t* offsets,
+                             int32_t* sorted_pair, int32_t* pair_pos, int32_t* n_kept,
+                             void* h, void* y_perm, void* y, void* ws, size_t ws_bytes,
+                             void* stream) {
+  if (T < 0) return MOE_ERR_INVALID_ARG;
+  moe_status st = check_topk(E, k);
+  if (st != MOE_OK) return st;
+  if (gate != MOE_GATE_SOFTMAX_TOPK_RENORM && gate != MOE_GATE_SIGMOID_TOPK_NORM)
+    return MOE_ERR_INVALID_ARG;
+  if (!(0 <= e_begin && e_begin < e_end && e_end <= E)) return MOE_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(T) * k > INT32_MAX) return MOE_ERR_INVALID_ARG;
+  const int E_loc = e_end - e_begin;
+  const int64_t max_rows = moe_max_rows(T, k, E_loc, capacity);
+  // the two GEMMs' rules (shape, alignment) on the buffers they touch
+  // GEMM1 reads x in place (rows gathered through sorted_pair)
+  st = check_ffn(x, offsets, E_loc, max_rows, d, f, dtype, w13_packed, h);
+  if (st != MOE_OK) return st;
+  st = check_ffn(h, offsets, E_loc, max_rows, d, f, dtype, w2_packed, y_perm);
+  if (st != MOE_OK) return st;
+  const double big = static_cast<double>(max_rows > T ? max_rows : T);
+  if (dtype == MOE_BF16 && (big * (d > f ? d : f) * 2 >= 4294967296.0 ||
+                            static_cast<double>(2) * f * d * 2 >= 4294967296.0))
+    return MOE_ERR_UNSUPPORTED;  // the fused GEMMs address operands with 32-bit offsets
+  if (!ws || !counts || !n_kept || !y) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && (!logits || !x || !topk_idx || !topk_w || !sorted_pair || !pair_pos))
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned16(logits) || !aligned16(x) || !aligned16(topk_idx) || !aligned16(topk_w) ||
+      !aligned16(counts) || !aligned16(sorted_pair) || !aligned16(pair_pos) ||
+      !aligned16(n_kept) || !aligned16(y) || !aligned16(ws))
+    return MOE_ERR_MISALIGNED;
+  if (ws_bytes < moe::dispatch_ws_bytes(T, E)) return MOE_ERR_WORKSPACE;
+  const moe::DispatchWs w = moe::dispatch_ws(ws, T, E);
+  moe::FusedArgs a;
+  a.logits = logits;
+  a.x = x;
+  a.w13 = w13_packed;
+  a.w2 = w2_packed;
+  a.T = T;
+  a.E = E;
+  a.k = k;
+  a.gate = gate;
+  a.capacity = capacity;
+  a.e_begin = e_begin;
+  a.e_end = e_end;
+  a.d = d;
+  a.f = f;
+  a.ffn_all_rows = max_rows / E_loc <= 48 ? 1 : 0;
+  a.topk_idx = topk_idx;
+  a.topk_w = topk_w;
+  a.counts = counts;
+  a.offsets = offsets;
+  a.sorted_pair = sorted_pair;
+  a.pair_pos = pair_pos;
+  a.n_kept = n_kept;
+  a.h = h;
+  a.y_perm = y_perm;
+  a.y = y;
+  a.err = w.err;
+  a.block_counts = w.block_counts;
+  a.bar_gen = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + moe::kWsBarGen);
+  a.bar_count = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + moe::kWsBarCount);
+  a.bar_group = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + moe::kWsBarGroup);
+  return hip_status(moe::launch_fused(a, dtype == MOE_BF16, max_rows, stream));
 }
 
 }  // extern "C"

@@ -1,0 +1,308 @@
+// Pipelined grouped GEMM (bf16 in, fp32 accumulation, v_mfma_f32_32x32x16_bf16)
+// for the expert FFN halves.
+//
+// DWDP page, key optimisations: the first grouped GEMM takes every local
+// expert's rows against its fused [W1 | W3] operand with SwiGLU in the
+// epilogue; the second grouped GEMM applies W2.
+//
+// Tile: BM activation rows x 256 weight rows (SwiGLU: 128 W1 rows + the
+// matching 128 W3 rows -> 128 h columns).  4 waves split the tile 2 x 2; each
+// wave owns (BM / 2) x 128, i.e. BM / 64 x 4 MFMA tiles of 32 x 32.
+//   BM = 256  experts with many rows (MFMA-bound; 256 accumulators per lane);
+//   BM = 128 / 64  experts with few rows, where the weights stream from HBM
+//             and the smaller A tile leaves LDS for a deeper pipeline.
+//
+// Memory pipeline: operands go HBM/L2 -> LDS directly (global_load_lds_dwordx4,
+// no staging registers) in K-steps of 32 through STAGES LDS buffers, so loads
+// run STAGES - 1 steps ahead of the MFMAs.  A step's loads are spread over the
+// MFMAs of the step before; MFMA operands are double buffered in registers
+// (the next 16-deep substep's LDS reads overlap the current substep's MFMAs),
+// and each step's barrier sits under the last substep's MFMAs.  The load
+// stream runs across tile boundaries, so the next tile's operands are in
+// flight during the current tile's epilogue.  Rows are 64 bytes (4 chunks of
+// 16 B); chunk c of row r sits at chunk c ^ ((r >> 2) & 3), so each 16-lane
+// phase of a ds_read_b128 touches 16 distinct bank groups; the direct loads
+// realise this by choosing which global chunk each lane fetches.
+//
+// Rows: the rows of row class CLASS of each expert (tile_sched.h).
+//
+// Scheduling: persistent grid (one workgroup per CU); tiles in expert order,
+// M-tiles fastest so consecutive tiles share a weight tile; workgroup ids
+// remapped so each XCD (ids dealt round-robin over 8 XCDs) owns contiguous
+// tile ranges and shares weight tiles in its own L2.
+#pragma once
+
+#include "common.h"
+#include "tile_sched.h"
+
+namespace moe {
+
+namespace pipe {
+
+constexpr int kBNW = 256;        // weight rows per tile
+constexpr int kBK = 32;          // K depth of one pipeline step
+constexpr int kKC = kBK / 8;     // 16-byte chunks per 64-byte row
+constexpr int kRPI = 64 / kKC;   // rows covered by one 64-lane 16-byte load (16)
+constexpr int kSUB = kBK / 16;   // MFMA K-substeps per step (2)
+
+__device__ __forceinline__ float silu_fast(float a) {
+  return a * __builtin_amdgcn_rcpf(1.f + __expf(-a));
+}
+
+// s_waitcnt vmcnt(N) (N < 64) with the other counters left alone
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt out of range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// scheduling groups of one substep: MFMA g is preceded by its share of the NDS
+// LDS reads (evenly spread, first one before MFMA 0) and followed by its share
+// of the NVM global loads (evenly spread, none after the last MFMA)
+template <int G, int NMF, int NDS, int NVM>
+__device__ __forceinline__ void interleave() {
+  if constexpr (G < NMF) {
+    constexpr int nds = ((G + 1) * NDS + NMF - 1) / NMF - (G * NDS + NMF - 1) / NMF;
+    constexpr int nvm = ((G + 2) * NVM) / NMF - ((G + 1) * NVM) / NMF;
+    if constexpr (nds > 0) __builtin_amdgcn_sched_group_barrier(0x100, nds, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (nvm > 0) __builtin_amdgcn_sched_group_barrier(0x020, nvm, 0);
+    interleave<G + 1, NMF, NDS, NVM>();
+  }
+}
+
+struct Tile {
+  int e, m0, seg1, n0;
+};
+
+template <int BM, int BN, int CLASS>
+__device__ __forceinline__ Tile decode_tile(int t, int NT, const int* prefix, const int* segs,
+                                            int E_loc) {
+  Tile r;
+  r.e = find_expert(prefix, E_loc, t / NT);
+  const int mt_e = prefix[r.e + 1] - prefix[r.e];
+  const int local = t - prefix[r.e] * NT;
+  const int nt = local / mt_e, mti = local % mt_e;
+  int first, count;
+  class_rows<CLASS>(segs[r.e + 1] - segs[r.e], first, count);
+  r.m0 = segs[r.e] + first + mti * BM;
+  r.seg1 = segs[r.e] + first + count;
+  r.n0 = nt * BN;
+  // the tile is the same for the whole wave: keep its fields in scalar registers
+  r.e = __builtin_amdgcn_readfirstlane(r.e);
+  r.m0 = __builtin_amdgcn_readfirstlane(r.m0);
+  r.seg1 = __builtin_amdgcn_readfirstlane(r.seg1);
+  r.n0 = __builtin_amdgcn_readfirstlane(r.n0);
+  return r;
+}
+
+}  // namespace pipe
+
+using namespace pipe;
+
+// dynamic LDS bytes of gemm_pipe_body<..., BM, STAGES, ...>
+constexpr size_t pipe_lds_bytes(int BM, int STAGES) {
+  return static_cast<size_t>(STAGES) * (BM + kBNW) * kBK * sizeof(uint16_t);
+}
+
+// One workgroup's share of the grouped GEMM: workgroup `bid` of `G` walks its
+// tiles.  lds: STAGES * (BM + 256) * 64 bytes; prefix, segs: E_loc + 1 ints of
+// LDS each.  Every thread of the workgroup must call it (it has barriers).
+// gather: if not null, activation row r is row gather[r] / gk of A (A rows
+// read in place through the dispatch permutation instead of a permuted copy).
+template <bool SWIGLU, int BM, int STAGES, int CLASS>
+__device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
+                                               const int32_t* __restrict__ offsets, int E_loc,
+                                               const uint16_t* __restrict__ W,
+                                               uint16_t* __restrict__ C, int N, int K, int bid,
+                                               int G, uint4* lds, int* prefix, int* segs,
+                                               const int32_t* __restrict__ gather = nullptr,
+                                               int gk = 1) {
+  constexpr int BN = SWIGLU ? 128 : 256;   // output columns per tile
+  constexpr int FM = BM / 64;              // 32-row MFMA blocks per wave
+  constexpr int LA = BM / kRPI / 4;        // A loads per wave per step
+  constexpr int LB = kBNW / kRPI / 4;      // B loads per wave per step (4)
+  constexpr int LSTEP = LA + LB;
+  constexpr int STAGE_U4 = (BM + kBNW) * kKC;
+  static_assert(FM >= 1 && LB % kSUB == 0, "unsupported tile");
+  for (int i = threadIdx.x; i <= E_loc; i += blockDim.x) segs[i] = offsets[i];
+  mtile_prefix<BM, CLASS>(offsets, E_loc, prefix);  // ends with a barrier
+  const int NT = (N + BN - 1) / BN;
+  const int total = prefix[E_loc] * NT;
+  int vb = bid;
+  if ((G & 7) == 0) vb = (bid & 7) * (G >> 3) + (bid >> 3);
+  if (vb >= total) {
+    __syncthreads();  // prefix / segs may be rewritten by the caller's next phase
+    return;
+  }
+  const int ntiles = (total - vb + G - 1) / G;
+  const int KT = K / kBK;
+  const int S = ntiles * KT;  // this workgroup's K-steps over all its tiles
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const size_t wstride = static_cast<size_t>(SWIGLU ? 2 * N : N) * K;
+  // LDS swizzle: chunk c of row r is stored at c ^ swz(r); swz spreads the 16
+  // rows read by one 16-lane ds_read_b128 phase over all bank groups
+  auto swz = [](int r) { return (r >> 2) & 3; };
+  // the chunk this lane fetches in every 16-row group it loads (row = g * 16 +
+  // lane / 4, so swz(row) depends only on the lane)
+  const int lkc = (lane % kKC) ^ swz(lane / kKC);
+  const char* Ab = reinterpret_cast<const char*>(A);
+
+  // ---- issue side: the tile whose operands are being fetched
+  int it_tile = -1;
+  const char* iWb = nullptr;
+  uint32_t aoff[LA], boff[LB];
+  auto set_issue_tile = [&](int j) {
+    const Tile t = decode_tile<BM, BN, CLASS>(vb + j * G, NT, prefix, segs, E_loc);
+    iWb = reinterpret_cast<const char*>(W + t.e * wstride);
+#pragma unroll
+    for (int i = 0; i < LA; ++i) {
+      const int rt = (i * 4 + wave) * kRPI + lane / kKC;  // row within the tile
+      int arow = min(t.m0 + rt, t.seg1 - 1);
+      if (gather != nullptr) arow = gather[arow] / gk;
+      aoff[i] = (static_cast<uint32_t>(arow) * K + lkc * 8) * 2u;
+    }
+#pragma unroll
+    for (int i = 0; i < LB; ++i) {
+      const int rt = (i * 4 + wave) * kRPI + lane / kKC;
+      int wrow;
+      if (SWIGLU) wrow = (rt >> 7) * N + min(t.n0 + (rt & 127), N - 1);
+      else wrow = min(t.n0 + rt, N - 1);
+      boff[i] = (static_cast<uint32_t>(wrow) * K + lkc * 8) * 2u;
+    }
+    it_tile = j;
+  };
+  // part p (of kSUB) of a step's loads into buffer buf
+  auto issue_part = [&](int p, int buf, uint32_t koff) {
+    uint4* As = lds + buf * STAGE_U4;
+    uint4* Bs = As + BM * kKC;
+#pragma unroll
+    for (int i = p * LA / kSUB; i < (p + 1) * LA / kSUB; ++i)
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(Ab + (aoff[i] + koff)),
+          (__attribute__((address_space(3))) void*)(As + (i * 4 + wave) * 64), 16, 0, 0);
+#pragma unroll
+    for (int i = p * LB / kSUB; i < (p + 1) * LB / kSUB; ++i)
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(iWb + (boff[i] + koff)),
+          (__attribute__((address_space(3))) void*)(Bs + (i * 4 + wave) * 64), 16, 0, 0);
+  };
+  // byte offset along K of step p's operands, switching the issue tile when p
+  // starts a new one; steps past the end re-fetch the last step (valid
+  // addresses, result unused)
+  auto issue_koff = [&](int p) -> uint32_t {
+    if (p >= S) p = S - 1;
+    const int j = p / KT, kt = p - j * KT;
+    if (j != it_tile) set_issue_tile(j);
+    return static_cast<uint32_t>(kt) * kBK * 2u;
+  };
+
+  // LDS fragments of substep ks of the step held in buffer `buf`
+  bf16x8_t fa[2][FM], fb[2][4];
+  auto load_frags = [&](int buf, int ks, int slot) {
+    const uint4* As = lds + buf * STAGE_U4;
+    const uint4* Bs = As + BM * kKC;
+    const int ch = ks * 2 + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (i < FM) {
+        const int r = wm * (BM / 2) + i * 32 + (lane & 31);
+        fa[slot][i] = __builtin_bit_cast(bf16x8_t, As[r * kKC + (ch ^ swz(r))]);
+      }
+      const int q = SWIGLU ? ((i >> 1) * 128 + wn * 64 + (i & 1) * 32 + (lane & 31))
+                           : (wn * 128 + i * 32 + (lane & 31));
+      fb[slot][i] = __builtin_bit_cast(bf16x8_t, Bs[q * kKC + (ch ^ swz(q))]);
+    }
+  };
+  // Step p becomes readable: this wave's loads of step p are done once at most
+  // the (STAGES - 2) younger steps' loads are outstanding (loads complete in
+  // order) and its own LDS reads of the step before are done; the barrier then
+  // publishes every wave's step-p data and frees the buffer of step p - 1.
+  // The loads of step p + STAGES - 1 go into that buffer in kSUB parts: part 0
+  // right after the barrier, the others during the first substeps of step p
+  // (pk / pb hold the pending step's K offset and buffer meanwhile).
+  uint32_t pk = 0u;
+  int pb = 0;
+  auto sync_and_issue = [&](int p) {
+    wait_vmcnt<(STAGES - 2) * LSTEP>();
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    pk = issue_koff(p + STAGES - 1);
+    pb = (p + STAGES - 1) % STAGES;
+    issue_part(0, pb, pk);
+  };
+
+  // ---- prologue: steps 0 .. STAGES - 2 in flight, step 0 made readable
+  for (int p = 0; p < STAGES - 1; ++p) {
+    const uint32_t ko = issue_koff(p);
+#pragma unroll
+    for (int q = 0; q < kSUB; ++q) issue_part(q, p % STAGES, ko);
+  }
+  sync_and_issue(0);
+
+  // instruction interleave of one substep: FM * 4 MFMAs with the FM + 4 LDS
+  // reads of the next substep and about LSTEP / kSUB global loads between them
+  constexpr int NMF = FM * 4, NDS = FM + 4, NVM = (LSTEP + kSUB - 1) / kSUB;
+
+  for (int j = 0; j < ntiles; ++j) {
+    const Tile ct = decode_tile<BM, BN, CLASS>(vb + j * G, NT, prefix, segs, E_loc);
+    const int valid = min(BM, ct.seg1 - ct.m0);
+    f32x16_t acc[FM][4];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[i][q] = f32x16_t{};
+    load_frags((j * KT) % STAGES, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+
+    for (int kt = 0; kt < KT; ++kt) {
+      const int s = j * KT + kt;
+      const int buf = s % STAGES;
+#pragma unroll
+      for (int ks = 0; ks < kSUB; ++ks) {
+        const int cur = ks & 1;  // kSUB is even: substep 0 of every step uses slot 0
+        if (ks + 1 < kSUB) {
+          load_frags(buf, ks + 1, cur ^ 1);
+          issue_part(ks + 1, pb, pk);
+        } else if (s + 1 < S) {
+          // the next step's barrier sits under this substep's MFMAs; within
+          // the tile its first fragments are fetched right behind it
+          sync_and_issue(s + 1);
+          if (kt + 1 < KT) load_frags((s + 1) % STAGES, 0, cur ^ 1);
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            acc[i][q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][q], acc[i][q], 0, 0, 0);
+        interleave<0, NMF, NDS, NVM>();
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+
+    // epilogue (registers -> global); D[m][n] of a 32x32 MFMA tile is in lane
+    // n + 32 * ((m / 4) % 2), register 4 * (m / 8) + m % 4
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      if (wm * (BM / 2) + i * 32 >= valid) continue;
+#pragma unroll
+      for (int q = 0; q < (SWIGLU ? 2 : 4); ++q) {
+        const int col = ct.n0 + (SWIGLU ? wn * 64 : wn * 128) + q * 32 + (lane & 31);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          const int row = ct.m0 + wm * (BM / 2) + i * 32 + m;
+          float v = acc[i][q][r];
+          if constexpr (SWIGLU) v = silu_fast(v) * acc[i][q + 2][r];
+          if (row < ct.seg1 && col < N) C[static_cast<size_t>(row) * N + col] = f32_to_bf16(v);
+        }
+      }
+    }
+  }
+  wait_vmcnt<0>();  // redundant tail loads must land before the LDS is released
+  __syncthreads();
+}
+
+}  // namespace moe

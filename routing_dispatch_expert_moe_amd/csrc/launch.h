@@ -8,7 +8,7 @@
 namespace moe {
 
 // device error word lives at the start of the workspace
-constexpr size_t kWsHeader = 256;
+constexpr size_t kWsHeader = 2048;
 constexpr int kDispatchTokensPerBlock = 256;
 
 struct DispatchWs {
@@ -48,6 +48,39 @@ int launch_combine(const void* y_perm, const int32_t* pair_pos, const float* w, 
 int launch_pack(const void* w1, const void* w3, const void* w2, int E_loc, int d, int f,
                 int elem_bytes, void* w13, void* w2p, void* stream);
 int check_error(void* ws, void* stream, int* device_flags);
+
+// Arguments of the fused persistent layer (every pointer already validated).
+struct FusedArgs {
+  const float* logits;
+  const void* x;
+  const void* w13;
+  const void* w2;
+  int T, E, k, gate, capacity, e_begin, e_end, d, f;
+  int ffn_all_rows;  // bf16: 1 = every row in 128-row tiles (few rows per expert)
+  int32_t* topk_idx;
+  float* topk_w;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* sorted_pair;
+  int32_t* pair_pos;
+  int32_t* n_kept;
+  void* h;
+  void* y_perm;
+  void* y;
+  int* err;             // workspace error word
+  int* block_counts;    // workspace per-block expert counts
+  uint32_t* bar_gen;    // workspace barrier words: generation,
+  uint32_t* bar_count;  // top-level arrivals,
+  uint32_t* bar_group;  // 8 group arrival counters, kWsBarStride words apart
+};
+// byte offsets of the barrier words inside the workspace header (each on its
+// own 128-byte line)
+constexpr size_t kWsBarGen = 128;
+constexpr size_t kWsBarCount = 256;
+constexpr size_t kWsBarGroup = 512;
+constexpr size_t kWsBarStride = 32;  // uint32 words = 128 bytes
+size_t fused_lds_bytes(int E, bool bf16);
+int launch_fused(const FusedArgs& a, bool bf16, int64_t max_rows, void* stream);
 
 int device_cu_count();
 

@@ -7,6 +7,7 @@
 // or sigmoid normalised over the k.
 #include "common.h"
 #include "launch.h"
+#include "route_dev.h"
 
 namespace moe {
 
@@ -78,81 +79,13 @@ int launch_router_logits(const void* x, const float* wg, int T, int d, int E, fl
   return static_cast<int>(hipGetLastError());
 }
 
-// ---------------------------------------------------------------------------
-// A1: one wave per token.  Each lane holds EPL logits (expert e = lane + 64*i)
-// as 64-bit keys: high word = order-preserving image of the fp32 value (with
-// -0.0 mapped to +0.0), low word = ~e, so the largest key is the largest
-// logit and, among equal logits, the lowest expert index.  k rounds of a
-// wave-wide max pick the experts best first.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t ordered_bits(float v) {
-  uint32_t u = __float_as_uint(v);
-  if (u == 0x80000000u) u = 0u;  // -0.0 and +0.0 share one key
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-__device__ __forceinline__ float from_ordered(uint32_t o) {
-  uint32_t u = (o & 0x80000000u) ? (o & 0x7fffffffu) : ~o;
-  return __uint_as_float(u);
-}
-
 template <int EPL>
 __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int T, int E,
                                                     int k, int gate, int32_t* __restrict__ topk_idx,
                                                     float* __restrict__ topk_w) {
-  const int lane = lane_id();
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  const float* row = logits + (size_t)t * E;
-  uint64_t key[EPL];
-#pragma unroll
-  for (int i = 0; i < EPL; ++i) {
-    const int e = lane + kWave * i;
-    key[i] = 0;
-    if (e < E) key[i] = (static_cast<uint64_t>(ordered_bits(row[e])) << 32) | static_cast<uint32_t>(~e);
-  }
-  int sel_e[MOE_MAX_K];
-  float sel_v[MOE_MAX_K];
-#pragma unroll
-  for (int j = 0; j < MOE_MAX_K; ++j) {
-    if (j < k) {
-      uint64_t best = 0;
-#pragma unroll
-      for (int i = 0; i < EPL; ++i) best = key[i] > best ? key[i] : best;
-      best = wave_max_u64(best);
-#pragma unroll
-      for (int i = 0; i < EPL; ++i)
-        if (key[i] == best) key[i] = 0;
-      sel_e[j] = static_cast<int>(~static_cast<uint32_t>(best));
-      sel_v[j] = from_ordered(static_cast<uint32_t>(best >> 32));
-    } else {
-      sel_e[j] = 0;
-      sel_v[j] = 0.f;
-    }
-  }
-  float g[MOE_MAX_K];
-  float sum = 0.f;
-  if (gate == 0) {
-    const float m = sel_v[0];
-#pragma unroll
-    for (int j = 0; j < MOE_MAX_K; ++j) {
-      g[j] = j < k ? expf(sel_v[j] - m) : 0.f;
-      sum += g[j];
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < MOE_MAX_K; ++j) {
-      g[j] = j < k ? 1.f / (1.f + expf(-sel_v[j])) : 0.f;
-      sum += g[j];
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < MOE_MAX_K; ++j) {
-    if (j < k && lane == j) {
-      topk_idx[(size_t)t * k + j] = sel_e[j];
-      topk_w[(size_t)t * k + j] = g[j] / sum;
-    }
-  }
+  route_token<EPL>(logits, t, E, k, gate, topk_idx, topk_w);
 }
 
 int launch_route(const float* logits, int T, int E, int k, int gate, int32_t* idx, float* w,

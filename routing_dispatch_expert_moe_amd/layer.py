@@ -3,6 +3,7 @@
 forward() enqueues, on the current HIP stream:
   [moe_router_logits] -> moe_route -> moe_dispatch -> moe_ffn_up -> moe_ffn_down -> moe_combine
 and never synchronises with the host (row counts stay on the device).
+forward_fused() enqueues the same path as one moe_forward_fused launch.
 """
 from __future__ import annotations
 
@@ -74,6 +75,14 @@ class MoELayer:
         self.ffn_down()
         self.combine()
         return self.y
+
+    def forward_fused(self, x: torch.Tensor, logits: torch.Tensor) -> torch.Tensor:
+        """route -> dispatch -> expert FFN -> combine as one persistent launch."""
+        if x.shape[0] != self.T:
+            raise ValueError(f"layer was sized for T={self.T}, got {x.shape[0]}")
+        return ops.moe_forward_fused(logits, x, self.k, self.gate, self.capacity, self.e_begin,
+                                     self.e_end, self.w13, self.w2, self.ws, self.plan,
+                                     self.topk_idx, self.topk_w, self.h, self.y_perm, self.y)
 
     def outputs(self) -> Dict[str, torch.Tensor]:
         p = self.plan

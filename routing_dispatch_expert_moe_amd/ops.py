@@ -208,3 +208,23 @@ def moe_combine(y_perm, pair_pos, topk_w, y=None, stream=None):
 def moe_check_error(ws, stream=None) -> int:
     """Synchronise and return the device-side status (0 = OK) without raising."""
     return int(lib().moe_check_error(_ptr(ws), _stream(stream)))
+
+
+def moe_forward_fused(logits, x, k, gate, capacity, e_begin, e_end, w13_packed, w2_packed, ws,
+                      plan: DispatchPlan, topk_idx, topk_w, h, y_perm, y, stream=None):
+    """The whole layer (route, dispatch, expert FFN, combine) in one persistent launch.
+
+    Every output buffer is caller-provided (the layer preallocates them); they
+    receive the same bits as the four separate calls, except that no permuted
+    copy of x is written (the first GEMM reads x through the permutation)."""
+    T, E = logits.shape
+    d = x.shape[1]
+    f = w13_packed.shape[1] // 2
+    check(lib().moe_forward_fused(_ptr(logits), _ptr(x), T, E, k, _gate_code(gate), capacity,
+                                  e_begin, e_end, d, f, _dtype_code(x.dtype), _ptr(w13_packed),
+                                  _ptr(w2_packed), _ptr(topk_idx), _ptr(topk_w), _ptr(plan.counts),
+                                  _ptr(plan.offsets), _ptr(plan.sorted_pair), _ptr(plan.pair_pos),
+                                  _ptr(plan.n_kept), _ptr(h), _ptr(y_perm), _ptr(y), _ptr(ws),
+                                  ws.numel(), _stream(stream)),
+          "moe_forward_fused")
+    return y

@@ -82,3 +82,24 @@ def layer_for(wl, w13, w2p, capacity=None) -> M.MoELayer:
     C = capacity_of(wl) if capacity is None else capacity
     return M.MoELayer(w13, w2p, E=wl.E, k=wl.k, gate=wl.gate, T=wl.T, capacity=C,
                       e_begin=wl.e_begin, e_end=wl.e_end)
+
+
+def fused_matches_unfused(wl, w13, w2p, layer, x, logits, capacity=None):
+    """Run moe_forward_fused into a second layer's buffers and check that every
+    output carries the same bits as the separate calls in `layer`."""
+    fl = layer_for(wl, w13, w2p, capacity=capacity)
+    fl.forward_fused(x, logits)
+    assert M.moe_check_error(fl.ws) == 0
+    a, b = layer.outputs(), fl.outputs()
+    n = int(t_out(a["n_kept"])[0])
+    assert int(t_out(b["n_kept"])[0]) == n
+    for key in ("topk_idx", "topk_w", "counts", "offsets", "pair_pos", "y"):
+        assert np.array_equal(t_out(a[key]), t_out(b[key])), key
+    for key in ("sorted_pair", "h", "y_perm"):
+        assert np.array_equal(t_out(a[key])[:n], t_out(b[key])[:n]), key
+    # a second fused call on the same workspace (barrier words re-armed) is identical
+    y1 = t_out(fl.y).copy()
+    fl.forward_fused(x, logits)
+    assert M.moe_check_error(fl.ws) == 0
+    assert np.array_equal(t_out(fl.y), y1)
+    return fl

@@ -31,7 +31,8 @@ def declared_functions():
 def test_header_declares_the_path():
     names = declared_functions()
     for n in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_router_logits",
-              "moe_pack_weights", "moe_check_error", "moe_ffn_up", "moe_ffn_down"):
+              "moe_pack_weights", "moe_check_error", "moe_ffn_up", "moe_ffn_down",
+              "moe_forward_fused"):
         assert n in names
 
 
@@ -131,6 +132,38 @@ def test_combine_router_pack_validation(lib):
     assert lib.moe_pack_weights(FAKE, FAKE, FAKE, 0, 64, 64, L.MOE_BF16, FAKE, FAKE, None) == L.MOE_ERR_INVALID_ARG
     assert lib.moe_pack_weights(FAKE, MIS, FAKE, 2, 64, 64, L.MOE_BF16, FAKE, FAKE, None) == L.MOE_ERR_MISALIGNED
     assert lib.moe_check_error(None, None) == L.MOE_ERR_INVALID_ARG
+
+
+def test_fused_validation(lib):
+    f = lib.moe_forward_fused
+    ws_ok = M.moe_workspace_bytes(100, 8, 2, 8)
+    ok = dict(lg=FAKE, x=FAKE, T=100, E=8, k=2, gate=0, cap=-1, e0=0, e1=8, d=128, f=256,
+              dt=L.MOE_BF16, w13=FAKE, w2=FAKE, idx=FAKE, w=FAKE, counts=FAKE, off=FAKE, sp=FAKE,
+              pp=FAKE, nk=FAKE, h=FAKE, yp=FAKE, y=FAKE, ws=FAKE, wsb=ws_ok)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return f(a["lg"], a["x"], a["T"], a["E"], a["k"], a["gate"], a["cap"], a["e0"], a["e1"],
+                 a["d"], a["f"], a["dt"], a["w13"], a["w2"], a["idx"], a["w"], a["counts"],
+                 a["off"], a["sp"], a["pp"], a["nk"], a["h"], a["yp"], a["y"], a["ws"], a["wsb"],
+                 None)
+
+    assert call(k=9) == L.MOE_ERR_INVALID_TOPK
+    assert call(k=0) == L.MOE_ERR_INVALID_TOPK
+    assert call(E=2000) == L.MOE_ERR_INVALID_ARG
+    assert call(gate=5) == L.MOE_ERR_INVALID_ARG
+    assert call(e0=4, e1=2) == L.MOE_ERR_INVALID_ARG
+    assert call(T=-1) == L.MOE_ERR_INVALID_ARG
+    assert call(d=100) == L.MOE_ERR_UNSUPPORTED         # bf16 needs d % 64 == 0
+    assert call(dt=7) == L.MOE_ERR_UNSUPPORTED
+    assert call(x=None) == L.MOE_ERR_INVALID_ARG
+    assert call(ws=None) == L.MOE_ERR_INVALID_ARG
+    assert call(y=MIS) == L.MOE_ERR_MISALIGNED
+    assert call(h=MIS) == L.MOE_ERR_MISALIGNED
+    assert call(wsb=ws_ok - 1) == L.MOE_ERR_WORKSPACE
+    # bf16 operands beyond 32-bit byte offsets are refused up front
+    assert call(T=600000, k=8, E=8, d=4096, f=4096) == L.MOE_ERR_UNSUPPORTED
 
 
 def test_package_fails_loudly_without_library(monkeypatch, tmp_path):

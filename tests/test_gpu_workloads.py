@@ -14,8 +14,8 @@ import routing_dispatch_expert_moe_amd as M
 from oracle import moe_oracle as O
 from workloads import make
 
-from gpu_util import (DEV, as64, capacity_of, layer_for, log, packed_weights, t_in, t_out,
-                      weights_fn)
+from gpu_util import (DEV, as64, capacity_of, fused_matches_unfused, layer_for, log,
+                      packed_weights, t_in, t_out, weights_fn)
 
 pytestmark = pytest.mark.gpu
 
@@ -90,6 +90,9 @@ def test_workload_with_given_logits(name):
     y1 = t_out(y).copy()
     layer.forward(x, logits=t_in(wl.logits, "f32"))
     assert np.array_equal(t_out(layer.y), y1)
+    # the fused persistent launch produces the same bits as the separate calls
+    log(f"{name}: fused layer")
+    fused_matches_unfused(wl, w13, w2p, layer, x, t_in(wl.logits, "f32"))
 
 
 @pytest.mark.timeout(600)
@@ -135,3 +138,6 @@ def test_mixtral_prefill_with_router():
     skip = set(diff.tolist())
     toks = [t for t in sampled_tokens(wl.T, ref["pair_pos"], wl.k, n=32) if t not in skip]
     check_outputs(wl, host, y, idx, w, ref["pair_pos"], toks)
+    # the fused persistent launch on the same GPU logits: same bits as the separate calls
+    log("mixtral_prefill: fused layer")
+    fused_matches_unfused(wl, w13, w2p, layer, x, out["logits"])
