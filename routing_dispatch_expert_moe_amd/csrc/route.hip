@@ -12,70 +12,77 @@
 namespace moe {
 
 // ---------------------------------------------------------------------------
-// A0: logits[t][e] = sum_i x[t][i] * wg[i][e]; x bf16, wg fp32.
-// One wave handles TPW tokens; lanes stride over 8-element chunks of d, so
-// each x load is a coalesced 16-byte access and wg rows are shared by the
-// TPW tokens.  Partial sums meet in a fixed butterfly (deterministic).
+// A0: logits[t][e] = sum_i x[t][i] * wg[i][e]; x bf16 (exact in fp32), wg fp32,
+// fp32 products and sums.
+// A workgroup takes 16 tokens; each token's 16 threads are 16 consecutive
+// lanes of one wave and split d into interleaved 8-element chunks (lane s
+// takes chunks s, s + 16, ...), so the 16 lanes of a token read 256
+// contiguous bytes of x per step and the 4 tokens of a wave share every wg
+// row they read.  Each thread keeps EB partial sums; the 16 partials of a
+// token meet in a fixed xor butterfly (deterministic).
 // ---------------------------------------------------------------------------
-template <int EB, int TPW>
+template <int EB>
 __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __restrict__ x,
                                                             const float* __restrict__ wg,
                                                             int T, int d, int E,
                                                             float* __restrict__ logits) {
-  const int lane = lane_id();
-  const int t0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * TPW;
-  if (t0 >= T) return;
-  float acc[TPW][EB];
+  constexpr int S = 16;  // threads per token
+  const int s = threadIdx.x % S;
+  const int t = blockIdx.x * (256 / S) + threadIdx.x / S;
+  float acc[EB];
 #pragma unroll
-  for (int a = 0; a < TPW; ++a)
+  for (int e = 0; e < EB; ++e) acc[e] = 0.f;
+  if (t < T) {
+    const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)t * d);
+    const int nchunk = d >> 3;
+    constexpr int U = 4;  // chunks per thread in flight
+    for (int c0 = s; c0 < nchunk; c0 += U * S) {
+      uint4 xv[U];
 #pragma unroll
-    for (int e = 0; e < EB; ++e) acc[a][e] = 0.f;
-  const int nchunk = d >> 3;
-  for (int c = lane; c < nchunk; c += kWave) {
-    float xv[TPW][8];
+      for (int u = 0; u < U; ++u)
+        if (c0 + u * S < nchunk) xv[u] = xr[c0 + u * S];
 #pragma unroll
-    for (int a = 0; a < TPW; ++a) {
-      if (t0 + a < T) {
-        uint4 v = *reinterpret_cast<const uint4*>(x + (size_t)(t0 + a) * d + c * 8);
-        unpack8(v, xv[a]);
-      } else {
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + u * S;
+        if (c >= nchunk) break;
+        float xf[8];
+        unpack8(xv[u], xf);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) xv[a][i] = 0.f;
-      }
-    }
+        for (int i = 0; i < 8; ++i) {
+          const float* wrow = wg + (size_t)(c * 8 + i) * E;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float* wrow = wg + (size_t)(c * 8 + i) * E;
-#pragma unroll
-      for (int e = 0; e < EB; ++e) {
-        float wv = e < E ? wrow[e] : 0.f;
-#pragma unroll
-        for (int a = 0; a < TPW; ++a) acc[a][e] = fmaf(xv[a][i], wv, acc[a][e]);
+          for (int e = 0; e < EB; ++e)
+            if (e < E) acc[e] = fmaf(xf[i], wrow[e], acc[e]);
+        }
       }
     }
   }
+  // butterfly over the token's 16 lanes (all 64 lanes take part)
 #pragma unroll
-  for (int a = 0; a < TPW; ++a)
+  for (int e = 0; e < EB; ++e) {
 #pragma unroll
-    for (int e = 0; e < EB; ++e) {
-      float s = wave_sum_f32(acc[a][e]);
-      if (lane == a * EB + e && e < E && t0 + a < T) logits[(size_t)(t0 + a) * E + e] = s;
-    }
+    for (int off = 1; off < S; off <<= 1) acc[e] += __shfl_xor(acc[e], off, kWave);
+  }
+  if (t < T) {
+#pragma unroll
+    for (int e = 0; e < EB; ++e)
+      if (e % S == s && e < E) logits[(size_t)t * E + e] = acc[e];
+  }
 }
 
 int launch_router_logits(const void* x, const float* wg, int T, int d, int E, float* logits,
                          void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   const uint16_t* xb = static_cast<const uint16_t*>(x);
-  auto grid = [&](int tpw) { return dim3((T + 4 * tpw - 1) / (4 * tpw)); };
+  const dim3 grid((T + 15) / 16), block(256);
   if (E <= 8)
-    hipLaunchKernelGGL((router_logits_kernel<8, 4>), grid(4), dim3(256), 0, s, xb, wg, T, d, E, logits);
+    hipLaunchKernelGGL(router_logits_kernel<8>, grid, block, 0, s, xb, wg, T, d, E, logits);
   else if (E <= 16)
-    hipLaunchKernelGGL((router_logits_kernel<16, 2>), grid(2), dim3(256), 0, s, xb, wg, T, d, E, logits);
+    hipLaunchKernelGGL(router_logits_kernel<16>, grid, block, 0, s, xb, wg, T, d, E, logits);
   else if (E <= 32)
-    hipLaunchKernelGGL((router_logits_kernel<32, 1>), grid(1), dim3(256), 0, s, xb, wg, T, d, E, logits);
+    hipLaunchKernelGGL(router_logits_kernel<32>, grid, block, 0, s, xb, wg, T, d, E, logits);
   else
-    hipLaunchKernelGGL((router_logits_kernel<64, 1>), grid(1), dim3(256), 0, s, xb, wg, T, d, E, logits);
+    hipLaunchKernelGGL(router_logits_kernel<64>, grid, block, 0, s, xb, wg, T, d, E, logits);
   return static_cast<int>(hipGetLastError());
 }
 
