@@ -56,16 +56,16 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// scheduling groups of one substep: MFMA g is preceded by its share of the NDS
-// LDS reads (evenly spread, first one before MFMA 0) and followed by its share
-// of the NVM global loads (evenly spread, none after the last MFMA)
+// scheduling groups of one substep: MFMA g is followed by its share of the NDS
+// LDS reads and of the NVM global loads (both evenly spread; the substep opens
+// with an MFMA so the wait for its own operands never covers the new reads)
 template <int G, int NMF, int NDS, int NVM>
 __device__ __forceinline__ void interleave() {
   if constexpr (G < NMF) {
-    constexpr int nds = ((G + 1) * NDS + NMF - 1) / NMF - (G * NDS + NMF - 1) / NMF;
+    constexpr int nds = ((G + 1) * NDS) / NMF - (G * NDS) / NMF;
     constexpr int nvm = ((G + 2) * NVM) / NMF - ((G + 1) * NVM) / NMF;
-    if constexpr (nds > 0) __builtin_amdgcn_sched_group_barrier(0x100, nds, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (nds > 0) __builtin_amdgcn_sched_group_barrier(0x100, nds, 0);
     if constexpr (nvm > 0) __builtin_amdgcn_sched_group_barrier(0x020, nvm, 0);
     interleave<G + 1, NMF, NDS, NVM>();
   }
@@ -140,7 +140,9 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
   const int S = ntiles * KT;  // this workgroup's K-steps over all its tiles
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  // the wave index is uniform: keep it (and everything derived from it, such
+  // as the M0 bases of the direct loads) in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
   const size_t wstride = static_cast<size_t>(SWIGLU ? 2 * N : N) * K;
   // LDS swizzle: chunk c of row r is stored at c ^ swz(r); swz spreads the 16
@@ -234,71 +236,145 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
     issue_part(0, pb, pk);
   };
 
-  // ---- prologue: steps 0 .. STAGES - 2 in flight, step 0 made readable
-  for (int p = 0; p < STAGES - 1; ++p) {
-    const uint32_t ko = issue_koff(p);
-#pragma unroll
-    for (int q = 0; q < kSUB; ++q) issue_part(q, p % STAGES, ko);
-  }
-  sync_and_issue(0);
-
   // instruction interleave of one substep: FM * 4 MFMAs with the FM + 4 LDS
   // reads of the next substep and about LSTEP / kSUB global loads between them
   constexpr int NMF = FM * 4, NDS = FM + 4, NVM = (LSTEP + kSUB - 1) / kSUB;
+  constexpr uint32_t kStepBytes = kBK * 2;  // K bytes of one step in a row
 
-  for (int j = 0; j < ntiles; ++j) {
-    const Tile ct = decode_tile<BM, BN, CLASS>(vb + j * G, NT, prefix, segs, E_loc);
-    const int valid = min(BM, ct.seg1 - ct.m0);
-    f32x16_t acc[FM][4];
+  auto mfma_substep = [&](f32x16_t (&acc)[FM][4], int slot) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) acc[i][q] = f32x16_t{};
-    load_frags((j * KT) % STAGES, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-
-    for (int kt = 0; kt < KT; ++kt) {
-      const int s = j * KT + kt;
-      const int buf = s % STAGES;
-#pragma unroll
-      for (int ks = 0; ks < kSUB; ++ks) {
-        const int cur = ks & 1;  // kSUB is even: substep 0 of every step uses slot 0
-        if (ks + 1 < kSUB) {
-          load_frags(buf, ks + 1, cur ^ 1);
-          issue_part(ks + 1, pb, pk);
-        } else if (s + 1 < S) {
-          // the next step's barrier sits under this substep's MFMAs; within
-          // the tile its first fragments are fetched right behind it
-          sync_and_issue(s + 1);
-          if (kt + 1 < KT) load_frags((s + 1) % STAGES, 0, cur ^ 1);
-        }
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            acc[i][q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][q], acc[i][q], 0, 0, 0);
-        interleave<0, NMF, NDS, NVM>();
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-
-    // epilogue (registers -> global); D[m][n] of a 32x32 MFMA tile is in lane
-    // n + 32 * ((m / 4) % 2), register 4 * (m / 8) + m % 4
+      for (int q = 0; q < 4; ++q)
+        acc[i][q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i], fb[slot][q], acc[i][q], 0, 0, 0);
+  };
+  auto epilogue = [&](const Tile& ct, f32x16_t (&acc)[FM][4]) {
+    const int valid = min(BM, ct.seg1 - ct.m0);
+    // registers -> global; D[m][n] of a 32x32 MFMA tile is in lane
+    // n + 32 * ((m / 4) % 2), register 4 * (m / 8) + m % 4.  Stores address C
+    // with a uniform base and 32-bit byte offsets (C is below 4 GiB), which
+    // keeps the epilogue's address registers few.
+    char* Cb = reinterpret_cast<char*>(C);
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       if (wm * (BM / 2) + i * 32 >= valid) continue;
+      const int row0 = ct.m0 + wm * (BM / 2) + i * 32 + 4 * (lane >> 5);
 #pragma unroll
       for (int q = 0; q < (SWIGLU ? 2 : 4); ++q) {
         const int col = ct.n0 + (SWIGLU ? wn * 64 : wn * 128) + q * 32 + (lane & 31);
+        const uint32_t base = (static_cast<uint32_t>(row0) * static_cast<uint32_t>(N) +
+                               static_cast<uint32_t>(col)) * 2u;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int m = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          const int row = ct.m0 + wm * (BM / 2) + i * 32 + m;
+          const int dm = 8 * (r >> 2) + (r & 3);
           float v = acc[i][q][r];
           if constexpr (SWIGLU) v = silu_fast(v) * acc[i][q + 2][r];
-          if (row < ct.seg1 && col < N) C[static_cast<size_t>(row) * N + col] = f32_to_bf16(v);
+          if (row0 + dm < ct.seg1 && col < N)
+            *reinterpret_cast<uint16_t*>(Cb + (base + static_cast<uint32_t>(dm * N) * 2u)) =
+                f32_to_bf16(v);
         }
       }
+    }
+  };
+
+  if (KT >= STAGES) {
+    // Straight-line steps: the issue side changes tile only at tile
+    // boundaries (the last STAGES steps of tile j fetch the first STAGES steps
+    // of tile j + 1), so a step has no branch and the compiler sees every
+    // outstanding LDS read when it places its waits.
+    set_issue_tile(0);
+#pragma unroll
+    for (int p = 0; p < STAGES - 1; ++p)
+#pragma unroll
+      for (int q = 0; q < kSUB; ++q) issue_part(q, p, p * kStepBytes);
+    wait_vmcnt<(STAGES - 2) * LSTEP>();
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    pk = (STAGES - 1) * kStepBytes;
+    pb = STAGES - 1;
+    issue_part(0, pb, pk);
+    load_frags(0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+
+    for (int j = 0; j < ntiles; ++j) {
+      const Tile ct = decode_tile<BM, BN, CLASS>(vb + j * G, NT, prefix, segs, E_loc);
+      f32x16_t acc[FM][4];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[i][q] = f32x16_t{};
+      // one step: substep 0 fetches substep 1's fragments and the second
+      // half of the pending step's loads between its MFMAs; substep 1 makes
+      // step s + 1 readable (barrier), sends the first half of step
+      // s + STAGES's loads into this step's buffer and fetches step s + 1's
+      // first fragments
+      auto substep0 = [&](int s) {
+        load_frags(s % STAGES, 1, 1);
+        issue_part(1, pb, pk);
+        mfma_substep(acc, 0);
+        interleave<0, NMF, NDS, NVM>();
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      auto substep1 = [&](int s, uint32_t koff_next) {
+        wait_vmcnt<(STAGES - 2) * LSTEP>();
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        pk = koff_next;
+        pb = s % STAGES;  // (s + STAGES) % STAGES
+        issue_part(0, pb, pk);
+        load_frags((s + 1) % STAGES, 0, 0);
+        mfma_substep(acc, 1);
+        interleave<0, NMF, NDS, NVM>();
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      const int s0 = j * KT;
+      for (int kt = 0; kt < KT - STAGES; ++kt) {
+        substep0(s0 + kt);
+        substep1(s0 + kt, (kt + STAGES) * kStepBytes);
+      }
+      // The last STAGES steps fetch the next tile's first steps (after the
+      // last tile: re-fetch this tile's last step, valid and unused).  The
+      // first of them still sends the second half of this tile's last step,
+      // so the issue side switches tiles between its two substeps.
+      const bool more = j + 1 < ntiles;
+      substep0(s0 + KT - STAGES);
+      if (more) set_issue_tile(j + 1);
+      substep1(s0 + KT - STAGES, more ? 0u : (KT - 1) * kStepBytes);
+      for (int kt = KT - STAGES + 1; kt < KT; ++kt) {
+        substep0(s0 + kt);
+        substep1(s0 + kt, more ? (kt + STAGES - KT) * kStepBytes : (KT - 1) * kStepBytes);
+      }
+      epilogue(ct, acc);
+    }
+  } else {
+    // short K (fewer steps than stages): the issue side may run several
+    // tiles ahead, so it switches tiles step by step
+    for (int p = 0; p < STAGES - 1; ++p) {
+      const uint32_t ko = issue_koff(p);
+#pragma unroll
+      for (int q = 0; q < kSUB; ++q) issue_part(q, p % STAGES, ko);
+    }
+    sync_and_issue(0);
+    for (int j = 0; j < ntiles; ++j) {
+      const Tile ct = decode_tile<BM, BN, CLASS>(vb + j * G, NT, prefix, segs, E_loc);
+      f32x16_t acc[FM][4];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[i][q] = f32x16_t{};
+      load_frags((j * KT) % STAGES, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      for (int kt = 0; kt < KT; ++kt) {
+        const int s = j * KT + kt;
+        const int buf = s % STAGES;
+        load_frags(buf, 1, 1);
+        issue_part(1, pb, pk);
+        mfma_substep(acc, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (s + 1 < S) sync_and_issue(s + 1);
+        mfma_substep(acc, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        if (s + 1 < S && kt + 1 < KT) load_frags((s + 1) % STAGES, 0, 0);
+      }
+      epilogue(ct, acc);
     }
   }
   wait_vmcnt<0>();  // redundant tail loads must land before the LDS is released
