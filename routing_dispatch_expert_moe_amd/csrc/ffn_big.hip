@@ -5,7 +5,7 @@
 
 namespace moe {
 
-template <bool SWIGLU, int BM, int STAGES, int CLASS>
+template <bool SWIGLU, int BM, int BNW, int STAGES, int CLASS>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_pipe(const uint16_t* __restrict__ A,
                                                          const int32_t* __restrict__ offsets,
                                                          int E_loc,
@@ -14,18 +14,19 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_pipe(const uint16_t* __restr
   extern __shared__ uint4 lds[];
   __shared__ int prefix[MOE_MAX_E + 1];
   __shared__ int segs[MOE_MAX_E + 1];
-  gemm_pipe_body<SWIGLU, BM, STAGES, CLASS>(A, offsets, E_loc, W, C, N, K, blockIdx.x, gridDim.x,
-                                            lds, prefix, segs);
+  gemm_pipe_body<SWIGLU, BM, BNW, STAGES, CLASS>(A, offsets, E_loc, W, C, N, K, blockIdx.x,
+                                                 gridDim.x, lds, prefix, segs);
 }
 
 namespace {
 
-template <bool SWIGLU, int BM, int STAGES, int CLASS>
+template <bool SWIGLU, int BM, int BNW, int STAGES, int CLASS>
 int launch_pipe(const void* A, const int32_t* offsets, int E_loc, int64_t max_rows, const void* W,
                 void* C, int N, int K, hipStream_t s) {
-  const size_t lds = pipe_lds_bytes(BM, STAGES);
-  static_assert(pipe_lds_bytes(BM, STAGES) + 2 * (MOE_MAX_E + 1) * 4 <= 160 * 1024, "LDS budget");
-  auto kern = gemm_bf16_pipe<SWIGLU, BM, STAGES, CLASS>;
+  const size_t lds = pipe_lds_bytes(BM, BNW, STAGES);
+  static_assert(pipe_lds_bytes(BM, BNW, STAGES) + 2 * (MOE_MAX_E + 1) * 4 <= 160 * 1024,
+                "LDS budget");
+  auto kern = gemm_bf16_pipe<SWIGLU, BM, BNW, STAGES, CLASS>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -34,7 +35,7 @@ int launch_pipe(const void* A, const int32_t* offsets, int E_loc, int64_t max_ro
     if (e != hipSuccess) return static_cast<int>(e);
     attr_set = true;
   }
-  const int BN = SWIGLU ? 128 : 256;
+  const int BN = SWIGLU ? BNW / 2 : BNW;
   const int64_t NT = (N + BN - 1) / BN;
   int64_t tiles_ub = (max_rows / BM + E_loc) * NT;
   if (CLASS == ROWS_TAIL) tiles_ub = static_cast<int64_t>(E_loc) * ((kTailMax + BM - 1) / BM) * NT;
@@ -48,24 +49,30 @@ int launch_pipe(const void* A, const int32_t* offsets, int E_loc, int64_t max_ro
   return static_cast<int>(hipGetLastError());
 }
 
-#ifndef MOE_SMALL_BM
-#define MOE_SMALL_BM 128
-#endif
-#ifndef MOE_SMALL_STAGES
-#define MOE_SMALL_STAGES 6
-#endif
+// The few-row tiles are 128 activation rows by 128 weight rows with 8 stages
+// when the remainders would give few tiles (twice as many tiles as with 256
+// weight rows keeps every CU busy when only a few experts have remainders),
+// else 128 x 256 with 6 stages (half the re-reads of the activation rows).
+constexpr int kSmallBM = 128, kSmallBNW = 128, kSmallStages = 8;
 
 template <bool SWIGLU>
 int launch_kind(PipeRows rows, const void* A, const int32_t* offsets, int E_loc, int64_t max_rows,
                 const void* W, void* C, int N, int K, hipStream_t s) {
-  constexpr int SB = MOE_SMALL_BM, SS = MOE_SMALL_STAGES;
   switch (rows) {
     case PipeRows::kBigTiles:
-      return launch_pipe<SWIGLU, 256, 4, ROWS_BIG>(A, offsets, E_loc, max_rows, W, C, N, K, s);
-    case PipeRows::kTailTiles:
-      return launch_pipe<SWIGLU, SB, SS, ROWS_TAIL>(A, offsets, E_loc, max_rows, W, C, N, K, s);
+      return launch_pipe<SWIGLU, 256, 256, 4, ROWS_BIG>(A, offsets, E_loc, max_rows, W, C, N, K, s);
+    case PipeRows::kTailTiles: {
+      const int64_t tiles256 = static_cast<int64_t>(E_loc) * ((N + (SWIGLU ? 127 : 255)) /
+                                                              (SWIGLU ? 128 : 256));
+      if (tiles256 >= 4 * static_cast<int64_t>(device_cu_count()))
+        return launch_pipe<SWIGLU, 128, 256, 6, ROWS_TAIL>(A, offsets, E_loc, max_rows, W, C, N,
+                                                            K, s);
+      return launch_pipe<SWIGLU, kSmallBM, kSmallBNW, kSmallStages, ROWS_TAIL>(
+          A, offsets, E_loc, max_rows, W, C, N, K, s);
+    }
     default:
-      return launch_pipe<SWIGLU, SB, SS, ROWS_ALL>(A, offsets, E_loc, max_rows, W, C, N, K, s);
+      return launch_pipe<SWIGLU, kSmallBM, kSmallBNW, kSmallStages, ROWS_ALL>(
+          A, offsets, E_loc, max_rows, W, C, N, K, s);
   }
 }
 

@@ -193,24 +193,24 @@ __global__ __launch_bounds__(256, 1) void moe_fused_kernel(FusedArgs a) {
     const uint16_t* w13 = static_cast<const uint16_t*>(a.w13);
     uint16_t* h = static_cast<uint16_t*>(a.h);
     if (a.ffn_all_rows) {
-      gemm_pipe_body<true, 128, 6, ROWS_ALL>(xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G, lds,
+      gemm_pipe_body<true, 128, 128, 8, ROWS_ALL>(xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G, lds,
                                              prefix, segs, a.sorted_pair, k);
     } else {
-      gemm_pipe_body<true, 256, 4, ROWS_BIG>(xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G, lds,
+      gemm_pipe_body<true, 256, 256, 4, ROWS_BIG>(xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G, lds,
                                              prefix, segs, a.sorted_pair, k);
-      gemm_pipe_body<true, 128, 6, ROWS_TAIL>(xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G,
+      gemm_pipe_body<true, 128, 128, 8, ROWS_TAIL>(xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G,
                                               lds, prefix, segs, a.sorted_pair, k);
     }
     grid_barrier(a, G);
     const uint16_t* w2 = static_cast<const uint16_t*>(a.w2);
     uint16_t* yp = static_cast<uint16_t*>(a.y_perm);
     if (a.ffn_all_rows) {
-      gemm_pipe_body<false, 128, 6, ROWS_ALL>(h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G, lds,
+      gemm_pipe_body<false, 128, 128, 8, ROWS_ALL>(h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G, lds,
                                               prefix, segs);
     } else {
-      gemm_pipe_body<false, 256, 4, ROWS_BIG>(h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G, lds,
+      gemm_pipe_body<false, 256, 256, 4, ROWS_BIG>(h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G, lds,
                                               prefix, segs);
-      gemm_pipe_body<false, 128, 6, ROWS_TAIL>(h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G,
+      gemm_pipe_body<false, 128, 128, 8, ROWS_TAIL>(h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G,
                                                lds, prefix, segs);
     }
   } else {
@@ -234,9 +234,9 @@ __global__ __launch_bounds__(256, 1) void moe_fused_kernel(FusedArgs a) {
 size_t fused_lds_bytes(int E, bool bf16) {
   const size_t plan = static_cast<size_t>(E) * kWords * sizeof(unsigned long long) +
                       2 * static_cast<size_t>(E) * sizeof(int);
-  const size_t gemm = bf16 ? (pipe_lds_bytes(128, 6) > pipe_lds_bytes(256, 4)
-                                  ? pipe_lds_bytes(128, 6)
-                                  : pipe_lds_bytes(256, 4))
+  const size_t gemm = bf16 ? (pipe_lds_bytes(128, 128, 8) > pipe_lds_bytes(256, 256, 4)
+                                  ? pipe_lds_bytes(128, 128, 8)
+                                  : pipe_lds_bytes(256, 256, 4))
                            : f32_lds_floats(true) * sizeof(float);
   return plan > gemm ? plan : gemm;
 }
@@ -263,8 +263,8 @@ int launch_fused(const FusedArgs& a, bool bf16, int64_t max_rows, void* stream) 
   const int64_t nb = (a.T + kTB - 1) / kTB;
   const int64_t tok_groups = (a.T + 3) / 4;
   const int64_t mtiles = bf16 ? max_rows / 128 + E_loc : max_rows / 64 + E_loc;
-  const int64_t up_tiles = mtiles * (bf16 ? (a.f + 127) / 128 : (a.f + 63) / 64);
-  const int64_t down_tiles = mtiles * (bf16 ? (a.d + 255) / 256 : (a.d + 63) / 64);
+  const int64_t up_tiles = mtiles * (bf16 ? (a.f + 63) / 64 : (a.f + 63) / 64);
+  const int64_t down_tiles = mtiles * (bf16 ? (a.d + 127) / 128 : (a.d + 63) / 64);
   const int64_t gemm_tiles = up_tiles > down_tiles ? up_tiles : down_tiles;
   int64_t want = nb;
   if (tok_groups > want) want = tok_groups;

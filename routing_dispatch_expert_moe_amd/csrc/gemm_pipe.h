@@ -39,7 +39,6 @@ namespace moe {
 
 namespace pipe {
 
-constexpr int kBNW = 256;        // weight rows per tile
 constexpr int kBK = 32;          // K depth of one pipeline step
 constexpr int kKC = kBK / 8;     // 16-byte chunks per 64-byte row
 constexpr int kRPI = 64 / kKC;   // rows covered by one 64-lane 16-byte load (16)
@@ -100,17 +99,18 @@ __device__ __forceinline__ Tile decode_tile(int t, int NT, const int* prefix, co
 
 using namespace pipe;
 
-// dynamic LDS bytes of gemm_pipe_body<..., BM, STAGES, ...>
-constexpr size_t pipe_lds_bytes(int BM, int STAGES) {
-  return static_cast<size_t>(STAGES) * (BM + kBNW) * kBK * sizeof(uint16_t);
+// dynamic LDS bytes of gemm_pipe_body<..., BM, BNW, STAGES, ...>
+constexpr size_t pipe_lds_bytes(int BM, int BNW, int STAGES) {
+  return static_cast<size_t>(STAGES) * (BM + BNW) * kBK * sizeof(uint16_t);
 }
 
 // One workgroup's share of the grouped GEMM: workgroup `bid` of `G` walks its
-// tiles.  lds: STAGES * (BM + 256) * 64 bytes; prefix, segs: E_loc + 1 ints of
-// LDS each.  Every thread of the workgroup must call it (it has barriers).
+// tiles.  lds: pipe_lds_bytes(BM, BNW, STAGES); prefix, segs: E_loc + 1 ints
+// of LDS each.  Every thread of the workgroup must call it (it has barriers).
+// BNW weight rows per tile (256 or 128; SwiGLU: half W1, half W3).
 // gather: if not null, activation row r is row gather[r] / gk of A (A rows
 // read in place through the dispatch permutation instead of a permuted copy).
-template <bool SWIGLU, int BM, int STAGES, int CLASS>
+template <bool SWIGLU, int BM, int BNW, int STAGES, int CLASS>
 __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
                                                const int32_t* __restrict__ offsets, int E_loc,
                                                const uint16_t* __restrict__ W,
@@ -118,13 +118,15 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
                                                int G, uint4* lds, int* prefix, int* segs,
                                                const int32_t* __restrict__ gather = nullptr,
                                                int gk = 1) {
-  constexpr int BN = SWIGLU ? 128 : 256;   // output columns per tile
-  constexpr int FM = BM / 64;              // 32-row MFMA blocks per wave
-  constexpr int LA = BM / kRPI / 4;        // A loads per wave per step
-  constexpr int LB = kBNW / kRPI / 4;      // B loads per wave per step (4)
+  constexpr int BN = SWIGLU ? BNW / 2 : BNW;  // output columns per tile
+  constexpr int HALF = BNW / 2;               // SwiGLU: W1 rows (then as many W3 rows)
+  constexpr int FM = BM / 64;                 // 32-row MFMA blocks per wave
+  constexpr int NQ = BNW / 64;                // 32-column MFMA blocks per wave
+  constexpr int LA = BM / kRPI / 4;           // A loads per wave per step
+  constexpr int LB = BNW / kRPI / 4;          // B loads per wave per step
   constexpr int LSTEP = LA + LB;
-  constexpr int STAGE_U4 = (BM + kBNW) * kKC;
-  static_assert(FM >= 1 && LB % kSUB == 0, "unsupported tile");
+  constexpr int STAGE_U4 = (BM + BNW) * kKC;
+  static_assert(FM >= 1 && NQ >= 2 && LB % kSUB == 0, "unsupported tile");
   for (int i = threadIdx.x; i <= E_loc; i += blockDim.x) segs[i] = offsets[i];
   mtile_prefix<BM, CLASS>(offsets, E_loc, prefix);  // ends with a barrier
   const int NT = (N + BN - 1) / BN;
@@ -171,7 +173,7 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
     for (int i = 0; i < LB; ++i) {
       const int rt = (i * 4 + wave) * kRPI + lane / kKC;
       int wrow;
-      if (SWIGLU) wrow = (rt >> 7) * N + min(t.n0 + (rt & 127), N - 1);
+      if (SWIGLU) wrow = (rt / HALF) * N + min(t.n0 + rt % HALF, N - 1);
       else wrow = min(t.n0 + rt, N - 1);
       boff[i] = (static_cast<uint32_t>(wrow) * K + lkc * 8) * 2u;
     }
@@ -203,20 +205,25 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
   };
 
   // LDS fragments of substep ks of the step held in buffer `buf`
-  bf16x8_t fa[2][FM], fb[2][4];
+  bf16x8_t fa[2][FM], fb[2][NQ];
   auto load_frags = [&](int buf, int ks, int slot) {
     const uint4* As = lds + buf * STAGE_U4;
     const uint4* Bs = As + BM * kKC;
     const int ch = ks * 2 + (lane >> 5);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < (FM > NQ ? FM : NQ); ++i) {
       if (i < FM) {
         const int r = wm * (BM / 2) + i * 32 + (lane & 31);
         fa[slot][i] = __builtin_bit_cast(bf16x8_t, As[r * kKC + (ch ^ swz(r))]);
       }
-      const int q = SWIGLU ? ((i >> 1) * 128 + wn * 64 + (i & 1) * 32 + (lane & 31))
-                           : (wn * 128 + i * 32 + (lane & 31));
-      fb[slot][i] = __builtin_bit_cast(bf16x8_t, Bs[q * kKC + (ch ^ swz(q))]);
+      if (i < NQ) {
+        // SwiGLU: blocks [0, NQ/2) are this wave's W1 rows, [NQ/2, NQ) the
+        // matching W3 rows
+        const int q = SWIGLU ? ((i / (NQ / 2)) * HALF + wn * (HALF / 2) + (i % (NQ / 2)) * 32 +
+                                (lane & 31))
+                             : (wn * (BNW / 2) + i * 32 + (lane & 31));
+        fb[slot][i] = __builtin_bit_cast(bf16x8_t, Bs[q * kKC + (ch ^ swz(q))]);
+      }
     }
   };
   // Step p becomes readable: this wave's loads of step p are done once at most
@@ -236,19 +243,19 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
     issue_part(0, pb, pk);
   };
 
-  // instruction interleave of one substep: FM * 4 MFMAs with the FM + 4 LDS
+  // instruction interleave of one substep: FM * NQ MFMAs with the FM + NQ LDS
   // reads of the next substep and about LSTEP / kSUB global loads between them
-  constexpr int NMF = FM * 4, NDS = FM + 4, NVM = (LSTEP + kSUB - 1) / kSUB;
+  constexpr int NMF = FM * NQ, NDS = FM + NQ, NVM = (LSTEP + kSUB - 1) / kSUB;
   constexpr uint32_t kStepBytes = kBK * 2;  // K bytes of one step in a row
 
-  auto mfma_substep = [&](f32x16_t (&acc)[FM][4], int slot) {
+  auto mfma_substep = [&](f32x16_t (&acc)[FM][NQ], int slot) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
+      for (int q = 0; q < NQ; ++q)
         acc[i][q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i], fb[slot][q], acc[i][q], 0, 0, 0);
   };
-  auto epilogue = [&](const Tile& ct, f32x16_t (&acc)[FM][4]) {
+  auto epilogue = [&](const Tile& ct, f32x16_t (&acc)[FM][NQ]) {
     const int valid = min(BM, ct.seg1 - ct.m0);
     // registers -> global; D[m][n] of a 32x32 MFMA tile is in lane
     // n + 32 * ((m / 4) % 2), register 4 * (m / 8) + m % 4.  Stores address C
@@ -260,15 +267,15 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
       if (wm * (BM / 2) + i * 32 >= valid) continue;
       const int row0 = ct.m0 + wm * (BM / 2) + i * 32 + 4 * (lane >> 5);
 #pragma unroll
-      for (int q = 0; q < (SWIGLU ? 2 : 4); ++q) {
-        const int col = ct.n0 + (SWIGLU ? wn * 64 : wn * 128) + q * 32 + (lane & 31);
+      for (int q = 0; q < (SWIGLU ? NQ / 2 : NQ); ++q) {
+        const int col = ct.n0 + (SWIGLU ? wn * (HALF / 2) : wn * (BNW / 2)) + q * 32 + (lane & 31);
         const uint32_t base = (static_cast<uint32_t>(row0) * static_cast<uint32_t>(N) +
                                static_cast<uint32_t>(col)) * 2u;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int dm = 8 * (r >> 2) + (r & 3);
           float v = acc[i][q][r];
-          if constexpr (SWIGLU) v = silu_fast(v) * acc[i][q + 2][r];
+          if constexpr (SWIGLU) v = silu_fast(v) * acc[i][q + NQ / 2][r];
           if (row0 + dm < ct.seg1 && col < N)
             *reinterpret_cast<uint16_t*>(Cb + (base + static_cast<uint32_t>(dm * N) * 2u)) =
                 f32_to_bf16(v);
@@ -297,11 +304,11 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
 
     for (int j = 0; j < ntiles; ++j) {
       const Tile ct = decode_tile<BM, BN, CLASS>(vb + j * G, NT, prefix, segs, E_loc);
-      f32x16_t acc[FM][4];
+      f32x16_t acc[FM][NQ];
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[i][q] = f32x16_t{};
+        for (int q = 0; q < NQ; ++q) acc[i][q] = f32x16_t{};
       // one step: substep 0 fetches substep 1's fragments and the second
       // half of the pending step's loads between its MFMAs; substep 1 makes
       // step s + 1 readable (barrier), sends the first half of step
@@ -355,11 +362,11 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
     sync_and_issue(0);
     for (int j = 0; j < ntiles; ++j) {
       const Tile ct = decode_tile<BM, BN, CLASS>(vb + j * G, NT, prefix, segs, E_loc);
-      f32x16_t acc[FM][4];
+      f32x16_t acc[FM][NQ];
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[i][q] = f32x16_t{};
+        for (int q = 0; q < NQ; ++q) acc[i][q] = f32x16_t{};
       load_frags((j * KT) % STAGES, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
       for (int kt = 0; kt < KT; ++kt) {

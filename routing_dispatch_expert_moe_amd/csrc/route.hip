@@ -14,59 +14,83 @@ namespace moe {
 // ---------------------------------------------------------------------------
 // A0: logits[t][e] = sum_i x[t][i] * wg[i][e]; x bf16 (exact in fp32), wg fp32,
 // fp32 products and sums.
-// A workgroup takes 16 tokens; each token's 16 threads are 16 consecutive
-// lanes of one wave and split d into interleaved 8-element chunks (lane s
-// takes chunks s, s + 16, ...), so the 16 lanes of a token read 256
-// contiguous bytes of x per step and the 4 tokens of a wave share every wg
-// row they read.  Each thread keeps EB partial sums; the 16 partials of a
-// token meet in a fixed xor butterfly (deterministic).
+// A workgroup takes TPW = 64 / EB tokens (EB = E rounded up to 8, 16, 32 or
+// 64), so each lane's partial sums are TPW x EB = 64 values.  The 4 waves
+// split d into quarters; in a wave, lane c takes 8-element chunks c, c + 64,
+// ... of its quarter: the x loads of one token are 1 KB contiguous per wave,
+// and each wg row segment a lane loads serves all TPW tokens.  The 64 partial
+// sums are then reduce-scattered across the 64 lanes (6 xor rounds, halving
+// the values each round: lane l ends with the wave's total of value l) and
+// the 4 waves' totals are added in wave order through LDS.  Every sum has a
+// fixed order, so the result is deterministic.
 // ---------------------------------------------------------------------------
 template <int EB>
 __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __restrict__ x,
                                                             const float* __restrict__ wg,
                                                             int T, int d, int E,
                                                             float* __restrict__ logits) {
-  constexpr int S = 16;  // threads per token
-  const int s = threadIdx.x % S;
-  const int t = blockIdx.x * (256 / S) + threadIdx.x / S;
-  float acc[EB];
+  constexpr int TPW = 64 / EB;  // tokens per workgroup
+  __shared__ float part[4][64];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t0 = blockIdx.x * TPW;
+  const int nchunk = d >> 3;
+  const int per = (nchunk + 3) / 4;
+  const int c_lo = wave * per, c_hi = min(nchunk, c_lo + per);
+  const bool vec = (E & 3) == 0;  // wg rows are 16-byte aligned runs of E floats
+  float v[64];
 #pragma unroll
-  for (int e = 0; e < EB; ++e) acc[e] = 0.f;
-  if (t < T) {
-    const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)t * d);
-    const int nchunk = d >> 3;
-    constexpr int U = 4;  // chunks per thread in flight
-    for (int c0 = s; c0 < nchunk; c0 += U * S) {
-      uint4 xv[U];
+  for (int i = 0; i < 64; ++i) v[i] = 0.f;
+  for (int c = c_lo + lane; c < c_hi; c += kWave) {
+    float xf[TPW][8];
 #pragma unroll
-      for (int u = 0; u < U; ++u)
-        if (c0 + u * S < nchunk) xv[u] = xr[c0 + u * S];
+    for (int a = 0; a < TPW; ++a) {
+      if (t0 + a < T) {
+        unpack8(*reinterpret_cast<const uint4*>(x + (size_t)(t0 + a) * d + c * 8), xf[a]);
+      } else {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int c = c0 + u * S;
-        if (c >= nchunk) break;
-        float xf[8];
-        unpack8(xv[u], xf);
+        for (int i = 0; i < 8; ++i) xf[a][i] = 0.f;
+      }
+    }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float* wrow = wg + (size_t)(c * 8 + i) * E;
+    for (int i = 0; i < 8; ++i) {
+      const float* wrow = wg + (size_t)(c * 8 + i) * E;
 #pragma unroll
-          for (int e = 0; e < EB; ++e)
-            if (e < E) acc[e] = fmaf(xf[i], wrow[e], acc[e]);
+      for (int e4 = 0; e4 < EB / 4; ++e4) {
+        float w[4];
+        if (vec) {
+          float4 q = make_float4(0.f, 0.f, 0.f, 0.f);
+          if (e4 * 4 < E) q = reinterpret_cast<const float4*>(wrow)[e4];
+          w[0] = q.x; w[1] = q.y; w[2] = q.z; w[3] = q.w;
+        } else {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) w[u] = e4 * 4 + u < E ? wrow[e4 * 4 + u] : 0.f;
         }
+#pragma unroll
+        for (int a = 0; a < TPW; ++a)
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            v[a * EB + e4 * 4 + u] = fmaf(xf[a][i], w[u], v[a * EB + e4 * 4 + u]);
       }
     }
   }
-  // butterfly over the token's 16 lanes (all 64 lanes take part)
+  // reduce-scatter over the wave: after the round with mask m a lane keeps
+  // the upper half of its values if (lane & m), so lane l ends with value l
 #pragma unroll
-  for (int e = 0; e < EB; ++e) {
+  for (int m = 32, n = 64; m >= 1; m >>= 1, n >>= 1) {
+    const bool up = (lane & m) != 0;
 #pragma unroll
-    for (int off = 1; off < S; off <<= 1) acc[e] += __shfl_xor(acc[e], off, kWave);
+    for (int j = 0; j < n / 2; ++j) {
+      const float keep = up ? v[j + n / 2] : v[j];
+      const float give = up ? v[j] : v[j + n / 2];
+      v[j] = keep + __shfl_xor(give, m, kWave);
+    }
   }
-  if (t < T) {
-#pragma unroll
-    for (int e = 0; e < EB; ++e)
-      if (e % S == s && e < E) logits[(size_t)t * E + e] = acc[e];
+  part[wave][lane] = v[0];
+  __syncthreads();
+  if (wave == 0) {
+    const float sum = ((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane];
+    const int a = lane / EB, e = lane % EB;
+    if (t0 + a < T && e < E) logits[(size_t)(t0 + a) * E + e] = sum;
   }
 }
 
@@ -74,15 +98,15 @@ int launch_router_logits(const void* x, const float* wg, int T, int d, int E, fl
                          void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   const uint16_t* xb = static_cast<const uint16_t*>(x);
-  const dim3 grid((T + 15) / 16), block(256);
+  const dim3 block(256);
   if (E <= 8)
-    hipLaunchKernelGGL(router_logits_kernel<8>, grid, block, 0, s, xb, wg, T, d, E, logits);
+    hipLaunchKernelGGL(router_logits_kernel<8>, dim3((T + 7) / 8), block, 0, s, xb, wg, T, d, E, logits);
   else if (E <= 16)
-    hipLaunchKernelGGL(router_logits_kernel<16>, grid, block, 0, s, xb, wg, T, d, E, logits);
+    hipLaunchKernelGGL(router_logits_kernel<16>, dim3((T + 3) / 4), block, 0, s, xb, wg, T, d, E, logits);
   else if (E <= 32)
-    hipLaunchKernelGGL(router_logits_kernel<32>, grid, block, 0, s, xb, wg, T, d, E, logits);
+    hipLaunchKernelGGL(router_logits_kernel<32>, dim3((T + 1) / 2), block, 0, s, xb, wg, T, d, E, logits);
   else
-    hipLaunchKernelGGL(router_logits_kernel<64>, grid, block, 0, s, xb, wg, T, d, E, logits);
+    hipLaunchKernelGGL(router_logits_kernel<64>, dim3(T), block, 0, s, xb, wg, T, d, E, logits);
   return static_cast<int>(hipGetLastError());
 }
 
