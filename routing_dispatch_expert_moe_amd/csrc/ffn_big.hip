@@ -5,8 +5,12 @@
 
 namespace moe {
 
+// 256-row tiles run 8 waves (two per SIMD), the smaller tiles 4
+template <int BM>
+constexpr int pipe_waves() { return BM == 256 ? 8 : 4; }
+
 template <bool SWIGLU, int BM, int BNW, int STAGES, int CLASS>
-__global__ __launch_bounds__(256, 1) void gemm_bf16_pipe(const uint16_t* __restrict__ A,
+__global__ __launch_bounds__(pipe_waves<BM>() * 64, 1) void gemm_bf16_pipe(const uint16_t* __restrict__ A,
                                                          const int32_t* __restrict__ offsets,
                                                          int E_loc,
                                                          const uint16_t* __restrict__ W,
@@ -14,8 +18,8 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_pipe(const uint16_t* __restr
   extern __shared__ uint4 lds[];
   __shared__ int prefix[MOE_MAX_E + 1];
   __shared__ int segs[MOE_MAX_E + 1];
-  gemm_pipe_body<SWIGLU, BM, BNW, STAGES, CLASS>(A, offsets, E_loc, W, C, N, K, blockIdx.x,
-                                                 gridDim.x, lds, prefix, segs);
+  gemm_pipe_body<SWIGLU, BM, BNW, STAGES, CLASS, pipe_waves<BM>()>(
+      A, offsets, E_loc, W, C, N, K, blockIdx.x, gridDim.x, lds, prefix, segs);
 }
 
 namespace {
@@ -43,7 +47,7 @@ int launch_pipe(const void* A, const int32_t* offsets, int E_loc, int64_t max_ro
   if (grid > tiles_ub) grid = tiles_ub;
   if (grid >= 8) grid &= ~static_cast<int64_t>(7);
   if (grid < 1) grid = 1;
-  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(256), lds, s,
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(pipe_waves<BM>() * 64), lds, s,
                      static_cast<const uint16_t*>(A), offsets, E_loc,
                      static_cast<const uint16_t*>(W), static_cast<uint16_t*>(C), N, K);
   return static_cast<int>(hipGetLastError());

@@ -5,12 +5,14 @@
 // expert's rows against its fused [W1 | W3] operand with SwiGLU in the
 // epilogue; the second grouped GEMM applies W2.
 //
-// Tile: BM activation rows x 256 weight rows (SwiGLU: 128 W1 rows + the
-// matching 128 W3 rows -> 128 h columns).  4 waves split the tile 2 x 2; each
-// wave owns (BM / 2) x 128, i.e. BM / 64 x 4 MFMA tiles of 32 x 32.
-//   BM = 256  experts with many rows (MFMA-bound; 256 accumulators per lane);
-//   BM = 128 / 64  experts with few rows, where the weights stream from HBM
-//             and the smaller A tile leaves LDS for a deeper pipeline.
+// Tile: BM activation rows x BNW weight rows (SwiGLU: BNW/2 W1 rows + the
+// matching W3 rows -> BNW/2 h columns).  NW waves split the tile 2 x NW/2;
+// each wave owns (BM / 2) x (BNW / (NW/2)) in 32 x 32 MFMA tiles.
+//   BM = BNW = 256, NW = 8: experts with many rows (MFMA-bound; two waves per
+//             SIMD with 128 accumulators each, so one wave's waits are
+//             covered by the other's MFMAs);
+//   BM = 128, NW = 4: the short remainders, where the weights stream from
+//             HBM and the smaller tile leaves LDS for a deeper pipeline.
 //
 // Memory pipeline: operands go HBM/L2 -> LDS directly (global_load_lds_dwordx4,
 // no staging registers) in K-steps of 32 through STAGES LDS buffers, so loads
@@ -107,10 +109,11 @@ constexpr size_t pipe_lds_bytes(int BM, int BNW, int STAGES) {
 // One workgroup's share of the grouped GEMM: workgroup `bid` of `G` walks its
 // tiles.  lds: pipe_lds_bytes(BM, BNW, STAGES); prefix, segs: E_loc + 1 ints
 // of LDS each.  Every thread of the workgroup must call it (it has barriers).
-// BNW weight rows per tile (256 or 128; SwiGLU: half W1, half W3).
+// BNW weight rows per tile (256 or 128; SwiGLU: half W1, half W3).  NW waves
+// (4 or 8: one or two per SIMD) split the tile 2 x NW/2.
 // gather: if not null, activation row r is row gather[r] / gk of A (A rows
 // read in place through the dispatch permutation instead of a permuted copy).
-template <bool SWIGLU, int BM, int BNW, int STAGES, int CLASS>
+template <bool SWIGLU, int BM, int BNW, int STAGES, int CLASS, int NW = 4>
 __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
                                                const int32_t* __restrict__ offsets, int E_loc,
                                                const uint16_t* __restrict__ W,
@@ -121,9 +124,10 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
   constexpr int BN = SWIGLU ? BNW / 2 : BNW;  // output columns per tile
   constexpr int HALF = BNW / 2;               // SwiGLU: W1 rows (then as many W3 rows)
   constexpr int FM = BM / 64;                 // 32-row MFMA blocks per wave
-  constexpr int NQ = BNW / 64;                // 32-column MFMA blocks per wave
-  constexpr int LA = BM / kRPI / 4;           // A loads per wave per step
-  constexpr int LB = BNW / kRPI / 4;          // B loads per wave per step
+  constexpr int WN = NW / 2;                  // waves along the weight rows (2 along M)
+  constexpr int NQ = BNW / WN / 32;           // 32-column MFMA blocks per wave
+  constexpr int LA = BM / kRPI / NW;          // A loads per wave per step
+  constexpr int LB = BNW / kRPI / NW;         // B loads per wave per step
   constexpr int LSTEP = LA + LB;
   constexpr int STAGE_U4 = (BM + BNW) * kKC;
   static_assert(FM >= 1 && NQ >= 2 && LB % kSUB == 0, "unsupported tile");
@@ -145,7 +149,7 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
   // the wave index is uniform: keep it (and everything derived from it, such
   // as the M0 bases of the direct loads) in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
   const size_t wstride = static_cast<size_t>(SWIGLU ? 2 * N : N) * K;
   // LDS swizzle: chunk c of row r is stored at c ^ swz(r); swz spreads the 16
   // rows read by one 16-lane ds_read_b128 phase over all bank groups
@@ -164,14 +168,14 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
     iWb = reinterpret_cast<const char*>(W + t.e * wstride);
 #pragma unroll
     for (int i = 0; i < LA; ++i) {
-      const int rt = (i * 4 + wave) * kRPI + lane / kKC;  // row within the tile
+      const int rt = (i * NW + wave) * kRPI + lane / kKC;  // row within the tile
       int arow = min(t.m0 + rt, t.seg1 - 1);
       if (gather != nullptr) arow = gather[arow] / gk;
       aoff[i] = (static_cast<uint32_t>(arow) * K + lkc * 8) * 2u;
     }
 #pragma unroll
     for (int i = 0; i < LB; ++i) {
-      const int rt = (i * 4 + wave) * kRPI + lane / kKC;
+      const int rt = (i * NW + wave) * kRPI + lane / kKC;
       int wrow;
       if (SWIGLU) wrow = (rt / HALF) * N + min(t.n0 + rt % HALF, N - 1);
       else wrow = min(t.n0 + rt, N - 1);
@@ -187,12 +191,12 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
     for (int i = p * LA / kSUB; i < (p + 1) * LA / kSUB; ++i)
       __builtin_amdgcn_global_load_lds(
           (const __attribute__((address_space(1))) void*)(Ab + (aoff[i] + koff)),
-          (__attribute__((address_space(3))) void*)(As + (i * 4 + wave) * 64), 16, 0, 0);
+          (__attribute__((address_space(3))) void*)(As + (i * NW + wave) * 64), 16, 0, 0);
 #pragma unroll
     for (int i = p * LB / kSUB; i < (p + 1) * LB / kSUB; ++i)
       __builtin_amdgcn_global_load_lds(
           (const __attribute__((address_space(1))) void*)(iWb + (boff[i] + koff)),
-          (__attribute__((address_space(3))) void*)(Bs + (i * 4 + wave) * 64), 16, 0, 0);
+          (__attribute__((address_space(3))) void*)(Bs + (i * NW + wave) * 64), 16, 0, 0);
   };
   // byte offset along K of step p's operands, switching the issue tile when p
   // starts a new one; steps past the end re-fetch the last step (valid
@@ -219,9 +223,9 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
       if (i < NQ) {
         // SwiGLU: blocks [0, NQ/2) are this wave's W1 rows, [NQ/2, NQ) the
         // matching W3 rows
-        const int q = SWIGLU ? ((i / (NQ / 2)) * HALF + wn * (HALF / 2) + (i % (NQ / 2)) * 32 +
+        const int q = SWIGLU ? ((i / (NQ / 2)) * HALF + wn * (HALF / WN) + (i % (NQ / 2)) * 32 +
                                 (lane & 31))
-                             : (wn * (BNW / 2) + i * 32 + (lane & 31));
+                             : (wn * (BNW / WN) + i * 32 + (lane & 31));
         fb[slot][i] = __builtin_bit_cast(bf16x8_t, Bs[q * kKC + (ch ^ swz(q))]);
       }
     }
@@ -268,7 +272,7 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
       const int row0 = ct.m0 + wm * (BM / 2) + i * 32 + 4 * (lane >> 5);
 #pragma unroll
       for (int q = 0; q < (SWIGLU ? NQ / 2 : NQ); ++q) {
-        const int col = ct.n0 + (SWIGLU ? wn * (HALF / 2) : wn * (BNW / 2)) + q * 32 + (lane & 31);
+        const int col = ct.n0 + (SWIGLU ? wn * (HALF / WN) : wn * (BNW / WN)) + q * 32 + (lane & 31);
         const uint32_t base = (static_cast<uint32_t>(row0) * static_cast<uint32_t>(N) +
                                static_cast<uint32_t>(col)) * 2u;
 #pragma unroll
