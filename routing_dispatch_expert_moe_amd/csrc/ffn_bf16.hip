@@ -231,10 +231,12 @@ constexpr bool kDecodeSmallTiles = MOE_DECODE_SMALL_TILES != 0;
 constexpr int64_t kStreamRows = 48;
 
 // Rows per expert on average decide the kernels: with few rows per expert the
-// FFN is weight streaming and one small-tile kernel takes every row; otherwise
-// the large-tile kernel takes the full 256-row blocks and a small-tile kernel
-// the short remainders (ROWS_BIG / ROWS_TAIL), both reading the row counts on
-// the device.
+// FFN is weight streaming and one small-tile kernel takes every row.
+// Otherwise the 256-row-tile kernel takes each expert's rows; when the pass
+// has few, short tiles (few experts, K <= 4096) it also takes each expert's
+// last block, even when less than half full (that tile shares its weights
+// with the expert's other tiles through L2), else a small-tile kernel takes
+// the short remainders (ROWS_BIG / ROWS_TAIL).  Row counts stay on the device.
 int launch_ffn_up_bf16(const void* x_perm, const int32_t* offsets, int E_loc, int64_t max_rows,
                        int d, int f, const void* w13, void* h, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -250,6 +252,8 @@ int launch_ffn_up_bf16(const void* x_perm, const int32_t* offsets, int E_loc, in
       return launch_gemm<32, 128, 64, 1, 4, true, ROWS_ALL>(x_perm, offsets, E_loc, max_rows, w13, h, f, d, s);
     return launch_gemm_pipe_bf16(PipeRows::kAllRows, true, x_perm, offsets, E_loc, max_rows, w13, h, f, d, stream);
   }
+  if (remainders_with_big_tiles(E_loc, f, d, true))
+    return launch_gemm_pipe_bf16(PipeRows::kBigAll, true, x_perm, offsets, E_loc, max_rows, w13, h, f, d, stream);
   int e = launch_gemm_pipe_bf16(PipeRows::kBigTiles, true, x_perm, offsets, E_loc, max_rows, w13, h, f, d, stream);
   if (e != 0) return e;
   return launch_gemm_pipe_bf16(PipeRows::kTailTiles, true, x_perm, offsets, E_loc, max_rows, w13, h, f, d, stream);
@@ -269,6 +273,8 @@ int launch_ffn_down_bf16(const void* h, const int32_t* offsets, int E_loc, int64
       return launch_gemm<32, 128, 64, 1, 4, false, ROWS_ALL>(h, offsets, E_loc, max_rows, w2, y, d, f, s);
     return launch_gemm_pipe_bf16(PipeRows::kAllRows, false, h, offsets, E_loc, max_rows, w2, y, d, f, stream);
   }
+  if (remainders_with_big_tiles(E_loc, d, f, false))
+    return launch_gemm_pipe_bf16(PipeRows::kBigAll, false, h, offsets, E_loc, max_rows, w2, y, d, f, stream);
   int e = launch_gemm_pipe_bf16(PipeRows::kBigTiles, false, h, offsets, E_loc, max_rows, w2, y, d, f, stream);
   if (e != 0) return e;
   return launch_gemm_pipe_bf16(PipeRows::kTailTiles, false, h, offsets, E_loc, max_rows, w2, y, d, f, stream);

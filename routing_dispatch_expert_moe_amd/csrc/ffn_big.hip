@@ -65,10 +65,10 @@ int launch_kind(PipeRows rows, const void* A, const int32_t* offsets, int E_loc,
   switch (rows) {
     case PipeRows::kBigTiles:
       return launch_pipe<SWIGLU, 256, 256, 4, ROWS_BIG>(A, offsets, E_loc, max_rows, W, C, N, K, s);
+    case PipeRows::kBigAll:
+      return launch_pipe<SWIGLU, 256, 256, 4, ROWS_ALL>(A, offsets, E_loc, max_rows, W, C, N, K, s);
     case PipeRows::kTailTiles: {
-      const int64_t tiles256 = static_cast<int64_t>(E_loc) * ((N + (SWIGLU ? 127 : 255)) /
-                                                              (SWIGLU ? 128 : 256));
-      if (tiles256 >= 4 * static_cast<int64_t>(device_cu_count()))
+      if (!few_gemm_tiles(E_loc, N, SWIGLU))
         return launch_pipe<SWIGLU, 128, 256, 6, ROWS_TAIL>(A, offsets, E_loc, max_rows, W, C, N,
                                                             K, s);
       return launch_pipe<SWIGLU, kSmallBM, kSmallBNW, kSmallStages, ROWS_TAIL>(
@@ -81,6 +81,19 @@ int launch_kind(PipeRows rows, const void* A, const int32_t* offsets, int E_loc,
 }
 
 }  // namespace
+
+bool few_gemm_tiles(int E_loc, int N, bool swiglu) {
+  const int64_t tiles256 = static_cast<int64_t>(E_loc) * ((N + (swiglu ? 127 : 255)) /
+                                                          (swiglu ? 128 : 256));
+  return tiles256 < 4 * static_cast<int64_t>(device_cu_count());
+}
+
+bool remainders_with_big_tiles(int E_loc, int N, int K, bool swiglu) {
+  // with few tiles the remainder tiles would re-stream whole weight matrices,
+  // so they ride along with the expert's 256-row tiles; but a pass with long
+  // tiles (large K) pays a whole extra round for a few of them
+  return few_gemm_tiles(E_loc, N, swiglu) && K <= 4096;
+}
 
 int launch_gemm_pipe_bf16(PipeRows rows, bool swiglu, const void* A, const int32_t* offsets,
                           int E_loc, int64_t max_rows, const void* W, void* C, int N, int K,

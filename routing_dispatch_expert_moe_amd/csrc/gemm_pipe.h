@@ -34,6 +34,8 @@
 // tile ranges and shares weight tiles in its own L2.
 #pragma once
 
+#include <type_traits>
+
 #include "common.h"
 #include "tile_sched.h"
 
@@ -313,45 +315,62 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int q = 0; q < NQ; ++q) acc[i][q] = f32x16_t{};
-      // one step: substep 0 fetches substep 1's fragments and the second
-      // half of the pending step's loads between its MFMAs; substep 1 makes
-      // step s + 1 readable (barrier), sends the first half of step
-      // s + STAGES's loads into this step's buffer and fetches step s + 1's
-      // first fragments
-      auto substep0 = [&](int s) {
-        load_frags(s % STAGES, 1, 1);
-        issue_part(1, pb, pk);
-        mfma_substep(acc, 0);
-        interleave<0, NMF, NDS, NVM>();
-        __builtin_amdgcn_sched_barrier(0);
+      // The K loop of one tile.  ACT = false: this wave's rows of the tile
+      // are all past the segment (a tile less than half full), so it only
+      // helps with the loads and barriers and leaves its SIMD's MFMA pipe to
+      // the other wave there.
+      auto run_tile = [&](auto act) {
+        constexpr bool ACT = decltype(act)::value;
+        // one step: substep 0 fetches substep 1's fragments and the second
+        // half of the pending step's loads between its MFMAs; substep 1
+        // makes step s + 1 readable (barrier), sends the first half of step
+        // s + STAGES's loads into this step's buffer and fetches step
+        // s + 1's first fragments
+        auto substep0 = [&](int s) {
+          if constexpr (ACT) load_frags(s % STAGES, 1, 1);
+          issue_part(1, pb, pk);
+          if constexpr (ACT) {
+            mfma_substep(acc, 0);
+            interleave<0, NMF, NDS, NVM>();
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        };
+        auto substep1 = [&](int s, uint32_t koff_next) {
+          wait_vmcnt<(STAGES - 2) * LSTEP>();
+          asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+          pk = koff_next;
+          pb = s % STAGES;  // (s + STAGES) % STAGES
+          issue_part(0, pb, pk);
+          load_frags((s + 1) % STAGES, 0, 0);
+          if constexpr (ACT) {
+            mfma_substep(acc, 1);
+            interleave<0, NMF, NDS, NVM>();
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        };
+        const int s0 = j * KT;
+        for (int kt = 0; kt < KT - STAGES; ++kt) {
+          substep0(s0 + kt);
+          substep1(s0 + kt, (kt + STAGES) * kStepBytes);
+        }
+        // The last STAGES steps fetch the next tile's first steps (after the
+        // last tile: re-fetch this tile's last step, valid and unused).  The
+        // first of them still sends the second half of this tile's last
+        // step, so the issue side switches tiles between its two substeps.
+        const bool more = j + 1 < ntiles;
+        substep0(s0 + KT - STAGES);
+        if (more) set_issue_tile(j + 1);
+        substep1(s0 + KT - STAGES, more ? 0u : (KT - 1) * kStepBytes);
+        for (int kt = KT - STAGES + 1; kt < KT; ++kt) {
+          substep0(s0 + kt);
+          substep1(s0 + kt, more ? (kt + STAGES - KT) * kStepBytes : (KT - 1) * kStepBytes);
+        }
       };
-      auto substep1 = [&](int s, uint32_t koff_next) {
-        wait_vmcnt<(STAGES - 2) * LSTEP>();
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        pk = koff_next;
-        pb = s % STAGES;  // (s + STAGES) % STAGES
-        issue_part(0, pb, pk);
-        load_frags((s + 1) % STAGES, 0, 0);
-        mfma_substep(acc, 1);
-        interleave<0, NMF, NDS, NVM>();
-        __builtin_amdgcn_sched_barrier(0);
-      };
-      const int s0 = j * KT;
-      for (int kt = 0; kt < KT - STAGES; ++kt) {
-        substep0(s0 + kt);
-        substep1(s0 + kt, (kt + STAGES) * kStepBytes);
-      }
-      // The last STAGES steps fetch the next tile's first steps (after the
-      // last tile: re-fetch this tile's last step, valid and unused).  The
-      // first of them still sends the second half of this tile's last step,
-      // so the issue side switches tiles between its two substeps.
-      const bool more = j + 1 < ntiles;
-      substep0(s0 + KT - STAGES);
-      if (more) set_issue_tile(j + 1);
-      substep1(s0 + KT - STAGES, more ? 0u : (KT - 1) * kStepBytes);
-      for (int kt = KT - STAGES + 1; kt < KT; ++kt) {
-        substep0(s0 + kt);
-        substep1(s0 + kt, more ? (kt + STAGES - KT) * kStepBytes : (KT - 1) * kStepBytes);
+      if constexpr (NW == 8) {
+        if (wm * (BM / 2) < ct.seg1 - ct.m0) run_tile(std::true_type{});
+        else run_tile(std::false_type{});
+      } else {
+        run_tile(std::true_type{});
       }
       epilogue(ct, acc);
     }

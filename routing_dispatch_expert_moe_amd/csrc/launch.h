@@ -33,9 +33,18 @@ int launch_ffn_up_bf16(const void* x_perm, const int32_t* offsets, int E_loc, in
 int launch_ffn_down_bf16(const void* h, const int32_t* offsets, int E_loc, int64_t max_rows,
                          int d, int f, const void* w2, void* y, void* stream);
 // Pipelined direct-to-LDS grouped GEMM over one row class: 256-row tiles over
-// each expert's full blocks, smaller tiles over the short remainders, or
-// smaller tiles over every row.
-enum class PipeRows { kBigTiles, kTailTiles, kAllRows };
+// each expert's full blocks (kBigTiles), 256-row tiles over every row with
+// the last block of an expert as a possibly half-empty tile (kBigAll),
+// smaller tiles over the short remainders (kTailTiles), or smaller tiles over
+// every row (kAllRows).
+enum class PipeRows { kBigTiles, kBigAll, kTailTiles, kAllRows };
+// true when one GEMM pass over E_loc experts with N output columns gives few
+// tiles (fewer than 4 per CU with 256-row weight tiles): then remainders ride
+// along with the 256-row tiles instead of a second kernel re-streaming weights
+bool few_gemm_tiles(int E_loc, int N, bool swiglu);
+// whether a pass runs every row in 256-row tiles (kBigAll) rather than
+// 256-row tiles plus a remainder kernel
+bool remainders_with_big_tiles(int E_loc, int N, int K, bool swiglu);
 int launch_gemm_pipe_bf16(PipeRows rows, bool swiglu, const void* A, const int32_t* offsets,
                           int E_loc, int64_t max_rows, const void* W, void* C, int N, int K,
                           void* stream);
