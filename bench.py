@@ -65,8 +65,12 @@ def parse():
 # and the bench reports null.
 
 DOMINANT = "moe_ffn_up"                         # one GEMM1 + SwiGLU pass over all local rows
-DOMINANT_KERNELS = ("gemm_bf16_pipe<true",)     # the kernels that pass launches (demangled prefix)
+# the kernels that pass launches (demangled name prefixes): the pipelined
+# 256-row / remainder kernels, the register-staged few-rows kernel, fp32
+DOMINANT_KERNELS = ("gemm_bf16_pipe<true", "gemm_bf16_kernel<32, 128, 64, 1, 4, true",
+                    "gemm_f32_kernel<true")
 DOMINANT_SOURCES = ("routing_dispatch_expert_moe_amd/csrc/ffn_big.hip",
+                    "routing_dispatch_expert_moe_amd/csrc/gemm_pipe.h",
                     "routing_dispatch_expert_moe_amd/csrc/ffn_bf16.hip",
                     "routing_dispatch_expert_moe_amd/csrc/tile_sched.h",
                     "routing_dispatch_expert_moe_amd/csrc/common.h")
@@ -348,17 +352,29 @@ def main():
 
     dom = "ffn_up"
     dom_ms = per[dom]["ms"]
-    dom_fl = model[dom][0]
-    achieved = dom_fl / (dom_ms * 1e-3) / 1e12
+    dom_fl, dom_by = model[dom]
     traffic, traffic_note = load_traffic(args)
-    roofline = {"bound": "mfma", "kernel": f"{DOMINANT}: gemm_bf16_pipe<SwiGLU> over each "
-                                           "expert's 256-row blocks + its remainder tiles",
-                "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+    # the pass is bound by whichever of its algorithmic flops and bytes takes
+    # longer at peak: MFMA with many rows per expert, HBM (weight streaming)
+    # with few
+    if dom_fl / (PEAK_BF16_TFLOPS * 1e12) >= dom_by / (PEAK_HBM_GBS * 1e9):
+        bound, achieved, peak, unit = ("mfma", dom_fl / (dom_ms * 1e-3) / 1e12,
+                                       PEAK_BF16_TFLOPS, "TFLOP/s")
+    else:
+        bound, achieved, peak, unit = ("hbm", dom_by / (dom_ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s")
+    if wl.dtype != "bf16":
+        kernel = f"{DOMINANT}: gemm_f32_kernel<SwiGLU>"
+    elif layer.plan.max_rows // wl.E_loc <= 48:   # the launcher's few-rows rule
+        kernel = f"{DOMINANT}: gemm_bf16_kernel<SwiGLU>, 32-row tiles over every row"
+    else:
+        kernel = f"{DOMINANT}: gemm_bf16_pipe<SwiGLU>, 256-row tiles (+ remainder tiles)"
+    roofline = {"bound": bound, "kernel": kernel,
+                "achieved": round(achieved, 1), "peak": peak, "unit": unit,
+                "frac": round(achieved / peak, 4),
                 "traffic": round(traffic) if traffic is not None else None,
                 "traffic_note": traffic_note,
                 "algorithmic_flops_per_launch": dom_fl,
-                "algorithmic_bytes_per_launch": model[dom][1], "avg_launch_ms": dom_ms}
+                "algorithmic_bytes_per_launch": dom_by, "avg_launch_ms": dom_ms}
 
     cpu = None
     if not args.no_cpu_baseline:

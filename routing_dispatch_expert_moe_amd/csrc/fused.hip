@@ -51,6 +51,9 @@ constexpr uint32_t kSpinLimit = 1u << 21;
 // device-wide), polls are relaxed loads, and one acquire fence follows the
 // wait, so waiting does not keep invalidating the L2.
 __device__ __forceinline__ void grid_barrier(const FusedArgs& a, uint32_t G) {
+  // every wave's stores reach the L2 before the workgroup arrives (the
+  // arrival's release writes the L2 back; it does not wait for other waves)
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) {
     // the generation is read before arriving: it cannot advance until every
