@@ -315,6 +315,21 @@ def main():
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
 
+    # the same steps with the 256 MB Infinity Cache (MALL) evicted before each:
+    # a 1 GiB write between steps, outside the events, so that no step starts
+    # with its inputs or weights cache-resident (per-step HIP-event times)
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    cev = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    for s in range(args.steps):
+        scratch.fill_(s & 0xFF)
+        step(cev[s])
+    torch.cuda.synchronize()
+    del scratch
+    cold_ms = {name: float(np.median([cev[s][i].elapsed_time(cev[s][i + 1])
+                                      for s in range(args.steps)]))
+               for i, name in enumerate(STEPS)}
+    cold_step = float(np.median([cev[s][0].elapsed_time(cev[s][6]) for s in range(args.steps)]))
+
     # the same layer as one fused persistent launch (router logits stay a separate call)
     fev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
 
@@ -339,6 +354,9 @@ def main():
 
     per = {}
     model = work_model(wl, n, touched, T_read)
+    cold = {name: {"ms": round(ms, 5),
+                   "gbs": round(model[name][1] / (ms * 1e-3) / 1e9, 1) if model[name][1] else None}
+            for name, ms in cold_ms.items()}
     for i, name in enumerate(STEPS):
         ms = float(np.mean([events[s][i].elapsed_time(events[s][i + 1]) for s in range(args.steps)]))
         fl, by = model[name]
@@ -396,6 +414,10 @@ def main():
         "layer_tflops": round(tflops, 2), "layer_mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
         "layer_hbm_gbs": round(gbs, 1), "layer_hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
         "per_step": per, "roofline": roofline, "cpu_baseline": cpu,
+        "mall_flushed": {"ms_per_step_median": round(cold_step, 4),
+                         "per_step_median": cold,
+                         "note": "1 GiB written between steps (outside the events) to evict "
+                                 "the 256 MB Infinity Cache; HIP-event times per call"},
         "fused": {"entry": "moe_forward_fused", "ms_per_step_median": round(fused_ms, 4),
                   "tokens_per_s": round(wl.T / (fused_ms * 1e-3), 1),
                   "unfused_ms_per_step_median": round(unfused_ms, 4),
