@@ -42,6 +42,10 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="mixtral_prefill")
+    p.add_argument("--weights", choices=("native", "fp8"), default="native",
+                   help="fp8: quantise the packed bf16 expert weights to E4M3 codes with "
+                        "128 x 128 block scales (moe_quantize_fp8, untimed) and run the FFN "
+                        "steps on them")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-tokens", type=int, default=256)
     p.add_argument("--traffic", default=None,
@@ -153,6 +157,8 @@ def traffic_from(args):
 
 
 def load_traffic(args):
+    if getattr(args, "weights", "native") != "native":
+        return None, "counters were taken with the native-precision weights"
     path = args.traffic or os.path.join(ROOT, "profiles", f"traffic_{args.workload}.json")
     if not os.path.exists(path):
         return None, "no counter file"
@@ -174,17 +180,21 @@ def bf16_dev(a, dev):
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
 
 
-def work_model(wl, n, touched, T_read):
-    """Algorithmic flops and HBM bytes per launch of each step."""
+def work_model(wl, n, touched, T_read, wb=None):
+    """Algorithmic flops and HBM bytes per launch of each step (wb: bytes per
+    weight element when it differs from the activations', e.g. 1 for FP8
+    codes; their block scales add 4 B per 128 x 128 block)."""
     b = 2 if wl.dtype == "bf16" else 4
+    if wb is None:
+        wb = b
     T, d, f, E, k = wl.T, wl.d, wl.f, wl.E, wl.k
     m = {
         "router": (2.0 * T * d * E if wl.w_gate is not None else 0.0,
                    (T * d * b + d * E * 4 + T * E * 4) if wl.w_gate is not None else 0.0),
         "route": (0.0, T * E * 4 + T * k * 8),
         "dispatch": (0.0, 12.0 * T * k + T_read * d * b + n * d * b),
-        "ffn_up": (4.0 * n * d * f, touched * 2.0 * f * d * b + n * d * b + n * f * b),
-        "ffn_down": (2.0 * n * f * d, touched * 1.0 * d * f * b + n * f * b + n * d * b),
+        "ffn_up": (4.0 * n * d * f, touched * 2.0 * f * d * wb + n * d * b + n * f * b),
+        "ffn_down": (2.0 * n * f * d, touched * 1.0 * d * f * wb + n * f * b + n * d * b),
         "combine": (0.0, n * d * b + T * k * 8 + T * d * b),
     }
     return m
@@ -265,7 +275,19 @@ def main():
     log("weights packed")
 
     C = M.moe_capacity(wl.T, wl.k, wl.E, wl.capacity_factor)
+    fp8 = args.weights == "fp8"
+    if fp8:
+        if wl.dtype != "bf16":
+            raise SystemExit("--weights fp8 needs a bf16 workload")
+        q13, s13 = M.moe_quantize_fp8(w13)
+        q2, s2 = M.moe_quantize_fp8(w2p)
+        torch.cuda.synchronize()
+        del w13, w2p
+        torch.cuda.empty_cache()
+        w13, w2p = q13, q2
+        log("weights quantised to E4M3 with 128 x 128 block scales")
     layer = M.MoELayer(w13, w2p, E=wl.E, k=wl.k, gate=wl.gate, T=wl.T, capacity=C,
+                       w13_scale=s13 if fp8 else None, w2_scale=s2 if fp8 else None,
                        e_begin=wl.e_begin, e_end=wl.e_end)
     x = up(wl.x)
     logits = torch.from_numpy(wl.logits).to(dev) if wl.logits is not None else None
@@ -341,19 +363,21 @@ def main():
         if ev is not None:
             ev[1].record()
 
-    for _ in range(args.warmup):
-        fused_step()
-    torch.cuda.synchronize()
-    for s in range(args.steps):
-        fused_step(fev[s])
-    torch.cuda.synchronize()
-    if M.moe_check_error(layer.ws) != 0:
-        raise RuntimeError("device error in the fused layer")
-    fused_ms = float(np.median([e[0].elapsed_time(e[1]) for e in fev]))
+    fused_ms = None
+    if not fp8:   # the fused launch takes bf16 / fp32 weights
+        for _ in range(args.warmup):
+            fused_step()
+        torch.cuda.synchronize()
+        for s in range(args.steps):
+            fused_step(fev[s])
+        torch.cuda.synchronize()
+        if M.moe_check_error(layer.ws) != 0:
+            raise RuntimeError("device error in the fused layer")
+        fused_ms = float(np.median([e[0].elapsed_time(e[1]) for e in fev]))
     unfused_ms = float(np.median([events[s][0].elapsed_time(events[s][6]) for s in range(args.steps)]))
 
     per = {}
-    model = work_model(wl, n, touched, T_read)
+    model = work_model(wl, n, touched, T_read, wb=(1 + 4.0 / (128 * 128)) if fp8 else None)
     cold = {name: {"ms": round(ms, 5),
                    "gbs": round(model[name][1] / (ms * 1e-3) / 1e9, 1) if model[name][1] else None}
             for name, ms in cold_ms.items()}
@@ -383,7 +407,10 @@ def main():
     if wl.dtype != "bf16":
         kernel = f"{DOMINANT}: gemm_f32_kernel<SwiGLU>"
     elif layer.plan.max_rows // wl.E_loc <= 48:   # the launcher's few-rows rule
-        kernel = f"{DOMINANT}: gemm_bf16_kernel<SwiGLU>, 32-row tiles over every row"
+        kernel = (f"{DOMINANT}: gemm_bf16_kernel<SwiGLU{', FP8 weights' if fp8 else ''}>, "
+                  "32-row tiles over every row")
+    elif fp8:
+        kernel = f"{DOMINANT}: gemm_bf16_kernel<SwiGLU, FP8 weights>, 64-row tiles"
     else:
         kernel = f"{DOMINANT}: gemm_bf16_pipe<SwiGLU>, 256-row tiles (+ remainder tiles)"
     roofline = {"bound": bound, "kernel": kernel,
@@ -410,7 +437,8 @@ def main():
         "dtype": "bf16" if wl.dtype == "bf16" else "f32", "data": "synthetic",
         "config": {"workload": wl.name, "tokens": wl.T, "d_model": wl.d, "d_ff": wl.f,
                    "experts": wl.E, "local_experts": wl.E_loc, "top_k": wl.k, "gate": wl.gate,
-                   "capacity": C, "parallelism": "single GPU"},
+                   "capacity": C, "parallelism": "single GPU",
+                   "weights": "e4m3 codes, fp32 scale per 128x128 block" if fp8 else wl.dtype},
         "layer_tflops": round(tflops, 2), "layer_mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
         "layer_hbm_gbs": round(gbs, 1), "layer_hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
         "per_step": per, "roofline": roofline, "cpu_baseline": cpu,
@@ -418,10 +446,11 @@ def main():
                          "per_step_median": cold,
                          "note": "1 GiB written between steps (outside the events) to evict "
                                  "the 256 MB Infinity Cache; HIP-event times per call"},
-        "fused": {"entry": "moe_forward_fused", "ms_per_step_median": round(fused_ms, 4),
-                  "tokens_per_s": round(wl.T / (fused_ms * 1e-3), 1),
-                  "unfused_ms_per_step_median": round(unfused_ms, 4),
-                  "speedup_vs_unfused": round(unfused_ms / fused_ms, 3)},
+        "fused": None if fused_ms is None else {
+            "entry": "moe_forward_fused", "ms_per_step_median": round(fused_ms, 4),
+            "tokens_per_s": round(wl.T / (fused_ms * 1e-3), 1),
+            "unfused_ms_per_step_median": round(unfused_ms, 4),
+            "speedup_vs_unfused": round(unfused_ms / fused_ms, 3)},
     }
     print(json.dumps(line), flush=True)
 

@@ -175,6 +175,38 @@ moe_status moe_ffn_down(const void* h, const int32_t* offsets, int E_loc, int64_
                         int d, int f, moe_dtype dtype, const void* w2_packed, void* y_perm,
                         void* ws, size_t ws_bytes, void* stream);
 
+/* FP8 expert weights (NCCL EP page §2.1, expert-compute stage: FP8 compute
+ * with a scale tensor).  The page fixes neither format nor scale shape; this
+ * library uses E4M3-FN codes (OCP FP8, gfx950's FP8 type: bias 7, 3 mantissa
+ * bits, largest magnitude 448, no infinities) and one fp32 scale per block of
+ * 128 rows x 128 K-columns of each expert's packed weight matrix.
+ *
+ * moe_quantize_fp8: packed bf16 weights w_packed [E_loc][rows][K] (the
+ * moe_pack_weights layout: rows = 2f, K = d for w13; rows = d, K = f for w2)
+ * -> codes q [E_loc][rows][K] (uint8) and scales [E_loc][rows/128][K/128]
+ * (fp32).  Per block: amax = max |w|; scale = amax / 448 (fp32, correctly
+ * rounded; 1 for an all-zero block); q = E4M3(w / scale) rounded to nearest
+ * even, saturated at +-448.  rows and K must be multiples of 128
+ * (MOE_ERR_UNSUPPORTED); pointers 16-byte aligned; outputs must not alias the
+ * input.  One-time, like moe_pack_weights. */
+moe_status moe_quantize_fp8(const void* w_packed, int E_loc, int rows, int K, uint8_t* q,
+                            float* scales, void* stream);
+
+/* moe_expert_ffn with FP8 weights: the same operation and row layout, bf16
+ * activations (x_perm, h, y_perm) and fp32 accumulation, the weights being
+ * code value * block scale (each turned into bf16 as the weight tile is
+ * staged).  d and f must be multiples of 128.  No workspace. */
+moe_status moe_expert_ffn_fp8(const void* x_perm, const int32_t* offsets, int E_loc,
+                              int64_t max_rows, int d, int f, const uint8_t* w13_q,
+                              const float* w13_s, const uint8_t* w2_q, const float* w2_s,
+                              void* h, void* y_perm, void* stream);
+moe_status moe_ffn_up_fp8(const void* x_perm, const int32_t* offsets, int E_loc, int64_t max_rows,
+                          int d, int f, const uint8_t* w13_q, const float* w13_s, void* h,
+                          void* stream);
+moe_status moe_ffn_down_fp8(const void* h, const int32_t* offsets, int E_loc, int64_t max_rows,
+                            int d, int f, const uint8_t* w2_q, const float* w2_s, void* y_perm,
+                            void* stream);
+
 /* Weighted combine (NCCL EP page §2.1, LL combine):
  *   y[t] = sum_{j=0..k-1, pair_pos[t*k+j] >= 0} topk_w[t][j] * y_perm[pair_pos[t*k+j]]
  * accumulated in fp32 in ascending j, rounded once to `dtype`; tokens with no

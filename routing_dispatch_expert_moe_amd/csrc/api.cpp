@@ -50,6 +50,17 @@ moe_status check_ffn(const void* a, const int32_t* offsets, int E_loc, int64_t m
   return MOE_OK;
 }
 
+// FP8-weight FFN rules: bf16 activations, d and f multiples of the 128 x 128 scale blocks
+moe_status check_ffn_fp8(const void* a, const int32_t* offsets, int E_loc, int64_t max_rows,
+                         int d, int f, const void* wq, const float* ws, const void* out) {
+  moe_status st = check_ffn(a, offsets, E_loc, max_rows, d, f, MOE_BF16, wq, out);
+  if (st != MOE_OK) return st;
+  if (d % 128 != 0 || f % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  if (!ws) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(ws)) return MOE_ERR_MISALIGNED;
+  return MOE_OK;
+}
+
 }  // namespace
 
 namespace moe {
@@ -233,6 +244,46 @@ moe_status moe_expert_ffn(const void* x_perm, const int32_t* offsets, int E_loc,
   if (st != MOE_OK) return st;
   return moe_ffn_down(h, offsets, E_loc, max_rows, d, f, dtype, w2_packed, y_perm, ws, ws_bytes,
                       stream);
+}
+
+moe_status moe_quantize_fp8(const void* w_packed, int E_loc, int rows, int K, uint8_t* q,
+                            float* scales, void* stream) {
+  if (E_loc < 1 || rows < 1 || K < 1 || !w_packed || !q || !scales) return MOE_ERR_INVALID_ARG;
+  if (rows % 128 != 0 || K % 128 != 0 || E_loc > 65535) return MOE_ERR_UNSUPPORTED;
+  if (!aligned16(w_packed) || !aligned16(q) || !aligned16(scales)) return MOE_ERR_MISALIGNED;
+  return hip_status(moe::launch_quantize_fp8(w_packed, E_loc, rows, K, q, scales, stream));
+}
+
+
+moe_status moe_ffn_up_fp8(const void* x_perm, const int32_t* offsets, int E_loc, int64_t max_rows,
+                          int d, int f, const uint8_t* w13_q, const float* w13_s, void* h,
+                          void* stream) {
+  moe_status st = check_ffn_fp8(x_perm, offsets, E_loc, max_rows, d, f, w13_q, w13_s, h);
+  if (st != MOE_OK) return st;
+  return hip_status(moe::launch_ffn_up_fp8(x_perm, offsets, E_loc, max_rows, d, f, w13_q, w13_s,
+                                           h, stream));
+}
+
+moe_status moe_ffn_down_fp8(const void* h, const int32_t* offsets, int E_loc, int64_t max_rows,
+                            int d, int f, const uint8_t* w2_q, const float* w2_s, void* y_perm,
+                            void* stream) {
+  moe_status st = check_ffn_fp8(h, offsets, E_loc, max_rows, d, f, w2_q, w2_s, y_perm);
+  if (st != MOE_OK) return st;
+  return hip_status(moe::launch_ffn_down_fp8(h, offsets, E_loc, max_rows, d, f, w2_q, w2_s,
+                                             y_perm, stream));
+}
+
+moe_status moe_expert_ffn_fp8(const void* x_perm, const int32_t* offsets, int E_loc,
+                              int64_t max_rows, int d, int f, const uint8_t* w13_q,
+                              const float* w13_s, const uint8_t* w2_q, const float* w2_s,
+                              void* h, void* y_perm, void* stream) {
+  moe_status st = check_ffn_fp8(x_perm, offsets, E_loc, max_rows, d, f, w13_q, w13_s, h);
+  if (st != MOE_OK) return st;
+  st = check_ffn_fp8(h, offsets, E_loc, max_rows, d, f, w2_q, w2_s, y_perm);
+  if (st != MOE_OK) return st;
+  st = moe_ffn_up_fp8(x_perm, offsets, E_loc, max_rows, d, f, w13_q, w13_s, h, stream);
+  if (st != MOE_OK) return st;
+  return moe_ffn_down_fp8(h, offsets, E_loc, max_rows, d, f, w2_q, w2_s, y_perm, stream);
 }
 
 moe_status moe_combine(const void* y_perm, const int32_t* pair_pos, const float* topk_w, int T,

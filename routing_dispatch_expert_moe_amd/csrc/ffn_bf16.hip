@@ -22,6 +22,7 @@
 // round-robin over the 8 XCDs) owns contiguous tile ranges and the tiles that
 // share a weight tile meet in the same L2.
 #include "common.h"
+#include "fp8_dev.h"
 #include "launch.h"
 #include "tile_sched.h"
 
@@ -29,10 +30,19 @@ namespace moe {
 
 __device__ __forceinline__ float silu_f(float a) { return a * __builtin_amdgcn_rcpf(1.f + __expf(-a)); }
 
-template <int BM, int BN, int BK, int WM, int WN, bool SWIGLU, int CLASS>
+// FP8W: the weights are E4M3 codes (one byte each) with one fp32 scale per
+// 128 x 128 block of the packed matrix (Ws: [E][rows / 128][K / 128]) (NCCL
+// EP page §2.1: FP8 expert compute with a scale tensor).  Codes become bf16
+// exactly (every E4M3 value is a bf16 value) as the weight tile is staged
+// into LDS; the MFMAs accumulate each 128-deep K block into a partial sum,
+// which is multiplied by its block's scale and added to the result, so the
+// scale costs one fp32 FMA per output element and K block.  A 32 x 32 MFMA
+// tile's columns lie in one 128-row block, so its scale is uniform.
+template <int BM, int BN, int BK, int WM, int WN, bool SWIGLU, int CLASS, bool FP8W = false>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets, int E_loc,
-    const uint16_t* __restrict__ W, uint16_t* __restrict__ C, int N, int K) {
+    const void* __restrict__ Wv, const float* __restrict__ Ws, uint16_t* __restrict__ C, int N,
+    int K) {
   constexpr int NTHR = WM * WN * 64;
   constexpr int BNW = SWIGLU ? 2 * BN : BN;  // weight rows per tile
   constexpr int KC = BK / 8;                 // 16-byte chunks per tile row
@@ -42,6 +52,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(
   constexpr int CB = BNW * KC / NTHR;        // B chunks per thread per stage
   static_assert(BM * KC % NTHR == 0 && BNW * KC % NTHR == 0, "tile / thread mismatch");
   static_assert(TM % 32 == 0 && TN % 32 == 0 && BK % 16 == 0, "MFMA tiling");
+  static_assert(!FP8W || kFp8Block % BK == 0, "a K-step stays inside one scale block");
 
   extern __shared__ uint4 lds[];
   uint4* As = lds;                      // [2][BM * KC]
@@ -61,6 +72,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(
   const int wm = wave / WN, wn = wave % WN;
   const int KT = K / BK;
   const size_t wstride = static_cast<size_t>(SWIGLU ? 2 * N : N) * K;
+  const uint16_t* W = static_cast<const uint16_t*>(Wv);
+  const uint8_t* Wq = static_cast<const uint8_t*>(Wv);
+  const int KB = K / kFp8Block;                               // scale blocks along K
+  const int RB = (SWIGLU ? 2 * N : N) / kFp8Block;            // scale blocks along the rows
 
   for (int tile = vb; tile < total; tile += G) {
     const int mt = tile / NT;  // global M-tile index ... expert from prefix
@@ -75,6 +90,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(
     const int m0 = seg0 + mti * BM;
     const int n0 = nt * BN;
     const uint16_t* We = W + e * wstride;
+    const uint8_t* Wqe = Wq + e * wstride;
 
     // per-thread load descriptors
     const uint16_t* a_src[CA];
@@ -90,6 +106,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(
       a_dst[i] = r * KC + (kc ^ ((r >> 1) & (KC - 1)));
     }
     const uint16_t* b_src[CB];
+    const uint8_t* bq_src[CB];
     bool b_ok[CB];
     int b_dst[CB];
 #pragma unroll
@@ -99,44 +116,77 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(
       const int half = SWIGLU ? (r / BN) : 0;
       const int n = n0 + (r % BN);
       b_ok[i] = n < N;
-      b_src[i] = We + (static_cast<size_t>(half) * N + (b_ok[i] ? n : 0)) * K + kc * 8;
+      const size_t wrow = static_cast<size_t>(half) * N + (b_ok[i] ? n : 0);
+      b_src[i] = We + wrow * K + kc * 8;
+      bq_src[i] = Wqe + wrow * K + kc * 8;
       b_dst[i] = r * KC + (kc ^ ((r >> 1) & (KC - 1)));
     }
 
     f32x16_t acc[FM][FN];
     f32x16_t accg[SWIGLU ? FM : 1][SWIGLU ? FN : 1];
+    // FP8W: partial sums of the current 128-deep K block (before its scale)
+    f32x16_t part[FP8W ? FM : 1][FP8W ? FN : 1];
+    f32x16_t partg[FP8W && SWIGLU ? FM : 1][FP8W && SWIGLU ? FN : 1];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         acc[i][j] = f32x16_t{};
         if constexpr (SWIGLU) accg[i][j] = f32x16_t{};
+        if constexpr (FP8W) part[i][j] = f32x16_t{};
+        if constexpr (FP8W && SWIGLU) partg[i][j] = f32x16_t{};
       }
 
     const bool wave_active = m0 + wm * TM < seg1;
     uint4 ra[CA], rb[CB];
-    auto gload = [&](int kt) {
+    uint2 rq0[FP8W ? CB : 1];  // FP8W: the codes of the next K-step
+    // Loads are unconditional (rows past the segment or the matrix read a
+    // valid row instead) and the unused values are zeroed afterwards: no
+    // branch separates the loads, so the waits for one K-step's data leave
+    // the next step's loads in flight.
+    auto sel4 = [](bool ok, uint4 v) {
+      return make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u);
+    };
+    auto gload_a = [&](int kt) {
       const int koff = kt * BK;
 #pragma unroll
-      for (int i = 0; i < CA; ++i)
-        ra[i] = a_ok[i] ? *reinterpret_cast<const uint4*>(a_src[i] + koff) : make_uint4(0, 0, 0, 0);
+      for (int i = 0; i < CA; ++i) ra[i] = *reinterpret_cast<const uint4*>(a_src[i] + koff);
+    };
+    auto gload_b = [&](int kt) {
+      const int koff = kt * BK;
 #pragma unroll
-      for (int i = 0; i < CB; ++i)
-        rb[i] = b_ok[i] ? *reinterpret_cast<const uint4*>(b_src[i] + koff) : make_uint4(0, 0, 0, 0);
+      for (int i = 0; i < CB; ++i) rb[i] = *reinterpret_cast<const uint4*>(b_src[i] + koff);
+    };
+    auto gload_q = [&](int kt, uint2 (&rq)[FP8W ? CB : 1]) {
+      const int koff = kt * BK;
+#pragma unroll
+      for (int i = 0; i < CB; ++i)  // 8 codes (8 bytes) per chunk
+        rq[i] = *reinterpret_cast<const uint2*>(bq_src[i] + koff);
     };
     auto sstore = [&](int buf) {
 #pragma unroll
-      for (int i = 0; i < CA; ++i) As[buf * BM * KC + a_dst[i]] = ra[i];
+      for (int i = 0; i < CA; ++i) As[buf * BM * KC + a_dst[i]] = sel4(a_ok[i], ra[i]);
 #pragma unroll
-      for (int i = 0; i < CB; ++i) Bs[buf * BNW * KC + b_dst[i]] = rb[i];
+      for (int i = 0; i < CB; ++i) Bs[buf * BNW * KC + b_dst[i]] = sel4(b_ok[i], rb[i]);
+    };
+    // E4M3 -> bf16 into the staging registers, two codes per conversion
+    // (exact; unit scale)
+    auto convert = [&](const uint2 (&rq)[FP8W ? CB : 1]) {
+#pragma unroll
+      for (int i = 0; i < (FP8W ? CB : 0); ++i) {
+        const int x = static_cast<int>(rq[i].x), y = static_cast<int>(rq[i].y);
+        rb[i] = make_uint4(
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.f, false)),
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.f, true)),
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(y, 1.f, false)),
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(y, 1.f, true)));
+      }
     };
 
-    gload(0);
-    sstore(0);
-    __syncthreads();
-    for (int kt = 0; kt < KT; ++kt) {
+    // the MFMAs of K-step kt from LDS buffer kt & 1 (FP8W: into the block's
+    // partial sums, scaled into the result at the end of each 128-deep block)
+    auto compute = [&](int kt) {
       const int buf = kt & 1;
-      if (kt + 1 < KT) gload(kt + 1);
       const uint4* Ab = As + buf * BM * KC;
       const uint4* Bb = Bs + buf * BNW * KC;
 #pragma unroll
@@ -163,13 +213,70 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(
         for (int i = 0; i < FM; ++i)
 #pragma unroll
           for (int j = 0; j < FN; ++j) {
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
-            if constexpr (SWIGLU)
-              accg[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], gf[j], accg[i][j], 0, 0, 0);
+            if constexpr (FP8W) {
+              part[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], part[i][j], 0, 0, 0);
+              if constexpr (SWIGLU)
+                partg[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], gf[j], partg[i][j], 0, 0, 0);
+            } else {
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+              if constexpr (SWIGLU)
+                accg[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], gf[j], accg[i][j], 0, 0, 0);
+            }
           }
       }
-      if (kt + 1 < KT) sstore(buf ^ 1);
+      if constexpr (FP8W) {
+        if (wave_active && ((kt + 1) * BK) % kFp8Block == 0) {
+          const int kb = (kt * BK) / kFp8Block;
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            const int rowb = (n0 + wn * TN + j * 32) / kFp8Block;  // W1 (or W2) block row
+            const float sc = Ws[(static_cast<size_t>(e) * RB + rowb) * KB + kb];
+            float scg = 0.f;
+            if constexpr (SWIGLU) scg = Ws[(static_cast<size_t>(e) * RB + N / kFp8Block + rowb) * KB + kb];
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+              acc[i][j] += sc * part[i][j];
+              part[i][j] = f32x16_t{};
+              if constexpr (SWIGLU) {
+                accg[i][j] += scg * partg[i][j];
+                partg[i][j] = f32x16_t{};
+              }
+            }
+          }
+        }
+      }
+    };
+
+    if constexpr (FP8W) {
+      gload_a(0);
+      gload_q(0, rq0);
+      convert(rq0);
+      sstore(0);
       __syncthreads();
+      // branch-free steps: the last one re-fetches step KT - 1 (valid, unused)
+      // and stages it into the buffer no later step reads
+      for (int kt = 0; kt < KT; ++kt) {
+        gload_a(min(kt + 1, KT - 1));
+        gload_q(min(kt + 1, KT - 1), rq0);
+        compute(kt);
+        convert(rq0);
+        sstore((kt + 1) & 1);
+        __syncthreads();
+      }
+    } else {
+      gload_a(0);
+      gload_b(0);
+      sstore(0);
+      __syncthreads();
+      for (int kt = 0; kt < KT; ++kt) {
+        if (kt + 1 < KT) {
+          gload_a(kt + 1);
+          gload_b(kt + 1);
+        }
+        compute(kt);
+        if (kt + 1 < KT) sstore((kt + 1) & 1);
+        __syncthreads();
+      }
     }
 
     // epilogue: D[m][n] of a 32x32 tile sits in lane (n + 32 * ((m / 4) % 2)),
@@ -191,12 +298,13 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(
   }
 }
 
-template <int BM, int BN, int BK, int WM, int WN, bool SWIGLU, int CLASS>
+template <int BM, int BN, int BK, int WM, int WN, bool SWIGLU, int CLASS, bool FP8W = false>
 static int launch_gemm(const void* A, const int32_t* offsets, int E_loc, int64_t max_rows,
-                       const void* W, void* C, int N, int K, hipStream_t s) {
+                       const void* W, void* C, int N, int K, hipStream_t s,
+                       const float* Ws = nullptr) {
   constexpr int BNW = SWIGLU ? 2 * BN : BN;
   const size_t lds = static_cast<size_t>(2) * (BM + BNW) * BK * sizeof(uint16_t);
-  auto kern = gemm_bf16_kernel<BM, BN, BK, WM, WN, SWIGLU, CLASS>;
+  auto kern = gemm_bf16_kernel<BM, BN, BK, WM, WN, SWIGLU, CLASS, FP8W>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -218,8 +326,8 @@ static int launch_gemm(const void* A, const int32_t* offsets, int E_loc, int64_t
   if (grid >= 8) grid &= ~static_cast<int64_t>(7);
   if (grid < 1) grid = 1;
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(WM * WN * 64), lds, s,
-                     static_cast<const uint16_t*>(A), offsets, E_loc,
-                     static_cast<const uint16_t*>(W), static_cast<uint16_t*>(C), N, K);
+                     static_cast<const uint16_t*>(A), offsets, E_loc, W, Ws,
+                     static_cast<uint16_t*>(C), N, K);
   return static_cast<int>(hipGetLastError());
 }
 
@@ -278,6 +386,37 @@ int launch_ffn_down_bf16(const void* h, const int32_t* offsets, int E_loc, int64
   int e = launch_gemm_pipe_bf16(PipeRows::kBigTiles, false, h, offsets, E_loc, max_rows, w2, y, d, f, stream);
   if (e != 0) return e;
   return launch_gemm_pipe_bf16(PipeRows::kTailTiles, false, h, offsets, E_loc, max_rows, w2, y, d, f, stream);
+}
+
+}  // namespace moe
+
+namespace moe {
+
+// FP8 weights: few rows per expert (decode) stream the codes with 32-row
+// tiles, two workgroups per CU; more rows use 64-row tiles so each weight
+// tile is re-read less often.  Row counts stay on the device.
+int launch_ffn_up_fp8(const void* x_perm, const int32_t* offsets, int E_loc, int64_t max_rows,
+                      int d, int f, const uint8_t* w13q, const float* w13s, void* h,
+                      void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (max_rows == 0) return 0;
+  if (max_rows / E_loc <= kStreamRows)
+    return launch_gemm<32, 128, 64, 1, 4, true, ROWS_ALL, true>(x_perm, offsets, E_loc, max_rows,
+                                                               w13q, h, f, d, s, w13s);
+  return launch_gemm<64, 128, 64, 2, 2, true, ROWS_ALL, true>(x_perm, offsets, E_loc, max_rows,
+                                                              w13q, h, f, d, s, w13s);
+}
+
+int launch_ffn_down_fp8(const void* h, const int32_t* offsets, int E_loc, int64_t max_rows,
+                        int d, int f, const uint8_t* w2q, const float* w2s, void* y,
+                        void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (max_rows == 0) return 0;
+  if (max_rows / E_loc <= kStreamRows)
+    return launch_gemm<32, 128, 64, 1, 4, false, ROWS_ALL, true>(h, offsets, E_loc, max_rows, w2q,
+                                                                y, d, f, s, w2s);
+  return launch_gemm<64, 128, 64, 2, 2, false, ROWS_ALL, true>(h, offsets, E_loc, max_rows, w2q,
+                                                               y, d, f, s, w2s);
 }
 
 }  // namespace moe

@@ -48,6 +48,15 @@ bool remainders_with_big_tiles(int E_loc, int N, int K, bool swiglu);
 int launch_gemm_pipe_bf16(PipeRows rows, bool swiglu, const void* A, const int32_t* offsets,
                           int E_loc, int64_t max_rows, const void* W, void* C, int N, int K,
                           void* stream);
+// FP8 (E4M3-FN) weights with 128 x 128 block scales
+int launch_quantize_fp8(const void* w, int E_loc, int R, int K, uint8_t* q, float* scales,
+                        void* stream);
+int launch_ffn_up_fp8(const void* x_perm, const int32_t* offsets, int E_loc, int64_t max_rows,
+                      int d, int f, const uint8_t* w13q, const float* w13s, void* h,
+                      void* stream);
+int launch_ffn_down_fp8(const void* h, const int32_t* offsets, int E_loc, int64_t max_rows,
+                        int d, int f, const uint8_t* w2q, const float* w2s, void* y,
+                        void* stream);
 int launch_ffn_up_f32(const float* x_perm, const int32_t* offsets, int E_loc, int64_t max_rows,
                       int d, int f, const float* w13, float* h, void* stream);
 int launch_ffn_down_f32(const float* h, const int32_t* offsets, int E_loc, int64_t max_rows,

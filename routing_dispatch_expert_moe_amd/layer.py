@@ -4,6 +4,9 @@ forward() enqueues, on the current HIP stream:
   [moe_router_logits] -> moe_route -> moe_dispatch -> moe_ffn_up -> moe_ffn_down -> moe_combine
 and never synchronises with the host (row counts stay on the device).
 forward_fused() enqueues the same path as one moe_forward_fused launch.
+With FP8 weights (uint8 E4M3 codes from moe_quantize_fp8 plus their block
+scales) the FFN steps run moe_ffn_up_fp8 / moe_ffn_down_fp8 on bf16
+activations; the fused launch takes bf16 or fp32 weights only.
 """
 from __future__ import annotations
 
@@ -16,8 +19,13 @@ from . import ops
 
 class MoELayer:
     def __init__(self, w13_packed: torch.Tensor, w2_packed: torch.Tensor, *, E: int, k: int,
-                 gate, T: int, capacity: int = -1, e_begin: int = 0, e_end: Optional[int] = None):
+                 gate, T: int, capacity: int = -1, e_begin: int = 0, e_end: Optional[int] = None,
+                 w13_scale: Optional[torch.Tensor] = None, w2_scale: Optional[torch.Tensor] = None):
         self.w13, self.w2 = w13_packed, w2_packed
+        self.fp8 = w13_packed.dtype == torch.uint8
+        if self.fp8 and (w13_scale is None or w2_scale is None):
+            raise ValueError("FP8 weights need their block scales")
+        self.w13_scale, self.w2_scale = w13_scale, w2_scale
         self.E, self.k, self.gate, self.T = E, k, gate, T
         self.capacity = capacity
         self.e_begin = e_begin
@@ -25,7 +33,7 @@ class MoELayer:
         self.E_loc = self.e_end - self.e_begin
         self.d = w13_packed.shape[2]
         self.f = w13_packed.shape[1] // 2
-        self.dtype = w13_packed.dtype
+        self.dtype = torch.bfloat16 if self.fp8 else w13_packed.dtype
         dev = w13_packed.device
         if w13_packed.shape[0] != self.E_loc:
             raise ValueError("packed weights must hold exactly the local experts")
@@ -51,10 +59,16 @@ class MoELayer:
                                 self.ws, self.plan)
 
     def ffn_up(self):
+        if self.fp8:
+            return ops.moe_ffn_up_fp8(self.plan.x_perm, self.plan.offsets, self.E_loc,
+                                      self.plan.max_rows, self.w13, self.w13_scale, self.h)
         return ops.moe_ffn_up(self.plan.x_perm, self.plan.offsets, self.E_loc, self.plan.max_rows,
                               self.w13, self.h, self.ws)
 
     def ffn_down(self):
+        if self.fp8:
+            return ops.moe_ffn_down_fp8(self.h, self.plan.offsets, self.E_loc, self.plan.max_rows,
+                                        self.w2, self.w2_scale, self.y_perm)
         return ops.moe_ffn_down(self.h, self.plan.offsets, self.E_loc, self.plan.max_rows, self.w2,
                                 self.y_perm, self.ws)
 
@@ -80,6 +94,8 @@ class MoELayer:
         """route -> dispatch -> expert FFN -> combine as one persistent launch."""
         if x.shape[0] != self.T:
             raise ValueError(f"layer was sized for T={self.T}, got {x.shape[0]}")
+        if self.fp8:
+            raise NotImplementedError("the fused launch takes bf16 or fp32 weights")
         return ops.moe_forward_fused(logits, x, self.k, self.gate, self.capacity, self.e_begin,
                                      self.e_end, self.w13, self.w2, self.ws, self.plan,
                                      self.topk_idx, self.topk_w, self.h, self.y_perm, self.y)

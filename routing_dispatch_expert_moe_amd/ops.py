@@ -195,6 +195,55 @@ def moe_expert_ffn(x_perm, offsets, E_loc, max_rows, w13_packed, w2_packed, h=No
     return h, y_perm
 
 
+def moe_quantize_fp8(w_packed: torch.Tensor, q: Optional[torch.Tensor] = None,
+                     scales: Optional[torch.Tensor] = None, stream=None):
+    """Packed bf16 weights [E, rows, K] -> (E4M3 codes uint8 [E, rows, K],
+    fp32 scales [E, rows/128, K/128]); see moe_quantize_fp8 in include/moe.h."""
+    E, R, K = w_packed.shape
+    if q is None:
+        q = torch.empty((E, R, K), dtype=torch.uint8, device=w_packed.device)
+    if scales is None:
+        scales = torch.empty((E, max(R // 128, 1), max(K // 128, 1)), dtype=torch.float32,
+                             device=w_packed.device)
+    check(lib().moe_quantize_fp8(_ptr(w_packed), E, R, K, _ptr(q), _ptr(scales), _stream(stream)),
+          "moe_quantize_fp8")
+    return q, scales
+
+
+def moe_ffn_up_fp8(x_perm, offsets, E_loc, max_rows, w13_q, w13_s, h=None, stream=None):
+    d = x_perm.shape[1]
+    f = w13_q.shape[1] // 2
+    if h is None:
+        h = torch.empty((max(max_rows, 1), f), dtype=x_perm.dtype, device=x_perm.device)
+    check(lib().moe_ffn_up_fp8(_ptr(x_perm), _ptr(offsets), E_loc, max_rows, d, f, _ptr(w13_q),
+                               _ptr(w13_s), _ptr(h), _stream(stream)), "moe_ffn_up_fp8")
+    return h
+
+
+def moe_ffn_down_fp8(h, offsets, E_loc, max_rows, w2_q, w2_s, y_perm=None, stream=None):
+    f = h.shape[1]
+    d = w2_q.shape[1]
+    if y_perm is None:
+        y_perm = torch.empty((max(max_rows, 1), d), dtype=h.dtype, device=h.device)
+    check(lib().moe_ffn_down_fp8(_ptr(h), _ptr(offsets), E_loc, max_rows, d, f, _ptr(w2_q),
+                                 _ptr(w2_s), _ptr(y_perm), _stream(stream)), "moe_ffn_down_fp8")
+    return y_perm
+
+
+def moe_expert_ffn_fp8(x_perm, offsets, E_loc, max_rows, w13_q, w13_s, w2_q, w2_s, h=None,
+                       y_perm=None, stream=None):
+    d = x_perm.shape[1]
+    f = w13_q.shape[1] // 2
+    if h is None:
+        h = torch.empty((max(max_rows, 1), f), dtype=x_perm.dtype, device=x_perm.device)
+    if y_perm is None:
+        y_perm = torch.empty((max(max_rows, 1), d), dtype=x_perm.dtype, device=x_perm.device)
+    check(lib().moe_expert_ffn_fp8(_ptr(x_perm), _ptr(offsets), E_loc, max_rows, d, f,
+                                   _ptr(w13_q), _ptr(w13_s), _ptr(w2_q), _ptr(w2_s), _ptr(h),
+                                   _ptr(y_perm), _stream(stream)), "moe_expert_ffn_fp8")
+    return h, y_perm
+
+
 def moe_combine(y_perm, pair_pos, topk_w, y=None, stream=None):
     T, k = topk_w.shape
     d = y_perm.shape[1]

@@ -32,7 +32,8 @@ def test_header_declares_the_path():
     names = declared_functions()
     for n in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_router_logits",
               "moe_pack_weights", "moe_check_error", "moe_ffn_up", "moe_ffn_down",
-              "moe_forward_fused"):
+              "moe_forward_fused", "moe_quantize_fp8", "moe_expert_ffn_fp8", "moe_ffn_up_fp8",
+              "moe_ffn_down_fp8"):
         assert n in names
 
 
@@ -121,6 +122,29 @@ def test_ffn_validation(lib):
     assert f(*f32) == L.MOE_ERR_UNSUPPORTED
     up = lib.moe_ffn_up
     assert up(FAKE, FAKE, 8, -1, 64, 64, L.MOE_BF16, FAKE, FAKE, None, 0, None) == L.MOE_ERR_INVALID_ARG
+
+
+def test_fp8_validation(lib):
+    qz = lib.moe_quantize_fp8
+    assert qz(None, 1, 128, 128, FAKE, FAKE, None) == L.MOE_ERR_INVALID_ARG
+    assert qz(FAKE, 0, 128, 128, FAKE, FAKE, None) == L.MOE_ERR_INVALID_ARG
+    assert qz(FAKE, 1, 100, 128, FAKE, FAKE, None) == L.MOE_ERR_UNSUPPORTED   # rows % 128
+    assert qz(FAKE, 1, 128, 192, FAKE, FAKE, None) == L.MOE_ERR_UNSUPPORTED   # K % 128
+    assert qz(FAKE, 1, 128, 128, MIS, FAKE, None) == L.MOE_ERR_MISALIGNED
+    f = lib.moe_expert_ffn_fp8
+    ok = [FAKE, FAKE, 8, 100, 4096, 1024, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None]
+    bad = list(ok); bad[5] = 1000          # f % 64
+    assert f(*bad) == L.MOE_ERR_UNSUPPORTED
+    bad = list(ok); bad[5] = 960           # f % 128 (bf16 alone would take it)
+    assert f(*bad) == L.MOE_ERR_UNSUPPORTED
+    bad = list(ok); bad[7] = None          # no scales
+    assert f(*bad) == L.MOE_ERR_INVALID_ARG
+    bad = list(ok); bad[9] = MIS
+    assert f(*bad) == L.MOE_ERR_MISALIGNED
+    bad = list(ok); bad[2] = 0
+    assert f(*bad) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_ffn_up_fp8(FAKE, FAKE, 8, 100, 4096, 1024, FAKE, None, FAKE, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_ffn_down_fp8(FAKE, FAKE, 8, 100, 4096, 1024, FAKE, MIS, FAKE, None) == L.MOE_ERR_MISALIGNED
 
 
 def test_combine_router_pack_validation(lib):
