@@ -392,17 +392,17 @@ int launch_ffn_down_bf16(const void* h, const int32_t* offsets, int E_loc, int64
 
 namespace moe {
 
-// FP8 weights: few rows per expert (decode) stream the codes with 32-row
-// tiles, two workgroups per CU; more rows use 64-row tiles so each weight
-// tile is re-read less often.  Row counts stay on the device.
+// FP8 weights: few rows per expert (decode) run the code-streaming kernel
+// (fp8.hip: codes in LDS, 32-row tiles, three workgroups per CU); more rows
+// stage bf16 weight tiles with 64-row tiles so each is re-read less often.
+// Row counts stay on the device.
 int launch_ffn_up_fp8(const void* x_perm, const int32_t* offsets, int E_loc, int64_t max_rows,
                       int d, int f, const uint8_t* w13q, const float* w13s, void* h,
                       void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (max_rows == 0) return 0;
   if (max_rows / E_loc <= kStreamRows)
-    return launch_gemm<32, 128, 64, 1, 4, true, ROWS_ALL, true>(x_perm, offsets, E_loc, max_rows,
-                                                               w13q, h, f, d, s, w13s);
+    return launch_gemm_fp8w(true, x_perm, offsets, E_loc, max_rows, w13q, w13s, h, f, d, stream);
   return launch_gemm<64, 128, 64, 2, 2, true, ROWS_ALL, true>(x_perm, offsets, E_loc, max_rows,
                                                               w13q, h, f, d, s, w13s);
 }
@@ -413,8 +413,7 @@ int launch_ffn_down_fp8(const void* h, const int32_t* offsets, int E_loc, int64_
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (max_rows == 0) return 0;
   if (max_rows / E_loc <= kStreamRows)
-    return launch_gemm<32, 128, 64, 1, 4, false, ROWS_ALL, true>(h, offsets, E_loc, max_rows, w2q,
-                                                                y, d, f, s, w2s);
+    return launch_gemm_fp8w(false, h, offsets, E_loc, max_rows, w2q, w2s, y, d, f, stream);
   return launch_gemm<64, 128, 64, 2, 2, false, ROWS_ALL, true>(h, offsets, E_loc, max_rows, w2q,
                                                                y, d, f, s, w2s);
 }

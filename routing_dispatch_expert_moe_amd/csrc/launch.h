@@ -51,6 +51,10 @@ int launch_gemm_pipe_bf16(PipeRows rows, bool swiglu, const void* A, const int32
 // FP8 (E4M3-FN) weights with 128 x 128 block scales
 int launch_quantize_fp8(const void* w, int E_loc, int R, int K, uint8_t* q, float* scales,
                         void* stream);
+// few rows per expert: codes kept in LDS, converted per MFMA operand
+int launch_gemm_fp8w(bool swiglu, const void* A, const int32_t* offsets, int E_loc,
+                     int64_t max_rows, const uint8_t* Wq, const float* Ws, void* C, int N, int K,
+                     void* stream);
 int launch_ffn_up_fp8(const void* x_perm, const int32_t* offsets, int E_loc, int64_t max_rows,
                       int d, int f, const uint8_t* w13q, const float* w13s, void* h,
                       void* stream);
