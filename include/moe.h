@@ -175,6 +175,27 @@ moe_status moe_ffn_down(const void* h, const int32_t* offsets, int E_loc, int64_
                         int d, int f, moe_dtype dtype, const void* w2_packed, void* y_perm,
                         void* ws, size_t ws_bytes, void* stream);
 
+/* moe_expert_ffn over a table of per-expert weight buffers instead of one
+ * packed tensor (DWDP page, key optimisations and TensorList: the grouped
+ * GEMM takes a list of weight buffers -- locally resident ones and ones
+ * fetched from elsewhere -- so nothing is copied into one contiguous tensor).
+ * w13_list / w2_list: device arrays of E_loc device pointers; entry i points
+ * to local expert i's weights in the packed layout of moe_pack_weights
+ * ([2f][d] for w13, [d][f] for w2), each buffer 16-byte aligned and alive
+ * until the call's kernels have run.  The tables themselves are 16-byte
+ * aligned.  Same operation, kernels and bits as moe_expert_ffn on packed
+ * weights.  No workspace. */
+moe_status moe_expert_ffn_list(const void* x_perm, const int32_t* offsets, int E_loc,
+                               int64_t max_rows, int d, int f, moe_dtype dtype,
+                               const void* const* w13_list, const void* const* w2_list, void* h,
+                               void* y_perm, void* stream);
+moe_status moe_ffn_up_list(const void* x_perm, const int32_t* offsets, int E_loc,
+                           int64_t max_rows, int d, int f, moe_dtype dtype,
+                           const void* const* w13_list, void* h, void* stream);
+moe_status moe_ffn_down_list(const void* h, const int32_t* offsets, int E_loc, int64_t max_rows,
+                             int d, int f, moe_dtype dtype, const void* const* w2_list,
+                             void* y_perm, void* stream);
+
 /* FP8 expert weights (NCCL EP page §2.1, expert-compute stage: FP8 compute
  * with a scale tensor).  The page fixes neither format nor scale shape; this
  * library uses E4M3-FN codes (OCP FP8, gfx950's FP8 type: bias 7, 3 mantissa

@@ -45,6 +45,9 @@ SIGNATURES = {
     "moe_ffn_down": (_i, [_vp, _i32p, _i, _i64, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]),
     "moe_combine": (_i, [_vp, _i32p, _fp, _i, _i, _i, _i, _vp, _vp]),
     "moe_check_error": (_i, [_vp, _vp]),
+    "moe_expert_ffn_list": (_i, [_vp, _i32p, _i, _i64, _i, _i, _i, _vp, _vp, _vp, _vp, _vp]),
+    "moe_ffn_up_list": (_i, [_vp, _i32p, _i, _i64, _i, _i, _i, _vp, _vp, _vp]),
+    "moe_ffn_down_list": (_i, [_vp, _i32p, _i, _i64, _i, _i, _i, _vp, _vp, _vp]),
     "moe_quantize_fp8": (_i, [_vp, _i, _i, _i, _vp, _fp, _vp]),
     "moe_expert_ffn_fp8": (_i, [_vp, _i32p, _i, _i64, _i, _i, _vp, _fp, _vp, _fp, _vp, _vp, _vp]),
     "moe_ffn_up_fp8": (_i, [_vp, _i32p, _i, _i64, _i, _i, _vp, _fp, _vp, _vp]),

@@ -61,6 +61,29 @@ moe_status check_ffn_fp8(const void* a, const int32_t* offsets, int E_loc, int64
   return MOE_OK;
 }
 
+// the two FFN halves on packed weights (wlist null) or a per-expert weight table
+moe_status launch_up(const void* x_perm, const int32_t* offsets, int E_loc, int64_t max_rows, int d,
+                     int f, int dtype, const void* w13, const void* const* wlist, void* h,
+                     void* stream) {
+  if (dtype == MOE_BF16)
+    return hip_status(moe::launch_ffn_up_bf16(x_perm, offsets, E_loc, max_rows, d, f, w13, h,
+                                              wlist, stream));
+  return hip_status(moe::launch_ffn_up_f32(static_cast<const float*>(x_perm), offsets, E_loc,
+                                           max_rows, d, f, static_cast<const float*>(w13),
+                                           static_cast<float*>(h), wlist, stream));
+}
+
+moe_status launch_down(const void* h, const int32_t* offsets, int E_loc, int64_t max_rows, int d,
+                       int f, int dtype, const void* w2, const void* const* wlist, void* y,
+                       void* stream) {
+  if (dtype == MOE_BF16)
+    return hip_status(moe::launch_ffn_down_bf16(h, offsets, E_loc, max_rows, d, f, w2, y, wlist,
+                                                stream));
+  return hip_status(moe::launch_ffn_down_f32(static_cast<const float*>(h), offsets, E_loc,
+                                             max_rows, d, f, static_cast<const float*>(w2),
+                                             static_cast<float*>(y), wlist, stream));
+}
+
 }  // namespace
 
 namespace moe {
@@ -208,12 +231,7 @@ moe_status moe_ffn_up(const void* x_perm, const int32_t* offsets, int E_loc, int
   (void)ws_bytes;
   moe_status st = check_ffn(x_perm, offsets, E_loc, max_rows, d, f, dtype, w13_packed, h);
   if (st != MOE_OK) return st;
-  if (dtype == MOE_BF16)
-    return hip_status(moe::launch_ffn_up_bf16(x_perm, offsets, E_loc, max_rows, d, f, w13_packed,
-                                              h, stream));
-  return hip_status(moe::launch_ffn_up_f32(static_cast<const float*>(x_perm), offsets, E_loc,
-                                           max_rows, d, f, static_cast<const float*>(w13_packed),
-                                           static_cast<float*>(h), stream));
+  return launch_up(x_perm, offsets, E_loc, max_rows, d, f, dtype, w13_packed, nullptr, h, stream);
 }
 
 moe_status moe_ffn_down(const void* h, const int32_t* offsets, int E_loc, int64_t max_rows,
@@ -223,12 +241,7 @@ moe_status moe_ffn_down(const void* h, const int32_t* offsets, int E_loc, int64_
   (void)ws_bytes;
   moe_status st = check_ffn(h, offsets, E_loc, max_rows, d, f, dtype, w2_packed, y_perm);
   if (st != MOE_OK) return st;
-  if (dtype == MOE_BF16)
-    return hip_status(moe::launch_ffn_down_bf16(h, offsets, E_loc, max_rows, d, f, w2_packed,
-                                                y_perm, stream));
-  return hip_status(moe::launch_ffn_down_f32(static_cast<const float*>(h), offsets, E_loc,
-                                             max_rows, d, f, static_cast<const float*>(w2_packed),
-                                             static_cast<float*>(y_perm), stream));
+  return launch_down(h, offsets, E_loc, max_rows, d, f, dtype, w2_packed, nullptr, y_perm, stream);
 }
 
 moe_status moe_expert_ffn(const void* x_perm, const int32_t* offsets, int E_loc,
@@ -284,6 +297,35 @@ moe_status moe_expert_ffn_fp8(const void* x_perm, const int32_t* offsets, int E_
   st = moe_ffn_up_fp8(x_perm, offsets, E_loc, max_rows, d, f, w13_q, w13_s, h, stream);
   if (st != MOE_OK) return st;
   return moe_ffn_down_fp8(h, offsets, E_loc, max_rows, d, f, w2_q, w2_s, y_perm, stream);
+}
+
+moe_status moe_ffn_up_list(const void* x_perm, const int32_t* offsets, int E_loc,
+                          int64_t max_rows, int d, int f, moe_dtype dtype,
+                          const void* const* w13_list, void* h, void* stream) {
+  moe_status st = check_ffn(x_perm, offsets, E_loc, max_rows, d, f, dtype, w13_list, h);
+  if (st != MOE_OK) return st;
+  return launch_up(x_perm, offsets, E_loc, max_rows, d, f, dtype, nullptr, w13_list, h, stream);
+}
+
+moe_status moe_ffn_down_list(const void* h, const int32_t* offsets, int E_loc, int64_t max_rows,
+                            int d, int f, moe_dtype dtype, const void* const* w2_list,
+                            void* y_perm, void* stream) {
+  moe_status st = check_ffn(h, offsets, E_loc, max_rows, d, f, dtype, w2_list, y_perm);
+  if (st != MOE_OK) return st;
+  return launch_down(h, offsets, E_loc, max_rows, d, f, dtype, nullptr, w2_list, y_perm, stream);
+}
+
+moe_status moe_expert_ffn_list(const void* x_perm, const int32_t* offsets, int E_loc,
+                               int64_t max_rows, int d, int f, moe_dtype dtype,
+                               const void* const* w13_list, const void* const* w2_list, void* h,
+                               void* y_perm, void* stream) {
+  moe_status st = check_ffn(x_perm, offsets, E_loc, max_rows, d, f, dtype, w13_list, h);
+  if (st != MOE_OK) return st;
+  st = check_ffn(h, offsets, E_loc, max_rows, d, f, dtype, w2_list, y_perm);
+  if (st != MOE_OK) return st;
+  st = moe_ffn_up_list(x_perm, offsets, E_loc, max_rows, d, f, dtype, w13_list, h, stream);
+  if (st != MOE_OK) return st;
+  return moe_ffn_down_list(h, offsets, E_loc, max_rows, d, f, dtype, w2_list, y_perm, stream);
 }
 
 moe_status moe_combine(const void* y_perm, const int32_t* pair_pos, const float* topk_w, int T,

@@ -42,7 +42,7 @@ template <int BM, int BN, int BK, int WM, int WN, bool SWIGLU, int CLASS, bool F
 __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets, int E_loc,
     const void* __restrict__ Wv, const float* __restrict__ Ws, uint16_t* __restrict__ C, int N,
-    int K) {
+    int K, const void* const* __restrict__ wlist) {
   constexpr int NTHR = WM * WN * 64;
   constexpr int BNW = SWIGLU ? 2 * BN : BN;  // weight rows per tile
   constexpr int KC = BK / 8;                 // 16-byte chunks per tile row
@@ -89,8 +89,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(
     const int seg0 = offsets[e] + first, seg1 = seg0 + count;
     const int m0 = seg0 + mti * BM;
     const int n0 = nt * BN;
-    const uint16_t* We = W + e * wstride;
-    const uint8_t* Wqe = Wq + e * wstride;
+    // expert e's packed weights: W + e * stride, or wlist[e] (a table of per-expert buffers)
+    const uint16_t* We = wlist != nullptr ? static_cast<const uint16_t*>(wlist[e]) : W + e * wstride;
+    const uint8_t* Wqe = wlist != nullptr ? static_cast<const uint8_t*>(wlist[e]) : Wq + e * wstride;
 
     // per-thread load descriptors
     const uint16_t* a_src[CA];
@@ -301,7 +302,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(
 template <int BM, int BN, int BK, int WM, int WN, bool SWIGLU, int CLASS, bool FP8W = false>
 static int launch_gemm(const void* A, const int32_t* offsets, int E_loc, int64_t max_rows,
                        const void* W, void* C, int N, int K, hipStream_t s,
-                       const float* Ws = nullptr) {
+                       const float* Ws = nullptr, const void* const* wlist = nullptr) {
   constexpr int BNW = SWIGLU ? 2 * BN : BN;
   const size_t lds = static_cast<size_t>(2) * (BM + BNW) * BK * sizeof(uint16_t);
   auto kern = gemm_bf16_kernel<BM, BN, BK, WM, WN, SWIGLU, CLASS, FP8W>;
@@ -327,7 +328,7 @@ static int launch_gemm(const void* A, const int32_t* offsets, int E_loc, int64_t
   if (grid < 1) grid = 1;
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(WM * WN * 64), lds, s,
                      static_cast<const uint16_t*>(A), offsets, E_loc, W, Ws,
-                     static_cast<uint16_t*>(C), N, K);
+                     static_cast<uint16_t*>(C), N, K, wlist);
   return static_cast<int>(hipGetLastError());
 }
 
@@ -346,7 +347,8 @@ constexpr int64_t kStreamRows = 48;
 // with the expert's other tiles through L2), else a small-tile kernel takes
 // the short remainders (ROWS_BIG / ROWS_TAIL).  Row counts stay on the device.
 int launch_ffn_up_bf16(const void* x_perm, const int32_t* offsets, int E_loc, int64_t max_rows,
-                       int d, int f, const void* w13, void* h, void* stream) {
+                       int d, int f, const void* w13, void* h, const void* const* wlist,
+                       void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (max_rows == 0) return 0;
   const int64_t avg = max_rows / E_loc;
@@ -354,38 +356,39 @@ int launch_ffn_up_bf16(const void* x_perm, const int32_t* offsets, int E_loc, in
   const bool fits32 = static_cast<double>(max_rows) * d * 2 < 4294967296.0 &&
                       static_cast<double>(2) * f * d * 2 < 4294967296.0;
   if (!fits32)
-    return launch_gemm<32, 128, 64, 1, 4, true, ROWS_ALL>(x_perm, offsets, E_loc, max_rows, w13, h, f, d, s);
+    return launch_gemm<32, 128, 64, 1, 4, true, ROWS_ALL>(x_perm, offsets, E_loc, max_rows, w13, h, f, d, s, nullptr, wlist);
   if (avg <= kStreamRows) {
     if (kDecodeSmallTiles)
-      return launch_gemm<32, 128, 64, 1, 4, true, ROWS_ALL>(x_perm, offsets, E_loc, max_rows, w13, h, f, d, s);
-    return launch_gemm_pipe_bf16(PipeRows::kAllRows, true, x_perm, offsets, E_loc, max_rows, w13, h, f, d, stream);
+      return launch_gemm<32, 128, 64, 1, 4, true, ROWS_ALL>(x_perm, offsets, E_loc, max_rows, w13, h, f, d, s, nullptr, wlist);
+    return launch_gemm_pipe_bf16(PipeRows::kAllRows, true, x_perm, offsets, E_loc, max_rows, w13, h, f, d, wlist, stream);
   }
   if (remainders_with_big_tiles(E_loc, f, d, true))
-    return launch_gemm_pipe_bf16(PipeRows::kBigAll, true, x_perm, offsets, E_loc, max_rows, w13, h, f, d, stream);
-  int e = launch_gemm_pipe_bf16(PipeRows::kBigTiles, true, x_perm, offsets, E_loc, max_rows, w13, h, f, d, stream);
+    return launch_gemm_pipe_bf16(PipeRows::kBigAll, true, x_perm, offsets, E_loc, max_rows, w13, h, f, d, wlist, stream);
+  int e = launch_gemm_pipe_bf16(PipeRows::kBigTiles, true, x_perm, offsets, E_loc, max_rows, w13, h, f, d, wlist, stream);
   if (e != 0) return e;
-  return launch_gemm_pipe_bf16(PipeRows::kTailTiles, true, x_perm, offsets, E_loc, max_rows, w13, h, f, d, stream);
+  return launch_gemm_pipe_bf16(PipeRows::kTailTiles, true, x_perm, offsets, E_loc, max_rows, w13, h, f, d, wlist, stream);
 }
 
 int launch_ffn_down_bf16(const void* h, const int32_t* offsets, int E_loc, int64_t max_rows,
-                         int d, int f, const void* w2, void* y, void* stream) {
+                         int d, int f, const void* w2, void* y, const void* const* wlist,
+                         void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (max_rows == 0) return 0;
   const int64_t avg = max_rows / E_loc;
   const bool fits32 = static_cast<double>(max_rows) * f * 2 < 4294967296.0 &&
                       static_cast<double>(d) * f * 2 < 4294967296.0;
   if (!fits32)
-    return launch_gemm<32, 128, 64, 1, 4, false, ROWS_ALL>(h, offsets, E_loc, max_rows, w2, y, d, f, s);
+    return launch_gemm<32, 128, 64, 1, 4, false, ROWS_ALL>(h, offsets, E_loc, max_rows, w2, y, d, f, s, nullptr, wlist);
   if (avg <= kStreamRows) {
     if (kDecodeSmallTiles)
-      return launch_gemm<32, 128, 64, 1, 4, false, ROWS_ALL>(h, offsets, E_loc, max_rows, w2, y, d, f, s);
-    return launch_gemm_pipe_bf16(PipeRows::kAllRows, false, h, offsets, E_loc, max_rows, w2, y, d, f, stream);
+      return launch_gemm<32, 128, 64, 1, 4, false, ROWS_ALL>(h, offsets, E_loc, max_rows, w2, y, d, f, s, nullptr, wlist);
+    return launch_gemm_pipe_bf16(PipeRows::kAllRows, false, h, offsets, E_loc, max_rows, w2, y, d, f, wlist, stream);
   }
   if (remainders_with_big_tiles(E_loc, d, f, false))
-    return launch_gemm_pipe_bf16(PipeRows::kBigAll, false, h, offsets, E_loc, max_rows, w2, y, d, f, stream);
-  int e = launch_gemm_pipe_bf16(PipeRows::kBigTiles, false, h, offsets, E_loc, max_rows, w2, y, d, f, stream);
+    return launch_gemm_pipe_bf16(PipeRows::kBigAll, false, h, offsets, E_loc, max_rows, w2, y, d, f, wlist, stream);
+  int e = launch_gemm_pipe_bf16(PipeRows::kBigTiles, false, h, offsets, E_loc, max_rows, w2, y, d, f, wlist, stream);
   if (e != 0) return e;
-  return launch_gemm_pipe_bf16(PipeRows::kTailTiles, false, h, offsets, E_loc, max_rows, w2, y, d, f, stream);
+  return launch_gemm_pipe_bf16(PipeRows::kTailTiles, false, h, offsets, E_loc, max_rows, w2, y, d, f, wlist, stream);
 }
 
 }  // namespace moe

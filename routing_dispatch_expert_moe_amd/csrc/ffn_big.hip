@@ -14,19 +14,20 @@ __global__ __launch_bounds__(pipe_waves<BM>() * 64, 1) void gemm_bf16_pipe(const
                                                          const int32_t* __restrict__ offsets,
                                                          int E_loc,
                                                          const uint16_t* __restrict__ W,
-                                                         uint16_t* __restrict__ C, int N, int K) {
+                                                         uint16_t* __restrict__ C, int N, int K,
+                                                         const uint16_t* const* __restrict__ wlist) {
   extern __shared__ uint4 lds[];
   __shared__ int prefix[MOE_MAX_E + 1];
   __shared__ int segs[MOE_MAX_E + 1];
   gemm_pipe_body<SWIGLU, BM, BNW, STAGES, CLASS, pipe_waves<BM>()>(
-      A, offsets, E_loc, W, C, N, K, blockIdx.x, gridDim.x, lds, prefix, segs);
+      A, offsets, E_loc, W, C, N, K, blockIdx.x, gridDim.x, lds, prefix, segs, nullptr, 1, wlist);
 }
 
 namespace {
 
 template <bool SWIGLU, int BM, int BNW, int STAGES, int CLASS>
 int launch_pipe(const void* A, const int32_t* offsets, int E_loc, int64_t max_rows, const void* W,
-                void* C, int N, int K, hipStream_t s) {
+                void* C, int N, int K, const void* const* wlist, hipStream_t s) {
   const size_t lds = pipe_lds_bytes(BM, BNW, STAGES);
   static_assert(pipe_lds_bytes(BM, BNW, STAGES) + 2 * (MOE_MAX_E + 1) * 4 <= 160 * 1024,
                 "LDS budget");
@@ -49,7 +50,8 @@ int launch_pipe(const void* A, const int32_t* offsets, int E_loc, int64_t max_ro
   if (grid < 1) grid = 1;
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(pipe_waves<BM>() * 64), lds, s,
                      static_cast<const uint16_t*>(A), offsets, E_loc,
-                     static_cast<const uint16_t*>(W), static_cast<uint16_t*>(C), N, K);
+                     static_cast<const uint16_t*>(W), static_cast<uint16_t*>(C), N, K,
+                     reinterpret_cast<const uint16_t* const*>(wlist));
   return static_cast<int>(hipGetLastError());
 }
 
@@ -61,22 +63,22 @@ constexpr int kSmallBM = 128, kSmallBNW = 128, kSmallStages = 8;
 
 template <bool SWIGLU>
 int launch_kind(PipeRows rows, const void* A, const int32_t* offsets, int E_loc, int64_t max_rows,
-                const void* W, void* C, int N, int K, hipStream_t s) {
+                const void* W, void* C, int N, int K, const void* const* wlist, hipStream_t s) {
   switch (rows) {
     case PipeRows::kBigTiles:
-      return launch_pipe<SWIGLU, 256, 256, 4, ROWS_BIG>(A, offsets, E_loc, max_rows, W, C, N, K, s);
+      return launch_pipe<SWIGLU, 256, 256, 4, ROWS_BIG>(A, offsets, E_loc, max_rows, W, C, N, K, wlist, s);
     case PipeRows::kBigAll:
-      return launch_pipe<SWIGLU, 256, 256, 4, ROWS_ALL>(A, offsets, E_loc, max_rows, W, C, N, K, s);
+      return launch_pipe<SWIGLU, 256, 256, 4, ROWS_ALL>(A, offsets, E_loc, max_rows, W, C, N, K, wlist, s);
     case PipeRows::kTailTiles: {
       if (!few_gemm_tiles(E_loc, N, SWIGLU))
         return launch_pipe<SWIGLU, 128, 256, 6, ROWS_TAIL>(A, offsets, E_loc, max_rows, W, C, N,
-                                                            K, s);
+                                                            K, wlist, s);
       return launch_pipe<SWIGLU, kSmallBM, kSmallBNW, kSmallStages, ROWS_TAIL>(
-          A, offsets, E_loc, max_rows, W, C, N, K, s);
+          A, offsets, E_loc, max_rows, W, C, N, K, wlist, s);
     }
     default:
       return launch_pipe<SWIGLU, kSmallBM, kSmallBNW, kSmallStages, ROWS_ALL>(
-          A, offsets, E_loc, max_rows, W, C, N, K, s);
+          A, offsets, E_loc, max_rows, W, C, N, K, wlist, s);
   }
 }
 
@@ -97,10 +99,10 @@ bool remainders_with_big_tiles(int E_loc, int N, int K, bool swiglu) {
 
 int launch_gemm_pipe_bf16(PipeRows rows, bool swiglu, const void* A, const int32_t* offsets,
                           int E_loc, int64_t max_rows, const void* W, void* C, int N, int K,
-                          void* stream) {
+                          const void* const* wlist, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (swiglu) return launch_kind<true>(rows, A, offsets, E_loc, max_rows, W, C, N, K, s);
-  return launch_kind<false>(rows, A, offsets, E_loc, max_rows, W, C, N, K, s);
+  if (swiglu) return launch_kind<true>(rows, A, offsets, E_loc, max_rows, W, C, N, K, wlist, s);
+  return launch_kind<false>(rows, A, offsets, E_loc, max_rows, W, C, N, K, wlist, s);
 }
 
 }  // namespace moe

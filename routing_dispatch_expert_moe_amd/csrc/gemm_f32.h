@@ -20,13 +20,15 @@ constexpr size_t f32_lds_floats(bool swiglu) {
 // Workgroup `bid` of `G` walks its tiles.  smem: f32_lds_floats(SWIGLU) floats
 // of LDS; prefix: E_loc + 1 ints of LDS.  Every thread must call it.
 // gather: if not null, activation row r is row gather[r] / gk of A.
+// wlist: if not null, expert e's packed weights start at wlist[e].
 template <bool SWIGLU>
 __device__ __forceinline__ void gemm_f32_body(const float* __restrict__ A,
                                               const int32_t* __restrict__ offsets, int E_loc,
                                               const float* __restrict__ W, float* __restrict__ C,
                                               int N, int K, int bid, int G, float* smem,
                                               int* prefix, const int32_t* __restrict__ gather = nullptr,
-                                              int gk = 1) {
+                                              int gk = 1,
+                                              const float* const* __restrict__ wlist = nullptr) {
   constexpr int BM = kF32BM, BN = kF32BN, BK = kF32BK;
   constexpr int BNW = SWIGLU ? 2 * BN : BN;
   float (*As)[BM + 4] = reinterpret_cast<float (*)[BM + 4]>(smem);
@@ -46,7 +48,7 @@ __device__ __forceinline__ void gemm_f32_body(const float* __restrict__ A,
     const int seg1 = offsets[e + 1];
     const int m0 = offsets[e] + mti * BM;
     const int n0 = nt * BN;
-    const float* We = W + e * wstride;
+    const float* We = wlist != nullptr ? wlist[e] : W + e * wstride;
     float acc[4][4] = {}, accg[4][4] = {};
     for (int k0 = 0; k0 < K; k0 += BK) {
       {  // A: 64 rows x 16 k, one float4 per thread, stored k-major

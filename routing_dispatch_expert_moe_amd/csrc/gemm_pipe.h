@@ -115,6 +115,8 @@ constexpr size_t pipe_lds_bytes(int BM, int BNW, int STAGES) {
 // (4 or 8: one or two per SIMD) split the tile 2 x NW/2.
 // gather: if not null, activation row r is row gather[r] / gk of A (A rows
 // read in place through the dispatch permutation instead of a permuted copy).
+// wlist: if not null, expert e's packed weights start at wlist[e] (a table of
+// per-expert buffers) instead of W + e * (weight rows * K).
 template <bool SWIGLU, int BM, int BNW, int STAGES, int CLASS, int NW = 4>
 __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
                                                const int32_t* __restrict__ offsets, int E_loc,
@@ -122,7 +124,8 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
                                                uint16_t* __restrict__ C, int N, int K, int bid,
                                                int G, uint4* lds, int* prefix, int* segs,
                                                const int32_t* __restrict__ gather = nullptr,
-                                               int gk = 1) {
+                                               int gk = 1,
+                                               const uint16_t* const* __restrict__ wlist = nullptr) {
   constexpr int BN = SWIGLU ? BNW / 2 : BNW;  // output columns per tile
   constexpr int HALF = BNW / 2;               // SwiGLU: W1 rows (then as many W3 rows)
   constexpr int FM = BM / 64;                 // 32-row MFMA blocks per wave
@@ -167,7 +170,7 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
   uint32_t aoff[LA], boff[LB];
   auto set_issue_tile = [&](int j) {
     const Tile t = decode_tile<BM, BN, CLASS>(vb + j * G, NT, prefix, segs, E_loc);
-    iWb = reinterpret_cast<const char*>(W + t.e * wstride);
+    iWb = reinterpret_cast<const char*>(wlist != nullptr ? wlist[t.e] : W + t.e * wstride);
 #pragma unroll
     for (int i = 0; i < LA; ++i) {
       const int rt = (i * NW + wave) * kRPI + lane / kKC;  // row within the tile

@@ -28,10 +28,14 @@ int launch_dispatch(const int32_t* idx, int T, int E, int k, int capacity, int e
                     int e_end, const void* x, int d, int elem_bytes, int32_t* counts,
                     int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos, int32_t* n_kept,
                     void* x_perm, const DispatchWs& ws, void* stream);
+// wlist (all FFN launchers): null for one packed weight tensor (expert e at
+// W + e * rows * K), else a device table of E_loc per-expert packed buffers
 int launch_ffn_up_bf16(const void* x_perm, const int32_t* offsets, int E_loc, int64_t max_rows,
-                       int d, int f, const void* w13, void* h, void* stream);
+                       int d, int f, const void* w13, void* h, const void* const* wlist,
+                       void* stream);
 int launch_ffn_down_bf16(const void* h, const int32_t* offsets, int E_loc, int64_t max_rows,
-                         int d, int f, const void* w2, void* y, void* stream);
+                         int d, int f, const void* w2, void* y, const void* const* wlist,
+                         void* stream);
 // Pipelined direct-to-LDS grouped GEMM over one row class: 256-row tiles over
 // each expert's full blocks (kBigTiles), 256-row tiles over every row with
 // the last block of an expert as a possibly half-empty tile (kBigAll),
@@ -47,7 +51,7 @@ bool few_gemm_tiles(int E_loc, int N, bool swiglu);
 bool remainders_with_big_tiles(int E_loc, int N, int K, bool swiglu);
 int launch_gemm_pipe_bf16(PipeRows rows, bool swiglu, const void* A, const int32_t* offsets,
                           int E_loc, int64_t max_rows, const void* W, void* C, int N, int K,
-                          void* stream);
+                          const void* const* wlist, void* stream);
 // FP8 (E4M3-FN) weights with 128 x 128 block scales
 int launch_quantize_fp8(const void* w, int E_loc, int R, int K, uint8_t* q, float* scales,
                         void* stream);
@@ -62,9 +66,11 @@ int launch_ffn_down_fp8(const void* h, const int32_t* offsets, int E_loc, int64_
                         int d, int f, const uint8_t* w2q, const float* w2s, void* y,
                         void* stream);
 int launch_ffn_up_f32(const float* x_perm, const int32_t* offsets, int E_loc, int64_t max_rows,
-                      int d, int f, const float* w13, float* h, void* stream);
+                      int d, int f, const float* w13, float* h, const void* const* wlist,
+                      void* stream);
 int launch_ffn_down_f32(const float* h, const int32_t* offsets, int E_loc, int64_t max_rows,
-                        int d, int f, const float* w2, float* y, void* stream);
+                        int d, int f, const float* w2, float* y, const void* const* wlist,
+                        void* stream);
 int launch_combine(const void* y_perm, const int32_t* pair_pos, const float* w, int T, int k,
                    int d, int bf16, void* y, void* stream);
 int launch_pack(const void* w1, const void* w3, const void* w2, int E_loc, int d, int f,

@@ -9,7 +9,7 @@ from __future__ import annotations
 
 import dataclasses
 from fractions import Fraction
-from typing import Optional, Tuple
+from typing import Optional, Sequence, Tuple
 
 import torch
 
@@ -192,6 +192,31 @@ def moe_expert_ffn(x_perm, offsets, E_loc, max_rows, w13_packed, w2_packed, h=No
                                _dtype_code(x_perm.dtype), _ptr(w13_packed), _ptr(w2_packed),
                                _ptr(h), _ptr(y_perm), _ptr(ws), ws.numel() if ws is not None else 0,
                                _stream(stream)), "moe_expert_ffn")
+    return h, y_perm
+
+
+def weight_table(weights: Sequence[torch.Tensor]) -> torch.Tensor:
+    """Device table (int64) of the data pointers of per-expert weight buffers,
+    for the *_list calls; the buffers must stay alive while calls use it."""
+    if not weights:
+        raise ValueError("empty weight list")
+    dev = weights[0].device
+    for w in weights:
+        if w.device != dev or not w.is_contiguous():
+            raise ValueError("weight buffers must be contiguous tensors on one device")
+    return torch.tensor([w.data_ptr() for w in weights], dtype=torch.int64, device=dev)
+
+
+def moe_expert_ffn_list(x_perm, offsets, E_loc, max_rows, w13_table, w2_table, d, f, h=None,
+                        y_perm=None, stream=None):
+    """moe_expert_ffn over per-expert weight buffers (tables from weight_table)."""
+    if h is None:
+        h = torch.empty((max(max_rows, 1), f), dtype=x_perm.dtype, device=x_perm.device)
+    if y_perm is None:
+        y_perm = torch.empty((max(max_rows, 1), d), dtype=x_perm.dtype, device=x_perm.device)
+    check(lib().moe_expert_ffn_list(_ptr(x_perm), _ptr(offsets), E_loc, max_rows, d, f,
+                                    _dtype_code(x_perm.dtype), _ptr(w13_table), _ptr(w2_table),
+                                    _ptr(h), _ptr(y_perm), _stream(stream)), "moe_expert_ffn_list")
     return h, y_perm
 
 

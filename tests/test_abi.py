@@ -33,7 +33,7 @@ def test_header_declares_the_path():
     for n in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_router_logits",
               "moe_pack_weights", "moe_check_error", "moe_ffn_up", "moe_ffn_down",
               "moe_forward_fused", "moe_quantize_fp8", "moe_expert_ffn_fp8", "moe_ffn_up_fp8",
-              "moe_ffn_down_fp8"):
+              "moe_ffn_down_fp8", "moe_expert_ffn_list", "moe_ffn_up_list", "moe_ffn_down_list"):
         assert n in names
 
 
@@ -122,6 +122,21 @@ def test_ffn_validation(lib):
     assert f(*f32) == L.MOE_ERR_UNSUPPORTED
     up = lib.moe_ffn_up
     assert up(FAKE, FAKE, 8, -1, 64, 64, L.MOE_BF16, FAKE, FAKE, None, 0, None) == L.MOE_ERR_INVALID_ARG
+
+
+def test_list_validation(lib):
+    f = lib.moe_expert_ffn_list
+    ok = [FAKE, FAKE, 8, 100, 4096, 1024, L.MOE_BF16, FAKE, FAKE, FAKE, FAKE, None]
+    bad = list(ok); bad[7] = None          # no w13 table
+    assert f(*bad) == L.MOE_ERR_INVALID_ARG
+    bad = list(ok); bad[8] = MIS           # misaligned w2 table
+    assert f(*bad) == L.MOE_ERR_MISALIGNED
+    bad = list(ok); bad[4] = 100           # bf16 d % 64
+    assert f(*bad) == L.MOE_ERR_UNSUPPORTED
+    bad = list(ok); bad[6] = 9             # dtype
+    assert f(*bad) == L.MOE_ERR_UNSUPPORTED
+    assert lib.moe_ffn_up_list(FAKE, FAKE, 0, 100, 64, 64, L.MOE_BF16, FAKE, FAKE, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_ffn_down_list(FAKE, FAKE, 8, 100, 64, 64, L.MOE_BF16, None, FAKE, None) == L.MOE_ERR_INVALID_ARG
 
 
 def test_fp8_validation(lib):

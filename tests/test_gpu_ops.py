@@ -137,6 +137,39 @@ def test_expert_ffn(dtype, d, f, rows):
                 assert O.rel_err(as64(h, dtype)[r0:r1], href) <= TOL[dtype]
 
 
+# per-expert weight buffers through a pointer table (TensorList): the same
+# kernels and bits as the packed tensor, and the oracle's values
+@pytest.mark.parametrize("dtype,d,f,rows", [
+    ("bf16", 128, 192, [1024, 1152, 1100, 128, 127, 255, 256, 0, 384, 513]),  # 256-row + remainder tiles
+    ("bf16", 256, 512, [300, 31, 64]),
+    ("bf16", 128, 128, [3, 2, 7, 0, 1, 11, 4, 5, 6, 9]),                        # few rows per expert
+    ("f32", 128, 256, [17, 0, 111])])
+def test_expert_ffn_list(dtype, d, f, rows):
+    log(f"ffn list {dtype} d={d} f={f} rows={rows}")
+    E_loc = len(rows)
+    wl = custom(T=max(sum(rows), 1), d=d, f=f, E=E_loc, k=1, dtype=dtype, seed=7 * d + f)
+    offsets = np.concatenate([[0], np.cumsum(rows)]).astype(np.int32)
+    n = int(offsets[-1])
+    w13, w2p, host = packed_weights(wl, keep_host=True)
+    # one allocation per expert, made in reverse order
+    l13, l2 = [None] * E_loc, [None] * E_loc
+    for i in reversed(range(E_loc)):
+        l13[i] = w13[i].clone()
+        l2[i] = w2p[i].clone()
+    t13, t2 = M.weight_table(l13), M.weight_table(l2)
+    max_rows = n + 3
+    xt = torch.zeros((max(max_rows, 1), d), dtype=w13.dtype, device=DEV)
+    if n:
+        xt[:n] = t_in(wl.x[:n], dtype)
+    off_t = torch.from_numpy(offsets).to(DEV)
+    h0, y0 = M.moe_expert_ffn(xt, off_t, E_loc, max_rows, w13, w2p)
+    h1, y1 = M.moe_expert_ffn_list(xt, off_t, E_loc, max_rows, t13, t2, d, f)
+    assert np.array_equal(t_out(h1)[:n], t_out(h0)[:n])
+    assert np.array_equal(t_out(y1)[:n], t_out(y0)[:n])
+    ref = O.expert_ffn(O.widen(wl.x[:n], dtype), offsets, weights_fn(wl, host))
+    assert O.rel_err(as64(y1, dtype)[:n], ref) <= TOL[dtype]
+
+
 def test_pack_weights_layout():
     wl = custom(T=4, d=64, f=128, E=3, k=1, dtype="bf16", seed=3)
     w13, w2p, host = packed_weights(wl, keep_host=True)
