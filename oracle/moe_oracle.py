@@ -50,6 +50,14 @@ design notes):
   R13 Inside an expert's segment rows ascend in token index.
   R14 Pairs routed to a non-local expert are "remote": kept for capacity
       accounting, absent from the local FFN and from the local combine.
+  R26 Overflow rerouting (the page's stage 3, "replace the full top-1 with the
+      top-3" for top-2): in token order, an expert's load is the number of
+      earlier tokens whose final choice holds it; a token whose best expert
+      has reached the capacity takes its (k+1)-th best instead of the best;
+      the dispatch capacity rule applies afterwards.  (Stage 1's logit
+      threshold and stage 4's random choice stay out: the first changes which
+      experts exist with no rule for fewer than k survivors, the second is
+      not deterministic.)
 
 Parity pins live in tests/test_oracle_*.py (brute force, closed forms,
 invariants, library special cases, the page's worked capacity example).
@@ -122,6 +130,51 @@ def route(logits_f32: np.ndarray, k: int, gate: str) -> Tuple[np.ndarray, np.nda
     sel = np.take_along_axis(l64, order, axis=-1)
     if gate == GATE_SOFTMAX:
         # R5: softmax over the chosen k, shifted by the largest chosen logit
+        z = np.exp(sel - sel[:, :1])
+        w = z / z.sum(axis=1, keepdims=True)
+    elif gate == GATE_SIGMOID:
+        s = 1.0 / (1.0 + np.exp(-sel))
+        w = s / s.sum(axis=1, keepdims=True)
+    else:
+        raise ValueError(gate)
+    return topk_idx, w
+
+
+def route_reroute(logits_f32: np.ndarray, k: int, gate: str,
+                  capacity: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Top-k routing with overflow rerouting (sparse-activation page §3.2,
+    stage 3: when the best expert is already at its capacity limit, the token
+    takes the next expert after its k instead) (R26).
+
+    Tokens are taken in index order.  The load of expert e at token t is the
+    number of earlier tokens whose final choice contains e.  If the best
+    expert's load has reached the capacity (capacity >= 0, k < E), the best
+    expert is replaced by the (k+1)-th best; the other k - 1 stay.  The final k
+    are listed best first and the gates are computed over them exactly as in
+    `route`.  The capacity rule of `dispatch` still applies afterwards (a
+    replacement expert that is itself full drops the pair).
+    """
+    l32 = np.asarray(logits_f32, dtype=np.float32)
+    T, E = l32.shape
+    if not (1 <= k <= E):
+        raise ValueError(f"k={k} outside [1, E={E}]")
+    if not np.all(np.isfinite(l32)):
+        raise ValueError("logits must be finite")
+    l32 = l32 + np.float32(0.0)
+    l64 = l32.astype(np.float64)
+    idx_key = np.broadcast_to(np.arange(E), (T, E))
+    ranked = np.lexsort((idx_key, -l64), axis=-1)[:, :min(k + 1, E)]
+    load = np.zeros(E, dtype=np.int64)
+    topk_idx = np.empty((T, k), dtype=np.int32)
+    for t in range(T):
+        chosen = list(ranked[t, :k])
+        if capacity >= 0 and k < E and load[chosen[0]] >= capacity:
+            chosen = chosen[1:] + [ranked[t, k]]
+        for e in chosen:
+            load[e] += 1
+        topk_idx[t] = chosen
+    sel = np.take_along_axis(l64, topk_idx.astype(np.int64), axis=-1)
+    if gate == GATE_SOFTMAX:
         z = np.exp(sel - sel[:, :1])
         w = z / z.sum(axis=1, keepdims=True)
     elif gate == GATE_SIGMOID:

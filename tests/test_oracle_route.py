@@ -153,3 +153,63 @@ def test_router_logits_one_hot_rows_and_linearity():
     lhs = O.router_logits(2.0 * xa + xb, wg)
     rhs = 2.0 * O.router_logits(xa, wg) + O.router_logits(xb, wg)
     assert np.max(np.abs(lhs - rhs)) < 1e-12
+
+
+# ---------------------------------------------------------------- overflow rerouting (R26)
+def test_reroute_without_pressure_is_plain_routing():
+    rng = np.random.default_rng(11)
+    for T, E, k in [(50, 8, 2), (40, 16, 4), (30, 4, 4)]:
+        logits = rng.standard_normal((T, E)).astype(np.float32)
+        for cap in (-1, T):                      # no limit, or a limit nobody reaches
+            idx, w = O.route_reroute(logits, k, O.GATE_SOFTMAX, cap)
+            ridx, rw = O.route(logits, k, O.GATE_SOFTMAX)
+            assert np.array_equal(idx, ridx) and np.allclose(w, rw, rtol=0, atol=0)
+
+
+def test_reroute_hand_examples():
+    # k = 1, every token prefers 0 > 1 > 2, capacity 2: the third and fourth go to 1
+    l = np.tile(np.array([[2.0, 1.0, 0.0]], np.float32), (4, 1))
+    idx, w = O.route_reroute(l, 1, O.GATE_SOFTMAX, 2)
+    assert idx[:, 0].tolist() == [0, 0, 1, 1] and np.all(w == 1.0)
+    # k = 2, capacity 1 (worked by hand):
+    #   t0 ranks 0,1,2 -> {0,1}; t1 ranks 0,2,3, 0 is full -> {2,3};
+    #   t2 ranks 1,2,3, 1 is full -> {2,3}; t3 ranks 2,3,0, 2 is full -> {3,0}
+    l = np.array([[3, 2, 1, 0], [3, 0, 2, 1], [0, 3, 2, 1], [1, 0, 3, 2]], np.float32)
+    idx, w = O.route_reroute(l, 2, O.GATE_SOFTMAX, 1)
+    assert idx.tolist() == [[0, 1], [2, 3], [2, 3], [3, 0]]
+    e = np.exp(-1.0)
+    assert np.allclose(w[0], [1 / (1 + e), e / (1 + e)], rtol=1e-15)
+    # sigmoid gates over the final pair of t3 (logits 2 and 1)
+    idx, w = O.route_reroute(l, 2, O.GATE_SIGMOID, 1)
+    s2, s1 = 1 / (1 + np.exp(-2.0)), 1 / (1 + np.exp(-1.0))
+    assert np.allclose(w[3], [s2 / (s1 + s2), s1 / (s1 + s2)], rtol=1e-15)
+
+
+def _reroute_brute(logits, k, cap):
+    """The definition with every load recounted from the earlier tokens' final sets."""
+    T, E = logits.shape
+    final = []
+    for t in range(T):
+        ranked = sorted(range(E), key=lambda e: (-float(logits[t, e] + np.float32(0)), e))
+        chosen = ranked[:k]
+        if cap >= 0 and k < E:
+            load = sum(1 for s in final if chosen[0] in s)
+            if load >= cap:
+                chosen = ranked[1:k] + [ranked[k]]
+        final.append(chosen)
+    return np.array(final, np.int32)
+
+
+def test_reroute_matches_brute_force_and_invariants():
+    rng = np.random.default_rng(12)
+    for T, E, k, cap in [(60, 8, 2, 5), (80, 16, 4, 9), (40, 6, 1, 3), (50, 5, 5, 2),
+                         (64, 12, 3, 0)]:
+        logits = (rng.integers(-3, 4, (T, E)) * 0.5).astype(np.float32)   # many ties
+        logits += rng.standard_normal(E).astype(np.float32)               # per-expert skew
+        idx, w = O.route_reroute(logits, k, O.GATE_SOFTMAX, cap)
+        assert np.array_equal(idx, _reroute_brute(logits, k, cap))
+        ridx, _ = O.route(logits, min(k + 1, E), O.GATE_SOFTMAX)
+        for t in range(T):
+            assert len(set(idx[t])) == k and set(idx[t]) <= set(ridx[t])
+            assert set(ridx[t, 1:k]) <= set(idx[t])                        # ranks 2..k always stay
+        assert np.allclose(w.sum(axis=1), 1.0)
