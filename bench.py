@@ -42,6 +42,8 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="mixtral_prefill")
+    p.add_argument("--reroute", action="store_true",
+                   help="route with capacity-overflow rerouting (moe_route_reroute)")
     p.add_argument("--weights", choices=("native", "fp8"), default="native",
                    help="fp8: quantise the packed bf16 expert weights to E4M3 codes with "
                         "128 x 128 block scales (moe_quantize_fp8, untimed) and run the FFN "
@@ -288,6 +290,7 @@ def main():
         log("weights quantised to E4M3 with 128 x 128 block scales")
     layer = M.MoELayer(w13, w2p, E=wl.E, k=wl.k, gate=wl.gate, T=wl.T, capacity=C,
                        w13_scale=s13 if fp8 else None, w2_scale=s2 if fp8 else None,
+                       reroute=args.reroute,
                        e_begin=wl.e_begin, e_end=wl.e_end)
     x = up(wl.x)
     logits = torch.from_numpy(wl.logits).to(dev) if wl.logits is not None else None
@@ -364,7 +367,7 @@ def main():
             ev[1].record()
 
     fused_ms = None
-    if not fp8:   # the fused launch takes bf16 / fp32 weights
+    if not fp8 and not args.reroute:   # the fused launch: bf16 / fp32 weights, plain routing
         for _ in range(args.warmup):
             fused_step()
         torch.cuda.synchronize()
@@ -438,7 +441,8 @@ def main():
         "config": {"workload": wl.name, "tokens": wl.T, "d_model": wl.d, "d_ff": wl.f,
                    "experts": wl.E, "local_experts": wl.E_loc, "top_k": wl.k, "gate": wl.gate,
                    "capacity": C, "parallelism": "single GPU",
-                   "weights": "e4m3 codes, fp32 scale per 128x128 block" if fp8 else wl.dtype},
+                   "weights": "e4m3 codes, fp32 scale per 128x128 block" if fp8 else wl.dtype,
+                   "routing": "top-k with overflow rerouting" if args.reroute else "top-k"},
         "layer_tflops": round(tflops, 2), "layer_mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
         "layer_hbm_gbs": round(gbs, 1), "layer_hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
         "per_step": per, "roofline": roofline, "cpu_baseline": cpu,

@@ -130,6 +130,23 @@ moe_status moe_router_logits(const void* x, const float* w_gate, int T, int d, i
 moe_status moe_route(const float* logits, int T, int E, int k, int gate, int32_t* topk_idx,
                      float* topk_w, void* stream);
 
+/* Top-k routing with capacity-overflow rerouting (sparse-activation page
+ * §3.2, stage 3: when a token's best expert is already at its capacity
+ * limit, the token takes the next expert after its k instead).  Tokens are
+ * taken in index order; the load of an expert is the number of earlier
+ * tokens whose final choice holds it.  If capacity >= 0, k < E and the best
+ * expert's load has reached capacity, the best expert is replaced by the
+ * (k+1)-th best and the other k - 1 stay.  Outputs as moe_route (final
+ * experts best first, gates over the final k).  capacity = -1: plain routing.
+ * Pass the same capacity to moe_dispatch, whose rule still drops pairs whose
+ * expert is full (a replacement can be).  ws: moe_workspace_bytes(T, E, k, .)
+ * bytes (the k + 1 candidates per token and a bit per token are kept there).
+ * The rule is sequential in token order: one wave decides the tokens 64 at a
+ * time; candidates and gates are computed for all tokens in parallel. */
+moe_status moe_route_reroute(const float* logits, int T, int E, int k, int gate, int capacity,
+                             int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes,
+                             void* stream);
+
 /* Dispatch plan and permutation (ThunderEP page §2.1/§2.2: rows packed per
  * owner, per-expert index lists; NCCL EP page §2.2: compact expert-major
  * layout; sparse-activation page §2.3: capacity).

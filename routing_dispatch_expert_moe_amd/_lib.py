@@ -38,6 +38,7 @@ SIGNATURES = {
     "moe_pack_weights": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp]),
     "moe_router_logits": (_i, [_vp, _fp, _i, _i, _i, _fp, _vp]),
     "moe_route": (_i, [_fp, _i, _i, _i, _i, _i32p, _fp, _vp]),
+    "moe_route_reroute": (_i, [_fp, _i, _i, _i, _i, _i, _i32p, _fp, _vp, _sz, _vp]),
     "moe_dispatch": (_i, [_i32p, _i, _i, _i, _i, _i, _i, _vp, _i, _i, _i32p, _i32p, _i32p, _i32p,
                           _i32p, _vp, _vp, _sz, _vp]),
     "moe_expert_ffn": (_i, [_vp, _i32p, _i, _i64, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),

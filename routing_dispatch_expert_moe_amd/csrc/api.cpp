@@ -140,7 +140,7 @@ int moe_last_hip_error(void) { return g_last_hip_error; }
 size_t moe_workspace_bytes(int T, int E, int k, int E_loc) {
   if (T < 0 || E < 1 || E > MOE_MAX_E || k < 1 || k > MOE_MAX_K || k > E || E_loc < 1 || E_loc > E)
     return 0;
-  return moe::dispatch_ws_bytes(T, E);
+  return moe::dispatch_ws_bytes(T, E) + moe::reroute_ws_bytes(T, k);
 }
 
 int64_t moe_capacity(int T, int k, int E, int64_t cf_num, int64_t cf_den) {
@@ -297,6 +297,30 @@ moe_status moe_expert_ffn_fp8(const void* x_perm, const int32_t* offsets, int E_
   st = moe_ffn_up_fp8(x_perm, offsets, E_loc, max_rows, d, f, w13_q, w13_s, h, stream);
   if (st != MOE_OK) return st;
   return moe_ffn_down_fp8(h, offsets, E_loc, max_rows, d, f, w2_q, w2_s, y_perm, stream);
+}
+
+moe_status moe_route_reroute(const float* logits, int T, int E, int k, int gate, int capacity,
+                             int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes,
+                             void* stream) {
+  moe_status st = check_topk(E, k);
+  if (st != MOE_OK) return st;
+  if (T < 0 || capacity < -1 || (gate != MOE_GATE_SOFTMAX_TOPK_RENORM &&
+                                 gate != MOE_GATE_SIGMOID_TOPK_NORM))
+    return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!logits || !topk_idx || !topk_w || !ws) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(logits) || !aligned16(topk_idx) || !aligned16(topk_w) || !aligned16(ws))
+    return MOE_ERR_MISALIGNED;
+  const size_t off = moe::dispatch_ws_bytes(T, E);
+  if (ws_bytes < off + moe::reroute_ws_bytes(T, k)) return MOE_ERR_WORKSPACE;
+  char* c = static_cast<char*>(ws) + off;
+  const size_t n = static_cast<size_t>(T) * (k + 1);
+  const size_t cand_bytes = (n * sizeof(int32_t) + 255) & ~static_cast<size_t>(255);
+  int32_t* cand_e = reinterpret_cast<int32_t*>(c);
+  float* cand_v = reinterpret_cast<float*>(c + cand_bytes);
+  uint64_t* rerouted = reinterpret_cast<uint64_t*>(c + 2 * cand_bytes);
+  return hip_status(moe::launch_route_reroute(logits, T, E, k, gate, capacity, topk_idx, topk_w,
+                                              cand_e, cand_v, rerouted, stream));
 }
 
 moe_status moe_ffn_up_list(const void* x_perm, const int32_t* offsets, int E_loc,

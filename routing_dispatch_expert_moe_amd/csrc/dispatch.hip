@@ -10,6 +10,12 @@ size_t dispatch_ws_bytes(int T, int E) {
   return (b + 255) & ~static_cast<size_t>(255);
 }
 
+size_t reroute_ws_bytes(int T, int k) {
+  const size_t n = static_cast<size_t>(T) * (k + 1);
+  const size_t masks = (static_cast<size_t>(T) + 63) / 64 * sizeof(uint64_t);
+  return 2 * ((n * 4 + 255) & ~static_cast<size_t>(255)) + ((masks + 255) & ~static_cast<size_t>(255));
+}
+
 DispatchWs dispatch_ws(void* ws, int T, int E) {
   const size_t nb = (static_cast<size_t>(T) + kTB - 1) / kTB;
   char* p = static_cast<char*>(ws);

@@ -24,6 +24,13 @@ int launch_router_logits(const void* x, const float* wg, int T, int d, int E, fl
                          void* stream);
 int launch_route(const float* logits, int T, int E, int k, int gate, int32_t* idx, float* w,
                  void* stream);
+// routing with overflow rerouting; cand_e / cand_v: [T][k+1] scratch,
+// rerouted: ceil(T / 64) scratch masks
+int launch_route_reroute(const float* logits, int T, int E, int k, int gate, int capacity,
+                         int32_t* idx, float* w, int32_t* cand_e, float* cand_v,
+                         uint64_t* rerouted, void* stream);
+// workspace bytes of the rerouting candidates, placed after the dispatch scratch
+size_t reroute_ws_bytes(int T, int k);
 int launch_dispatch(const int32_t* idx, int T, int E, int k, int capacity, int e_begin,
                     int e_end, const void* x, int d, int elem_bytes, int32_t* counts,
                     int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos, int32_t* n_kept,

@@ -25,11 +25,11 @@ __device__ __forceinline__ float from_ordered(uint32_t o) {
   return __uint_as_float(u);
 }
 
-// Top-k and gates of token t, computed by one whole wave (E <= 64 * EPL).
-template <int EPL>
-__device__ __forceinline__ void route_token(const float* __restrict__ logits, int t, int E, int k,
-                                            int gate, int32_t* __restrict__ topk_idx,
-                                            float* __restrict__ topk_w) {
+// The kc best experts of token t (best first) and their logits, by one whole
+// wave (E <= 64 * EPL, kc <= KMAX); entries past kc are 0.
+template <int EPL, int KMAX>
+__device__ __forceinline__ void select_top(const float* __restrict__ logits, int t, int E, int kc,
+                                           int (&sel_e)[KMAX], float (&sel_v)[KMAX]) {
   const int lane = lane_id();
   const float* row = logits + (size_t)t * E;
   uint64_t key[EPL];
@@ -39,11 +39,9 @@ __device__ __forceinline__ void route_token(const float* __restrict__ logits, in
     key[i] = 0;
     if (e < E) key[i] = (static_cast<uint64_t>(ordered_bits(row[e])) << 32) | static_cast<uint32_t>(~e);
   }
-  int sel_e[MOE_MAX_K];
-  float sel_v[MOE_MAX_K];
 #pragma unroll
-  for (int j = 0; j < MOE_MAX_K; ++j) {
-    if (j < k) {
+  for (int j = 0; j < KMAX; ++j) {
+    if (j < kc) {
       uint64_t best = 0;
 #pragma unroll
       for (int i = 0; i < EPL; ++i) best = key[i] > best ? key[i] : best;
@@ -58,6 +56,17 @@ __device__ __forceinline__ void route_token(const float* __restrict__ logits, in
       sel_v[j] = 0.f;
     }
   }
+}
+
+// Top-k and gates of token t, computed by one whole wave (E <= 64 * EPL).
+template <int EPL>
+__device__ __forceinline__ void route_token(const float* __restrict__ logits, int t, int E, int k,
+                                            int gate, int32_t* __restrict__ topk_idx,
+                                            float* __restrict__ topk_w) {
+  const int lane = lane_id();
+  int sel_e[MOE_MAX_K];
+  float sel_v[MOE_MAX_K];
+  select_top<EPL, MOE_MAX_K>(logits, t, E, k, sel_e, sel_v);
   float g[MOE_MAX_K];
   float sum = 0.f;
   if (gate == 0) {

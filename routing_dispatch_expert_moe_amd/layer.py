@@ -20,12 +20,15 @@ from . import ops
 class MoELayer:
     def __init__(self, w13_packed: torch.Tensor, w2_packed: torch.Tensor, *, E: int, k: int,
                  gate, T: int, capacity: int = -1, e_begin: int = 0, e_end: Optional[int] = None,
-                 w13_scale: Optional[torch.Tensor] = None, w2_scale: Optional[torch.Tensor] = None):
+                 w13_scale: Optional[torch.Tensor] = None, w2_scale: Optional[torch.Tensor] = None,
+                 reroute: bool = False):
         self.w13, self.w2 = w13_packed, w2_packed
         self.fp8 = w13_packed.dtype == torch.uint8
         if self.fp8 and (w13_scale is None or w2_scale is None):
             raise ValueError("FP8 weights need their block scales")
         self.w13_scale, self.w2_scale = w13_scale, w2_scale
+        # route with capacity-overflow rerouting (moe_route_reroute) instead of plain top-k
+        self.reroute = reroute
         self.E, self.k, self.gate, self.T = E, k, gate, T
         self.capacity = capacity
         self.e_begin = e_begin
@@ -52,6 +55,9 @@ class MoELayer:
         return ops.moe_router_logits(x, w_gate, self.logits)
 
     def route(self, logits):
+        if self.reroute:
+            return ops.moe_route_reroute(logits, self.k, self.gate, self.capacity, self.ws,
+                                         self.topk_idx, self.topk_w)
         return ops.moe_route(logits, self.k, self.gate, self.topk_idx, self.topk_w)
 
     def dispatch(self, x):
@@ -94,8 +100,8 @@ class MoELayer:
         """route -> dispatch -> expert FFN -> combine as one persistent launch."""
         if x.shape[0] != self.T:
             raise ValueError(f"layer was sized for T={self.T}, got {x.shape[0]}")
-        if self.fp8:
-            raise NotImplementedError("the fused launch takes bf16 or fp32 weights")
+        if self.fp8 or self.reroute:
+            raise NotImplementedError("the fused launch takes bf16 / fp32 weights and plain top-k routing")
         return ops.moe_forward_fused(logits, x, self.k, self.gate, self.capacity, self.e_begin,
                                      self.e_end, self.w13, self.w2, self.ws, self.plan,
                                      self.topk_idx, self.topk_w, self.h, self.y_perm, self.y)

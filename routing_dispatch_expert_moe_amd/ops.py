@@ -129,6 +129,25 @@ class DispatchPlan:
     max_rows: int
 
 
+
+def moe_route_reroute(logits: torch.Tensor, k: int, gate, capacity: int, ws: torch.Tensor,
+                      topk_idx: Optional[torch.Tensor] = None,
+                      topk_w: Optional[torch.Tensor] = None,
+                      stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Top-k routing with capacity-overflow rerouting (see include/moe.h)."""
+    T, E = logits.shape
+    if logits.dtype != torch.float32:
+        raise TypeError("logits must be fp32")
+    if topk_idx is None:
+        topk_idx = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+    if topk_w is None:
+        topk_w = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    check(lib().moe_route_reroute(_ptr(logits), T, E, k, _gate_code(gate), capacity,
+                                  _ptr(topk_idx), _ptr(topk_w), _ptr(ws), ws.numel(),
+                                  _stream(stream)), "moe_route_reroute")
+    return topk_idx, topk_w
+
+
 def alloc_plan(T: int, E: int, k: int, E_loc: int, capacity: int, d: int, dtype,
                device="cuda") -> DispatchPlan:
     rows = moe_max_rows(T, k, E_loc, capacity)

@@ -33,7 +33,8 @@ def test_header_declares_the_path():
     for n in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_router_logits",
               "moe_pack_weights", "moe_check_error", "moe_ffn_up", "moe_ffn_down",
               "moe_forward_fused", "moe_quantize_fp8", "moe_expert_ffn_fp8", "moe_ffn_up_fp8",
-              "moe_ffn_down_fp8", "moe_expert_ffn_list", "moe_ffn_up_list", "moe_ffn_down_list"):
+              "moe_ffn_down_fp8", "moe_expert_ffn_list", "moe_ffn_up_list", "moe_ffn_down_list",
+              "moe_route_reroute"):
         assert n in names
 
 
@@ -96,7 +97,7 @@ def test_dispatch_validation(lib):
                  a["wsb"], None)
 
     assert call() == L.MOE_ERR_WORKSPACE
-    assert call(wsb=M.moe_workspace_bytes(10, 8, 2, 8) - 1) == L.MOE_ERR_WORKSPACE
+    assert call(wsb=2047) == L.MOE_ERR_WORKSPACE    # smaller than the 2 KiB header
     assert call(k=9) == L.MOE_ERR_INVALID_TOPK
     assert call(e0=3, e1=3) == L.MOE_ERR_INVALID_ARG
     assert call(e1=9) == L.MOE_ERR_INVALID_ARG
@@ -122,6 +123,27 @@ def test_ffn_validation(lib):
     assert f(*f32) == L.MOE_ERR_UNSUPPORTED
     up = lib.moe_ffn_up
     assert up(FAKE, FAKE, 8, -1, 64, 64, L.MOE_BF16, FAKE, FAKE, None, 0, None) == L.MOE_ERR_INVALID_ARG
+
+
+def test_reroute_validation(lib):
+    r = lib.moe_route_reroute
+    need = lib.moe_workspace_bytes(100, 8, 2, 8)
+    ok = [FAKE, 100, 8, 2, 0, 30, FAKE, FAKE, FAKE, need, None]
+    bad = list(ok); bad[3] = 9
+    assert r(*bad) == L.MOE_ERR_INVALID_TOPK
+    bad = list(ok); bad[4] = 3             # gate
+    assert r(*bad) == L.MOE_ERR_INVALID_ARG
+    bad = list(ok); bad[5] = -2            # capacity
+    assert r(*bad) == L.MOE_ERR_INVALID_ARG
+    bad = list(ok); bad[9] = need - 1
+    assert r(*bad) == L.MOE_ERR_WORKSPACE
+    bad = list(ok); bad[8] = None
+    assert r(*bad) == L.MOE_ERR_INVALID_ARG
+    bad = list(ok); bad[0] = MIS
+    assert r(*bad) == L.MOE_ERR_MISALIGNED
+    assert r(None, 0, 8, 2, 0, 30, None, None, None, 0, None) == L.MOE_OK   # empty batch
+    # the workspace holds the k + 1 candidates per token beyond the dispatch scratch
+    assert lib.moe_workspace_bytes(1000, 8, 8, 8) - lib.moe_workspace_bytes(1000, 8, 1, 8) >= 1000 * 7 * 8 - 512
 
 
 def test_list_validation(lib):
@@ -200,7 +222,7 @@ def test_fused_validation(lib):
     assert call(ws=None) == L.MOE_ERR_INVALID_ARG
     assert call(y=MIS) == L.MOE_ERR_MISALIGNED
     assert call(h=MIS) == L.MOE_ERR_MISALIGNED
-    assert call(wsb=ws_ok - 1) == L.MOE_ERR_WORKSPACE
+    assert call(wsb=2047) == L.MOE_ERR_WORKSPACE
     # bf16 operands beyond 32-bit byte offsets are refused up front
     assert call(T=600000, k=8, E=8, d=4096, f=4096) == L.MOE_ERR_UNSUPPORTED
 

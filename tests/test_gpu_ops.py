@@ -11,7 +11,7 @@ import torch
 
 import routing_dispatch_expert_moe_amd as M
 from oracle import moe_oracle as O
-from workloads import custom
+from workloads import custom, make
 
 from gpu_util import DEV, as64, capacity_of, layer_for, log, packed_weights, t_in, t_out, weights_fn
 
@@ -46,6 +46,51 @@ def test_route(T, E, k, gate, kind):
     ridx, rw = O.route(logits, k, gate)
     assert np.array_equal(t_out(idx), ridx)
     assert O.rel_err(t_out(w), rw) <= GATE_TOL
+
+
+# routing with capacity-overflow rerouting: indices bit-exact, gates 1e-6,
+# and the dispatch plan that follows it
+@pytest.mark.parametrize("T,E,k,gate,cap", [
+    (200, 8, 2, O.GATE_SOFTMAX, 30), (257, 16, 4, O.GATE_SIGMOID, 40), (130, 64, 8, O.GATE_SOFTMAX, 5),
+    (100, 4, 4, O.GATE_SOFTMAX, 10),          # k == E: nothing to reroute to
+    (64, 8, 1, O.GATE_SIGMOID, 0),            # capacity 0: every token reroutes
+    (77, 1024, 8, O.GATE_SIGMOID, 1), (300, 32, 2, O.GATE_SOFTMAX, -1),
+    # several LDS chunks of candidates (1024, 768 and 384 tokens for k = 1..2, 4, 8), ragged last
+    (2500, 16, 2, O.GATE_SOFTMAX, 250), (3001, 8, 1, O.GATE_SIGMOID, 330),
+    (1000, 32, 4, O.GATE_SIGMOID, 110), (1700, 64, 8, O.GATE_SOFTMAX, 190)])
+@pytest.mark.parametrize("kind", ["skewed", "ties"])
+def test_route_reroute(T, E, k, gate, cap, kind):
+    log(f"reroute T={T} E={E} k={k} {gate} cap={cap} {kind}")
+    rng = np.random.default_rng(T + E + k)
+    if kind == "skewed":
+        logits = (rng.standard_normal((T, E)) + rng.standard_normal(E) * 1.5).astype(np.float32)
+    else:
+        logits = (rng.integers(-2, 3, size=(T, E)) * 0.5).astype(np.float32)
+    ws = M.alloc_workspace(T, E, k, E)
+    idx, w = M.moe_route_reroute(t_in(logits, "f32"), k, gate, cap, ws)
+    ridx, rw = O.route_reroute(logits, k, gate, cap)
+    assert np.array_equal(t_out(idx), ridx)
+    assert O.rel_err(t_out(w), rw) <= GATE_TOL
+    plan = M.moe_dispatch(idx, E, cap, 0, E, None, ws, d=64)
+    ref = O.dispatch(ridx, E, cap, 0, E)
+    assert np.array_equal(t_out(plan.offsets), ref["offsets"])
+    assert np.array_equal(t_out(plan.pair_pos)[:T * k], ref["pair_pos"])
+    assert M.moe_check_error(ws) == 0
+
+
+def test_route_reroute_ep_rank_shape():
+    # the EP-rank routing shape (T 16384, E 128, k 2, capacity 320, biased logits)
+    wl = make("ep_rank_share")
+    C = M.moe_capacity(wl.T, wl.k, wl.E, wl.capacity_factor)
+    ws = M.alloc_workspace(wl.T, wl.E, wl.k, wl.E_loc)
+    idx, w = M.moe_route_reroute(t_in(wl.logits, "f32"), wl.k, wl.gate, C, ws)
+    ridx, rw = O.route_reroute(wl.logits, wl.k, wl.gate, C)
+    assert np.array_equal(t_out(idx), ridx)
+    assert O.rel_err(t_out(w), rw) <= GATE_TOL
+    base, _ = O.route(wl.logits, wl.k, wl.gate)
+    moved = int((ridx[:, 0] != base[:, 0]).sum())
+    log(f"reroute at the EP-rank shape: {moved} of {wl.T} tokens took their third expert")
+    assert moved > 0
 
 
 def test_route_all_equal_rows_exact():
