@@ -128,16 +128,20 @@ def route(logits_f32: np.ndarray, k: int, gate: str) -> Tuple[np.ndarray, np.nda
     order = np.lexsort((idx_key, -l64), axis=-1)[:, :k]
     topk_idx = order.astype(np.int32)
     sel = np.take_along_axis(l64, order, axis=-1)
+    return topk_idx, gate_values(sel, gate)
+
+
+def gate_values(sel: np.ndarray, gate: str) -> np.ndarray:
+    """Gate weights [T, k] from the chosen logits [T, k] (best first), float64 (R5, R6)."""
+    sel = np.asarray(sel, dtype=np.float64)
     if gate == GATE_SOFTMAX:
         # R5: softmax over the chosen k, shifted by the largest chosen logit
         z = np.exp(sel - sel[:, :1])
-        w = z / z.sum(axis=1, keepdims=True)
-    elif gate == GATE_SIGMOID:
+        return z / z.sum(axis=1, keepdims=True)
+    if gate == GATE_SIGMOID:
         s = 1.0 / (1.0 + np.exp(-sel))
-        w = s / s.sum(axis=1, keepdims=True)
-    else:
-        raise ValueError(gate)
-    return topk_idx, w
+        return s / s.sum(axis=1, keepdims=True)
+    raise ValueError(gate)
 
 
 def route_reroute(logits_f32: np.ndarray, k: int, gate: str,
@@ -174,15 +178,7 @@ def route_reroute(logits_f32: np.ndarray, k: int, gate: str,
             load[e] += 1
         topk_idx[t] = chosen
     sel = np.take_along_axis(l64, topk_idx.astype(np.int64), axis=-1)
-    if gate == GATE_SOFTMAX:
-        z = np.exp(sel - sel[:, :1])
-        w = z / z.sum(axis=1, keepdims=True)
-    elif gate == GATE_SIGMOID:
-        s = 1.0 / (1.0 + np.exp(-sel))
-        w = s / s.sum(axis=1, keepdims=True)
-    else:
-        raise ValueError(gate)
-    return topk_idx, w
+    return topk_idx, gate_values(sel, gate)
 
 
 # --------------------------------------------------------------------------
