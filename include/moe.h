@@ -248,7 +248,9 @@ moe_status moe_ffn_down_fp8(const void* h, const int32_t* offsets, int E_loc, in
 /* Weighted combine (NCCL EP page §2.1, LL combine):
  *   y[t] = sum_{j=0..k-1, pair_pos[t*k+j] >= 0} topk_w[t][j] * y_perm[pair_pos[t*k+j]]
  * accumulated in fp32 in ascending j, rounded once to `dtype`; tokens with no
- * local kept pair get zero rows.  y: [T][d] (output). */
+ * local kept pair get zero rows.  y: [T][d] (output).  topk_w may be NULL:
+ * every weight is then 1 (the backward pass sums a token's input-gradient
+ * rows this way). */
 moe_status moe_combine(const void* y_perm, const int32_t* pair_pos, const float* topk_w, int T,
                        int k, int d, moe_dtype dtype, void* y, void* stream);
 
@@ -284,6 +286,113 @@ moe_status moe_forward_fused(const float* logits, const void* x, int T, int E, i
                              int32_t* sorted_pair, int32_t* pair_pos, int32_t* n_kept,
                              void* h, void* y_perm, void* y, void* ws, size_t ws_bytes,
                              void* stream);
+
+/* ------------------------------------------------------------------------
+ * Backward pass (NCCL EP page §3.2, training adaptation: the backward step
+ * reuses the forward's routing handle, sends the output gradient to the
+ * experts through it, runs the experts' backward and brings the input
+ * gradients back through the same handle).  Here the handle is the forward's
+ * dispatch plan (offsets, pair_pos) and its saved tensors (x_perm, the
+ * pre-activations ab, h, y_perm, topk_idx, topk_w).  What is computed is the
+ * exact gradient of the forward layer at the given point with the routing
+ * decisions (top-k sets, capacity drops, local/remote split) held fixed.
+ * One training step on one stream:
+ *
+ *   forward : router_logits -> route -> dispatch -> ffn_up_train -> ffn_down -> combine
+ *   backward: combine_backward -> gate_backward -> [router_backward]
+ *             ffn_down_backward -> ffn_up_backward -> combine(topk_w = NULL) -> dx
+ *             ffn_wgrad (dW13, dW2)
+ *
+ * Rounding points: do_perm, dh, dab, dx_perm and dx are stored in the layer
+ * dtype (fp32 accumulation inside each call); dgate, dlogits, the weight
+ * gradients and dW_g are fp32.  Conventions as above (caller-owned, 16-byte
+ * aligned device buffers; nothing is allocated; host validation first).
+ * ------------------------------------------------------------------------ */
+
+/* moe_ffn_up with the pre-activations kept for the backward pass: h as
+ * moe_ffn_up, and ab [max_rows][2f] (layer dtype): row r holds a = x W1 in
+ * columns [0, f) and g = x W3 in [f, 2f) (before SwiGLU; bf16: rounded from
+ * the same fp32 sums that h is computed from).  bf16 needs max_rows * 2f * 2,
+ * max_rows * d * 2 and 4 * f * d below 2^32 (else MOE_ERR_UNSUPPORTED). */
+moe_status moe_ffn_up_train(const void* x_perm, const int32_t* offsets, int E_loc,
+                            int64_t max_rows, int d, int f, moe_dtype dtype,
+                            const void* w13_packed, void* h, void* ab, void* stream);
+
+/* The first FFN half's backward operand: w13_t [E_loc][d][2f] with row c =
+ * W1[e][c][0..f) followed by W3[e][c][0..f) (w1, w3: [E_loc][d][f], the
+ * layout moe_pack_weights reads).  The second half's backward operand is W2
+ * itself, [E_loc][f][d], so it needs no re-layout.  f * elem_bytes must be a
+ * multiple of 16. */
+moe_status moe_pack_weights_backward(const void* w1, const void* w3, int E_loc, int d, int f,
+                                     moe_dtype dtype, void* w13_t, void* stream);
+
+/* Backward of moe_combine.  dy: [T][d] (layer dtype).  For every pair p =
+ * t*k + j with a local row r = pair_pos[p] >= 0:
+ *   do_perm[r]  = topk_w[t][j] * dy[t]            (rounded once to dtype)
+ *   dgate[t][j] = sum_c dy[t][c] * y_perm[r][c]    (fp32)
+ * Pairs without a local row get dgate 0 (their gradient, if remote, comes
+ * from the rank that holds the expert) and no do_perm row.  y_perm: the
+ * forward's unweighted expert outputs.  do_perm rows not named by pair_pos
+ * are left untouched. */
+moe_status moe_combine_backward(const void* dy, const void* y_perm, const int32_t* pair_pos,
+                                const float* topk_w, int T, int k, int d, moe_dtype dtype,
+                                void* do_perm, float* dgate, void* stream);
+
+/* Backward of the gate functions of moe_route / moe_route_reroute: dlogits
+ * [T][E] fp32 from dgate [T][k], with the gates recomputed from the chosen
+ * logits (the experts in topk_idx):
+ *   softmax-renorm: dl_j = w_j (dg_j - sum_i w_i dg_i)
+ *   sigmoid-norm:   dl_j = s_j (1 - s_j) (dg_j - sum_i w_i dg_i) / sum_i s_i
+ * and 0 for every expert not chosen (the selection is piecewise constant). */
+moe_status moe_gate_backward(const float* logits, const int32_t* topk_idx, const float* dgate,
+                             int T, int E, int k, int gate, float* dlogits, void* stream);
+
+/* Backward through the second FFN half and SwiGLU: dh = do_perm . W2^T per
+ * expert segment (the down GEMM with the roles of d and f swapped; w2_t =
+ * W2 in its logical layout [E_loc][f][d]), then from the saved
+ * pre-activations ab (moe_ffn_up_train), with s = sigmoid(a):
+ *   da = dh * g * s * (1 + a (1 - s)),   dg = dh * a * s
+ * written as dab [max_rows][2f] (da then dg).  dh: [max_rows][f] (output).
+ * Shape rules as moe_ffn_down. */
+moe_status moe_ffn_down_backward(const void* do_perm, const int32_t* offsets, int E_loc,
+                                 int64_t max_rows, int d, int f, moe_dtype dtype,
+                                 const void* w2_t, const void* ab, void* dh, void* dab,
+                                 void* stream);
+
+/* Input gradient of the first FFN half: dx_perm = dab . [W1 | W3]^T per expert
+ * segment, i.e. da W1^T + dg W3^T (w13_t from moe_pack_weights_backward).
+ * dx_perm: [max_rows][d] (output).  moe_combine(dx_perm, pair_pos, NULL, ...)
+ * then gives each token's dx. */
+moe_status moe_ffn_up_backward(const void* dab, const int32_t* offsets, int E_loc,
+                               int64_t max_rows, int d, int f, moe_dtype dtype,
+                               const void* w13_t, void* dx_perm, void* stream);
+
+/* Expert weight gradients, in the packed layouts of the forward weights, fp32:
+ *   dw13[e] [2f][d]: rows n < f are dW1^T (dW1 = x_perm_e^T da_e), rows
+ *                    f + n are dW3^T (dW3 = x_perm_e^T dg_e)
+ *   dw2[e]  [d][f]:  dW2^T (dW2 = h_e^T do_e)
+ * summed over each expert's rows (offsets); an expert with no rows gets
+ * zeros.  x_perm [max_rows][d], h [max_rows][f], do_perm [max_rows][d], dab
+ * [max_rows][2f] in the layer dtype.  ws: moe_wgrad_workspace_bytes bytes
+ * (bf16: the operands transposed so the reduction over rows runs along
+ * memory; fp32: a small segment table).  Shape rules as moe_expert_ffn. */
+size_t moe_wgrad_workspace_bytes(int64_t max_rows, int E_loc, int d, int f, moe_dtype dtype);
+moe_status moe_ffn_wgrad(const void* x_perm, const void* h, const void* do_perm, const void* dab,
+                         const int32_t* offsets, int E_loc, int64_t max_rows, int d, int f,
+                         moe_dtype dtype, float* dw13, float* dw2, void* ws, size_t ws_bytes,
+                         void* stream);
+
+/* Backward of moe_router_logits (sparse-activation page §3.1 router row, §5.3
+ * fp32 router): with dlogits [T][E] fp32,
+ *   dx[t][c]   += sum_e dlogits[t][e] * w_gate[c][e]   (fp32 sum added to dx's
+ *                 value, rounded once more to dtype)
+ *   dw_gate[c][e] = sum_t x[t][c] * dlogits[t][e]      (fp32, fixed order)
+ * E <= 64, d a multiple of 8.  ws: moe_router_backward_workspace_bytes bytes
+ * (per-64-token partial sums of dw_gate, added in order: no atomics). */
+size_t moe_router_backward_workspace_bytes(int T, int d, int E);
+moe_status moe_router_backward(const void* x, const float* w_gate, const float* dlogits, int T,
+                               int d, int E, moe_dtype dtype, void* dx, float* dw_gate, void* ws,
+                               size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

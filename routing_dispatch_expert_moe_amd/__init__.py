@@ -10,4 +10,7 @@ from .ops import (alloc_plan, alloc_workspace, moe_check_error, moe_combine, moe
                   moe_capacity, moe_expert_ffn, moe_ffn_down, moe_ffn_up, moe_max_rows, moe_pack_weights,
                   moe_route, moe_router_logits, moe_workspace_bytes, moe_quantize_fp8,
                   moe_expert_ffn_fp8, moe_ffn_up_fp8, moe_ffn_down_fp8, moe_expert_ffn_list,
-                  weight_table, moe_route_reroute)
+                  weight_table, moe_route_reroute, moe_ffn_up_train, moe_pack_weights_backward,
+                  moe_combine_backward, moe_gate_backward, moe_ffn_down_backward,
+                  moe_ffn_up_backward, moe_ffn_wgrad, moe_wgrad_workspace_bytes,
+                  moe_router_backward, moe_router_backward_workspace_bytes)

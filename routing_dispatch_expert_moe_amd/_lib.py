@@ -53,6 +53,17 @@ SIGNATURES = {
     "moe_expert_ffn_fp8": (_i, [_vp, _i32p, _i, _i64, _i, _i, _vp, _fp, _vp, _fp, _vp, _vp, _vp]),
     "moe_ffn_up_fp8": (_i, [_vp, _i32p, _i, _i64, _i, _i, _vp, _fp, _vp, _vp]),
     "moe_ffn_down_fp8": (_i, [_vp, _i32p, _i, _i64, _i, _i, _vp, _fp, _vp, _vp]),
+    "moe_ffn_up_train": (_i, [_vp, _i32p, _i, _i64, _i, _i, _i, _vp, _vp, _vp, _vp]),
+    "moe_pack_weights_backward": (_i, [_vp, _vp, _i, _i, _i, _i, _vp, _vp]),
+    "moe_combine_backward": (_i, [_vp, _vp, _i32p, _fp, _i, _i, _i, _i, _vp, _fp, _vp]),
+    "moe_gate_backward": (_i, [_fp, _i32p, _fp, _i, _i, _i, _i, _fp, _vp]),
+    "moe_ffn_down_backward": (_i, [_vp, _i32p, _i, _i64, _i, _i, _i, _vp, _vp, _vp, _vp, _vp]),
+    "moe_ffn_up_backward": (_i, [_vp, _i32p, _i, _i64, _i, _i, _i, _vp, _vp, _vp]),
+    "moe_wgrad_workspace_bytes": (_sz, [_i64, _i, _i, _i, _i]),
+    "moe_ffn_wgrad": (_i, [_vp, _vp, _vp, _vp, _i32p, _i, _i64, _i, _i, _i, _fp, _fp, _vp, _sz,
+                           _vp]),
+    "moe_router_backward_workspace_bytes": (_sz, [_i, _i, _i]),
+    "moe_router_backward": (_i, [_vp, _fp, _fp, _i, _i, _i, _i, _vp, _fp, _vp, _sz, _vp]),
     "moe_forward_fused": (_i, [_fp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _i32p,
                                _fp, _i32p, _i32p, _i32p, _i32p, _i32p, _vp, _vp, _vp, _vp, _sz,
                                _vp]),

@@ -358,7 +358,7 @@ moe_status moe_combine(const void* y_perm, const int32_t* pair_pos, const float*
   if (!elem_ok(dtype)) return MOE_ERR_UNSUPPORTED;
   if ((static_cast<int64_t>(d) * elem_bytes(dtype)) % 16 != 0) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
-  if (!pair_pos || !topk_w || !y) return MOE_ERR_INVALID_ARG;
+  if (!pair_pos || !y) return MOE_ERR_INVALID_ARG;  // topk_w null: unit weights
   if (!aligned16(y_perm) || !aligned16(pair_pos) || !aligned16(topk_w) || !aligned16(y))
     return MOE_ERR_MISALIGNED;
   return hip_status(moe::launch_combine(y_perm, pair_pos, topk_w, T, k, d, dtype == MOE_BF16, y,
@@ -375,6 +375,139 @@ moe_status moe_check_error(void* ws, void* stream) {
   if (flags & (1 << MOE_ERR_HIP)) return MOE_ERR_HIP;
   if (flags != 0) return MOE_ERR_INVALID_ARG;
   return MOE_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Backward pass
+// ---------------------------------------------------------------------------
+
+moe_status moe_ffn_up_train(const void* x_perm, const int32_t* offsets, int E_loc,
+                            int64_t max_rows, int d, int f, moe_dtype dtype,
+                            const void* w13_packed, void* h, void* ab, void* stream) {
+  moe_status st = check_ffn(x_perm, offsets, E_loc, max_rows, d, f, dtype, w13_packed, h);
+  if (st != MOE_OK) return st;
+  if (max_rows > 0 && !ab) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(ab)) return MOE_ERR_MISALIGNED;
+  if (dtype == MOE_BF16) {
+    const double rows = static_cast<double>(max_rows);
+    if (rows * d * 2 >= 4294967296.0 || rows * 2 * f * 2 >= 4294967296.0 ||
+        2.0 * f * d * 2 >= 4294967296.0)
+      return MOE_ERR_UNSUPPORTED;  // the pipelined GEMM addresses operands with 32-bit offsets
+    return hip_status(moe::launch_ffn_up_train_bf16(x_perm, offsets, E_loc, max_rows, d, f,
+                                                    w13_packed, h, ab, stream));
+  }
+  return hip_status(moe::launch_ffn_up_train_f32(
+      static_cast<const float*>(x_perm), offsets, E_loc, max_rows, d, f,
+      static_cast<const float*>(w13_packed), static_cast<float*>(h), static_cast<float*>(ab),
+      stream));
+}
+
+moe_status moe_pack_weights_backward(const void* w1, const void* w3, int E_loc, int d, int f,
+                                     moe_dtype dtype, void* w13_t, void* stream) {
+  if (!elem_ok(dtype)) return MOE_ERR_UNSUPPORTED;
+  if (E_loc < 1 || E_loc > MOE_MAX_E || d < 1 || f < 1) return MOE_ERR_INVALID_ARG;
+  if ((static_cast<int64_t>(f) * elem_bytes(dtype)) % 16 != 0) return MOE_ERR_UNSUPPORTED;
+  if (!w1 || !w3 || !w13_t) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(w1) || !aligned16(w3) || !aligned16(w13_t)) return MOE_ERR_MISALIGNED;
+  return hip_status(moe::launch_pack_backward(w1, w3, E_loc, d, f, elem_bytes(dtype), w13_t,
+                                              stream));
+}
+
+moe_status moe_combine_backward(const void* dy, const void* y_perm, const int32_t* pair_pos,
+                                const float* topk_w, int T, int k, int d, moe_dtype dtype,
+                                void* do_perm, float* dgate, void* stream) {
+  if (T < 0 || d < 1 || k < 1 || k > MOE_MAX_K) return MOE_ERR_INVALID_ARG;
+  if (!elem_ok(dtype)) return MOE_ERR_UNSUPPORTED;
+  if ((static_cast<int64_t>(d) * elem_bytes(dtype)) % 16 != 0) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!dy || !pair_pos || !topk_w || !dgate) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(dy) || !aligned16(y_perm) || !aligned16(pair_pos) || !aligned16(topk_w) ||
+      !aligned16(do_perm) || !aligned16(dgate))
+    return MOE_ERR_MISALIGNED;
+  return hip_status(moe::launch_combine_backward(dy, y_perm, pair_pos, topk_w, T, k, d,
+                                                 dtype == MOE_BF16, do_perm, dgate, stream));
+}
+
+moe_status moe_gate_backward(const float* logits, const int32_t* topk_idx, const float* dgate,
+                             int T, int E, int k, int gate, float* dlogits, void* stream) {
+  if (T < 0) return MOE_ERR_INVALID_ARG;
+  moe_status st = check_topk(E, k);
+  if (st != MOE_OK) return st;
+  if (gate != MOE_GATE_SOFTMAX_TOPK_RENORM && gate != MOE_GATE_SIGMOID_TOPK_NORM)
+    return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!logits || !topk_idx || !dgate || !dlogits) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(logits) || !aligned16(topk_idx) || !aligned16(dgate) || !aligned16(dlogits))
+    return MOE_ERR_MISALIGNED;
+  return hip_status(moe::launch_gate_backward(logits, topk_idx, dgate, T, E, k, gate, dlogits,
+                                              stream));
+}
+
+moe_status moe_ffn_down_backward(const void* do_perm, const int32_t* offsets, int E_loc,
+                                 int64_t max_rows, int d, int f, moe_dtype dtype,
+                                 const void* w2_t, const void* ab, void* dh, void* dab,
+                                 void* stream) {
+  // dh = do . W2^T is the down GEMM's form with the roles of d and f swapped
+  moe_status st = check_ffn(do_perm, offsets, E_loc, max_rows, f, d, dtype, w2_t, dh);
+  if (st != MOE_OK) return st;
+  if (max_rows > 0 && (!ab || !dab)) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(ab) || !aligned16(dab)) return MOE_ERR_MISALIGNED;
+  st = launch_down(do_perm, offsets, E_loc, max_rows, f, d, dtype, w2_t, nullptr, dh, stream);
+  if (st != MOE_OK) return st;
+  return hip_status(moe::launch_swiglu_backward(dh, ab, offsets, E_loc, max_rows, f,
+                                                dtype == MOE_BF16, dab, stream));
+}
+
+moe_status moe_ffn_up_backward(const void* dab, const int32_t* offsets, int E_loc,
+                               int64_t max_rows, int d, int f, moe_dtype dtype,
+                               const void* w13_t, void* dx_perm, void* stream) {
+  // dx = dab . [W1 | W3]^T: the down GEMM's form with K = 2f
+  moe_status st = check_ffn(dab, offsets, E_loc, max_rows, d, 2 * f, dtype, w13_t, dx_perm);
+  if (st != MOE_OK) return st;
+  return launch_down(dab, offsets, E_loc, max_rows, d, 2 * f, dtype, w13_t, nullptr, dx_perm,
+                     stream);
+}
+
+size_t moe_wgrad_workspace_bytes(int64_t max_rows, int E_loc, int d, int f, moe_dtype dtype) {
+  if (max_rows < 0 || E_loc < 1 || d < 1 || f < 1) return 0;
+  return moe::wgrad_ws_bytes(max_rows, E_loc, d, f, dtype == MOE_BF16);
+}
+
+moe_status moe_ffn_wgrad(const void* x_perm, const void* h, const void* do_perm, const void* dab,
+                         const int32_t* offsets, int E_loc, int64_t max_rows, int d, int f,
+                         moe_dtype dtype, float* dw13, float* dw2, void* ws, size_t ws_bytes,
+                         void* stream) {
+  moe_status st = check_ffn(x_perm, offsets, E_loc, max_rows, d, f, dtype, dw13, h);
+  if (st != MOE_OK) return st;
+  if (!dw2 || !ws) return MOE_ERR_INVALID_ARG;
+  if (max_rows > 0 && (!do_perm || !dab)) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(do_perm) || !aligned16(dab) || !aligned16(dw2) || !aligned16(ws))
+    return MOE_ERR_MISALIGNED;
+  if (ws_bytes < moe::wgrad_ws_bytes(max_rows, E_loc, d, f, dtype == MOE_BF16))
+    return MOE_ERR_WORKSPACE;
+  return hip_status(moe::launch_ffn_wgrad(x_perm, h, do_perm, dab, offsets, E_loc, max_rows, d,
+                                          f, dtype == MOE_BF16, dw13, dw2, ws, stream));
+}
+
+size_t moe_router_backward_workspace_bytes(int T, int d, int E) {
+  if (T < 0 || d < 1 || E < 1) return 0;
+  return moe::router_backward_ws_bytes(T, d, E);
+}
+
+moe_status moe_router_backward(const void* x, const float* w_gate, const float* dlogits, int T,
+                               int d, int E, moe_dtype dtype, void* dx, float* dw_gate, void* ws,
+                               size_t ws_bytes, void* stream) {
+  if (T < 0 || d < 1 || E < 1 || E > 64) return MOE_ERR_INVALID_ARG;
+  if (!elem_ok(dtype)) return MOE_ERR_UNSUPPORTED;
+  if (d % 8 != 0) return MOE_ERR_UNSUPPORTED;
+  if (!w_gate || !dw_gate || !ws) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && (!x || !dlogits || !dx)) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w_gate) || !aligned16(dlogits) || !aligned16(dx) ||
+      !aligned16(dw_gate) || !aligned16(ws))
+    return MOE_ERR_MISALIGNED;
+  if (ws_bytes < moe::router_backward_ws_bytes(T, d, E)) return MOE_ERR_WORKSPACE;
+  return hip_status(moe::launch_router_backward(x, w_gate, dlogits, T, d, E, dtype == MOE_BF16,
+                                                dx, dw_gate, static_cast<float*>(ws), stream));
 }
 
 moe_status moe_forward_fused(const float* logits, const void* x, int T, int E, int k, int gate,

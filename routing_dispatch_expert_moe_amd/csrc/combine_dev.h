@@ -9,7 +9,9 @@
 
 namespace moe {
 
-// Output row of token t, computed by one whole wave.
+// Output row of token t, computed by one whole wave.  topk_w == nullptr: every
+// weight is 1 (the plain sum of the token's rows, as the backward pass needs
+// for the input gradient).
 template <bool BF16>
 __device__ __forceinline__ void combine_token(const uint4* __restrict__ y_perm,
                                               const int32_t* __restrict__ pair_pos,
@@ -22,7 +24,7 @@ __device__ __forceinline__ void combine_token(const uint4* __restrict__ y_perm,
 #pragma unroll
   for (int j = 0; j < MOE_MAX_K; ++j) {
     rows[j] = j < k ? pair_pos[(size_t)t * k + j] : -1;
-    w[j] = j < k ? topk_w[(size_t)t * k + j] : 0.f;
+    w[j] = j < k ? (topk_w != nullptr ? topk_w[(size_t)t * k + j] : 1.f) : 0.f;
   }
   // U chunks per lane: all of their k row loads are in flight before the sums
   constexpr int U = 2;

@@ -369,6 +369,22 @@ int launch_ffn_up_bf16(const void* x_perm, const int32_t* offsets, int E_loc, in
   return launch_gemm_pipe_bf16(PipeRows::kTailTiles, true, x_perm, offsets, E_loc, max_rows, w13, h, f, d, wlist, stream);
 }
 
+// Always the pipelined kernels (the only ones with the pre-activation store);
+// the caller checks that every operand is below 4 GiB.
+int launch_ffn_up_train_bf16(const void* x_perm, const int32_t* offsets, int E_loc,
+                             int64_t max_rows, int d, int f, const void* w13, void* h, void* ab,
+                             void* stream) {
+  if (max_rows == 0) return 0;
+  const int64_t avg = max_rows / E_loc;
+  if (avg <= kStreamRows)
+    return launch_gemm_pipe_bf16(PipeRows::kAllRows, true, x_perm, offsets, E_loc, max_rows, w13, h, f, d, nullptr, stream, ab);
+  if (remainders_with_big_tiles(E_loc, f, d, true))
+    return launch_gemm_pipe_bf16(PipeRows::kBigAll, true, x_perm, offsets, E_loc, max_rows, w13, h, f, d, nullptr, stream, ab);
+  int e = launch_gemm_pipe_bf16(PipeRows::kBigTiles, true, x_perm, offsets, E_loc, max_rows, w13, h, f, d, nullptr, stream, ab);
+  if (e != 0) return e;
+  return launch_gemm_pipe_bf16(PipeRows::kTailTiles, true, x_perm, offsets, E_loc, max_rows, w13, h, f, d, nullptr, stream, ab);
+}
+
 int launch_ffn_down_bf16(const void* h, const int32_t* offsets, int E_loc, int64_t max_rows,
                          int d, int f, const void* w2, void* y, const void* const* wlist,
                          void* stream) {

@@ -9,29 +9,31 @@ namespace moe {
 template <int BM>
 constexpr int pipe_waves() { return BM == 256 ? 8 : 4; }
 
-template <bool SWIGLU, int BM, int BNW, int STAGES, int CLASS>
+template <bool SWIGLU, int BM, int BNW, int STAGES, int CLASS, bool SAVE>
 __global__ __launch_bounds__(pipe_waves<BM>() * 64, 1) void gemm_bf16_pipe(const uint16_t* __restrict__ A,
                                                          const int32_t* __restrict__ offsets,
                                                          int E_loc,
                                                          const uint16_t* __restrict__ W,
                                                          uint16_t* __restrict__ C, int N, int K,
-                                                         const uint16_t* const* __restrict__ wlist) {
+                                                         const uint16_t* const* __restrict__ wlist,
+                                                         uint16_t* __restrict__ AB) {
   extern __shared__ uint4 lds[];
   __shared__ int prefix[MOE_MAX_E + 1];
   __shared__ int segs[MOE_MAX_E + 1];
-  gemm_pipe_body<SWIGLU, BM, BNW, STAGES, CLASS, pipe_waves<BM>()>(
-      A, offsets, E_loc, W, C, N, K, blockIdx.x, gridDim.x, lds, prefix, segs, nullptr, 1, wlist);
+  gemm_pipe_body<SWIGLU, BM, BNW, STAGES, CLASS, pipe_waves<BM>(), SAVE>(
+      A, offsets, E_loc, W, C, N, K, blockIdx.x, gridDim.x, lds, prefix, segs, nullptr, 1, wlist,
+      AB);
 }
 
 namespace {
 
-template <bool SWIGLU, int BM, int BNW, int STAGES, int CLASS>
+template <bool SWIGLU, int BM, int BNW, int STAGES, int CLASS, bool SAVE>
 int launch_pipe(const void* A, const int32_t* offsets, int E_loc, int64_t max_rows, const void* W,
-                void* C, int N, int K, const void* const* wlist, hipStream_t s) {
+                void* C, int N, int K, const void* const* wlist, void* AB, hipStream_t s) {
   const size_t lds = pipe_lds_bytes(BM, BNW, STAGES);
   static_assert(pipe_lds_bytes(BM, BNW, STAGES) + 2 * (MOE_MAX_E + 1) * 4 <= 160 * 1024,
                 "LDS budget");
-  auto kern = gemm_bf16_pipe<SWIGLU, BM, BNW, STAGES, CLASS>;
+  auto kern = gemm_bf16_pipe<SWIGLU, BM, BNW, STAGES, CLASS, SAVE>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -51,7 +53,7 @@ int launch_pipe(const void* A, const int32_t* offsets, int E_loc, int64_t max_ro
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(pipe_waves<BM>() * 64), lds, s,
                      static_cast<const uint16_t*>(A), offsets, E_loc,
                      static_cast<const uint16_t*>(W), static_cast<uint16_t*>(C), N, K,
-                     reinterpret_cast<const uint16_t* const*>(wlist));
+                     reinterpret_cast<const uint16_t* const*>(wlist), static_cast<uint16_t*>(AB));
   return static_cast<int>(hipGetLastError());
 }
 
@@ -61,24 +63,25 @@ int launch_pipe(const void* A, const int32_t* offsets, int E_loc, int64_t max_ro
 // else 128 x 256 with 6 stages (half the re-reads of the activation rows).
 constexpr int kSmallBM = 128, kSmallBNW = 128, kSmallStages = 8;
 
-template <bool SWIGLU>
+template <bool SWIGLU, bool SAVE>
 int launch_kind(PipeRows rows, const void* A, const int32_t* offsets, int E_loc, int64_t max_rows,
-                const void* W, void* C, int N, int K, const void* const* wlist, hipStream_t s) {
+                const void* W, void* C, int N, int K, const void* const* wlist, void* AB,
+                hipStream_t s) {
   switch (rows) {
     case PipeRows::kBigTiles:
-      return launch_pipe<SWIGLU, 256, 256, 4, ROWS_BIG>(A, offsets, E_loc, max_rows, W, C, N, K, wlist, s);
+      return launch_pipe<SWIGLU, 256, 256, 4, ROWS_BIG, SAVE>(A, offsets, E_loc, max_rows, W, C, N, K, wlist, AB, s);
     case PipeRows::kBigAll:
-      return launch_pipe<SWIGLU, 256, 256, 4, ROWS_ALL>(A, offsets, E_loc, max_rows, W, C, N, K, wlist, s);
+      return launch_pipe<SWIGLU, 256, 256, 4, ROWS_ALL, SAVE>(A, offsets, E_loc, max_rows, W, C, N, K, wlist, AB, s);
     case PipeRows::kTailTiles: {
       if (!few_gemm_tiles(E_loc, N, SWIGLU))
-        return launch_pipe<SWIGLU, 128, 256, 6, ROWS_TAIL>(A, offsets, E_loc, max_rows, W, C, N,
-                                                            K, wlist, s);
-      return launch_pipe<SWIGLU, kSmallBM, kSmallBNW, kSmallStages, ROWS_TAIL>(
-          A, offsets, E_loc, max_rows, W, C, N, K, wlist, s);
+        return launch_pipe<SWIGLU, 128, 256, 6, ROWS_TAIL, SAVE>(A, offsets, E_loc, max_rows, W, C,
+                                                                  N, K, wlist, AB, s);
+      return launch_pipe<SWIGLU, kSmallBM, kSmallBNW, kSmallStages, ROWS_TAIL, SAVE>(
+          A, offsets, E_loc, max_rows, W, C, N, K, wlist, AB, s);
     }
     default:
-      return launch_pipe<SWIGLU, kSmallBM, kSmallBNW, kSmallStages, ROWS_ALL>(
-          A, offsets, E_loc, max_rows, W, C, N, K, wlist, s);
+      return launch_pipe<SWIGLU, kSmallBM, kSmallBNW, kSmallStages, ROWS_ALL, SAVE>(
+          A, offsets, E_loc, max_rows, W, C, N, K, wlist, AB, s);
   }
 }
 
@@ -99,10 +102,13 @@ bool remainders_with_big_tiles(int E_loc, int N, int K, bool swiglu) {
 
 int launch_gemm_pipe_bf16(PipeRows rows, bool swiglu, const void* A, const int32_t* offsets,
                           int E_loc, int64_t max_rows, const void* W, void* C, int N, int K,
-                          const void* const* wlist, void* stream) {
+                          const void* const* wlist, void* stream, void* ab) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (swiglu) return launch_kind<true>(rows, A, offsets, E_loc, max_rows, W, C, N, K, wlist, s);
-  return launch_kind<false>(rows, A, offsets, E_loc, max_rows, W, C, N, K, wlist, s);
+  if (swiglu && ab != nullptr)
+    return launch_kind<true, true>(rows, A, offsets, E_loc, max_rows, W, C, N, K, wlist, ab, s);
+  if (swiglu)
+    return launch_kind<true, false>(rows, A, offsets, E_loc, max_rows, W, C, N, K, wlist, nullptr, s);
+  return launch_kind<false, false>(rows, A, offsets, E_loc, max_rows, W, C, N, K, wlist, nullptr, s);
 }
 
 }  // namespace moe

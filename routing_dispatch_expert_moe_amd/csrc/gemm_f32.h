@@ -21,14 +21,18 @@ constexpr size_t f32_lds_floats(bool swiglu) {
 // of LDS; prefix: E_loc + 1 ints of LDS.  Every thread must call it.
 // gather: if not null, activation row r is row gather[r] / gk of A.
 // wlist: if not null, expert e's packed weights start at wlist[e].
-template <bool SWIGLU>
+// SAVE (SwiGLU only): also store a = A W1 at AB[row][col] and g = A W3 at
+// AB[row][N + col] (row pitch 2N) for the backward pass.
+template <bool SWIGLU, bool SAVE = false>
 __device__ __forceinline__ void gemm_f32_body(const float* __restrict__ A,
                                               const int32_t* __restrict__ offsets, int E_loc,
                                               const float* __restrict__ W, float* __restrict__ C,
                                               int N, int K, int bid, int G, float* smem,
                                               int* prefix, const int32_t* __restrict__ gather = nullptr,
                                               int gk = 1,
-                                              const float* const* __restrict__ wlist = nullptr) {
+                                              const float* const* __restrict__ wlist = nullptr,
+                                              float* __restrict__ AB = nullptr) {
+  static_assert(SWIGLU || !SAVE, "pre-activations exist only with SwiGLU");
   constexpr int BM = kF32BM, BN = kF32BN, BK = kF32BK;
   constexpr int BNW = SWIGLU ? 2 * BN : BN;
   float (*As)[BM + 4] = reinterpret_cast<float (*)[BM + 4]>(smem);
@@ -99,6 +103,10 @@ __device__ __forceinline__ void gemm_f32_body(const float* __restrict__ A,
         const int col = n0 + tx * 4 + j;
         if (col >= N) continue;
         float v = acc[i][j];
+        if constexpr (SAVE) {
+          AB[(size_t)row * 2 * N + col] = v;
+          AB[(size_t)row * 2 * N + N + col] = accg[i][j];
+        }
         if (SWIGLU) v = v / (1.f + expf(-v)) * accg[i][j];
         C[(size_t)row * N + col] = v;
       }

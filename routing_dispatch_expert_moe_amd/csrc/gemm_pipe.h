@@ -117,7 +117,10 @@ constexpr size_t pipe_lds_bytes(int BM, int BNW, int STAGES) {
 // read in place through the dispatch permutation instead of a permuted copy).
 // wlist: if not null, expert e's packed weights start at wlist[e] (a table of
 // per-expert buffers) instead of W + e * (weight rows * K).
-template <bool SWIGLU, int BM, int BNW, int STAGES, int CLASS, int NW = 4>
+// SAVE (SwiGLU only): the pre-activations are also stored, a = A W1 at
+// AB[row][col] and g = A W3 at AB[row][N + col] (row pitch 2N), rounded to
+// bf16, for the backward pass.
+template <bool SWIGLU, int BM, int BNW, int STAGES, int CLASS, int NW = 4, bool SAVE = false>
 __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
                                                const int32_t* __restrict__ offsets, int E_loc,
                                                const uint16_t* __restrict__ W,
@@ -125,7 +128,9 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
                                                int G, uint4* lds, int* prefix, int* segs,
                                                const int32_t* __restrict__ gather = nullptr,
                                                int gk = 1,
-                                               const uint16_t* const* __restrict__ wlist = nullptr) {
+                                               const uint16_t* const* __restrict__ wlist = nullptr,
+                                               uint16_t* __restrict__ AB = nullptr) {
+  static_assert(SWIGLU || !SAVE, "pre-activations exist only with SwiGLU");
   constexpr int BN = SWIGLU ? BNW / 2 : BNW;  // output columns per tile
   constexpr int HALF = BNW / 2;               // SwiGLU: W1 rows (then as many W3 rows)
   constexpr int FM = BM / 64;                 // 32-row MFMA blocks per wave
@@ -284,7 +289,19 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
         for (int r = 0; r < 16; ++r) {
           const int dm = 8 * (r >> 2) + (r & 3);
           float v = acc[i][q][r];
-          if constexpr (SWIGLU) v = silu_fast(v) * acc[i][q + NQ / 2][r];
+          if constexpr (SWIGLU) {
+            const float g = acc[i][q + NQ / 2][r];
+            if constexpr (SAVE) {
+              if (row0 + dm < ct.seg1 && col < N) {
+                const uint32_t ab = (static_cast<uint32_t>(row0 + dm) * static_cast<uint32_t>(2 * N) +
+                                     static_cast<uint32_t>(col)) * 2u;
+                char* ABb = reinterpret_cast<char*>(AB);
+                *reinterpret_cast<uint16_t*>(ABb + ab) = f32_to_bf16(v);
+                *reinterpret_cast<uint16_t*>(ABb + ab + static_cast<uint32_t>(N) * 2u) = f32_to_bf16(g);
+              }
+            }
+            v = silu_fast(v) * g;
+          }
           if (row0 + dm < ct.seg1 && col < N)
             *reinterpret_cast<uint16_t*>(Cb + (base + static_cast<uint32_t>(dm * N) * 2u)) =
                 f32_to_bf16(v);

@@ -56,9 +56,19 @@ bool few_gemm_tiles(int E_loc, int N, bool swiglu);
 // whether a pass runs every row in 256-row tiles (kBigAll) rather than
 // 256-row tiles plus a remainder kernel
 bool remainders_with_big_tiles(int E_loc, int N, int K, bool swiglu);
+// ab (SwiGLU only): if not null, the pre-activations are stored there too
+// ([rows][2N]: a then g)
 int launch_gemm_pipe_bf16(PipeRows rows, bool swiglu, const void* A, const int32_t* offsets,
                           int E_loc, int64_t max_rows, const void* W, void* C, int N, int K,
-                          const void* const* wlist, void* stream);
+                          const void* const* wlist, void* stream, void* ab = nullptr);
+// training forward of the first FFN half: h as launch_ffn_up_* and the
+// pre-activations ab [rows][2f] (a = x W1, then g = x W3) for the backward
+int launch_ffn_up_train_bf16(const void* x_perm, const int32_t* offsets, int E_loc,
+                             int64_t max_rows, int d, int f, const void* w13, void* h, void* ab,
+                             void* stream);
+int launch_ffn_up_train_f32(const float* x_perm, const int32_t* offsets, int E_loc,
+                            int64_t max_rows, int d, int f, const float* w13, float* h, float* ab,
+                            void* stream);
 // FP8 (E4M3-FN) weights with 128 x 128 block scales
 int launch_quantize_fp8(const void* w, int E_loc, int R, int K, uint8_t* q, float* scales,
                         void* stream);
@@ -78,8 +88,29 @@ int launch_ffn_up_f32(const float* x_perm, const int32_t* offsets, int E_loc, in
 int launch_ffn_down_f32(const float* h, const int32_t* offsets, int E_loc, int64_t max_rows,
                         int d, int f, const float* w2, float* y, const void* const* wlist,
                         void* stream);
+// w == nullptr: unit weights
 int launch_combine(const void* y_perm, const int32_t* pair_pos, const float* w, int T, int k,
                    int d, int bf16, void* y, void* stream);
+// backward pass (backward.hip, wgrad.hip, pack.hip)
+int launch_pack_backward(const void* w1, const void* w3, int E_loc, int d, int f, int elem_bytes,
+                         void* w13_t, void* stream);
+int launch_combine_backward(const void* dy, const void* y_perm, const int32_t* pair_pos,
+                            const float* topk_w, int T, int k, int d, int bf16, void* do_perm,
+                            float* dgate, void* stream);
+int launch_gate_backward(const float* logits, const int32_t* topk_idx, const float* dgate, int T,
+                         int E, int k, int gate, float* dlogits, void* stream);
+int launch_swiglu_backward(const void* dh, const void* ab, const int32_t* offsets, int E_loc,
+                           int64_t max_rows, int f, int bf16, void* dab, void* stream);
+size_t router_backward_ws_bytes(int T, int d, int E);
+int launch_router_backward(const void* x, const float* wg, const float* dlogits, int T, int d,
+                           int E, int bf16, void* dx, float* dwg, float* part, void* stream);
+// padded row pitch of the transposed weight-gradient operands, and the
+// workspace they need (bf16; fp32 needs only the segment table)
+size_t wgrad_ldk(int64_t max_rows, int E_loc);
+size_t wgrad_ws_bytes(int64_t max_rows, int E_loc, int d, int f, int bf16);
+int launch_ffn_wgrad(const void* x_perm, const void* h, const void* do_perm, const void* dab,
+                     const int32_t* offsets, int E_loc, int64_t max_rows, int d, int f, int bf16,
+                     float* dw13, float* dw2, void* ws, void* stream);
 int launch_pack(const void* w1, const void* w3, const void* w2, int E_loc, int d, int f,
                 int elem_bytes, void* w13, void* w2p, void* stream);
 int check_error(void* ws, void* stream, int* device_flags);

@@ -57,4 +57,32 @@ int launch_pack(const void* w1, const void* w3, const void* w2, int E_loc, int d
   return static_cast<int>(hipGetLastError());
 }
 
+// The first FFN half's backward operand: w13_t[e][c] = W1[e][c][:] ‖ W3[e][c][:]
+// (rows of 2f, K-contiguous for the input-gradient GEMM), 16-byte chunks.
+__global__ __launch_bounds__(256) void concat_rows_kernel(const uint4* __restrict__ a,
+                                                          const uint4* __restrict__ b,
+                                                          int64_t rows, int chunks,
+                                                          uint4* __restrict__ out) {
+  const int64_t total = rows * 2 * chunks;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < total;
+       i += static_cast<int64_t>(gridDim.x) * 256) {
+    const int64_t r = i / (2 * chunks);
+    const int c = static_cast<int>(i - r * 2 * chunks);
+    out[i] = c < chunks ? a[r * chunks + c] : b[r * chunks + c - chunks];
+  }
+}
+
+int launch_pack_backward(const void* w1, const void* w3, int E_loc, int d, int f, int elem_bytes,
+                         void* w13_t, void* stream) {
+  const int chunks = f * elem_bytes / 16;
+  const int64_t rows = static_cast<int64_t>(E_loc) * d;
+  int64_t blocks = (rows * 2 * chunks + 255) / 256;
+  const int64_t cap = static_cast<int64_t>(device_cu_count()) * 16;
+  if (blocks > cap) blocks = cap;
+  hipLaunchKernelGGL(concat_rows_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const uint4*>(w1),
+                     static_cast<const uint4*>(w3), rows, chunks, static_cast<uint4*>(w13_t));
+  return static_cast<int>(hipGetLastError());
+}
+
 }  // namespace moe

@@ -288,8 +288,10 @@ def moe_expert_ffn_fp8(x_perm, offsets, E_loc, max_rows, w13_q, w13_s, w2_q, w2_
     return h, y_perm
 
 
-def moe_combine(y_perm, pair_pos, topk_w, y=None, stream=None):
-    T, k = topk_w.shape
+def moe_combine(y_perm, pair_pos, topk_w, y=None, stream=None, T=None, k=None):
+    """y [T, d]; topk_w None: unit weights (then pass T and k)."""
+    if topk_w is not None:
+        T, k = topk_w.shape
     d = y_perm.shape[1]
     if y is None:
         y = torch.empty((T, d), dtype=y_perm.dtype, device=y_perm.device)
@@ -321,3 +323,129 @@ def moe_forward_fused(logits, x, k, gate, capacity, e_begin, e_end, w13_packed, 
                                   ws.numel(), _stream(stream)),
           "moe_forward_fused")
     return y
+
+
+# --------------------------------------------------------------------------
+# backward pass
+# --------------------------------------------------------------------------
+def moe_ffn_up_train(x_perm, offsets, E_loc, max_rows, w13_packed, h=None, ab=None, stream=None):
+    """moe_ffn_up that also keeps the pre-activations ab [rows, 2f] (a then g)."""
+    d = x_perm.shape[1]
+    f = w13_packed.shape[1] // 2
+    rows = max(max_rows, 1)
+    if h is None:
+        h = torch.empty((rows, f), dtype=x_perm.dtype, device=x_perm.device)
+    if ab is None:
+        ab = torch.empty((rows, 2 * f), dtype=x_perm.dtype, device=x_perm.device)
+    check(lib().moe_ffn_up_train(_ptr(x_perm), _ptr(offsets), E_loc, max_rows, d, f,
+                                 _dtype_code(x_perm.dtype), _ptr(w13_packed), _ptr(h), _ptr(ab),
+                                 _stream(stream)), "moe_ffn_up_train")
+    return h, ab
+
+
+def moe_pack_weights_backward(w1: torch.Tensor, w3: torch.Tensor,
+                              w13_t: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """w1, w3 [E_loc, d, f] -> w13_t [E_loc, d, 2f] (row c = W1[c] then W3[c])."""
+    E_loc, d, f = w1.shape
+    if w13_t is None:
+        w13_t = torch.empty((E_loc, d, 2 * f), dtype=w1.dtype, device=w1.device)
+    check(lib().moe_pack_weights_backward(_ptr(w1), _ptr(w3), E_loc, d, f, _dtype_code(w1.dtype),
+                                          _ptr(w13_t), _stream(stream)),
+          "moe_pack_weights_backward")
+    return w13_t
+
+
+def moe_combine_backward(dy, y_perm, pair_pos, topk_w, do_perm=None, dgate=None, stream=None):
+    """(do_perm [rows, d], dgate [T, k] fp32) from dy [T, d] through the forward's plan."""
+    T, k = topk_w.shape
+    d = dy.shape[1]
+    if do_perm is None:
+        do_perm = torch.empty((max(y_perm.shape[0], 1), d), dtype=dy.dtype, device=dy.device)
+    if dgate is None:
+        dgate = torch.empty((T, k), dtype=torch.float32, device=dy.device)
+    check(lib().moe_combine_backward(_ptr(dy), _ptr(y_perm), _ptr(pair_pos), _ptr(topk_w), T, k, d,
+                                     _dtype_code(dy.dtype), _ptr(do_perm), _ptr(dgate),
+                                     _stream(stream)), "moe_combine_backward")
+    return do_perm, dgate
+
+
+def moe_gate_backward(logits, topk_idx, dgate, gate, dlogits=None, stream=None):
+    """dlogits [T, E] fp32 (zero outside the chosen experts)."""
+    T, E = logits.shape
+    k = topk_idx.shape[1]
+    if dlogits is None:
+        dlogits = torch.empty((T, E), dtype=torch.float32, device=logits.device)
+    check(lib().moe_gate_backward(_ptr(logits), _ptr(topk_idx), _ptr(dgate), T, E, k,
+                                  _gate_code(gate), _ptr(dlogits), _stream(stream)),
+          "moe_gate_backward")
+    return dlogits
+
+
+def moe_ffn_down_backward(do_perm, offsets, E_loc, max_rows, w2_t, ab, dh=None, dab=None,
+                          stream=None):
+    """(dh [rows, f], dab [rows, 2f]); w2_t = W2 in its logical layout [E_loc, f, d]."""
+    d = do_perm.shape[1]
+    f = w2_t.shape[1]
+    rows = max(max_rows, 1)
+    if dh is None:
+        dh = torch.empty((rows, f), dtype=do_perm.dtype, device=do_perm.device)
+    if dab is None:
+        dab = torch.empty((rows, 2 * f), dtype=do_perm.dtype, device=do_perm.device)
+    check(lib().moe_ffn_down_backward(_ptr(do_perm), _ptr(offsets), E_loc, max_rows, d, f,
+                                      _dtype_code(do_perm.dtype), _ptr(w2_t), _ptr(ab), _ptr(dh),
+                                      _ptr(dab), _stream(stream)), "moe_ffn_down_backward")
+    return dh, dab
+
+
+def moe_ffn_up_backward(dab, offsets, E_loc, max_rows, w13_t, dx_perm=None, stream=None):
+    """dx_perm [rows, d] = dab . [W1 | W3]^T per expert segment."""
+    d = w13_t.shape[1]
+    f = dab.shape[1] // 2
+    if dx_perm is None:
+        dx_perm = torch.empty((max(max_rows, 1), d), dtype=dab.dtype, device=dab.device)
+    check(lib().moe_ffn_up_backward(_ptr(dab), _ptr(offsets), E_loc, max_rows, d, f,
+                                    _dtype_code(dab.dtype), _ptr(w13_t), _ptr(dx_perm),
+                                    _stream(stream)), "moe_ffn_up_backward")
+    return dx_perm
+
+
+def moe_wgrad_workspace_bytes(max_rows: int, E_loc: int, d: int, f: int, dtype) -> int:
+    return int(lib().moe_wgrad_workspace_bytes(max_rows, E_loc, d, f, _dtype_code(dtype)))
+
+
+def moe_ffn_wgrad(x_perm, h, do_perm, dab, offsets, E_loc, max_rows, dw13=None, dw2=None, ws=None,
+                  stream=None):
+    """fp32 weight gradients in the packed layouts: dw13 [E_loc, 2f, d], dw2 [E_loc, d, f]."""
+    d = x_perm.shape[1]
+    f = h.shape[1]
+    dev = x_perm.device
+    if dw13 is None:
+        dw13 = torch.empty((E_loc, 2 * f, d), dtype=torch.float32, device=dev)
+    if dw2 is None:
+        dw2 = torch.empty((E_loc, d, f), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = torch.empty(moe_wgrad_workspace_bytes(max_rows, E_loc, d, f, x_perm.dtype),
+                         dtype=torch.uint8, device=dev)
+    check(lib().moe_ffn_wgrad(_ptr(x_perm), _ptr(h), _ptr(do_perm), _ptr(dab), _ptr(offsets), E_loc,
+                              max_rows, d, f, _dtype_code(x_perm.dtype), _ptr(dw13), _ptr(dw2),
+                              _ptr(ws), ws.numel(), _stream(stream)), "moe_ffn_wgrad")
+    return dw13, dw2
+
+
+def moe_router_backward_workspace_bytes(T: int, d: int, E: int) -> int:
+    return int(lib().moe_router_backward_workspace_bytes(T, d, E))
+
+
+def moe_router_backward(x, w_gate, dlogits, dx, dw_gate=None, ws=None, stream=None):
+    """dx += dlogits . W_g^T (in place), and dW_g [d, E] fp32 = x^T . dlogits."""
+    T, d = x.shape
+    E = w_gate.shape[1]
+    if dw_gate is None:
+        dw_gate = torch.empty((d, E), dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = torch.empty(max(moe_router_backward_workspace_bytes(T, d, E), 16), dtype=torch.uint8,
+                         device=x.device)
+    check(lib().moe_router_backward(_ptr(x), _ptr(w_gate), _ptr(dlogits), T, d, E,
+                                    _dtype_code(x.dtype), _ptr(dx), _ptr(dw_gate), _ptr(ws),
+                                    ws.numel(), _stream(stream)), "moe_router_backward")
+    return dx, dw_gate

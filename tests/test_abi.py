@@ -232,3 +232,99 @@ def test_package_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(L, "_lib", None)
     with pytest.raises(RuntimeError, match="no CPU fallback"):
         L.lib()
+
+
+def test_header_declares_the_backward(lib):
+    names = declared_functions()
+    for n in ("moe_ffn_up_train", "moe_pack_weights_backward", "moe_combine_backward",
+              "moe_gate_backward", "moe_ffn_down_backward", "moe_ffn_up_backward",
+              "moe_wgrad_workspace_bytes", "moe_ffn_wgrad", "moe_router_backward",
+              "moe_router_backward_workspace_bytes"):
+        assert n in names
+
+
+def test_backward_validation(lib):
+    BF, F32 = L.MOE_BF16, L.MOE_F32
+    # ffn_up_train: the forward's rules plus the pre-activation buffer
+    up = lib.moe_ffn_up_train
+    ok = [FAKE, FAKE, 4, 64, 128, 256, BF, FAKE, FAKE, FAKE, None]
+    bad = list(ok); bad[9] = None
+    assert up(*bad) == L.MOE_ERR_INVALID_ARG
+    bad = list(ok); bad[9] = MIS
+    assert up(*bad) == L.MOE_ERR_MISALIGNED
+    bad = list(ok); bad[5] = 100                                  # f not a multiple of 64 (bf16)
+    assert up(*bad) == L.MOE_ERR_UNSUPPORTED
+    bad = list(ok); bad[3] = 1 << 24; bad[5] = 8192               # ab beyond 32-bit offsets
+    assert up(*bad) == L.MOE_ERR_UNSUPPORTED
+    # combine backward
+    cb = lib.moe_combine_backward
+    ok = [FAKE, FAKE, FAKE, FAKE, 10, 2, 64, BF, FAKE, FAKE, None]
+    bad = list(ok); bad[5] = 9
+    assert cb(*bad) == L.MOE_ERR_INVALID_ARG
+    bad = list(ok); bad[6] = 4                                     # d * 2 bytes not a multiple of 16
+    assert cb(*bad) == L.MOE_ERR_UNSUPPORTED
+    bad = list(ok); bad[9] = None
+    assert cb(*bad) == L.MOE_ERR_INVALID_ARG
+    bad = list(ok); bad[8] = MIS
+    assert cb(*bad) == L.MOE_ERR_MISALIGNED
+    assert cb(None, None, None, None, 0, 2, 64, BF, None, None, None) == L.MOE_OK
+    # gate backward
+    gb = lib.moe_gate_backward
+    ok = [FAKE, FAKE, FAKE, 10, 8, 2, 0, FAKE, None]
+    bad = list(ok); bad[5] = 9
+    assert gb(*bad) == L.MOE_ERR_INVALID_TOPK
+    bad = list(ok); bad[6] = 5
+    assert gb(*bad) == L.MOE_ERR_INVALID_ARG
+    bad = list(ok); bad[7] = None
+    assert gb(*bad) == L.MOE_ERR_INVALID_ARG
+    bad = list(ok); bad[0] = MIS
+    assert gb(*bad) == L.MOE_ERR_MISALIGNED
+    # down / up backward
+    db = lib.moe_ffn_down_backward
+    ok = [FAKE, FAKE, 4, 64, 128, 256, BF, FAKE, FAKE, FAKE, FAKE, None]
+    bad = list(ok); bad[10] = None
+    assert db(*bad) == L.MOE_ERR_INVALID_ARG
+    bad = list(ok); bad[8] = MIS
+    assert db(*bad) == L.MOE_ERR_MISALIGNED
+    bad = list(ok); bad[4] = 96
+    assert db(*bad) == L.MOE_ERR_UNSUPPORTED
+    ub = lib.moe_ffn_up_backward
+    ok = [FAKE, FAKE, 4, 64, 128, 256, BF, FAKE, FAKE, None]
+    bad = list(ok); bad[7] = None
+    assert ub(*bad) == L.MOE_ERR_INVALID_ARG
+    bad = list(ok); bad[2] = 0
+    assert ub(*bad) == L.MOE_ERR_INVALID_ARG
+    # weight gradients: workspace sized for the transposed operands (bf16)
+    need = lib.moe_wgrad_workspace_bytes(1000, 8, 128, 256, BF)
+    assert need >= (2 * 256 + 128) * (1000 + 8 * 31) * 2
+    assert lib.moe_wgrad_workspace_bytes(1000, 8, 128, 256, F32) < 4096
+    wg = lib.moe_ffn_wgrad
+    ok = [FAKE, FAKE, FAKE, FAKE, FAKE, 8, 1000, 128, 256, BF, FAKE, FAKE, FAKE, need, None]
+    bad = list(ok); bad[13] = need - 1
+    assert wg(*bad) == L.MOE_ERR_WORKSPACE
+    bad = list(ok); bad[11] = None
+    assert wg(*bad) == L.MOE_ERR_INVALID_ARG
+    bad = list(ok); bad[3] = None
+    assert wg(*bad) == L.MOE_ERR_INVALID_ARG
+    bad = list(ok); bad[2] = MIS
+    assert wg(*bad) == L.MOE_ERR_MISALIGNED
+    # router backward
+    rb = lib.moe_router_backward
+    rneed = lib.moe_router_backward_workspace_bytes(100, 64, 8)
+    assert rneed >= 2 * 64 * 8 * 4
+    ok = [FAKE, FAKE, FAKE, 100, 64, 8, BF, FAKE, FAKE, FAKE, rneed, None]
+    bad = list(ok); bad[5] = 65
+    assert rb(*bad) == L.MOE_ERR_INVALID_ARG
+    bad = list(ok); bad[4] = 60
+    assert rb(*bad) == L.MOE_ERR_UNSUPPORTED
+    bad = list(ok); bad[10] = rneed - 1
+    assert rb(*bad) == L.MOE_ERR_WORKSPACE
+    bad = list(ok); bad[7] = None
+    assert rb(*bad) == L.MOE_ERR_INVALID_ARG
+    # pack for the backward
+    pb = lib.moe_pack_weights_backward
+    assert pb(FAKE, FAKE, 2, 64, 4, BF, FAKE, None) == L.MOE_ERR_UNSUPPORTED   # f * 2 bytes not a multiple of 16
+    assert pb(FAKE, None, 2, 64, 64, BF, FAKE, None) == L.MOE_ERR_INVALID_ARG
+    assert pb(FAKE, FAKE, 2, 64, 64, BF, MIS, None) == L.MOE_ERR_MISALIGNED
+    # combine with unit weights is allowed (topk_w NULL) but still needs its other buffers
+    assert lib.moe_combine(FAKE, None, None, 10, 2, 64, BF, FAKE, None) == L.MOE_ERR_INVALID_ARG

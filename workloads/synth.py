@@ -209,6 +209,13 @@ WORKLOADS = {
 }
 
 
+def output_grad(wl: Workload) -> np.ndarray:
+    """A seeded output gradient dy [T, d] for the backward pass: N(0, 1) in the
+    layer dtype, from its own stream (independent of every other input)."""
+    ss = _child(np.random.SeedSequence(wl.seed), 5)
+    return _normal(ss, (wl.T, wl.d), 1.0, wl.dtype)
+
+
 def make(name: str, seed: int = 0, **overrides) -> Workload:
     """One of the named workloads (optionally with fields overridden, e.g. T)."""
     kw = dict(WORKLOADS[name])
