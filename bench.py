@@ -48,6 +48,10 @@ def parse():
                    help="fp8: quantise the packed bf16 expert weights to E4M3 codes with "
                         "128 x 128 block scales (moe_quantize_fp8, untimed) and run the FFN "
                         "steps on them")
+    p.add_argument("--backward", action="store_true",
+                   help="also time a training step: the forward with the SwiGLU pre-activations "
+                        "kept, then the whole backward pass (gradients of x, the gate logits "
+                        "or router, and the expert weights); reported under 'training'")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-tokens", type=int, default=256)
     p.add_argument("--traffic", default=None,
@@ -237,6 +241,119 @@ def _cpu_oracle(wl, host_w, n_tok):
     return n_tok / dt, dt
 
 
+TRAIN_STEPS = ("router", "route", "dispatch", "ffn_up_train", "ffn_down", "combine",
+               "combine_bwd", "gate_bwd", "ffn_down_bwd", "ffn_up_bwd", "combine_dx",
+               "router_bwd", "wgrad")
+
+
+def train_work_model(wl, n, touched, T_read):
+    """Algorithmic flops and bytes of each call of a training step."""
+    b = 2 if wl.dtype == "bf16" else 4
+    T, d, f, E, k = wl.T, wl.d, wl.f, wl.E, wl.k
+    m = work_model(wl, n, touched, T_read)
+    m["ffn_up_train"] = (m["ffn_up"][0], m["ffn_up"][1] + 2.0 * n * f * b)
+    router = wl.w_gate is not None
+    m.update({
+        "combine_bwd": (2.0 * n * d, T * d * b + 2.0 * n * d * b + T * k * 12),
+        "gate_bwd": (0.0, T * E * 4 + T * k * 12),
+        # dh = do W2^T, then SwiGLU' from the saved pre-activations
+        "ffn_down_bwd": (2.0 * n * d * f, touched * 1.0 * f * d * b + n * d * b + 2.0 * n * f * b
+                         + 4.0 * n * f * b),
+        "ffn_up_bwd": (4.0 * n * d * f, touched * 2.0 * f * d * b + 2.0 * n * f * b + n * d * b),
+        "combine_dx": (0.0, n * d * b + T * d * b),
+        "router_bwd": ((4.0 * T * d * E, 3.0 * T * d * b + d * E * 8 + T * E * 4) if router
+                       else (0.0, 0.0)),
+        # dW13 = dab^T x_perm, dW2 = do^T h: read the four operands, write fp32 gradients
+        "wgrad": (6.0 * n * d * f, n * (2 * d + 3 * f) * b + touched * 3.0 * d * f * 4),
+    })
+    return m
+
+
+def train_bench(args, wl, layer, x, logits, wg, w13_t, w2_t, n, touched, T_read, dev):
+    """Time training steps (forward with saved pre-activations + backward) with
+    HIP events around every call; returns the 'training' object."""
+    import torch
+    from workloads import output_grad
+    layer.enable_training(w13_t, w2_t)
+    dy = (bf16_dev(output_grad(wl), dev) if wl.dtype == "bf16"
+          else torch.from_numpy(output_grad(wl)).to(dev))
+    router = wg is not None
+
+    def tstep(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record()
+        mark(0)
+        lg = layer.router(x, wg) if router else logits
+        mark(1)
+        layer.route(lg)
+        mark(2)
+        layer.dispatch(x)
+        mark(3)
+        layer.ffn_up_train()
+        mark(4)
+        layer.ffn_down()
+        mark(5)
+        layer.combine()
+        mark(6)
+        layer.combine_backward(dy)
+        mark(7)
+        layer.gate_backward(lg)
+        mark(8)
+        layer.ffn_down_backward()
+        mark(9)
+        layer.ffn_up_backward()
+        mark(10)
+        layer.combine_dx()
+        mark(11)
+        if router:
+            layer.router_backward(x, wg)
+        mark(12)
+        layer.wgrad()
+        mark(13)
+
+    import routing_dispatch_expert_moe_amd as M
+    for _ in range(args.warmup):
+        tstep()
+    torch.cuda.synchronize()
+    if M.moe_check_error(layer.ws) != 0:
+        raise RuntimeError("device error in the training step")
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(14)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        tstep(ev[s])
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    model = train_work_model(wl, n, touched, T_read)
+    per = {}
+    for i, name in enumerate(TRAIN_STEPS):
+        ms = float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)]))
+        fl, by = model[name]
+        per[name] = {"ms": round(ms, 5),
+                     "tflops": round(fl / (ms * 1e-3) / 1e12, 2) if fl and ms > 0 else None,
+                     "gbs": round(by / (ms * 1e-3) / 1e9, 1) if by and ms > 0 else None}
+    bwd_ms = float(np.mean([ev[s][6].elapsed_time(ev[s][13]) for s in range(args.steps)]))
+    fl = sum(v[0] for v in model.values() if v is not None) - model["ffn_up"][0]
+    # the dominant backward call: the longest one
+    dom = max(TRAIN_STEPS[6:], key=lambda k: per[k]["ms"])
+    dfl, dby = model[dom]
+    dms = per[dom]["ms"]
+    if dfl / (PEAK_BF16_TFLOPS * 1e12) >= dby / (PEAK_HBM_GBS * 1e9):
+        roof = {"bound": "mfma", "achieved": round(dfl / (dms * 1e-3) / 1e12, 1),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(dby / (dms * 1e-3) / 1e9, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof.update(call=dom, frac=round(roof["achieved"] / roof["peak"], 4), avg_launch_ms=dms,
+                algorithmic_flops_per_launch=dfl, algorithmic_bytes_per_launch=dby)
+    return {"ms_per_step": round(ms_step, 4), "tokens_per_s": round(wl.T / (ms_step * 1e-3), 1),
+            "backward_ms": round(bwd_ms, 4), "step_tflops": round(fl / (ms_step * 1e-3) / 1e12, 2),
+            "per_call": per, "roofline": roof,
+            "note": "one step = forward (pre-activations kept) + backward: combine, gate and "
+                    "router backward, dh and SwiGLU', dx, fp32 weight gradients; HIP events "
+                    "around every call on the launch stream"}
+
+
 def main():
     args = parse()
     if args.traffic_from:
@@ -267,12 +384,21 @@ def main():
     def up(a):
         return bf16_dev(a, dev) if wl.dtype == "bf16" else torch.from_numpy(a).to(dev)
 
+    train = args.backward
+    if train:   # the backward operands: [W1 | W3] rows per d, and W2 as it is
+        w13_t = torch.empty((wl.E_loc, wl.d, 2 * wl.f), dtype=tdt, device=dev)
+        w2_t = torch.empty((wl.E_loc, wl.f, wl.d), dtype=tdt, device=dev)
     for c0 in range(0, wl.E_loc, 8):
         ids = list(range(wl.e_begin + c0, wl.e_begin + min(wl.E_loc, c0 + 8)))
         a, b, c = wl.stacked_weights(ids)
         if keep_host:
             host_w.extend(zip(a, b, c))
-        M.moe_pack_weights(up(a), up(b), up(c), w13[c0:c0 + len(ids)], w2p[c0:c0 + len(ids)])
+        ga, gb, gc = up(a), up(b), up(c)
+        M.moe_pack_weights(ga, gb, gc, w13[c0:c0 + len(ids)], w2p[c0:c0 + len(ids)])
+        if train:
+            M.moe_pack_weights_backward(ga, gb, w13_t[c0:c0 + len(ids)])
+            w2_t[c0:c0 + len(ids)] = gc
+        del ga, gb, gc
     torch.cuda.synchronize()
     log("weights packed")
 
@@ -424,6 +550,12 @@ def main():
                 "algorithmic_flops_per_launch": dom_fl,
                 "algorithmic_bytes_per_launch": dom_by, "avg_launch_ms": dom_ms}
 
+    training = None
+    if train:
+        if fp8 or args.reroute:
+            raise SystemExit("--backward takes native weights and plain top-k routing")
+        training = train_bench(args, wl, layer, x, logits, wg, w13_t, w2_t, n, touched, T_read, dev)
+
     cpu = None
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle on {args.cpu_sample_tokens} tokens")
@@ -450,6 +582,7 @@ def main():
                          "per_step_median": cold,
                          "note": "1 GiB written between steps (outside the events) to evict "
                                  "the 256 MB Infinity Cache; HIP-event times per call"},
+        "training": training,
         "fused": None if fused_ms is None else {
             "entry": "moe_forward_fused", "ms_per_step_median": round(fused_ms, 4),
             "tokens_per_s": round(wl.T / (fused_ms * 1e-3), 1),

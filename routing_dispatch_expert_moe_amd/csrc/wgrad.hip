@@ -7,9 +7,11 @@
 //
 // bf16: the MFMA operands must run along the reduction, which here is the
 // row (token) dimension, so both operands are first transposed into
-// K-contiguous buffers PT [M][ldk], QT [N][ldk] whose columns are the experts'
-// rows, each expert's block zero-padded to a multiple of 32 columns
-// (kseg[e] = first column of expert e).  The GEMM then runs 256 x 256 output
+// K-contiguous form, one block per expert: expert e's block of PT is
+// [M][Kpad_e] (its rows, zero-padded to Kpad_e, a multiple of 32) at element
+// M * kseg[e], with kseg the prefix of the Kpad (QT likewise with N), so the
+// 256 operand rows a tile reads are one contiguous run of memory whatever the
+// number of experts.  The GEMM then runs 256 x 256 output
 // tiles (8 waves, 32x32x16 bf16 MFMA, direct-to-LDS loads through a 4-stage
 // pipeline, the same LDS layout and swizzle as the forward's grouped GEMM),
 // one tile per workgroup, K = the expert's padded rows, fp32 results.
@@ -52,17 +54,21 @@ __global__ __launch_bounds__(64) void kseg_kernel(const int32_t* __restrict__ of
   if (lane == kWave - 1) kseg[E_loc] = incl;
 }
 
-// PT[m][kk] for kk in the padded column space: the value of row r = offsets[e]
-// + (kk - kseg[e]) of P (row pitch M) at column m, or 0 in the padding.  A
-// 64 x 64 tile per workgroup through LDS; columns past kseg[E_loc] are left
-// alone (never read).
+// For a column kk of the padded space (expert e: kseg[e] <= kk < kseg[e+1],
+// local column j = kk - kseg[e]) the element (m, kk) of the transposed operand
+// lives at M * kseg[e] + m * Kpad_e + j and holds row r = offsets[e] + j of P
+// (row pitch M) at column m, or 0 in the padding (j >= rows of e).  A 64 x 64
+// tile of (kk, m) per workgroup through LDS; a 16-byte run of 8 columns never
+// crosses an expert (every Kpad is a multiple of 32).  Columns past kseg[E_loc]
+// do not exist.
 __global__ __launch_bounds__(256) void transpose_seg_kernel(const uint16_t* __restrict__ P,
                                                             int M, const int32_t* __restrict__ offsets,
                                                             const int32_t* __restrict__ kseg,
-                                                            int E_loc, int ldk,
-                                                            uint16_t* __restrict__ PT) {
+                                                            int E_loc, uint16_t* __restrict__ PT) {
   __shared__ uint16_t tile[64][64 + 8];
   __shared__ int src_row[64];
+  __shared__ int64_t dst_base[64];   // M * kseg[e] + j for column kk0 + i
+  __shared__ int dst_pitch[64];      // Kpad_e
   const int kk0 = blockIdx.x * 64, m0 = blockIdx.y * 64;
   const int total = kseg[E_loc];
   if (kk0 >= total) return;
@@ -78,6 +84,8 @@ __global__ __launch_bounds__(256) void transpose_seg_kernel(const uint16_t* __re
       }
       const int local = kk - kseg[lo];
       if (local < offsets[lo + 1] - offsets[lo]) r = offsets[lo] + local;
+      dst_base[tid] = static_cast<int64_t>(M) * kseg[lo] + local;
+      dst_pitch[tid] = kseg[lo + 1] - kseg[lo];
     }
     src_row[tid] = r;
   }
@@ -109,7 +117,8 @@ __global__ __launch_bounds__(256) void transpose_seg_kernel(const uint16_t* __re
     for (int q = 0; q < 4; ++q)
       pw[q] = static_cast<uint32_t>(tile[ch * 8 + 2 * q][mr]) |
               (static_cast<uint32_t>(tile[ch * 8 + 2 * q + 1][mr]) << 16);
-    *reinterpret_cast<uint4*>(PT + (size_t)(m0 + mr) * ldk + kk0 + ch * 8) =
+    const int c0 = ch * 8;
+    *reinterpret_cast<uint4*>(PT + dst_base[c0] + static_cast<int64_t>(m0 + mr) * dst_pitch[c0]) =
         make_uint4(pw[0], pw[1], pw[2], pw[3]);
   }
 }
@@ -129,35 +138,106 @@ constexpr int STAGE_U4 = (BM + BN) * kKC;
 
 }  // namespace wgt
 
+// epilogue staging: half the tile's rows, fp32, rows padded to 264 floats
+// (the two row groups one store instruction covers land 32 banks apart)
+constexpr int kOutPitch = wgt::BN + 8;
 constexpr size_t wgrad_lds_bytes() {
-  return static_cast<size_t>(wgt::STAGES) * wgt::STAGE_U4 * sizeof(uint4);
+  const size_t pipe = static_cast<size_t>(wgt::STAGES) * wgt::STAGE_U4 * sizeof(uint4);
+  const size_t out = static_cast<size_t>(wgt::BM / 2) * kOutPitch * sizeof(float);
+  return pipe > out ? pipe : out;
 }
 
-// One 256 x 256 tile of C_e (fp32, row pitch N) per workgroup.  Tiles are
-// numbered expert-major, then M-tiles, then N-tiles (neighbouring ids share a
-// PT tile); ids are dealt so each XCD owns a contiguous range.
+// Tiles: 256 x 256 blocks of C_e (fp32, row pitch N), numbered expert-major,
+// then M-tiles, then N-tiles (neighbouring ids share a PT tile).  A tile of
+// expert e costs about KT_e + kTileOverhead pipeline steps, so the tile
+// sequence is cut into 8 ranges of equal cost, one per XCD (workgroup ids are
+// dealt round-robin over the XCDs), and the XCD's workgroups take its tiles
+// in turn: neighbouring tiles run together and share operands in that XCD's
+// L2, and a few hot experts cannot pile up on one XCD.
+constexpr int kTileOverhead = 4;
+
+// First tile of the split point `part` of `parts`: the smallest tile index
+// whose preceding tiles cost at least part / parts of the total.  Run by one
+// whole wave; every lane returns the same value.
+__device__ int cost_split(const int32_t* __restrict__ kseg, int E_loc, int per_e, int part,
+                          int parts) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int per = (E_loc + kWave - 1) / kWave;
+  const int lo = lane * per;
+  auto cost = [&](int e) {  // per-tile cost of expert e
+    return static_cast<int64_t>((kseg[e + 1] - kseg[e]) / kBK + kTileOverhead);
+  };
+  int64_t local = 0;
+  for (int i = 0; i < per; ++i)
+    if (lo + i < E_loc) local += cost(lo + i);
+  int64_t incl = local;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int64_t v = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += v;
+  }
+  const int64_t total = __shfl(incl, kWave - 1, kWave);
+  // target in (per-tile cost) x (tiles) units
+  const int64_t tau = total * per_e * part / parts;
+  int64_t run = (incl - local) * per_e;
+  int found = part >= parts ? E_loc * per_e : -1;
+  if (found < 0) {
+    for (int i = 0; i < per; ++i) {
+      const int e = lo + i;
+      if (e >= E_loc) break;
+      const int64_t c = cost(e);
+      if (tau < run + c * per_e) {
+        const int64_t t = tau <= run ? 0 : (tau - run + c - 1) / c;
+        found = (run <= tau || lane == 0) ? e * per_e + static_cast<int>(t) : -1;
+        break;
+      }
+      run += c * per_e;
+    }
+  }
+  // exactly one lane's run holds the target (every expert costs at least
+  // kTileOverhead); an empty result means the target is the end
+  const uint64_t has = __ballot(found >= 0 && !(lo >= E_loc));
+  if (has == 0) return E_loc * per_e;
+  return __shfl(found, __builtin_ctzll(has), kWave);
+}
+
+// Persistent: one workgroup per CU walks its XCD's tile range.
 __global__ __launch_bounds__(512, 1) void wgrad_bf16_kernel(const uint16_t* __restrict__ PT,
                                                             const uint16_t* __restrict__ QT,
                                                             const int32_t* __restrict__ kseg,
-                                                            int M, int N, int ldk, int tiles_m,
-                                                            int tiles_n, int total,
-                                                            float* __restrict__ C) {
+                                                            int E_loc, int M, int N, int tiles_m,
+                                                            int tiles_n, float* __restrict__ C) {
   using namespace wgt;
   extern __shared__ uint4 lds[];
+  __shared__ int range[2];
   const int G = gridDim.x, bid = blockIdx.x;
-  const int vb = (G & 7) == 0 ? (bid & 7) * (G >> 3) + (bid >> 3) : bid;
-  if (vb >= total) return;
   const int per_e = tiles_m * tiles_n;
-  const int e = vb / per_e;
-  const int rem = vb - e * per_e;
-  const int m0 = (rem / tiles_n) * BM, n0 = (rem % tiles_n) * BN;
-  const int k0 = kseg[e];
-  const int KT = (kseg[e + 1] - k0) / kBK;
+  const bool by_xcd = (G & 7) == 0;
+  const int xcd = by_xcd ? (bid & 7) : 0, parts = by_xcd ? 8 : 1;
+  const int local = by_xcd ? (bid >> 3) : bid, stride = by_xcd ? (G >> 3) : G;
+  if (threadIdx.x < kWave) {
+    const int a = cost_split(kseg, E_loc, per_e, xcd, parts);
+    const int b = cost_split(kseg, E_loc, per_e, xcd + 1, parts);
+    if (threadIdx.x == 0) {
+      range[0] = a;
+      range[1] = b;
+    }
+  }
+  __syncthreads();
+  const int t_lo = range[0], t_hi = range[1];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int wm = wave / WN, wn = wave % WN;
   auto swz = [](int r) { return (r >> 2) & 3; };
   const int lkc = (lane % kKC) ^ swz(lane / kKC);
+
+  for (int vb = t_lo + local; vb < t_hi; vb += stride) {
+  const int e = vb / per_e;
+  const int rem = vb - e * per_e;
+  const int m0 = (rem / tiles_n) * BM, n0 = (rem % tiles_n) * BN;
+  const int k0 = kseg[e];
+  const int kpad = kseg[e + 1] - k0;  // the expert's padded rows: the K of its tiles
+  const int KT = kpad / kBK;
 
   f32x16_t acc[FM][NQ];
 #pragma unroll
@@ -171,12 +251,14 @@ __global__ __launch_bounds__(512, 1) void wgrad_bf16_kernel(const uint16_t* __re
 #pragma unroll
     for (int i = 0; i < LA; ++i) {
       const int rt = (i * NW + wave) * kRPI + lane / kKC;
-      pa[i] = reinterpret_cast<const char*>(PT + (size_t)min(m0 + rt, M - 1) * ldk + k0 + lkc * 8);
+      pa[i] = reinterpret_cast<const char*>(PT + static_cast<size_t>(M) * k0 +
+                                            (size_t)min(m0 + rt, M - 1) * kpad + lkc * 8);
     }
 #pragma unroll
     for (int i = 0; i < LB; ++i) {
       const int rt = (i * NW + wave) * kRPI + lane / kKC;
-      pb[i] = reinterpret_cast<const char*>(QT + (size_t)min(n0 + rt, N - 1) * ldk + k0 + lkc * 8);
+      pb[i] = reinterpret_cast<const char*>(QT + static_cast<size_t>(N) * k0 +
+                                            (size_t)min(n0 + rt, N - 1) * kpad + lkc * 8);
     }
     // step p's loads into buffer p % STAGES (steps past the end re-fetch the
     // last one: valid addresses, result unused)
@@ -236,22 +318,38 @@ __global__ __launch_bounds__(512, 1) void wgrad_bf16_kernel(const uint16_t* __re
     }
     wait_vmcnt<0>();
   }
-  // D[m][n] of a 32x32 MFMA tile sits in lane n + 32 * ((m / 4) % 2),
-  // register 4 * (m / 8) + m % 4
+  // Epilogue through LDS, half the rows at a time: the waves owning those rows
+  // place their accumulators (D[m][n] of a 32x32 MFMA tile sits in lane
+  // n + 32 * ((m / 4) % 2), register 4 * (m / 8) + m % 4), then every wave
+  // writes whole 1 KB row runs with 16-byte streaming stores (the gradients
+  // are not read again here).
+  __syncthreads();  // every wave is done with the pipeline's buffers
+  float* Ls = reinterpret_cast<float*>(lds);
   float* Ce = C + (size_t)e * M * N;
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    const int row0 = m0 + wm * (BM / 2) + i * 32 + 4 * (lane >> 5);
+  for (int half = 0; half < 2; ++half) {
+    if (wm == half) {
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      const int col = n0 + wn * (BN / WN) + q * 32 + (lane & 31);
-      if (col >= N) continue;
+      for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = row0 + 8 * (r >> 2) + (r & 3);
-        if (m < M) Ce[(size_t)m * N + col] = acc[i][q][r];
-      }
+        for (int q = 0; q < NQ; ++q)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = i * 32 + 8 * (r >> 2) + (r & 3) + 4 * (lane >> 5);
+            const int col = wn * (BN / WN) + q * 32 + (lane & 31);
+            Ls[row * kOutPitch + col] = acc[i][q][r];
+          }
     }
+    __syncthreads();
+    const int c = n0 + lane * 4;
+    for (int rr = wave; rr < BM / 2; rr += NW) {
+      const int m = m0 + half * (BM / 2) + rr;
+      if (m < M && c < N)
+        __builtin_nontemporal_store(*reinterpret_cast<const f32x4_t*>(Ls + rr * kOutPitch + lane * 4),
+                                    reinterpret_cast<f32x4_t*>(Ce + (size_t)m * N + c));
+    }
+    __syncthreads();
+  }
   }
 }
 
@@ -318,7 +416,7 @@ size_t wgrad_ldk(int64_t max_rows, int E_loc) {
 size_t wgrad_ws_bytes(int64_t max_rows, int E_loc, int d, int f, int bf16) {
   const size_t head = (static_cast<size_t>(E_loc + 1) * 4 + 255) & ~static_cast<size_t>(255);
   if (!bf16) return head;
-  // the larger pass (dW13) holds PT [2f][ldk] and QT [d][ldk]
+  // the larger pass (dW13) holds 2f x ldk elements of PT and d x ldk of QT
   return head + static_cast<size_t>(2 * f + d) * wgrad_ldk(max_rows, E_loc) * 2;
 }
 
@@ -328,11 +426,9 @@ int run_bf16(const uint16_t* P, int M, const uint16_t* Q, int N, const int32_t* 
              int E_loc, const int32_t* kseg, size_t ldk, uint16_t* PT, uint16_t* QT, float* C,
              hipStream_t s) {
   const dim3 tp(static_cast<unsigned>(ldk / 64), static_cast<unsigned>((M + 63) / 64));
-  hipLaunchKernelGGL(transpose_seg_kernel, tp, dim3(256), 0, s, P, M, offsets, kseg, E_loc,
-                     static_cast<int>(ldk), PT);
+  hipLaunchKernelGGL(transpose_seg_kernel, tp, dim3(256), 0, s, P, M, offsets, kseg, E_loc, PT);
   const dim3 tq(static_cast<unsigned>(ldk / 64), static_cast<unsigned>((N + 63) / 64));
-  hipLaunchKernelGGL(transpose_seg_kernel, tq, dim3(256), 0, s, Q, N, offsets, kseg, E_loc,
-                     static_cast<int>(ldk), QT);
+  hipLaunchKernelGGL(transpose_seg_kernel, tq, dim3(256), 0, s, Q, N, offsets, kseg, E_loc, QT);
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(wgrad_bf16_kernel),
@@ -342,11 +438,8 @@ int run_bf16(const uint16_t* P, int M, const uint16_t* Q, int N, const int32_t* 
     attr_set = true;
   }
   const int tiles_m = (M + wgt::BM - 1) / wgt::BM, tiles_n = (N + wgt::BN - 1) / wgt::BN;
-  const int64_t total = static_cast<int64_t>(E_loc) * tiles_m * tiles_n;
-  const int64_t grid = (total + 7) / 8 * 8;
-  hipLaunchKernelGGL(wgrad_bf16_kernel, dim3(static_cast<unsigned>(grid)), dim3(512),
-                     wgrad_lds_bytes(), s, PT, QT, kseg, M, N, static_cast<int>(ldk), tiles_m,
-                     tiles_n, static_cast<int>(total), C);
+  hipLaunchKernelGGL(wgrad_bf16_kernel, dim3(static_cast<unsigned>(device_cu_count())), dim3(512),
+                     wgrad_lds_bytes(), s, PT, QT, kseg, E_loc, M, N, tiles_m, tiles_n, C);
   return static_cast<int>(hipGetLastError());
 }
 
@@ -373,11 +466,11 @@ int launch_ffn_wgrad(const void* x_perm, const void* h, const void* do_perm, con
   const size_t ldk = wgrad_ldk(max_rows, E_loc);
   uint16_t* PT = reinterpret_cast<uint16_t*>(w + head);
   hipLaunchKernelGGL(kseg_kernel, dim3(1), dim3(64), 0, s, offsets, E_loc, kseg);
-  // dW2 = do^T h: PT = do^T [d][ldk], QT = h^T [f][ldk]
+  // dW2 = do^T h: PT from do (M = d), QT from h (N = f)
   int e = run_bf16(static_cast<const uint16_t*>(do_perm), d, static_cast<const uint16_t*>(h), f,
                    offsets, E_loc, kseg, ldk, PT, PT + static_cast<size_t>(d) * ldk, dw2, s);
   if (e != 0) return e;
-  // dW13 = dab^T x_perm: PT = dab^T [2f][ldk], QT = x_perm^T [d][ldk]
+  // dW13 = dab^T x_perm: PT from dab (M = 2f), QT from x_perm (N = d)
   return run_bf16(static_cast<const uint16_t*>(dab), 2 * f, static_cast<const uint16_t*>(x_perm),
                   d, offsets, E_loc, kseg, ldk, PT, PT + static_cast<size_t>(2 * f) * ldk, dw13, s);
 }

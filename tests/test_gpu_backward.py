@@ -171,3 +171,67 @@ def test_repeatable_bits():
         assert np.array_equal(t_out(a[key])[:n], t_out(b[key])[:n]), key
     for key in ("dgate", "dlogits", "dx", "dw13", "dw2"):
         assert np.array_equal(t_out(a[key]), t_out(b[key])), key
+
+
+def test_mixtral_prefill_training_sampled():
+    """The Mixtral-shaped prefill layer (T=4096, d=4096, f=14336, E=8, k=2, router
+    in the graph) at full size, as the benchmark runs it: sampled tokens' gate
+    gradients and dx, and sampled columns of three experts' weight gradients,
+    each computed by the oracle from its definition."""
+    wl = make("mixtral_prefill")
+    ops = upload(wl, chunk=2)[:4]
+    g = train_step(wl, ops, -1)
+    k, f, d = wl.k, wl.f, wl.d
+    logits = t_out(g["logits"])
+    idx, w = O.route(logits, k, wl.gate)
+    assert np.array_equal(t_out(g["idx"]), idx)
+    plan = O.dispatch(idx, wl.E, -1, 0, wl.E)
+    assert np.array_equal(t_out(g["plan"].pair_pos)[:wl.T * k], plan["pair_pos"])
+    x64 = O.widen(wl.x, "bf16")
+    dy64 = O.widen(output_grad(wl), "bf16")
+    wg64 = O.widen(wl.w_gate, "f32")
+    cache = {}
+
+    def W(e):
+        if e not in cache:
+            cache[e] = tuple(O.widen(a, "bf16") for a in wl.expert_weights(e))
+        return cache[e]
+
+    tokens = (0, 1234, 4095)
+    dgate_ref = np.zeros((len(tokens), k))
+    dx_ref = np.zeros((len(tokens), d))
+    for i, t in enumerate(tokens):
+        for j in range(k):
+            w1, w3, w2 = W(int(idx[t, j]))
+            dgate_ref[i, j] = float(dy64[t] @ O.swiglu_ffn(x64[t:t + 1], w1, w3, w2)[0])
+            eb = B.expert_ffn_backward(x64[t:t + 1], np.array([0, 1]), lambda _: (w1, w3, w2),
+                                       w[t, j] * dy64[t:t + 1])
+            dx_ref[i] += eb["dx_perm"][0]
+        dl = B.gate_backward(logits[t:t + 1], idx[t:t + 1], dgate_ref[i:i + 1], wl.gate)
+        dx_ref[i] += (dl @ wg64.T)[0]
+    sel = list(tokens)
+    e_dg = O.rel_err(t_out(g["dgate"])[sel], dgate_ref)
+    e_dx = O.rel_err(as64(g["dx"], "bf16")[sel], dx_ref)
+    log(f"mixtral training: sampled dgate err {e_dg:.2e}, dx err {e_dx:.2e}")
+    assert e_dg <= 1e-2 and e_dx <= 1e-2
+    # weight-gradient columns: the FFN splits over the f columns, so the oracle's
+    # backward of the sub-FFN on columns S gives exactly dW1[:, S], dW3[:, S], dW2[S, :]
+    off, sp = plan["offsets"], plan["sorted_pair"]
+    dw13, dw2 = g["dw13"], g["dw2"]
+    S = np.array([0, 777, 14335])
+    for e in (0, 3, 7):
+        r0, r1 = int(off[e]), int(off[e + 1])
+        pairs = sp[r0:r1].astype(np.int64)
+        toks, js = pairs // k, pairs % k
+        do_e = w[toks, js][:, None] * dy64[toks]
+        w1, w3, w2 = W(e)
+        eb = B.expert_ffn_backward(x64[toks], np.array([0, r1 - r0]),
+                                   lambda _: (w1[:, S], w3[:, S], w2[S, :]), do_e)
+        got1 = dw13[e, torch.from_numpy(S).to(DEV)].cpu().numpy()
+        got3 = dw13[e, torch.from_numpy(S + f).to(DEV)].cpu().numpy()
+        got2 = dw2[e][:, torch.from_numpy(S).to(DEV)].cpu().numpy()
+        errs = (O.rel_err(got1, eb["dW1"][0].T), O.rel_err(got3, eb["dW3"][0].T),
+                O.rel_err(got2, eb["dW2"][0].T))
+        log(f"mixtral training: expert {e} ({r1 - r0} rows) dW1/dW3/dW2 column errs "
+            + " ".join(f"{v:.2e}" for v in errs))
+        assert max(errs) <= 1e-2
