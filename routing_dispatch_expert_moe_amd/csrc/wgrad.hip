@@ -303,17 +303,25 @@ __global__ __launch_bounds__(512, 1) void wgrad_bf16_kernel(const uint16_t* __re
     };
 #pragma unroll
     for (int p = 0; p < STAGES - 1; ++p) issue(p);
+    // step p becomes readable once at most the STAGES - 2 younger steps'
+    // loads are outstanding (loads complete in order) and the barrier has
+    // published every wave's share
+    wait_vmcnt<(STAGES - 2) * LSTEP>();
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    issue(STAGES - 1);
+    frags(0, 0, 0);
     for (int s = 0; s < KT; ++s) {
-      // step s landed (its loads are older than the STAGES - 2 younger
-      // steps'); every wave's reads of step s - 1 are done before its buffer
-      // is refilled
-      wait_vmcnt<(STAGES - 2) * LSTEP>();
-      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      issue(s + STAGES - 1);
       const int buf = s % STAGES;
-      frags(buf, 0, 0);
+      // substep 0: the second half's fragments load under the first half's MFMAs
       frags(buf, 1, 1);
       mfma(0);
+      // step s + 1 becomes readable; this wave's reads of step s are done, so
+      // after the barrier step s's buffer takes step s + STAGES; the next
+      // step's first fragments load under the second half's MFMAs
+      wait_vmcnt<(STAGES - 2) * LSTEP>();
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      issue(s + STAGES);
+      frags((s + 1) % STAGES, 0, 0);
       mfma(1);
     }
     wait_vmcnt<0>();
