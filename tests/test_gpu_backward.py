@@ -235,3 +235,23 @@ def test_mixtral_prefill_training_sampled():
         log(f"mixtral training: expert {e} ({r1 - r0} rows) dW1/dW3/dW2 column errs "
             + " ".join(f"{v:.2e}" for v in errs))
         assert max(errs) <= 1e-2
+
+
+@pytest.mark.parametrize("kw", [
+    dict(T=50, d=128, f=128, E=4, k=2, capacity_factor=0.0, seed=8),      # capacity 0: every pair drops
+    dict(T=40, d=128, f=192, E=4, k=4, seed=9),                           # k = E
+    dict(T=1, d=64, f=64, E=8, k=2, seed=10),                              # one token, most experts empty
+    dict(T=64, d=128, f=128, E=8, k=2, e_begin=3, e_end=4, seed=11),      # one local expert
+])
+def test_backward_edge_cases(kw):
+    wl = custom("edge", dtype="bf16", **kw)
+    w13, w2p, w13_t, w2_t, host = upload(wl, keep_host=True)
+    C = capacity_of(wl)
+    g = train_step(wl, (w13, w2p, w13_t, w2_t), C)
+    n = int(t_out(g["plan"].offsets)[-1])
+    if C == 0:
+        assert n == 0
+        assert not t_out(g["dx"]).any() and not t_out(g["dgate"]).any()
+        assert not t_out(g["dlogits"]).any()
+        assert not t_out(g["dw13"]).any() and not t_out(g["dw2"]).any()
+    check_against_oracle(wl, g, 1e-2, host)
