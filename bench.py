@@ -177,6 +177,37 @@ def load_traffic(args):
     return t[DOMINANT]["bytes"], "rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by a 1 GiB copy"
 
 
+def smi_snapshot():
+    """Graphics and memory clocks and socket power read from the driver's sysfs
+    files (plain reads; no program is started): {"sclk_mhz", "mclk_mhz",
+    "socket_power_w", "power_cap_w"}, or None where they are missing."""
+    import glob
+    import re
+
+    def current(path):
+        with open(path) as fh:
+            for line in fh:
+                if line.rstrip().endswith("*"):
+                    m = re.search(r"(\d+)\s*Mhz", line, re.I)
+                    return int(m.group(1)) if m else None
+        return None
+
+    try:
+        dev = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))[0].rsplit("/", 1)[0]
+        out = {"sclk_mhz": current(dev + "/pp_dpm_sclk"), "mclk_mhz": current(dev + "/pp_dpm_mclk")}
+        hw = sorted(glob.glob(dev + "/hwmon/hwmon*"))
+        if hw:
+            for key, name in (("socket_power_w", "power1_input"), ("power_cap_w", "power1_cap")):
+                try:
+                    with open(f"{hw[0]}/{name}") as fh:
+                        out[key] = round(int(fh.read().strip()) / 1e6, 1)
+                except (OSError, ValueError):
+                    out[key] = None
+        return out
+    except (IndexError, OSError):
+        return None
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -458,12 +489,14 @@ def main():
     log(f"n_kept={n} experts touched={touched} counts min={counts.min()} max={counts.max()}")
 
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    smi_before = smi_snapshot()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
         step(events[s])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    smi_after = smi_snapshot()
     ms_step = (t1 - t0) * 1e3 / args.steps
 
     # the same steps with the 256 MB Infinity Cache (MALL) evicted before each:
@@ -582,6 +615,10 @@ def main():
                          "per_step_median": cold,
                          "note": "1 GiB written between steps (outside the events) to evict "
                                  "the 256 MB Infinity Cache; HIP-event times per call"},
+        "power_clock": {"before_timed_steps": smi_before, "after_timed_steps": smi_after,
+                        "note": "driver sysfs snapshots (current graphics and memory clock "
+                                "levels, socket power) just before and just after the timed "
+                                "steps"},
         "training": training,
         "fused": None if fused_ms is None else {
             "entry": "moe_forward_fused", "ms_per_step_median": round(fused_ms, 4),
