@@ -526,7 +526,7 @@ def main():
             ev[1].record()
 
     fused_ms = None
-    if not fp8 and not args.reroute:   # the fused launch: bf16 / fp32 weights, plain routing
+    if not fp8:   # the fused launch: bf16 / fp32 weights (with the layer's routing)
         for _ in range(args.warmup):
             fused_step()
         torch.cuda.synchronize()
@@ -621,7 +621,8 @@ def main():
                                 "steps"},
         "training": training,
         "fused": None if fused_ms is None else {
-            "entry": "moe_forward_fused", "ms_per_step_median": round(fused_ms, 4),
+            "entry": "moe_forward_fused_reroute" if args.reroute else "moe_forward_fused",
+            "ms_per_step_median": round(fused_ms, 4),
             "tokens_per_s": round(wl.T / (fused_ms * 1e-3), 1),
             "unfused_ms_per_step_median": round(unfused_ms, 4),
             "speedup_vs_unfused": round(unfused_ms / fused_ms, 3)},

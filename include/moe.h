@@ -287,6 +287,23 @@ moe_status moe_forward_fused(const float* logits, const void* x, int T, int E, i
                              void* h, void* y_perm, void* y, void* ws, size_t ws_bytes,
                              void* stream);
 
+/* moe_forward_fused with moe_route_reroute's routing (sparse-activation page
+ * §3.2 stage 3, capacity-overflow rerouting in token order) in place of
+ * moe_route's: the same arguments (capacity drives both the rerouting and the
+ * dispatch's drops) and the same bits as moe_route_reroute -> moe_dispatch ->
+ * moe_expert_ffn -> moe_combine.  Inside the launch the candidates are taken
+ * by every workgroup, workgroup 0 resolves who reroutes (the rule is
+ * sequential) while the others wait at the next barrier, and the gates
+ * follow.  ws: moe_workspace_bytes(T, E, k, .) bytes (it holds the rerouting
+ * scratch after the dispatch scratch). */
+moe_status moe_forward_fused_reroute(const float* logits, const void* x, int T, int E, int k,
+                                     int gate, int capacity, int e_begin, int e_end, int d, int f,
+                                     moe_dtype dtype, const void* w13_packed,
+                                     const void* w2_packed, int32_t* topk_idx, float* topk_w,
+                                     int32_t* counts, int32_t* offsets, int32_t* sorted_pair,
+                                     int32_t* pair_pos, int32_t* n_kept, void* h, void* y_perm,
+                                     void* y, void* ws, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------------------
  * Backward pass (NCCL EP page §3.2, training adaptation: the backward step
  * reuses the forward's routing handle, sends the output gradient to the

@@ -510,13 +510,14 @@ moe_status moe_router_backward(const void* x, const float* w_gate, const float* 
                                                 dx, dw_gate, static_cast<float*>(ws), stream));
 }
 
-moe_status moe_forward_fused(const float* logits, const void* x, int T, int E, int k, int gate,
-                             int capacity, int e_begin, int e_end, int d, int f, moe_dtype dtype,
-                             const void* w13_packed, const void* w2_packed, int32_t* topk_idx,
-                             float* topk_w, int32_t* counts, int32_t* offsets,
-                             int32_t* sorted_pair, int32_t* pair_pos, int32_t* n_kept,
-                             void* h, void* y_perm, void* y, void* ws, size_t ws_bytes,
-                             void* stream) {
+static moe_status forward_fused_impl(const float* logits, const void* x, int T, int E, int k,
+                                     int gate, int capacity, int e_begin, int e_end, int d, int f,
+                                     moe_dtype dtype, const void* w13_packed,
+                                     const void* w2_packed, int32_t* topk_idx, float* topk_w,
+                                     int32_t* counts, int32_t* offsets, int32_t* sorted_pair,
+                                     int32_t* pair_pos, int32_t* n_kept, void* h, void* y_perm,
+                                     void* y, void* ws, size_t ws_bytes, void* stream,
+                                     bool reroute) {
   if (T < 0) return MOE_ERR_INVALID_ARG;
   moe_status st = check_topk(E, k);
   if (st != MOE_OK) return st;
@@ -543,9 +544,22 @@ moe_status moe_forward_fused(const float* logits, const void* x, int T, int E, i
       !aligned16(counts) || !aligned16(sorted_pair) || !aligned16(pair_pos) ||
       !aligned16(n_kept) || !aligned16(y) || !aligned16(ws))
     return MOE_ERR_MISALIGNED;
-  if (ws_bytes < moe::dispatch_ws_bytes(T, E)) return MOE_ERR_WORKSPACE;
+  if (ws_bytes < moe::dispatch_ws_bytes(T, E) + (reroute ? moe::reroute_ws_bytes(T, k) : 0))
+    return MOE_ERR_WORKSPACE;
   const moe::DispatchWs w = moe::dispatch_ws(ws, T, E);
   moe::FusedArgs a;
+  a.reroute = reroute ? 1 : 0;
+  a.cand_e = nullptr;
+  a.cand_v = nullptr;
+  a.rerouted = nullptr;
+  if (reroute) {  // the same workspace layout as moe_route_reroute
+    char* c = static_cast<char*>(ws) + moe::dispatch_ws_bytes(T, E);
+    const size_t cand_bytes =
+        (static_cast<size_t>(T) * (k + 1) * sizeof(int32_t) + 255) & ~static_cast<size_t>(255);
+    a.cand_e = reinterpret_cast<int32_t*>(c);
+    a.cand_v = reinterpret_cast<float*>(c + cand_bytes);
+    a.rerouted = reinterpret_cast<uint64_t*>(c + 2 * cand_bytes);
+  }
   a.logits = logits;
   a.x = x;
   a.w13 = w13_packed;
@@ -576,6 +590,30 @@ moe_status moe_forward_fused(const float* logits, const void* x, int T, int E, i
   a.bar_count = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + moe::kWsBarCount);
   a.bar_group = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + moe::kWsBarGroup);
   return hip_status(moe::launch_fused(a, dtype == MOE_BF16, max_rows, stream));
+}
+
+moe_status moe_forward_fused(const float* logits, const void* x, int T, int E, int k, int gate,
+                             int capacity, int e_begin, int e_end, int d, int f, moe_dtype dtype,
+                             const void* w13_packed, const void* w2_packed, int32_t* topk_idx,
+                             float* topk_w, int32_t* counts, int32_t* offsets,
+                             int32_t* sorted_pair, int32_t* pair_pos, int32_t* n_kept,
+                             void* h, void* y_perm, void* y, void* ws, size_t ws_bytes,
+                             void* stream) {
+  return forward_fused_impl(logits, x, T, E, k, gate, capacity, e_begin, e_end, d, f, dtype,
+                            w13_packed, w2_packed, topk_idx, topk_w, counts, offsets, sorted_pair,
+                            pair_pos, n_kept, h, y_perm, y, ws, ws_bytes, stream, false);
+}
+
+moe_status moe_forward_fused_reroute(const float* logits, const void* x, int T, int E, int k,
+                                     int gate, int capacity, int e_begin, int e_end, int d, int f,
+                                     moe_dtype dtype, const void* w13_packed,
+                                     const void* w2_packed, int32_t* topk_idx, float* topk_w,
+                                     int32_t* counts, int32_t* offsets, int32_t* sorted_pair,
+                                     int32_t* pair_pos, int32_t* n_kept, void* h, void* y_perm,
+                                     void* y, void* ws, size_t ws_bytes, void* stream) {
+  return forward_fused_impl(logits, x, T, E, k, gate, capacity, e_begin, e_end, d, f, dtype,
+                            w13_packed, w2_packed, topk_idx, topk_w, counts, offsets, sorted_pair,
+                            pair_pos, n_kept, h, y_perm, y, ws, ws_bytes, stream, true);
 }
 
 }  // extern "C"

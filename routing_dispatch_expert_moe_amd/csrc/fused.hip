@@ -10,7 +10,9 @@
 // One workgroup of 256 threads per CU (cooperative launch: every workgroup is
 // resident, so the device-wide barriers below cannot deadlock).  Phases, each
 // a loop over the phase's work units with stride = grid size:
-//   1. route (one wave per token);
+//   1. route (one wave per token); with rerouting: candidates (one wave per
+//      token), the sequential resolver on workgroup 0, then the gates (one
+//      thread per token), each step followed by a barrier;
 //   2. dispatch count pass of each 256-token block;
 //   3. every workgroup rebuilds the local segment offsets from the per-block
 //      counts (workgroup 0 also writes counts / offsets / n_kept), then places
@@ -32,6 +34,7 @@
 #include "gemm_f32.h"
 #include "gemm_pipe.h"
 #include "launch.h"
+#include "reroute_dev.h"
 #include "route_dev.h"
 
 namespace moe {
@@ -142,10 +145,49 @@ __global__ __launch_bounds__(256, 1) void moe_fused_kernel(FusedArgs a) {
   const int chunks = static_cast<int>((static_cast<size_t>(a.d) * (BF16 ? 2 : 4)) / 16);
 
   // ---- 1: route, one wave per token
-  for (int t = bid * 4 + wave; t < T; t += G * 4) {
-    if (E <= 64) route_token<1>(a.logits, t, E, k, a.gate, a.topk_idx, a.topk_w);
-    else if (E <= 256) route_token<4>(a.logits, t, E, k, a.gate, a.topk_idx, a.topk_w);
-    else route_token<16>(a.logits, t, E, k, a.gate, a.topk_idx, a.topk_w);
+  if (a.reroute) {
+    const int kc = k < E ? k + 1 : k;
+    for (int t = bid * 4 + wave; t < T; t += G * 4) {
+      if (E <= 64) reroute_candidates_token<1>(a.logits, t, E, kc, a.cand_e, a.cand_v);
+      else if (E <= 256) reroute_candidates_token<4>(a.logits, t, E, kc, a.cand_e, a.cand_v);
+      else reroute_candidates_token<16>(a.logits, t, E, kc, a.cand_e, a.cand_v);
+    }
+    grid_barrier(a, G);
+    const bool can = a.capacity >= 0 && k < E;
+    if (can && bid == 0) {
+      int* load = reinterpret_cast<int*>(lds);
+      int32_t* ce = load + MOE_MAX_E;
+      switch (k) {
+#define MOE_FUSED_RESOLVE(KK)                                                                   \
+  case KK:                                                                                     \
+    reroute_resolve_body<KK, 256>(a.cand_e, T, E, a.capacity, a.rerouted, load, ce);           \
+    break;
+        MOE_FUSED_RESOLVE(1) MOE_FUSED_RESOLVE(2) MOE_FUSED_RESOLVE(3) MOE_FUSED_RESOLVE(4)
+        MOE_FUSED_RESOLVE(5) MOE_FUSED_RESOLVE(6) MOE_FUSED_RESOLVE(7) MOE_FUSED_RESOLVE(8)
+#undef MOE_FUSED_RESOLVE
+        default: break;
+      }
+    }
+    grid_barrier(a, G);
+    for (int t = bid * 256 + static_cast<int>(threadIdx.x); t < T; t += G * 256) {
+      const uint64_t* rr = can ? a.rerouted : nullptr;
+      switch (k) {
+#define MOE_FUSED_GATES(KK)                                                                     \
+  case KK:                                                                                     \
+    reroute_finalize_token<KK>(a.cand_e, a.cand_v, rr, t, kc, a.gate, a.topk_idx, a.topk_w);   \
+    break;
+        MOE_FUSED_GATES(1) MOE_FUSED_GATES(2) MOE_FUSED_GATES(3) MOE_FUSED_GATES(4)
+        MOE_FUSED_GATES(5) MOE_FUSED_GATES(6) MOE_FUSED_GATES(7) MOE_FUSED_GATES(8)
+#undef MOE_FUSED_GATES
+        default: break;
+      }
+    }
+  } else {
+    for (int t = bid * 4 + wave; t < T; t += G * 4) {
+      if (E <= 64) route_token<1>(a.logits, t, E, k, a.gate, a.topk_idx, a.topk_w);
+      else if (E <= 256) route_token<4>(a.logits, t, E, k, a.gate, a.topk_idx, a.topk_w);
+      else route_token<16>(a.logits, t, E, k, a.gate, a.topk_idx, a.topk_w);
+    }
   }
   grid_barrier(a, G);
 
@@ -234,9 +276,21 @@ __global__ __launch_bounds__(256, 1) void moe_fused_kernel(FusedArgs a) {
                         static_cast<uint4*>(a.y));
 }
 
+// the rerouting resolver's LDS for any k
+constexpr size_t resolver_lds_bytes() {
+  size_t m = reroute_resolve_lds_bytes<1>();
+  const size_t b[] = {reroute_resolve_lds_bytes<2>(), reroute_resolve_lds_bytes<3>(),
+                      reroute_resolve_lds_bytes<4>(), reroute_resolve_lds_bytes<5>(),
+                      reroute_resolve_lds_bytes<6>(), reroute_resolve_lds_bytes<7>(),
+                      reroute_resolve_lds_bytes<8>()};
+  for (size_t v : b) m = v > m ? v : m;
+  return m;
+}
+
 size_t fused_lds_bytes(int E, bool bf16) {
-  const size_t plan = static_cast<size_t>(E) * kWords * sizeof(unsigned long long) +
-                      2 * static_cast<size_t>(E) * sizeof(int);
+  size_t plan = static_cast<size_t>(E) * kWords * sizeof(unsigned long long) +
+                2 * static_cast<size_t>(E) * sizeof(int);
+  if (plan < resolver_lds_bytes()) plan = resolver_lds_bytes();
   const size_t gemm = bf16 ? (pipe_lds_bytes(128, 128, 8) > pipe_lds_bytes(256, 256, 4)
                                   ? pipe_lds_bytes(128, 128, 8)
                                   : pipe_lds_bytes(256, 256, 4))

@@ -133,6 +133,10 @@ struct FusedArgs {
   void* h;
   void* y_perm;
   void* y;
+  int reroute;          // route with capacity-overflow rerouting (candidates below)
+  int32_t* cand_e;      // rerouting scratch in the workspace: [T][k+1] candidates,
+  float* cand_v;        //   their logits,
+  uint64_t* rerouted;   //   one rerouted mask per 64 tokens
   int* err;             // workspace error word
   int* block_counts;    // workspace per-block expert counts
   uint32_t* bar_gen;    // workspace barrier words: generation,

@@ -106,11 +106,12 @@ class MoELayer:
         """route -> dispatch -> expert FFN -> combine as one persistent launch."""
         if x.shape[0] != self.T:
             raise ValueError(f"layer was sized for T={self.T}, got {x.shape[0]}")
-        if self.fp8 or self.reroute:
-            raise NotImplementedError("the fused launch takes bf16 / fp32 weights and plain top-k routing")
+        if self.fp8:
+            raise NotImplementedError("the fused launch takes bf16 / fp32 weights")
         return ops.moe_forward_fused(logits, x, self.k, self.gate, self.capacity, self.e_begin,
                                      self.e_end, self.w13, self.w2, self.ws, self.plan,
-                                     self.topk_idx, self.topk_w, self.h, self.y_perm, self.y)
+                                     self.topk_idx, self.topk_w, self.h, self.y_perm, self.y,
+                                     reroute=self.reroute)
 
     # ---------------------------------------------------------------- training
     def enable_training(self, w13_t: torch.Tensor, w2_t: torch.Tensor) -> None:

@@ -306,7 +306,8 @@ def moe_check_error(ws, stream=None) -> int:
 
 
 def moe_forward_fused(logits, x, k, gate, capacity, e_begin, e_end, w13_packed, w2_packed, ws,
-                      plan: DispatchPlan, topk_idx, topk_w, h, y_perm, y, stream=None):
+                      plan: DispatchPlan, topk_idx, topk_w, h, y_perm, y, stream=None,
+                      reroute: bool = False):
     """The whole layer (route, dispatch, expert FFN, combine) in one persistent launch.
 
     Every output buffer is caller-provided (the layer preallocates them); they
@@ -315,13 +316,13 @@ def moe_forward_fused(logits, x, k, gate, capacity, e_begin, e_end, w13_packed, 
     T, E = logits.shape
     d = x.shape[1]
     f = w13_packed.shape[1] // 2
-    check(lib().moe_forward_fused(_ptr(logits), _ptr(x), T, E, k, _gate_code(gate), capacity,
-                                  e_begin, e_end, d, f, _dtype_code(x.dtype), _ptr(w13_packed),
-                                  _ptr(w2_packed), _ptr(topk_idx), _ptr(topk_w), _ptr(plan.counts),
-                                  _ptr(plan.offsets), _ptr(plan.sorted_pair), _ptr(plan.pair_pos),
-                                  _ptr(plan.n_kept), _ptr(h), _ptr(y_perm), _ptr(y), _ptr(ws),
-                                  ws.numel(), _stream(stream)),
-          "moe_forward_fused")
+    fn = lib().moe_forward_fused_reroute if reroute else lib().moe_forward_fused
+    check(fn(_ptr(logits), _ptr(x), T, E, k, _gate_code(gate), capacity, e_begin, e_end, d, f,
+             _dtype_code(x.dtype), _ptr(w13_packed), _ptr(w2_packed), _ptr(topk_idx), _ptr(topk_w),
+             _ptr(plan.counts), _ptr(plan.offsets), _ptr(plan.sorted_pair), _ptr(plan.pair_pos),
+             _ptr(plan.n_kept), _ptr(h), _ptr(y_perm), _ptr(y), _ptr(ws), ws.numel(),
+             _stream(stream)),
+          "moe_forward_fused_reroute" if reroute else "moe_forward_fused")
     return y
 
 

@@ -78,16 +78,17 @@ def capacity_of(wl) -> int:
     return c
 
 
-def layer_for(wl, w13, w2p, capacity=None) -> M.MoELayer:
+def layer_for(wl, w13, w2p, capacity=None, reroute=False) -> M.MoELayer:
     C = capacity_of(wl) if capacity is None else capacity
     return M.MoELayer(w13, w2p, E=wl.E, k=wl.k, gate=wl.gate, T=wl.T, capacity=C,
-                      e_begin=wl.e_begin, e_end=wl.e_end)
+                      e_begin=wl.e_begin, e_end=wl.e_end, reroute=reroute)
 
 
 def fused_matches_unfused(wl, w13, w2p, layer, x, logits, capacity=None):
-    """Run moe_forward_fused into a second layer's buffers and check that every
-    output carries the same bits as the separate calls in `layer`."""
-    fl = layer_for(wl, w13, w2p, capacity=capacity)
+    """Run moe_forward_fused (or its rerouting form, as `layer` routes) into a
+    second layer's buffers and check that every output carries the same bits as
+    the separate calls in `layer`."""
+    fl = layer_for(wl, w13, w2p, capacity=capacity, reroute=layer.reroute)
     fl.forward_fused(x, logits)
     assert M.moe_check_error(fl.ws) == 0
     a, b = layer.outputs(), fl.outputs()

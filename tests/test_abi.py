@@ -34,7 +34,7 @@ def test_header_declares_the_path():
               "moe_pack_weights", "moe_check_error", "moe_ffn_up", "moe_ffn_down",
               "moe_forward_fused", "moe_quantize_fp8", "moe_expert_ffn_fp8", "moe_ffn_up_fp8",
               "moe_ffn_down_fp8", "moe_expert_ffn_list", "moe_ffn_up_list", "moe_ffn_down_list",
-              "moe_route_reroute"):
+              "moe_route_reroute", "moe_forward_fused_reroute"):
         assert n in names
 
 
@@ -225,6 +225,23 @@ def test_fused_validation(lib):
     assert call(wsb=2047) == L.MOE_ERR_WORKSPACE
     # bf16 operands beyond 32-bit byte offsets are refused up front
     assert call(T=600000, k=8, E=8, d=4096, f=4096) == L.MOE_ERR_UNSUPPORTED
+    # the rerouting form takes the same arguments and needs the rerouting scratch too
+    g = lib.moe_forward_fused_reroute
+
+    def call_r(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return g(a["lg"], a["x"], a["T"], a["E"], a["k"], a["gate"], a["cap"], a["e0"], a["e1"],
+                 a["d"], a["f"], a["dt"], a["w13"], a["w2"], a["idx"], a["w"], a["counts"],
+                 a["off"], a["sp"], a["pp"], a["nk"], a["h"], a["yp"], a["y"], a["ws"], a["wsb"],
+                 None)
+
+    assert call_r(k=9) == L.MOE_ERR_INVALID_TOPK
+    assert call_r(gate=5) == L.MOE_ERR_INVALID_ARG
+    assert call_r(y=MIS) == L.MOE_ERR_MISALIGNED
+    # a workspace sized for the dispatch alone is too small once rerouting needs its scratch
+    dispatch_only = ws_ok - (100 * 3 * 4 + 255) // 256 * 256 * 2 - 256
+    assert call_r(wsb=dispatch_only) == L.MOE_ERR_WORKSPACE
 
 
 def test_package_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -66,3 +66,42 @@ def test_fused_all_dropped():
     assert int(t_out(layer.plan.n_kept)[0]) == 0
     assert np.all(t_out(layer.plan.pair_pos) == -1)
     assert np.all(t_out(y) == 0)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(name="r1", T=300, d=128, f=128, E=8, k=2, dtype="bf16", capacity_factor=0.8,
+         logit_bias="zipf"),
+    dict(name="r2", T=2500, d=64, f=128, E=16, k=2, dtype="bf16", capacity_factor=1.0,
+         e_begin=2, e_end=11, logit_bias="normal"),                     # several resolver chunks
+    dict(name="r3", T=200, d=64, f=64, E=32, k=8, dtype="f32", capacity_factor=1.0,
+         gate=O.GATE_SIGMOID, logit_bias="zipf"),
+    dict(name="r4", T=90, d=64, f=64, E=4, k=4, dtype="bf16", capacity_factor=0.5),  # k = E
+])
+def test_fused_layer_with_rerouting(kw):
+    """moe_forward_fused_reroute against the separate calls (bit for bit) and the
+    oracle's rerouting -> dispatch -> FFN -> combine."""
+    kw = dict(kw)
+    log(f"fused layer with rerouting {kw}")
+    name = kw.pop("name")
+    wl = custom(name, seed=6, **kw)
+    w13, w2p, host = packed_weights(wl, keep_host=True)
+    C = capacity_of(wl)
+    layer = layer_for(wl, w13, w2p, reroute=True)
+    x = t_in(wl.x, wl.dtype)
+    logits = t_in(wl.logits, "f32")
+    layer.forward(x, logits=logits)
+    assert M.moe_check_error(layer.ws) == 0
+    fl = fused_matches_unfused(wl, w13, w2p, layer, x, logits)
+    idx, w = O.route_reroute(wl.logits, wl.k, wl.gate, C)
+    plan = O.dispatch(idx, wl.E, C, wl.e_begin, wl.e_end)
+    x64 = O.widen(wl.x, wl.dtype)
+    y_perm = O.expert_ffn(O.permute(x64, plan["sorted_pair"], wl.k), plan["offsets"],
+                          weights_fn(wl, host))
+    y = O.combine(y_perm, plan["pair_pos"], w)
+    out = fl.outputs()
+    assert np.array_equal(t_out(out["topk_idx"]), idx)
+    assert O.rel_err(t_out(out["topk_w"]), w) <= GATE_TOL
+    assert np.array_equal(t_out(out["pair_pos"]), plan["pair_pos"])
+    moved = int((idx[:, 0] != O.route(wl.logits, wl.k, wl.gate)[0][:, 0]).sum())
+    log(f"{name}: {moved} of {wl.T} tokens rerouted")
+    assert O.rel_err(as64(fl.y, wl.dtype), y) <= TOL[wl.dtype]

@@ -141,3 +141,33 @@ def test_mixtral_prefill_with_router():
     # the fused persistent launch on the same GPU logits: same bits as the separate calls
     log("mixtral_prefill: fused layer")
     fused_matches_unfused(wl, w13, w2p, layer, x, out["logits"])
+
+
+@pytest.mark.timeout(600)
+def test_ep_rank_share_with_rerouting():
+    """The EP-rank layer with capacity-overflow rerouting in front of the
+    dispatch (as `bench.py --reroute` runs it): rerouted indices, the plan and
+    x_perm bit-exact, sampled token outputs against the oracle."""
+    wl = make("ep_rank_share")
+    w13, w2p, host = weights(wl)
+    C = capacity_of(wl)
+    layer = M.MoELayer(w13, w2p, E=wl.E, k=wl.k, gate=wl.gate, T=wl.T, capacity=C,
+                       e_begin=wl.e_begin, e_end=wl.e_end, reroute=True)
+    x = t_in(wl.x, wl.dtype)
+    y = layer.forward(x, logits=t_in(wl.logits, "f32"))
+    assert M.moe_check_error(layer.ws) == 0
+    out = layer.outputs()
+    idx, w = O.route_reroute(wl.logits, wl.k, wl.gate, C)
+    assert np.array_equal(t_out(out["topk_idx"]), idx)
+    assert O.rel_err(t_out(out["topk_w"]), w) <= 1e-6
+    ref = O.dispatch(idx, wl.E, C, wl.e_begin, wl.e_end)
+    check_plan(out, ref, wl.T, wl.k)
+    n = ref["n_kept"]
+    plain = O.dispatch(O.route(wl.logits, wl.k, wl.gate)[0], wl.E, C, wl.e_begin, wl.e_end)
+    log(f"ep_rank_share with rerouting: n_kept={n} (plain top-k {plain['n_kept']}), "
+        f"dropped={(ref['pair_pos'] == O.DROPPED).sum()} (plain {(plain['pair_pos'] == O.DROPPED).sum()})")
+    assert np.array_equal(t_out(out["x_perm"])[:n], O.permute(wl.x, ref["sorted_pair"], wl.k))
+    toks = sampled_tokens(wl.T, ref["pair_pos"], wl.k, n=24, seed=3)
+    check_outputs(wl, host, y, idx, w, ref["pair_pos"], toks)
+    log("ep_rank_share with rerouting: fused layer")
+    fused_matches_unfused(wl, w13, w2p, layer, x, t_in(wl.logits, "f32"), capacity=C)
