@@ -77,7 +77,7 @@ int launch_quantize_fp8(const void* w, int E_loc, int R, int K, uint8_t* q, floa
 // the segment [offsets[e], offsets[e+1]); the persistent grid walks tiles in
 // expert order, M-tiles fastest, with the XCD-aware workgroup remap.
 template <int BN, bool SWIGLU>
-__global__ __launch_bounds__(256, 3) void gemm_fp8w_kernel(const uint16_t* __restrict__ A,
+__global__ __launch_bounds__(256, 2) void gemm_fp8w_kernel(const uint16_t* __restrict__ A,
                                                         const int32_t* __restrict__ offsets,
                                                         int E_loc, const uint8_t* __restrict__ Wq,
                                                         const float* __restrict__ Ws,
@@ -173,11 +173,35 @@ __global__ __launch_bounds__(256, 3) void gemm_fp8w_kernel(const uint16_t* __res
       acc[j] = part[j] = f32x16_t{};
       if constexpr (SWIGLU) accg[j] = partg[j] = f32x16_t{};
     }
+    // block scales of step kt (the wave's columns lie in one 128-row block)
+    float sc[FN], scg[SWIGLU ? FN : 1];
+    auto sload = [&](int kt) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int rowb = (n0 + wn * TN + j * 32) / kFp8Block;
+        sc[j] = Ws[(static_cast<size_t>(e) * RB + rowb) * KT + kt];
+        if constexpr (SWIGLU)
+          scg[j] = Ws[(static_cast<size_t>(e) * RB + N / kFp8Block + rowb) * KT + kt];
+      }
+    };
+    sload(0);
     gload(0);
     sstore();
     __syncthreads();
     for (int kt = 0; kt < KT; ++kt) {
-      gload(min(kt + 1, KT - 1));  // the last step re-fetches (valid, unused)
+      float scc[FN], scgc[SWIGLU ? FN : 1];
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        scc[j] = sc[j];
+        if constexpr (SWIGLU) scgc[j] = scg[j];
+      }
+      // the next step's scales and codes load under this step's MFMAs (the
+      // last step re-fetches: valid, unused); the scheduling barrier keeps
+      // them ahead of the MFMAs (left to itself the scheduler sinks them next
+      // to the LDS stores that consume them, exposing the memory latency)
+      sload(min(kt + 1, KT - 1));
+      gload(min(kt + 1, KT - 1));
+      __builtin_amdgcn_sched_barrier(0);
       const int h = lane >> 5;
 #pragma unroll
       for (int ks = 0; ks < BK / 16; ++ks) {
@@ -195,11 +219,10 @@ __global__ __launch_bounds__(256, 3) void gemm_fp8w_kernel(const uint16_t* __res
       // the step is one scale block: scale its partial sums into the result
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        const int rowb = (n0 + wn * TN + j * 32) / kFp8Block;
-        acc[j] += Ws[(static_cast<size_t>(e) * RB + rowb) * KT + kt] * part[j];
+        acc[j] += scc[j] * part[j];
         part[j] = f32x16_t{};
         if constexpr (SWIGLU) {
-          accg[j] += Ws[(static_cast<size_t>(e) * RB + N / kFp8Block + rowb) * KT + kt] * partg[j];
+          accg[j] += scgc[j] * partg[j];
           partg[j] = f32x16_t{};
         }
       }
