@@ -30,6 +30,18 @@ namespace moe {
 
 __device__ __forceinline__ float silu_f(float a) { return a * __builtin_amdgcn_rcpf(1.f + __expf(-a)); }
 
+// 16 / 8 bytes through a global-address-space pointer (a global load)
+typedef uint32_t u32x4_g __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_g __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 gload16(const __attribute__((address_space(1))) void* p) {
+  const u32x4_g v = *static_cast<const __attribute__((address_space(1))) u32x4_g*>(p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 gload8(const __attribute__((address_space(1))) void* p) {
+  const u32x2_g v = *static_cast<const __attribute__((address_space(1))) u32x2_g*>(p);
+  return make_uint2(v.x, v.y);
+}
+
 // FP8W: the weights are E4M3 codes (one byte each) with one fp32 scale per
 // 128 x 128 block of the packed matrix (Ws: [E][rows / 128][K / 128]) (NCCL
 // EP page §2.1: FP8 expert compute with a scale tensor).  Codes become bf16
@@ -89,9 +101,14 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(
     const int seg0 = offsets[e] + first, seg1 = seg0 + count;
     const int m0 = seg0 + mti * BM;
     const int n0 = nt * BN;
-    // expert e's packed weights: W + e * stride, or wlist[e] (a table of per-expert buffers)
-    const uint16_t* We = wlist != nullptr ? static_cast<const uint16_t*>(wlist[e]) : W + e * wstride;
-    const uint8_t* Wqe = wlist != nullptr ? static_cast<const uint8_t*>(wlist[e]) : Wq + e * wstride;
+    // expert e's packed weights: W + e * stride, or wlist[e] (a table of
+    // per-expert buffers).  A pointer read from the table is generic; marked
+    // global, the weight loads stay global loads (a flat load also counts on
+    // the LDS counter, so every LDS wait before an MFMA would wait for HBM)
+    using gu16 = const __attribute__((address_space(1))) uint16_t;
+    using gu8 = const __attribute__((address_space(1))) uint8_t;
+    gu16* We = (gu16*)(wlist != nullptr ? static_cast<const uint16_t*>(wlist[e]) : W + e * wstride);
+    gu8* Wqe = (gu8*)(wlist != nullptr ? static_cast<const uint8_t*>(wlist[e]) : Wq + e * wstride);
 
     // per-thread load descriptors
     const uint16_t* a_src[CA];
@@ -106,8 +123,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(
       a_src[i] = A + static_cast<size_t>(a_ok[i] ? row : seg0) * K + kc * 8;
       a_dst[i] = r * KC + (kc ^ ((r >> 1) & (KC - 1)));
     }
-    const uint16_t* b_src[CB];
-    const uint8_t* bq_src[CB];
+    gu16* b_src[CB];
+    gu8* bq_src[CB];
     bool b_ok[CB];
     int b_dst[CB];
 #pragma unroll
@@ -156,13 +173,13 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(
     auto gload_b = [&](int kt) {
       const int koff = kt * BK;
 #pragma unroll
-      for (int i = 0; i < CB; ++i) rb[i] = *reinterpret_cast<const uint4*>(b_src[i] + koff);
+      for (int i = 0; i < CB; ++i) rb[i] = gload16(b_src[i] + koff);
     };
     auto gload_q = [&](int kt, uint2 (&rq)[FP8W ? CB : 1]) {
       const int koff = kt * BK;
 #pragma unroll
       for (int i = 0; i < CB; ++i)  // 8 codes (8 bytes) per chunk
-        rq[i] = *reinterpret_cast<const uint2*>(bq_src[i] + koff);
+        rq[i] = gload8(bq_src[i] + koff);
     };
     auto sstore = [&](int buf) {
 #pragma unroll
