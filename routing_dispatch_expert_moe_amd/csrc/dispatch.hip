@@ -98,7 +98,7 @@ __global__ __launch_bounds__(256) void permute_rows_kernel(const uint4* __restri
                                                            uint4* __restrict__ x_perm) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  permute_token(x, t, k, chunks, pair_pos, x_perm);
+  permute_token<8, true>(x, t, k, chunks, pair_pos, x_perm);
 }
 
 int launch_dispatch(const int32_t* idx, int T, int E, int k, int capacity, int e_begin,

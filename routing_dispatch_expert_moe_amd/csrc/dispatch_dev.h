@@ -105,6 +105,9 @@ __device__ __forceinline__ void dispatch_place_block(
 
 // x_perm[row] = x[t] for every kept local pair of token t: one wave per token
 // reads the token's row once (16-byte loads) and writes it to its <= k rows.
+// U: 16-byte chunks per lane loaded before their stores; NT: streaming
+// (non-temporal) stores
+template <int U = 4, bool NT = false>
 __device__ __forceinline__ void permute_token(const uint4* __restrict__ x, int t, int k, int chunks,
                                               const int32_t* __restrict__ pair_pos,
                                               uint4* __restrict__ x_perm) {
@@ -118,8 +121,6 @@ __device__ __forceinline__ void permute_token(const uint4* __restrict__ x, int t
   }
   if (!any) return;
   const uint4* src = x + (size_t)t * chunks;
-  // 4 chunks per lane in flight before the stores
-  constexpr int U = 4;
   for (int c0 = lane; c0 < chunks; c0 += U * kWave) {
     uint4 v[U];
 #pragma unroll
@@ -130,8 +131,17 @@ __device__ __forceinline__ void permute_token(const uint4* __restrict__ x, int t
       const int c = c0 + u * kWave;
       if (c >= chunks) break;
 #pragma unroll
-      for (int j = 0; j < MOE_MAX_K; ++j)
-        if (rows[j] >= 0) x_perm[(size_t)rows[j] * chunks + c] = v[u];
+      for (int j = 0; j < MOE_MAX_K; ++j) {
+        if (rows[j] < 0) continue;
+        uint4* dst = x_perm + (size_t)rows[j] * chunks + c;
+        if constexpr (NT) {
+          typedef uint32_t u32x4_nt __attribute__((ext_vector_type(4)));
+          __builtin_nontemporal_store(u32x4_nt{v[u].x, v[u].y, v[u].z, v[u].w},
+                                      reinterpret_cast<u32x4_nt*>(dst));
+        } else {
+          *dst = v[u];
+        }
+      }
     }
   }
 }
