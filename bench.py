@@ -508,7 +508,19 @@ def main():
         scratch.fill_(s & 0xFF)
         step(cev[s])
     torch.cuda.synchronize()
-    del scratch
+    # a plain-copy reference on the same device and under the same eviction:
+    # torch's copy_ of a 1 GiB buffer, read + write bytes counted
+    src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    rev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(5)]
+    for s in range(5):
+        scratch.fill_(s)
+        rev[s][0].record()
+        dst.copy_(src)
+        rev[s][1].record()
+    torch.cuda.synchronize()
+    copy_ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in rev]))
+    del scratch, src, dst
     cold_ms = {name: float(np.median([cev[s][i].elapsed_time(cev[s][i + 1])
                                       for s in range(args.steps)]))
                for i, name in enumerate(STEPS)}
@@ -615,6 +627,12 @@ def main():
                          "per_step_median": cold,
                          "note": "1 GiB written between steps (outside the events) to evict "
                                  "the 256 MB Infinity Cache; HIP-event times per call"},
+        "hbm_copy_reference": {"gbs": round(2 * COPY_BYTES / (copy_ms * 1e-3) / 1e9, 1),
+                               "frac_of_peak": round(2 * COPY_BYTES / (copy_ms * 1e-3) / 1e9
+                                                     / PEAK_HBM_GBS, 4),
+                               "note": "torch copy_ of a 1 GiB buffer (read + write bytes), "
+                                       "Infinity Cache evicted before each, median of 5: "
+                                       "what a plain copy reaches on this device"},
         "power_clock": {"before_timed_steps": smi_before, "after_timed_steps": smi_after,
                         "note": "driver sysfs snapshots (current graphics and memory clock "
                                 "levels, socket power) just before and just after the timed "
