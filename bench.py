@@ -62,6 +62,10 @@ def parse():
     p.add_argument("--traffic-from", default=None, metavar="DIR",
                    help="turn rocprofv3 --pmc databases under DIR/{fetch,write,copy_fetch,"
                         "copy_write} into profiles/traffic_<workload>.json and exit")
+    p.add_argument("--counters-from", default=None, metavar="DIR",
+                   help="summarise a rocprofv3 --pmc database under DIR taken with "
+                        + " ".join(MFMA_COUNTERS) + " (MFMA busy fraction and counted "
+                        "MFMA flops per kernel) and exit")
     return p.parse_args()
 
 
@@ -125,6 +129,41 @@ def _pmc_per_dispatch(path, counter):
             name, v = out.get(k, (kname, 0.0))
             out[k] = (name, v + float(val))
     return out
+
+
+# ---- MFMA utilisation of the MFMA kernels from hardware counters ------------
+#
+# One rocprofv3 --pmc pass with MFMA_COUNTERS over a short bench run.  As the
+# database stores them, SQ_VALU_MFMA_BUSY_CYCLES is summed over every SIMD and
+# GRBM_GUI_ACTIVE over the XCDs, so the busy fraction of the MFMA pipes while a
+# kernel runs is busy / (GUI_ACTIVE / XCDs * SIMDs); SQ_INSTS_VALU_MFMA_MOPS_BF16
+# counts MFMA work in units of 512 flops.
+MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_BUSY_CYCLES",
+                 "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_WAIT_INST_LDS", "SQ_INSTS_LDS",
+                 "SQ_WAVE_CYCLES", "GRBM_GUI_ACTIVE")
+N_XCD, N_SIMD = 8, 256 * 4                      # MI355X: 8 XCDs, 256 CUs of 4 SIMDs
+
+
+def counters_from(args):
+    per = {}
+    for ctr in MFMA_COUNTERS:
+        for (f, did), (name, v) in _pmc_per_dispatch(args.counters_from, ctr).items():
+            per.setdefault((f, did), {"kernel": name.split("(")[0]})[ctr] = v
+    groups = {}
+    for rec in per.values():
+        if rec.get("SQ_VALU_MFMA_BUSY_CYCLES", 0) > 0 and rec.get("GRBM_GUI_ACTIVE", 0) > 0:
+            groups.setdefault(rec["kernel"], []).append(rec)
+    for name, recs in sorted(groups.items(), key=lambda kv: -sum(r["SQ_VALU_MFMA_BUSY_CYCLES"]
+                                                                 for r in kv[1])):
+        mean = {c: float(np.mean([r.get(c, 0.0) for r in recs])) for c in MFMA_COUNTERS}
+        cycles = mean["GRBM_GUI_ACTIVE"] / N_XCD
+        print(json.dumps({
+            "kernel": name, "dispatches": len(recs), "active_cycles": round(cycles),
+            "mfma_busy_frac": round(mean["SQ_VALU_MFMA_BUSY_CYCLES"] / (cycles * N_SIMD), 4),
+            "mfma_flops_counted": mean["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512,
+            "lds_bank_conflict_cycles": mean["SQ_LDS_BANK_CONFLICT"],
+            "lds_instructions": mean["SQ_INSTS_LDS"],
+            "lds_issue_wait_quad_cycles": mean["SQ_WAIT_INST_LDS"]}))
 
 
 def traffic_from(args):
@@ -392,6 +431,9 @@ def main():
         return
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.counters_from:
+        counters_from(args)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; "
