@@ -333,7 +333,7 @@ static int launch_gemm(const void* A, const int32_t* offsets, int E_loc, int64_t
   }
   const int64_t NT = (N + BN - 1) / BN;
   int64_t tiles_ub = (max_rows / BM + E_loc) * NT;
-  if (CLASS == ROWS_TAIL) tiles_ub = static_cast<int64_t>(E_loc) * ((kTailMax + BM - 1) / BM) * NT;
+  if (is_tail_class(CLASS)) tiles_ub = static_cast<int64_t>(E_loc) * ((kTailMax + BM - 1) / BM) * NT;
   int occ = 0;
   hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(kern),
                                                              WM * WN * 64, lds);
@@ -355,6 +355,10 @@ static int launch_gemm(const void* A, const int32_t* offsets, int E_loc, int64_t
 #endif
 constexpr bool kDecodeSmallTiles = MOE_DECODE_SMALL_TILES != 0;
 constexpr int64_t kStreamRows = 48;
+#ifndef MOE_RIDE
+#define MOE_RIDE 1
+#endif
+constexpr bool kRide = MOE_RIDE != 0;
 
 // Rows per expert on average decide the kernels: with few rows per expert the
 // FFN is weight streaming and one small-tile kernel takes every row.
@@ -362,7 +366,10 @@ constexpr int64_t kStreamRows = 48;
 // has few, short tiles (few experts, K <= 4096) it also takes each expert's
 // last block, even when less than half full (that tile shares its weights
 // with the expert's other tiles through L2), else a small-tile kernel takes
-// the short remainders (ROWS_BIG / ROWS_TAIL).  Row counts stay on the device.
+// the short remainders (ROWS_BIG / ROWS_TAIL); with many tiles, an expert
+// that has a full block keeps its short last block in the large tiles too
+// (ROWS_BIGR / ROWS_TAILR), so no expert's weights are streamed by both
+// kernels.  Row counts stay on the device.
 int launch_ffn_up_bf16(const void* x_perm, const int32_t* offsets, int E_loc, int64_t max_rows,
                        int d, int f, const void* w13, void* h, const void* const* wlist,
                        void* stream) {
@@ -381,9 +388,10 @@ int launch_ffn_up_bf16(const void* x_perm, const int32_t* offsets, int E_loc, in
   }
   if (remainders_with_big_tiles(E_loc, f, d, true))
     return launch_gemm_pipe_bf16(PipeRows::kBigAll, true, x_perm, offsets, E_loc, max_rows, w13, h, f, d, wlist, stream);
-  int e = launch_gemm_pipe_bf16(PipeRows::kBigTiles, true, x_perm, offsets, E_loc, max_rows, w13, h, f, d, wlist, stream);
+  const bool ride = kRide && !few_gemm_tiles(E_loc, f, true);
+  int e = launch_gemm_pipe_bf16(ride ? PipeRows::kBigRide : PipeRows::kBigTiles, true, x_perm, offsets, E_loc, max_rows, w13, h, f, d, wlist, stream);
   if (e != 0) return e;
-  return launch_gemm_pipe_bf16(PipeRows::kTailTiles, true, x_perm, offsets, E_loc, max_rows, w13, h, f, d, wlist, stream);
+  return launch_gemm_pipe_bf16(ride ? PipeRows::kTailRide : PipeRows::kTailTiles, true, x_perm, offsets, E_loc, max_rows, w13, h, f, d, wlist, stream);
 }
 
 // Always the pipelined kernels (the only ones with the pre-activation store);
@@ -397,9 +405,10 @@ int launch_ffn_up_train_bf16(const void* x_perm, const int32_t* offsets, int E_l
     return launch_gemm_pipe_bf16(PipeRows::kAllRows, true, x_perm, offsets, E_loc, max_rows, w13, h, f, d, nullptr, stream, ab);
   if (remainders_with_big_tiles(E_loc, f, d, true))
     return launch_gemm_pipe_bf16(PipeRows::kBigAll, true, x_perm, offsets, E_loc, max_rows, w13, h, f, d, nullptr, stream, ab);
-  int e = launch_gemm_pipe_bf16(PipeRows::kBigTiles, true, x_perm, offsets, E_loc, max_rows, w13, h, f, d, nullptr, stream, ab);
+  const bool ride = kRide && !few_gemm_tiles(E_loc, f, true);
+  int e = launch_gemm_pipe_bf16(ride ? PipeRows::kBigRide : PipeRows::kBigTiles, true, x_perm, offsets, E_loc, max_rows, w13, h, f, d, nullptr, stream, ab);
   if (e != 0) return e;
-  return launch_gemm_pipe_bf16(PipeRows::kTailTiles, true, x_perm, offsets, E_loc, max_rows, w13, h, f, d, nullptr, stream, ab);
+  return launch_gemm_pipe_bf16(ride ? PipeRows::kTailRide : PipeRows::kTailTiles, true, x_perm, offsets, E_loc, max_rows, w13, h, f, d, nullptr, stream, ab);
 }
 
 int launch_ffn_down_bf16(const void* h, const int32_t* offsets, int E_loc, int64_t max_rows,
@@ -419,9 +428,10 @@ int launch_ffn_down_bf16(const void* h, const int32_t* offsets, int E_loc, int64
   }
   if (remainders_with_big_tiles(E_loc, d, f, false))
     return launch_gemm_pipe_bf16(PipeRows::kBigAll, false, h, offsets, E_loc, max_rows, w2, y, d, f, wlist, stream);
-  int e = launch_gemm_pipe_bf16(PipeRows::kBigTiles, false, h, offsets, E_loc, max_rows, w2, y, d, f, wlist, stream);
+  const bool ride = kRide && !few_gemm_tiles(E_loc, d, false);
+  int e = launch_gemm_pipe_bf16(ride ? PipeRows::kBigRide : PipeRows::kBigTiles, false, h, offsets, E_loc, max_rows, w2, y, d, f, wlist, stream);
   if (e != 0) return e;
-  return launch_gemm_pipe_bf16(PipeRows::kTailTiles, false, h, offsets, E_loc, max_rows, w2, y, d, f, wlist, stream);
+  return launch_gemm_pipe_bf16(ride ? PipeRows::kTailRide : PipeRows::kTailTiles, false, h, offsets, E_loc, max_rows, w2, y, d, f, wlist, stream);
 }
 
 }  // namespace moe

@@ -45,7 +45,7 @@ int launch_pipe(const void* A, const int32_t* offsets, int E_loc, int64_t max_ro
   const int BN = SWIGLU ? BNW / 2 : BNW;
   const int64_t NT = (N + BN - 1) / BN;
   int64_t tiles_ub = (max_rows / BM + E_loc) * NT;
-  if (CLASS == ROWS_TAIL) tiles_ub = static_cast<int64_t>(E_loc) * ((kTailMax + BM - 1) / BM) * NT;
+  if (is_tail_class(CLASS)) tiles_ub = static_cast<int64_t>(E_loc) * ((kTailMax + BM - 1) / BM) * NT;
   int64_t grid = device_cu_count();
   if (grid > tiles_ub) grid = tiles_ub;
   if (grid >= 8) grid &= ~static_cast<int64_t>(7);
@@ -70,6 +70,11 @@ int launch_kind(PipeRows rows, const void* A, const int32_t* offsets, int E_loc,
   switch (rows) {
     case PipeRows::kBigTiles:
       return launch_pipe<SWIGLU, 256, 256, 4, ROWS_BIG, SAVE>(A, offsets, E_loc, max_rows, W, C, N, K, wlist, AB, s);
+    case PipeRows::kBigRide:
+      return launch_pipe<SWIGLU, 256, 256, 4, ROWS_BIGR, SAVE>(A, offsets, E_loc, max_rows, W, C, N, K, wlist, AB, s);
+    case PipeRows::kTailRide:
+      return launch_pipe<SWIGLU, 128, 256, 6, ROWS_TAILR, SAVE>(A, offsets, E_loc, max_rows, W, C, N,
+                                                                 K, wlist, AB, s);
     case PipeRows::kBigAll:
       return launch_pipe<SWIGLU, 256, 256, 4, ROWS_ALL, SAVE>(A, offsets, E_loc, max_rows, W, C, N, K, wlist, AB, s);
     case PipeRows::kTailTiles: {

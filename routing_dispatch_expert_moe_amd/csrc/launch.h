@@ -47,8 +47,10 @@ int launch_ffn_down_bf16(const void* h, const int32_t* offsets, int E_loc, int64
 // each expert's full blocks (kBigTiles), 256-row tiles over every row with
 // the last block of an expert as a possibly half-empty tile (kBigAll),
 // smaller tiles over the short remainders (kTailTiles), or smaller tiles over
-// every row (kAllRows).
-enum class PipeRows { kBigTiles, kBigAll, kTailTiles, kAllRows };
+// every row (kAllRows); kBigRide / kTailRide: 256-row tiles over every row of
+// the experts with at least one full block, smaller tiles over the experts
+// with fewer than 128 rows (passes with many tiles).
+enum class PipeRows { kBigTiles, kBigAll, kTailTiles, kAllRows, kBigRide, kTailRide };
 // true when one GEMM pass over E_loc experts with N output columns gives few
 // tiles (fewer than 4 per CU with 256-row weight tiles): then remainders ride
 // along with the 256-row tiles instead of a second kernel re-streaming weights

@@ -6,7 +6,13 @@
 //   ROWS_BIG   the full 256-row blocks, plus a last partial block when it is
 //              at least half full (large-tile kernel),
 //   ROWS_TAIL  whatever ROWS_BIG leaves: a last block of fewer than 128 rows,
-//              or all rows of an expert with fewer than 128 (small-tile kernel).
+//              or all rows of an expert with fewer than 128 (small-tile kernel);
+//   ROWS_BIGR / ROWS_TAILR  the same split for passes with many tiles, except
+//              that an expert with at least one full block also takes its
+//              short last block in the large tiles: that tile reads the weight
+//              tiles the expert's full blocks stream anyway, where the
+//              small-tile kernel would stream the expert's weights a second
+//              time; the small tiles keep the experts with fewer than 128 rows.
 // With this split no large tile runs less than half full, and skewed expert
 // loads (a few experts with thousands of rows, most with tens) keep both
 // kernels busy on useful rows.
@@ -19,7 +25,9 @@ namespace moe {
 constexpr int kBigM = 256;     // rows per large tile
 constexpr int kTailMax = 128;  // a last block below this many rows goes to the small tiles
 
-enum RowClass { ROWS_ALL = 0, ROWS_BIG = 1, ROWS_TAIL = 2 };
+enum RowClass { ROWS_ALL = 0, ROWS_BIG = 1, ROWS_TAIL = 2, ROWS_BIGR = 3, ROWS_TAILR = 4 };
+
+constexpr bool is_tail_class(int c) { return c == ROWS_TAIL || c == ROWS_TAILR; }
 
 // rows [first, first + count) of an n-row segment belong to class CLASS
 template <int CLASS>
@@ -30,8 +38,10 @@ __device__ __forceinline__ void class_rows(int n, int& first, int& count) {
   } else {
     const int full = (n / kBigM) * kBigM;
     const int rem = n - full;
-    const int split = rem >= kTailMax ? n : full;  // rows [0, split) are large-tile rows
-    if constexpr (CLASS == ROWS_BIG) {
+    constexpr bool ride = CLASS == ROWS_BIGR || CLASS == ROWS_TAILR;
+    // rows [0, split) are large-tile rows
+    const int split = (rem >= kTailMax || (ride && n >= kBigM)) ? n : full;
+    if constexpr (!is_tail_class(CLASS)) {
       first = 0;
       count = split;
     } else {

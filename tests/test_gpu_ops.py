@@ -153,6 +153,10 @@ def test_dispatch_flags_invalid_index():
     ("bf16", 192, 128, [40] * 8), ("bf16", 128, 128, [3, 2, 7, 0, 1, 11, 4, 5, 6, 9]),
     # large/small tile split boundaries: 256-row blocks, remainders of 127/128, empty experts
     ("bf16", 128, 192, [1024, 1152, 1100, 128, 127, 255, 256, 0, 384, 513]),
+    # many tiles per pass (256 experts x 4 weight tiles each way): experts with
+    # a full 256-row block keep their short last block (44 or 88 rows) in the
+    # large tiles, the 50-row experts go to the small tiles
+    ("bf16", 1024, 512, [50] * 200 + [300] * 20 + [600] * 10 + [160] * 10 + [512] * 10 + [0] * 6),
     ("f32", 128, 256, [17, 0, 111]), ("f32", 32, 48, [5, 70, 1]), ("f32", 12, 20, [3, 64, 65])])
 def test_expert_ffn(dtype, d, f, rows):
     log(f"ffn {dtype} d={d} f={f} rows={rows}")
