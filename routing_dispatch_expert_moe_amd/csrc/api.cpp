@@ -574,6 +574,9 @@ static moe_status forward_fused_impl(const float* logits, const void* x, int T, 
   a.d = d;
   a.f = f;
   a.ffn_all_rows = max_rows / E_loc <= 48 ? 1 : 0;
+  // the same many-tiles rule as the separate FFN calls
+  a.ride_up = moe::few_gemm_tiles(E_loc, f, true) ? 0 : 1;
+  a.ride_down = moe::few_gemm_tiles(E_loc, d, false) ? 0 : 1;
   a.topk_idx = topk_idx;
   a.topk_w = topk_w;
   a.counts = counts;

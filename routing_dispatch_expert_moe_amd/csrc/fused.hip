@@ -240,6 +240,11 @@ __global__ __launch_bounds__(256, 1) void moe_fused_kernel(FusedArgs a) {
     if (a.ffn_all_rows) {
       gemm_pipe_body<true, 128, 128, 8, ROWS_ALL>(xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G, lds,
                                              prefix, segs, a.sorted_pair, k);
+    } else if (a.ride_up) {
+      gemm_pipe_body<true, 256, 256, 4, ROWS_BIGR>(xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G,
+                                              lds, prefix, segs, a.sorted_pair, k);
+      gemm_pipe_body<true, 128, 128, 8, ROWS_TAILR>(xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G,
+                                               lds, prefix, segs, a.sorted_pair, k);
     } else {
       gemm_pipe_body<true, 256, 256, 4, ROWS_BIG>(xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G, lds,
                                              prefix, segs, a.sorted_pair, k);
@@ -252,6 +257,11 @@ __global__ __launch_bounds__(256, 1) void moe_fused_kernel(FusedArgs a) {
     if (a.ffn_all_rows) {
       gemm_pipe_body<false, 128, 128, 8, ROWS_ALL>(h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G, lds,
                                               prefix, segs);
+    } else if (a.ride_down) {
+      gemm_pipe_body<false, 256, 256, 4, ROWS_BIGR>(h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G,
+                                               lds, prefix, segs);
+      gemm_pipe_body<false, 128, 128, 8, ROWS_TAILR>(h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G,
+                                                lds, prefix, segs);
     } else {
       gemm_pipe_body<false, 256, 256, 4, ROWS_BIG>(h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G, lds,
                                               prefix, segs);

@@ -125,6 +125,8 @@ struct FusedArgs {
   const void* w2;
   int T, E, k, gate, capacity, e_begin, e_end, d, f;
   int ffn_all_rows;  // bf16: 1 = every row in 128-row tiles (few rows per expert)
+  int ride_up, ride_down;  // bf16: 1 = the pass keeps short last blocks of experts with a
+                           // full block in the 256-row tiles (ROWS_BIGR / ROWS_TAILR)
   int32_t* topk_idx;
   float* topk_w;
   int32_t* counts;
