@@ -101,6 +101,18 @@ int device_cu_count() {
   return cached[dev];
 }
 
+int set_dynamic_lds_once(const void* kern, size_t bytes, LdsAttr& rec) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return static_cast<int>(e);
+  if (dev < 0 || dev >= LdsAttr::kMaxDevices) return static_cast<int>(hipErrorInvalidDevice);
+  if (rec.done[dev]) return 0;
+  e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes));
+  if (e != hipSuccess) return static_cast<int>(e);
+  rec.done[dev] = 1;
+  return 0;
+}
+
 int check_error(void* ws, void* stream, int* device_flags) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipStreamSynchronize(s);

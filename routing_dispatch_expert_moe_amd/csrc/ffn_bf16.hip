@@ -323,14 +323,8 @@ static int launch_gemm(const void* A, const int32_t* offsets, int E_loc, int64_t
   constexpr int BNW = SWIGLU ? 2 * BN : BN;
   const size_t lds = static_cast<size_t>(2) * (BM + BNW) * BK * sizeof(uint16_t);
   auto kern = gemm_bf16_kernel<BM, BN, BK, WM, WN, SWIGLU, CLASS, FP8W>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       static_cast<int>(lds));
-    if (e != hipSuccess) return static_cast<int>(e);
-    attr_set = true;
-  }
+  static LdsAttr attr;
+  if (int rc = set_dynamic_lds_once(reinterpret_cast<const void*>(kern), lds, attr)) return rc;
   const int64_t NT = (N + BN - 1) / BN;
   int64_t tiles_ub = (max_rows / BM + E_loc) * NT;
   if (is_tail_class(CLASS)) tiles_ub = static_cast<int64_t>(E_loc) * ((kTailMax + BM - 1) / BM) * NT;

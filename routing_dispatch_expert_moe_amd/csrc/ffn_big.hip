@@ -34,14 +34,8 @@ int launch_pipe(const void* A, const int32_t* offsets, int E_loc, int64_t max_ro
   static_assert(pipe_lds_bytes(BM, BNW, STAGES) + 2 * (MOE_MAX_E + 1) * 4 <= 160 * 1024,
                 "LDS budget");
   auto kern = gemm_bf16_pipe<SWIGLU, BM, BNW, STAGES, CLASS, SAVE>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       static_cast<int>(lds));
-    if (e != hipSuccess) return static_cast<int>(e);
-    attr_set = true;
-  }
+  static LdsAttr attr;
+  if (int rc = set_dynamic_lds_once(reinterpret_cast<const void*>(kern), lds, attr)) return rc;
   const int BN = SWIGLU ? BNW / 2 : BNW;
   const int64_t NT = (N + BN - 1) / BN;
   int64_t tiles_ub = (max_rows / BM + E_loc) * NT;

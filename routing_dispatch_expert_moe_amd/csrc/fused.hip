@@ -313,14 +313,10 @@ int launch_fused(const FusedArgs& a, bool bf16, int64_t max_rows, void* stream) 
   const size_t lds = fused_lds_bytes(a.E, bf16);
   const void* kern = bf16 ? reinterpret_cast<const void*>(moe_fused_kernel<true>)
                           : reinterpret_cast<const void*>(moe_fused_kernel<false>);
-  static bool attr_set[2] = {false, false};
-  if (!attr_set[bf16]) {
-    // the largest dynamic LDS any E can ask for
-    hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       static_cast<int>(fused_lds_bytes(MOE_MAX_E, bf16)));
-    if (e != hipSuccess) return static_cast<int>(e);
-    attr_set[bf16] = true;
-  }
+  // the largest dynamic LDS any E can ask for
+  static LdsAttr attr[2];
+  if (int rc = set_dynamic_lds_once(kern, fused_lds_bytes(MOE_MAX_E, bf16), attr[bf16 ? 1 : 0]))
+    return rc;
   int occ = 0;
   hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, 256, lds);
   if (e != hipSuccess) return static_cast<int>(e);

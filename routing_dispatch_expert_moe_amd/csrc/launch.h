@@ -158,4 +158,15 @@ int launch_fused(const FusedArgs& a, bool bf16, int64_t max_rows, void* stream);
 
 int device_cu_count();
 
+// Per-kernel record of the devices on which the kernel's dynamic-LDS limit has
+// been raised (hipFuncAttributeMaxDynamicSharedMemorySize); zero-initialised
+// as a static object.
+struct LdsAttr {
+  static constexpr int kMaxDevices = 64;
+  volatile int done[kMaxDevices];
+};
+// raises kern's dynamic-LDS limit to `bytes` on the current device the first
+// time it is asked for there (racing first calls both set it: harmless)
+int set_dynamic_lds_once(const void* kern, size_t bytes, LdsAttr& rec);
+
 }  // namespace moe

@@ -437,14 +437,10 @@ int run_bf16(const uint16_t* P, int M, const uint16_t* Q, int N, const int32_t* 
   hipLaunchKernelGGL(transpose_seg_kernel, tp, dim3(256), 0, s, P, M, offsets, kseg, E_loc, PT);
   const dim3 tq(static_cast<unsigned>(ldk / 64), static_cast<unsigned>((N + 63) / 64));
   hipLaunchKernelGGL(transpose_seg_kernel, tq, dim3(256), 0, s, Q, N, offsets, kseg, E_loc, QT);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(wgrad_bf16_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       static_cast<int>(wgrad_lds_bytes()));
-    if (e != hipSuccess) return static_cast<int>(e);
-    attr_set = true;
-  }
+  static LdsAttr attr;
+  if (int rc = set_dynamic_lds_once(reinterpret_cast<const void*>(wgrad_bf16_kernel),
+                                    wgrad_lds_bytes(), attr))
+    return rc;
   const int tiles_m = (M + wgt::BM - 1) / wgt::BM, tiles_n = (N + wgt::BN - 1) / wgt::BN;
   hipLaunchKernelGGL(wgrad_bf16_kernel, dim3(static_cast<unsigned>(device_cu_count())), dim3(512),
                      wgrad_lds_bytes(), s, PT, QT, kseg, E_loc, M, N, tiles_m, tiles_n, C);
