@@ -44,16 +44,50 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(const int* __restri
                                                              int32_t* __restrict__ n_kept) {
   __shared__ int kept_s[MOE_MAX_E];
   __shared__ int scan_s[1024];
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    int run = 0;
-    for (int b = 0; b < nb; ++b) {
-      block_base[(size_t)b * E + e] = run;
-      run += block_counts[(size_t)b * E + e];
+  constexpr int U = 4;  // block counts in flight per thread
+  // P threads per expert each take a contiguous range of blocks: a first pass
+  // sums each range (parts in scan_s), a second writes the running bases from
+  // the sum of the ranges before it (integer sums: the same values in any order)
+  const int P = E <= 512 ? min(16, static_cast<int>(blockDim.x) / E) : 1;
+  const int e_t = threadIdx.x % E, p_t = threadIdx.x / E;
+  const int per_b = (nb + P - 1) / P;
+  const int b0 = p_t * per_b, b1 = min(nb, b0 + per_b);
+  if (P > 1) {
+    if (p_t < P) {
+      int sum = 0;
+      for (int b = b0; b < b1; b += U) {
+        int c[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) c[u] = b + u < b1 ? block_counts[(size_t)(b + u) * E + e_t] : 0;
+#pragma unroll
+        for (int u = 0; u < U; ++u) sum += c[u];
+      }
+      scan_s[p_t * E + e_t] = sum;
     }
-    counts[e] = run;
-    kept_s[e] = capacity < 0 ? run : min(run, capacity);
+    __syncthreads();
   }
-  __syncthreads();
+  for (int e = P > 1 ? e_t : threadIdx.x; e < E && p_t < P; e += P > 1 ? E : blockDim.x) {
+    const int lo = P > 1 ? b0 : 0, hi = P > 1 ? b1 : nb;
+    int run = 0;
+    for (int q = 0; q < p_t && P > 1; ++q) run += scan_s[q * E + e];
+    for (int b = lo; b < hi; b += U) {
+      int c[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) c[u] = b + u < hi ? block_counts[(size_t)(b + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (b + u < hi) {
+          block_base[(size_t)(b + u) * E + e] = run;
+          run += c[u];
+        }
+      }
+    }
+    if (P == 1 || p_t == P - 1) {  // the last part ends with the expert's total
+      counts[e] = run;
+      kept_s[e] = capacity < 0 ? run : min(run, capacity);
+    }
+  }
+  __syncthreads();  // kept_s complete; scan_s free again
   // exclusive scan of kept_s[e_begin, e_end): each thread owns a contiguous run
   const int E_loc = e_end - e_begin;
   const int per = (E_loc + blockDim.x - 1) / blockDim.x;
