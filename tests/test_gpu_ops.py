@@ -114,7 +114,10 @@ def test_router_logits():
 @pytest.mark.parametrize("T,E,k,cap,e0,e1", [
     (1, 1, 1, -1, 0, 1), (64, 8, 2, -1, 0, 8), (300, 16, 4, 40, 0, 16), (700, 64, 8, 60, 16, 48),
     (1000, 128, 2, 0, 0, 32), (513, 256, 8, -1, 0, 256), (257, 1024, 8, 3, 100, 900),
-    (200, 8, 2, 1000, 2, 3), (600, 4, 4, 150, 0, 4)])
+    (200, 8, 2, 1000, 2, 3), (600, 4, 4, 150, 0, 4),
+    # the scan's split of each expert's blocks over several threads: 79 blocks
+    # over 16 parts (ragged last part); more than 512 experts: one thread each
+    (20000, 64, 2, 700, 0, 64), (3000, 600, 4, -1, 100, 500)])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_dispatch(T, E, k, cap, e0, e1, dtype):
     log(f"dispatch T={T} E={E} k={k} cap={cap} [{e0},{e1}) {dtype}")
