@@ -349,6 +349,11 @@ static int launch_gemm(const void* A, const int32_t* offsets, int E_loc, int64_t
 #endif
 constexpr bool kDecodeSmallTiles = MOE_DECODE_SMALL_TILES != 0;
 constexpr int64_t kStreamRows = 48;
+// at most this many rows per expert (the host's bound) on a first-half pass
+// with few tiles (an expert-parallel rank's share of a layer): 128-row tiles
+// over 256 weight rows, whose six stages keep more weight bytes in flight per
+// CU than the 256-row tiles' four (the pass streams weights)
+constexpr int64_t kWideRows = 512;
 #ifndef MOE_RIDE
 #define MOE_RIDE 1
 #endif
@@ -380,6 +385,8 @@ int launch_ffn_up_bf16(const void* x_perm, const int32_t* offsets, int E_loc, in
       return launch_gemm<32, 128, 64, 1, 4, true, ROWS_ALL>(x_perm, offsets, E_loc, max_rows, w13, h, f, d, s, nullptr, wlist);
     return launch_gemm_pipe_bf16(PipeRows::kAllRows, true, x_perm, offsets, E_loc, max_rows, w13, h, f, d, wlist, stream);
   }
+  if (few_gemm_tiles(E_loc, f, true) && avg <= kWideRows)
+    return launch_gemm_pipe_bf16(PipeRows::kAllRowsWide, true, x_perm, offsets, E_loc, max_rows, w13, h, f, d, wlist, stream);
   if (remainders_with_big_tiles(E_loc, f, d, true))
     return launch_gemm_pipe_bf16(PipeRows::kBigAll, true, x_perm, offsets, E_loc, max_rows, w13, h, f, d, wlist, stream);
   const bool ride = kRide && !few_gemm_tiles(E_loc, f, true);
@@ -397,6 +404,8 @@ int launch_ffn_up_train_bf16(const void* x_perm, const int32_t* offsets, int E_l
   const int64_t avg = max_rows / E_loc;
   if (avg <= kStreamRows)
     return launch_gemm_pipe_bf16(PipeRows::kAllRows, true, x_perm, offsets, E_loc, max_rows, w13, h, f, d, nullptr, stream, ab);
+  if (few_gemm_tiles(E_loc, f, true) && avg <= kWideRows)
+    return launch_gemm_pipe_bf16(PipeRows::kAllRowsWide, true, x_perm, offsets, E_loc, max_rows, w13, h, f, d, nullptr, stream, ab);
   if (remainders_with_big_tiles(E_loc, f, d, true))
     return launch_gemm_pipe_bf16(PipeRows::kBigAll, true, x_perm, offsets, E_loc, max_rows, w13, h, f, d, nullptr, stream, ab);
   const bool ride = kRide && !few_gemm_tiles(E_loc, f, true);

@@ -69,6 +69,8 @@ int launch_kind(PipeRows rows, const void* A, const int32_t* offsets, int E_loc,
     case PipeRows::kTailRide:
       return launch_pipe<SWIGLU, 128, 256, 6, ROWS_TAILR, SAVE>(A, offsets, E_loc, max_rows, W, C, N,
                                                                  K, wlist, AB, s);
+    case PipeRows::kAllRowsWide:
+      return launch_pipe<SWIGLU, 128, 256, 6, ROWS_ALL, SAVE>(A, offsets, E_loc, max_rows, W, C, N, K, wlist, AB, s);
     case PipeRows::kBigAll:
       return launch_pipe<SWIGLU, 256, 256, 4, ROWS_ALL, SAVE>(A, offsets, E_loc, max_rows, W, C, N, K, wlist, AB, s);
     case PipeRows::kTailTiles: {

@@ -49,8 +49,9 @@ int launch_ffn_down_bf16(const void* h, const int32_t* offsets, int E_loc, int64
 // smaller tiles over the short remainders (kTailTiles), or smaller tiles over
 // every row (kAllRows); kBigRide / kTailRide: 256-row tiles over every row of
 // the experts with at least one full block, smaller tiles over the experts
-// with fewer than 128 rows (passes with many tiles).
-enum class PipeRows { kBigTiles, kBigAll, kTailTiles, kAllRows, kBigRide, kTailRide };
+// with fewer than 128 rows (passes with many tiles); kAllRowsWide: 128-row
+// tiles of 256 weight rows (six stages) over every row.
+enum class PipeRows { kBigTiles, kBigAll, kTailTiles, kAllRows, kBigRide, kTailRide, kAllRowsWide };
 // true when one GEMM pass over E_loc experts with N output columns gives few
 // tiles (fewer than 4 per CU with 256-row weight tiles): then remainders ride
 // along with the 256-row tiles instead of a second kernel re-streaming weights
