@@ -127,6 +127,24 @@ __device__ __forceinline__ void block_exclusive_scan(const int* v, int n, int* o
 
 }  // namespace
 
+// sum over blocks [0, nb) of expert e's per-block pair counts, eight loads in
+// flight (integer sums: the value does not depend on the order)
+__device__ __forceinline__ int sum_block_counts(const int* __restrict__ block_counts, int E, int e,
+                                                int nb) {
+  constexpr int U = 8;
+  int part[U] = {};
+  int b = 0;
+  for (; b + U <= nb; b += U) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) part[u] += block_counts[(size_t)(b + u) * E + e];
+  }
+  for (; b < nb; ++b) part[0] += block_counts[(size_t)b * E + e];
+  int c = 0;
+#pragma unroll
+  for (int u = 0; u < U; ++u) c += part[u];
+  return c;
+}
+
 template <bool BF16>
 __global__ __launch_bounds__(256, 1) void moe_fused_kernel(FusedArgs a) {
   extern __shared__ uint4 lds[];
@@ -200,8 +218,7 @@ __global__ __launch_bounds__(256, 1) void moe_fused_kernel(FusedArgs a) {
   // workgroup rebuilds the block's bitmaps and places only its slice of the
   // block's pairs, so the work spreads over the grid.
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    int c = 0;
-    for (int b = 0; b < nb; ++b) c += a.block_counts[(size_t)b * E + e];
+    const int c = sum_block_counts(a.block_counts, E, e, nb);
     cnt_s[e] = c;
     if (bid == 0) a.counts[e] = c;
   }
@@ -220,11 +237,8 @@ __global__ __launch_bounds__(256, 1) void moe_fused_kernel(FusedArgs a) {
   const int per_slice = (kTB + slices - 1) / slices;
   for (int u = bid; u < nb * slices; u += G) {
     const int vb = u / slices, sl = u - vb * slices;
-    for (int e = threadIdx.x; e < E; e += blockDim.x) {
-      int c = 0;
-      for (int b = 0; b < vb; ++b) c += a.block_counts[(size_t)b * E + e];
-      base_s[e] = c;
-    }
+    for (int e = threadIdx.x; e < E; e += blockDim.x)
+      base_s[e] = sum_block_counts(a.block_counts, E, e, vb);
     __syncthreads();
     const int t0 = vb * kTB + sl * per_slice;
     dispatch_place_block(vb, bits, a.topk_idx, T, E, k, a.capacity, a.e_begin, a.e_end, base_s,
