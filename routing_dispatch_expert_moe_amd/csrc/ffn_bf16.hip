@@ -349,11 +349,10 @@ static int launch_gemm(const void* A, const int32_t* offsets, int E_loc, int64_t
 #endif
 constexpr bool kDecodeSmallTiles = MOE_DECODE_SMALL_TILES != 0;
 constexpr int64_t kStreamRows = 48;
-// at most this many rows per expert (the host's bound) on a first-half pass
-// with few tiles (an expert-parallel rank's share of a layer): 128-row tiles
-// over 256 weight rows, whose six stages keep more weight bytes in flight per
-// CU than the 256-row tiles' four (the pass streams weights)
-constexpr int64_t kWideRows = 512;
+// kWideRows (launch.h): a first-half pass with few tiles and few rows per
+// expert (an expert-parallel rank's share of a layer) streams weights; the
+// 128-row tiles over 256 weight rows keep five stages of weight bytes in
+// flight per CU where the 256-row tiles keep three
 #ifndef MOE_RIDE
 #define MOE_RIDE 1
 #endif

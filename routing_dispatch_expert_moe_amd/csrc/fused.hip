@@ -254,7 +254,13 @@ __global__ __launch_bounds__(256, 1) void moe_fused_kernel(FusedArgs a) {
     if (a.ffn_all_rows) {
       gemm_pipe_body<true, 128, 128, 8, ROWS_ALL>(xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G, lds,
                                              prefix, segs, a.sorted_pair, k);
-    } else if (a.ride_up) {
+    } else if (a.rows_up == kFusedWide) {
+      gemm_pipe_body<true, 128, 256, 6, ROWS_ALL>(xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G, lds,
+                                             prefix, segs, a.sorted_pair, k);
+    } else if (a.rows_up == kFusedAllBig) {
+      gemm_pipe_body<true, 256, 256, 4, ROWS_ALL>(xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G, lds,
+                                             prefix, segs, a.sorted_pair, k);
+    } else if (a.rows_up == kFusedRide) {
       gemm_pipe_body<true, 256, 256, 4, ROWS_BIGR>(xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G,
                                               lds, prefix, segs, a.sorted_pair, k);
       gemm_pipe_body<true, 128, 128, 8, ROWS_TAILR>(xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G,
@@ -271,7 +277,10 @@ __global__ __launch_bounds__(256, 1) void moe_fused_kernel(FusedArgs a) {
     if (a.ffn_all_rows) {
       gemm_pipe_body<false, 128, 128, 8, ROWS_ALL>(h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G, lds,
                                               prefix, segs);
-    } else if (a.ride_down) {
+    } else if (a.rows_down == kFusedAllBig) {
+      gemm_pipe_body<false, 256, 256, 4, ROWS_ALL>(h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G, lds,
+                                              prefix, segs);
+    } else if (a.rows_down == kFusedRide) {
       gemm_pipe_body<false, 256, 256, 4, ROWS_BIGR>(h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G,
                                                lds, prefix, segs);
       gemm_pipe_body<false, 128, 128, 8, ROWS_TAILR>(h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G,
@@ -315,10 +324,12 @@ size_t fused_lds_bytes(int E, bool bf16) {
   size_t plan = static_cast<size_t>(E) * kWords * sizeof(unsigned long long) +
                 2 * static_cast<size_t>(E) * sizeof(int);
   if (plan < resolver_lds_bytes()) plan = resolver_lds_bytes();
-  const size_t gemm = bf16 ? (pipe_lds_bytes(128, 128, 8) > pipe_lds_bytes(256, 256, 4)
-                                  ? pipe_lds_bytes(128, 128, 8)
-                                  : pipe_lds_bytes(256, 256, 4))
-                           : f32_lds_floats(true) * sizeof(float);
+  size_t gemm = f32_lds_floats(true) * sizeof(float);
+  if (bf16) {
+    gemm = pipe_lds_bytes(128, 128, 8);
+    if (gemm < pipe_lds_bytes(256, 256, 4)) gemm = pipe_lds_bytes(256, 256, 4);
+    if (gemm < pipe_lds_bytes(128, 256, 6)) gemm = pipe_lds_bytes(128, 256, 6);
+  }
   return plan > gemm ? plan : gemm;
 }
 

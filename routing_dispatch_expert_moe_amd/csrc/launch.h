@@ -51,6 +51,14 @@ int launch_ffn_down_bf16(const void* h, const int32_t* offsets, int E_loc, int64
 // the experts with at least one full block, smaller tiles over the experts
 // with fewer than 128 rows (passes with many tiles); kAllRowsWide: 128-row
 // tiles of 256 weight rows (six stages) over every row.
+// How the fused layer's bf16 GEMM phases split each expert's rows, chosen by
+// the same rules as the separate FFN calls: 256-row tiles then 128-row tiles
+// for the remainders; the ride-along split (ROWS_BIGR / ROWS_TAILR); every
+// row in 256-row tiles; every row in 128-row tiles of 256 weight rows.
+enum FusedRows { kFusedBigTail = 0, kFusedRide = 1, kFusedAllBig = 2, kFusedWide = 3 };
+// first-half passes with few tiles and at most this many rows per expert (the
+// host's bound) run 128-row tiles of 256 weight rows over every row
+constexpr int64_t kWideRows = 512;
 enum class PipeRows { kBigTiles, kBigAll, kTailTiles, kAllRows, kBigRide, kTailRide, kAllRowsWide };
 // true when one GEMM pass over E_loc experts with N output columns gives few
 // tiles (fewer than 4 per CU with 256-row weight tiles): then remainders ride
@@ -126,8 +134,7 @@ struct FusedArgs {
   const void* w2;
   int T, E, k, gate, capacity, e_begin, e_end, d, f;
   int ffn_all_rows;  // bf16: 1 = every row in 128-row tiles (few rows per expert)
-  int ride_up, ride_down;  // bf16: 1 = the pass keeps short last blocks of experts with a
-                           // full block in the 256-row tiles (ROWS_BIGR / ROWS_TAILR)
+  int rows_up, rows_down;  // bf16 GEMM phases (unless ffn_all_rows): a FusedRows value
   int32_t* topk_idx;
   float* topk_w;
   int32_t* counts;
