@@ -201,11 +201,24 @@ __global__ __launch_bounds__(256, 1) void moe_fused_kernel(FusedArgs a) {
       }
     }
   } else {
-    for (int t = bid * 4 + wave; t < T; t += G * 4) {
-      if (E <= 64) route_token<1>(a.logits, t, E, k, a.gate, a.topk_idx, a.topk_w);
-      else if (E <= 256) route_token<4>(a.logits, t, E, k, a.gate, a.topk_idx, a.topk_w);
-      else route_token<16>(a.logits, t, E, k, a.gate, a.topk_idx, a.topk_w);
-    }
+    // a wave routes several tokens in turn: the next token's logits are loaded
+    // while the current one is ranked
+    auto route_all = [&](auto epl) {
+      constexpr int EPL = decltype(epl)::value;
+      int t = bid * 4 + wave;
+      float cur[EPL];
+      if (t < T) load_logits<EPL>(a.logits, t, E, cur);
+      for (; t < T; t += G * 4) {
+        float nxt[EPL] = {};
+        if (t + G * 4 < T) load_logits<EPL>(a.logits, t + G * 4, E, nxt);
+        route_token_vals<EPL>(cur, t, E, k, a.gate, a.topk_idx, a.topk_w);
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) cur[i] = nxt[i];
+      }
+    };
+    if (E <= 64) route_all(std::integral_constant<int, 1>{});
+    else if (E <= 256) route_all(std::integral_constant<int, 4>{});
+    else route_all(std::integral_constant<int, 16>{});
   }
   grid_barrier(a, G);
 

@@ -25,19 +25,32 @@ __device__ __forceinline__ float from_ordered(uint32_t o) {
   return __uint_as_float(u);
 }
 
-// The kc best experts of token t (best first) and their logits, by one whole
-// wave (E <= 64 * EPL, kc <= KMAX); entries past kc are 0.
-template <int EPL, int KMAX>
-__device__ __forceinline__ void select_top(const float* __restrict__ logits, int t, int E, int kc,
-                                           int (&sel_e)[KMAX], float (&sel_v)[KMAX]) {
+// This lane's logits of token t: v[i] is expert lane + 64 i (0 past E).
+template <int EPL>
+__device__ __forceinline__ void load_logits(const float* __restrict__ logits, int t, int E,
+                                            float (&v)[EPL]) {
   const int lane = lane_id();
   const float* row = logits + (size_t)t * E;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane + kWave * i;
+    v[i] = e < E ? row[e] : 0.f;
+  }
+}
+
+// The kc best experts (best first) and their logits among the wave's values v
+// (as load_logits leaves them), by one whole wave (E <= 64 * EPL, kc <= KMAX);
+// entries past kc are 0.
+template <int EPL, int KMAX>
+__device__ __forceinline__ void select_top_vals(const float (&v)[EPL], int E, int kc,
+                                                int (&sel_e)[KMAX], float (&sel_v)[KMAX]) {
+  const int lane = lane_id();
   uint64_t key[EPL];
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
     const int e = lane + kWave * i;
     key[i] = 0;
-    if (e < E) key[i] = (static_cast<uint64_t>(ordered_bits(row[e])) << 32) | static_cast<uint32_t>(~e);
+    if (e < E) key[i] = (static_cast<uint64_t>(ordered_bits(v[i])) << 32) | static_cast<uint32_t>(~e);
   }
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) {
@@ -58,15 +71,26 @@ __device__ __forceinline__ void select_top(const float* __restrict__ logits, int
   }
 }
 
-// Top-k and gates of token t, computed by one whole wave (E <= 64 * EPL).
+// The kc best experts of token t (best first) and their logits, by one whole
+// wave (E <= 64 * EPL, kc <= KMAX); entries past kc are 0.
+template <int EPL, int KMAX>
+__device__ __forceinline__ void select_top(const float* __restrict__ logits, int t, int E, int kc,
+                                           int (&sel_e)[KMAX], float (&sel_v)[KMAX]) {
+  float v[EPL];
+  load_logits<EPL>(logits, t, E, v);
+  select_top_vals<EPL, KMAX>(v, E, kc, sel_e, sel_v);
+}
+
+// Top-k and gates of token t from the wave's values v of its logits (as
+// load_logits leaves them), computed by one whole wave (E <= 64 * EPL).
 template <int EPL>
-__device__ __forceinline__ void route_token(const float* __restrict__ logits, int t, int E, int k,
-                                            int gate, int32_t* __restrict__ topk_idx,
-                                            float* __restrict__ topk_w) {
+__device__ __forceinline__ void route_token_vals(const float (&v)[EPL], int t, int E, int k,
+                                                 int gate, int32_t* __restrict__ topk_idx,
+                                                 float* __restrict__ topk_w) {
   const int lane = lane_id();
   int sel_e[MOE_MAX_K];
   float sel_v[MOE_MAX_K];
-  select_top<EPL, MOE_MAX_K>(logits, t, E, k, sel_e, sel_v);
+  select_top_vals<EPL, MOE_MAX_K>(v, E, k, sel_e, sel_v);
   float g[MOE_MAX_K];
   float sum = 0.f;
   if (gate == 0) {
@@ -90,6 +114,16 @@ __device__ __forceinline__ void route_token(const float* __restrict__ logits, in
       topk_w[(size_t)t * k + j] = g[j] / sum;
     }
   }
+}
+
+// Top-k and gates of token t, computed by one whole wave (E <= 64 * EPL).
+template <int EPL>
+__device__ __forceinline__ void route_token(const float* __restrict__ logits, int t, int E, int k,
+                                            int gate, int32_t* __restrict__ topk_idx,
+                                            float* __restrict__ topk_w) {
+  float v[EPL];
+  load_logits<EPL>(logits, t, E, v);
+  route_token_vals<EPL>(v, t, E, k, gate, topk_idx, topk_w);
 }
 
 }  // namespace moe
