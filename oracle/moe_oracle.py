@@ -269,11 +269,16 @@ def silu(a: np.ndarray) -> np.ndarray:
     return a / (1.0 + np.exp(-a))
 
 
-def swiglu_ffn(x64: np.ndarray, w1: np.ndarray, w3: np.ndarray, w2: np.ndarray) -> np.ndarray:
-    """(silu(x W1) * (x W3)) W2 for rows x [n, d]; weights float64, x.W orientation."""
+def swiglu_hidden(x64: np.ndarray, w1: np.ndarray, w3: np.ndarray) -> np.ndarray:
+    """h = silu(x W1) * (x W3) for rows x [n, d] (the first FFN half); float64."""
     a = x64 @ w1
     g = x64 @ w3
-    return (silu(a) * g) @ w2
+    return silu(a) * g
+
+
+def swiglu_ffn(x64: np.ndarray, w1: np.ndarray, w3: np.ndarray, w2: np.ndarray) -> np.ndarray:
+    """(silu(x W1) * (x W3)) W2 for rows x [n, d]; weights float64, x.W orientation."""
+    return swiglu_hidden(x64, w1, w3) @ w2
 
 
 def expert_ffn(x_perm64: np.ndarray, offsets: np.ndarray,
@@ -390,9 +395,14 @@ def token_outputs(tokens: Sequence[int], x64_rows: np.ndarray, topk_idx: np.ndar
 
 
 def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
-    """max|got - ref| / max|ref| (0 when both are empty or ref is all zero and got matches)."""
+    """The parity measure max|got - ref| / max|ref|, element by element over
+    arrays of one shape (a shape mismatch raises instead of broadcasting).
+    Empty arrays give 0; an all-zero reference gives the absolute error
+    max|got|; a NaN anywhere gives NaN, which fails every tolerance."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
+    if got.shape != ref.shape:
+        raise ValueError(f"rel_err: shapes {got.shape} and {ref.shape} differ")
     if ref.size == 0:
         return 0.0
     den = float(np.max(np.abs(ref)))
