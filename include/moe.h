@@ -192,6 +192,34 @@ moe_status moe_ffn_down(const void* h, const int32_t* offsets, int E_loc, int64_
                         int d, int f, moe_dtype dtype, const void* w2_packed, void* y_perm,
                         void* ws, size_t ws_bytes, void* stream);
 
+/* Kernels that one FFN half launches (DWDP page, key optimisations: one
+ * grouped GEMM over all local experts, whose per-expert loads differ).  The
+ * choice depends only on the sizes (row counts stay on the device): */
+typedef enum {
+  MOE_FFN_PLAN_NONE = 0,      /* max_rows == 0: nothing is launched                     */
+  MOE_FFN_PLAN_F32 = 1,       /* fp32 grouped GEMM                                      */
+  MOE_FFN_PLAN_STREAM = 2,    /* 32-row tiles over every row: few rows per expert       */
+                              /* (at most 48 on average by max_rows / E_loc)            */
+  MOE_FFN_PLAN_STREAM_WIDE_OPERANDS = 3, /* the same kernel because an operand --      */
+                              /* max_rows x max(d, f) or one expert's weights, in bf16 -- */
+                              /* reaches 4 GiB (the other kernels use 32-bit offsets)     */
+  MOE_FFN_PLAN_WIDE = 4,      /* first half only: 128-row tiles of 256 weight rows over */
+                              /* every row (few tiles, at most 512 rows per expert)     */
+  MOE_FFN_PLAN_BIG_ALL = 5,   /* 256-row tiles over every row (few, short tiles)        */
+  MOE_FFN_PLAN_BIG_TAIL = 6,  /* 256-row tiles over each expert's full blocks, 128-row  */
+                              /* tiles over the remainders below 128 rows (few tiles,   */
+                              /* K > 4096)                                              */
+  MOE_FFN_PLAN_BIG_RIDE = 7   /* many tiles: 256-row tiles over every row of the experts */
+                              /* with a full block, 128-row tiles over the experts with */
+                              /* fewer than 128 rows                                    */
+} moe_ffn_plan_t;
+
+/* Host-only query (no GPU needed): the moe_ffn_plan_t value that moe_ffn_up
+ * (half = 0) or moe_ffn_down / the backward dgrad GEMMs on the same sizes
+ * (half = 1) use for max_rows rows, E_loc experts, d, f and dtype on a device
+ * with cu_count compute units.  -1 if an argument is invalid. */
+int moe_ffn_plan(int half, int64_t max_rows, int E_loc, int d, int f, int dtype, int cu_count);
+
 /* moe_expert_ffn over a table of per-expert weight buffers instead of one
  * packed tensor (DWDP page, key optimisations and TensorList: the grouped
  * GEMM takes a list of weight buffers -- locally resident ones and ones

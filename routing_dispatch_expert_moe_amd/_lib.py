@@ -23,6 +23,14 @@ MOE_F32 = 0
 MOE_BF16 = 1
 MOE_GATE_SOFTMAX_TOPK_RENORM = 0
 MOE_GATE_SIGMOID_TOPK_NORM = 1
+MOE_FFN_PLAN_NONE = 0
+MOE_FFN_PLAN_F32 = 1
+MOE_FFN_PLAN_STREAM = 2
+MOE_FFN_PLAN_STREAM_WIDE_OPERANDS = 3
+MOE_FFN_PLAN_WIDE = 4
+MOE_FFN_PLAN_BIG_ALL = 5
+MOE_FFN_PLAN_BIG_TAIL = 6
+MOE_FFN_PLAN_BIG_RIDE = 7
 MOE_MAX_K = 8
 MOE_MAX_E = 1024
 
@@ -44,6 +52,7 @@ SIGNATURES = {
     "moe_expert_ffn": (_i, [_vp, _i32p, _i, _i64, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_ffn_up": (_i, [_vp, _i32p, _i, _i64, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]),
     "moe_ffn_down": (_i, [_vp, _i32p, _i, _i64, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]),
+    "moe_ffn_plan": (_i, [_i, _i64, _i, _i, _i, _i, _i]),
     "moe_combine": (_i, [_vp, _i32p, _fp, _i, _i, _i, _i, _vp, _vp]),
     "moe_check_error": (_i, [_vp, _vp]),
     "moe_expert_ffn_list": (_i, [_vp, _i32p, _i, _i64, _i, _i, _i, _vp, _vp, _vp, _vp, _vp]),

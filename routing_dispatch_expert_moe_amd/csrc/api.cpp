@@ -588,18 +588,19 @@ static moe_status forward_fused_impl(const float* logits, const void* x, int T, 
   a.ffn_all_rows = max_rows / E_loc <= 48 ? 1 : 0;
   // the row splits of the separate FFN calls
   const int64_t avg_rows = max_rows / E_loc;
-  if (!moe::few_gemm_tiles(E_loc, f, true))
+  const int cu = moe::device_cu_count();
+  if (!moe::few_gemm_tiles(E_loc, f, true, cu))
     a.rows_up = moe::kFusedRide;
   else if (avg_rows <= moe::kWideRows)
     a.rows_up = moe::kFusedWide;
   else
-    a.rows_up = moe::remainders_with_big_tiles(E_loc, f, d, true) ? moe::kFusedAllBig
-                                                                  : moe::kFusedBigTail;
-  if (!moe::few_gemm_tiles(E_loc, d, false))
+    a.rows_up = moe::remainders_with_big_tiles(E_loc, f, d, true, cu) ? moe::kFusedAllBig
+                                                                      : moe::kFusedBigTail;
+  if (!moe::few_gemm_tiles(E_loc, d, false, cu))
     a.rows_down = moe::kFusedRide;
   else
-    a.rows_down = moe::remainders_with_big_tiles(E_loc, d, f, false) ? moe::kFusedAllBig
-                                                                     : moe::kFusedBigTail;
+    a.rows_down = moe::remainders_with_big_tiles(E_loc, d, f, false, cu) ? moe::kFusedAllBig
+                                                                         : moe::kFusedBigTail;
   a.topk_idx = topk_idx;
   a.topk_w = topk_w;
   a.counts = counts;

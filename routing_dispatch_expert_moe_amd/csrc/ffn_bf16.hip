@@ -344,54 +344,45 @@ static int launch_gemm(const void* A, const int32_t* offsets, int E_loc, int64_t
 }
 
 
-#ifndef MOE_DECODE_SMALL_TILES
-#define MOE_DECODE_SMALL_TILES 1
-#endif
-constexpr bool kDecodeSmallTiles = MOE_DECODE_SMALL_TILES != 0;
-constexpr int64_t kStreamRows = 48;
-// kWideRows (launch.h): a first-half pass with few tiles and few rows per
-// expert (an expert-parallel rank's share of a layer) streams weights; the
-// 128-row tiles over 256 weight rows keep five stages of weight bytes in
-// flight per CU where the 256-row tiles keep three
-#ifndef MOE_RIDE
-#define MOE_RIDE 1
-#endif
-constexpr bool kRide = MOE_RIDE != 0;
-
-// Rows per expert on average decide the kernels: with few rows per expert the
-// FFN is weight streaming and one small-tile kernel takes every row.
-// Otherwise the 256-row-tile kernel takes each expert's rows; when the pass
-// has few, short tiles (few experts, K <= 4096) it also takes each expert's
-// last block, even when less than half full (that tile shares its weights
-// with the expert's other tiles through L2), else a small-tile kernel takes
-// the short remainders (ROWS_BIG / ROWS_TAIL); with many tiles, an expert
-// that has a full block keeps its short last block in the large tiles too
-// (ROWS_BIGR / ROWS_TAILR), so no expert's weights are streamed by both
-// kernels.  Row counts stay on the device.
+// The kernels of each pass come from ffn_plan_bf16 (ffn_plan.cpp), which
+// decides from the sizes on the host: with few rows per expert (or an
+// operand of 4 GiB or more) one register-staged 32-row-tile kernel streams
+// the weights over every row; a first-half pass with few tiles and few rows
+// per expert runs 128-row tiles of 256 weight rows over every row (five
+// stages of weight bytes in flight per CU where the 256-row tiles keep
+// three); a pass with few, short tiles runs every row in 256-row tiles (an
+// expert's last block shares its weight tiles with the expert's other tiles
+// through L2); long-K passes with few tiles run 256-row tiles over the full
+// blocks and 128-row tiles over the short remainders; passes with many tiles
+// keep an expert's short last block in the 256-row tiles whenever the expert
+// has a full block, and give the experts below 128 rows to the 128-row tiles,
+// so no expert's weights are streamed by both kernels.  Row counts stay on
+// the device.
 int launch_ffn_up_bf16(const void* x_perm, const int32_t* offsets, int E_loc, int64_t max_rows,
                        int d, int f, const void* w13, void* h, const void* const* wlist,
                        void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (max_rows == 0) return 0;
-  const int64_t avg = max_rows / E_loc;
-  // the large-tile kernel addresses operands with 32-bit byte offsets
-  const bool fits32 = static_cast<double>(max_rows) * d * 2 < 4294967296.0 &&
-                      static_cast<double>(2) * f * d * 2 < 4294967296.0;
-  if (!fits32)
-    return launch_gemm<32, 128, 64, 1, 4, true, ROWS_ALL>(x_perm, offsets, E_loc, max_rows, w13, h, f, d, s, nullptr, wlist);
-  if (avg <= kStreamRows) {
-    if (kDecodeSmallTiles)
+  auto pipe = [&](PipeRows r) {
+    return launch_gemm_pipe_bf16(r, true, x_perm, offsets, E_loc, max_rows, w13, h, f, d, wlist, stream);
+  };
+  switch (ffn_plan_bf16(true, max_rows, E_loc, d, f, device_cu_count())) {
+    case MOE_FFN_PLAN_STREAM:
+    case MOE_FFN_PLAN_STREAM_WIDE_OPERANDS:
       return launch_gemm<32, 128, 64, 1, 4, true, ROWS_ALL>(x_perm, offsets, E_loc, max_rows, w13, h, f, d, s, nullptr, wlist);
-    return launch_gemm_pipe_bf16(PipeRows::kAllRows, true, x_perm, offsets, E_loc, max_rows, w13, h, f, d, wlist, stream);
+    case MOE_FFN_PLAN_WIDE:
+      return pipe(PipeRows::kAllRowsWide);
+    case MOE_FFN_PLAN_BIG_ALL:
+      return pipe(PipeRows::kBigAll);
+    case MOE_FFN_PLAN_BIG_RIDE: {
+      int e = pipe(PipeRows::kBigRide);
+      return e != 0 ? e : pipe(PipeRows::kTailRide);
+    }
+    default: {
+      int e = pipe(PipeRows::kBigTiles);
+      return e != 0 ? e : pipe(PipeRows::kTailTiles);
+    }
   }
-  if (few_gemm_tiles(E_loc, f, true) && avg <= kWideRows)
-    return launch_gemm_pipe_bf16(PipeRows::kAllRowsWide, true, x_perm, offsets, E_loc, max_rows, w13, h, f, d, wlist, stream);
-  if (remainders_with_big_tiles(E_loc, f, d, true))
-    return launch_gemm_pipe_bf16(PipeRows::kBigAll, true, x_perm, offsets, E_loc, max_rows, w13, h, f, d, wlist, stream);
-  const bool ride = kRide && !few_gemm_tiles(E_loc, f, true);
-  int e = launch_gemm_pipe_bf16(ride ? PipeRows::kBigRide : PipeRows::kBigTiles, true, x_perm, offsets, E_loc, max_rows, w13, h, f, d, wlist, stream);
-  if (e != 0) return e;
-  return launch_gemm_pipe_bf16(ride ? PipeRows::kTailRide : PipeRows::kTailTiles, true, x_perm, offsets, E_loc, max_rows, w13, h, f, d, wlist, stream);
 }
 
 // Always the pipelined kernels (the only ones with the pre-activation store);
@@ -400,17 +391,26 @@ int launch_ffn_up_train_bf16(const void* x_perm, const int32_t* offsets, int E_l
                              int64_t max_rows, int d, int f, const void* w13, void* h, void* ab,
                              void* stream) {
   if (max_rows == 0) return 0;
-  const int64_t avg = max_rows / E_loc;
-  if (avg <= kStreamRows)
-    return launch_gemm_pipe_bf16(PipeRows::kAllRows, true, x_perm, offsets, E_loc, max_rows, w13, h, f, d, nullptr, stream, ab);
-  if (few_gemm_tiles(E_loc, f, true) && avg <= kWideRows)
-    return launch_gemm_pipe_bf16(PipeRows::kAllRowsWide, true, x_perm, offsets, E_loc, max_rows, w13, h, f, d, nullptr, stream, ab);
-  if (remainders_with_big_tiles(E_loc, f, d, true))
-    return launch_gemm_pipe_bf16(PipeRows::kBigAll, true, x_perm, offsets, E_loc, max_rows, w13, h, f, d, nullptr, stream, ab);
-  const bool ride = kRide && !few_gemm_tiles(E_loc, f, true);
-  int e = launch_gemm_pipe_bf16(ride ? PipeRows::kBigRide : PipeRows::kBigTiles, true, x_perm, offsets, E_loc, max_rows, w13, h, f, d, nullptr, stream, ab);
-  if (e != 0) return e;
-  return launch_gemm_pipe_bf16(ride ? PipeRows::kTailRide : PipeRows::kTailTiles, true, x_perm, offsets, E_loc, max_rows, w13, h, f, d, nullptr, stream, ab);
+  auto pipe = [&](PipeRows r) {
+    return launch_gemm_pipe_bf16(r, true, x_perm, offsets, E_loc, max_rows, w13, h, f, d, nullptr, stream, ab);
+  };
+  switch (ffn_plan_bf16(true, max_rows, E_loc, d, f, device_cu_count())) {
+    case MOE_FFN_PLAN_STREAM:
+    case MOE_FFN_PLAN_STREAM_WIDE_OPERANDS:
+      return pipe(PipeRows::kAllRows);
+    case MOE_FFN_PLAN_WIDE:
+      return pipe(PipeRows::kAllRowsWide);
+    case MOE_FFN_PLAN_BIG_ALL:
+      return pipe(PipeRows::kBigAll);
+    case MOE_FFN_PLAN_BIG_RIDE: {
+      int e = pipe(PipeRows::kBigRide);
+      return e != 0 ? e : pipe(PipeRows::kTailRide);
+    }
+    default: {
+      int e = pipe(PipeRows::kBigTiles);
+      return e != 0 ? e : pipe(PipeRows::kTailTiles);
+    }
+  }
 }
 
 int launch_ffn_down_bf16(const void* h, const int32_t* offsets, int E_loc, int64_t max_rows,
@@ -418,22 +418,24 @@ int launch_ffn_down_bf16(const void* h, const int32_t* offsets, int E_loc, int64
                          void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (max_rows == 0) return 0;
-  const int64_t avg = max_rows / E_loc;
-  const bool fits32 = static_cast<double>(max_rows) * f * 2 < 4294967296.0 &&
-                      static_cast<double>(d) * f * 2 < 4294967296.0;
-  if (!fits32)
-    return launch_gemm<32, 128, 64, 1, 4, false, ROWS_ALL>(h, offsets, E_loc, max_rows, w2, y, d, f, s, nullptr, wlist);
-  if (avg <= kStreamRows) {
-    if (kDecodeSmallTiles)
+  auto pipe = [&](PipeRows r) {
+    return launch_gemm_pipe_bf16(r, false, h, offsets, E_loc, max_rows, w2, y, d, f, wlist, stream);
+  };
+  switch (ffn_plan_bf16(false, max_rows, E_loc, d, f, device_cu_count())) {
+    case MOE_FFN_PLAN_STREAM:
+    case MOE_FFN_PLAN_STREAM_WIDE_OPERANDS:
       return launch_gemm<32, 128, 64, 1, 4, false, ROWS_ALL>(h, offsets, E_loc, max_rows, w2, y, d, f, s, nullptr, wlist);
-    return launch_gemm_pipe_bf16(PipeRows::kAllRows, false, h, offsets, E_loc, max_rows, w2, y, d, f, wlist, stream);
+    case MOE_FFN_PLAN_BIG_ALL:
+      return pipe(PipeRows::kBigAll);
+    case MOE_FFN_PLAN_BIG_RIDE: {
+      int e = pipe(PipeRows::kBigRide);
+      return e != 0 ? e : pipe(PipeRows::kTailRide);
+    }
+    default: {
+      int e = pipe(PipeRows::kBigTiles);
+      return e != 0 ? e : pipe(PipeRows::kTailTiles);
+    }
   }
-  if (remainders_with_big_tiles(E_loc, d, f, false))
-    return launch_gemm_pipe_bf16(PipeRows::kBigAll, false, h, offsets, E_loc, max_rows, w2, y, d, f, wlist, stream);
-  const bool ride = kRide && !few_gemm_tiles(E_loc, d, false);
-  int e = launch_gemm_pipe_bf16(ride ? PipeRows::kBigRide : PipeRows::kBigTiles, false, h, offsets, E_loc, max_rows, w2, y, d, f, wlist, stream);
-  if (e != 0) return e;
-  return launch_gemm_pipe_bf16(ride ? PipeRows::kTailRide : PipeRows::kTailTiles, false, h, offsets, E_loc, max_rows, w2, y, d, f, wlist, stream);
 }
 
 }  // namespace moe

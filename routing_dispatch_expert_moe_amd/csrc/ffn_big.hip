@@ -74,7 +74,7 @@ int launch_kind(PipeRows rows, const void* A, const int32_t* offsets, int E_loc,
     case PipeRows::kBigAll:
       return launch_pipe<SWIGLU, 256, 256, 4, ROWS_ALL, SAVE>(A, offsets, E_loc, max_rows, W, C, N, K, wlist, AB, s);
     case PipeRows::kTailTiles: {
-      if (!few_gemm_tiles(E_loc, N, SWIGLU))
+      if (!few_gemm_tiles(E_loc, N, SWIGLU, device_cu_count()))
         return launch_pipe<SWIGLU, 128, 256, 6, ROWS_TAIL, SAVE>(A, offsets, E_loc, max_rows, W, C,
                                                                   N, K, wlist, AB, s);
       return launch_pipe<SWIGLU, kSmallBM, kSmallBNW, kSmallStages, ROWS_TAIL, SAVE>(
@@ -87,19 +87,6 @@ int launch_kind(PipeRows rows, const void* A, const int32_t* offsets, int E_loc,
 }
 
 }  // namespace
-
-bool few_gemm_tiles(int E_loc, int N, bool swiglu) {
-  const int64_t tiles256 = static_cast<int64_t>(E_loc) * ((N + (swiglu ? 127 : 255)) /
-                                                          (swiglu ? 128 : 256));
-  return tiles256 < 4 * static_cast<int64_t>(device_cu_count());
-}
-
-bool remainders_with_big_tiles(int E_loc, int N, int K, bool swiglu) {
-  // with few tiles the remainder tiles would re-stream whole weight matrices,
-  // so they ride along with the expert's 256-row tiles; but a pass with long
-  // tiles (large K) pays a whole extra round for a few of them
-  return few_gemm_tiles(E_loc, N, swiglu) && K <= 4096;
-}
 
 int launch_gemm_pipe_bf16(PipeRows rows, bool swiglu, const void* A, const int32_t* offsets,
                           int E_loc, int64_t max_rows, const void* W, void* C, int N, int K,

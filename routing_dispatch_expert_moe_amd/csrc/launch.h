@@ -61,12 +61,22 @@ enum FusedRows { kFusedBigTail = 0, kFusedRide = 1, kFusedAllBig = 2, kFusedWide
 constexpr int64_t kWideRows = 512;
 enum class PipeRows { kBigTiles, kBigAll, kTailTiles, kAllRows, kBigRide, kTailRide, kAllRowsWide };
 // true when one GEMM pass over E_loc experts with N output columns gives few
-// tiles (fewer than 4 per CU with 256-row weight tiles): then remainders ride
-// along with the 256-row tiles instead of a second kernel re-streaming weights
-bool few_gemm_tiles(int E_loc, int N, bool swiglu);
+// tiles (fewer than 4 per CU with 256-row weight tiles on a device of cu
+// compute units): then remainders ride along with the 256-row tiles instead
+// of a second kernel re-streaming weights
+bool few_gemm_tiles(int E_loc, int N, bool swiglu, int cu);
 // whether a pass runs every row in 256-row tiles (kBigAll) rather than
 // 256-row tiles plus a remainder kernel
-bool remainders_with_big_tiles(int E_loc, int N, int K, bool swiglu);
+bool remainders_with_big_tiles(int E_loc, int N, int K, bool swiglu, int cu);
+// whether every operand of a bf16 FFN half (activations, one expert's
+// weights, output) fits 32-bit byte offsets (the pipelined kernels' rule)
+bool ffn_operands_fit32(bool up, int64_t max_rows, int d, int f);
+// rows per expert on average (host bound) at or below which a pass streams
+// weights with 32-row tiles
+constexpr int64_t kStreamRows = 48;
+// the kernels of one bf16 FFN half (up = GEMM1 + SwiGLU, else GEMM2): a
+// moe_ffn_plan_t value (include/moe.h)
+int ffn_plan_bf16(bool up, int64_t max_rows, int E_loc, int d, int f, int cu);
 // ab (SwiGLU only): if not null, the pre-activations are stored there too
 // ([rows][2N]: a then g)
 int launch_gemm_pipe_bf16(PipeRows rows, bool swiglu, const void* A, const int32_t* offsets,

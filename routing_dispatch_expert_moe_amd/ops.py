@@ -68,6 +68,21 @@ def moe_max_rows(T: int, k: int, E_loc: int, capacity: int) -> int:
     return int(lib().moe_max_rows(T, k, E_loc, capacity))
 
 
+_PLAN_NAMES = {0: "none", 1: "f32", 2: "stream", 3: "stream (operands of 4 GiB or more)",
+               4: "wide", 5: "big_all", 6: "big_tail", 7: "big_ride"}
+
+
+def moe_ffn_plan(half: str, max_rows: int, E_loc: int, d: int, f: int, dtype: str = "bf16",
+                 cu_count: int = 256) -> str:
+    """Name of the kernel plan moe_ffn_up (half='up') or moe_ffn_down
+    (half='down') uses for these sizes (host-only query, no GPU)."""
+    code = int(lib().moe_ffn_plan({"up": 0, "down": 1}[half], max_rows, E_loc, d, f,
+                                  {"f32": L.MOE_F32, "bf16": L.MOE_BF16}[dtype], cu_count))
+    if code < 0:
+        raise ValueError("invalid arguments for moe_ffn_plan")
+    return _PLAN_NAMES[code]
+
+
 def alloc_workspace(T: int, E: int, k: int, E_loc: int, device="cuda") -> torch.Tensor:
     n = moe_workspace_bytes(T, E, k, E_loc)
     if n == 0:

@@ -345,3 +345,46 @@ def test_backward_validation(lib):
     assert pb(FAKE, FAKE, 2, 64, 64, BF, MIS, None) == L.MOE_ERR_MISALIGNED
     # combine with unit weights is allowed (topk_w NULL) but still needs its other buffers
     assert lib.moe_combine(FAKE, None, None, 10, 2, 64, BF, FAKE, None) == L.MOE_ERR_INVALID_ARG
+
+
+def test_ffn_plan_on_the_workload_shapes(lib):
+    """The kernel choice of each FFN half, from the sizes alone (no GPU)."""
+    plan = M.moe_ffn_plan
+    # Mixtral-shaped prefill: few short tiles for GEMM1, 14336-deep GEMM2
+    assert plan("up", 8192, 8, 4096, 14336) == "big_all"
+    assert plan("down", 8192, 8, 4096, 14336) == "big_tail"
+    # DeepSeek-shaped decode and the Zipf-skewed prefill (256 experts)
+    assert plan("up", 1024, 256, 7168, 2048) == "stream"
+    assert plan("down", 1024, 256, 7168, 2048) == "stream"
+    assert plan("up", 65536, 256, 7168, 2048) == "big_ride"
+    assert plan("down", 65536, 256, 7168, 2048) == "big_ride"
+    # one expert-parallel rank's share: 32 local experts, capacity 320
+    rows = M.moe_max_rows(16384, 2, 32, 320)
+    assert rows == 10240
+    assert plan("up", rows, 32, 4096, 1536) == "wide"
+    assert plan("down", rows, 32, 4096, 1536) == "big_all"
+    assert plan("up", 128, 8, 128, 256, dtype="f32") == "f32"
+    assert plan("up", 0, 8, 128, 256) == "none"
+    with pytest.raises(ValueError):
+        plan("up", 10, 0, 128, 256)
+
+
+def test_ffn_plan_falls_back_when_an_operand_reaches_4_gib(lib):
+    """The pipelined kernels use 32-bit byte offsets for the activations, one
+    expert's weights and the output: once max_rows x max(d, f) bf16 elements
+    reach 4 GiB the pass takes the 64-bit-addressed streaming kernel."""
+    plan = M.moe_ffn_plan
+    lim = 1 << 32
+    # Mixtral shape: the output h of GEMM1 (max_rows x 14336) crosses first
+    r = (lim - 1) // (14336 * 2)
+    assert r * 14336 * 2 < lim <= (r + 1) * 14336 * 2
+    assert plan("up", r, 8, 4096, 14336) == "big_all"
+    assert plan("up", r + 1, 8, 4096, 14336) == "stream (operands of 4 GiB or more)"
+    assert plan("down", r + 1, 8, 4096, 14336) == "stream (operands of 4 GiB or more)"
+    # DeepSeek shape: the output y_perm of GEMM2 (max_rows x 7168) crosses first
+    r = (lim - 1) // (7168 * 2)
+    assert plan("down", r, 256, 7168, 2048) == "big_ride"
+    assert plan("down", r + 1, 256, 7168, 2048) == "stream (operands of 4 GiB or more)"
+    assert plan("up", r + 1, 256, 7168, 2048) == "stream (operands of 4 GiB or more)"
+    # one expert's weights of 4 GiB or more
+    assert plan("up", 4096, 1, 16384, 65536) == "stream (operands of 4 GiB or more)"
