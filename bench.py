@@ -1,20 +1,28 @@
 #!/usr/bin/env python3
 """Benchmark of the MoE expert path on one MI355X.
 
-One step = one whole MoE layer on one batch: router logits -> top-k routing ->
-dispatch (plan + permutation) -> grouped GEMM1 + SwiGLU -> grouped GEMM2 ->
+One step = one whole MoE layer on one batch: [router logits] -> top-k routing
+-> dispatch (plan + permutation) -> grouped GEMM1 + SwiGLU -> grouped GEMM2 ->
 weighted combine, all through the library's C ABI on one HIP stream, inputs
-resident in HBM.  Default workload: the Mixtral-shaped bf16 prefill layer
-(T=4096 tokens, d_model=4096, d_ff=14336, 8 experts, top-2), synthetic seeded
-inputs.  Prints ONE JSON line.
+resident in HBM.  The headline workload is the largest one-GPU configuration:
+the DeepSeek-V3-shaped bf16 prefill layer with Zipf-skewed expert popularity
+(T=8192 tokens, d_model=7168, d_ff=2048, 256 experts, top-8, sigmoid gates),
+synthetic seeded inputs.  The other four workloads (tiny fp32 layer,
+Mixtral-shaped prefill, DeepSeek-shaped decode, one expert-parallel rank's
+share) are timed in the same run and reported under "others".  Prints ONE
+JSON line.
 
-Also reports, for the dominant kernel (GEMM1 + SwiGLU), its achieved MFMA
-throughput against the bf16 dense peak, and the CPU oracle timed on a bounded
-sample of the same workload.
+Also reports, for the dominant pass (GEMM1 + SwiGLU), its achieved throughput
+against the bound of its algorithmic work (HBM or bf16 MFMA), every pass's
+roofline fraction, and the CPU oracle timed on a bounded sample of the
+headline workload.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -33,15 +41,42 @@ import numpy as np  # noqa: E402
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "MoE-layer tokens/s + TFLOP/s (MFMA %) and HBM GB/s (% peak), 1×MI355X"
+HEADLINE = "dsv3_prefill_zipf"
+# (the decode workload first: it shares the headline's expert weights)
+OTHERS = ("dsv3_decode", "mixtral_prefill", "ep_rank_share", "tiny_fp32")
 STEPS = ("router", "route", "dispatch", "ffn_up", "ffn_down", "combine")
+DOMINANT = "ffn_up"                 # one GEMM1 + SwiGLU pass over all local rows
+COPY_BYTES = 1 << 30
+
+# kernels of each pass (substrings of the demangled names rocprofv3 reports)
+PASS_KERNELS = {
+    "router": ("router_logits_kernel",),
+    "route": ("route_kernel", "route_candidates_kernel", "reroute_resolve_kernel",
+              "reroute_finalize_kernel"),
+    "dispatch_plan": ("dispatch_count_kernel", "dispatch_scan_kernel", "dispatch_place_kernel"),
+    "permute": ("permute_rows_kernel",),
+    "ffn_up": ("gemm_bf16_pipe<true", "gemm_bf16_kernel<32, 128, 64, 1, 4, true",
+               "gemm_f32_kernel<true"),
+    "ffn_down": ("gemm_bf16_pipe<false", "gemm_bf16_kernel<32, 128, 64, 1, 4, false",
+                 "gemm_f32_kernel<false"),
+    "combine": ("combine_kernel",),
+}
+# stored counter and kernel-time summaries are tied to the kernel sources
+SOURCE_GLOBS = ("routing_dispatch_expert_moe_amd/csrc/*.hip", "routing_dispatch_expert_moe_amd/csrc/*.h",
+                "routing_dispatch_expert_moe_amd/csrc/*.cpp")
 
 
-def parse():
+def parse(argv=None):
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="mixtral_prefill")
+    p.add_argument("--workload", default=HEADLINE)
+    p.add_argument("--others", default=None,
+                   help="comma-separated workloads timed after the headline one, or 'none' "
+                        "(default: the other four when the headline is the default workload)")
+    p.add_argument("--no-fused", action="store_true",
+                   help="leave out the fused persistent launch (moe_forward_fused)")
     p.add_argument("--reroute", action="store_true",
                    help="route with capacity-overflow rerouting (moe_route_reroute)")
     p.add_argument("--weights", choices=("native", "fp8"), default="native",
@@ -53,10 +88,7 @@ def parse():
                         "kept, then the whole backward pass (gradients of x, the gate logits "
                         "or router, and the expert weights); reported under 'training'")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample-tokens", type=int, default=256)
-    p.add_argument("--traffic", default=None,
-                   help="JSON file with counter-derived HBM bytes per launch of the dominant "
-                        "kernel (default: profiles/traffic_<workload>.json if present)")
+    p.add_argument("--cpu-sample-tokens", type=int, default=64)
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device copy (the counter calibration kernel)")
     p.add_argument("--traffic-from", default=None, metavar="DIR",
@@ -66,39 +98,40 @@ def parse():
                    help="summarise a rocprofv3 --pmc database under DIR taken with "
                         + " ".join(MFMA_COUNTERS) + " (MFMA busy fraction and counted "
                         "MFMA flops per kernel) and exit")
-    return p.parse_args()
+    p.add_argument("--trace-from", default=None, metavar="DIR",
+                   help="summarise a rocprofv3 --kernel-trace run under DIR of this script "
+                        "(--workload W --steps K --warmup W --others none --no-fused) into "
+                        "profiles/kernels_<workload>.md and profiles/kernel_times_<workload>.json "
+                        "and exit")
+    p.add_argument("--profiles-dir", default=os.path.join(ROOT, "profiles"))
+    return p.parse_args(argv)
 
 
-# ---- HBM traffic of the dominant kernel from hardware counters -------------
+def sources_hash():
+    h = hashlib.sha256()
+    for pat in SOURCE_GLOBS:
+        for path in sorted(glob.glob(os.path.join(ROOT, pat))):
+            h.update(os.path.basename(path).encode())
+            with open(path, "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def pass_of(kernel_name):
+    for name, pats in PASS_KERNELS.items():
+        if any(p in kernel_name for p in pats):
+            return name
+    return None
+
+
+# ---- HBM traffic per pass from hardware counters --------------------------
 #
 # FETCH_SIZE and WRITE_SIZE (KiB per dispatch, summed over the channels) are
 # taken in two rocprofv3 --pmc passes over a short bench run, and in two passes
 # over a plain device copy of known size; the copy's counted bytes over its
-# true bytes is the scale applied to the kernel's counts.  The result records a
-# hash of the kernel's sources: once they change, the stored traffic is stale
+# true bytes is the scale applied to the kernels' counts.  The result records a
+# hash of the kernel sources: once they change, the stored traffic is stale
 # and the bench reports null.
-
-DOMINANT = "moe_ffn_up"                         # one GEMM1 + SwiGLU pass over all local rows
-# the kernels that pass launches (demangled name prefixes): the pipelined
-# 256-row / remainder kernels, the register-staged few-rows kernel, fp32
-DOMINANT_KERNELS = ("gemm_bf16_pipe<true", "gemm_bf16_kernel<32, 128, 64, 1, 4, true",
-                    "gemm_f32_kernel<true")
-DOMINANT_SOURCES = ("routing_dispatch_expert_moe_amd/csrc/ffn_big.hip",
-                    "routing_dispatch_expert_moe_amd/csrc/gemm_pipe.h",
-                    "routing_dispatch_expert_moe_amd/csrc/ffn_bf16.hip",
-                    "routing_dispatch_expert_moe_amd/csrc/tile_sched.h",
-                    "routing_dispatch_expert_moe_amd/csrc/common.h")
-COPY_BYTES = 1 << 30
-
-
-def sources_hash():
-    import hashlib
-    h = hashlib.sha256()
-    for rel in DOMINANT_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
-
 
 def copy_calibration():
     import torch
@@ -112,8 +145,7 @@ def copy_calibration():
 
 
 def _pmc_per_dispatch(path, counter):
-    """{dispatch_id: (kernel_name, value summed over dimensions)} from rocprofv3 databases."""
-    import glob
+    """{(db, dispatch_id): (kernel_name, value summed over dimensions)} from rocprofv3 databases."""
     import sqlite3
     out = {}
     files = glob.glob(os.path.join(path, "**", "*.db"), recursive=True)
@@ -167,60 +199,155 @@ def counters_from(args):
 
 
 def traffic_from(args):
+    """Counter bytes per call of every pass (each pass's kernels' mean counted
+    KiB per dispatch, summed, scaled by the copy calibration)."""
     d = args.traffic_from
-    res = {}
+    scale = {}
+    per_pass = {}
     for ctr, sub in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
         copy = [v for n, v in _pmc_per_dispatch(os.path.join(d, "copy_" + sub), ctr).values()
                 if "copy" in n.lower() or "elementwise" in n.lower()]
-        kern = [v for n, v in _pmc_per_dispatch(os.path.join(d, sub), ctr).values()
-                if any(p in n for p in DOMINANT_KERNELS)]
-        if not copy or not kern:
-            raise SystemExit(f"{ctr}: found {len(copy)} copy and {len(kern)} kernel dispatches")
+        if not copy:
+            raise SystemExit(f"{ctr}: no copy dispatches in the calibration run")
         copy_kib = float(np.median(copy))
-        scale = (COPY_BYTES / 1024.0) / copy_kib   # true KiB per counted KiB
-        res[ctr] = {"copy_counted_kib": copy_kib, "scale": scale,
-                    "kernel_dispatches": len(kern),
-                    "kernel_counted_kib_per_dispatch": float(np.mean(kern))}
-    # the dominant pass launches len(DOMINANT_KERNELS)-many kernels per call at most;
-    # bytes per call = sum over its kernels of their mean counted KiB, scaled
-    per_call = {}
-    for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+        scale[ctr] = {"copy_counted_kib": copy_kib, "scale": (COPY_BYTES / 1024.0) / copy_kib}
         groups = {}
-        sub = "fetch" if ctr == "FETCH_SIZE" else "write"
         for n, v in _pmc_per_dispatch(os.path.join(d, sub), ctr).values():
-            if any(p in n for p in DOMINANT_KERNELS):
-                groups.setdefault(n.split("(")[0], []).append(v)
-        per_call[ctr] = sum(float(np.mean(v)) for v in groups.values()) * 1024.0 * res[ctr]["scale"]
-        res[ctr]["kernels"] = {k: float(np.mean(v)) for k, v in groups.items()}
-    out = {DOMINANT: {"fetch_bytes": per_call["FETCH_SIZE"], "write_bytes": per_call["WRITE_SIZE"],
-                      "bytes": per_call["FETCH_SIZE"] + per_call["WRITE_SIZE"]},
-           "workload": args.workload, "sources_sha256_16": sources_hash(), "counters": res}
-    path = args.traffic or os.path.join(ROOT, "profiles", f"traffic_{args.workload}.json")
+            p = pass_of(n)
+            if p is not None:
+                groups.setdefault(p, {}).setdefault(n.split("(")[0], []).append(v)
+        for p, kern in groups.items():
+            rec = per_pass.setdefault(p, {"kernels": {}})
+            b = sum(float(np.mean(v)) for v in kern.values()) * 1024.0 * scale[ctr]["scale"]
+            rec["fetch_bytes" if ctr == "FETCH_SIZE" else "write_bytes"] = b
+            for kname, v in kern.items():
+                rec["kernels"].setdefault(kname, {})[ctr + "_kib_per_dispatch"] = float(np.mean(v))
+                rec["kernels"][kname]["dispatches"] = len(v)
+    if DOMINANT not in per_pass:
+        raise SystemExit("no dispatch of the dominant pass in the counter runs")
+    for rec in per_pass.values():
+        rec["bytes"] = rec.get("fetch_bytes", 0.0) + rec.get("write_bytes", 0.0)
+    out = {"workload": args.workload, "sources_sha256_16": sources_hash(), "calibration": scale,
+           "passes": per_pass}
+    path = os.path.join(args.profiles_dir, f"traffic_{args.workload}.json")
     with open(path, "w") as fh:
         json.dump(out, fh, indent=1)
-    print(json.dumps(out[DOMINANT]))
+    print(json.dumps({p: round(r["bytes"]) for p, r in per_pass.items()}))
 
 
-def load_traffic(args):
+def load_stored(args, kind, workload):
+    """profiles/<kind>_<workload>.json if it exists and matches the current
+    kernel sources: (dict, note) or (None, reason)."""
     if getattr(args, "weights", "native") != "native":
-        return None, "counters were taken with the native-precision weights"
-    path = args.traffic or os.path.join(ROOT, "profiles", f"traffic_{args.workload}.json")
+        return None, "stored figures were taken with the native-precision weights"
+    path = os.path.join(args.profiles_dir, f"{kind}_{workload}.json")
     if not os.path.exists(path):
-        return None, "no counter file"
+        return None, f"no {os.path.basename(path)}"
     with open(path) as fh:
         t = json.load(fh)
-    if t.get("workload") != args.workload:
-        return None, "counter file is for another workload"
+    if t.get("workload") != workload:
+        return None, "stored file is for another workload"
     if t.get("sources_sha256_16") != sources_hash():
-        return None, "kernel sources changed since the counters were taken"
-    return t[DOMINANT]["bytes"], "rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by a 1 GiB copy"
+        return None, "kernel sources changed since the stored figures were taken"
+    return t, os.path.relpath(path, ROOT)
 
+
+# ---- kernel-trace summary --------------------------------------------------
+
+def _read_trace(d):
+    files = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no *kernel_trace.csv under {d}")
+    rows = []
+    for f in files:
+        with open(f, newline="") as fh:
+            rd = csv.DictReader(fh)
+            cols = {c.lower(): c for c in rd.fieldnames or []}
+            kn, st, en = cols["kernel_name"], cols["start_timestamp"], cols["end_timestamp"]
+            for r in rd:
+                rows.append((int(r[st]), int(r[en]), r[kn]))
+    rows.sort()
+    return rows
+
+
+def trace_from(args):
+    """Per-kernel statistics of a profiled bench run and, per pass, the
+    kernel time of each timed step (the run's dispatches of a pass are its
+    warm-up steps, then the timed steps, then the cache-evicted steps)."""
+    rows = _read_trace(args.trace_from)
+    stats = {}
+    total = 0.0
+    for s0, s1, n in rows:
+        us = (s1 - s0) / 1e3
+        total += us
+        stats.setdefault(n.split("(")[0], []).append(us)
+    per_pass = {}
+    for s0, s1, n in rows:
+        p = pass_of(n)
+        if p is not None:
+            per_pass.setdefault(p, []).append((s0, s1, n.split("(")[0]))
+    W, K = args.warmup, args.steps
+    passes = {}
+    for p, disp in per_pass.items():
+        names = sorted({n for _, _, n in disp})
+        per_call = len(names)
+        if len(disp) < (W + K) * per_call:
+            continue
+        timed = disp[W * per_call:(W + K) * per_call]
+        steps = [sum((b - a) / 1e3 for a, b, _ in timed[i * per_call:(i + 1) * per_call])
+                 for i in range(K)]
+        passes[p] = {"kernels": names, "launches_per_call": per_call,
+                     "per_step_us": [round(v, 2) for v in steps],
+                     "mean_us": round(float(np.mean(steps)), 2)}
+    event = None
+    bl = os.path.join(args.trace_from, "bench.json")
+    if os.path.exists(bl):
+        with open(bl) as fh:
+            event = json.loads(fh.read().strip().splitlines()[-1])
+    out = {"workload": args.workload, "sources_sha256_16": sources_hash(), "steps": K,
+           "warmup": W, "passes": passes}
+    if event is not None:
+        out["bench_event_mean_us"] = {p: round(v["ms"] * 1e3, 2)
+                                      for p, v in event.get("per_step", {}).items()}
+    with open(os.path.join(args.profiles_dir, f"kernel_times_{args.workload}.json"), "w") as fh:
+        json.dump(out, fh, indent=1)
+    cmd = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --output-format csv "
+           f"-d <out> -o kt -- python3 <repo>/bench.py --workload {args.workload} --steps {K} "
+           f"--warmup {W} --others none --no-fused --no-cpu-baseline > <out>/bench.json")
+    lines = [f"# Kernel time summary: MoE layer, workload {args.workload}", "",
+             "Command (from the repository root, on one MI355X):", "", "    " + cmd, "",
+             f"{W} warm-up and {K} timed layer steps of the separate calls, then {K} more with the "
+             "Infinity Cache evicted before each (a 1 GiB fill between steps), then the "
+             "dispatch plan alone, then five 1 GiB copies (the bench's plain-copy reference); "
+             "weight packing and input upload run once before them.  Durations are the kernel "
+             "trace's start/end stamps, in microseconds.", "",
+             "| kernel | calls | avg us | min us | max us | % of traced GPU time |",
+             "|---|---|---|---|---|---|"]
+    for n, v in sorted(stats.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"| `{n}` | {len(v)} | {np.mean(v):.2f} | {min(v):.2f} | {max(v):.2f} | "
+                     f"{100 * sum(v) / total:.2f} |")
+    lines += ["", "Per pass, kernel time of each timed step (sum over the pass's kernels):", "",
+              "| pass | kernels | per-step us | mean us | bench HIP-event mean us |",
+              "|---|---|---|---|---|"]
+    for p in ("router", "route", "dispatch_plan", "permute", "ffn_up", "ffn_down", "combine"):
+        if p in passes:
+            r = passes[p]
+            ev = (out.get("bench_event_mean_us") or {}).get(p, "")
+            lines.append(f"| {p} | {', '.join('`' + k + '`' for k in r['kernels'])} | "
+                         f"{', '.join(f'{v:.1f}' for v in r['per_step_us'])} | {r['mean_us']:.1f} | "
+                         f"{ev} |")
+    lines.append("")
+    with open(os.path.join(args.profiles_dir, f"kernels_{args.workload}.md"), "w") as fh:
+        fh.write("\n".join(lines))
+    print(json.dumps({p: r["mean_us"] for p, r in passes.items()}))
+
+
+# ---- the benchmark ----------------------------------------------------------
 
 def smi_snapshot():
     """Graphics and memory clocks and socket power read from the driver's sysfs
     files (plain reads; no program is started): {"sclk_mhz", "mclk_mhz",
     "socket_power_w", "power_cap_w"}, or None where they are missing."""
-    import glob
     import re
 
     def current(path):
@@ -259,7 +386,8 @@ def bf16_dev(a, dev):
 def work_model(wl, n, touched, T_read, wb=None):
     """Algorithmic flops and HBM bytes per launch of each step (wb: bytes per
     weight element when it differs from the activations', e.g. 1 for FP8
-    codes; their block scales add 4 B per 128 x 128 block)."""
+    codes; their block scales add 4 B per 128 x 128 block).  'dispatch' is the
+    whole call; 'dispatch_plan' and 'permute' are its two parts."""
     b = 2 if wl.dtype == "bf16" else 4
     if wb is None:
         wb = b
@@ -268,12 +396,29 @@ def work_model(wl, n, touched, T_read, wb=None):
         "router": (2.0 * T * d * E if wl.w_gate is not None else 0.0,
                    (T * d * b + d * E * 4 + T * E * 4) if wl.w_gate is not None else 0.0),
         "route": (0.0, T * E * 4 + T * k * 8),
-        "dispatch": (0.0, 12.0 * T * k + T_read * d * b + n * d * b),
+        "dispatch_plan": (0.0, 12.0 * T * k),
+        "permute": (0.0, T_read * d * b + n * d * b),
         "ffn_up": (4.0 * n * d * f, touched * 2.0 * f * d * wb + n * d * b + n * f * b),
         "ffn_down": (2.0 * n * f * d, touched * 1.0 * d * f * wb + n * f * b + n * d * b),
         "combine": (0.0, n * d * b + T * k * 8 + T * d * b),
     }
+    m["dispatch"] = (0.0, m["dispatch_plan"][1] + m["permute"][1])
     return m
+
+
+def roofline_of(fl, by, ms):
+    """The pass's bound (whichever of its algorithmic flops at the bf16 MFMA peak
+    and its algorithmic bytes at the HBM peak takes longer) and the fraction
+    of that bound's time its measured time reaches."""
+    t_mfma = fl / (PEAK_BF16_TFLOPS * 1e12)
+    t_hbm = by / (PEAK_HBM_GBS * 1e9)
+    if ms <= 0 or (t_mfma == 0 and t_hbm == 0):
+        return None
+    if t_mfma >= t_hbm:
+        return {"bound": "mfma", "achieved": round(fl / (ms * 1e-3) / 1e12, 1),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(t_mfma / (ms * 1e-3), 4)}
+    return {"bound": "hbm", "achieved": round(by / (ms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": round(t_hbm / (ms * 1e-3), 4)}
 
 
 def cpu_baseline(wl, host_w, n_tok):
@@ -403,19 +548,14 @@ def train_bench(args, wl, layer, x, logits, wg, w13_t, w2_t, n, touched, T_read,
                      "tflops": round(fl / (ms * 1e-3) / 1e12, 2) if fl and ms > 0 else None,
                      "gbs": round(by / (ms * 1e-3) / 1e9, 1) if by and ms > 0 else None}
     bwd_ms = float(np.mean([ev[s][6].elapsed_time(ev[s][13]) for s in range(args.steps)]))
-    fl = sum(v[0] for v in model.values() if v is not None) - model["ffn_up"][0]
+    fl = sum(model[k][0] for k in TRAIN_STEPS)
     # the dominant backward call: the longest one
     dom = max(TRAIN_STEPS[6:], key=lambda k: per[k]["ms"])
     dfl, dby = model[dom]
     dms = per[dom]["ms"]
-    if dfl / (PEAK_BF16_TFLOPS * 1e12) >= dby / (PEAK_HBM_GBS * 1e9):
-        roof = {"bound": "mfma", "achieved": round(dfl / (dms * 1e-3) / 1e12, 1),
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
-    else:
-        roof = {"bound": "hbm", "achieved": round(dby / (dms * 1e-3) / 1e9, 1),
-                "peak": PEAK_HBM_GBS, "unit": "GB/s"}
-    roof.update(call=dom, frac=round(roof["achieved"] / roof["peak"], 4), avg_launch_ms=dms,
-                algorithmic_flops_per_launch=dfl, algorithmic_bytes_per_launch=dby)
+    roof = roofline_of(dfl, dby, dms)
+    roof.update(call=dom, avg_launch_ms=dms, algorithmic_flops_per_launch=dfl,
+                algorithmic_bytes_per_launch=dby)
     return {"ms_per_step": round(ms_step, 4), "tokens_per_s": round(wl.T / (ms_step * 1e-3), 1),
             "backward_ms": round(bwd_ms, 4), "step_tflops": round(fl / (ms_step * 1e-3) / 1e12, 2),
             "per_call": per, "roofline": roof,
@@ -424,74 +564,81 @@ def train_bench(args, wl, layer, x, logits, wg, w13_t, w2_t, n, touched, T_read,
                     "around every call on the launch stream"}
 
 
-def main():
-    args = parse()
-    if args.traffic_from:
-        traffic_from(args)
-        return
-    if args.copy_calibration:
-        copy_calibration()
-        return
-    if args.counters_from:
-        counters_from(args)
-        return
-    if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark runs on exactly one GPU; "
-                                   f"--gpus {args.gpus} is not supported (the path is single-GPU)"}))
-        sys.exit(2)
+class Weights:
+    """Packed device weights of the workloads, generated on the host once per
+    weight set (the DeepSeek-shaped decode and prefill workloads share theirs)."""
+
+    def __init__(self, dev):
+        self.dev = dev
+        self.key = None
+        self.val = None
+
+    def get(self, wl, keep_host=False, train=False):
+        import torch
+        import routing_dispatch_expert_moe_amd as M
+        key = (wl.E_loc, wl.e_begin, wl.d, wl.f, wl.seed, wl.dtype)
+        if (self.key == key and (not keep_host or self.val[2] is not None)
+                and (not train or self.val[3] is not None)):
+            return self.val
+        self.key = self.val = None
+        torch.cuda.empty_cache()
+        dev = self.dev
+        tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+        w13 = torch.empty((wl.E_loc, 2 * wl.f, wl.d), dtype=tdt, device=dev)
+        w2p = torch.empty((wl.E_loc, wl.d, wl.f), dtype=tdt, device=dev)
+        host_w = [] if keep_host else None
+        w13_t = w2_t = None
+        if train:   # the backward operands: [W1 | W3] rows per d, and W2 as it is
+            w13_t = torch.empty((wl.E_loc, wl.d, 2 * wl.f), dtype=tdt, device=dev)
+            w2_t = torch.empty((wl.E_loc, wl.f, wl.d), dtype=tdt, device=dev)
+
+        def up(a):
+            return bf16_dev(a, dev) if wl.dtype == "bf16" else torch.from_numpy(a).to(dev)
+
+        for c0 in range(0, wl.E_loc, 16):
+            ids = list(range(wl.e_begin + c0, wl.e_begin + min(wl.E_loc, c0 + 16)))
+            a, b, c = wl.stacked_weights(ids)
+            if keep_host:
+                host_w.extend(zip(a, b, c))
+            ga, gb, gc = up(a), up(b), up(c)
+            M.moe_pack_weights(ga, gb, gc, w13[c0:c0 + len(ids)], w2p[c0:c0 + len(ids)])
+            if train:
+                M.moe_pack_weights_backward(ga, gb, w13_t[c0:c0 + len(ids)])
+                w2_t[c0:c0 + len(ids)] = gc
+            del ga, gb, gc
+        torch.cuda.synchronize()
+        self.key, self.val = key, (w13, w2p, host_w, w13_t, w2_t)
+        return self.val
+
+
+def run_workload(args, wl, weights, dev, headline):
+    """Time one workload's layer: K steps of the separate calls (HIP events
+    around each call), the same steps with the Infinity Cache evicted, the
+    dispatch plan alone, and the fused launch; returns the results dict."""
     import torch
     import routing_dispatch_expert_moe_amd as M
-    from workloads import make
 
-    dev = torch.device("cuda:0")
-    wl = make(args.workload)
     log(f"workload {wl.name}: T={wl.T} d={wl.d} f={wl.f} E={wl.E} k={wl.k} dtype={wl.dtype}")
-
-    # weights: generated on the host, uploaded, packed once (untimed)
-    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
-    w13 = torch.empty((wl.E_loc, 2 * wl.f, wl.d), dtype=tdt, device=dev)
-    w2p = torch.empty((wl.E_loc, wl.d, wl.f), dtype=tdt, device=dev)
-    host_w = []
-    keep_host = not args.no_cpu_baseline
-
-    def up(a):
-        return bf16_dev(a, dev) if wl.dtype == "bf16" else torch.from_numpy(a).to(dev)
-
-    train = args.backward
-    if train:   # the backward operands: [W1 | W3] rows per d, and W2 as it is
-        w13_t = torch.empty((wl.E_loc, wl.d, 2 * wl.f), dtype=tdt, device=dev)
-        w2_t = torch.empty((wl.E_loc, wl.f, wl.d), dtype=tdt, device=dev)
-    for c0 in range(0, wl.E_loc, 8):
-        ids = list(range(wl.e_begin + c0, wl.e_begin + min(wl.E_loc, c0 + 8)))
-        a, b, c = wl.stacked_weights(ids)
-        if keep_host:
-            host_w.extend(zip(a, b, c))
-        ga, gb, gc = up(a), up(b), up(c)
-        M.moe_pack_weights(ga, gb, gc, w13[c0:c0 + len(ids)], w2p[c0:c0 + len(ids)])
-        if train:
-            M.moe_pack_weights_backward(ga, gb, w13_t[c0:c0 + len(ids)])
-            w2_t[c0:c0 + len(ids)] = gc
-        del ga, gb, gc
-    torch.cuda.synchronize()
+    train = headline and args.backward
+    keep_host = headline and not args.no_cpu_baseline
+    w13, w2p, host_w, w13_t, w2_t = weights.get(wl, keep_host=keep_host, train=train)
     log("weights packed")
-
     C = M.moe_capacity(wl.T, wl.k, wl.E, wl.capacity_factor)
-    fp8 = args.weights == "fp8"
+    fp8 = headline and args.weights == "fp8"
+    reroute = headline and args.reroute
+    s13 = s2 = None
     if fp8:
         if wl.dtype != "bf16":
             raise SystemExit("--weights fp8 needs a bf16 workload")
         q13, s13 = M.moe_quantize_fp8(w13)
         q2, s2 = M.moe_quantize_fp8(w2p)
         torch.cuda.synchronize()
-        del w13, w2p
-        torch.cuda.empty_cache()
         w13, w2p = q13, q2
         log("weights quantised to E4M3 with 128 x 128 block scales")
     layer = M.MoELayer(w13, w2p, E=wl.E, k=wl.k, gate=wl.gate, T=wl.T, capacity=C,
-                       w13_scale=s13 if fp8 else None, w2_scale=s2 if fp8 else None,
-                       reroute=args.reroute,
+                       w13_scale=s13, w2_scale=s2, reroute=reroute,
                        e_begin=wl.e_begin, e_end=wl.e_end)
-    x = up(wl.x)
+    x = bf16_dev(wl.x, dev) if wl.dtype == "bf16" else torch.from_numpy(wl.x).to(dev)
     logits = torch.from_numpy(wl.logits).to(dev) if wl.logits is not None else None
     wg = torch.from_numpy(wl.w_gate).to(dev) if wl.w_gate is not None else None
 
@@ -517,6 +664,7 @@ def main():
         if ev is not None:
             ev[6].record()
 
+    K = args.steps
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -525,133 +673,241 @@ def main():
         raise RuntimeError(f"device error {status}")
     n = int(layer.plan.n_kept[0].item())
     counts = layer.plan.counts.cpu().numpy()[wl.e_begin:wl.e_end]
-    touched = int((np.minimum(counts, C if C >= 0 else counts.max()) > 0).sum())
+    kept = np.minimum(counts, C) if C >= 0 else counts
+    touched = int((kept > 0).sum())
     pp = layer.plan.pair_pos.cpu().numpy()[:wl.T * wl.k].reshape(wl.T, wl.k)
     T_read = int((pp >= 0).any(axis=1).sum())
-    log(f"n_kept={n} experts touched={touched} counts min={counts.min()} max={counts.max()}")
+    log(f"n_kept={n} experts touched={touched} rows per expert min={kept.min()} max={kept.max()}")
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
-    smi_before = smi_snapshot()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(K)]
+    smi_before = smi_snapshot() if headline else None
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(args.steps):
+    for s in range(K):
         step(events[s])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    smi_after = smi_snapshot()
-    ms_step = (t1 - t0) * 1e3 / args.steps
+    smi_after = smi_snapshot() if headline else None
+    ms_step = (t1 - t0) * 1e3 / K
 
     # the same steps with the 256 MB Infinity Cache (MALL) evicted before each:
     # a 1 GiB write between steps, outside the events, so that no step starts
     # with its inputs or weights cache-resident (per-step HIP-event times)
     scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-    cev = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
-    for s in range(args.steps):
+    cev = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(K)]
+    for s in range(K):
         scratch.fill_(s & 0xFF)
         step(cev[s])
+    # the dispatch plan alone (no permutation), so the permutation's own time
+    # is the dispatch call's minus this
+    pev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+    for s in range(K):
+        pev[s][0].record()
+        M.moe_dispatch(layer.topk_idx, wl.E, C, wl.e_begin, wl.e_end, None, layer.ws,
+                       layer.plan, d=layer.d, dtype=layer.dtype)
+        pev[s][1].record()
     torch.cuda.synchronize()
-    # a plain-copy reference on the same device and under the same eviction:
-    # torch's copy_ of a 1 GiB buffer, read + write bytes counted
-    src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
-    dst = torch.empty_like(src)
-    rev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(5)]
-    for s in range(5):
-        scratch.fill_(s)
-        rev[s][0].record()
-        dst.copy_(src)
-        rev[s][1].record()
-    torch.cuda.synchronize()
-    copy_ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in rev]))
-    del scratch, src, dst
-    cold_ms = {name: float(np.median([cev[s][i].elapsed_time(cev[s][i + 1])
-                                      for s in range(args.steps)]))
+    copy_ms = None
+    if headline:
+        # a plain-copy reference on the same device and under the same eviction:
+        # torch's copy_ of a 1 GiB buffer, read + write bytes counted
+        src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        rev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(5)]
+        for s in range(5):
+            scratch.fill_(s)
+            rev[s][0].record()
+            dst.copy_(src)
+            rev[s][1].record()
+        torch.cuda.synchronize()
+        copy_ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in rev]))
+        del src, dst
+    del scratch
+    cold_ms = {name: float(np.median([cev[s][i].elapsed_time(cev[s][i + 1]) for s in range(K)]))
                for i, name in enumerate(STEPS)}
-    cold_step = float(np.median([cev[s][0].elapsed_time(cev[s][6]) for s in range(args.steps)]))
+    cold_step = float(np.median([cev[s][0].elapsed_time(cev[s][6]) for s in range(K)]))
+    plan_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in pev]))
 
     # the same layer as one fused persistent launch (router logits stay a separate call)
-    fev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-
-    def fused_step(ev=None):
-        if ev is not None:
-            ev[0].record()
-        lg = layer.router(x, wg) if wg is not None else logits
-        layer.forward_fused(x, lg)
-        if ev is not None:
-            ev[1].record()
-
     fused_ms = None
-    if not fp8:   # the fused launch: bf16 / fp32 weights (with the layer's routing)
+    if not (fp8 or args.no_fused):
+        fev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+
+        def fused_step(ev=None):
+            if ev is not None:
+                ev[0].record()
+            lg = layer.router(x, wg) if wg is not None else logits
+            layer.forward_fused(x, lg)
+            if ev is not None:
+                ev[1].record()
         for _ in range(args.warmup):
             fused_step()
         torch.cuda.synchronize()
-        for s in range(args.steps):
+        for s in range(K):
             fused_step(fev[s])
         torch.cuda.synchronize()
         if M.moe_check_error(layer.ws) != 0:
             raise RuntimeError("device error in the fused layer")
         fused_ms = float(np.median([e[0].elapsed_time(e[1]) for e in fev]))
-    unfused_ms = float(np.median([events[s][0].elapsed_time(events[s][6]) for s in range(args.steps)]))
+    unfused_ms = float(np.median([events[s][0].elapsed_time(events[s][6]) for s in range(K)]))
 
-    per = {}
     model = work_model(wl, n, touched, T_read, wb=(1 + 4.0 / (128 * 128)) if fp8 else None)
+    per = {}
+    for i, name in enumerate(STEPS):
+        ms = float(np.mean([events[s][i].elapsed_time(events[s][i + 1]) for s in range(K)]))
+        per[name] = {"ms": round(ms, 5)}
+    per["dispatch_plan"] = {"ms": round(plan_ms, 5)}
+    per["permute"] = {"ms": round(max(per["dispatch"]["ms"] - plan_ms, 0.0), 5),
+                      "note": "dispatch call minus the plan alone"}
+    for name, rec in per.items():
+        fl, by = model[name]
+        ms = rec["ms"]
+        rec["tflops"] = round(fl / (ms * 1e-3) / 1e12, 2) if fl and ms > 0 else None
+        rec["gbs"] = round(by / (ms * 1e-3) / 1e9, 1) if by and ms > 0 else None
+        rec["roofline"] = roofline_of(fl, by, ms) if (fl or by) else None
     cold = {name: {"ms": round(ms, 5),
                    "gbs": round(model[name][1] / (ms * 1e-3) / 1e9, 1) if model[name][1] else None}
             for name, ms in cold_ms.items()}
-    for i, name in enumerate(STEPS):
-        ms = float(np.mean([events[s][i].elapsed_time(events[s][i + 1]) for s in range(args.steps)]))
-        fl, by = model[name]
-        per[name] = {"ms": round(ms, 5),
-                     "tflops": round(fl / (ms * 1e-3) / 1e12, 2) if fl else None,
-                     "gbs": round(by / (ms * 1e-3) / 1e9, 1) if by else None}
-    flops = sum(v[0] for v in model.values())
-    bytes_ = sum(v[1] for v in model.values())
-    tflops = flops / (ms_step * 1e-3) / 1e12
-    gbs = bytes_ / (ms_step * 1e-3) / 1e9
+    flops = sum(model[k][0] for k in STEPS)
+    bytes_ = sum(model[k][1] for k in STEPS)
+    plan_code = M.moe_ffn_plan("up", layer.plan.max_rows, wl.E_loc, wl.d, wl.f,
+                               dtype=wl.dtype, cu_count=torch.cuda.get_device_properties(dev)
+                               .multi_processor_count) if not fp8 else "fp8"
+    res = {"wl": wl, "layer": layer, "x": x, "logits": logits, "wg": wg, "host_w": host_w,
+           "w13_t": w13_t, "w2_t": w2_t, "n": n, "touched": touched, "T_read": T_read, "C": C,
+           "ms_step": ms_step, "per": per, "cold": cold, "cold_step": cold_step,
+           "fused_ms": fused_ms, "unfused_ms": unfused_ms, "model": model, "flops": flops,
+           "bytes": bytes_, "copy_ms": copy_ms, "smi": (smi_before, smi_after), "fp8": fp8,
+           "reroute": reroute, "plan_up": plan_code,
+           "rows_per_expert": [int(kept.min()), int(kept.max())]}
+    return res
 
-    dom = "ffn_up"
-    dom_ms = per[dom]["ms"]
-    dom_fl, dom_by = model[dom]
-    traffic, traffic_note = load_traffic(args)
-    # the pass is bound by whichever of its algorithmic flops and bytes takes
-    # longer at peak: MFMA with many rows per expert, HBM (weight streaming)
-    # with few
-    if dom_fl / (PEAK_BF16_TFLOPS * 1e12) >= dom_by / (PEAK_HBM_GBS * 1e9):
-        bound, achieved, peak, unit = ("mfma", dom_fl / (dom_ms * 1e-3) / 1e12,
-                                       PEAK_BF16_TFLOPS, "TFLOP/s")
+
+def dominant_roofline(args, r):
+    """The roofline object of the dominant pass (GEMM1 + SwiGLU)."""
+    wl = r["wl"]
+    fl, by = r["model"][DOMINANT]
+    ms = r["per"][DOMINANT]["ms"]
+    roof = roofline_of(fl, by, ms)
+    kernels = {"f32": "gemm_f32_kernel<SwiGLU>", "stream": "gemm_bf16_kernel<32-row tiles, SwiGLU>",
+               "wide": "gemm_bf16_pipe<SwiGLU, 128-row tiles>",
+               "big_all": "gemm_bf16_pipe<SwiGLU, 256-row tiles>",
+               "big_tail": "gemm_bf16_pipe<SwiGLU, 256-row tiles> + 128-row remainder tiles",
+               "big_ride": "gemm_bf16_pipe<SwiGLU, 256-row tiles> + 128-row tiles (experts < 128 rows)",
+               "fp8": "FP8-weight GEMM1 + SwiGLU"}
+    roof["kernel"] = f"{DOMINANT}: " + kernels.get(r["plan_up"], r["plan_up"])
+    roof["algorithmic_flops_per_launch"] = fl
+    roof["algorithmic_bytes_per_launch"] = by
+    roof["avg_launch_ms"] = ms
+    roof["timing"] = "HIP events on the launch stream around each call, mean over the timed steps"
+    tr, note = load_stored(args, "traffic", wl.name)
+    if tr is not None and r["fp8"] is False:
+        roof["traffic"] = round(tr["passes"][DOMINANT]["bytes"])
+        roof["traffic_note"] = f"rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by a 1 GiB copy ({note})"
     else:
-        bound, achieved, peak, unit = ("hbm", dom_by / (dom_ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s")
-    if wl.dtype != "bf16":
-        kernel = f"{DOMINANT}: gemm_f32_kernel<SwiGLU>"
-    elif layer.plan.max_rows // wl.E_loc <= 48:   # the launcher's few-rows rule
-        kernel = (f"{DOMINANT}: gemm_bf16_kernel<SwiGLU{', FP8 weights' if fp8 else ''}>, "
-                  "32-row tiles over every row")
-    elif fp8:
-        kernel = f"{DOMINANT}: gemm_bf16_kernel<SwiGLU, FP8 weights>, 64-row tiles"
+        roof["traffic"] = None
+        roof["traffic_note"] = note
+    kt, note = load_stored(args, "kernel_times", wl.name)
+    if kt is not None and DOMINANT in kt["passes"]:
+        pm = kt["passes"][DOMINANT]["mean_us"] * 1e-3
+        pr = roofline_of(fl, by, pm)
+        roof["profile"] = {"avg_launch_ms": round(pm, 5), "achieved": pr["achieved"],
+                           "frac": pr["frac"], "file": note.replace("kernel_times_", "kernels_")
+                           .replace(".json", ".md"),
+                           "note": "kernel-trace duration of the pass per timed step in a "
+                                   "rocprofv3 run of the same sources (another run, maybe "
+                                   "another box)"}
     else:
-        kernel = f"{DOMINANT}: gemm_bf16_pipe<SwiGLU>, 256-row tiles (+ remainder tiles)"
-    roofline = {"bound": bound, "kernel": kernel,
-                "achieved": round(achieved, 1), "peak": peak, "unit": unit,
-                "frac": round(achieved / peak, 4),
-                "traffic": round(traffic) if traffic is not None else None,
-                "traffic_note": traffic_note,
-                "algorithmic_flops_per_launch": dom_fl,
-                "algorithmic_bytes_per_launch": dom_by, "avg_launch_ms": dom_ms}
+        roof["profile"] = None
+        roof["profile_note"] = note
+    return roof
+
+
+def traffic_per_pass(args, r):
+    tr, note = load_stored(args, "traffic", r["wl"].name)
+    if tr is None or r["fp8"]:
+        return None
+    out = {}
+    for p, rec in tr["passes"].items():
+        alg = r["model"].get(p, (0, 0))[1]
+        out[p] = {"counter_bytes": round(rec["bytes"]), "algorithmic_bytes": round(alg),
+                  "counter_over_algorithmic": round(rec["bytes"] / alg, 3) if alg else None}
+    return {"passes": out, "source": note}
+
+
+def summary_of(args, r):
+    """The compact record of a non-headline workload."""
+    wl = r["wl"]
+    out = {"workload": wl.name, "tokens": wl.T, "d_model": wl.d, "d_ff": wl.f, "experts": wl.E,
+           "local_experts": wl.E_loc, "top_k": wl.k, "dtype": wl.dtype, "capacity": r["C"],
+           "n_kept": r["n"], "rows_per_expert_min_max": r["rows_per_expert"],
+           "ms_per_step": round(r["ms_step"], 4),
+           "tokens_per_s": round(wl.T / (r["ms_step"] * 1e-3), 1),
+           "layer_tflops": round(r["flops"] / (r["ms_step"] * 1e-3) / 1e12, 2),
+           "layer_hbm_gbs": round(r["bytes"] / (r["ms_step"] * 1e-3) / 1e9, 1),
+           "per_step": r["per"], "mall_flushed_ms_per_step": round(r["cold_step"], 4),
+           "roofline": dominant_roofline(args, r), "traffic_per_pass": traffic_per_pass(args, r)}
+    if r["fused_ms"] is not None:
+        out["fused"] = {"ms_per_step_median": round(r["fused_ms"], 4),
+                        "unfused_ms_per_step_median": round(r["unfused_ms"], 4),
+                        "speedup_vs_unfused": round(r["unfused_ms"] / r["fused_ms"], 3)}
+    return out
+
+
+def main(argv=None):
+    args = parse(argv)
+    if args.traffic_from:
+        traffic_from(args)
+        return
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    if args.counters_from:
+        counters_from(args)
+        return
+    if args.trace_from:
+        trace_from(args)
+        return
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; "
+                                   f"--gpus {args.gpus} is not supported (the path is single-GPU)"}))
+        sys.exit(2)
+    import torch
+    from workloads import make
+
+    dev = torch.device("cuda:0")
+    if args.others is None:
+        others = list(OTHERS) if args.workload == HEADLINE else []
+    elif args.others == "none":
+        others = []
+    else:
+        others = [w for w in args.others.split(",") if w and w != args.workload]
+    weights = Weights(dev)
+    wl = make(args.workload)
+    r = run_workload(args, wl, weights, dev, headline=True)
+    ms_step = r["ms_step"]
+    roofline = dominant_roofline(args, r)
 
     training = None
-    if train:
-        if fp8 or args.reroute:
+    if args.backward:
+        if r["fp8"] or args.reroute:
             raise SystemExit("--backward takes native weights and plain top-k routing")
-        training = train_bench(args, wl, layer, x, logits, wg, w13_t, w2_t, n, touched, T_read, dev)
+        training = train_bench(args, wl, r["layer"], r["x"], r["logits"], r["wg"], r["w13_t"],
+                               r["w2_t"], r["n"], r["touched"], r["T_read"], dev)
 
     cpu = None
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle on {args.cpu_sample_tokens} tokens")
-        rate, dt, n_tok, passes = cpu_baseline(wl, host_w, args.cpu_sample_tokens)
+        rate, dt, n_tok, passes = cpu_baseline(wl, r["host_w"], args.cpu_sample_tokens)
         cpu = {"value": round(rate, 2), "unit": "tokens/s", "cores": _CORES, "kind": "oracle",
                "sample": f"first {n_tok} of {wl.T} tokens of {wl.name} (capacity rule applied "
                          f"to the sample), whole layer in float64 (router..combine), "
                          f"{passes} pass(es), {dt:.1f} s timed"}
-
+    head_summary = {k: r[k] for k in ("fused_ms", "unfused_ms")}
+    smi_before, smi_after = r["smi"]
+    copy_ms = r["copy_ms"]
+    tflops = r["flops"] / (ms_step * 1e-3) / 1e12
+    gbs = r["bytes"] / (ms_step * 1e-3) / 1e9
     line = {
         "metric": METRIC, "value": round(wl.T / (ms_step * 1e-3), 1), "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
@@ -659,14 +915,16 @@ def main():
         "dtype": "bf16" if wl.dtype == "bf16" else "f32", "data": "synthetic",
         "config": {"workload": wl.name, "tokens": wl.T, "d_model": wl.d, "d_ff": wl.f,
                    "experts": wl.E, "local_experts": wl.E_loc, "top_k": wl.k, "gate": wl.gate,
-                   "capacity": C, "parallelism": "single GPU",
-                   "weights": "e4m3 codes, fp32 scale per 128x128 block" if fp8 else wl.dtype,
-                   "routing": "top-k with overflow rerouting" if args.reroute else "top-k"},
+                   "capacity": r["C"], "parallelism": "single GPU",
+                   "weights": "e4m3 codes, fp32 scale per 128x128 block" if r["fp8"] else wl.dtype,
+                   "routing": "top-k with overflow rerouting" if r["reroute"] else "top-k",
+                   "rows_per_expert_min_max": r["rows_per_expert"], "n_kept": r["n"]},
         "layer_tflops": round(tflops, 2), "layer_mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
         "layer_hbm_gbs": round(gbs, 1), "layer_hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
-        "per_step": per, "roofline": roofline, "cpu_baseline": cpu,
-        "mall_flushed": {"ms_per_step_median": round(cold_step, 4),
-                         "per_step_median": cold,
+        "per_step": r["per"], "roofline": roofline, "traffic_per_pass": traffic_per_pass(args, r),
+        "cpu_baseline": cpu,
+        "mall_flushed": {"ms_per_step_median": round(r["cold_step"], 4),
+                         "per_step_median": r["cold"],
                          "note": "1 GiB written between steps (outside the events) to evict "
                                  "the 256 MB Infinity Cache; HIP-event times per call"},
         "hbm_copy_reference": {"gbs": round(2 * COPY_BYTES / (copy_ms * 1e-3) / 1e9, 1),
@@ -680,13 +938,21 @@ def main():
                                 "levels, socket power) just before and just after the timed "
                                 "steps"},
         "training": training,
-        "fused": None if fused_ms is None else {
-            "entry": "moe_forward_fused_reroute" if args.reroute else "moe_forward_fused",
-            "ms_per_step_median": round(fused_ms, 4),
-            "tokens_per_s": round(wl.T / (fused_ms * 1e-3), 1),
-            "unfused_ms_per_step_median": round(unfused_ms, 4),
-            "speedup_vs_unfused": round(unfused_ms / fused_ms, 3)},
+        "fused": None if head_summary["fused_ms"] is None else {
+            "entry": "moe_forward_fused_reroute" if r["reroute"] else "moe_forward_fused",
+            "ms_per_step_median": round(head_summary["fused_ms"], 4),
+            "tokens_per_s": round(wl.T / (head_summary["fused_ms"] * 1e-3), 1),
+            "unfused_ms_per_step_median": round(head_summary["unfused_ms"], 4),
+            "speedup_vs_unfused": round(head_summary["unfused_ms"] / head_summary["fused_ms"], 3)},
     }
+    del r
+    others_out = {}
+    for name in others:
+        wo = make(name)
+        ro = run_workload(args, wo, weights, dev, headline=False)
+        others_out[name] = summary_of(args, ro)
+        del ro
+    line["others"] = others_out or None
     print(json.dumps(line), flush=True)
 
 

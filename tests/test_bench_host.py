@@ -3,6 +3,7 @@ rocprofv3 databases, the stored-traffic bookkeeping, and the single-GPU rule.
 The databases are small synthetic sqlite files with the counter table the
 summaries read (one row per dispatch and counter)."""
 import contextlib
+import csv
 import io
 import json
 import os
@@ -65,35 +66,89 @@ def test_counters_summary(tmp_path):
 
 
 def test_traffic_from_scales_by_the_copy(tmp_path, monkeypatch):
-    # the copy's counters read 2x its true bytes, so the kernel's counts halve
+    # the copy's counters read 2x its true bytes, so the kernels' counts halve;
+    # each pass's bytes per call add up its kernels (two for a split GEMM1)
     copy_kib = 2.0 * bench.COPY_BYTES / 1024
+    tail = GEMM.replace("256, 256, 4, 0", "128, 256, 6, 4")
+    comb = "void moe::combine_kernel<true>(unsigned short const*)"
     d = tmp_path / "tr"
     for ctr, sub, kib in (("FETCH_SIZE", "fetch", 4096.0), ("WRITE_SIZE", "write", 1024.0)):
         write_db(str(d / sub / "k_results.db"),
-                 [(1, GEMM, ctr, kib), (2, GEMM, ctr, kib), (3, COPY, ctr, 5.0)])
+                 [(1, GEMM, ctr, kib), (2, GEMM, ctr, kib), (3, tail, ctr, 10.0),
+                  (4, comb, ctr, 6.0), (5, COPY, ctr, 5.0)])
         write_db(str(d / ("copy_" + sub) / "c_results.db"),
                  [(1, COPY, ctr, copy_kib), (2, COPY, ctr, copy_kib)])
-    dst = tmp_path / "traffic.json"
-    args = SimpleNamespace(traffic_from=str(d), traffic=str(dst), workload="mixtral_prefill")
+    args = SimpleNamespace(traffic_from=str(d), profiles_dir=str(tmp_path), workload="mixtral_prefill")
     run_quiet(bench.traffic_from, args)
+    dst = tmp_path / "traffic_mixtral_prefill.json"
     t = json.loads(dst.read_text())
-    up = t[bench.DOMINANT]
-    assert up["fetch_bytes"] == pytest.approx(4096.0 * 1024 / 2)
-    assert up["write_bytes"] == pytest.approx(1024.0 * 1024 / 2)
+    up = t["passes"][bench.DOMINANT]
+    assert up["fetch_bytes"] == pytest.approx((4096.0 + 10.0) * 1024 / 2)
+    assert up["write_bytes"] == pytest.approx((1024.0 + 10.0) * 1024 / 2)
     assert up["bytes"] == pytest.approx(up["fetch_bytes"] + up["write_bytes"])
+    assert t["passes"]["combine"]["bytes"] == pytest.approx(2 * 6.0 * 1024 / 2)
+    assert "ffn_down" not in t["passes"]
     assert t["sources_sha256_16"] == bench.sources_hash()
 
     # the stored figure is used while the sources are unchanged, else dropped
-    load_args = SimpleNamespace(weights="native", traffic=str(dst), workload="mixtral_prefill")
-    val, note = bench.load_traffic(load_args)
-    assert val == pytest.approx(up["bytes"]) and "FETCH_SIZE" in note
-    assert bench.load_traffic(SimpleNamespace(weights="native", traffic=str(dst),
-                                              workload="dsv3_decode"))[0] is None
+    load_args = SimpleNamespace(weights="native", profiles_dir=str(tmp_path))
+    val, note = bench.load_stored(load_args, "traffic", "mixtral_prefill")
+    assert val["passes"][bench.DOMINANT]["bytes"] == pytest.approx(up["bytes"])
+    assert bench.load_stored(load_args, "traffic", "dsv3_decode")[0] is None
     monkeypatch.setattr(bench, "sources_hash", lambda: "0" * 16)
-    val, note = bench.load_traffic(load_args)
+    val, note = bench.load_stored(load_args, "traffic", "mixtral_prefill")
     assert val is None and "changed" in note
-    assert bench.load_traffic(SimpleNamespace(weights="fp8", traffic=str(dst),
-                                              workload="mixtral_prefill"))[0] is None
+    fp8 = SimpleNamespace(weights="fp8", profiles_dir=str(tmp_path))
+    assert bench.load_stored(fp8, "traffic", "mixtral_prefill")[0] is None
+
+
+def test_trace_summary_takes_the_timed_steps(tmp_path):
+    """warm-up steps, then timed steps, then cache-evicted steps: the summary
+    averages the timed steps of each pass, its kernels added per step."""
+    big = "void moe::gemm_bf16_pipe<true, 256, 256, 4, 3, false>(unsigned short const*)"
+    tail = "void moe::gemm_bf16_pipe<true, 128, 256, 6, 4, false>(unsigned short const*)"
+    comb = "void moe::combine_kernel<true>(unsigned short const*)"
+    W, K = 2, 3
+    rows, t = [], 1000
+    for step in range(W + 2 * K):
+        timed = W <= step < W + K
+        for name, us in ((big, 100 + (10 * step if timed else 500)), (tail, 20), (comb, 5)):
+            rows.append((t, t + int(us * 1000), name))
+            t += int(us * 1000) + 50
+    d = tmp_path / "kt" / "host" / "123"
+    d.mkdir(parents=True)
+    with open(d / "kt_kernel_trace.csv", "w", newline="") as fh:
+        w = csv.writer(fh)
+        w.writerow(["Kind", "Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        for s0, s1, n in rows:
+            w.writerow(["KERNEL_DISPATCH", n, s0, s1])
+    (tmp_path / "kt" / "bench.json").write_text(json.dumps(
+        {"per_step": {"ffn_up": {"ms": 0.141}, "combine": {"ms": 0.005}}}) + "\n")
+    args = SimpleNamespace(trace_from=str(tmp_path / "kt"), profiles_dir=str(tmp_path),
+                           workload="dsv3_prefill_zipf", steps=K, warmup=W)
+    run_quiet(bench.trace_from, args)
+    out = json.loads((tmp_path / "kernel_times_dsv3_prefill_zipf.json").read_text())
+    up = out["passes"]["ffn_up"]
+    assert up["launches_per_call"] == 2
+    assert up["per_step_us"] == pytest.approx([100 + 20 + 10 * s for s in range(W, W + K)])
+    assert up["mean_us"] == pytest.approx(120 + 10 * (W + 1))
+    assert out["passes"]["combine"]["mean_us"] == pytest.approx(5)
+    assert out["bench_event_mean_us"]["ffn_up"] == pytest.approx(141)
+    md = (tmp_path / "kernels_dsv3_prefill_zipf.md").read_text()
+    assert "gemm_bf16_pipe<true, 256, 256, 4, 3, false>" in md and "| ffn_up |" in md
+
+
+def test_roofline_of_picks_the_longer_bound():
+    # 2.5 TFLOP in 2 ms: MFMA bound 1 ms -> half the MFMA roofline
+    r = bench.roofline_of(2.5e12, 1e9, 2.0)
+    assert r["bound"] == "mfma" and r["frac"] == pytest.approx(0.5)
+    assert r["achieved"] == pytest.approx(1250.0)
+    # 16 GB in 4 ms: HBM bound 2 ms
+    r = bench.roofline_of(1e12, 16e9, 4.0)
+    assert r["bound"] == "hbm" and r["frac"] == pytest.approx(0.5) and r["achieved"] == 4000.0
+    assert bench.pass_of("void moe::permute_rows_kernel(int)") == "permute"
+    assert bench.pass_of("void moe::combine_backward_kernel<true>(int)") is None
+    assert bench.pass_of("void moe::gemm_bf16_kernel<32, 128, 64, 1, 4, false, 0, false>(x)") == "ffn_down"
 
 
 def test_more_than_one_gpu_is_refused():

@@ -160,6 +160,10 @@ def test_dispatch_flags_invalid_index():
     # a full 256-row block keep their short last block (44 or 88 rows) in the
     # large tiles, the 50-row experts go to the small tiles
     ("bf16", 1024, 512, [50] * 200 + [300] * 20 + [600] * 10 + [160] * 10 + [512] * 10 + [0] * 6),
+    # few tiles and more than 512 rows per expert by the host's bound: the up pass
+    # runs every row in 256-row tiles (K = d <= 4096), the down pass (K = f > 4096)
+    # 256-row tiles over the full blocks and 128-row remainder tiles (88, 6, 8 rows)
+    ("bf16", 128, 4160, [600, 600]), ("bf16", 192, 4352, [1030, 520]),
     ("f32", 128, 256, [17, 0, 111]), ("f32", 32, 48, [5, 70, 1]), ("f32", 12, 20, [3, 64, 65])])
 def test_expert_ffn(dtype, d, f, rows):
     log(f"ffn {dtype} d={d} f={f} rows={rows}")
@@ -184,8 +188,7 @@ def test_expert_ffn(dtype, d, f, rows):
             r0, r1 = offsets[i], offsets[i + 1]
             if r1 > r0:
                 w1, w3, _ = w(i)
-                xa = O.widen(x[r0:r1], dtype)
-                href = O.silu(xa @ w1) * (xa @ w3)
+                href = O.swiglu_hidden(O.widen(x[r0:r1], dtype), w1, w3)
                 assert O.rel_err(as64(h, dtype)[r0:r1], href) <= TOL[dtype]
 
 

@@ -4,7 +4,14 @@ launch configuration the benchmark times (MoELayer.forward).
 Routing, counts, offsets, sorted pairs, pair positions and the permuted rows
 are compared bit-exactly over the whole layer; expert outputs y are compared
 on sampled tokens that the oracle computes one at a time from the layer's
-definition (max|err|/max|ref| <= 1e-2 bf16, 1e-5 fp32).
+definition (max|err|/max|ref| <= 1e-2 bf16, 1e-5 fp32); and for chosen
+experts -- one from each kernel and row class the launch selects at that
+shape (the hottest expert of the skewed prefill, an expert below 128 rows
+that the remainder tiles take, one whose short last block rides along in the
+256-row tiles, a Mixtral-shaped expert whose last block goes to the
+remainder tiles of the 14336-deep second GEMM) -- every row of h and y_perm
+is compared with the oracle's FFN of that expert (DWDP page, key
+optimisations: the grouped GEMM + SwiGLU over all local experts).
 """
 import numpy as np
 import pytest
@@ -59,6 +66,56 @@ def check_outputs(wl, host, y, idx, w, pair_pos, tokens):
     assert err <= TOL[wl.dtype]
 
 
+def check_expert_rows(wl, host, out, plan, experts, why):
+    """Every row of h and y_perm of the chosen local experts against the
+    oracle's FFN on the same rows (the rows of x that the oracle's plan puts
+    in each expert's segment)."""
+    off, sp = np.asarray(plan["offsets"]), np.asarray(plan["sorted_pair"])
+    wfn = weights_fn(wl, host)
+    tol = TOL[wl.dtype]
+    for i in experts:
+        r0, r1 = int(off[i]), int(off[i + 1])
+        assert r1 > r0, f"expert {i} has no rows"
+        x64 = O.widen(O.permute(wl.x, sp[r0:r1], wl.k), wl.dtype)
+        w1, w3, w2 = wfn(i)
+        h_ref = O.swiglu_hidden(x64, w1, w3)
+        y_ref = O.expert_ffn(x64, np.array([0, r1 - r0]), lambda _: (w1, w3, w2))
+        eh = O.rel_err(as64(out["h"][r0:r1], wl.dtype), h_ref)
+        ey = O.rel_err(as64(out["y_perm"][r0:r1], wl.dtype), y_ref)
+        log(f"{wl.name}: expert {wl.e_begin + i} ({why[i]}), all {r1 - r0} rows: "
+            f"h rel err {eh:.3e}, y_perm rel err {ey:.3e}")
+        assert eh <= tol and ey <= tol
+
+
+def _split(pick):
+    return sorted(pick), pick
+
+
+def chosen_experts(name, counts, capacity):
+    """Local experts whose rows exercise each kernel / row class at this shape."""
+    n = counts if capacity < 0 else np.minimum(counts, capacity)
+    pick = {}
+    if name == "dsv3_prefill_zipf":
+        pick[int(np.argmax(n))] = "hottest, 256-row tiles"
+        small = np.nonzero((n > 0) & (n < 128))[0]
+        pick[int(small[np.argmin(n[small])])] = "fewest rows, remainder tiles"
+        ride = [e for e in np.nonzero((n > 256) & (n % 256 > 0) & (n % 256 < 128))[0] if e not in pick]
+        pick[int(min(ride, key=lambda e: n[e]))] = "short last block rides in the 256-row tiles"
+        mid = np.nonzero((n >= 128) & (n < 256))[0]
+        pick[int(mid[0])] = "one partial 256-row tile"
+    elif name == "mixtral_prefill":
+        tail = np.nonzero(n % 256 < 128)[0]
+        pick[int(tail[np.argmin(n[tail] % 256)])] = "last block in the remainder tiles of GEMM2"
+        big = np.nonzero(n % 256 >= 128)[0]
+        if len(big):
+            pick[int(big[0])] = "last block in a half-full 256-row tile"
+    else:
+        nz = np.nonzero(n)[0]
+        pick[int(nz[np.argmax(n[nz])])] = "most rows"
+        pick[int(nz[np.argmin(n[nz])])] = "fewest rows"
+    return pick
+
+
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("name", ["tiny_fp32", "ep_rank_share", "dsv3_decode", "dsv3_prefill_zipf"])
 def test_workload_with_given_logits(name):
@@ -83,9 +140,11 @@ def test_workload_with_given_logits(name):
     if name == "tiny_fp32":
         full = O.moe_layer(wl.x, wl.dtype, wl.logits, wl.k, wl.gate, weights_fn(wl, host), wl.E)
         assert O.rel_err(as64(y, wl.dtype), full["y"]) <= TOL["f32"]
+        assert O.rel_err(as64(out["y_perm"][:n], wl.dtype), full["y_perm"]) <= TOL["f32"]
     else:
-        toks = sampled_tokens(wl.T, ref["pair_pos"], wl.k, n=12 if wl.E >= 256 else 24)
+        toks = sampled_tokens(wl.T, ref["pair_pos"], wl.k, n=16 if wl.E >= 256 else 24)
         check_outputs(wl, host, y, idx, w, ref["pair_pos"], toks)
+        check_expert_rows(wl, host, out, ref, *_split(chosen_experts(name, counts, capacity_of(wl))))
     # a second pass is bitwise identical
     y1 = t_out(y).copy()
     layer.forward(x, logits=t_in(wl.logits, "f32"))
@@ -130,10 +189,15 @@ def test_mixtral_prefill_with_router():
     assert np.array_equal(t_out(gi2), idx)
     assert O.rel_err(t_out(gw2), w) <= 1e-6
     ref = O.dispatch(idx, wl.E)
-    if len(diff) == 0:
-        check_plan(out, ref, wl.T, wl.k)
-        n = ref["n_kept"]
-        assert np.array_equal(t_out(out["x_perm"])[:n], O.permute(wl.x, ref["sorted_pair"], wl.k))
+    # the dispatch of the GPU's own routing is deterministic: its plan and
+    # permuted rows are bit-exact whether or not a near-tie routed a token
+    # differently above
+    gref = O.dispatch(gidx, wl.E)
+    check_plan(out, gref, wl.T, wl.k)
+    n = gref["n_kept"]
+    assert np.array_equal(t_out(out["x_perm"])[:n], O.permute(wl.x, gref["sorted_pair"], wl.k))
+    check_expert_rows(wl, host, out, gref,
+                      *_split(chosen_experts("mixtral_prefill", gref["counts"], -1)))
     # sampled outputs: tokens routed identically on both sides, all oracle inputs
     skip = set(diff.tolist())
     toks = [t for t in sampled_tokens(wl.T, ref["pair_pos"], wl.k, n=32) if t not in skip]
@@ -169,5 +233,7 @@ def test_ep_rank_share_with_rerouting():
     assert np.array_equal(t_out(out["x_perm"])[:n], O.permute(wl.x, ref["sorted_pair"], wl.k))
     toks = sampled_tokens(wl.T, ref["pair_pos"], wl.k, n=24, seed=3)
     check_outputs(wl, host, y, idx, w, ref["pair_pos"], toks)
+    check_expert_rows(wl, host, out, ref,
+                      *_split(chosen_experts("ep_rank_share", ref["counts"][wl.e_begin:wl.e_end], C)))
     log("ep_rank_share with rerouting: fused layer")
     fused_matches_unfused(wl, w13, w2p, layer, x, t_in(wl.logits, "f32"), capacity=C)
