@@ -147,6 +147,28 @@ moe_status moe_route_reroute(const float* logits, int T, int E, int k, int gate,
                              int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes,
                              void* stream);
 
+/* Bytes of the library's fixed device scratch array (one per GPU, held until
+ * the process ends) used by moe_route_reroute_noalloc. */
+#define MOE_NOALLOC_SCRATCH_BYTES (4u << 20)
+
+/* moe_route_reroute for callers that cannot allocate device memory or pass a
+ * workspace (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same operation, outputs and bits, with the rerouting
+ * scratch (the k + 1 candidates per token and a bit per token) in the
+ * library's fixed device array instead of a workspace.  It allocates nothing
+ * and calls no allocating routine.  The scratch it needs,
+ * 2 * ceil256(4 T (k + 1)) + ceil256(8 ceil(T / 64)) bytes, must not exceed
+ * MOE_NOALLOC_SCRATCH_BYTES (about T (k + 1) <= 524000), else
+ * MOE_ERR_WORKSPACE with nothing enqueued.  The array needs no clearing
+ * (every call writes the scratch it reads before reading it), but every call
+ * on one GPU uses that GPU's one array: calls that overlap in time on one GPU
+ * (on different streams, or from different host threads) race and must be
+ * serialised by the caller.  The first call on a device looks the array's
+ * address up there (with that device current). */
+moe_status moe_route_reroute_noalloc(const float* logits, int T, int E, int k, int gate,
+                                     int capacity, int32_t* topk_idx, float* topk_w,
+                                     void* stream);
+
 /* Dispatch plan and permutation (ThunderEP page §2.1/§2.2: rows packed per
  * owner, per-expert index lists; NCCL EP page §2.2: compact expert-major
  * layout; sparse-activation page §2.3: capacity).

@@ -32,6 +32,7 @@ MOE_FFN_PLAN_BIG_ALL = 5
 MOE_FFN_PLAN_BIG_TAIL = 6
 MOE_FFN_PLAN_BIG_RIDE = 7
 MOE_MAX_K = 8
+MOE_NOALLOC_SCRATCH_BYTES = 4 << 20
 MOE_MAX_E = 1024
 
 _vp, _i, _i64, _sz, _i32p, _fp = C.c_void_p, C.c_int, C.c_int64, C.c_size_t, C.c_void_p, C.c_void_p
@@ -47,6 +48,7 @@ SIGNATURES = {
     "moe_router_logits": (_i, [_vp, _fp, _i, _i, _i, _fp, _vp]),
     "moe_route": (_i, [_fp, _i, _i, _i, _i, _i32p, _fp, _vp]),
     "moe_route_reroute": (_i, [_fp, _i, _i, _i, _i, _i, _i32p, _fp, _vp, _sz, _vp]),
+    "moe_route_reroute_noalloc": (_i, [_fp, _i, _i, _i, _i, _i, _i32p, _fp, _vp]),
     "moe_dispatch": (_i, [_i32p, _i, _i, _i, _i, _i, _i, _vp, _i, _i, _i32p, _i32p, _i32p, _i32p,
                           _i32p, _vp, _vp, _sz, _vp]),
     "moe_expert_ffn": (_i, [_vp, _i32p, _i, _i64, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),

@@ -84,6 +84,20 @@ moe_status launch_down(const void* h, const int32_t* offsets, int E_loc, int64_t
                                              static_cast<float*>(y), wlist, stream));
 }
 
+// the rerouting launches with their scratch (candidates [T][k+1] as expert
+// ids, then as logits, then one mask per 64 tokens; moe::reroute_ws_bytes)
+// starting at c
+moe_status launch_reroute_in(const float* logits, int T, int E, int k, int gate, int capacity,
+                             int32_t* topk_idx, float* topk_w, char* c, void* stream) {
+  const size_t n = static_cast<size_t>(T) * (k + 1);
+  const size_t cand_bytes = (n * sizeof(int32_t) + 255) & ~static_cast<size_t>(255);
+  int32_t* cand_e = reinterpret_cast<int32_t*>(c);
+  float* cand_v = reinterpret_cast<float*>(c + cand_bytes);
+  uint64_t* rerouted = reinterpret_cast<uint64_t*>(c + 2 * cand_bytes);
+  return hip_status(moe::launch_route_reroute(logits, T, E, k, gate, capacity, topk_idx, topk_w,
+                                              cand_e, cand_v, rerouted, stream));
+}
+
 }  // namespace
 
 namespace moe {
@@ -325,14 +339,26 @@ moe_status moe_route_reroute(const float* logits, int T, int E, int k, int gate,
     return MOE_ERR_MISALIGNED;
   const size_t off = moe::dispatch_ws_bytes(T, E);
   if (ws_bytes < off + moe::reroute_ws_bytes(T, k)) return MOE_ERR_WORKSPACE;
-  char* c = static_cast<char*>(ws) + off;
-  const size_t n = static_cast<size_t>(T) * (k + 1);
-  const size_t cand_bytes = (n * sizeof(int32_t) + 255) & ~static_cast<size_t>(255);
-  int32_t* cand_e = reinterpret_cast<int32_t*>(c);
-  float* cand_v = reinterpret_cast<float*>(c + cand_bytes);
-  uint64_t* rerouted = reinterpret_cast<uint64_t*>(c + 2 * cand_bytes);
-  return hip_status(moe::launch_route_reroute(logits, T, E, k, gate, capacity, topk_idx, topk_w,
-                                              cand_e, cand_v, rerouted, stream));
+  return launch_reroute_in(logits, T, E, k, gate, capacity, topk_idx, topk_w,
+                           static_cast<char*>(ws) + off, stream);
+}
+
+moe_status moe_route_reroute_noalloc(const float* logits, int T, int E, int k, int gate,
+                                     int capacity, int32_t* topk_idx, float* topk_w,
+                                     void* stream) {
+  moe_status st = check_topk(E, k);
+  if (st != MOE_OK) return st;
+  if (T < 0 || capacity < -1 || (gate != MOE_GATE_SOFTMAX_TOPK_RENORM &&
+                                 gate != MOE_GATE_SIGMOID_TOPK_NORM))
+    return MOE_ERR_INVALID_ARG;
+  if (moe::reroute_ws_bytes(T, k) > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+  if (T == 0) return MOE_OK;
+  if (!logits || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(logits) || !aligned16(topk_idx) || !aligned16(topk_w)) return MOE_ERR_MISALIGNED;
+  void* scratch = nullptr;
+  if (int e = moe::noalloc_scratch(&scratch)) return hip_status(e);
+  return launch_reroute_in(logits, T, E, k, gate, capacity, topk_idx, topk_w,
+                           static_cast<char*>(scratch), stream);
 }
 
 moe_status moe_ffn_up_list(const void* x_perm, const int32_t* offsets, int E_loc,

@@ -31,6 +31,9 @@ int launch_route_reroute(const float* logits, int T, int E, int k, int gate, int
                          uint64_t* rerouted, void* stream);
 // workspace bytes of the rerouting candidates, placed after the dispatch scratch
 size_t reroute_ws_bytes(int T, int k);
+// this device's address of the library's fixed scratch array
+// (MOE_NOALLOC_SCRATCH_BYTES, route.hip), looked up once per device
+int noalloc_scratch(void** ptr);
 int launch_dispatch(const int32_t* idx, int T, int E, int k, int capacity, int e_begin,
                     int e_end, const void* x, int d, int elem_bytes, int32_t* counts,
                     int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos, int32_t* n_kept,

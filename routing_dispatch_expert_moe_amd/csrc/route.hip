@@ -5,6 +5,8 @@
 // Top-k (same page §3.2 stage 2): the k largest fp32 logits per token, ties to
 // the lower expert index, best first; gates softmax-renormalised over the k,
 // or sigmoid normalised over the k.
+#include <mutex>
+
 #include "common.h"
 #include "launch.h"
 #include "reroute_dev.h"
@@ -169,6 +171,35 @@ __global__ __launch_bounds__(256) void reroute_finalize_kernel(
   const int t = blockIdx.x * 256 + threadIdx.x;
   if (t >= T) return;
   reroute_finalize_token<K>(cand_e, cand_v, rerouted, t, kc, gate, topk_idx, topk_w);
+}
+
+// The fixed scratch of moe_route_reroute_noalloc: one array per GPU, held
+// until the process ends.  Host code never passes the array's name to a
+// kernel (in host code it is a host-side stand-in, not a device address):
+// each device's address is looked up once, with that device current, and
+// kept here.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+}  // namespace
+
+int noalloc_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return static_cast<int>(e);
+  if (dev < 0 || dev >= kMaxScratchDevices) return static_cast<int>(hipErrorInvalidDevice);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return static_cast<int>(e);
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return 0;
 }
 
 int launch_route_reroute(const float* logits, int T, int E, int k, int gate, int capacity,
