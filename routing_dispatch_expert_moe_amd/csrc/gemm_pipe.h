@@ -337,8 +337,8 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
         for (int q = 0; q < NQ; ++q) acc[i][q] = f32x16_t{};
       // The K loop of one tile.  ACT = false: this wave's rows of the tile
       // are all past the segment (a tile less than half full), so it only
-      // helps with the loads and barriers and leaves its SIMD's MFMA pipe to
-      // the other wave there.
+      // helps with the loads and barriers and issues no MFMAs (with 8 waves
+      // it leaves its SIMD's MFMA pipe to the other wave there).
       auto run_tile = [&](auto act) {
         constexpr bool ACT = decltype(act)::value;
         // one step: substep 0 fetches substep 1's fragments and the second
@@ -386,12 +386,8 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
           substep1(s0 + kt, more ? (kt + STAGES - KT) * kStepBytes : (KT - 1) * kStepBytes);
         }
       };
-      if constexpr (NW == 8) {
-        if (wm * (BM / 2) < ct.seg1 - ct.m0) run_tile(std::true_type{});
-        else run_tile(std::false_type{});
-      } else {
-        run_tile(std::true_type{});
-      }
+      if (wm * (BM / 2) < ct.seg1 - ct.m0) run_tile(std::true_type{});
+      else run_tile(std::false_type{});
       epilogue(ct, acc);
     }
   } else {
