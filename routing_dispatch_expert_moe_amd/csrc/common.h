@@ -14,6 +14,8 @@ constexpr int kWave = 64;
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // bf16 bit pattern -> fp32 (exact)
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {

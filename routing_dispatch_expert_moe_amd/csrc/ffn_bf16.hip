@@ -444,8 +444,26 @@ namespace moe {
 
 // FP8 weights: few rows per expert (decode) run the code-streaming kernel
 // (fp8.hip: codes in LDS, 32-row tiles, three workgroups per CU); more rows
-// stage bf16 weight tiles with 64-row tiles so each is re-read less often.
-// Row counts stay on the device.
+// run the pipelined kernels with the bf16 pass's tiles and row classes (codes
+// in LDS; see fp8_pipe_pass), or, for K below their pipeline depth, register-staged 64-row
+// tiles that convert codes to bf16 as they stage them.  Row counts stay on
+// the device.
+static int fp8_pipe_pass(bool up, const void* A, const int32_t* offsets, int E_loc,
+                         int64_t max_rows, int d, int f, const uint8_t* wq, const float* ws,
+                         void* C, void* stream) {
+  const int N = up ? f : d, K = up ? d : f;
+  auto run = [&](PipeRows r) {
+    return launch_gemm_pipe_fp8(r, up, A, offsets, E_loc, max_rows, wq, ws, C, N, K, stream);
+  };
+  // 256-row tiles over every row, except for long-K passes with few tiles,
+  // whose short remainders take 128-row tiles as in the bf16 pass (the FP8
+  // 128-row tiles run one wave per SIMD and measured slower elsewhere)
+  if (ffn_plan_bf16(up, max_rows, E_loc, d, f, device_cu_count()) == MOE_FFN_PLAN_BIG_TAIL) {
+    int e = run(PipeRows::kBigTiles);
+    return e != 0 ? e : run(PipeRows::kTailTiles);
+  }
+  return run(PipeRows::kBigAll);
+}
 int launch_ffn_up_fp8(const void* x_perm, const int32_t* offsets, int E_loc, int64_t max_rows,
                       int d, int f, const uint8_t* w13q, const float* w13s, void* h,
                       void* stream) {
@@ -453,6 +471,8 @@ int launch_ffn_up_fp8(const void* x_perm, const int32_t* offsets, int E_loc, int
   if (max_rows == 0) return 0;
   if (max_rows / E_loc <= kStreamRows)
     return launch_gemm_fp8w(true, x_perm, offsets, E_loc, max_rows, w13q, w13s, h, f, d, stream);
+  if (d >= fp8_pipe_min_k() && ffn_operands_fit32(true, max_rows, d, f))
+    return fp8_pipe_pass(true, x_perm, offsets, E_loc, max_rows, d, f, w13q, w13s, h, stream);
   return launch_gemm<64, 128, 64, 2, 2, true, ROWS_ALL, true>(x_perm, offsets, E_loc, max_rows,
                                                               w13q, h, f, d, s, w13s);
 }
@@ -464,6 +484,8 @@ int launch_ffn_down_fp8(const void* h, const int32_t* offsets, int E_loc, int64_
   if (max_rows == 0) return 0;
   if (max_rows / E_loc <= kStreamRows)
     return launch_gemm_fp8w(false, h, offsets, E_loc, max_rows, w2q, w2s, y, d, f, stream);
+  if (f >= fp8_pipe_min_k() && ffn_operands_fit32(false, max_rows, d, f))
+    return fp8_pipe_pass(false, h, offsets, E_loc, max_rows, d, f, w2q, w2s, y, stream);
   return launch_gemm<64, 128, 64, 2, 2, false, ROWS_ALL, true>(h, offsets, E_loc, max_rows, w2q,
                                                                y, d, f, s, w2s);
 }

@@ -25,6 +25,75 @@ __global__ __launch_bounds__(pipe_waves<BM>() * 64, 1) void gemm_bf16_pipe(const
       AB);
 }
 
+// FP8 weights with many rows per expert: the bf16 kernels' tiles with the
+// weight tiles held in LDS as codes (a step's stage is 24 KB for 256-row
+// tiles, five stages; 16 KB for the 128-row remainder tiles, eight)
+template <int BM>
+constexpr int fp8_stages() { return BM == 256 ? 5 : 8; }
+
+template <bool SWIGLU, int BM, int CLASS>
+__global__ __launch_bounds__(pipe_waves<BM>() * 64, 1) void gemm_fp8_pipe(
+    const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets, int E_loc,
+    const uint8_t* __restrict__ Wq, const float* __restrict__ Ws, uint16_t* __restrict__ C,
+    int N, int K) {
+  extern __shared__ uint4 lds[];
+  __shared__ int prefix[MOE_MAX_E + 1];
+  __shared__ int segs[MOE_MAX_E + 1];
+  gemm_pipe_body<SWIGLU, BM, 256, fp8_stages<BM>(), CLASS, pipe_waves<BM>(), false, true>(
+      A, offsets, E_loc, reinterpret_cast<const uint16_t*>(Wq), C, N, K, blockIdx.x, gridDim.x,
+      lds, prefix, segs, nullptr, 1, nullptr, nullptr, Ws);
+}
+
+int fp8_pipe_min_k() { return fp8_stages<128>() * kBK; }
+
+namespace {
+
+template <bool SWIGLU, int BM, int CLASS>
+int launch_fp8(const void* A, const int32_t* offsets, int E_loc, int64_t max_rows,
+               const uint8_t* Wq, const float* Ws, void* C, int N, int K, hipStream_t s) {
+  constexpr size_t lds = pipe_lds_bytes(BM, 256, fp8_stages<BM>(), true);
+  static_assert(lds + 2 * (MOE_MAX_E + 1) * 4 <= 160 * 1024, "LDS budget");
+  auto kern = gemm_fp8_pipe<SWIGLU, BM, CLASS>;
+  static LdsAttr attr;
+  if (int rc = set_dynamic_lds_once(reinterpret_cast<const void*>(kern), lds, attr)) return rc;
+  const int BN = SWIGLU ? 128 : 256;
+  const int64_t NT = (N + BN - 1) / BN;
+  int64_t tiles_ub = (max_rows / BM + E_loc) * NT;
+  if (is_tail_class(CLASS)) tiles_ub = static_cast<int64_t>(E_loc) * ((kTailMax + BM - 1) / BM) * NT;
+  int64_t grid = device_cu_count();
+  if (grid > tiles_ub) grid = tiles_ub;
+  if (grid >= 8) grid &= ~static_cast<int64_t>(7);
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(pipe_waves<BM>() * 64), lds, s,
+                     static_cast<const uint16_t*>(A), offsets, E_loc, Wq, Ws,
+                     static_cast<uint16_t*>(C), N, K);
+  return static_cast<int>(hipGetLastError());
+}
+
+template <bool SWIGLU>
+int launch_fp8_kind(PipeRows rows, const void* A, const int32_t* offsets, int E_loc,
+                    int64_t max_rows, const uint8_t* Wq, const float* Ws, void* C, int N, int K,
+                    hipStream_t s) {
+  switch (rows) {
+    case PipeRows::kBigTiles:
+      return launch_fp8<SWIGLU, 256, ROWS_BIG>(A, offsets, E_loc, max_rows, Wq, Ws, C, N, K, s);
+    case PipeRows::kTailTiles:
+      return launch_fp8<SWIGLU, 128, ROWS_TAIL>(A, offsets, E_loc, max_rows, Wq, Ws, C, N, K, s);
+    default:
+      return launch_fp8<SWIGLU, 256, ROWS_ALL>(A, offsets, E_loc, max_rows, Wq, Ws, C, N, K, s);
+  }
+}
+
+}  // namespace
+
+int launch_gemm_pipe_fp8(PipeRows rows, bool swiglu, const void* A, const int32_t* offsets,
+                         int E_loc, int64_t max_rows, const uint8_t* Wq, const float* Ws, void* C,
+                         int N, int K, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (swiglu) return launch_fp8_kind<true>(rows, A, offsets, E_loc, max_rows, Wq, Ws, C, N, K, s);
+  return launch_fp8_kind<false>(rows, A, offsets, E_loc, max_rows, Wq, Ws, C, N, K, s);
+}
+
 namespace {
 
 template <bool SWIGLU, int BM, int BNW, int STAGES, int CLASS, bool SAVE>

@@ -103,9 +103,10 @@ __device__ __forceinline__ Tile decode_tile(int t, int NT, const int* prefix, co
 
 using namespace pipe;
 
-// dynamic LDS bytes of gemm_pipe_body<..., BM, BNW, STAGES, ...>
-constexpr size_t pipe_lds_bytes(int BM, int BNW, int STAGES) {
-  return static_cast<size_t>(STAGES) * (BM + BNW) * kBK * sizeof(uint16_t);
+// dynamic LDS bytes of gemm_pipe_body<..., BM, BNW, STAGES, ...> (FP8W: the
+// weight rows of a step are 32 one-byte codes instead of 32 bf16 values)
+constexpr size_t pipe_lds_bytes(int BM, int BNW, int STAGES, bool fp8w = false) {
+  return static_cast<size_t>(STAGES) * (BM + (fp8w ? BNW / 2 : BNW)) * kBK * sizeof(uint16_t);
 }
 
 // One workgroup's share of the grouped GEMM: workgroup `bid` of `G` walks its
@@ -120,7 +121,25 @@ constexpr size_t pipe_lds_bytes(int BM, int BNW, int STAGES) {
 // SAVE (SwiGLU only): the pre-activations are also stored, a = A W1 at
 // AB[row][col] and g = A W3 at AB[row][N + col] (row pitch 2N), rounded to
 // bf16, for the backward pass.
-template <bool SWIGLU, int BM, int BNW, int STAGES, int CLASS, int NW = 4, bool SAVE = false>
+// FP8W: W holds E4M3 codes (one byte per weight, same packed layout) and Ws
+// one fp32 scale per 128 x 128 block ([E][rows / 128][K / 128]) (NCCL EP page
+// §2.1: FP8 expert compute with a scale tensor).  The codes go to LDS as they
+// are (half the bytes of bf16 weights); each MFMA operand is converted from 8
+// codes to 8 bf16 values (exact: every E4M3 value is a bf16 value) just
+// before the MFMAs that use it, so the MFMAs accumulate code x activation
+// products.  The running sum is kept in units of the current
+// 128-deep K block's scale: after block kb, acc *= s_kb / s_(kb+1) for each
+// MFMA tile (s_KB = 1; a 32 x 32 tile's weight rows lie in one 128-row
+// block, so its scale is one number).  The result is sum_kb s_kb x (block
+// kb's partial sum), the dequantised weights' product re-associated, with one
+// fp32 rounding per block and no second set of accumulators.  K must be at
+// least STAGES steps deep and a multiple of 128.  A weight row of a step is 32
+// bytes, two 16-byte halves fetched by two neighbouring lanes (a 64-lane
+// direct load covers 32 rows); in LDS row r's half c sits at position
+// c ^ ((r >> 3) & 1) of the row, so the 16 rows one 16-lane phase of a
+// fragment read touches cover every bank once.
+template <bool SWIGLU, int BM, int BNW, int STAGES, int CLASS, int NW = 4, bool SAVE = false,
+          bool FP8W = false>
 __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
                                                const int32_t* __restrict__ offsets, int E_loc,
                                                const uint16_t* __restrict__ W,
@@ -129,18 +148,23 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
                                                const int32_t* __restrict__ gather = nullptr,
                                                int gk = 1,
                                                const uint16_t* const* __restrict__ wlist = nullptr,
-                                               uint16_t* __restrict__ AB = nullptr) {
+                                               uint16_t* __restrict__ AB = nullptr,
+                                               const float* __restrict__ Ws = nullptr) {
   static_assert(SWIGLU || !SAVE, "pre-activations exist only with SwiGLU");
+  static_assert(!FP8W || !SAVE, "FP8 weights have no training forward");
   constexpr int BN = SWIGLU ? BNW / 2 : BNW;  // output columns per tile
   constexpr int HALF = BNW / 2;               // SwiGLU: W1 rows (then as many W3 rows)
   constexpr int FM = BM / 64;                 // 32-row MFMA blocks per wave
   constexpr int WN = NW / 2;                  // waves along the weight rows (2 along M)
   constexpr int NQ = BNW / WN / 32;           // 32-column MFMA blocks per wave
   constexpr int LA = BM / kRPI / NW;          // A loads per wave per step
-  constexpr int LB = BNW / kRPI / NW;         // B loads per wave per step
+  // B loads per wave per step (FP8W: 64 lanes x 16 codes cover 32 rows x 32 K)
+  constexpr int LB = FP8W ? BNW * 2 / 64 / NW : BNW / kRPI / NW;
   constexpr int LSTEP = LA + LB;
-  constexpr int STAGE_U4 = (BM + BNW) * kKC;
-  static_assert(FM >= 1 && NQ >= 2 && LB % kSUB == 0, "unsupported tile");
+  constexpr int BROW_U4 = FP8W ? 2 : kKC;     // 16-byte chunks per weight row per step
+  constexpr int STAGE_U4 = BM * kKC + BNW * BROW_U4;
+  static_assert(FM >= 1 && NQ >= 2 && LB >= 1 && (FP8W || LB % kSUB == 0), "unsupported tile");
+  static_assert(!FP8W || (BNW * 2) % (64 * NW) == 0, "FP8 weight loads must tile the step");
   for (int i = threadIdx.x; i <= E_loc; i += blockDim.x) segs[i] = offsets[i];
   mtile_prefix<BM, CLASS>(offsets, E_loc, prefix);  // ends with a barrier
   const int NT = (N + BN - 1) / BN;
@@ -175,7 +199,10 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
   uint32_t aoff[LA], boff[LB];
   auto set_issue_tile = [&](int j) {
     const Tile t = decode_tile<BM, BN, CLASS>(vb + j * G, NT, prefix, segs, E_loc);
-    iWb = reinterpret_cast<const char*>(wlist != nullptr ? wlist[t.e] : W + t.e * wstride);
+    if constexpr (FP8W)
+      iWb = reinterpret_cast<const char*>(W) + t.e * wstride;  // one byte per code
+    else
+      iWb = reinterpret_cast<const char*>(wlist != nullptr ? wlist[t.e] : W + t.e * wstride);
 #pragma unroll
     for (int i = 0; i < LA; ++i) {
       const int rt = (i * NW + wave) * kRPI + lane / kKC;  // row within the tile
@@ -185,11 +212,22 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
     }
 #pragma unroll
     for (int i = 0; i < LB; ++i) {
-      const int rt = (i * NW + wave) * kRPI + lane / kKC;
-      int wrow;
-      if (SWIGLU) wrow = (rt / HALF) * N + min(t.n0 + rt % HALF, N - 1);
-      else wrow = min(t.n0 + rt, N - 1);
-      boff[i] = (static_cast<uint32_t>(wrow) * K + lkc * 8) * 2u;
+      if constexpr (FP8W) {
+        // 16-byte slot (i * NW + wave) * 64 + lane: position p of tile row rt,
+        // holding that row's K half c = p ^ ((rt >> 3) & 1)
+        const int slot = (i * NW + wave) * 64 + lane;
+        const int rt = slot >> 1, c = (slot & 1) ^ ((rt >> 3) & 1);
+        int wrow;
+        if (SWIGLU) wrow = (rt / HALF) * N + min(t.n0 + rt % HALF, N - 1);
+        else wrow = min(t.n0 + rt, N - 1);
+        boff[i] = static_cast<uint32_t>(wrow) * K + c * 16u;
+      } else {
+        const int rt = (i * NW + wave) * kRPI + lane / kKC;
+        int wrow;
+        if (SWIGLU) wrow = (rt / HALF) * N + min(t.n0 + rt % HALF, N - 1);
+        else wrow = min(t.n0 + rt, N - 1);
+        boff[i] = (static_cast<uint32_t>(wrow) * K + lkc * 8) * 2u;
+      }
     }
     it_tile = j;
   };
@@ -202,10 +240,11 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
       __builtin_amdgcn_global_load_lds(
           (const __attribute__((address_space(1))) void*)(Ab + (aoff[i] + koff)),
           (__attribute__((address_space(3))) void*)(As + (i * NW + wave) * 64), 16, 0, 0);
+    const uint32_t bkoff = FP8W ? koff / 2u : koff;  // codes: one byte per K
 #pragma unroll
     for (int i = p * LB / kSUB; i < (p + 1) * LB / kSUB; ++i)
       __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(iWb + (boff[i] + koff)),
+          (const __attribute__((address_space(1))) void*)(iWb + (boff[i] + bkoff)),
           (__attribute__((address_space(3))) void*)(Bs + (i * NW + wave) * 64), 16, 0, 0);
   };
   // byte offset along K of step p's operands, switching the issue tile when p
@@ -218,8 +257,11 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
     return static_cast<uint32_t>(kt) * kBK * 2u;
   };
 
-  // LDS fragments of substep ks of the step held in buffer `buf`
+  // LDS fragments of substep ks of the step held in buffer `buf` (FP8W: the
+  // weight fragments' 16 codes of both K halves as read, fbr, converted to fb
+  // by cvt_frags before the MFMAs that use them)
   bf16x8_t fa[2][FM], fb[2][NQ];
+  uint4 fbr[2][FP8W ? NQ : 1];
   auto load_frags = [&](int buf, int ks, int slot) {
     const uint4* As = lds + buf * STAGE_U4;
     const uint4* Bs = As + BM * kKC;
@@ -236,7 +278,38 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
         const int q = SWIGLU ? ((i / (NQ / 2)) * HALF + wn * (HALF / WN) + (i % (NQ / 2)) * 32 +
                                 (lane & 31))
                              : (wn * (BNW / WN) + i * 32 + (lane & 31));
-        fb[slot][i] = __builtin_bit_cast(bf16x8_t, Bs[q * kKC + (ch ^ swz(q))]);
+        if constexpr (FP8W)
+          fbr[slot][i] = Bs[q * 2 + (ks ^ ((q >> 3) & 1))];
+        else
+          fb[slot][i] = __builtin_bit_cast(bf16x8_t, Bs[q * kKC + (ch ^ swz(q))]);
+      }
+    }
+  };
+  // FP8W: the scale of this wave's MFMA tile q (its weight rows' 128-row
+  // block) in K block kb
+  constexpr int kScaleBlock = 128;
+  const int RB = (SWIGLU ? 2 * N : N) / kScaleBlock, KB = K / kScaleBlock;
+  auto frag_scale = [&](const Tile& ct, int q, int kb) -> float {
+    int wrow = SWIGLU ? (q / (NQ / 2)) * N + ct.n0 + wn * (HALF / WN) + (q % (NQ / 2)) * 32
+                      : ct.n0 + wn * (BNW / WN) + q * 32;
+    if (!SWIGLU) wrow = min(wrow, N - 1);  // columns past N are computed and dropped
+    return Ws[(static_cast<size_t>(ct.e) * RB + wrow / kScaleBlock) * KB + kb];
+  };
+  // FP8W: codes of slot `slot` to bf16 operands; lanes 0..31 take codes 0..7
+  // of their 16, lanes 32..63 codes 8..15 (the K halves of the 32 x 32 x 16
+  // operand), two codes per conversion
+  auto cvt_frags = [&](int slot) {
+    if constexpr (FP8W) {
+      const bool hi = lane >= 32;
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        const uint4 v = fbr[slot][q];
+        const int w0 = static_cast<int>(hi ? v.z : v.x), w1 = static_cast<int>(hi ? v.w : v.y);
+        fb[slot][q] = __builtin_bit_cast(bf16x8_t, make_uint4(
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.f, false)),
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.f, true)),
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.f, false)),
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.f, true))));
       }
     }
   };
@@ -268,6 +341,19 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
 #pragma unroll
       for (int q = 0; q < NQ; ++q)
         acc[i][q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i], fb[slot][q], acc[i][q], 0, 0, 0);
+  };
+  // FP8W: after the last step of K block kb, acc *= s_kb / s_(kb+1) per MFMA
+  // tile (s_KB = 1).  sc holds s_kb and s_(kb+1) of each tile; the scales of
+  // block kb + 2 are loaded here, a whole block before they are used.
+  auto rescale = [&](const Tile& ct, int kb, f32x16_t (&acc)[FM][NQ], float (&sc)[2][NQ]) {
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const float r = kb + 1 < KB ? sc[0][q] / sc[1][q] : sc[0][q];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) acc[i][q] *= r;
+      sc[0][q] = sc[1][q];
+      sc[1][q] = kb + 2 < KB ? frag_scale(ct, q, kb + 2) : 1.f;
+    }
   };
   auto epilogue = [&](const Tile& ct, f32x16_t (&acc)[FM][NQ]) {
     const int valid = min(BM, ct.seg1 - ct.m0);
@@ -335,6 +421,15 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int q = 0; q < NQ; ++q) acc[i][q] = f32x16_t{};
+      // FP8W: the block scales of K blocks 0 and 1 of this tile's MFMA tiles
+      float sc[2][NQ];
+      if constexpr (FP8W) {
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+          sc[0][q] = frag_scale(ct, q, 0);
+          sc[1][q] = KB > 1 ? frag_scale(ct, q, 1) : 1.f;
+        }
+      }
       // The K loop of one tile.  ACT = false: this wave's rows of the tile
       // are all past the segment (a tile less than half full), so it only
       // helps with the loads and barriers and issues no MFMAs (with 8 waves
@@ -350,6 +445,7 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
           if constexpr (ACT) load_frags(s % STAGES, 1, 1);
           issue_part(1, pb, pk);
           if constexpr (ACT) {
+            cvt_frags(0);
             mfma_substep(acc, 0);
             interleave<0, NMF, NDS, NVM>();
           }
@@ -363,10 +459,15 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
           issue_part(0, pb, pk);
           load_frags((s + 1) % STAGES, 0, 0);
           if constexpr (ACT) {
+            cvt_frags(1);
             mfma_substep(acc, 1);
             interleave<0, NMF, NDS, NVM>();
           }
           __builtin_amdgcn_sched_barrier(0);
+          if constexpr (ACT && FP8W) {
+            const int kt = s % KT;
+            if ((kt + 1) % (kScaleBlock / kBK) == 0) rescale(ct, kt / (kScaleBlock / kBK), acc, sc);
+          }
         };
         const int s0 = j * KT;
         for (int kt = 0; kt < KT - STAGES; ++kt) {
@@ -390,9 +491,10 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
       else run_tile(std::false_type{});
       epilogue(ct, acc);
     }
-  } else {
+  } else if constexpr (!FP8W) {
     // short K (fewer steps than stages): the issue side may run several
     // tiles ahead, so it switches tiles step by step
+    // (FP8W: never reached, the launcher requires K >= STAGES steps)
     for (int p = 0; p < STAGES - 1; ++p) {
       const uint32_t ko = issue_koff(p);
 #pragma unroll

@@ -80,6 +80,13 @@ constexpr int64_t kStreamRows = 48;
 // the kernels of one bf16 FFN half (up = GEMM1 + SwiGLU, else GEMM2): a
 // moe_ffn_plan_t value (include/moe.h)
 int ffn_plan_bf16(bool up, int64_t max_rows, int E_loc, int d, int f, int cu);
+// FP8 (E4M3-FN) weights with 128 x 128 block scales, many rows per expert:
+// the pipelined kernels of one row class with codes in LDS (K must be at
+// least fp8_pipe_min_k() and a multiple of 128; operands below 4 GiB)
+int fp8_pipe_min_k();
+int launch_gemm_pipe_fp8(PipeRows rows, bool swiglu, const void* A, const int32_t* offsets,
+                         int E_loc, int64_t max_rows, const uint8_t* Wq, const float* Ws, void* C,
+                         int N, int K, void* stream);
 // ab (SwiGLU only): if not null, the pre-activations are stored there too
 // ([rows][2N]: a then g)
 int launch_gemm_pipe_bf16(PipeRows rows, bool swiglu, const void* A, const int32_t* offsets,
@@ -94,6 +101,7 @@ int launch_ffn_up_train_f32(const float* x_perm, const int32_t* offsets, int E_l
                             int64_t max_rows, int d, int f, const float* w13, float* h, float* ab,
                             void* stream);
 // FP8 (E4M3-FN) weights with 128 x 128 block scales
+
 int launch_quantize_fp8(const void* w, int E_loc, int R, int K, uint8_t* q, float* scales,
                         void* stream);
 // few rows per expert: codes kept in LDS, converted per MFMA operand

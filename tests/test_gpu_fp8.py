@@ -76,8 +76,18 @@ def _host_packed(host, f):
 @pytest.mark.parametrize("d,f,rows", [
     (256, 384, [5, 0, 40, 1]),                    # few rows per expert: 32-row tiles
     (128, 256, [3, 1, 0, 7, 2, 9, 4, 11]),
-    (512, 256, [300, 0, 513]),                    # many rows: 128-row tiles, ragged tails
-    (384, 640, [129, 127, 256, 1]),
+    # many rows per expert and K >= 256: the pipelined kernel (codes in LDS,
+    # 128-row tiles, partial sums per 128-deep K block), ragged tiles
+    (512, 256, [300, 0, 513]), (384, 640, [129, 127, 256, 1]),
+    (1024, 2048, [700, 300, 0, 1100]), (256, 256, [129, 400, 77]),
+    # many rows and K = 128 (up) / 256 (down): register-staged 64-row tiles, then the pipe
+    (128, 256, [200, 90, 131]),
+    # the bf16 passes' row classes with FP8 weights: a 4224-deep second GEMM with few
+    # tiles (256-row tiles over full blocks, 128-row remainder tiles of 88 and 44 rows);
+    # 64 experts x 16 weight tiles (many tiles: short last blocks ride along in the
+    # 256-row tiles, the 50-row experts go to 128-row tiles)
+    (256, 4224, [600, 300]),
+    (256, 2048, [50] * 40 + [300] * 12 + [600] * 6 + [0] * 6),
 ])
 def test_expert_ffn_fp8(d, f, rows):
     log(f"ffn fp8 d={d} f={f} rows={rows}")
