@@ -95,16 +95,21 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(const int* __restri
   int local = 0;
   for (int i = 0; i < per; ++i)
     if (lo + i < E_loc) local += kept_s[e_begin + lo + i];
-  scan_s[threadIdx.x] = local;
-  __syncthreads();
-  // Hillis-Steele inclusive scan over the per-thread sums (integers: exact)
-  for (int off = 1; off < (int)blockDim.x; off <<= 1) {
-    int v = threadIdx.x >= off ? scan_s[threadIdx.x - off] : 0;
-    __syncthreads();
-    scan_s[threadIdx.x] += v;
-    __syncthreads();
+  // wave-level inclusive prefix sums of the per-thread sums (lane shuffles,
+  // no barrier), then each wave adds the totals of the waves before it
+  // (integers: exact)
+  const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+  int incl = local;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int v = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += v;
   }
-  int run = scan_s[threadIdx.x] - local;
+  if (lane == kWave - 1) scan_s[wv] = incl;  // wave totals
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wv; ++w) before += scan_s[w];
+  int run = before + incl - local;
   for (int i = 0; i < per; ++i) {
     if (lo + i < E_loc) {
       offsets[lo + i] = run;
@@ -112,8 +117,8 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(const int* __restri
     }
   }
   if (threadIdx.x == blockDim.x - 1) {
-    offsets[E_loc] = scan_s[threadIdx.x];
-    *n_kept = scan_s[threadIdx.x];
+    offsets[E_loc] = before + incl;
+    *n_kept = before + incl;
   }
 }
 

@@ -9,7 +9,7 @@ namespace moe {
 template <int BM>
 constexpr int pipe_waves() { return BM == 256 ? 8 : 4; }
 
-template <bool SWIGLU, int BM, int BNW, int STAGES, int CLASS, bool SAVE>
+template <bool SWIGLU, int BM, int BNW, int STAGES, int CLASS, bool SAVE, int BK>
 __global__ __launch_bounds__(pipe_waves<BM>() * 64, 1) void gemm_bf16_pipe(const uint16_t* __restrict__ A,
                                                          const int32_t* __restrict__ offsets,
                                                          int E_loc,
@@ -20,7 +20,7 @@ __global__ __launch_bounds__(pipe_waves<BM>() * 64, 1) void gemm_bf16_pipe(const
   extern __shared__ uint4 lds[];
   __shared__ int prefix[MOE_MAX_E + 1];
   __shared__ int segs[MOE_MAX_E + 1];
-  gemm_pipe_body<SWIGLU, BM, BNW, STAGES, CLASS, pipe_waves<BM>(), SAVE>(
+  gemm_pipe_body<SWIGLU, BM, BNW, STAGES, CLASS, pipe_waves<BM>(), SAVE, false, BK>(
       A, offsets, E_loc, W, C, N, K, blockIdx.x, gridDim.x, lds, prefix, segs, nullptr, 1, wlist,
       AB);
 }
@@ -96,13 +96,20 @@ int launch_gemm_pipe_fp8(PipeRows rows, bool swiglu, const void* A, const int32_
 
 namespace {
 
+// bf16 tiles step K 64 deep (whole 128-byte lines per row and load; K is a
+// multiple of 64 for bf16): 256 x 256 tiles in two 64 KB stages, 128 x 256
+// in three of 48 KB, 128 x 128 in four of 32 KB
+constexpr int kPipeBK = 64;
+
 template <bool SWIGLU, int BM, int BNW, int STAGES, int CLASS, bool SAVE>
 int launch_pipe(const void* A, const int32_t* offsets, int E_loc, int64_t max_rows, const void* W,
                 void* C, int N, int K, const void* const* wlist, void* AB, hipStream_t s) {
-  const size_t lds = pipe_lds_bytes(BM, BNW, STAGES);
-  static_assert(pipe_lds_bytes(BM, BNW, STAGES) + 2 * (MOE_MAX_E + 1) * 4 <= 160 * 1024,
+  constexpr int BK = kPipeBK;
+  const size_t lds = pipe_lds_bytes(BM, BNW, STAGES, false, BK);
+  static_assert(pipe_lds_bytes(BM, BNW, STAGES, false, BK) + 2 * (MOE_MAX_E + 1) * 4 <= 160 * 1024,
                 "LDS budget");
-  auto kern = gemm_bf16_pipe<SWIGLU, BM, BNW, STAGES, CLASS, SAVE>;
+  if (K % BK != 0) return static_cast<int>(hipErrorInvalidValue);
+  auto kern = gemm_bf16_pipe<SWIGLU, BM, BNW, STAGES, CLASS, SAVE, BK>;
   static LdsAttr attr;
   if (int rc = set_dynamic_lds_once(reinterpret_cast<const void*>(kern), lds, attr)) return rc;
   const int BN = SWIGLU ? BNW / 2 : BNW;
@@ -120,11 +127,12 @@ int launch_pipe(const void* A, const int32_t* offsets, int E_loc, int64_t max_ro
   return static_cast<int>(hipGetLastError());
 }
 
-// The few-row tiles are 128 activation rows by 128 weight rows with 8 stages
+// The few-row tiles are 128 activation rows by 128 weight rows with 4 stages
 // when the remainders would give few tiles (twice as many tiles as with 256
 // weight rows keeps every CU busy when only a few experts have remainders),
-// else 128 x 256 with 6 stages (half the re-reads of the activation rows).
-constexpr int kSmallBM = 128, kSmallBNW = 128, kSmallStages = 8;
+// else 128 x 256 with 3 stages (half the re-reads of the activation rows).
+constexpr int kSmallBM = 128, kSmallBNW = 128, kSmallStages = 4;
+constexpr int kBigStages = 2, kWideStages = 3;
 
 template <bool SWIGLU, bool SAVE>
 int launch_kind(PipeRows rows, const void* A, const int32_t* offsets, int E_loc, int64_t max_rows,
@@ -132,19 +140,19 @@ int launch_kind(PipeRows rows, const void* A, const int32_t* offsets, int E_loc,
                 hipStream_t s) {
   switch (rows) {
     case PipeRows::kBigTiles:
-      return launch_pipe<SWIGLU, 256, 256, 4, ROWS_BIG, SAVE>(A, offsets, E_loc, max_rows, W, C, N, K, wlist, AB, s);
+      return launch_pipe<SWIGLU, 256, 256, kBigStages, ROWS_BIG, SAVE>(A, offsets, E_loc, max_rows, W, C, N, K, wlist, AB, s);
     case PipeRows::kBigRide:
-      return launch_pipe<SWIGLU, 256, 256, 4, ROWS_BIGR, SAVE>(A, offsets, E_loc, max_rows, W, C, N, K, wlist, AB, s);
+      return launch_pipe<SWIGLU, 256, 256, kBigStages, ROWS_BIGR, SAVE>(A, offsets, E_loc, max_rows, W, C, N, K, wlist, AB, s);
     case PipeRows::kTailRide:
-      return launch_pipe<SWIGLU, 128, 256, 6, ROWS_TAILR, SAVE>(A, offsets, E_loc, max_rows, W, C, N,
+      return launch_pipe<SWIGLU, 128, 256, kWideStages, ROWS_TAILR, SAVE>(A, offsets, E_loc, max_rows, W, C, N,
                                                                  K, wlist, AB, s);
     case PipeRows::kAllRowsWide:
-      return launch_pipe<SWIGLU, 128, 256, 6, ROWS_ALL, SAVE>(A, offsets, E_loc, max_rows, W, C, N, K, wlist, AB, s);
+      return launch_pipe<SWIGLU, 128, 256, kWideStages, ROWS_ALL, SAVE>(A, offsets, E_loc, max_rows, W, C, N, K, wlist, AB, s);
     case PipeRows::kBigAll:
-      return launch_pipe<SWIGLU, 256, 256, 4, ROWS_ALL, SAVE>(A, offsets, E_loc, max_rows, W, C, N, K, wlist, AB, s);
+      return launch_pipe<SWIGLU, 256, 256, kBigStages, ROWS_ALL, SAVE>(A, offsets, E_loc, max_rows, W, C, N, K, wlist, AB, s);
     case PipeRows::kTailTiles: {
       if (!few_gemm_tiles(E_loc, N, SWIGLU, device_cu_count()))
-        return launch_pipe<SWIGLU, 128, 256, 6, ROWS_TAIL, SAVE>(A, offsets, E_loc, max_rows, W, C,
+        return launch_pipe<SWIGLU, 128, 256, kWideStages, ROWS_TAIL, SAVE>(A, offsets, E_loc, max_rows, W, C,
                                                                   N, K, wlist, AB, s);
       return launch_pipe<SWIGLU, kSmallBM, kSmallBNW, kSmallStages, ROWS_TAIL, SAVE>(
           A, offsets, E_loc, max_rows, W, C, N, K, wlist, AB, s);

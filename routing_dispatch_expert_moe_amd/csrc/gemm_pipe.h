@@ -15,16 +15,22 @@
 //             HBM and the smaller tile leaves LDS for a deeper pipeline.
 //
 // Memory pipeline: operands go HBM/L2 -> LDS directly (global_load_lds_dwordx4,
-// no staging registers) in K-steps of 32 through STAGES LDS buffers, so loads
-// run STAGES - 1 steps ahead of the MFMAs.  A step's loads are spread over the
-// MFMAs of the step before; MFMA operands are double buffered in registers
+// no staging registers) in K-steps of BK (32 or 64) through STAGES LDS
+// buffers, so loads run STAGES - 1 steps ahead of the MFMAs.  A step's loads
+// go out in two parts, right after the barrier that frees their buffer and
+// during the first substep; MFMA operands are double buffered in registers
 // (the next 16-deep substep's LDS reads overlap the current substep's MFMAs),
 // and each step's barrier sits under the last substep's MFMAs.  The load
 // stream runs across tile boundaries, so the next tile's operands are in
-// flight during the current tile's epilogue.  Rows are 64 bytes (4 chunks of
-// 16 B); chunk c of row r sits at chunk c ^ ((r >> 2) & 3), so each 16-lane
-// phase of a ds_read_b128 touches 16 distinct bank groups; the direct loads
-// realise this by choosing which global chunk each lane fetches.
+// flight during the current tile's epilogue.  A step's row is BK * 2 bytes in
+// 16-byte chunks; chunk c of row r sits at chunk c ^ swz(r) (BK = 32: 4
+// chunks, swz = (r >> 2) & 3; BK = 64: 8 chunks, swz = (r >> 1) & 7), so each
+// 16-lane phase of a ds_read_b128 touches 16 distinct bank groups; the direct
+// loads realise this by choosing which global chunk each lane fetches.  With
+// BK = 64 one load instruction covers 8 rows x 128 bytes, whole 128-byte
+// lines, where BK = 32 covers 16 rows x half a line: on gfx950 the whole-line
+// pattern keeps the MFMA pipes measurably busier with the same bytes in
+// flight, and halves the barriers per K.
 //
 // Rows: the rows of row class CLASS of each expert (tile_sched.h).
 //
@@ -43,10 +49,19 @@ namespace moe {
 
 namespace pipe {
 
-constexpr int kBK = 32;          // K depth of one pipeline step
+constexpr int kBK = 32;          // K depth of one pipeline step (default; FP8 weights)
 constexpr int kKC = kBK / 8;     // 16-byte chunks per 64-byte row
 constexpr int kRPI = 64 / kKC;   // rows covered by one 64-lane 16-byte load (16)
 constexpr int kSUB = kBK / 16;   // MFMA K-substeps per step (2)
+
+// LDS row swizzle of a step with KC 16-byte chunks per row: chunk c of row r
+// at c ^ swz(r), so 16 consecutive rows read at one chunk cover all 16
+// 16-byte bank groups of a 256-byte bank row
+template <int KC>
+__device__ __forceinline__ int step_swz(int r) {
+  static_assert(KC == 4 || KC == 8, "64- or 128-byte rows");
+  return KC == 4 ? (r >> 2) & 3 : (r >> 1) & 7;
+}
 
 __device__ __forceinline__ float silu_fast(float a) {
   return a * __builtin_amdgcn_rcpf(1.f + __expf(-a));
@@ -103,10 +118,10 @@ __device__ __forceinline__ Tile decode_tile(int t, int NT, const int* prefix, co
 
 using namespace pipe;
 
-// dynamic LDS bytes of gemm_pipe_body<..., BM, BNW, STAGES, ...> (FP8W: the
-// weight rows of a step are 32 one-byte codes instead of 32 bf16 values)
-constexpr size_t pipe_lds_bytes(int BM, int BNW, int STAGES, bool fp8w = false) {
-  return static_cast<size_t>(STAGES) * (BM + (fp8w ? BNW / 2 : BNW)) * kBK * sizeof(uint16_t);
+// dynamic LDS bytes of gemm_pipe_body<..., BM, BNW, STAGES, ..., BK> (FP8W:
+// the weight rows of a step are 32 one-byte codes instead of 32 bf16 values)
+constexpr size_t pipe_lds_bytes(int BM, int BNW, int STAGES, bool fp8w = false, int BK = kBK) {
+  return static_cast<size_t>(STAGES) * (BM + (fp8w ? BNW / 2 : BNW)) * BK * sizeof(uint16_t);
 }
 
 // One workgroup's share of the grouped GEMM: workgroup `bid` of `G` walks its
@@ -138,8 +153,10 @@ constexpr size_t pipe_lds_bytes(int BM, int BNW, int STAGES, bool fp8w = false) 
 // direct load covers 32 rows); in LDS row r's half c sits at position
 // c ^ ((r >> 3) & 1) of the row, so the 16 rows one 16-lane phase of a
 // fragment read touches cover every bank once.
+// BK: K depth of a pipeline step, 32 or 64 (64 needs K a multiple of 64; FP8W
+// takes 32).
 template <bool SWIGLU, int BM, int BNW, int STAGES, int CLASS, int NW = 4, bool SAVE = false,
-          bool FP8W = false>
+          bool FP8W = false, int BK = kBK>
 __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
                                                const int32_t* __restrict__ offsets, int E_loc,
                                                const uint16_t* __restrict__ W,
@@ -152,18 +169,24 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
                                                const float* __restrict__ Ws = nullptr) {
   static_assert(SWIGLU || !SAVE, "pre-activations exist only with SwiGLU");
   static_assert(!FP8W || !SAVE, "FP8 weights have no training forward");
+  static_assert(BK == 32 || BK == 64, "step depth");
+  static_assert(!FP8W || BK == 32, "FP8 weight steps are 32 deep");
+  constexpr int KC = BK / 8;                  // 16-byte chunks per row per step
+  constexpr int RPI = 64 / KC;                // rows covered by one 64-lane load
+  constexpr int SUB = BK / 16;                // MFMA K-substeps per step
   constexpr int BN = SWIGLU ? BNW / 2 : BNW;  // output columns per tile
   constexpr int HALF = BNW / 2;               // SwiGLU: W1 rows (then as many W3 rows)
   constexpr int FM = BM / 64;                 // 32-row MFMA blocks per wave
   constexpr int WN = NW / 2;                  // waves along the weight rows (2 along M)
   constexpr int NQ = BNW / WN / 32;           // 32-column MFMA blocks per wave
-  constexpr int LA = BM / kRPI / NW;          // A loads per wave per step
+  constexpr int LA = BM / RPI / NW;           // A loads per wave per step
   // B loads per wave per step (FP8W: 64 lanes x 16 codes cover 32 rows x 32 K)
-  constexpr int LB = FP8W ? BNW * 2 / 64 / NW : BNW / kRPI / NW;
+  constexpr int LB = FP8W ? BNW * 2 / 64 / NW : BNW / RPI / NW;
   constexpr int LSTEP = LA + LB;
-  constexpr int BROW_U4 = FP8W ? 2 : kKC;     // 16-byte chunks per weight row per step
-  constexpr int STAGE_U4 = BM * kKC + BNW * BROW_U4;
-  static_assert(FM >= 1 && NQ >= 2 && LB >= 1 && (FP8W || LB % kSUB == 0), "unsupported tile");
+  constexpr int BROW_U4 = FP8W ? 2 : KC;      // 16-byte chunks per weight row per step
+  constexpr int STAGE_U4 = BM * KC + BNW * BROW_U4;
+  static_assert(FM >= 1 && NQ >= 2 && LB >= 1 && (FP8W || LB % 2 == 0), "unsupported tile");
+  static_assert((STAGES - 2) * LSTEP < 64, "outstanding loads exceed the vmcnt range");
   static_assert(!FP8W || (BNW * 2) % (64 * NW) == 0, "FP8 weight loads must tile the step");
   for (int i = threadIdx.x; i <= E_loc; i += blockDim.x) segs[i] = offsets[i];
   mtile_prefix<BM, CLASS>(offsets, E_loc, prefix);  // ends with a barrier
@@ -176,7 +199,7 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
     return;
   }
   const int ntiles = (total - vb + G - 1) / G;
-  const int KT = K / kBK;
+  const int KT = K / BK;
   const int S = ntiles * KT;  // this workgroup's K-steps over all its tiles
 
   const int tid = threadIdx.x;
@@ -187,10 +210,7 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
   const size_t wstride = static_cast<size_t>(SWIGLU ? 2 * N : N) * K;
   // LDS swizzle: chunk c of row r is stored at c ^ swz(r); swz spreads the 16
   // rows read by one 16-lane ds_read_b128 phase over all bank groups
-  auto swz = [](int r) { return (r >> 2) & 3; };
-  // the chunk this lane fetches in every 16-row group it loads (row = g * 16 +
-  // lane / 4, so swz(row) depends only on the lane)
-  const int lkc = (lane % kKC) ^ swz(lane / kKC);
+  auto swz = [](int r) { return step_swz<KC>(r); };
   const char* Ab = reinterpret_cast<const char*>(A);
 
   // ---- issue side: the tile whose operands are being fetched
@@ -203,12 +223,14 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
       iWb = reinterpret_cast<const char*>(W) + t.e * wstride;  // one byte per code
     else
       iWb = reinterpret_cast<const char*>(wlist != nullptr ? wlist[t.e] : W + t.e * wstride);
+    // lane % KC is the LDS chunk position the lane writes; it fetches the
+    // global chunk that belongs there
 #pragma unroll
     for (int i = 0; i < LA; ++i) {
-      const int rt = (i * NW + wave) * kRPI + lane / kKC;  // row within the tile
+      const int rt = (i * NW + wave) * RPI + lane / KC;  // row within the tile
       int arow = min(t.m0 + rt, t.seg1 - 1);
       if (gather != nullptr) arow = gather[arow] / gk;
-      aoff[i] = (static_cast<uint32_t>(arow) * K + lkc * 8) * 2u;
+      aoff[i] = (static_cast<uint32_t>(arow) * K + ((lane % KC) ^ swz(rt)) * 8) * 2u;
     }
 #pragma unroll
     for (int i = 0; i < LB; ++i) {
@@ -222,27 +244,27 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
         else wrow = min(t.n0 + rt, N - 1);
         boff[i] = static_cast<uint32_t>(wrow) * K + c * 16u;
       } else {
-        const int rt = (i * NW + wave) * kRPI + lane / kKC;
+        const int rt = (i * NW + wave) * RPI + lane / KC;
         int wrow;
         if (SWIGLU) wrow = (rt / HALF) * N + min(t.n0 + rt % HALF, N - 1);
         else wrow = min(t.n0 + rt, N - 1);
-        boff[i] = (static_cast<uint32_t>(wrow) * K + lkc * 8) * 2u;
+        boff[i] = (static_cast<uint32_t>(wrow) * K + ((lane % KC) ^ swz(rt)) * 8) * 2u;
       }
     }
     it_tile = j;
   };
-  // part p (of kSUB) of a step's loads into buffer buf
+  // part p (of 2) of a step's loads into buffer buf
   auto issue_part = [&](int p, int buf, uint32_t koff) {
     uint4* As = lds + buf * STAGE_U4;
-    uint4* Bs = As + BM * kKC;
+    uint4* Bs = As + BM * KC;
 #pragma unroll
-    for (int i = p * LA / kSUB; i < (p + 1) * LA / kSUB; ++i)
+    for (int i = p * LA / 2; i < (p + 1) * LA / 2; ++i)
       __builtin_amdgcn_global_load_lds(
           (const __attribute__((address_space(1))) void*)(Ab + (aoff[i] + koff)),
           (__attribute__((address_space(3))) void*)(As + (i * NW + wave) * 64), 16, 0, 0);
     const uint32_t bkoff = FP8W ? koff / 2u : koff;  // codes: one byte per K
 #pragma unroll
-    for (int i = p * LB / kSUB; i < (p + 1) * LB / kSUB; ++i)
+    for (int i = p * LB / 2; i < (p + 1) * LB / 2; ++i)
       __builtin_amdgcn_global_load_lds(
           (const __attribute__((address_space(1))) void*)(iWb + (boff[i] + bkoff)),
           (__attribute__((address_space(3))) void*)(Bs + (i * NW + wave) * 64), 16, 0, 0);
@@ -254,7 +276,7 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
     if (p >= S) p = S - 1;
     const int j = p / KT, kt = p - j * KT;
     if (j != it_tile) set_issue_tile(j);
-    return static_cast<uint32_t>(kt) * kBK * 2u;
+    return static_cast<uint32_t>(kt) * BK * 2u;
   };
 
   // LDS fragments of substep ks of the step held in buffer `buf` (FP8W: the
@@ -264,13 +286,13 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
   uint4 fbr[2][FP8W ? NQ : 1];
   auto load_frags = [&](int buf, int ks, int slot) {
     const uint4* As = lds + buf * STAGE_U4;
-    const uint4* Bs = As + BM * kKC;
+    const uint4* Bs = As + BM * KC;
     const int ch = ks * 2 + (lane >> 5);
 #pragma unroll
     for (int i = 0; i < (FM > NQ ? FM : NQ); ++i) {
       if (i < FM) {
         const int r = wm * (BM / 2) + i * 32 + (lane & 31);
-        fa[slot][i] = __builtin_bit_cast(bf16x8_t, As[r * kKC + (ch ^ swz(r))]);
+        fa[slot][i] = __builtin_bit_cast(bf16x8_t, As[r * KC + (ch ^ swz(r))]);
       }
       if (i < NQ) {
         // SwiGLU: blocks [0, NQ/2) are this wave's W1 rows, [NQ/2, NQ) the
@@ -281,7 +303,7 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
         if constexpr (FP8W)
           fbr[slot][i] = Bs[q * 2 + (ks ^ ((q >> 3) & 1))];
         else
-          fb[slot][i] = __builtin_bit_cast(bf16x8_t, Bs[q * kKC + (ch ^ swz(q))]);
+          fb[slot][i] = __builtin_bit_cast(bf16x8_t, Bs[q * KC + (ch ^ swz(q))]);
       }
     }
   };
@@ -317,9 +339,9 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
   // the (STAGES - 2) younger steps' loads are outstanding (loads complete in
   // order) and its own LDS reads of the step before are done; the barrier then
   // publishes every wave's step-p data and frees the buffer of step p - 1.
-  // The loads of step p + STAGES - 1 go into that buffer in kSUB parts: part 0
-  // right after the barrier, the others during the first substeps of step p
-  // (pk / pb hold the pending step's K offset and buffer meanwhile).
+  // The loads of step p + STAGES - 1 go into that buffer in two parts: part 0
+  // right after the barrier, part 1 during the first substep of step p (pk /
+  // pb hold the pending step's K offset and buffer meanwhile).
   uint32_t pk = 0u;
   int pb = 0;
   auto sync_and_issue = [&](int p) {
@@ -331,9 +353,10 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
   };
 
   // instruction interleave of one substep: FM * NQ MFMAs with the FM + NQ LDS
-  // reads of the next substep and about LSTEP / kSUB global loads between them
-  constexpr int NMF = FM * NQ, NDS = FM + NQ, NVM = (LSTEP + kSUB - 1) / kSUB;
-  constexpr uint32_t kStepBytes = kBK * 2;  // K bytes of one step in a row
+  // reads of the next substep and (substeps that send a load part) about
+  // LSTEP / 2 global loads between them
+  constexpr int NMF = FM * NQ, NDS = FM + NQ, NVM = (LSTEP + 1) / 2;
+  constexpr uint32_t kStepBytes = BK * 2;  // K bytes of one step in a row
 
   auto mfma_substep = [&](f32x16_t (&acc)[FM][NQ], int slot) {
 #pragma unroll
@@ -405,7 +428,7 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
 #pragma unroll
     for (int p = 0; p < STAGES - 1; ++p)
 #pragma unroll
-      for (int q = 0; q < kSUB; ++q) issue_part(q, p, p * kStepBytes);
+      for (int q = 0; q < 2; ++q) issue_part(q, p, p * kStepBytes);
     wait_vmcnt<(STAGES - 2) * LSTEP>();
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     pk = (STAGES - 1) * kStepBytes;
@@ -436,11 +459,12 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
       // it leaves its SIMD's MFMA pipe to the other wave there).
       auto run_tile = [&](auto act) {
         constexpr bool ACT = decltype(act)::value;
-        // one step: substep 0 fetches substep 1's fragments and the second
-        // half of the pending step's loads between its MFMAs; substep 1
-        // makes step s + 1 readable (barrier), sends the first half of step
-        // s + STAGES's loads into this step's buffer and fetches step
-        // s + 1's first fragments
+        // one step: substep 0 fetches substep 1's fragments and sends the
+        // second half of the pending step's loads between its MFMAs (BK =
+        // 64: substeps 1 and 2 fetch the fragments of the substep after
+        // them); the last substep makes step s + 1 readable (barrier), sends
+        // the first half of step s + STAGES's loads into this step's buffer
+        // and fetches step s + 1's first fragments
         auto substep0 = [&](int s) {
           if constexpr (ACT) load_frags(s % STAGES, 1, 1);
           issue_part(1, pb, pk);
@@ -450,6 +474,20 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
             interleave<0, NMF, NDS, NVM>();
           }
           __builtin_amdgcn_sched_barrier(0);
+          if constexpr (SUB == 4) {
+            if constexpr (ACT) {
+              load_frags(s % STAGES, 2, 0);
+              mfma_substep(acc, 1);
+              interleave<0, NMF, NDS, 0>();
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (ACT) {
+              load_frags(s % STAGES, 3, 1);
+              mfma_substep(acc, 0);
+              interleave<0, NMF, NDS, 0>();
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
         };
         auto substep1 = [&](int s, uint32_t koff_next) {
           wait_vmcnt<(STAGES - 2) * LSTEP>();
@@ -466,7 +504,7 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
           __builtin_amdgcn_sched_barrier(0);
           if constexpr (ACT && FP8W) {
             const int kt = s % KT;
-            if ((kt + 1) % (kScaleBlock / kBK) == 0) rescale(ct, kt / (kScaleBlock / kBK), acc, sc);
+            if ((kt + 1) % (kScaleBlock / BK) == 0) rescale(ct, kt / (kScaleBlock / BK), acc, sc);
           }
         };
         const int s0 = j * KT;
@@ -498,7 +536,7 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
     for (int p = 0; p < STAGES - 1; ++p) {
       const uint32_t ko = issue_koff(p);
 #pragma unroll
-      for (int q = 0; q < kSUB; ++q) issue_part(q, p % STAGES, ko);
+      for (int q = 0; q < 2; ++q) issue_part(q, p % STAGES, ko);
     }
     sync_and_issue(0);
     for (int j = 0; j < ntiles; ++j) {
@@ -517,6 +555,14 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
         issue_part(1, pb, pk);
         mfma_substep(acc, 0);
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (SUB == 4) {
+          load_frags(buf, 2, 0);
+          mfma_substep(acc, 1);
+          __builtin_amdgcn_sched_barrier(0);
+          load_frags(buf, 3, 1);
+          mfma_substep(acc, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
         if (s + 1 < S) sync_and_issue(s + 1);
         mfma_substep(acc, 1);
         __builtin_amdgcn_sched_barrier(0);
