@@ -363,7 +363,7 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int q = 0; q < NQ; ++q)
-        acc[i][q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i], fb[slot][q], acc[i][q], 0, 0, 0);
+        acc[i][q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[slot][q], fa[slot][i], acc[i][q], 0, 0, 0);
   };
   // FP8W: after the last step of K block kb, acc *= s_kb / s_(kb+1) per MFMA
   // tile (s_KB = 1).  sc holds s_kb and s_(kb+1) of each tile; the scales of
@@ -380,40 +380,54 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
   };
   auto epilogue = [&](const Tile& ct, f32x16_t (&acc)[FM][NQ]) {
     const int valid = min(BM, ct.seg1 - ct.m0);
-    // registers -> global; D[m][n] of a 32x32 MFMA tile is in lane
-    // n + 32 * ((m / 4) % 2), register 4 * (m / 8) + m % 4.  Stores address C
-    // with a uniform base and 32-bit byte offsets (C is below 4 GiB), which
-    // keeps the epilogue's address registers few.
+    // registers -> global.  The MFMAs take the weight fragment as their
+    // first operand, so a 32 x 32 tile holds D[n][m] (n: output column, m:
+    // activation row): lane l has row m = l % 32 and, in registers 4g ..
+    // 4g + 3, the four consecutive columns 8g + 4 (l / 32) .. + 3, which it
+    // writes as one 8-byte store (N is a multiple of 64, so the four columns
+    // lie on the same side of N).  Stores address C with a uniform base and
+    // 32-bit byte offsets (C is below 4 GiB), which keeps the epilogue's
+    // address registers few.
     char* Cb = reinterpret_cast<char*>(C);
+    auto pack4 = [](const float (&v)[4]) {
+      return make_uint2(static_cast<uint32_t>(f32_to_bf16(v[0])) |
+                            (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16),
+                        static_cast<uint32_t>(f32_to_bf16(v[2])) |
+                            (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16));
+    };
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       if (wm * (BM / 2) + i * 32 >= valid) continue;
-      const int row0 = ct.m0 + wm * (BM / 2) + i * 32 + 4 * (lane >> 5);
+      const int row = ct.m0 + wm * (BM / 2) + i * 32 + (lane & 31);
+      if (row >= ct.seg1) continue;
 #pragma unroll
       for (int q = 0; q < (SWIGLU ? NQ / 2 : NQ); ++q) {
-        const int col = ct.n0 + (SWIGLU ? wn * (HALF / WN) : wn * (BNW / WN)) + q * 32 + (lane & 31);
-        const uint32_t base = (static_cast<uint32_t>(row0) * static_cast<uint32_t>(N) +
-                               static_cast<uint32_t>(col)) * 2u;
+        const int col0 = ct.n0 + (SWIGLU ? wn * (HALF / WN) : wn * (BNW / WN)) + q * 32 +
+                         4 * (lane >> 5);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int dm = 8 * (r >> 2) + (r & 3);
-          float v = acc[i][q][r];
+        for (int g = 0; g < 4; ++g) {
+          const int col = col0 + 8 * g;
+          if (col >= N) continue;
+          float v[4];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) v[c] = acc[i][q][4 * g + c];
           if constexpr (SWIGLU) {
-            const float g = acc[i][q + NQ / 2][r];
+            float gv[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) gv[c] = acc[i][q + NQ / 2][4 * g + c];
             if constexpr (SAVE) {
-              if (row0 + dm < ct.seg1 && col < N) {
-                const uint32_t ab = (static_cast<uint32_t>(row0 + dm) * static_cast<uint32_t>(2 * N) +
-                                     static_cast<uint32_t>(col)) * 2u;
-                char* ABb = reinterpret_cast<char*>(AB);
-                *reinterpret_cast<uint16_t*>(ABb + ab) = f32_to_bf16(v);
-                *reinterpret_cast<uint16_t*>(ABb + ab + static_cast<uint32_t>(N) * 2u) = f32_to_bf16(g);
-              }
+              const uint32_t ab = (static_cast<uint32_t>(row) * static_cast<uint32_t>(2 * N) +
+                                   static_cast<uint32_t>(col)) * 2u;
+              char* ABb = reinterpret_cast<char*>(AB);
+              *reinterpret_cast<uint2*>(ABb + ab) = pack4(v);
+              *reinterpret_cast<uint2*>(ABb + ab + static_cast<uint32_t>(N) * 2u) = pack4(gv);
             }
-            v = silu_fast(v) * g;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) v[c] = silu_fast(v[c]) * gv[c];
           }
-          if (row0 + dm < ct.seg1 && col < N)
-            *reinterpret_cast<uint16_t*>(Cb + (base + static_cast<uint32_t>(dm * N) * 2u)) =
-                f32_to_bf16(v);
+          const uint32_t off = (static_cast<uint32_t>(row) * static_cast<uint32_t>(N) +
+                                static_cast<uint32_t>(col)) * 2u;
+          *reinterpret_cast<uint2*>(Cb + off) = pack4(v);
         }
       }
     }
