@@ -265,43 +265,43 @@ __global__ __launch_bounds__(256, 1) void moe_fused_kernel(FusedArgs a) {
     const uint16_t* w13 = static_cast<const uint16_t*>(a.w13);
     uint16_t* h = static_cast<uint16_t*>(a.h);
     if (a.ffn_all_rows) {
-      gemm_pipe_body<true, 128, 128, 8, ROWS_ALL>(xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G, lds,
+      gemm_pipe_body<true, 128, 128, 4, ROWS_ALL, 4, false, false, 64>(xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G, lds,
                                              prefix, segs, a.sorted_pair, k);
     } else if (a.rows_up == kFusedWide) {
-      gemm_pipe_body<true, 128, 256, 6, ROWS_ALL>(xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G, lds,
+      gemm_pipe_body<true, 128, 256, 3, ROWS_ALL, 4, false, false, 64>(xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G, lds,
                                              prefix, segs, a.sorted_pair, k);
     } else if (a.rows_up == kFusedAllBig) {
-      gemm_pipe_body<true, 256, 256, 4, ROWS_ALL>(xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G, lds,
+      gemm_pipe_body<true, 256, 256, 2, ROWS_ALL, 4, false, false, 64>(xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G, lds,
                                              prefix, segs, a.sorted_pair, k);
     } else if (a.rows_up == kFusedRide) {
-      gemm_pipe_body<true, 256, 256, 4, ROWS_BIGR>(xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G,
+      gemm_pipe_body<true, 256, 256, 2, ROWS_BIGR, 4, false, false, 64>(xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G,
                                               lds, prefix, segs, a.sorted_pair, k);
-      gemm_pipe_body<true, 128, 128, 8, ROWS_TAILR>(xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G,
+      gemm_pipe_body<true, 128, 128, 4, ROWS_TAILR, 4, false, false, 64>(xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G,
                                                lds, prefix, segs, a.sorted_pair, k);
     } else {
-      gemm_pipe_body<true, 256, 256, 4, ROWS_BIG>(xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G, lds,
+      gemm_pipe_body<true, 256, 256, 2, ROWS_BIG, 4, false, false, 64>(xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G, lds,
                                              prefix, segs, a.sorted_pair, k);
-      gemm_pipe_body<true, 128, 128, 8, ROWS_TAIL>(xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G,
+      gemm_pipe_body<true, 128, 128, 4, ROWS_TAIL, 4, false, false, 64>(xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G,
                                               lds, prefix, segs, a.sorted_pair, k);
     }
     grid_barrier(a, G);
     const uint16_t* w2 = static_cast<const uint16_t*>(a.w2);
     uint16_t* yp = static_cast<uint16_t*>(a.y_perm);
     if (a.ffn_all_rows) {
-      gemm_pipe_body<false, 128, 128, 8, ROWS_ALL>(h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G, lds,
+      gemm_pipe_body<false, 128, 128, 4, ROWS_ALL, 4, false, false, 64>(h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G, lds,
                                               prefix, segs);
     } else if (a.rows_down == kFusedAllBig) {
-      gemm_pipe_body<false, 256, 256, 4, ROWS_ALL>(h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G, lds,
+      gemm_pipe_body<false, 256, 256, 2, ROWS_ALL, 4, false, false, 64>(h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G, lds,
                                               prefix, segs);
     } else if (a.rows_down == kFusedRide) {
-      gemm_pipe_body<false, 256, 256, 4, ROWS_BIGR>(h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G,
+      gemm_pipe_body<false, 256, 256, 2, ROWS_BIGR, 4, false, false, 64>(h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G,
                                                lds, prefix, segs);
-      gemm_pipe_body<false, 128, 128, 8, ROWS_TAILR>(h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G,
+      gemm_pipe_body<false, 128, 128, 4, ROWS_TAILR, 4, false, false, 64>(h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G,
                                                 lds, prefix, segs);
     } else {
-      gemm_pipe_body<false, 256, 256, 4, ROWS_BIG>(h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G, lds,
+      gemm_pipe_body<false, 256, 256, 2, ROWS_BIG, 4, false, false, 64>(h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G, lds,
                                               prefix, segs);
-      gemm_pipe_body<false, 128, 128, 8, ROWS_TAIL>(h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G,
+      gemm_pipe_body<false, 128, 128, 4, ROWS_TAIL, 4, false, false, 64>(h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G,
                                                lds, prefix, segs);
     }
   } else {
@@ -339,9 +339,10 @@ size_t fused_lds_bytes(int E, bool bf16) {
   if (plan < resolver_lds_bytes()) plan = resolver_lds_bytes();
   size_t gemm = f32_lds_floats(true) * sizeof(float);
   if (bf16) {
-    gemm = pipe_lds_bytes(128, 128, 8);
-    if (gemm < pipe_lds_bytes(256, 256, 4)) gemm = pipe_lds_bytes(256, 256, 4);
-    if (gemm < pipe_lds_bytes(128, 256, 6)) gemm = pipe_lds_bytes(128, 256, 6);
+    // GEMM phases step K 64 deep (K = d or f, multiples of 64 for bf16)
+    gemm = pipe_lds_bytes(128, 128, 4, false, 64);
+    if (gemm < pipe_lds_bytes(256, 256, 2, false, 64)) gemm = pipe_lds_bytes(256, 256, 2, false, 64);
+    if (gemm < pipe_lds_bytes(128, 256, 3, false, 64)) gemm = pipe_lds_bytes(128, 256, 3, false, 64);
   }
   return plan > gemm ? plan : gemm;
 }
