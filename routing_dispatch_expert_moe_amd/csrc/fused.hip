@@ -7,8 +7,9 @@
 // them.  MoE sparse-activation page, §4.2 layer 1: router, top-k and expert
 // compute fused into one kernel.
 //
-// One workgroup of 256 threads per CU (cooperative launch: every workgroup is
-// resident, so the device-wide barriers below cannot deadlock).  Phases, each
+// One workgroup per CU (cooperative launch: every workgroup is resident, so
+// the device-wide barriers below cannot deadlock): 8 waves for bf16 (two per
+// SIMD, as the stand-alone GEMM kernels run), 4 for fp32.  Phases, each
 // a loop over the phase's work units with stride = grid size:
 //   1. route (one wave per token); with rerouting: candidates (one wave per
 //      token), the sequential resolver on workgroup 0, then the gates (one
@@ -94,15 +95,16 @@ __device__ __forceinline__ void grid_barrier(const FusedArgs& a, uint32_t G) {
 }
 
 // Inclusive-to-exclusive scan over n <= 1024 ints held in LDS `v` into `out`
-// (out[0..n]), by the whole workgroup (256 threads, each owns a run of 4).
+// (out[0..n]), by the whole workgroup (at most 8 waves; each thread owns a
+// contiguous run of 4 (256 threads) or 2 (512)).  scratch: one int per wave.
 __device__ __forceinline__ void block_exclusive_scan(const int* v, int n, int* out, int* scratch) {
   const int tid = threadIdx.x;
-  const int lo = tid * 4;
+  const int per = (MOE_MAX_E + static_cast<int>(blockDim.x) - 1) / static_cast<int>(blockDim.x);
+  const int lo = tid * per;
   int local = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < per; ++i)
     if (lo + i < n) local += v[lo + i];
-  // wave-level inclusive scan, then across the 4 waves
+  // wave-level inclusive scan, then across the waves
   int incl = local;
 #pragma unroll
   for (int off = 1; off < kWave; off <<= 1) {
@@ -114,8 +116,7 @@ __device__ __forceinline__ void block_exclusive_scan(const int* v, int n, int* o
   int wave_base = 0;
   for (int w = 0; w < (tid >> 6); ++w) wave_base += scratch[w];
   int run = wave_base + incl - local;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < per; ++i) {
     if (lo + i < n) {
       out[lo + i] = run;
       run += v[lo + i];
@@ -146,11 +147,16 @@ __device__ __forceinline__ int sum_block_counts(const int* __restrict__ block_co
 }
 
 template <bool BF16>
-__global__ __launch_bounds__(256, 1) void moe_fused_kernel(FusedArgs a) {
+constexpr int fused_threads() { return BF16 ? 512 : 256; }
+
+template <bool BF16>
+__global__ __launch_bounds__(fused_threads<BF16>(), 1) void moe_fused_kernel(FusedArgs a) {
+  constexpr int NT = fused_threads<BF16>();
+  constexpr int NWV = NT / kWave;  // waves per workgroup
   extern __shared__ uint4 lds[];
   __shared__ int prefix[MOE_MAX_E + 1];
   __shared__ int segs[MOE_MAX_E + 1];
-  __shared__ int scan_scratch[4];
+  __shared__ int scan_scratch[NWV];
   const int bid = blockIdx.x, G = gridDim.x;
   const int T = a.T, E = a.E, k = a.k;
   const int E_loc = a.e_end - a.e_begin;
@@ -165,7 +171,7 @@ __global__ __launch_bounds__(256, 1) void moe_fused_kernel(FusedArgs a) {
   // ---- 1: route, one wave per token
   if (a.reroute) {
     const int kc = k < E ? k + 1 : k;
-    for (int t = bid * 4 + wave; t < T; t += G * 4) {
+    for (int t = bid * NWV + wave; t < T; t += G * NWV) {
       if (E <= 64) reroute_candidates_token<1>(a.logits, t, E, kc, a.cand_e, a.cand_v);
       else if (E <= 256) reroute_candidates_token<4>(a.logits, t, E, kc, a.cand_e, a.cand_v);
       else reroute_candidates_token<16>(a.logits, t, E, kc, a.cand_e, a.cand_v);
@@ -178,7 +184,7 @@ __global__ __launch_bounds__(256, 1) void moe_fused_kernel(FusedArgs a) {
       switch (k) {
 #define MOE_FUSED_RESOLVE(KK)                                                                   \
   case KK:                                                                                     \
-    reroute_resolve_body<KK, 256>(a.cand_e, T, E, a.capacity, a.rerouted, load, ce);           \
+    reroute_resolve_body<KK, NT>(a.cand_e, T, E, a.capacity, a.rerouted, load, ce);            \
     break;
         MOE_FUSED_RESOLVE(1) MOE_FUSED_RESOLVE(2) MOE_FUSED_RESOLVE(3) MOE_FUSED_RESOLVE(4)
         MOE_FUSED_RESOLVE(5) MOE_FUSED_RESOLVE(6) MOE_FUSED_RESOLVE(7) MOE_FUSED_RESOLVE(8)
@@ -187,7 +193,7 @@ __global__ __launch_bounds__(256, 1) void moe_fused_kernel(FusedArgs a) {
       }
     }
     grid_barrier(a, G);
-    for (int t = bid * 256 + static_cast<int>(threadIdx.x); t < T; t += G * 256) {
+    for (int t = bid * NT + static_cast<int>(threadIdx.x); t < T; t += G * NT) {
       const uint64_t* rr = can ? a.rerouted : nullptr;
       switch (k) {
 #define MOE_FUSED_GATES(KK)                                                                     \
@@ -205,12 +211,12 @@ __global__ __launch_bounds__(256, 1) void moe_fused_kernel(FusedArgs a) {
     // while the current one is ranked
     auto route_all = [&](auto epl) {
       constexpr int EPL = decltype(epl)::value;
-      int t = bid * 4 + wave;
+      int t = bid * NWV + wave;
       float cur[EPL];
       if (t < T) load_logits<EPL>(a.logits, t, E, cur);
-      for (; t < T; t += G * 4) {
+      for (; t < T; t += G * NWV) {
         float nxt[EPL] = {};
-        if (t + G * 4 < T) load_logits<EPL>(a.logits, t + G * 4, E, nxt);
+        if (t + G * NWV < T) load_logits<EPL>(a.logits, t + G * NWV, E, nxt);
         route_token_vals<EPL>(cur, t, E, k, a.gate, a.topk_idx, a.topk_w);
 #pragma unroll
         for (int i = 0; i < EPL; ++i) cur[i] = nxt[i];
@@ -265,43 +271,43 @@ __global__ __launch_bounds__(256, 1) void moe_fused_kernel(FusedArgs a) {
     const uint16_t* w13 = static_cast<const uint16_t*>(a.w13);
     uint16_t* h = static_cast<uint16_t*>(a.h);
     if (a.ffn_all_rows) {
-      gemm_pipe_body<true, 128, 128, 4, ROWS_ALL, 4, false, false, 64>(xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G, lds,
+      gemm_pipe_body<true, 128, 256, 3, ROWS_ALL, 8, false, false, 64>(xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G, lds,
                                              prefix, segs, a.sorted_pair, k);
     } else if (a.rows_up == kFusedWide) {
-      gemm_pipe_body<true, 128, 256, 3, ROWS_ALL, 4, false, false, 64>(xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G, lds,
+      gemm_pipe_body<true, 128, 256, 3, ROWS_ALL, 8, false, false, 64>(xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G, lds,
                                              prefix, segs, a.sorted_pair, k);
     } else if (a.rows_up == kFusedAllBig) {
-      gemm_pipe_body<true, 256, 256, 2, ROWS_ALL, 4, false, false, 64>(xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G, lds,
+      gemm_pipe_body<true, 256, 256, 2, ROWS_ALL, 8, false, false, 64>(xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G, lds,
                                              prefix, segs, a.sorted_pair, k);
     } else if (a.rows_up == kFusedRide) {
-      gemm_pipe_body<true, 256, 256, 2, ROWS_BIGR, 4, false, false, 64>(xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G,
+      gemm_pipe_body<true, 256, 256, 2, ROWS_BIGR, 8, false, false, 64>(xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G,
                                               lds, prefix, segs, a.sorted_pair, k);
-      gemm_pipe_body<true, 128, 128, 4, ROWS_TAILR, 4, false, false, 64>(xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G,
+      gemm_pipe_body<true, 128, 256, 3, ROWS_TAILR, 8, false, false, 64>(xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G,
                                                lds, prefix, segs, a.sorted_pair, k);
     } else {
-      gemm_pipe_body<true, 256, 256, 2, ROWS_BIG, 4, false, false, 64>(xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G, lds,
+      gemm_pipe_body<true, 256, 256, 2, ROWS_BIG, 8, false, false, 64>(xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G, lds,
                                              prefix, segs, a.sorted_pair, k);
-      gemm_pipe_body<true, 128, 128, 4, ROWS_TAIL, 4, false, false, 64>(xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G,
+      gemm_pipe_body<true, 128, 256, 3, ROWS_TAIL, 8, false, false, 64>(xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G,
                                               lds, prefix, segs, a.sorted_pair, k);
     }
     grid_barrier(a, G);
     const uint16_t* w2 = static_cast<const uint16_t*>(a.w2);
     uint16_t* yp = static_cast<uint16_t*>(a.y_perm);
     if (a.ffn_all_rows) {
-      gemm_pipe_body<false, 128, 128, 4, ROWS_ALL, 4, false, false, 64>(h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G, lds,
+      gemm_pipe_body<false, 128, 256, 3, ROWS_ALL, 8, false, false, 64>(h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G, lds,
                                               prefix, segs);
     } else if (a.rows_down == kFusedAllBig) {
-      gemm_pipe_body<false, 256, 256, 2, ROWS_ALL, 4, false, false, 64>(h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G, lds,
+      gemm_pipe_body<false, 256, 256, 2, ROWS_ALL, 8, false, false, 64>(h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G, lds,
                                               prefix, segs);
     } else if (a.rows_down == kFusedRide) {
-      gemm_pipe_body<false, 256, 256, 2, ROWS_BIGR, 4, false, false, 64>(h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G,
+      gemm_pipe_body<false, 256, 256, 2, ROWS_BIGR, 8, false, false, 64>(h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G,
                                                lds, prefix, segs);
-      gemm_pipe_body<false, 128, 128, 4, ROWS_TAILR, 4, false, false, 64>(h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G,
+      gemm_pipe_body<false, 128, 256, 3, ROWS_TAILR, 8, false, false, 64>(h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G,
                                                 lds, prefix, segs);
     } else {
-      gemm_pipe_body<false, 256, 256, 2, ROWS_BIG, 4, false, false, 64>(h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G, lds,
+      gemm_pipe_body<false, 256, 256, 2, ROWS_BIG, 8, false, false, 64>(h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G, lds,
                                               prefix, segs);
-      gemm_pipe_body<false, 128, 128, 4, ROWS_TAIL, 4, false, false, 64>(h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G,
+      gemm_pipe_body<false, 128, 256, 3, ROWS_TAIL, 8, false, false, 64>(h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G,
                                                lds, prefix, segs);
     }
   } else {
@@ -317,7 +323,7 @@ __global__ __launch_bounds__(256, 1) void moe_fused_kernel(FusedArgs a) {
   grid_barrier(a, G);
 
   // ---- 5: combine
-  for (int t = bid * 4 + wave; t < T; t += G * 4)
+  for (int t = bid * NWV + wave; t < T; t += G * NWV)
     combine_token<BF16>(static_cast<const uint4*>(a.y_perm), a.pair_pos, a.topk_w, t, k, chunks,
                         static_cast<uint4*>(a.y));
 }
@@ -340,8 +346,7 @@ size_t fused_lds_bytes(int E, bool bf16) {
   size_t gemm = f32_lds_floats(true) * sizeof(float);
   if (bf16) {
     // GEMM phases step K 64 deep (K = d or f, multiples of 64 for bf16)
-    gemm = pipe_lds_bytes(128, 128, 4, false, 64);
-    if (gemm < pipe_lds_bytes(256, 256, 2, false, 64)) gemm = pipe_lds_bytes(256, 256, 2, false, 64);
+    gemm = pipe_lds_bytes(256, 256, 2, false, 64);
     if (gemm < pipe_lds_bytes(128, 256, 3, false, 64)) gemm = pipe_lds_bytes(128, 256, 3, false, 64);
   }
   return plan > gemm ? plan : gemm;
@@ -357,7 +362,8 @@ int launch_fused(const FusedArgs& a, bool bf16, int64_t max_rows, void* stream) 
   if (int rc = set_dynamic_lds_once(kern, fused_lds_bytes(MOE_MAX_E, bf16), attr[bf16 ? 1 : 0]))
     return rc;
   int occ = 0;
-  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, 256, lds);
+  const int threads = bf16 ? fused_threads<true>() : fused_threads<false>();
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, threads, lds);
   if (e != hipSuccess) return static_cast<int>(e);
   if (occ < 1) return static_cast<int>(hipErrorCooperativeLaunchTooLarge);
   // enough workgroups for the widest phase, never more than can be resident
@@ -376,7 +382,7 @@ int launch_fused(const FusedArgs& a, bool bf16, int64_t max_rows, void* stream) 
   if (grid >= 8) grid &= ~static_cast<int64_t>(7);
   if (grid < 1) grid = 1;
   void* args[] = {const_cast<FusedArgs*>(&a)};
-  e = hipLaunchCooperativeKernel(kern, dim3(static_cast<unsigned>(grid)), dim3(256), args,
+  e = hipLaunchCooperativeKernel(kern, dim3(static_cast<unsigned>(grid)), dim3(threads), args,
                                  static_cast<unsigned>(lds), s);
   if (e != hipSuccess) return static_cast<int>(e);
   return static_cast<int>(hipGetLastError());
