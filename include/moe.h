@@ -119,7 +119,8 @@ moe_status moe_pack_weights(const void* w1, const void* w3, const void* w2, int 
 /* Router logits (sparse-activation page §3.1 router row, §5.3 fp32 router):
  *   logits[t][e] = sum_i x[t][i] * w_gate[i][e]
  * x: [T][d] bf16; w_gate: [d][E] fp32; logits: [T][E] fp32 (output).
- * fp32 products and accumulation.  Requires d % 8 == 0, 1 <= E <= 64. */
+ * fp32 products and accumulation, each logit one fixed-order sum
+ * (deterministic).  Requires d % 8 == 0, 1 <= E <= MOE_MAX_E. */
 moe_status moe_router_logits(const void* x, const float* w_gate, int T, int d, int E,
                              float* logits, void* stream);
 

@@ -199,7 +199,7 @@ moe_status moe_pack_weights(const void* w1, const void* w3, const void* w2, int 
 
 moe_status moe_router_logits(const void* x, const float* w_gate, int T, int d, int E,
                              float* logits, void* stream) {
-  if (T < 0 || d < 1 || E < 1 || E > 64) return MOE_ERR_INVALID_ARG;
+  if (T < 0 || d < 1 || E < 1 || E > MOE_MAX_E) return MOE_ERR_INVALID_ARG;
   if (d % 8 != 0) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!x || !w_gate || !logits) return MOE_ERR_INVALID_ARG;

@@ -97,11 +97,110 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
   }
 }
 
+// More than 64 experts: a workgroup computes a tile of TT tokens x 64
+// experts (TT = 64, or 16 when there are few tokens, for more workgroups).
+// K-chunks of KC = 32 of x (bf16 -> fp32, exact) and of wg go through LDS,
+// the next chunk's loads in flight in registers while the current chunk is
+// summed; thread (ty, tx) of 16 x 16 accumulates tokens ty * TT/16 ..
+// (ty + 1) * TT/16 - 1 by experts 4tx .. 4tx+3, each sum one fp32 fma per i in
+// increasing order, so the result is deterministic.  x is read once per
+// 64-expert column of tiles and wg once per row of token tiles.
+constexpr int kRlE = 64;
+
+template <int TT, int KC>
+__global__ __launch_bounds__(256) void router_logits_tiled_kernel(const uint16_t* __restrict__ x,
+                                                                  const float* __restrict__ wg,
+                                                                  int T, int d, int E,
+                                                                  float* __restrict__ logits) {
+  constexpr int R = TT / 16;                // token rows per thread
+  constexpr int XCH = KC / 8;               // 8-value x chunks per token and K-chunk
+  constexpr int WPT = KC * kRlE / 256;      // wg values staged per thread
+  static_assert(TT * XCH <= 256 && WPT * 256 == KC * kRlE, "staging roles");
+  __shared__ float xs[TT][KC + 1];          // [token][i], padded against bank conflicts
+  __shared__ float ws[KC][kRlE];            // [i][expert]
+  const int tid = threadIdx.x;
+  const int ty = tid / 16, tx = tid % 16;
+  const int t0 = blockIdx.x * TT, e0 = blockIdx.y * kRlE;
+  float acc[R][4];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[r][c] = 0.f;
+  // staging roles: x, thread < TT * XCH -> (token tid / XCH, 8 values at
+  // chunk tid % XCH); wg, element j * 256 + tid of the KC x 64 tile (row
+  // 4j + tid / 64, expert tid % 64): coalesced loads, conflict-free LDS writes
+  const int xt = tid / XCH, xc = (tid % XCH) * 8;
+  const bool xrole = tid < TT * XCH;
+  const int wi = tid / kRlE, we = tid % kRlE;
+  constexpr int WROWS = 256 / kRlE;  // tile rows one pass of the threads covers
+  uint4 xr = make_uint4(0u, 0u, 0u, 0u);
+  float wr[WPT];
+  auto fetch = [&](int d0) {
+    xr = make_uint4(0u, 0u, 0u, 0u);
+    if (xrole && t0 + xt < T && d0 + xc < d)  // d % 8 == 0: a chunk is wholly in or out
+      xr = *reinterpret_cast<const uint4*>(x + (size_t)(t0 + xt) * d + d0 + xc);
+    const int e = e0 + we;
+#pragma unroll
+    for (int j = 0; j < WPT; ++j) {
+      const int i = d0 + j * WROWS + wi;
+      wr[j] = (i < d && e < E) ? wg[(size_t)i * E + e] : 0.f;
+    }
+  };
+  fetch(0);
+  for (int d0 = 0; d0 < d; d0 += KC) {
+    if (xrole) {
+      float xf[8];
+      unpack8(xr, xf);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) xs[xt][xc + i] = xf[i];
+    }
+#pragma unroll
+    for (int j = 0; j < WPT; ++j) ws[j * WROWS + wi][we] = wr[j];
+    __syncthreads();
+    if (d0 + KC < d) fetch(d0 + KC);
+#pragma unroll 8
+    for (int i = 0; i < KC; ++i) {
+      float a[R], b[4];
+#pragma unroll
+      for (int r = 0; r < R; ++r) a[r] = xs[ty * R + r][i];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) b[c] = ws[i][tx * 4 + c];
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[r][c] = fmaf(a[r], b[c], acc[r][c]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int t = t0 + ty * R + r;
+    if (t >= T) continue;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int e = e0 + tx * 4 + c;
+      if (e < E) logits[(size_t)t * E + e] = acc[r][c];
+    }
+  }
+}
+
 int launch_router_logits(const void* x, const float* wg, int T, int d, int E, float* logits,
                          void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   const uint16_t* xb = static_cast<const uint16_t*>(x);
   const dim3 block(256);
+  if (E > 64) {
+    // 64-token tiles once they give a few workgroups per CU, else 16
+    const int ecol = (E + kRlE - 1) / kRlE;
+    if (static_cast<int64_t>((T + 63) / 64) * ecol >= 2 * device_cu_count()) {
+      const dim3 grid((T + 63) / 64, ecol);
+      hipLaunchKernelGGL((router_logits_tiled_kernel<64, 32>), grid, block, 0, s, xb, wg, T, d, E, logits);
+    } else {
+      const dim3 grid((T + 15) / 16, ecol);
+      hipLaunchKernelGGL((router_logits_tiled_kernel<16, 32>), grid, block, 0, s, xb, wg, T, d, E, logits);
+    }
+    return static_cast<int>(hipGetLastError());
+  }
   if (E <= 8)
     hipLaunchKernelGGL(router_logits_kernel<8>, dim3((T + 7) / 8), block, 0, s, xb, wg, T, d, E, logits);
   else if (E <= 16)

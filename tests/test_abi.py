@@ -188,7 +188,7 @@ def test_combine_router_pack_validation(lib):
     assert lib.moe_combine(FAKE, FAKE, FAKE, 10, 9, 64, L.MOE_BF16, FAKE, None) == L.MOE_ERR_INVALID_ARG
     assert lib.moe_combine(FAKE, FAKE, FAKE, 10, 2, 6, L.MOE_F32, FAKE, None) == L.MOE_ERR_UNSUPPORTED
     assert lib.moe_combine(FAKE, FAKE, MIS, 10, 2, 64, L.MOE_BF16, FAKE, None) == L.MOE_ERR_MISALIGNED
-    assert lib.moe_router_logits(FAKE, FAKE, 10, 4096, 65, FAKE, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_router_logits(FAKE, FAKE, 10, 4096, L.MOE_MAX_E + 1, FAKE, None) == L.MOE_ERR_INVALID_ARG
     assert lib.moe_router_logits(FAKE, FAKE, 10, 4092, 8, FAKE, None) == L.MOE_ERR_UNSUPPORTED
     assert lib.moe_pack_weights(FAKE, FAKE, FAKE, 0, 64, 64, L.MOE_BF16, FAKE, FAKE, None) == L.MOE_ERR_INVALID_ARG
     assert lib.moe_pack_weights(FAKE, MIS, FAKE, 2, 64, 64, L.MOE_BF16, FAKE, FAKE, None) == L.MOE_ERR_MISALIGNED

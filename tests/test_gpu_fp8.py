@@ -112,13 +112,14 @@ def test_expert_ffn_fp8(d, f, rows):
     x64 = O.widen(wl.x[:n], "bf16")
     wf = F.expert_weights(rq13, rs13, rq2, rs2, f)
     ref = O.expert_ffn(x64, offsets, wf)
-    assert O.rel_err(as64(y, "bf16")[:n], ref) <= TOL
+    # rows past n are never written: slice before widening
+    assert O.rel_err(as64(y[:n], "bf16"), ref) <= TOL
     for i in range(E_loc):
         r0, r1 = offsets[i], offsets[i + 1]
         if r1 > r0:
             w1, w3, _ = wf(i)
             href = O.swiglu_hidden(x64[r0:r1], w1, w3)
-            assert O.rel_err(as64(h, "bf16")[r0:r1], href) <= TOL
+            assert O.rel_err(as64(h[r0:r1], "bf16"), href) <= TOL
     # same bits on a second call
     y1 = t_out(y).copy()
     M.moe_expert_ffn_fp8(xt, off_t, E_loc, max_rows, q13, s13, q2, s2, h, y)
