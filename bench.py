@@ -50,15 +50,15 @@ COPY_BYTES = 1 << 30
 
 # kernels of each pass (substrings of the demangled names rocprofv3 reports)
 PASS_KERNELS = {
-    "router": ("router_logits_kernel",),
+    "router": ("router_logits_kernel", "router_logits_tiled_kernel"),
     "route": ("route_kernel", "route_candidates_kernel", "reroute_resolve_kernel",
               "reroute_finalize_kernel"),
     "dispatch_plan": ("dispatch_count_kernel", "dispatch_scan_kernel", "dispatch_place_kernel"),
     "permute": ("permute_rows_kernel",),
     "ffn_up": ("gemm_bf16_pipe<true", "gemm_bf16_kernel<32, 128, 64, 1, 4, true",
-               "gemm_f32_kernel<true"),
+               "gemm_f32_kernel<true", "gemm_fp8_pipe<true", "gemm_fp8w_kernel<128, true"),
     "ffn_down": ("gemm_bf16_pipe<false", "gemm_bf16_kernel<32, 128, 64, 1, 4, false",
-                 "gemm_f32_kernel<false"),
+                 "gemm_f32_kernel<false", "gemm_fp8_pipe<false", "gemm_fp8w_kernel<128, false"),
     "combine": ("combine_kernel",),
 }
 # stored counter and kernel-time summaries are tied to the kernel sources
@@ -273,7 +273,14 @@ def _read_trace(d):
 def trace_from(args):
     """Per-kernel statistics of a profiled bench run and, per pass, the
     kernel time of each timed step (the run's dispatches of a pass are its
-    warm-up steps, then the timed steps, then the cache-evicted steps)."""
+    warm-up steps, then the timed steps, then the cache-evicted steps).
+    A run with --weights fp8 or --backward gets its own summary file
+    (kernels_<workload>_fp8.md, kernels_training_<workload>.md) and no stored
+    per-pass times (the forward passes' times are those of the native run;
+    a training run's backward calls launch the same GEMM kernels)."""
+    fp8 = getattr(args, "weights", "native") == "fp8"
+    training = bool(getattr(args, "backward", False))
+    forward_native = not (fp8 or training)
     rows = _read_trace(args.trace_from)
     stats = {}
     total = 0.0
@@ -309,26 +316,38 @@ def trace_from(args):
     if event is not None:
         out["bench_event_mean_us"] = {p: round(v["ms"] * 1e3, 2)
                                       for p, v in event.get("per_step", {}).items()}
-    with open(os.path.join(args.profiles_dir, f"kernel_times_{args.workload}.json"), "w") as fh:
-        json.dump(out, fh, indent=1)
+    if forward_native:
+        with open(os.path.join(args.profiles_dir, f"kernel_times_{args.workload}.json"), "w") as fh:
+            json.dump(out, fh, indent=1)
+    extra = (" --weights fp8" if fp8 else "") + (" --backward" if training else "")
     cmd = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --output-format csv "
-           f"-d <out> -o kt -- python3 <repo>/bench.py --workload {args.workload} --steps {K} "
+           f"-d <out> -o kt -- python3 <repo>/bench.py --workload {args.workload}{extra} --steps {K} "
            f"--warmup {W} --others none --no-fused --no-cpu-baseline > <out>/bench.json")
-    lines = [f"# Kernel time summary: MoE layer, workload {args.workload}", "",
+    what = ("MoE training step (forward + backward)" if training else "MoE layer") + \
+        (", FP8 (E4M3) expert weights" if fp8 else "")
+    runs = (f"{W} warm-up and {K} timed layer steps of the separate calls, then {K} more with the "
+            "Infinity Cache evicted before each (a 1 GiB fill between steps), then the "
+            "dispatch plan alone, then five 1 GiB copies (the bench's plain-copy reference)")
+    if fp8:
+        runs += "; the weights are quantised once first (`moe_quantize_fp8`)"
+    if training:
+        runs += (f"; then {W} warm-up and {K} timed training steps (the forward with the "
+                 "pre-activations kept, then the backward calls)")
+    lines = [f"# Kernel time summary: {what}, workload {args.workload}", "",
              "Command (from the repository root, on one MI355X):", "", "    " + cmd, "",
-             f"{W} warm-up and {K} timed layer steps of the separate calls, then {K} more with the "
-             "Infinity Cache evicted before each (a 1 GiB fill between steps), then the "
-             "dispatch plan alone, then five 1 GiB copies (the bench's plain-copy reference); "
-             "weight packing and input upload run once before them.  Durations are the kernel "
-             "trace's start/end stamps, in microseconds.", "",
+             runs + ".  Weight packing and input upload run once before them.  Durations are "
+             "the kernel trace's start/end stamps, in microseconds.", "",
              "| kernel | calls | avg us | min us | max us | % of traced GPU time |",
              "|---|---|---|---|---|---|"]
     for n, v in sorted(stats.items(), key=lambda kv: -sum(kv[1])):
         lines.append(f"| `{n}` | {len(v)} | {np.mean(v):.2f} | {min(v):.2f} | {max(v):.2f} | "
                      f"{100 * sum(v) / total:.2f} |")
-    lines += ["", "Per pass, kernel time of each timed step (sum over the pass's kernels):", "",
-              "| pass | kernels | per-step us | mean us | bench HIP-event mean us |",
-              "|---|---|---|---|---|"]
+    if training:
+        passes = {}  # the backward launches the forward's GEMM kernels too
+    else:
+        lines += ["", "Per pass, kernel time of each timed step (sum over the pass's kernels):", "",
+                  "| pass | kernels | per-step us | mean us | bench HIP-event mean us |",
+                  "|---|---|---|---|---|"]
     for p in ("router", "route", "dispatch_plan", "permute", "ffn_up", "ffn_down", "combine"):
         if p in passes:
             r = passes[p]
@@ -337,7 +356,8 @@ def trace_from(args):
                          f"{', '.join(f'{v:.1f}' for v in r['per_step_us'])} | {r['mean_us']:.1f} | "
                          f"{ev} |")
     lines.append("")
-    with open(os.path.join(args.profiles_dir, f"kernels_{args.workload}.md"), "w") as fh:
+    name = ("training_" if training else "") + args.workload + ("_fp8" if fp8 else "")
+    with open(os.path.join(args.profiles_dir, f"kernels_{name}.md"), "w") as fh:
         fh.write("\n".join(lines))
     print(json.dumps({p: r["mean_us"] for p, r in passes.items()}))
 
