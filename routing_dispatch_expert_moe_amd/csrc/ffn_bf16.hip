@@ -456,8 +456,10 @@ static int fp8_pipe_pass(bool up, const void* A, const int32_t* offsets, int E_l
     return launch_gemm_pipe_fp8(r, up, A, offsets, E_loc, max_rows, wq, ws, C, N, K, stream);
   };
   // 256-row tiles over every row, except for long-K passes with few tiles,
-  // whose short remainders take 128-row tiles as in the bf16 pass (the FP8
-  // 128-row tiles run one wave per SIMD and measured slower elsewhere)
+  // whose short remainders take 128-row tiles as in the bf16 pass.  The
+  // bf16 pass's ride-along split measured slower here (Zipf-skewed prefill
+  // FFN 8.19 vs 7.74 ms): the FP8 128-row tiles convert codes with one wave
+  // per SIMD, so the experts below 128 rows go faster through 256-row tiles.
   if (ffn_plan_bf16(up, max_rows, E_loc, d, f, device_cu_count()) == MOE_FFN_PLAN_BIG_TAIL) {
     int e = run(PipeRows::kBigTiles);
     return e != 0 ? e : run(PipeRows::kTailTiles);

@@ -26,10 +26,11 @@ __global__ __launch_bounds__(pipe_waves<BM>() * 64, 1) void gemm_bf16_pipe(const
 }
 
 // FP8 weights with many rows per expert: the bf16 kernels' tiles with the
-// weight tiles held in LDS as codes (a step's stage is 24 KB for 256-row
-// tiles, five stages; 16 KB for the 128-row remainder tiles, eight)
+// weight tiles held in LDS as codes, 64-deep steps (a stage is 48 KB for
+// 256-row tiles, three stages; 32 KB for the 128-row remainder tiles, four)
+constexpr int kFp8BK = 64;
 template <int BM>
-constexpr int fp8_stages() { return BM == 256 ? 5 : 8; }
+constexpr int fp8_stages() { return BM == 256 ? 3 : 4; }
 
 template <bool SWIGLU, int BM, int CLASS>
 __global__ __launch_bounds__(pipe_waves<BM>() * 64, 1) void gemm_fp8_pipe(
@@ -39,19 +40,22 @@ __global__ __launch_bounds__(pipe_waves<BM>() * 64, 1) void gemm_fp8_pipe(
   extern __shared__ uint4 lds[];
   __shared__ int prefix[MOE_MAX_E + 1];
   __shared__ int segs[MOE_MAX_E + 1];
-  gemm_pipe_body<SWIGLU, BM, 256, fp8_stages<BM>(), CLASS, pipe_waves<BM>(), false, true>(
+  gemm_pipe_body<SWIGLU, BM, 256, fp8_stages<BM>(), CLASS, pipe_waves<BM>(), false, true, kFp8BK>(
       A, offsets, E_loc, reinterpret_cast<const uint16_t*>(Wq), C, N, K, blockIdx.x, gridDim.x,
       lds, prefix, segs, nullptr, 1, nullptr, nullptr, Ws);
 }
 
-int fp8_pipe_min_k() { return fp8_stages<128>() * kBK; }
+int fp8_pipe_min_k() {
+  constexpr int a = fp8_stages<128>(), b = fp8_stages<256>();
+  return (a > b ? a : b) * kFp8BK;
+}
 
 namespace {
 
 template <bool SWIGLU, int BM, int CLASS>
 int launch_fp8(const void* A, const int32_t* offsets, int E_loc, int64_t max_rows,
                const uint8_t* Wq, const float* Ws, void* C, int N, int K, hipStream_t s) {
-  constexpr size_t lds = pipe_lds_bytes(BM, 256, fp8_stages<BM>(), true);
+  constexpr size_t lds = pipe_lds_bytes(BM, 256, fp8_stages<BM>(), true, kFp8BK);
   static_assert(lds + 2 * (MOE_MAX_E + 1) * 4 <= 160 * 1024, "LDS budget");
   auto kern = gemm_fp8_pipe<SWIGLU, BM, CLASS>;
   static LdsAttr attr;

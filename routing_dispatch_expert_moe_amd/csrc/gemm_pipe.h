@@ -148,13 +148,13 @@ constexpr size_t pipe_lds_bytes(int BM, int BNW, int STAGES, bool fp8w = false, 
 // block, so its scale is one number).  The result is sum_kb s_kb x (block
 // kb's partial sum), the dequantised weights' product re-associated, with one
 // fp32 rounding per block and no second set of accumulators.  K must be at
-// least STAGES steps deep and a multiple of 128.  A weight row of a step is 32
-// bytes, two 16-byte halves fetched by two neighbouring lanes (a 64-lane
-// direct load covers 32 rows); in LDS row r's half c sits at position
-// c ^ ((r >> 3) & 1) of the row, so the 16 rows one 16-lane phase of a
+// least STAGES steps deep and a multiple of 128.  A weight row of a step is BK
+// bytes of codes in 16-byte pieces fetched by BK / 16 neighbouring lanes (a
+// 64-lane direct load covers 32 rows for BK = 32, 16 rows for BK = 64); in
+// LDS piece c of row r sits at position c ^ fswz(r) of the row (BK = 32:
+// (r >> 3) & 1; BK = 64: (r >> 2) & 3), so the 16 rows one 16-lane phase of a
 // fragment read touches cover every bank once.
-// BK: K depth of a pipeline step, 32 or 64 (64 needs K a multiple of 64; FP8W
-// takes 32).
+// BK: K depth of a pipeline step, 32 or 64 (64 needs K a multiple of 64).
 template <bool SWIGLU, int BM, int BNW, int STAGES, int CLASS, int NW = 4, bool SAVE = false,
           bool FP8W = false, int BK = kBK>
 __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
@@ -170,7 +170,7 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
   static_assert(SWIGLU || !SAVE, "pre-activations exist only with SwiGLU");
   static_assert(!FP8W || !SAVE, "FP8 weights have no training forward");
   static_assert(BK == 32 || BK == 64, "step depth");
-  static_assert(!FP8W || BK == 32, "FP8 weight steps are 32 deep");
+  constexpr int FPR = BK / 16;                // FP8W: 16-byte code pieces per weight row and step
   constexpr int KC = BK / 8;                  // 16-byte chunks per row per step
   constexpr int RPI = 64 / KC;                // rows covered by one 64-lane load
   constexpr int SUB = BK / 16;                // MFMA K-substeps per step
@@ -180,14 +180,14 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
   constexpr int WN = NW / 2;                  // waves along the weight rows (2 along M)
   constexpr int NQ = BNW / WN / 32;           // 32-column MFMA blocks per wave
   constexpr int LA = BM / RPI / NW;           // A loads per wave per step
-  // B loads per wave per step (FP8W: 64 lanes x 16 codes cover 32 rows x 32 K)
-  constexpr int LB = FP8W ? BNW * 2 / 64 / NW : BNW / RPI / NW;
+  // B loads per wave per step (FP8W: 64 lanes x 16 codes cover 64 / FPR rows)
+  constexpr int LB = FP8W ? BNW * FPR / 64 / NW : BNW / RPI / NW;
   constexpr int LSTEP = LA + LB;
-  constexpr int BROW_U4 = FP8W ? 2 : KC;      // 16-byte chunks per weight row per step
+  constexpr int BROW_U4 = FP8W ? FPR : KC;    // 16-byte chunks per weight row per step
   constexpr int STAGE_U4 = BM * KC + BNW * BROW_U4;
   static_assert(FM >= 1 && NQ >= 2 && LB >= 1 && (FP8W || LB % 2 == 0), "unsupported tile");
   static_assert((STAGES - 2) * LSTEP < 64, "outstanding loads exceed the vmcnt range");
-  static_assert(!FP8W || (BNW * 2) % (64 * NW) == 0, "FP8 weight loads must tile the step");
+  static_assert(!FP8W || (BNW * FPR) % (64 * NW) == 0, "FP8 weight loads must tile the step");
   for (int i = threadIdx.x; i <= E_loc; i += blockDim.x) segs[i] = offsets[i];
   mtile_prefix<BM, CLASS>(offsets, E_loc, prefix);  // ends with a barrier
   const int NT = (N + BN - 1) / BN;
@@ -211,6 +211,8 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
   // LDS swizzle: chunk c of row r is stored at c ^ swz(r); swz spreads the 16
   // rows read by one 16-lane ds_read_b128 phase over all bank groups
   auto swz = [](int r) { return step_swz<KC>(r); };
+  // FP8W: position swizzle of a code row's 16-byte pieces
+  auto fswz = [](int r) { return FPR == 2 ? (r >> 3) & 1 : (r >> 2) & 3; };
   const char* Ab = reinterpret_cast<const char*>(A);
 
   // ---- issue side: the tile whose operands are being fetched
@@ -236,9 +238,9 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
     for (int i = 0; i < LB; ++i) {
       if constexpr (FP8W) {
         // 16-byte slot (i * NW + wave) * 64 + lane: position p of tile row rt,
-        // holding that row's K half c = p ^ ((rt >> 3) & 1)
+        // holding that row's piece c = p ^ fswz(rt)
         const int slot = (i * NW + wave) * 64 + lane;
-        const int rt = slot >> 1, c = (slot & 1) ^ ((rt >> 3) & 1);
+        const int rt = slot / FPR, c = (slot % FPR) ^ fswz(rt);
         int wrow;
         if (SWIGLU) wrow = (rt / HALF) * N + min(t.n0 + rt % HALF, N - 1);
         else wrow = min(t.n0 + rt, N - 1);
@@ -301,7 +303,7 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
                                 (lane & 31))
                              : (wn * (BNW / WN) + i * 32 + (lane & 31));
         if constexpr (FP8W)
-          fbr[slot][i] = Bs[q * 2 + (ks ^ ((q >> 3) & 1))];
+          fbr[slot][i] = Bs[q * FPR + (ks ^ fswz(q))];
         else
           fb[slot][i] = __builtin_bit_cast(bf16x8_t, Bs[q * KC + (ch ^ swz(q))]);
       }
@@ -389,11 +391,11 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
     // 32-bit byte offsets (C is below 4 GiB), which keeps the epilogue's
     // address registers few.
     char* Cb = reinterpret_cast<char*>(C);
+    // fp32 -> bf16 by the hardware's packed conversion (round to nearest even)
     auto pack4 = [](const float (&v)[4]) {
-      return make_uint2(static_cast<uint32_t>(f32_to_bf16(v[0])) |
-                            (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16),
-                        static_cast<uint32_t>(f32_to_bf16(v[2])) |
-                            (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16));
+      const bf16x2_t lo = __builtin_convertvector(f32x2_t{v[0], v[1]}, bf16x2_t);
+      const bf16x2_t hi = __builtin_convertvector(f32x2_t{v[2], v[3]}, bf16x2_t);
+      return make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
     };
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
@@ -491,12 +493,14 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
           if constexpr (SUB == 4) {
             if constexpr (ACT) {
               load_frags(s % STAGES, 2, 0);
+              cvt_frags(1);
               mfma_substep(acc, 1);
               interleave<0, NMF, NDS, 0>();
             }
             __builtin_amdgcn_sched_barrier(0);
             if constexpr (ACT) {
               load_frags(s % STAGES, 3, 1);
+              cvt_frags(0);
               mfma_substep(acc, 0);
               interleave<0, NMF, NDS, 0>();
             }
