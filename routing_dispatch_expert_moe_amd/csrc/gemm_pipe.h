@@ -120,8 +120,15 @@ using namespace pipe;
 
 // dynamic LDS bytes of gemm_pipe_body<..., BM, BNW, STAGES, ..., BK> (FP8W:
 // the weight rows of a step are 32 one-byte codes instead of 32 bf16 values)
+// Output staging of the 8-wave 256-row bf16 tiles: one 32 x 32 bf16 block per
+// wave, rows padded to 80 bytes (16-byte aligned reads, at most 2-way bank
+// conflicts on the 8-byte writes)
+constexpr int kOutRowBytes = 80;
+constexpr size_t kOutStageBytes = static_cast<size_t>(8) * 32 * kOutRowBytes;
+
 constexpr size_t pipe_lds_bytes(int BM, int BNW, int STAGES, bool fp8w = false, int BK = kBK) {
-  return static_cast<size_t>(STAGES) * (BM + (fp8w ? BNW / 2 : BNW)) * BK * sizeof(uint16_t);
+  return static_cast<size_t>(STAGES) * (BM + (fp8w ? BNW / 2 : BNW)) * BK * sizeof(uint16_t) +
+         (BM == 256 && !fp8w ? kOutStageBytes : 0);
 }
 
 // One workgroup's share of the grouped GEMM: workgroup `bid` of `G` walks its
@@ -187,6 +194,11 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
   constexpr int STAGE_U4 = BM * KC + BNW * BROW_U4;
   static_assert(FM >= 1 && NQ >= 2 && LB >= 1 && (FP8W || LB % 2 == 0), "unsupported tile");
   static_assert((STAGES - 2) * LSTEP < 64, "outstanding loads exceed the vmcnt range");
+  // 256-row bf16 tiles stage each 32 x 32 output block through LDS (the
+  // bytes after the pipeline stages, pipe_lds_bytes) so that every store
+  // writes whole 64-byte row segments
+  constexpr bool STAGE_OUT = BM == 256 && !FP8W && !SAVE;
+  static_assert(!(BM == 256 && !FP8W) || NW == 8, "the output staging holds 8 waves' blocks");
   static_assert(!FP8W || (BNW * FPR) % (64 * NW) == 0, "FP8 weight loads must tile the step");
   for (int i = threadIdx.x; i <= E_loc; i += blockDim.x) segs[i] = offsets[i];
   mtile_prefix<BM, CLASS>(offsets, E_loc, prefix);  // ends with a barrier
@@ -385,11 +397,10 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
     // registers -> global.  The MFMAs take the weight fragment as their
     // first operand, so a 32 x 32 tile holds D[n][m] (n: output column, m:
     // activation row): lane l has row m = l % 32 and, in registers 4g ..
-    // 4g + 3, the four consecutive columns 8g + 4 (l / 32) .. + 3, which it
-    // writes as one 8-byte store (N is a multiple of 64, so the four columns
-    // lie on the same side of N).  Stores address C with a uniform base and
-    // 32-bit byte offsets (C is below 4 GiB), which keeps the epilogue's
-    // address registers few.
+    // 4g + 3, the four consecutive columns 8g + 4 (l / 32) .. + 3 (N is a
+    // multiple of 64, so groups of four or eight columns lie on the same side
+    // of N).  Stores address C with a uniform base and 32-bit byte offsets (C
+    // is below 4 GiB), which keeps the epilogue's address registers few.
     char* Cb = reinterpret_cast<char*>(C);
     // fp32 -> bf16 by the hardware's packed conversion (round to nearest even)
     auto pack4 = [](const float (&v)[4]) {
@@ -397,39 +408,76 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
       const bf16x2_t hi = __builtin_convertvector(f32x2_t{v[2], v[3]}, bf16x2_t);
       return make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
     };
+    // the four output columns of register group g of block (i, q), SwiGLU applied
+    auto block_vals = [&](int i, int q, int g, float (&v)[4]) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) v[c] = acc[i][q][4 * g + c];
+      if constexpr (SWIGLU) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v[c] = silu_fast(v[c]) * acc[i][q + NQ / 2][4 * g + c];
+      }
+    };
+    char* stg = reinterpret_cast<char*>(lds + STAGES * STAGE_U4) + wave * (32 * kOutRowBytes);
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       if (wm * (BM / 2) + i * 32 >= valid) continue;
-      const int row = ct.m0 + wm * (BM / 2) + i * 32 + (lane & 31);
-      if (row >= ct.seg1) continue;
+      const int rbase = ct.m0 + wm * (BM / 2) + i * 32;
 #pragma unroll
       for (int q = 0; q < (SWIGLU ? NQ / 2 : NQ); ++q) {
-        const int col0 = ct.n0 + (SWIGLU ? wn * (HALF / WN) : wn * (BNW / WN)) + q * 32 +
-                         4 * (lane >> 5);
+        const int cbase = ct.n0 + (SWIGLU ? wn * (HALF / WN) : wn * (BNW / WN)) + q * 32;
+        if constexpr (STAGE_OUT) {
+          // the block into this wave's LDS rows (8 bytes per lane and group),
+          // back as 16-byte pieces: lane l takes piece l % 4 of rows l / 4
+          // and 16 + l / 4, so a store covers 16 rows x 64 bytes.  LDS
+          // operations of one wave complete in order; the compiler barriers
+          // keep the writes, reads and the next block's writes in that order.
+          const int m = lane & 31;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int col = col0 + 8 * g;
-          if (col >= N) continue;
-          float v[4];
+          for (int g = 0; g < 4; ++g) {
+            float v[4];
+            block_vals(i, q, g, v);
+            *reinterpret_cast<uint2*>(stg + m * kOutRowBytes + (8 * g + 4 * (lane >> 5)) * 2) =
+                pack4(v);
+          }
+          asm volatile("" ::: "memory");
+          const int pc = lane & 3, col = cbase + pc * 8;
 #pragma unroll
-          for (int c = 0; c < 4; ++c) v[c] = acc[i][q][4 * g + c];
-          if constexpr (SWIGLU) {
-            float gv[4];
+          for (int t = 0; t < 2; ++t) {
+            const int r = (lane >> 2) + 16 * t;
+            const uint4 w = *reinterpret_cast<const uint4*>(stg + r * kOutRowBytes + pc * 16);
+            if (rbase + r < ct.seg1 && col < N)
+              *reinterpret_cast<uint4*>(Cb + (static_cast<uint32_t>(rbase + r) *
+                                                   static_cast<uint32_t>(N) +
+                                               static_cast<uint32_t>(col)) * 2u) = w;
+          }
+          asm volatile("" ::: "memory");
+        } else {
+          const int row = rbase + (lane & 31);
+          if (row >= ct.seg1) continue;
+          const int col0 = cbase + 4 * (lane >> 5);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) gv[c] = acc[i][q + NQ / 2][4 * g + c];
+          for (int g = 0; g < 4; ++g) {
+            const int col = col0 + 8 * g;
+            if (col >= N) continue;
             if constexpr (SAVE) {
+              float a[4], gv[4];
+#pragma unroll
+              for (int c = 0; c < 4; ++c) {
+                a[c] = acc[i][q][4 * g + c];
+                gv[c] = acc[i][q + NQ / 2][4 * g + c];
+              }
               const uint32_t ab = (static_cast<uint32_t>(row) * static_cast<uint32_t>(2 * N) +
                                    static_cast<uint32_t>(col)) * 2u;
               char* ABb = reinterpret_cast<char*>(AB);
-              *reinterpret_cast<uint2*>(ABb + ab) = pack4(v);
+              *reinterpret_cast<uint2*>(ABb + ab) = pack4(a);
               *reinterpret_cast<uint2*>(ABb + ab + static_cast<uint32_t>(N) * 2u) = pack4(gv);
             }
-#pragma unroll
-            for (int c = 0; c < 4; ++c) v[c] = silu_fast(v[c]) * gv[c];
+            float v[4];
+            block_vals(i, q, g, v);
+            const uint32_t off = (static_cast<uint32_t>(row) * static_cast<uint32_t>(N) +
+                                  static_cast<uint32_t>(col)) * 2u;
+            *reinterpret_cast<uint2*>(Cb + off) = pack4(v);
           }
-          const uint32_t off = (static_cast<uint32_t>(row) * static_cast<uint32_t>(N) +
-                                static_cast<uint32_t>(col)) * 2u;
-          *reinterpret_cast<uint2*>(Cb + off) = pack4(v);
         }
       }
     }
