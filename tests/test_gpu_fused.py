@@ -31,6 +31,9 @@ TOL = {"f32": 1e-5, "bf16": 1e-2}
     dict(name="b6", T=1300, d=128, f=128, E=4, k=1, dtype="bf16"),
     dict(name="b7", T=600, d=64, f=128, E=300, k=3, dtype="bf16"),
     dict(name="b8", T=1, d=64, f=64, E=8, k=2, dtype="bf16"),
+    # 1000 local experts: the workgroup scan's runs of two experts per thread
+    # (512 threads) and the widest routing phase
+    dict(name="b9", T=300, d=64, f=64, E=1000, k=2, dtype="bf16", logit_bias="zipf"),
 ])
 def test_fused_layer(kw):
     kw = dict(kw)
@@ -76,6 +79,8 @@ def test_fused_all_dropped():
     dict(name="r3", T=200, d=64, f=64, E=32, k=8, dtype="f32", capacity_factor=1.0,
          gate=O.GATE_SIGMOID, logit_bias="zipf"),
     dict(name="r4", T=90, d=64, f=64, E=4, k=4, dtype="bf16", capacity_factor=0.5),  # k = E
+    dict(name="r5", T=700, d=64, f=64, E=320, k=2, dtype="bf16", capacity_factor=1.0,
+         logit_bias="zipf"),                                           # more than 256 experts
 ])
 def test_fused_layer_with_rerouting(kw):
     """moe_forward_fused_reroute against the separate calls (bit for bit) and the
