@@ -750,7 +750,8 @@ def run_workload(args, wl, weights, dev, headline):
 
     # the same layer as one fused persistent launch (router logits stay a separate call)
     fused_ms = None
-    if not (fp8 or args.no_fused):
+    # (FP8 weights: moe_forward_fused_fp8, which routes without rerouting)
+    if not (args.no_fused or (fp8 and reroute)):
         fev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
 
         def fused_step(ev=None):
@@ -959,7 +960,8 @@ def main(argv=None):
                                 "steps"},
         "training": training,
         "fused": None if head_summary["fused_ms"] is None else {
-            "entry": "moe_forward_fused_reroute" if r["reroute"] else "moe_forward_fused",
+            "entry": ("moe_forward_fused_reroute" if r["reroute"] else
+                      "moe_forward_fused_fp8" if r["fp8"] else "moe_forward_fused"),
             "ms_per_step_median": round(head_summary["fused_ms"], 4),
             "tokens_per_s": round(wl.T / (head_summary["fused_ms"] * 1e-3), 1),
             "unfused_ms_per_step_median": round(head_summary["unfused_ms"], 4),

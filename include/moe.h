@@ -355,6 +355,26 @@ moe_status moe_forward_fused_reroute(const float* logits, const void* x, int T, 
                                      int32_t* pair_pos, int32_t* n_kept, void* h, void* y_perm,
                                      void* y, void* ws, size_t ws_bytes, void* stream);
 
+/* moe_forward_fused with FP8 expert weights (NCCL EP page §2.1: FP8 expert
+ * compute with a scale tensor; MegaMoE comparison page, core differences §1:
+ * the layer as one kernel): w13_q / w2_q are the E4M3-FN codes and w13_s /
+ * w2_s the fp32 128 x 128 block scales that moe_quantize_fp8 makes from
+ * w13_packed / w2_packed; x, h, y_perm and y are bf16.  The GEMM phases run
+ * the FP8 pipelined body of moe_expert_ffn_fp8 (codes in LDS, converted to
+ * bf16 per MFMA operand, the running sum rescaled at each 128-deep K block),
+ * so the result has the same bits as moe_route -> moe_dispatch ->
+ * moe_expert_ffn_fp8 -> moe_combine wherever those calls run their
+ * pipelined kernels (more than 48 rows per expert on average).  Requires d
+ * and f multiples of 128 and at least 256 (the pipeline's depth), else
+ * MOE_ERR_UNSUPPORTED; the other arguments and errors as moe_forward_fused. */
+moe_status moe_forward_fused_fp8(const float* logits, const void* x, int T, int E, int k,
+                                 int gate, int capacity, int e_begin, int e_end, int d, int f,
+                                 const uint8_t* w13_q, const float* w13_s, const uint8_t* w2_q,
+                                 const float* w2_s, int32_t* topk_idx, float* topk_w,
+                                 int32_t* counts, int32_t* offsets, int32_t* sorted_pair,
+                                 int32_t* pair_pos, int32_t* n_kept, void* h, void* y_perm,
+                                 void* y, void* ws, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------------------
  * Backward pass (NCCL EP page §3.2, training adaptation: the backward step
  * reuses the forward's routing handle, sends the output gradient to the

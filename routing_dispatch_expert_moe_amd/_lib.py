@@ -81,6 +81,9 @@ SIGNATURES = {
     "moe_forward_fused_reroute": (_i, [_fp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _vp, _vp,
                                        _i32p, _fp, _i32p, _i32p, _i32p, _i32p, _i32p, _vp, _vp, _vp,
                                        _vp, _sz, _vp]),
+    "moe_forward_fused_fp8": (_i, [_fp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i, _vp, _fp, _vp,
+                                   _fp, _i32p, _fp, _i32p, _i32p, _i32p, _i32p, _i32p, _vp, _vp,
+                                   _vp, _vp, _sz, _vp]),
 }
 
 _lib = None

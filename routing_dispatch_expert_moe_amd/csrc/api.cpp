@@ -555,7 +555,10 @@ static moe_status forward_fused_impl(const float* logits, const void* x, int T, 
                                      int32_t* counts, int32_t* offsets, int32_t* sorted_pair,
                                      int32_t* pair_pos, int32_t* n_kept, void* h, void* y_perm,
                                      void* y, void* ws, size_t ws_bytes, void* stream,
-                                     bool reroute) {
+                                     bool reroute, const float* w13s = nullptr,
+                                     const float* w2s = nullptr) {
+  // w13s / w2s set: FP8 weights (codes in w13_packed / w2_packed, bf16 activations)
+  const bool fp8 = w13s != nullptr || w2s != nullptr;
   if (T < 0) return MOE_ERR_INVALID_ARG;
   moe_status st = check_topk(E, k);
   if (st != MOE_OK) return st;
@@ -567,10 +570,20 @@ static moe_status forward_fused_impl(const float* logits, const void* x, int T, 
   const int64_t max_rows = moe_max_rows(T, k, E_loc, capacity);
   // the two GEMMs' rules (shape, alignment) on the buffers they touch
   // GEMM1 reads x in place (rows gathered through sorted_pair)
-  st = check_ffn(x, offsets, E_loc, max_rows, d, f, dtype, w13_packed, h);
-  if (st != MOE_OK) return st;
-  st = check_ffn(h, offsets, E_loc, max_rows, d, f, dtype, w2_packed, y_perm);
-  if (st != MOE_OK) return st;
+  if (fp8) {
+    if (dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+    st = check_ffn_fp8(x, offsets, E_loc, max_rows, d, f, w13_packed, w13s, h);
+    if (st != MOE_OK) return st;
+    st = check_ffn_fp8(h, offsets, E_loc, max_rows, d, f, w2_packed, w2s, y_perm);
+    if (st != MOE_OK) return st;
+    // the pipelined FP8 body's depth
+    if (d < moe::fp8_pipe_min_k() || f < moe::fp8_pipe_min_k()) return MOE_ERR_UNSUPPORTED;
+  } else {
+    st = check_ffn(x, offsets, E_loc, max_rows, d, f, dtype, w13_packed, h);
+    if (st != MOE_OK) return st;
+    st = check_ffn(h, offsets, E_loc, max_rows, d, f, dtype, w2_packed, y_perm);
+    if (st != MOE_OK) return st;
+  }
   const double big = static_cast<double>(max_rows > T ? max_rows : T);
   if (dtype == MOE_BF16 && (big * (d > f ? d : f) * 2 >= 4294967296.0 ||
                             static_cast<double>(2) * f * d * 2 >= 4294967296.0))
@@ -602,6 +615,8 @@ static moe_status forward_fused_impl(const float* logits, const void* x, int T, 
   a.x = x;
   a.w13 = w13_packed;
   a.w2 = w2_packed;
+  a.w13s = w13s;
+  a.w2s = w2s;
   a.T = T;
   a.E = E;
   a.k = k;
@@ -642,7 +657,7 @@ static moe_status forward_fused_impl(const float* logits, const void* x, int T, 
   a.bar_gen = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + moe::kWsBarGen);
   a.bar_count = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + moe::kWsBarCount);
   a.bar_group = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + moe::kWsBarGroup);
-  return hip_status(moe::launch_fused(a, dtype == MOE_BF16, max_rows, stream));
+  return hip_status(moe::launch_fused(a, dtype == MOE_BF16, max_rows, stream, fp8));
 }
 
 moe_status moe_forward_fused(const float* logits, const void* x, int T, int E, int k, int gate,
@@ -667,6 +682,19 @@ moe_status moe_forward_fused_reroute(const float* logits, const void* x, int T, 
   return forward_fused_impl(logits, x, T, E, k, gate, capacity, e_begin, e_end, d, f, dtype,
                             w13_packed, w2_packed, topk_idx, topk_w, counts, offsets, sorted_pair,
                             pair_pos, n_kept, h, y_perm, y, ws, ws_bytes, stream, true);
+}
+
+moe_status moe_forward_fused_fp8(const float* logits, const void* x, int T, int E, int k,
+                                 int gate, int capacity, int e_begin, int e_end, int d, int f,
+                                 const uint8_t* w13_q, const float* w13_s, const uint8_t* w2_q,
+                                 const float* w2_s, int32_t* topk_idx, float* topk_w,
+                                 int32_t* counts, int32_t* offsets, int32_t* sorted_pair,
+                                 int32_t* pair_pos, int32_t* n_kept, void* h, void* y_perm,
+                                 void* y, void* ws, size_t ws_bytes, void* stream) {
+  if (!w13_s || !w2_s) return MOE_ERR_INVALID_ARG;
+  return forward_fused_impl(logits, x, T, E, k, gate, capacity, e_begin, e_end, d, f, MOE_BF16,
+                            w13_q, w2_q, topk_idx, topk_w, counts, offsets, sorted_pair, pair_pos,
+                            n_kept, h, y_perm, y, ws, ws_bytes, stream, false, w13_s, w2_s);
 }
 
 }  // extern "C"

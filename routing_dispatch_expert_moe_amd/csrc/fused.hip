@@ -149,8 +149,11 @@ __device__ __forceinline__ int sum_block_counts(const int* __restrict__ block_co
 template <bool BF16>
 constexpr int fused_threads() { return BF16 ? 512 : 256; }
 
-template <bool BF16>
+// FP8 (with BF16 only): the GEMM phases read E4M3 weight codes and their
+// block scales (a.w13s, a.w2s) through the FP8 pipelined body
+template <bool BF16, bool FP8 = false>
 __global__ __launch_bounds__(fused_threads<BF16>(), 1) void moe_fused_kernel(FusedArgs a) {
+  static_assert(BF16 || !FP8, "FP8 weights take bf16 activations");
   constexpr int NT = fused_threads<BF16>();
   constexpr int NWV = NT / kWave;  // waves per workgroup
   extern __shared__ uint4 lds[];
@@ -266,7 +269,51 @@ __global__ __launch_bounds__(fused_threads<BF16>(), 1) void moe_fused_kernel(Fus
   grid_barrier(a, G);
 
   // ---- 3 / 4: the two grouped GEMMs
-  if constexpr (BF16) {
+  if constexpr (FP8) {
+    // the FP8 weights' row splits: few rows per expert or a wide first half
+    // in 128-row tiles, long-K passes with few tiles in 256-row tiles plus
+    // 128-row remainder tiles, the others every row in 256-row tiles (the
+    // separate FP8 calls' split, whose 128-row remainder tiles measured
+    // slower where the bf16 pass rides remainders along)
+    const uint16_t* xp = static_cast<const uint16_t*>(a.x);
+    const uint16_t* w13 = static_cast<const uint16_t*>(a.w13);  // codes, read as bytes
+    uint16_t* h = static_cast<uint16_t*>(a.h);
+    if (a.ffn_all_rows || a.rows_up == kFusedWide) {
+      gemm_pipe_body<true, 128, 256, 4, ROWS_ALL, 8, false, true, 64>(
+          xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G, lds, prefix, segs, a.sorted_pair, k,
+          nullptr, nullptr, a.w13s);
+    } else if (a.rows_up == kFusedBigTail) {
+      gemm_pipe_body<true, 256, 256, 3, ROWS_BIG, 8, false, true, 64>(
+          xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G, lds, prefix, segs, a.sorted_pair, k,
+          nullptr, nullptr, a.w13s);
+      gemm_pipe_body<true, 128, 256, 4, ROWS_TAIL, 8, false, true, 64>(
+          xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G, lds, prefix, segs, a.sorted_pair, k,
+          nullptr, nullptr, a.w13s);
+    } else {
+      gemm_pipe_body<true, 256, 256, 3, ROWS_ALL, 8, false, true, 64>(
+          xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G, lds, prefix, segs, a.sorted_pair, k,
+          nullptr, nullptr, a.w13s);
+    }
+    grid_barrier(a, G);
+    const uint16_t* w2 = static_cast<const uint16_t*>(a.w2);
+    uint16_t* yp = static_cast<uint16_t*>(a.y_perm);
+    if (a.ffn_all_rows) {
+      gemm_pipe_body<false, 128, 256, 4, ROWS_ALL, 8, false, true, 64>(
+          h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G, lds, prefix, segs, nullptr, 1, nullptr,
+          nullptr, a.w2s);
+    } else if (a.rows_down == kFusedBigTail) {
+      gemm_pipe_body<false, 256, 256, 3, ROWS_BIG, 8, false, true, 64>(
+          h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G, lds, prefix, segs, nullptr, 1, nullptr,
+          nullptr, a.w2s);
+      gemm_pipe_body<false, 128, 256, 4, ROWS_TAIL, 8, false, true, 64>(
+          h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G, lds, prefix, segs, nullptr, 1, nullptr,
+          nullptr, a.w2s);
+    } else {
+      gemm_pipe_body<false, 256, 256, 3, ROWS_ALL, 8, false, true, 64>(
+          h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G, lds, prefix, segs, nullptr, 1, nullptr,
+          nullptr, a.w2s);
+    }
+  } else if constexpr (BF16) {
     const uint16_t* xp = static_cast<const uint16_t*>(a.x);
     const uint16_t* w13 = static_cast<const uint16_t*>(a.w13);
     uint16_t* h = static_cast<uint16_t*>(a.h);
@@ -339,12 +386,15 @@ constexpr size_t resolver_lds_bytes() {
   return m;
 }
 
-size_t fused_lds_bytes(int E, bool bf16) {
+size_t fused_lds_bytes(int E, bool bf16, bool fp8) {
   size_t plan = static_cast<size_t>(E) * kWords * sizeof(unsigned long long) +
                 2 * static_cast<size_t>(E) * sizeof(int);
   if (plan < resolver_lds_bytes()) plan = resolver_lds_bytes();
   size_t gemm = f32_lds_floats(true) * sizeof(float);
-  if (bf16) {
+  if (bf16 && fp8) {
+    gemm = pipe_lds_bytes(256, 256, 3, true, 64);
+    if (gemm < pipe_lds_bytes(128, 256, 4, true, 64)) gemm = pipe_lds_bytes(128, 256, 4, true, 64);
+  } else if (bf16) {
     // GEMM phases step K 64 deep (K = d or f, multiples of 64 for bf16)
     gemm = pipe_lds_bytes(256, 256, 2, false, 64);
     if (gemm < pipe_lds_bytes(128, 256, 3, false, 64)) gemm = pipe_lds_bytes(128, 256, 3, false, 64);
@@ -352,14 +402,17 @@ size_t fused_lds_bytes(int E, bool bf16) {
   return plan > gemm ? plan : gemm;
 }
 
-int launch_fused(const FusedArgs& a, bool bf16, int64_t max_rows, void* stream) {
+int launch_fused(const FusedArgs& a, bool bf16, int64_t max_rows, void* stream, bool fp8) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const size_t lds = fused_lds_bytes(a.E, bf16);
-  const void* kern = bf16 ? reinterpret_cast<const void*>(moe_fused_kernel<true>)
-                          : reinterpret_cast<const void*>(moe_fused_kernel<false>);
+  fp8 = fp8 && bf16;
+  const size_t lds = fused_lds_bytes(a.E, bf16, fp8);
+  const void* kern = fp8    ? reinterpret_cast<const void*>(moe_fused_kernel<true, true>)
+                     : bf16 ? reinterpret_cast<const void*>(moe_fused_kernel<true>)
+                            : reinterpret_cast<const void*>(moe_fused_kernel<false>);
   // the largest dynamic LDS any E can ask for
-  static LdsAttr attr[2];
-  if (int rc = set_dynamic_lds_once(kern, fused_lds_bytes(MOE_MAX_E, bf16), attr[bf16 ? 1 : 0]))
+  static LdsAttr attr[3];
+  if (int rc = set_dynamic_lds_once(kern, fused_lds_bytes(MOE_MAX_E, bf16, fp8),
+                                    attr[fp8 ? 2 : bf16 ? 1 : 0]))
     return rc;
   int occ = 0;
   const int threads = bf16 ? fused_threads<true>() : fused_threads<false>();

@@ -153,6 +153,8 @@ struct FusedArgs {
   const void* x;
   const void* w13;
   const void* w2;
+  const float* w13s;  // FP8 weights: the codes' 128 x 128 block scales (else null)
+  const float* w2s;
   int T, E, k, gate, capacity, e_begin, e_end, d, f;
   int ffn_all_rows;  // bf16: 1 = every row in 128-row tiles (few rows per expert)
   int rows_up, rows_down;  // bf16 GEMM phases (unless ffn_all_rows): a FusedRows value
@@ -182,8 +184,11 @@ constexpr size_t kWsBarGen = 128;
 constexpr size_t kWsBarCount = 256;
 constexpr size_t kWsBarGroup = 512;
 constexpr size_t kWsBarStride = 32;  // uint32 words = 128 bytes
-size_t fused_lds_bytes(int E, bool bf16);
-int launch_fused(const FusedArgs& a, bool bf16, int64_t max_rows, void* stream);
+size_t fused_lds_bytes(int E, bool bf16, bool fp8 = false);
+// fp8 (bf16 activations only): w13 / w2 hold E4M3 codes with block scales
+// w13s / w2s; their K (d and f) must be multiples of 128 and at least
+// fp8_pipe_min_k()
+int launch_fused(const FusedArgs& a, bool bf16, int64_t max_rows, void* stream, bool fp8 = false);
 
 int device_cu_count();
 

@@ -107,7 +107,13 @@ class MoELayer:
         if x.shape[0] != self.T:
             raise ValueError(f"layer was sized for T={self.T}, got {x.shape[0]}")
         if self.fp8:
-            raise NotImplementedError("the fused launch takes bf16 / fp32 weights")
+            if self.reroute:
+                raise NotImplementedError("the fused launch with FP8 weights routes without rerouting")
+            return ops.moe_forward_fused_fp8(logits, x, self.k, self.gate, self.capacity,
+                                             self.e_begin, self.e_end, self.w13, self.w13_scale,
+                                             self.w2, self.w2_scale, self.ws, self.plan,
+                                             self.topk_idx, self.topk_w, self.h, self.y_perm,
+                                             self.y)
         return ops.moe_forward_fused(logits, x, self.k, self.gate, self.capacity, self.e_begin,
                                      self.e_end, self.w13, self.w2, self.ws, self.plan,
                                      self.topk_idx, self.topk_w, self.h, self.y_perm, self.y,

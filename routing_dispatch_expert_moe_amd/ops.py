@@ -360,6 +360,22 @@ def moe_forward_fused(logits, x, k, gate, capacity, e_begin, e_end, w13_packed, 
     return y
 
 
+def moe_forward_fused_fp8(logits, x, k, gate, capacity, e_begin, e_end, w13_q, w13_s, w2_q, w2_s,
+                          ws, plan: DispatchPlan, topk_idx, topk_w, h, y_perm, y, stream=None):
+    """moe_forward_fused with FP8 expert weights (codes and block scales from
+    moe_quantize_fp8); bf16 activations, caller-provided outputs."""
+    T, E = logits.shape
+    d = x.shape[1]
+    f = w13_q.shape[1] // 2
+    check(lib().moe_forward_fused_fp8(
+        _ptr(logits), _ptr(x), T, E, k, _gate_code(gate), capacity, e_begin, e_end, d, f,
+        _ptr(w13_q), _ptr(w13_s), _ptr(w2_q), _ptr(w2_s), _ptr(topk_idx), _ptr(topk_w),
+        _ptr(plan.counts), _ptr(plan.offsets), _ptr(plan.sorted_pair), _ptr(plan.pair_pos),
+        _ptr(plan.n_kept), _ptr(h), _ptr(y_perm), _ptr(y), _ptr(ws), ws.numel(), _stream(stream)),
+        "moe_forward_fused_fp8")
+    return y
+
+
 # --------------------------------------------------------------------------
 # backward pass
 # --------------------------------------------------------------------------

@@ -34,7 +34,7 @@ def test_header_declares_the_path():
               "moe_pack_weights", "moe_check_error", "moe_ffn_up", "moe_ffn_down",
               "moe_forward_fused", "moe_quantize_fp8", "moe_expert_ffn_fp8", "moe_ffn_up_fp8",
               "moe_ffn_down_fp8", "moe_expert_ffn_list", "moe_ffn_up_list", "moe_ffn_down_list",
-              "moe_route_reroute", "moe_forward_fused_reroute"):
+              "moe_route_reroute", "moe_forward_fused_reroute", "moe_forward_fused_fp8"):
         assert n in names
 
 
@@ -236,6 +236,25 @@ def test_fused_validation(lib):
                  a["off"], a["sp"], a["pp"], a["nk"], a["h"], a["yp"], a["y"], a["ws"], a["wsb"],
                  None)
 
+    # FP8 weights: scales required, d and f multiples of 128 and at least 256
+    h8 = lib.moe_forward_fused_fp8
+
+    def call_8(**kw):
+        a = dict(ok, d=256, f=512, s13=FAKE, s2=FAKE)
+        a.update(kw)
+        return h8(a["lg"], a["x"], a["T"], a["E"], a["k"], a["gate"], a["cap"], a["e0"], a["e1"],
+                  a["d"], a["f"], a["w13"], a["s13"], a["w2"], a["s2"], a["idx"], a["w"],
+                  a["counts"], a["off"], a["sp"], a["pp"], a["nk"], a["h"], a["yp"], a["y"],
+                  a["ws"], a["wsb"], None)
+
+    assert call_8(s13=None) == L.MOE_ERR_INVALID_ARG
+    assert call_8(s2=None) == L.MOE_ERR_INVALID_ARG
+    assert call_8(d=192) == L.MOE_ERR_UNSUPPORTED        # not a multiple of the 128 scale block
+    assert call_8(d=128) == L.MOE_ERR_UNSUPPORTED        # below the pipeline's depth (256)
+    assert call_8(f=128) == L.MOE_ERR_UNSUPPORTED
+    assert call_8(k=9) == L.MOE_ERR_INVALID_TOPK
+    assert call_8(s13=MIS) == L.MOE_ERR_MISALIGNED
+    assert call_8(wsb=2047) == L.MOE_ERR_WORKSPACE
     assert call_r(k=9) == L.MOE_ERR_INVALID_TOPK
     assert call_r(gate=5) == L.MOE_ERR_INVALID_ARG
     assert call_r(y=MIS) == L.MOE_ERR_MISALIGNED

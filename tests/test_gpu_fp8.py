@@ -177,3 +177,65 @@ def test_decode_layer_fp8_sampled_tokens():
     err = O.rel_err(got[tokens], ref)
     log(f"decode fp8: {len(tokens)} tokens rel err {err:.2e}")
     assert err <= TOL
+
+
+@pytest.mark.parametrize("kw", [
+    # ~128 rows per expert: 256-row tiles over every row
+    dict(name="f8a", T=512, d=256, f=384, E=8, k=2),
+    # capacity drops and a local expert range, ~188 rows per expert
+    dict(name="f8b", T=600, d=256, f=256, E=16, k=4, capacity_factor=1.25, e_begin=2, e_end=14,
+         logit_bias="normal"),
+    # ~12 rows per expert: the fused launch's 128-row tiles (the separate calls
+    # run the code-streaming decode kernel, which sums in another order)
+    dict(name="f8c", T=200, d=512, f=256, E=32, k=2),
+    # a 4224-deep second GEMM with few tiles: 256-row tiles plus 128-row remainder tiles
+    dict(name="f8d", T=900, d=256, f=4224, E=4, k=1),
+])
+def test_fused_layer_fp8(kw):
+    """moe_forward_fused_fp8 against the separate FP8 calls (bit for bit where they
+    run the pipelined kernels) and the oracle on the dequantised weights."""
+    kw = dict(kw)
+    log(f"fused layer fp8 {kw}")
+    name = kw.pop("name")
+    wl = custom(name, seed=7, dtype="bf16", **kw)
+    w13, w2p, host = packed_weights(wl, keep_host=True)
+    q13, s13 = M.moe_quantize_fp8(w13)
+    q2, s2 = M.moe_quantize_fp8(w2p)
+    del w13, w2p
+    C = M.moe_capacity(wl.T, wl.k, wl.E, wl.capacity_factor)
+    assert C == O.capacity(wl.T, wl.k, wl.E, wl.capacity_factor)
+
+    def layer():
+        return M.MoELayer(q13, q2, E=wl.E, k=wl.k, gate=wl.gate, T=wl.T, capacity=C,
+                          e_begin=wl.e_begin, e_end=wl.e_end, w13_scale=s13, w2_scale=s2)
+
+    x = t_in(wl.x, "bf16")
+    lg = t_in(wl.logits, "f32")
+    sep = layer()
+    sep.forward(x, logits=lg)
+    assert M.moe_check_error(sep.ws) == 0
+    fl = layer()
+    fl.forward_fused(x, lg)
+    assert M.moe_check_error(fl.ws) == 0
+    a, b = sep.outputs(), fl.outputs()
+    n = int(t_out(a["n_kept"])[0])
+    assert int(t_out(b["n_kept"])[0]) == n
+    for key in ("topk_idx", "topk_w", "counts", "offsets", "pair_pos"):
+        assert np.array_equal(t_out(a[key]), t_out(b[key])), key
+    assert np.array_equal(t_out(a["sorted_pair"])[:n], t_out(b["sorted_pair"])[:n])
+    E_loc = wl.e_end - wl.e_begin
+    if M.moe_max_rows(wl.T, wl.k, E_loc, C) // E_loc > 48:   # separate calls: pipelined kernels
+        for key in ("h", "y_perm"):
+            assert np.array_equal(t_out(a[key])[:n], t_out(b[key])[:n]), key
+        assert np.array_equal(t_out(a["y"]), t_out(b["y"]))
+    h13, h2 = _host_packed(host, wl.f)
+    rq13, rs13 = F.quantize_blocks(h13)
+    rq2, rs2 = F.quantize_blocks(h2)
+    wf = F.expert_weights(rq13, rs13, rq2, rs2, wl.f)
+    ref = O.moe_layer(wl.x, "bf16", wl.logits, wl.k, wl.gate, wf, wl.E, C, wl.e_begin, wl.e_end)
+    assert np.array_equal(t_out(b["topk_idx"]), ref["topk_idx"])
+    assert O.rel_err(as64(fl.y, "bf16"), ref["y"]) <= TOL
+    y1 = t_out(fl.y).copy()
+    fl.forward_fused(x, lg)
+    assert M.moe_check_error(fl.ws) == 0
+    assert np.array_equal(t_out(fl.y), y1)
