@@ -19,7 +19,8 @@
 //      counts (workgroup 0 also writes counts / offsets / n_kept), then places
 //      the pairs of its slices of token blocks;
 //   4. GEMM1 + SwiGLU over the tile list (the pipelined MFMA body of the
-//      stand-alone kernels, or the fp32 body), reading each row straight from
+//      stand-alone kernels, for FP8 weights with few rows per expert their
+//      code-streaming body, or the fp32 body), reading each row straight from
 //      x through the dispatch permutation: no permuted copy is made (DWDP
 //      page, key optimisations: the row gather fused into the grouped GEMM);
 //   5. GEMM2;
@@ -33,6 +34,7 @@
 #include "common.h"
 #include "dispatch_dev.h"
 #include "gemm_f32.h"
+#include "gemm_fp8w.h"
 #include "gemm_pipe.h"
 #include "launch.h"
 #include "reroute_dev.h"
@@ -270,15 +272,22 @@ __global__ __launch_bounds__(fused_threads<BF16>(), 1) void moe_fused_kernel(Fus
 
   // ---- 3 / 4: the two grouped GEMMs
   if constexpr (FP8) {
-    // the FP8 weights' row splits: few rows per expert or a wide first half
-    // in 128-row tiles, long-K passes with few tiles in 256-row tiles plus
-    // 128-row remainder tiles, the others every row in 256-row tiles (the
-    // separate FP8 calls' split, whose 128-row remainder tiles measured
-    // slower where the bf16 pass rides remainders along)
+    // the FP8 weights' row splits, as in the separate FP8 calls: few rows per
+    // expert stream the codes through 32-row tiles (two 256-thread parts per
+    // workgroup, each on a tile of its own), a wide first half takes 128-row
+    // tiles, long-K passes with few tiles 256-row tiles plus 128-row
+    // remainder tiles, the others every row in 256-row tiles (128-row
+    // remainder tiles measured slower where the bf16 pass rides remainders
+    // along)
     const uint16_t* xp = static_cast<const uint16_t*>(a.x);
     const uint16_t* w13 = static_cast<const uint16_t*>(a.w13);  // codes, read as bytes
     uint16_t* h = static_cast<uint16_t*>(a.h);
-    if (a.ffn_all_rows || a.rows_up == kFusedWide) {
+    constexpr int kParts = NT / 256;
+    if (a.ffn_all_rows) {
+      gemm_fp8w_body<128, true, kParts>(xp, a.offsets, E_loc,
+                                        static_cast<const uint8_t*>(a.w13), a.w13s, h, a.f, a.d,
+                                        bid, G, lds, prefix, a.sorted_pair, k);
+    } else if (a.rows_up == kFusedWide) {
       gemm_pipe_body<true, 128, 256, 4, ROWS_ALL, 8, false, true, 64>(
           xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G, lds, prefix, segs, a.sorted_pair, k,
           nullptr, nullptr, a.w13s);
@@ -298,9 +307,8 @@ __global__ __launch_bounds__(fused_threads<BF16>(), 1) void moe_fused_kernel(Fus
     const uint16_t* w2 = static_cast<const uint16_t*>(a.w2);
     uint16_t* yp = static_cast<uint16_t*>(a.y_perm);
     if (a.ffn_all_rows) {
-      gemm_pipe_body<false, 128, 256, 4, ROWS_ALL, 8, false, true, 64>(
-          h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G, lds, prefix, segs, nullptr, 1, nullptr,
-          nullptr, a.w2s);
+      gemm_fp8w_body<128, false, kParts>(h, a.offsets, E_loc, static_cast<const uint8_t*>(a.w2),
+                                         a.w2s, yp, a.d, a.f, bid, G, lds, prefix);
     } else if (a.rows_down == kFusedBigTail) {
       gemm_pipe_body<false, 256, 256, 3, ROWS_BIG, 8, false, true, 64>(
           h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G, lds, prefix, segs, nullptr, 1, nullptr,
@@ -394,6 +402,8 @@ size_t fused_lds_bytes(int E, bool bf16, bool fp8) {
   if (bf16 && fp8) {
     gemm = pipe_lds_bytes(256, 256, 3, true, 64);
     if (gemm < pipe_lds_bytes(128, 256, 4, true, 64)) gemm = pipe_lds_bytes(128, 256, 4, true, 64);
+    constexpr size_t stream = fp8w_lds_bytes<128, true>(fused_threads<true>() / 256);
+    if (gemm < stream) gemm = stream;
   } else if (bf16) {
     // GEMM phases step K 64 deep (K = d or f, multiples of 64 for bf16)
     gemm = pipe_lds_bytes(256, 256, 2, false, 64);
