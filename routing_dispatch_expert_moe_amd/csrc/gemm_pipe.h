@@ -296,15 +296,18 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
   // LDS fragments of substep ks of the step held in buffer `buf` (FP8W: the
   // weight fragments' 16 codes of both K halves as read, fbr, converted to fb
   // by cvt_frags before the MFMAs that use them)
+  // (na: only the first NA of the wave's 32-row blocks, the ones holding rows
+  // of the segment)
   bf16x8_t fa[2][FM], fb[2][NQ];
   uint4 fbr[2][FP8W ? NQ : 1];
-  auto load_frags = [&](int buf, int ks, int slot) {
+  auto load_frags_n = [&](int buf, int ks, int slot, auto na) {
+    constexpr int NA = decltype(na)::value;
     const uint4* As = lds + buf * STAGE_U4;
     const uint4* Bs = As + BM * KC;
     const int ch = ks * 2 + (lane >> 5);
 #pragma unroll
     for (int i = 0; i < (FM > NQ ? FM : NQ); ++i) {
-      if (i < FM) {
+      if (i < NA) {
         const int r = wm * (BM / 2) + i * 32 + (lane & 31);
         fa[slot][i] = __builtin_bit_cast(bf16x8_t, As[r * KC + (ch ^ swz(r))]);
       }
@@ -320,6 +323,9 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
           fb[slot][i] = __builtin_bit_cast(bf16x8_t, Bs[q * KC + (ch ^ swz(q))]);
       }
     }
+  };
+  auto load_frags = [&](int buf, int ks, int slot) {
+    load_frags_n(buf, ks, slot, std::integral_constant<int, FM>{});
   };
   // FP8W: the scale of this wave's MFMA tile q (its weight rows' 128-row
   // block) in K block kb
@@ -372,12 +378,17 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
   constexpr int NMF = FM * NQ, NDS = FM + NQ, NVM = (LSTEP + 1) / 2;
   constexpr uint32_t kStepBytes = BK * 2;  // K bytes of one step in a row
 
-  auto mfma_substep = [&](f32x16_t (&acc)[FM][NQ], int slot) {
+  // (na: the MFMAs of the wave's first NA 32-row blocks only)
+  auto mfma_substep_n = [&](f32x16_t (&acc)[FM][NQ], int slot, auto na) {
+    constexpr int NA = decltype(na)::value;
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < NA; ++i)
 #pragma unroll
       for (int q = 0; q < NQ; ++q)
         acc[i][q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[slot][q], fa[slot][i], acc[i][q], 0, 0, 0);
+  };
+  auto mfma_substep = [&](f32x16_t (&acc)[FM][NQ], int slot) {
+    mfma_substep_n(acc, slot, std::integral_constant<int, FM>{});
   };
   // FP8W: after the last step of K block kb, acc *= s_kb / s_(kb+1) per MFMA
   // tile (s_KB = 1).  sc holds s_kb and s_(kb+1) of each tile; the scales of
@@ -392,7 +403,10 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
       sc[1][q] = kb + 2 < KB ? frag_scale(ct, q, kb + 2) : 1.f;
     }
   };
-  auto epilogue = [&](const Tile& ct, f32x16_t (&acc)[FM][NQ]) {
+  // (na: the wave's first NA 32-row blocks; the others hold no row of the
+  // segment)
+  auto epilogue_n = [&](const Tile& ct, f32x16_t (&acc)[FM][NQ], auto na) {
+    constexpr int NA = decltype(na)::value;
     const int valid = min(BM, ct.seg1 - ct.m0);
     // registers -> global.  The MFMAs take the weight fragment as their
     // first operand, so a 32 x 32 tile holds D[n][m] (n: output column, m:
@@ -419,7 +433,7 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
     };
     char* stg = reinterpret_cast<char*>(lds + STAGES * STAGE_U4) + wave * (32 * kOutRowBytes);
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
+    for (int i = 0; i < NA; ++i) {
       if (wm * (BM / 2) + i * 32 >= valid) continue;
       const int rbase = ct.m0 + wm * (BM / 2) + i * 32;
 #pragma unroll
@@ -482,6 +496,9 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
       }
     }
   };
+  auto epilogue = [&](const Tile& ct, f32x16_t (&acc)[FM][NQ]) {
+    epilogue_n(ct, acc, std::integral_constant<int, FM>{});
+  };
 
   if (KT >= STAGES) {
     // Straight-line steps: the issue side changes tile only at tile
@@ -517,12 +534,19 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
           sc[1][q] = KB > 1 ? frag_scale(ct, q, 1) : 1.f;
         }
       }
-      // The K loop of one tile.  ACT = false: this wave's rows of the tile
-      // are all past the segment (a tile less than half full), so it only
+      // The K loop of one tile.  NA = the wave's 32-row blocks that hold rows
+      // of the segment: the wave reads the fragments of and multiplies only
+      // those (its other blocks' rows are not stored).  NA = 0: the wave's
+      // rows are all past the segment (a tile less than half full), so it only
       // helps with the loads and barriers and issues no MFMAs (with 8 waves
-      // it leaves its SIMD's MFMA pipe to the other wave there).
+      // it leaves its SIMD's MFMA pipe to the other wave there).  The next
+      // step's first fragments are always read in full: they may belong to
+      // the next tile.
       auto run_tile = [&](auto act) {
-        constexpr bool ACT = decltype(act)::value;
+        constexpr int NA = decltype(act)::value;
+        constexpr bool ACT = NA > 0;
+        constexpr std::integral_constant<int, NA> na{};
+        constexpr int NMFA = NA * NQ;
         // one step: substep 0 fetches substep 1's fragments and sends the
         // second half of the pending step's loads between its MFMAs (BK =
         // 64: substeps 1 and 2 fetch the fragments of the substep after
@@ -530,27 +554,27 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
         // the first half of step s + STAGES's loads into this step's buffer
         // and fetches step s + 1's first fragments
         auto substep0 = [&](int s) {
-          if constexpr (ACT) load_frags(s % STAGES, 1, 1);
+          if constexpr (ACT) load_frags_n(s % STAGES, 1, 1, na);
           issue_part(1, pb, pk);
           if constexpr (ACT) {
             cvt_frags(0);
-            mfma_substep(acc, 0);
-            interleave<0, NMF, NDS, NVM>();
+            mfma_substep_n(acc, 0, na);
+            interleave<0, NMFA, NA + NQ, NVM>();
           }
           __builtin_amdgcn_sched_barrier(0);
           if constexpr (SUB == 4) {
             if constexpr (ACT) {
-              load_frags(s % STAGES, 2, 0);
+              load_frags_n(s % STAGES, 2, 0, na);
               cvt_frags(1);
-              mfma_substep(acc, 1);
-              interleave<0, NMF, NDS, 0>();
+              mfma_substep_n(acc, 1, na);
+              interleave<0, NMFA, NA + NQ, 0>();
             }
             __builtin_amdgcn_sched_barrier(0);
             if constexpr (ACT) {
-              load_frags(s % STAGES, 3, 1);
+              load_frags_n(s % STAGES, 3, 1, na);
               cvt_frags(0);
-              mfma_substep(acc, 0);
-              interleave<0, NMF, NDS, 0>();
+              mfma_substep_n(acc, 0, na);
+              interleave<0, NMFA, NA + NQ, 0>();
             }
             __builtin_amdgcn_sched_barrier(0);
           }
@@ -564,8 +588,8 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
           load_frags((s + 1) % STAGES, 0, 0);
           if constexpr (ACT) {
             cvt_frags(1);
-            mfma_substep(acc, 1);
-            interleave<0, NMF, NDS, NVM>();
+            mfma_substep_n(acc, 1, na);
+            interleave<0, NMFA, NDS, NVM>();
           }
           __builtin_amdgcn_sched_barrier(0);
           if constexpr (ACT && FP8W) {
@@ -590,10 +614,19 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
           substep0(s0 + kt);
           substep1(s0 + kt, more ? (kt + STAGES - KT) * kStepBytes : (KT - 1) * kStepBytes);
         }
+        epilogue_n(ct, acc, na);
       };
-      if (wm * (BM / 2) < ct.seg1 - ct.m0) run_tile(std::true_type{});
-      else run_tile(std::false_type{});
-      epilogue(ct, acc);
+      // the wave's rows in the segment: none, at most one 32-row block (the
+      // last tile of an expert with a few rows past a multiple of 256), or
+      // more (every block; the other partial counts measured no faster)
+      const int wrows = ct.seg1 - ct.m0 - wm * (BM / 2);
+      if (wrows > 32) {
+        run_tile(std::integral_constant<int, FM>{});
+      } else if (wrows <= 0) {
+        run_tile(std::integral_constant<int, 0>{});
+      } else {
+        run_tile(std::integral_constant<int, 1>{});
+      }
     }
   } else if constexpr (!FP8W) {
     // short K (fewer steps than stages): the issue side may run several
