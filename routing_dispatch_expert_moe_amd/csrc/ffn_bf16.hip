@@ -455,16 +455,22 @@ static int fp8_pipe_pass(bool up, const void* A, const int32_t* offsets, int E_l
   auto run = [&](PipeRows r) {
     return launch_gemm_pipe_fp8(r, up, A, offsets, E_loc, max_rows, wq, ws, C, N, K, stream);
   };
-  // 256-row tiles over every row, except for long-K passes with few tiles,
-  // whose short remainders take 128-row tiles as in the bf16 pass.  The
-  // bf16 pass's ride-along split measured slower here (Zipf-skewed prefill
-  // FFN 8.19 vs 7.74 ms): the FP8 128-row tiles convert codes with one wave
-  // per SIMD, so the experts below 128 rows go faster through 256-row tiles.
-  if (ffn_plan_bf16(up, max_rows, E_loc, d, f, device_cu_count()) == MOE_FFN_PLAN_BIG_TAIL) {
-    int e = run(PipeRows::kBigTiles);
-    return e != 0 ? e : run(PipeRows::kTailTiles);
+  // the bf16 pass's row classes: 256-row tiles then 128-row remainder tiles
+  // (long-K passes with few tiles), the ride-along split (many tiles: the
+  // experts below 128 rows stream their codes through 128-row tiles), else
+  // every row in 256-row tiles (the few-tile first half too)
+  switch (ffn_plan_bf16(up, max_rows, E_loc, d, f, device_cu_count())) {
+    case MOE_FFN_PLAN_BIG_TAIL: {
+      const int e = run(PipeRows::kBigTiles);
+      return e != 0 ? e : run(PipeRows::kTailTiles);
+    }
+    case MOE_FFN_PLAN_BIG_RIDE: {
+      const int e = run(PipeRows::kBigRide);
+      return e != 0 ? e : run(PipeRows::kTailRide);
+    }
+    default:
+      return run(PipeRows::kBigAll);
   }
-  return run(PipeRows::kBigAll);
 }
 int launch_ffn_up_fp8(const void* x_perm, const int32_t* offsets, int E_loc, int64_t max_rows,
                       int d, int f, const uint8_t* w13q, const float* w13s, void* h,

@@ -27,20 +27,22 @@ __global__ __launch_bounds__(pipe_waves<BM>() * 64, 1) void gemm_bf16_pipe(const
 
 // FP8 weights with many rows per expert: the bf16 kernels' tiles with the
 // weight tiles held in LDS as codes, 64-deep steps (a stage is 48 KB for
-// 256-row tiles, three stages; 32 KB for the 128-row remainder tiles, four)
-constexpr int kFp8BK = 64;
+// 256-row tiles, three stages; 32 KB for the 128-row remainder tiles, four).
+// Every tile runs 8 waves: each MFMA operand is converted from codes first,
+// and the second wave on a SIMD keeps its MFMA pipe busy meanwhile.
+constexpr int kFp8BK = 64, kFp8Waves = 8;
 template <int BM>
 constexpr int fp8_stages() { return BM == 256 ? 3 : 4; }
 
 template <bool SWIGLU, int BM, int CLASS>
-__global__ __launch_bounds__(pipe_waves<BM>() * 64, 1) void gemm_fp8_pipe(
+__global__ __launch_bounds__(kFp8Waves * 64, 1) void gemm_fp8_pipe(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets, int E_loc,
     const uint8_t* __restrict__ Wq, const float* __restrict__ Ws, uint16_t* __restrict__ C,
     int N, int K) {
   extern __shared__ uint4 lds[];
   __shared__ int prefix[MOE_MAX_E + 1];
   __shared__ int segs[MOE_MAX_E + 1];
-  gemm_pipe_body<SWIGLU, BM, 256, fp8_stages<BM>(), CLASS, pipe_waves<BM>(), false, true, kFp8BK>(
+  gemm_pipe_body<SWIGLU, BM, 256, fp8_stages<BM>(), CLASS, kFp8Waves, false, true, kFp8BK>(
       A, offsets, E_loc, reinterpret_cast<const uint16_t*>(Wq), C, N, K, blockIdx.x, gridDim.x,
       lds, prefix, segs, nullptr, 1, nullptr, nullptr, Ws);
 }
@@ -68,7 +70,7 @@ int launch_fp8(const void* A, const int32_t* offsets, int E_loc, int64_t max_row
   if (grid > tiles_ub) grid = tiles_ub;
   if (grid >= 8) grid &= ~static_cast<int64_t>(7);
   if (grid < 1) grid = 1;
-  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(pipe_waves<BM>() * 64), lds, s,
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(kFp8Waves * 64), lds, s,
                      static_cast<const uint16_t*>(A), offsets, E_loc, Wq, Ws,
                      static_cast<uint16_t*>(C), N, K);
   return static_cast<int>(hipGetLastError());
@@ -83,6 +85,10 @@ int launch_fp8_kind(PipeRows rows, const void* A, const int32_t* offsets, int E_
       return launch_fp8<SWIGLU, 256, ROWS_BIG>(A, offsets, E_loc, max_rows, Wq, Ws, C, N, K, s);
     case PipeRows::kTailTiles:
       return launch_fp8<SWIGLU, 128, ROWS_TAIL>(A, offsets, E_loc, max_rows, Wq, Ws, C, N, K, s);
+    case PipeRows::kBigRide:
+      return launch_fp8<SWIGLU, 256, ROWS_BIGR>(A, offsets, E_loc, max_rows, Wq, Ws, C, N, K, s);
+    case PipeRows::kTailRide:
+      return launch_fp8<SWIGLU, 128, ROWS_TAILR>(A, offsets, E_loc, max_rows, Wq, Ws, C, N, K, s);
     default:
       return launch_fp8<SWIGLU, 256, ROWS_ALL>(A, offsets, E_loc, max_rows, Wq, Ws, C, N, K, s);
   }

@@ -276,9 +276,8 @@ __global__ __launch_bounds__(fused_threads<BF16>(), 1) void moe_fused_kernel(Fus
     // expert stream the codes through 32-row tiles (two 256-thread parts per
     // workgroup, each on a tile of its own), a wide first half takes 128-row
     // tiles, long-K passes with few tiles 256-row tiles plus 128-row
-    // remainder tiles, the others every row in 256-row tiles (128-row
-    // remainder tiles measured slower where the bf16 pass rides remainders
-    // along)
+    // remainder tiles, passes with many tiles the ride-along split, the
+    // others every row in 256-row tiles
     const uint16_t* xp = static_cast<const uint16_t*>(a.x);
     const uint16_t* w13 = static_cast<const uint16_t*>(a.w13);  // codes, read as bytes
     uint16_t* h = static_cast<uint16_t*>(a.h);
@@ -298,6 +297,13 @@ __global__ __launch_bounds__(fused_threads<BF16>(), 1) void moe_fused_kernel(Fus
       gemm_pipe_body<true, 128, 256, 4, ROWS_TAIL, 8, false, true, 64>(
           xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G, lds, prefix, segs, a.sorted_pair, k,
           nullptr, nullptr, a.w13s);
+    } else if (a.rows_up == kFusedRide) {
+      gemm_pipe_body<true, 256, 256, 3, ROWS_BIGR, 8, false, true, 64>(
+          xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G, lds, prefix, segs, a.sorted_pair, k,
+          nullptr, nullptr, a.w13s);
+      gemm_pipe_body<true, 128, 256, 4, ROWS_TAILR, 8, false, true, 64>(
+          xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G, lds, prefix, segs, a.sorted_pair, k,
+          nullptr, nullptr, a.w13s);
     } else {
       gemm_pipe_body<true, 256, 256, 3, ROWS_ALL, 8, false, true, 64>(
           xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G, lds, prefix, segs, a.sorted_pair, k,
@@ -314,6 +320,13 @@ __global__ __launch_bounds__(fused_threads<BF16>(), 1) void moe_fused_kernel(Fus
           h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G, lds, prefix, segs, nullptr, 1, nullptr,
           nullptr, a.w2s);
       gemm_pipe_body<false, 128, 256, 4, ROWS_TAIL, 8, false, true, 64>(
+          h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G, lds, prefix, segs, nullptr, 1, nullptr,
+          nullptr, a.w2s);
+    } else if (a.rows_down == kFusedRide) {
+      gemm_pipe_body<false, 256, 256, 3, ROWS_BIGR, 8, false, true, 64>(
+          h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G, lds, prefix, segs, nullptr, 1, nullptr,
+          nullptr, a.w2s);
+      gemm_pipe_body<false, 128, 256, 4, ROWS_TAILR, 8, false, true, 64>(
           h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G, lds, prefix, segs, nullptr, 1, nullptr,
           nullptr, a.w2s);
     } else {
