@@ -194,6 +194,9 @@ def test_decode_layer_fp8_sampled_tokens():
     dict(name="f8e", T=96, d=640, f=384, E=23, k=3),
     # a 4224-deep second GEMM with few tiles: 256-row tiles plus 128-row remainder tiles
     dict(name="f8d", T=900, d=256, f=4224, E=4, k=1),
+    # 64 experts x 16 weight tiles in the first GEMM (many tiles): the ride-along
+    # split, 8 experts of 128 rows or more in 256-row tiles, 56 below in 128-row tiles
+    dict(name="f8f", T=1024, d=256, f=2048, E=64, k=4, logit_bias="normal"),
 ])
 def test_fused_layer_fp8(kw):
     """moe_forward_fused_fp8 against the separate FP8 calls (bit for bit: the
@@ -230,6 +233,10 @@ def test_fused_layer_fp8(kw):
     for key in ("h", "y_perm"):
         assert np.array_equal(t_out(a[key])[:n], t_out(b[key])[:n]), key
     assert np.array_equal(t_out(a["y"]), t_out(b["y"]))
+    if name == "f8f":
+        cu = torch.cuda.get_device_properties(DEV).multi_processor_count
+        mr = M.moe_max_rows(wl.T, wl.k, wl.E_loc, C)
+        assert M.moe_ffn_plan("up", mr, wl.E_loc, wl.d, wl.f, "bf16", cu) == "big_ride"
     if name == "f8e":
         # the case is meant to leave a part idle: an odd 32-row tile count
         rows = np.diff(t_out(b["offsets"]).astype(np.int64))
