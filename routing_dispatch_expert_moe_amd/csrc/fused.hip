@@ -373,9 +373,11 @@ __global__ __launch_bounds__(fused_threads<BF16>(), 1) void moe_fused_kernel(Fus
       gemm_pipe_body<false, 128, 256, 3, ROWS_TAILR, 8, false, false, 64>(h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G,
                                                 lds, prefix, segs);
     } else {
+      // few tiles (the split's condition): the remainders in 128 x 128 tiles,
+      // twice as many as with 256 weight rows, as the separate call runs them
       gemm_pipe_body<false, 256, 256, 2, ROWS_BIG, 8, false, false, 64>(h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G, lds,
                                               prefix, segs);
-      gemm_pipe_body<false, 128, 256, 3, ROWS_TAIL, 8, false, false, 64>(h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G,
+      gemm_pipe_body<false, 128, 128, 4, ROWS_TAIL, 8, false, false, 64>(h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G,
                                                lds, prefix, segs);
     }
   } else {
@@ -421,6 +423,7 @@ size_t fused_lds_bytes(int E, bool bf16, bool fp8) {
     // GEMM phases step K 64 deep (K = d or f, multiples of 64 for bf16)
     gemm = pipe_lds_bytes(256, 256, 2, false, 64);
     if (gemm < pipe_lds_bytes(128, 256, 3, false, 64)) gemm = pipe_lds_bytes(128, 256, 3, false, 64);
+    if (gemm < pipe_lds_bytes(128, 128, 4, false, 64)) gemm = pipe_lds_bytes(128, 128, 4, false, 64);
   }
   return plan > gemm ? plan : gemm;
 }

@@ -192,7 +192,10 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
   constexpr int LSTEP = LA + LB;
   constexpr int BROW_U4 = FP8W ? FPR : KC;    // 16-byte chunks per weight row per step
   constexpr int STAGE_U4 = BM * KC + BNW * BROW_U4;
-  static_assert(FM >= 1 && NQ >= 2 && LB >= 1 && (FP8W || LB % 2 == 0), "unsupported tile");
+  // (SwiGLU: a wave's blocks are W1 blocks and the matching W3 blocks, so at
+  // least two; 128 x 128 tiles with 8 waves give the other pass one)
+  static_assert(FM >= 1 && NQ >= (SWIGLU ? 2 : 1) && LB >= 1 && (FP8W || LB % 2 == 0),
+                "unsupported tile");
   static_assert((STAGES - 2) * LSTEP < 64, "outstanding loads exceed the vmcnt range");
   // 256-row bf16 tiles stage each 32 x 32 output block through LDS (the
   // bytes after the pipeline stages, pipe_lds_bytes) so that every store

@@ -34,6 +34,9 @@ TOL = {"f32": 1e-5, "bf16": 1e-2}
     # 1000 local experts: the workgroup scan's runs of two experts per thread
     # (512 threads) and the widest routing phase
     dict(name="b9", T=300, d=64, f=64, E=1000, k=2, dtype="bf16", logit_bias="zipf"),
+    # a 4224-deep second GEMM with few tiles: 256-row tiles over the full blocks,
+    # the short remainders in 128 x 128 tiles
+    dict(name="b10", T=1200, d=256, f=4224, E=4, k=1, dtype="bf16"),
 ])
 def test_fused_layer(kw):
     kw = dict(kw)
