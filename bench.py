@@ -750,6 +750,7 @@ def run_workload(args, wl, weights, dev, headline):
 
     # the same layer as one fused persistent launch (router logits stay a separate call)
     fused_ms = None
+    fused_orders = None
     # (FP8 weights: moe_forward_fused_fp8, which routes without rerouting)
     if not (args.no_fused or (fp8 and reroute)):
         fev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
@@ -761,15 +762,26 @@ def run_workload(args, wl, weights, dev, headline):
             layer.forward_fused(x, lg)
             if ev is not None:
                 ev[1].record()
-        for _ in range(args.warmup):
-            fused_step()
-        torch.cuda.synchronize()
-        for s in range(K):
-            fused_step(fev[s])
-        torch.cuda.synchronize()
-        if M.moe_check_error(layer.ws) != 0:
-            raise RuntimeError("device error in the fused layer")
-        fused_ms = float(np.median([e[0].elapsed_time(e[1]) for e in fev]))
+        def time_fused():
+            for _ in range(args.warmup):
+                fused_step()
+            torch.cuda.synchronize()
+            for s in range(K):
+                fused_step(fev[s])
+            torch.cuda.synchronize()
+            if M.moe_check_error(layer.ws) != 0:
+                raise RuntimeError("device error in the fused layer")
+            return float(np.median([e[0].elapsed_time(e[1]) for e in fev]))
+        fused_ms = time_fused()  # the library's own choice of GEMM-phase order
+        # both orders of the two GEMM phases, forced: a device-wide barrier
+        # between them, and per-expert waits (where possible)
+        fused_orders = {}
+        try:
+            for mode in ("never", "always"):
+                M.moe_set_fused_overlap(mode)
+                fused_orders[mode] = time_fused()
+        finally:
+            M.moe_set_fused_overlap("auto")
     unfused_ms = float(np.median([events[s][0].elapsed_time(events[s][6]) for s in range(K)]))
 
     model = work_model(wl, n, touched, T_read, wb=(1 + 4.0 / (128 * 128)) if fp8 else None)
@@ -797,7 +809,7 @@ def run_workload(args, wl, weights, dev, headline):
     res = {"wl": wl, "layer": layer, "x": x, "logits": logits, "wg": wg, "host_w": host_w,
            "w13_t": w13_t, "w2_t": w2_t, "n": n, "touched": touched, "T_read": T_read, "C": C,
            "ms_step": ms_step, "per": per, "cold": cold, "cold_step": cold_step,
-           "fused_ms": fused_ms, "unfused_ms": unfused_ms, "model": model, "flops": flops,
+           "fused_ms": fused_ms, "fused_orders": fused_orders, "unfused_ms": unfused_ms, "model": model, "flops": flops,
            "bytes": bytes_, "copy_ms": copy_ms, "smi": (smi_before, smi_after), "fp8": fp8,
            "reroute": reroute, "plan_up": plan_code,
            "rows_per_expert": [int(kept.min()), int(kept.max())]}
@@ -871,8 +883,21 @@ def summary_of(args, r):
     if r["fused_ms"] is not None:
         out["fused"] = {"ms_per_step_median": round(r["fused_ms"], 4),
                         "unfused_ms_per_step_median": round(r["unfused_ms"], 4),
-                        "speedup_vs_unfused": round(r["unfused_ms"] / r["fused_ms"], 3)}
+                        "speedup_vs_unfused": round(r["unfused_ms"] / r["fused_ms"], 3),
+                        **fused_orders_out(r)}
     return out
+
+
+def fused_orders_out(r):
+    """The fused launch's time with each order of its GEMM phases forced."""
+    o = r.get("fused_orders")
+    if not o:
+        return {}
+    return {"barrier_ms_per_step_median": round(o["never"], 4),
+            "overlap_ms_per_step_median": round(o["always"], 4),
+            "orders_note": "moe_set_fused_overlap forced: a device-wide barrier between the "
+                           "GEMM phases, then per-expert waits; ms_per_step_median is the "
+                           "library's automatic choice"}
 
 
 def main(argv=None):
@@ -925,6 +950,7 @@ def main(argv=None):
                          f"to the sample), whole layer in float64 (router..combine), "
                          f"{passes} pass(es), {dt:.1f} s timed"}
     head_summary = {k: r[k] for k in ("fused_ms", "unfused_ms")}
+    head_orders = fused_orders_out(r)
     smi_before, smi_after = r["smi"]
     copy_ms = r["copy_ms"]
     tflops = r["flops"] / (ms_step * 1e-3) / 1e12
@@ -965,7 +991,8 @@ def main(argv=None):
             "ms_per_step_median": round(head_summary["fused_ms"], 4),
             "tokens_per_s": round(wl.T / (head_summary["fused_ms"] * 1e-3), 1),
             "unfused_ms_per_step_median": round(head_summary["unfused_ms"], 4),
-            "speedup_vs_unfused": round(head_summary["unfused_ms"] / head_summary["fused_ms"], 3)},
+            "speedup_vs_unfused": round(head_summary["unfused_ms"] / head_summary["fused_ms"], 3),
+            **head_orders},
     }
     del r
     others_out = {}

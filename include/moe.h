@@ -89,7 +89,9 @@ int moe_last_hip_error(void);
 
 /* Bytes of workspace needed by moe_dispatch and moe_expert_ffn (and the
  * device error word read by moe_check_error) for T tokens, E global experts,
- * top-k k and E_loc local experts.  Returns 0 if the sizes are invalid.
+ * top-k k and E_loc local experts; it also holds the rerouting scratch and
+ * the fused launch's per-expert readiness counters (E_loc words).  Returns 0
+ * if the sizes are invalid.
  * The workspace must be zero-filled once before its first use; the library
  * keeps it consistent afterwards. */
 size_t moe_workspace_bytes(int T, int E, int k, int E_loc);
@@ -327,9 +329,15 @@ moe_status moe_check_error(void* ws, void* stream);
  * MOE_ERR_UNSUPPORTED).  One workgroup per CU at most; phases are
  * separated by device-wide barriers whose words live in the workspace header
  * (zero-filled once, as for every call), so two fused calls that share a
- * workspace must not run concurrently.  A barrier that does not complete
- * within seconds sets the device error word (see moe_check_error) instead of
- * hanging the GPU. */
+ * workspace must not run concurrently.  The two GEMM phases may instead
+ * overlap per expert (see moe_set_fused_overlap): a second-GEMM tile of
+ * expert e starts once every first-GEMM tile of e is stored (a per-expert
+ * counter in the workspace, released and acquired at device scope); that
+ * needs a workspace of moe_workspace_bytes(T, E, k, e_end - e_begin) bytes,
+ * and with a smaller one (at least the dispatch scratch) a barrier separates
+ * them.  Both orders give the same bits.  A barrier or wait that does not
+ * complete within seconds sets the device error word (see moe_check_error)
+ * instead of hanging the GPU. */
 moe_status moe_forward_fused(const float* logits, const void* x, int T, int E, int k, int gate,
                              int capacity, int e_begin, int e_end, int d, int f, moe_dtype dtype,
                              const void* w13_packed, const void* w2_packed, int32_t* topk_idx,
@@ -337,6 +345,24 @@ moe_status moe_forward_fused(const float* logits, const void* x, int T, int E, i
                              int32_t* sorted_pair, int32_t* pair_pos, int32_t* n_kept,
                              void* h, void* y_perm, void* y, void* ws, size_t ws_bytes,
                              void* stream);
+
+/* How moe_forward_fused (and its rerouting and FP8 forms) orders its two GEMM
+ * phases, for every later call in the process (default MOE_OVERLAP_AUTO):
+ *   MOE_OVERLAP_NEVER   a device-wide barrier between them;
+ *   MOE_OVERLAP_AUTO    per-expert waits where they measured faster: when
+ *                       every row runs in 128-row tiles (at most 48 rows per
+ *                       local expert on average), else the barrier;
+ *   MOE_OVERLAP_ALWAYS  per-expert waits wherever they are possible (bf16,
+ *                       both GEMM phases on the pipelined tiles, a workspace
+ *                       of moe_workspace_bytes).
+ * The waits let a second-GEMM tile start once its expert's first-GEMM tiles
+ * are all stored (MegaMoE comparison page, core differences §1: the stages
+ * of different experts overlap).  Every mode gives the same bits.  Returns
+ * MOE_ERR_INVALID_ARG for any other value. */
+#define MOE_OVERLAP_NEVER 0
+#define MOE_OVERLAP_AUTO 1
+#define MOE_OVERLAP_ALWAYS 2
+moe_status moe_set_fused_overlap(int mode);
 
 /* moe_forward_fused with moe_route_reroute's routing (sparse-activation page
  * §3.2 stage 3, capacity-overflow rerouting in token order) in place of

@@ -21,6 +21,9 @@ MOE_ERR_HIP = 6
 
 MOE_F32 = 0
 MOE_BF16 = 1
+MOE_OVERLAP_NEVER = 0
+MOE_OVERLAP_AUTO = 1
+MOE_OVERLAP_ALWAYS = 2
 MOE_GATE_SOFTMAX_TOPK_RENORM = 0
 MOE_GATE_SIGMOID_TOPK_NORM = 1
 MOE_FFN_PLAN_NONE = 0
@@ -84,6 +87,7 @@ SIGNATURES = {
     "moe_forward_fused_fp8": (_i, [_fp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i, _vp, _fp, _vp,
                                    _fp, _i32p, _fp, _i32p, _i32p, _i32p, _i32p, _i32p, _vp, _vp,
                                    _vp, _vp, _sz, _vp]),
+    "moe_set_fused_overlap": (_i, [_i]),
 }
 
 _lib = None

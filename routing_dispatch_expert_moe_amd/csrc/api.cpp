@@ -5,6 +5,7 @@
 // after validation do the entry points call the launchers.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
 #include <cstring>
 
@@ -14,6 +15,9 @@
 namespace {
 
 thread_local int g_last_hip_error = 0;
+
+// how the fused launch orders its two GEMM phases (moe_set_fused_overlap)
+std::atomic<int> g_fused_overlap{MOE_OVERLAP_AUTO};
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -166,7 +170,7 @@ int moe_last_hip_error(void) { return g_last_hip_error; }
 size_t moe_workspace_bytes(int T, int E, int k, int E_loc) {
   if (T < 0 || E < 1 || E > MOE_MAX_E || k < 1 || k > MOE_MAX_K || k > E || E_loc < 1 || E_loc > E)
     return 0;
-  return moe::dispatch_ws_bytes(T, E) + moe::reroute_ws_bytes(T, k);
+  return moe::dispatch_ws_bytes(T, E) + moe::reroute_ws_bytes(T, k) + moe::ready_ws_bytes(E_loc);
 }
 
 int64_t moe_capacity(int T, int k, int E, int64_t cf_num, int64_t cf_den) {
@@ -657,7 +661,30 @@ static moe_status forward_fused_impl(const float* logits, const void* x, int T, 
   a.bar_gen = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + moe::kWsBarGen);
   a.bar_count = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + moe::kWsBarCount);
   a.bar_group = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + moe::kWsBarGroup);
+  // GEMM1 -> GEMM2 per expert instead of a barrier.  Possible when both
+  // phases run the pipelined body (bf16; FP8 unless its code-streaming body
+  // runs), the workspace holds the counters and their largest value,
+  // max_rows * f / 32, fits 32 bits.  Chosen (auto) when every row goes to
+  // 128-row tiles: each expert is one M-tile, so no weight tile is shared
+  // between tiles and the consumer's acquire (which invalidates the L2)
+  // costs no re-fetch; with several M-tiles per expert it measured slower
+  // than the barrier.
+  const size_t ready_at = moe::dispatch_ws_bytes(T, E) + moe::reroute_ws_bytes(T, k);
+  const bool can_overlap = dtype == MOE_BF16 && !(fp8 && a.ffn_all_rows) &&
+                           ws_bytes >= ready_at + moe::ready_ws_bytes(E_loc) &&
+                           static_cast<double>(max_rows) * (f / 32) < 4294967296.0;
+  const int mode = g_fused_overlap.load(std::memory_order_relaxed);
+  a.overlap = can_overlap && (mode == MOE_OVERLAP_ALWAYS ||
+                              (mode == MOE_OVERLAP_AUTO && a.ffn_all_rows != 0));
+  a.up_ready = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + ready_at);
   return hip_status(moe::launch_fused(a, dtype == MOE_BF16, max_rows, stream, fp8));
+}
+
+moe_status moe_set_fused_overlap(int mode) {
+  if (mode != MOE_OVERLAP_NEVER && mode != MOE_OVERLAP_AUTO && mode != MOE_OVERLAP_ALWAYS)
+    return MOE_ERR_INVALID_ARG;
+  g_fused_overlap.store(mode, std::memory_order_relaxed);
+  return MOE_OK;
 }
 
 moe_status moe_forward_fused(const float* logits, const void* x, int T, int E, int k, int gate,

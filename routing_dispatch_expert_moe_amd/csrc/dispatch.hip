@@ -16,6 +16,10 @@ size_t reroute_ws_bytes(int T, int k) {
   return 2 * ((n * 4 + 255) & ~static_cast<size_t>(255)) + ((masks + 255) & ~static_cast<size_t>(255));
 }
 
+size_t ready_ws_bytes(int E_loc) {
+  return (static_cast<size_t>(E_loc) * sizeof(uint32_t) + 255) & ~static_cast<size_t>(255);
+}
+
 DispatchWs dispatch_ws(void* ws, int T, int E) {
   const size_t nb = (static_cast<size_t>(T) + kTB - 1) / kTB;
   char* p = static_cast<char*>(ws);

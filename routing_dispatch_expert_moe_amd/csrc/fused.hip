@@ -27,7 +27,11 @@
 //   6. weighted combine (one wave per token).
 // Phases are separated by a device-wide barrier (arrival counters +
 // generation word in the workspace header; agent-scope release / acquire, so
-// rows written through one XCD's L2 are seen by the others).  The bodies are the
+// rows written through one XCD's L2 are seen by the others), except GEMM1 and
+// GEMM2 when both run the pipelined body and the workspace holds the
+// per-expert readiness counters: then a GEMM2 tile waits only for its own
+// expert's GEMM1 rows, so workgroups that run out of GEMM1 tiles start on the
+// experts already done instead of idling at a barrier.  The bodies are the
 // same device functions the stand-alone kernels run, so both paths compute
 // identical bits.
 #include "combine_dev.h"
@@ -148,14 +152,25 @@ __device__ __forceinline__ int sum_block_counts(const int* __restrict__ block_co
   return c;
 }
 
+// tile shape of one pipelined GEMM phase: BM activation rows x BNW weight
+// rows, STAGES pipeline stages, the rows of class CLASS
+template <int BM_, int BNW_, int STAGES_, int CLASS_>
+struct TileCfg {
+  static constexpr int BM = BM_, BNW = BNW_, STAGES = STAGES_, CLASS = CLASS_;
+};
+
 template <bool BF16>
 constexpr int fused_threads() { return BF16 ? 512 : 256; }
 
 // FP8 (with BF16 only): the GEMM phases read E4M3 weight codes and their
 // block scales (a.w13s, a.w2s) through the FP8 pipelined body
-template <bool BF16, bool FP8 = false>
+// OVERLAP: the GEMM phases meet through the per-expert readiness counters
+// instead of a barrier (a separate instantiation, so the barrier form's GEMM
+// loops carry none of the waiting code)
+template <bool BF16, bool FP8 = false, bool OVERLAP = false>
 __global__ __launch_bounds__(fused_threads<BF16>(), 1) void moe_fused_kernel(FusedArgs a) {
   static_assert(BF16 || !FP8, "FP8 weights take bf16 activations");
+  static_assert(BF16 || !OVERLAP, "the fp32 GEMM body does not count its tiles");
   constexpr int NT = fused_threads<BF16>();
   constexpr int NWV = NT / kWave;  // waves per workgroup
   extern __shared__ uint4 lds[];
@@ -256,6 +271,11 @@ __global__ __launch_bounds__(fused_threads<BF16>(), 1) void moe_fused_kernel(Fus
   if (bid == 0) {
     for (int i = threadIdx.x; i <= E_loc; i += blockDim.x) a.offsets[i] = segs[i];
     if (threadIdx.x == 0) *a.n_kept = segs[E_loc];
+    // the GEMM1 readiness counts start at zero (the barrier below publishes it
+    // before any tile adds to them)
+    if (OVERLAP)
+      for (int i = threadIdx.x; i < E_loc; i += blockDim.x)
+        __hip_atomic_store(a.up_ready + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   const int slices = nb > 0 ? max(1, min(kTB / 4, G / nb)) : 1;
   const int per_slice = (kTB + slices - 1) / slices;
@@ -270,7 +290,30 @@ __global__ __launch_bounds__(fused_threads<BF16>(), 1) void moe_fused_kernel(Fus
   }
   grid_barrier(a, G);
 
-  // ---- 3 / 4: the two grouped GEMMs
+  // ---- 3 / 4: the two grouped GEMMs.  With OVERLAP (every GEMM phase on
+  // the pipelined body) no barrier separates them: GEMM1 tiles count their
+  // stored rows per expert in a.up_ready and a GEMM2 tile of expert e starts
+  // once e's count is complete (MegaMoE comparison page, core differences §1:
+  // the stages of different experts overlap instead of waiting for each
+  // other).  A workgroup runs all its GEMM1 tiles before any GEMM2 tile and
+  // every workgroup is resident, so every wait ends.
+  // (the launcher never picks OVERLAP with the FP8 code-streaming body,
+  // which does not count its tiles)
+  uint32_t* up = OVERLAP ? a.up_ready : nullptr;
+  auto pipe_up = [&](auto cfg, const uint16_t* w, const float* ws) {
+    using C = decltype(cfg);
+    gemm_pipe_body<true, C::BM, C::BNW, C::STAGES, C::CLASS, 8, false, FP8, 64>(
+        static_cast<const uint16_t*>(a.x), a.offsets, E_loc, w, static_cast<uint16_t*>(a.h), a.f,
+        a.d, bid, G, lds, prefix, segs, a.sorted_pair, k, nullptr, nullptr, ws, up, nullptr,
+        a.err);
+  };
+  auto pipe_down = [&](auto cfg, const uint16_t* w, const float* ws) {
+    using C = decltype(cfg);
+    gemm_pipe_body<false, C::BM, C::BNW, C::STAGES, C::CLASS, 8, false, FP8, 64>(
+        static_cast<const uint16_t*>(a.h), a.offsets, E_loc, w, static_cast<uint16_t*>(a.y_perm),
+        a.d, a.f, bid, G, lds, prefix, segs, nullptr, 1, nullptr, nullptr, ws, nullptr, up,
+        a.err);
+  };
   if constexpr (FP8) {
     // the FP8 weights' row splits, as in the separate FP8 calls: few rows per
     // expert stream the codes through 32-row tiles (two 256-thread parts per
@@ -278,107 +321,68 @@ __global__ __launch_bounds__(fused_threads<BF16>(), 1) void moe_fused_kernel(Fus
     // tiles, long-K passes with few tiles 256-row tiles plus 128-row
     // remainder tiles, passes with many tiles the ride-along split, the
     // others every row in 256-row tiles
-    const uint16_t* xp = static_cast<const uint16_t*>(a.x);
     const uint16_t* w13 = static_cast<const uint16_t*>(a.w13);  // codes, read as bytes
-    uint16_t* h = static_cast<uint16_t*>(a.h);
+    const uint16_t* w2 = static_cast<const uint16_t*>(a.w2);
     constexpr int kParts = NT / 256;
     if (a.ffn_all_rows) {
-      gemm_fp8w_body<128, true, kParts>(xp, a.offsets, E_loc,
-                                        static_cast<const uint8_t*>(a.w13), a.w13s, h, a.f, a.d,
-                                        bid, G, lds, prefix, a.sorted_pair, k);
+      gemm_fp8w_body<128, true, kParts>(static_cast<const uint16_t*>(a.x), a.offsets, E_loc,
+                                        static_cast<const uint8_t*>(a.w13), a.w13s,
+                                        static_cast<uint16_t*>(a.h), a.f, a.d, bid, G, lds, prefix,
+                                        a.sorted_pair, k);
     } else if (a.rows_up == kFusedWide) {
-      gemm_pipe_body<true, 128, 256, 4, ROWS_ALL, 8, false, true, 64>(
-          xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G, lds, prefix, segs, a.sorted_pair, k,
-          nullptr, nullptr, a.w13s);
+      pipe_up(TileCfg<128, 256, 4, ROWS_ALL>{}, w13, a.w13s);
     } else if (a.rows_up == kFusedBigTail) {
-      gemm_pipe_body<true, 256, 256, 3, ROWS_BIG, 8, false, true, 64>(
-          xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G, lds, prefix, segs, a.sorted_pair, k,
-          nullptr, nullptr, a.w13s);
-      gemm_pipe_body<true, 128, 256, 4, ROWS_TAIL, 8, false, true, 64>(
-          xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G, lds, prefix, segs, a.sorted_pair, k,
-          nullptr, nullptr, a.w13s);
+      pipe_up(TileCfg<256, 256, 3, ROWS_BIG>{}, w13, a.w13s);
+      pipe_up(TileCfg<128, 256, 4, ROWS_TAIL>{}, w13, a.w13s);
     } else if (a.rows_up == kFusedRide) {
-      gemm_pipe_body<true, 256, 256, 3, ROWS_BIGR, 8, false, true, 64>(
-          xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G, lds, prefix, segs, a.sorted_pair, k,
-          nullptr, nullptr, a.w13s);
-      gemm_pipe_body<true, 128, 256, 4, ROWS_TAILR, 8, false, true, 64>(
-          xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G, lds, prefix, segs, a.sorted_pair, k,
-          nullptr, nullptr, a.w13s);
+      pipe_up(TileCfg<256, 256, 3, ROWS_BIGR>{}, w13, a.w13s);
+      pipe_up(TileCfg<128, 256, 4, ROWS_TAILR>{}, w13, a.w13s);
     } else {
-      gemm_pipe_body<true, 256, 256, 3, ROWS_ALL, 8, false, true, 64>(
-          xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G, lds, prefix, segs, a.sorted_pair, k,
-          nullptr, nullptr, a.w13s);
+      pipe_up(TileCfg<256, 256, 3, ROWS_ALL>{}, w13, a.w13s);
     }
-    grid_barrier(a, G);
-    const uint16_t* w2 = static_cast<const uint16_t*>(a.w2);
-    uint16_t* yp = static_cast<uint16_t*>(a.y_perm);
+    // (the code-streaming bodies do not count their tiles: always a barrier)
+    if (!OVERLAP || a.ffn_all_rows) grid_barrier(a, G);
     if (a.ffn_all_rows) {
-      gemm_fp8w_body<128, false, kParts>(h, a.offsets, E_loc, static_cast<const uint8_t*>(a.w2),
-                                         a.w2s, yp, a.d, a.f, bid, G, lds, prefix);
+      gemm_fp8w_body<128, false, kParts>(static_cast<const uint16_t*>(a.h), a.offsets, E_loc,
+                                         static_cast<const uint8_t*>(a.w2), a.w2s,
+                                         static_cast<uint16_t*>(a.y_perm), a.d, a.f, bid, G, lds,
+                                         prefix);
     } else if (a.rows_down == kFusedBigTail) {
-      gemm_pipe_body<false, 256, 256, 3, ROWS_BIG, 8, false, true, 64>(
-          h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G, lds, prefix, segs, nullptr, 1, nullptr,
-          nullptr, a.w2s);
-      gemm_pipe_body<false, 128, 256, 4, ROWS_TAIL, 8, false, true, 64>(
-          h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G, lds, prefix, segs, nullptr, 1, nullptr,
-          nullptr, a.w2s);
+      pipe_down(TileCfg<256, 256, 3, ROWS_BIG>{}, w2, a.w2s);
+      pipe_down(TileCfg<128, 256, 4, ROWS_TAIL>{}, w2, a.w2s);
     } else if (a.rows_down == kFusedRide) {
-      gemm_pipe_body<false, 256, 256, 3, ROWS_BIGR, 8, false, true, 64>(
-          h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G, lds, prefix, segs, nullptr, 1, nullptr,
-          nullptr, a.w2s);
-      gemm_pipe_body<false, 128, 256, 4, ROWS_TAILR, 8, false, true, 64>(
-          h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G, lds, prefix, segs, nullptr, 1, nullptr,
-          nullptr, a.w2s);
+      pipe_down(TileCfg<256, 256, 3, ROWS_BIGR>{}, w2, a.w2s);
+      pipe_down(TileCfg<128, 256, 4, ROWS_TAILR>{}, w2, a.w2s);
     } else {
-      gemm_pipe_body<false, 256, 256, 3, ROWS_ALL, 8, false, true, 64>(
-          h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G, lds, prefix, segs, nullptr, 1, nullptr,
-          nullptr, a.w2s);
+      pipe_down(TileCfg<256, 256, 3, ROWS_ALL>{}, w2, a.w2s);
     }
   } else if constexpr (BF16) {
-    const uint16_t* xp = static_cast<const uint16_t*>(a.x);
     const uint16_t* w13 = static_cast<const uint16_t*>(a.w13);
-    uint16_t* h = static_cast<uint16_t*>(a.h);
-    if (a.ffn_all_rows) {
-      gemm_pipe_body<true, 128, 256, 3, ROWS_ALL, 8, false, false, 64>(xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G, lds,
-                                             prefix, segs, a.sorted_pair, k);
-    } else if (a.rows_up == kFusedWide) {
-      gemm_pipe_body<true, 128, 256, 3, ROWS_ALL, 8, false, false, 64>(xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G, lds,
-                                             prefix, segs, a.sorted_pair, k);
-    } else if (a.rows_up == kFusedAllBig) {
-      gemm_pipe_body<true, 256, 256, 2, ROWS_ALL, 8, false, false, 64>(xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G, lds,
-                                             prefix, segs, a.sorted_pair, k);
-    } else if (a.rows_up == kFusedRide) {
-      gemm_pipe_body<true, 256, 256, 2, ROWS_BIGR, 8, false, false, 64>(xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G,
-                                              lds, prefix, segs, a.sorted_pair, k);
-      gemm_pipe_body<true, 128, 256, 3, ROWS_TAILR, 8, false, false, 64>(xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G,
-                                               lds, prefix, segs, a.sorted_pair, k);
-    } else {
-      gemm_pipe_body<true, 256, 256, 2, ROWS_BIG, 8, false, false, 64>(xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G, lds,
-                                             prefix, segs, a.sorted_pair, k);
-      gemm_pipe_body<true, 128, 256, 3, ROWS_TAIL, 8, false, false, 64>(xp, a.offsets, E_loc, w13, h, a.f, a.d, bid, G,
-                                              lds, prefix, segs, a.sorted_pair, k);
-    }
-    grid_barrier(a, G);
     const uint16_t* w2 = static_cast<const uint16_t*>(a.w2);
-    uint16_t* yp = static_cast<uint16_t*>(a.y_perm);
+    if (a.ffn_all_rows || a.rows_up == kFusedWide) {
+      pipe_up(TileCfg<128, 256, 3, ROWS_ALL>{}, w13, nullptr);
+    } else if (a.rows_up == kFusedAllBig) {
+      pipe_up(TileCfg<256, 256, 2, ROWS_ALL>{}, w13, nullptr);
+    } else if (a.rows_up == kFusedRide) {
+      pipe_up(TileCfg<256, 256, 2, ROWS_BIGR>{}, w13, nullptr);
+      pipe_up(TileCfg<128, 256, 3, ROWS_TAILR>{}, w13, nullptr);
+    } else {
+      pipe_up(TileCfg<256, 256, 2, ROWS_BIG>{}, w13, nullptr);
+      pipe_up(TileCfg<128, 256, 3, ROWS_TAIL>{}, w13, nullptr);
+    }
+    if (!OVERLAP) grid_barrier(a, G);
     if (a.ffn_all_rows) {
-      gemm_pipe_body<false, 128, 256, 3, ROWS_ALL, 8, false, false, 64>(h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G, lds,
-                                              prefix, segs);
+      pipe_down(TileCfg<128, 256, 3, ROWS_ALL>{}, w2, nullptr);
     } else if (a.rows_down == kFusedAllBig) {
-      gemm_pipe_body<false, 256, 256, 2, ROWS_ALL, 8, false, false, 64>(h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G, lds,
-                                              prefix, segs);
+      pipe_down(TileCfg<256, 256, 2, ROWS_ALL>{}, w2, nullptr);
     } else if (a.rows_down == kFusedRide) {
-      gemm_pipe_body<false, 256, 256, 2, ROWS_BIGR, 8, false, false, 64>(h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G,
-                                               lds, prefix, segs);
-      gemm_pipe_body<false, 128, 256, 3, ROWS_TAILR, 8, false, false, 64>(h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G,
-                                                lds, prefix, segs);
+      pipe_down(TileCfg<256, 256, 2, ROWS_BIGR>{}, w2, nullptr);
+      pipe_down(TileCfg<128, 256, 3, ROWS_TAILR>{}, w2, nullptr);
     } else {
       // few tiles (the split's condition): the remainders in 128 x 128 tiles,
       // twice as many as with 256 weight rows, as the separate call runs them
-      gemm_pipe_body<false, 256, 256, 2, ROWS_BIG, 8, false, false, 64>(h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G, lds,
-                                              prefix, segs);
-      gemm_pipe_body<false, 128, 128, 4, ROWS_TAIL, 8, false, false, 64>(h, a.offsets, E_loc, w2, yp, a.d, a.f, bid, G,
-                                               lds, prefix, segs);
+      pipe_down(TileCfg<256, 256, 2, ROWS_BIG>{}, w2, nullptr);
+      pipe_down(TileCfg<128, 128, 4, ROWS_TAIL>{}, w2, nullptr);
     }
   } else {
     float* smem = reinterpret_cast<float*>(lds);
@@ -432,13 +436,17 @@ int launch_fused(const FusedArgs& a, bool bf16, int64_t max_rows, void* stream, 
   hipStream_t s = static_cast<hipStream_t>(stream);
   fp8 = fp8 && bf16;
   const size_t lds = fused_lds_bytes(a.E, bf16, fp8);
-  const void* kern = fp8    ? reinterpret_cast<const void*>(moe_fused_kernel<true, true>)
-                     : bf16 ? reinterpret_cast<const void*>(moe_fused_kernel<true>)
-                            : reinterpret_cast<const void*>(moe_fused_kernel<false>);
+  const bool ov = bf16 && a.overlap != 0;
+  const void* kern =
+      fp8    ? (ov ? reinterpret_cast<const void*>(moe_fused_kernel<true, true, true>)
+                   : reinterpret_cast<const void*>(moe_fused_kernel<true, true>))
+      : bf16 ? (ov ? reinterpret_cast<const void*>(moe_fused_kernel<true, false, true>)
+                   : reinterpret_cast<const void*>(moe_fused_kernel<true>))
+             : reinterpret_cast<const void*>(moe_fused_kernel<false>);
   // the largest dynamic LDS any E can ask for
-  static LdsAttr attr[3];
+  static LdsAttr attr[5];
   if (int rc = set_dynamic_lds_once(kern, fused_lds_bytes(MOE_MAX_E, bf16, fp8),
-                                    attr[fp8 ? 2 : bf16 ? 1 : 0]))
+                                    attr[(fp8 ? 2 : bf16 ? 1 : 0) + (ov ? 2 : 0)]))
     return rc;
   int occ = 0;
   const int threads = bf16 ? fused_threads<true>() : fused_threads<false>();

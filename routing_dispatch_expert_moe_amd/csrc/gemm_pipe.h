@@ -162,6 +162,16 @@ constexpr size_t pipe_lds_bytes(int BM, int BNW, int STAGES, bool fp8w = false, 
 // (r >> 3) & 1; BK = 64: (r >> 2) & 3), so the 16 rows one 16-lane phase of a
 // fragment read touches cover every bank once.
 // BK: K depth of a pipeline step, 32 or 64 (64 needs K a multiple of 64).
+// ready_out (producer): once all its tiles are stored, the workgroup releases
+// them at agent scope (one release: a release per tile writes the L2 back
+// every time and measured far slower) and adds each tile's rows x (output
+// columns / 32) to ready_out[e], so expert e's counter reaches n_e * N / 32
+// once every workgroup holding a tile of e, of any row class, is done.  ready_in (consumer, the next GEMM
+// whose A is that output): before a wave issues the loads of a tile of
+// expert e it waits until ready_in[e] reaches n_e * K / 32 and then
+// acquires at agent scope (once per run of tiles of one expert); a wait that
+// does not end within the spin limit sets MOE_ERR_HIP in err and goes on.
+// Both need N and K multiples of 32.
 template <bool SWIGLU, int BM, int BNW, int STAGES, int CLASS, int NW = 4, bool SAVE = false,
           bool FP8W = false, int BK = kBK>
 __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
@@ -173,7 +183,10 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
                                                int gk = 1,
                                                const uint16_t* const* __restrict__ wlist = nullptr,
                                                uint16_t* __restrict__ AB = nullptr,
-                                               const float* __restrict__ Ws = nullptr) {
+                                               const float* __restrict__ Ws = nullptr,
+                                               uint32_t* ready_out = nullptr,
+                                               const uint32_t* ready_in = nullptr,
+                                               int* err = nullptr) {
   static_assert(SWIGLU || !SAVE, "pre-activations exist only with SwiGLU");
   static_assert(!FP8W || !SAVE, "FP8 weights have no training forward");
   static_assert(BK == 32 || BK == 64, "step depth");
@@ -234,8 +247,32 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
   int it_tile = -1;
   const char* iWb = nullptr;
   uint32_t aoff[LA], boff[LB];
+  // ready_in: the expert whose rows were last seen complete and acquired; a
+  // wave whose wait timed out waits no more (the error is already raised)
+  int acq_e = -1;
+  bool timed_out = false;
   auto set_issue_tile = [&](int j) {
     const Tile t = decode_tile<BM, BN, CLASS>(vb + j * G, NT, prefix, segs, E_loc);
+    if (ready_in != nullptr && t.e != acq_e && !timed_out) {
+      const uint32_t need =
+          static_cast<uint32_t>(segs[t.e + 1] - segs[t.e]) * static_cast<uint32_t>(K / 32);
+      int late = 0;
+      if (lane == 0) {
+        uint32_t spins = 0;
+        while (__hip_atomic_load(ready_in + t.e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+               need) {
+          __builtin_amdgcn_s_sleep(2);
+          if (++spins == (1u << 21)) {
+            raise_error(err, MOE_ERR_HIP);
+            late = 1;
+            break;
+          }
+        }
+      }
+      timed_out = __builtin_amdgcn_readfirstlane(late) != 0;
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      acq_e = t.e;
+    }
     if constexpr (FP8W)
       iWb = reinterpret_cast<const char*>(W) + t.e * wstride;  // one byte per code
     else
@@ -675,6 +712,21 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
   }
   wait_vmcnt<0>();  // redundant tail loads must land before the LDS is released
   __syncthreads();
+  // ready_out: every tile of this workgroup is stored (the barrier above);
+  // one release at agent scope publishes them all, then each tile's rows x
+  // columns / 32 are counted for its expert
+  if (ready_out != nullptr) {
+    if (threadIdx.x == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      for (int j = 0; j < ntiles; ++j) {
+        const Tile t = decode_tile<BM, BN, CLASS>(vb + j * G, NT, prefix, segs, E_loc);
+        const int rows = min(BM, t.seg1 - t.m0), cols = min(BN, N - t.n0);
+        __hip_atomic_fetch_add(ready_out + t.e, static_cast<uint32_t>(rows * (cols / 32)),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    __syncthreads();  // prefix / segs may be rewritten by the caller's next phase
+  }
 }
 
 }  // namespace moe

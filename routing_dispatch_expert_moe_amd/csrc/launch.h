@@ -177,7 +177,12 @@ struct FusedArgs {
   uint32_t* bar_gen;    // workspace barrier words: generation,
   uint32_t* bar_count;  // top-level arrivals,
   uint32_t* bar_group;  // 8 group arrival counters, kWsBarStride words apart
+  int overlap;          // 1: GEMM2 tiles wait per expert on up_ready instead of a barrier
+  uint32_t* up_ready;   // workspace: [E_loc] GEMM1 stored rows x (columns / 32) per expert
 };
+// bytes of the per-expert readiness counters that follow the dispatch and
+// rerouting scratch in a moe_workspace_bytes workspace
+size_t ready_ws_bytes(int E_loc);
 // byte offsets of the barrier words inside the workspace header (each on its
 // own 128-byte line)
 constexpr size_t kWsBarGen = 128;

@@ -339,6 +339,17 @@ def moe_check_error(ws, stream=None) -> int:
     return int(lib().moe_check_error(_ptr(ws), _stream(stream)))
 
 
+OVERLAP_MODES = {"never": L.MOE_OVERLAP_NEVER, "auto": L.MOE_OVERLAP_AUTO,
+                 "always": L.MOE_OVERLAP_ALWAYS}
+
+
+def moe_set_fused_overlap(mode: str = "auto"):
+    """How the fused launch orders its two GEMM phases from now on in this
+    process: "never" (a device-wide barrier), "auto" (per-expert waits where
+    they measured faster) or "always" (per-expert waits wherever possible)."""
+    check(lib().moe_set_fused_overlap(OVERLAP_MODES[mode]), "moe_set_fused_overlap")
+
+
 def moe_forward_fused(logits, x, k, gate, capacity, e_begin, e_end, w13_packed, w2_packed, ws,
                       plan: DispatchPlan, topk_idx, topk_w, h, y_perm, y, stream=None,
                       reroute: bool = False):

@@ -103,4 +103,28 @@ def fused_matches_unfused(wl, w13, w2p, layer, x, logits, capacity=None):
     fl.forward_fused(x, logits)
     assert M.moe_check_error(fl.ws) == 0
     assert np.array_equal(t_out(fl.y), y1)
+    barrier_order_matches(fl, x, logits, y1)
     return fl
+
+
+def barrier_order_matches(fl, x, logits, y_ref):
+    """The fused call with its GEMM phases separated by a device-wide barrier
+    and with per-expert waits (both forced, whatever the automatic choice)
+    gives the same bits, and so does a call whose workspace is one byte short
+    of the readiness counters (always the barrier)."""
+    try:
+        for mode in ("never", "always"):
+            M.moe_set_fused_overlap(mode)
+            fl.forward_fused(x, logits)
+            assert M.moe_check_error(fl.ws) == 0
+            assert np.array_equal(t_out(fl.y), y_ref), mode
+        full = fl.ws
+        fl.ws = full[:full.numel() - 1]
+        try:
+            fl.forward_fused(x, logits)
+            assert M.moe_check_error(full) == 0
+            assert np.array_equal(t_out(fl.y), y_ref), "short workspace"
+        finally:
+            fl.ws = full
+    finally:
+        M.moe_set_fused_overlap("auto")

@@ -34,7 +34,8 @@ def test_header_declares_the_path():
               "moe_pack_weights", "moe_check_error", "moe_ffn_up", "moe_ffn_down",
               "moe_forward_fused", "moe_quantize_fp8", "moe_expert_ffn_fp8", "moe_ffn_up_fp8",
               "moe_ffn_down_fp8", "moe_expert_ffn_list", "moe_ffn_up_list", "moe_ffn_down_list",
-              "moe_route_reroute", "moe_forward_fused_reroute", "moe_forward_fused_fp8"):
+              "moe_route_reroute", "moe_forward_fused_reroute", "moe_forward_fused_fp8",
+              "moe_set_fused_overlap"):
         assert n in names
 
 
@@ -135,7 +136,9 @@ def test_reroute_validation(lib):
     assert r(*bad) == L.MOE_ERR_INVALID_ARG
     bad = list(ok); bad[5] = -2            # capacity
     assert r(*bad) == L.MOE_ERR_INVALID_ARG
-    bad = list(ok); bad[9] = need - 1
+    # the fused launch's readiness counters (E_loc words, one 256-byte block
+    # here) follow the rerouting scratch: one byte short of that scratch fails
+    bad = list(ok); bad[9] = need - 256 - 1
     assert r(*bad) == L.MOE_ERR_WORKSPACE
     bad = list(ok); bad[8] = None
     assert r(*bad) == L.MOE_ERR_INVALID_ARG
@@ -144,6 +147,17 @@ def test_reroute_validation(lib):
     assert r(None, 0, 8, 2, 0, 30, None, None, None, 0, None) == L.MOE_OK   # empty batch
     # the workspace holds the k + 1 candidates per token beyond the dispatch scratch
     assert lib.moe_workspace_bytes(1000, 8, 8, 8) - lib.moe_workspace_bytes(1000, 8, 1, 8) >= 1000 * 7 * 8 - 512
+    # and one readiness word per local expert, in 256-byte blocks
+    assert lib.moe_workspace_bytes(1000, 256, 8, 256) - lib.moe_workspace_bytes(1000, 256, 8, 1) == 1024 - 256
+
+
+def test_fused_overlap_setting(lib):
+    # host-only: the setting is validated and stored, no GPU call
+    for mode in (L.MOE_OVERLAP_NEVER, L.MOE_OVERLAP_ALWAYS, L.MOE_OVERLAP_AUTO):
+        assert lib.moe_set_fused_overlap(mode) == L.MOE_OK
+    assert lib.moe_set_fused_overlap(3) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_set_fused_overlap(-1) == L.MOE_ERR_INVALID_ARG
+    M.moe_set_fused_overlap("auto")
 
 
 def test_list_validation(lib):

@@ -13,7 +13,7 @@ from oracle import fp8_oracle as F
 from oracle import moe_oracle as O
 from workloads import custom, make
 
-from gpu_util import DEV, as64, log, packed_weights, t_in, t_out
+from gpu_util import DEV, as64, barrier_order_matches, log, packed_weights, t_in, t_out
 
 pytestmark = pytest.mark.gpu
 
@@ -253,3 +253,5 @@ def test_fused_layer_fp8(kw):
     fl.forward_fused(x, lg)
     assert M.moe_check_error(fl.ws) == 0
     assert np.array_equal(t_out(fl.y), y1)
+    # the GEMM phases separated by a barrier instead of the per-expert waits
+    barrier_order_matches(fl, x, lg, y1)
