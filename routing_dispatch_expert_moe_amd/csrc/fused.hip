@@ -243,6 +243,7 @@ __global__ __launch_bounds__(fused_threads<BF16>(), 1) void moe_fused_kernel(Fus
       }
     };
     if (E <= 64) route_all(std::integral_constant<int, 1>{});
+    else if (E <= 128) route_all(std::integral_constant<int, 2>{});
     else if (E <= 256) route_all(std::integral_constant<int, 4>{});
     else route_all(std::integral_constant<int, 16>{});
   }
@@ -396,10 +397,24 @@ __global__ __launch_bounds__(fused_threads<BF16>(), 1) void moe_fused_kernel(Fus
   }
   grid_barrier(a, G);
 
-  // ---- 5: combine
-  for (int t = bid * NWV + wave; t < T; t += G * NWV)
-    combine_token<BF16>(static_cast<const uint4*>(a.y_perm), a.pair_pos, a.topk_w, t, k, chunks,
-                        static_cast<uint4*>(a.y));
+  // ---- 5: combine.  With one workgroup per CU a wave holds few rows in
+  // flight unless the token's row slots match k (for k <= 2, 8 chunks per
+  // lane: 16 row loads, in the registers that k = 8 needs for 2), and each
+  // token's row loads wait for its pair indices unless those are fetched a
+  // token ahead
+  const uint4* yp = static_cast<const uint4*>(a.y_perm);
+  uint4* yo = static_cast<uint4*>(a.y);
+  const int t0 = bid * NWV + wave, ts = G * NWV;
+  const int32_t* pp = a.pair_pos;
+  const float* tw = a.topk_w;
+  switch (k) {
+    case 1: combine_tokens<BF16, 1, 8>(yp, pp, tw, t0, ts, T, chunks, yo); break;
+    case 2: combine_tokens<BF16, 2, 8>(yp, pp, tw, t0, ts, T, chunks, yo); break;
+    case 4: combine_tokens<BF16, 4, 4>(yp, pp, tw, t0, ts, T, chunks, yo); break;
+    case 8: combine_tokens<BF16, 8, 2>(yp, pp, tw, t0, ts, T, chunks, yo); break;
+    default:
+      for (int t = t0; t < T; t += ts) combine_token<BF16>(yp, pp, tw, t, k, chunks, yo);
+  }
 }
 
 // the rerouting resolver's LDS for any k
