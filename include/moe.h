@@ -275,9 +275,11 @@ moe_status moe_ffn_down_list(const void* h, const int32_t* offsets, int E_loc, i
  * moe_quantize_fp8: packed bf16 weights w_packed [E_loc][rows][K] (the
  * moe_pack_weights layout: rows = 2f, K = d for w13; rows = d, K = f for w2)
  * -> codes q [E_loc][rows][K] (uint8) and scales [E_loc][rows/128][K/128]
- * (fp32).  Per block: amax = max |w|; scale = amax / 448 (fp32, correctly
- * rounded; 1 for an all-zero block); q = E4M3(w / scale) rounded to nearest
- * even, saturated at +-448.  rows and K must be multiples of 128
+ * (fp32).  Per block: amax = max |w|; scale = the smallest power of two 2^e
+ * with amax <= 448 * 2^e (1 for an all-zero block), so code * scale is
+ * exactly a bf16 value and the block's largest code lies in [224, 448];
+ * q = E4M3(w / scale) rounded to nearest even (saturating at +-448, which no
+ * weight reaches).  rows and K must be multiples of 128
  * (MOE_ERR_UNSUPPORTED); pointers 16-byte aligned; outputs must not alias the
  * input.  One-time, like moe_pack_weights. */
 moe_status moe_quantize_fp8(const void* w_packed, int E_loc, int rows, int K, uint8_t* q,
@@ -386,8 +388,8 @@ moe_status moe_forward_fused_reroute(const float* logits, const void* x, int T, 
  * the layer as one kernel): w13_q / w2_q are the E4M3-FN codes and w13_s /
  * w2_s the fp32 128 x 128 block scales that moe_quantize_fp8 makes from
  * w13_packed / w2_packed; x, h, y_perm and y are bf16.  The GEMM phases run
- * the FP8 pipelined body of moe_expert_ffn_fp8 (codes in LDS, converted to
- * bf16 per MFMA operand, the running sum rescaled at each 128-deep K block),
+ * the FP8 pipelined body of moe_expert_ffn_fp8 (codes in LDS, each MFMA
+ * operand converted to its dequantised bf16 weights with the block's scale),
  * so the result has the same bits as moe_route -> moe_dispatch ->
  * moe_expert_ffn_fp8 -> moe_combine wherever those calls run their
  * pipelined kernels (more than 48 rows per expert on average).  Requires d

@@ -16,11 +16,15 @@ the readings below fix them (each also listed in the design notes):
       subnormal 2^-9.
   R23 Scales: one fp32 scale per block of 128 rows x 128 K-columns of each
       expert's packed (K-contiguous) weight matrix: W1 || W3 rows for the
-      first GEMM, W2^T rows for the second.  scale = amax / 448 in fp32
-      (amax = the block's largest |w|); an all-zero block gets scale 1.
-  R24 Codes: q = E4M3(w / scale) with the division in fp32 and the rounding
-      to nearest, ties to the even code, saturating at +-448 (no NaN is ever
-      produced).  Weights are the exact bf16 inputs.
+      first GEMM, W2^T rows for the second.  scale = the smallest power of
+      two 2^e with amax <= 448 * 2^e (amax = the block's largest |w|), so the
+      block's largest code lies in (224, 448] and nothing saturates; an
+      all-zero block gets scale 1.  (A power of two, as the shared exponents
+      of the OCP microscaling formats are, makes code * scale exactly
+      representable in bf16.)
+  R24 Codes: q = E4M3(w / scale) with the division in fp32 (exact for a power
+      of two) and the rounding to nearest, ties to the even code, saturating
+      at +-448 (no NaN is ever produced).  Weights are the exact bf16 inputs.
   R25 The method computes with the dequantised weights decode(q) * scale;
       activations (x, h) stay bf16 and the GEMMs accumulate in fp32, so the
       oracle's FFN is moe_oracle's FFN applied to the dequantised weights.
@@ -72,6 +76,13 @@ def e4m3_encode(x: np.ndarray) -> np.ndarray:
     return (code | np.where(neg, 0x80, 0)).astype(np.uint8)
 
 
+def scale_exponent(amax: np.ndarray) -> np.ndarray:
+    """The smallest integer e with amax <= 448 * 2^e, for amax > 0 (exact:
+    amax = m * 2^ex with m in [0.5, 1) and 448 = 0.875 * 2^9)."""
+    m, ex = np.frexp(np.where(amax > 0, amax, 1.0))
+    return np.where(m <= 0.875, ex - 9, ex - 8)
+
+
 def quantize_blocks(w_bits: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
     """Quantise packed bf16 weights [E][R][K] (uint16 bit patterns; R, K
     multiples of 128) to (codes uint8 [E][R][K], scales float32
@@ -81,8 +92,8 @@ def quantize_blocks(w_bits: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
     assert R % BLOCK == 0 and K % BLOCK == 0
     w = (w_bits.astype(np.uint32) << 16).view(np.float32)
     blocks = w.reshape(E, R // BLOCK, BLOCK, K // BLOCK, BLOCK)
-    amax = np.abs(blocks).max(axis=(2, 4)).astype(np.float32)       # [E][R/128][K/128]
-    scale = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    amax = np.abs(blocks).max(axis=(2, 4)).astype(np.float64)       # [E][R/128][K/128]
+    scale = np.where(amax > 0, np.ldexp(1.0, scale_exponent(amax)), 1.0).astype(np.float32)
     ratio = (blocks / scale[:, :, None, :, None]).astype(np.float32)  # fp32 division
     codes = e4m3_encode(ratio).reshape(E, R, K)
     return codes, scale

@@ -1,8 +1,12 @@
 // Block quantisation of packed bf16 expert weights to E4M3-FN codes with one
 // fp32 scale per 128 x 128 block (NCCL EP page §2.1: FP8 expert compute with
-// a scale tensor).  For each block: amax = max |w|, scale = amax / 448
-// (correctly rounded fp32 division; an all-zero block gets scale 1), and
-// code = E4M3(w / scale), rounded to nearest even and saturated at 448.
+// a scale tensor).  For each block: amax = max |w|, scale = the smallest
+// power of two 2^e with amax <= 448 * 2^e (an all-zero block gets scale 1),
+// and code = E4M3(w / scale), rounded to nearest even (the division by a
+// power of two is exact, and no weight reaches the saturation at 448).  A
+// power-of-two scale lets the GEMMs dequantise each operand exactly in the
+// hardware's scaled conversion (code * 2^e is a bf16 value), so their K loops
+// carry no per-block rescaling of the accumulators.
 //
 // One 256-thread workgroup per block: thread t owns row t / 2 of the block
 // and 64 consecutive K-columns (128 bytes of bf16 in, 64 bytes of codes out).
@@ -38,7 +42,12 @@ __global__ __launch_bounds__(256) void quantize_fp8_kernel(const uint16_t* __res
   if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = amax;
   __syncthreads();
   amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-  const float scale = amax > 0.f ? __fdiv_rn(amax, kE4M3Max) : 1.f;
+  // amax = m * 2^ex with m in [0.5, 1), and 448 = 0.875 * 2^9: the smallest e
+  // with amax <= 448 * 2^e is ex - 9 when m <= 0.875, else ex - 8 (bf16
+  // weights keep e >= -141, a normal or subnormal fp32 power of two)
+  int ex = 0;
+  const float m = frexpf(amax, &ex);
+  const float scale = amax > 0.f ? ldexpf(1.f, m <= 0.875f ? ex - 9 : ex - 8) : 1.f;
   if (threadIdx.x == 0) scales[(static_cast<size_t>(e) * RB + rb) * KB + kb] = scale;
   uint4* dst = reinterpret_cast<uint4*>(q + base);
 #pragma unroll

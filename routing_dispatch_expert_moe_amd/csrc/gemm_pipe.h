@@ -144,18 +144,16 @@ constexpr size_t pipe_lds_bytes(int BM, int BNW, int STAGES, bool fp8w = false, 
 // AB[row][col] and g = A W3 at AB[row][N + col] (row pitch 2N), rounded to
 // bf16, for the backward pass.
 // FP8W: W holds E4M3 codes (one byte per weight, same packed layout) and Ws
-// one fp32 scale per 128 x 128 block ([E][rows / 128][K / 128]) (NCCL EP page
-// §2.1: FP8 expert compute with a scale tensor).  The codes go to LDS as they
-// are (half the bytes of bf16 weights); each MFMA operand is converted from 8
-// codes to 8 bf16 values (exact: every E4M3 value is a bf16 value) just
-// before the MFMAs that use it, so the MFMAs accumulate code x activation
-// products.  The running sum is kept in units of the current
-// 128-deep K block's scale: after block kb, acc *= s_kb / s_(kb+1) for each
-// MFMA tile (s_KB = 1; a 32 x 32 tile's weight rows lie in one 128-row
-// block, so its scale is one number).  The result is sum_kb s_kb x (block
-// kb's partial sum), the dequantised weights' product re-associated, with one
-// fp32 rounding per block and no second set of accumulators.  K must be at
-// least STAGES steps deep and a multiple of 128.  A weight row of a step is BK
+// one fp32 power-of-two scale per 128 x 128 block ([E][rows / 128][K / 128])
+// (NCCL EP page §2.1: FP8 expert compute with a scale tensor).  The codes go
+// to LDS as they are (half the bytes of bf16 weights); each MFMA operand is
+// converted from 8 codes to the 8 dequantised bf16 weights code x scale by
+// the hardware's scaled conversion just before the MFMAs that use it (exact:
+// an E4M3 value times a power of two is a bf16 value; a 32 x 32 tile's
+// weight rows lie in one 128-row block, so each operand has one scale per
+// 128-deep K block), so the MFMAs accumulate the dequantised weights'
+// products in fp32 as the bf16 path does, with no rescaling of the
+// accumulators.  K must be at least STAGES steps deep and a multiple of 128.  A weight row of a step is BK
 // bytes of codes in 16-byte pieces fetched by BK / 16 neighbouring lanes (a
 // 64-lane direct load covers 32 rows for BK = 32, 16 rows for BK = 64); in
 // LDS piece c of row r sits at position c ^ fswz(r) of the row (BK = 32:
@@ -377,21 +375,23 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
     if (!SWIGLU) wrow = min(wrow, N - 1);  // columns past N are computed and dropped
     return Ws[(static_cast<size_t>(ct.e) * RB + wrow / kScaleBlock) * KB + kb];
   };
-  // FP8W: codes of slot `slot` to bf16 operands; lanes 0..31 take codes 0..7
-  // of their 16, lanes 32..63 codes 8..15 (the K halves of the 32 x 32 x 16
-  // operand), two codes per conversion
-  auto cvt_frags = [&](int slot) {
+  // FP8W: codes of slot `slot` to dequantised bf16 operands, code x sq[q]
+  // (the power-of-two scale of tile q's current K block); lanes 0..31 take
+  // codes 0..7 of their 16, lanes 32..63 codes 8..15 (the K halves of the
+  // 32 x 32 x 16 operand), two codes per conversion
+  auto cvt_frags = [&](int slot, const float (&sq)[NQ]) {
     if constexpr (FP8W) {
       const bool hi = lane >= 32;
 #pragma unroll
       for (int q = 0; q < NQ; ++q) {
         const uint4 v = fbr[slot][q];
         const int w0 = static_cast<int>(hi ? v.z : v.x), w1 = static_cast<int>(hi ? v.w : v.y);
+        const float c = sq[q];
         fb[slot][q] = __builtin_bit_cast(bf16x8_t, make_uint4(
-            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.f, false)),
-            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.f, true)),
-            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.f, false)),
-            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.f, true))));
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, c, false)),
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, c, true)),
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, c, false)),
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, c, true))));
       }
     }
   };
@@ -430,15 +430,13 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
   auto mfma_substep = [&](f32x16_t (&acc)[FM][NQ], int slot) {
     mfma_substep_n(acc, slot, std::integral_constant<int, FM>{});
   };
-  // FP8W: after the last step of K block kb, acc *= s_kb / s_(kb+1) per MFMA
-  // tile (s_KB = 1).  sc holds s_kb and s_(kb+1) of each tile; the scales of
-  // block kb + 2 are loaded here, a whole block before they are used.
-  auto rescale = [&](const Tile& ct, int kb, f32x16_t (&acc)[FM][NQ], float (&sc)[2][NQ]) {
+  // FP8W: after the last step of K block kb the conversions move on to block
+  // kb + 1's scales.  sc holds the scales of blocks kb and kb + 1 of each
+  // tile; those of block kb + 2 are loaded here, a whole block before they
+  // are used.
+  auto next_block_scales = [&](const Tile& ct, int kb, float (&sc)[2][NQ]) {
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
-      const float r = kb + 1 < KB ? sc[0][q] / sc[1][q] : sc[0][q];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) acc[i][q] *= r;
       sc[0][q] = sc[1][q];
       sc[1][q] = kb + 2 < KB ? frag_scale(ct, q, kb + 2) : 1.f;
     }
@@ -597,7 +595,7 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
           if constexpr (ACT) load_frags_n(s % STAGES, 1, 1, na);
           issue_part(1, pb, pk);
           if constexpr (ACT) {
-            cvt_frags(0);
+            cvt_frags(0, sc[0]);
             mfma_substep_n(acc, 0, na);
             interleave<0, NMFA, NA + NQ, NVM>();
           }
@@ -605,14 +603,14 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
           if constexpr (SUB == 4) {
             if constexpr (ACT) {
               load_frags_n(s % STAGES, 2, 0, na);
-              cvt_frags(1);
+              cvt_frags(1, sc[0]);
               mfma_substep_n(acc, 1, na);
               interleave<0, NMFA, NA + NQ, 0>();
             }
             __builtin_amdgcn_sched_barrier(0);
             if constexpr (ACT) {
               load_frags_n(s % STAGES, 3, 1, na);
-              cvt_frags(0);
+              cvt_frags(0, sc[0]);
               mfma_substep_n(acc, 0, na);
               interleave<0, NMFA, NA + NQ, 0>();
             }
@@ -627,14 +625,15 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
           issue_part(0, pb, pk);
           load_frags((s + 1) % STAGES, 0, 0);
           if constexpr (ACT) {
-            cvt_frags(1);
+            cvt_frags(1, sc[0]);
             mfma_substep_n(acc, 1, na);
             interleave<0, NMFA, NDS, NVM>();
           }
           __builtin_amdgcn_sched_barrier(0);
           if constexpr (ACT && FP8W) {
             const int kt = s % KT;
-            if ((kt + 1) % (kScaleBlock / BK) == 0) rescale(ct, kt / (kScaleBlock / BK), acc, sc);
+            if ((kt + 1) % (kScaleBlock / BK) == 0)
+              next_block_scales(ct, kt / (kScaleBlock / BK), sc);
           }
         };
         const int s0 = j * KT;

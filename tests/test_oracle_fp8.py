@@ -75,6 +75,25 @@ def test_block_scale_hand_example():
     assert np.count_nonzero(q) == 5
 
 
+def test_power_of_two_scale_hand_example():
+    # block 0: amax 450 (a bf16 value): 450 > 448 * 1, 450 <= 448 * 2, so the
+    # scale is 2; 450 / 2 = 225 lies in the binade [128, 256) of quantum 16 and
+    # rounds to 224 = 1.75 * 2^7, code (7 + 7) << 3 | 6 = 0x76.
+    # block 1: amax 1.0: 1 <= 448 * 2^-8 = 1.75 but 1 > 448 * 2^-9 = 0.875, so
+    # the scale is 2^-8; 1.0 -> 256 = 2^8, code 15 << 3 = 0x78; bf16(0.3) =
+    # 0.30078125 -> 77, quantum 8 in [64, 128): 9.625 quanta -> 10 -> 80 =
+    # 1.25 * 2^6, code 13 << 3 | 2 = 0x6A, dequantised 80 / 256 = 0.3125.
+    w = np.zeros((1, 128, 256), np.float32)
+    w[0, 5, 7] = 450.0
+    w[0, 9, 130] = 1.0
+    w[0, 10, 140] = 0.3
+    q, s = F.quantize_blocks(_bf16(w))
+    assert s.shape == (1, 1, 2) and s[0, 0, 0] == 2.0 and s[0, 0, 1] == 2.0 ** -8
+    assert (q[0, 5, 7], q[0, 9, 130], q[0, 10, 140]) == (0x76, 0x78, 0x6A)
+    deq = F.dequantize_blocks(q, s)
+    assert (deq[0, 5, 7], deq[0, 9, 130], deq[0, 10, 140]) == (448.0, 1.0, 0.3125)
+
+
 def test_zero_block_and_block_independence():
     rng = np.random.default_rng(1)
     w = rng.standard_normal((2, 256, 384)).astype(np.float32) * 0.02
@@ -101,10 +120,14 @@ def test_block_scale_property_and_error_bound():
     deq = F.dequantize_blocks(q, s)
     blocks = wexact.reshape(3, 2, 128, 2, 128)
     amax = np.abs(blocks).max(axis=(2, 4))
-    # scale = amax / 448 in fp32; the largest element lands on +-448
-    assert np.array_equal(s, (amax.astype(np.float32) / np.float32(448.0)).astype(np.float32))
+    # the scale is a power of two, the smallest with amax / scale <= 448
+    s64 = s.astype(np.float64)
+    mant, _ = np.frexp(s64)
+    assert np.all(mant == 0.5)
+    assert np.all(amax / s64 <= 448.0) and np.all(amax / (s64 / 2) > 448.0)
+    # so the block's largest code lies in [224, 448] and none saturates
     qa = np.abs(F.e4m3_decode(q)).reshape(3, 2, 128, 2, 128).max(axis=(2, 4))
-    assert np.all(qa == 448.0)
+    assert np.all((qa >= 224.0) & (qa <= 448.0))
     # |dequant - w| <= half a quantum of |w / scale| (plus the fp32 division's rounding)
     r = np.abs(wexact) / np.repeat(np.repeat(s.astype(np.float64), 128, 1), 128, 2)
     _, ex = np.frexp(np.where(r > 0, r, 1.0))

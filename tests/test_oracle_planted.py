@@ -278,6 +278,7 @@ FP8_PINS = [
     ("brute-force nearest code", PF.test_encode_matches_brute_force_nearest),
     ("round trip", PF.test_round_trip_of_every_finite_code),
     ("hand block", PF.test_block_scale_hand_example),
+    ("power-of-two hand blocks", PF.test_power_of_two_scale_hand_example),
     ("zero block, independence", PF.test_zero_block_and_block_independence),
     ("scale property, error bound", PF.test_block_scale_property_and_error_bound),
     ("representable weights", PF.test_representable_weights_reduce_to_the_bf16_ffn),
@@ -318,15 +319,24 @@ def _decode_variant(bias=7, sub_exp=-9):
     return dec
 
 
-def _quantize_scale_240(w_bits):
-    w_bits = np.asarray(w_bits, dtype=np.uint16)
-    E, R, K = w_bits.shape
-    w = (w_bits.astype(np.uint32) << 16).view(np.float32)
-    blocks = w.reshape(E, R // 128, 128, K // 128, 128)
-    amax = np.abs(blocks).max(axis=(2, 4)).astype(np.float32)
-    scale = np.where(amax > 0, amax / np.float32(240.0), np.float32(1.0)).astype(np.float32)
-    ratio = (blocks / scale[:, :, None, :, None]).astype(np.float32)
-    return F.e4m3_encode(ratio).reshape(E, R, K), scale
+def _quantize_with_scale(scale_of):
+    """The oracle's quantiser with another block-scale rule (scale_of(amax))."""
+    def quant(w_bits):
+        w_bits = np.asarray(w_bits, dtype=np.uint16)
+        E, R, K = w_bits.shape
+        w = (w_bits.astype(np.uint32) << 16).view(np.float32)
+        blocks = w.reshape(E, R // 128, 128, K // 128, 128)
+        amax = np.abs(blocks).max(axis=(2, 4)).astype(np.float64)
+        scale = np.where(amax > 0, scale_of(np.where(amax > 0, amax, 1.0)), 1.0).astype(np.float32)
+        ratio = (blocks / scale[:, :, None, :, None]).astype(np.float32)
+        return F.e4m3_encode(ratio).reshape(E, R, K), scale
+    return quant
+
+
+def _mx_floor_scale(amax):
+    # the microscaling rule 2^(floor(log2 amax) - 8): its top binade saturates
+    _, ex = np.frexp(amax)
+    return np.ldexp(1.0, ex - 1 - 8)
 
 
 def _expert_weights_swapped(w13_codes, w13_scale, w2_codes, w2_scale, f):
@@ -348,7 +358,11 @@ def test_real_fp8_oracle_passes_every_pin():
     ("subnormal quantum 2^-10 in the encoder", dict(e4m3_encode=_encode_variant(min_exp=-7))),
     ("exponent bias 8", dict(e4m3_decode=_decode_variant(bias=8))),
     ("subnormal scale 2^-10 in the decoder", dict(e4m3_decode=_decode_variant(sub_exp=-10))),
-    ("scale = amax / 240", dict(quantize_blocks=_quantize_scale_240)),
+    ("scale = amax / 448 (not a power of two)",
+     dict(quantize_blocks=_quantize_with_scale(lambda a: (a.astype(np.float32) / np.float32(448.0))))),
+    ("scale = 2^(floor(log2 amax) - 8)", dict(quantize_blocks=_quantize_with_scale(_mx_floor_scale))),
+    ("scale one power of two too large",
+     dict(quantize_blocks=_quantize_with_scale(lambda a: np.ldexp(1.0, F.scale_exponent(a) + 1)))),
     ("W1 and W3 swapped", dict(expert_weights=_expert_weights_swapped)),
 ], ids=lambda m: m[0])
 def test_planted_fp8_mistake_fails_a_pin(mistake, monkeypatch):
