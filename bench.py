@@ -44,6 +44,8 @@ METRIC = "MoE-layer tokens/s + TFLOP/s (MFMA %) and HBM GB/s (% peak), 1×MI355X
 HEADLINE = "dsv3_prefill_zipf"
 # (the decode workload first: it shares the headline's expert weights)
 OTHERS = ("dsv3_decode", "mixtral_prefill", "ep_rank_share", "tiny_fp32")
+# workloads also timed with FP8 expert weights in the default run
+FP8_WORKLOADS = ("dsv3_prefill_zipf", "dsv3_decode")
 STEPS = ("router", "route", "dispatch", "ffn_up", "ffn_down", "combine")
 DOMINANT = "ffn_up"                 # one GEMM1 + SwiGLU pass over all local rows
 COPY_BYTES = 1 << 30
@@ -83,6 +85,8 @@ def parse(argv=None):
                    help="fp8: quantise the packed bf16 expert weights to E4M3 codes with "
                         "128 x 128 block scales (moe_quantize_fp8, untimed) and run the FFN "
                         "steps on them")
+    p.add_argument("--no-fp8", action="store_true",
+                   help="leave out the FP8-weight runs of the DeepSeek-shaped workloads")
     p.add_argument("--backward", action="store_true",
                    help="also time a training step: the forward with the SwiGLU pre-activations "
                         "kept, then the whole backward pass (gradients of x, the gate logits "
@@ -631,7 +635,7 @@ class Weights:
         return self.val
 
 
-def run_workload(args, wl, weights, dev, headline):
+def run_workload(args, wl, weights, dev, headline, fp8=None):
     """Time one workload's layer: K steps of the separate calls (HIP events
     around each call), the same steps with the Infinity Cache evicted, the
     dispatch plan alone, and the fused launch; returns the results dict."""
@@ -644,7 +648,8 @@ def run_workload(args, wl, weights, dev, headline):
     w13, w2p, host_w, w13_t, w2_t = weights.get(wl, keep_host=keep_host, train=train)
     log("weights packed")
     C = M.moe_capacity(wl.T, wl.k, wl.E, wl.capacity_factor)
-    fp8 = headline and args.weights == "fp8"
+    if fp8 is None:
+        fp8 = headline and args.weights == "fp8"
     reroute = headline and args.reroute
     s13 = s2 = None
     if fp8:
@@ -995,13 +1000,31 @@ def main(argv=None):
             **head_orders},
     }
     del r
+    # (the default set of workloads only) the DeepSeek-shaped workloads again
+    # with FP8 weights, each right after its bf16 run while the weights it
+    # quantises are still on the device
+    fp8_names = ([] if args.no_fp8 or args.others is not None or args.weights == "fp8"
+                 or args.backward or args.reroute
+                 else [n for n in FP8_WORKLOADS if n == args.workload or n in others])
+    fp8_out = {}
+
+    def run_fp8(name):
+        log(f"{name} with FP8 weights")
+        rf = run_workload(args, make(name), weights, dev, headline=False, fp8=True)
+        fp8_out[name] = {"weights": "e4m3 codes, power-of-two fp32 scale per 128 x 128 block",
+                         **summary_of(args, rf)}
+    if args.workload in fp8_names:
+        run_fp8(args.workload)
     others_out = {}
     for name in others:
         wo = make(name)
         ro = run_workload(args, wo, weights, dev, headline=False)
         others_out[name] = summary_of(args, ro)
         del ro
+        if name in fp8_names:
+            run_fp8(name)
     line["others"] = others_out or None
+    line["fp8_weights"] = fp8_out or None
     print(json.dumps(line), flush=True)
 
 
