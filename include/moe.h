@@ -348,7 +348,25 @@ moe_status moe_forward_fused(const float* logits, const void* x, int T, int E, i
                              void* h, void* y_perm, void* y, void* ws, size_t ws_bytes,
                              void* stream);
 
-/* How moe_forward_fused (and its rerouting and FP8 forms) orders its two GEMM
+/* moe_forward_fused with the expert weights as per-expert buffers (DWDP page,
+ * key optimisations: the grouped GEMM reads each expert's weights through a
+ * TensorList, so experts need not be one packed tensor; MegaMoE comparison
+ * page, core differences §1: the layer as one kernel).  w13_list and w2_list
+ * are device tables of E_loc device pointers (the moe_expert_ffn_list
+ * tables): expert i's buffers hold expert i of moe_pack_weights' outputs,
+ * w13 [2f][d] and w2 [d][f], each 16-byte aligned.  Every output has the same
+ * bits as moe_forward_fused on the same weights packed.  Other arguments,
+ * rules and errors as moe_forward_fused; a NULL table is
+ * MOE_ERR_INVALID_ARG. */
+moe_status moe_forward_fused_list(const float* logits, const void* x, int T, int E, int k,
+                                  int gate, int capacity, int e_begin, int e_end, int d, int f,
+                                  moe_dtype dtype, const void* const* w13_list,
+                                  const void* const* w2_list, int32_t* topk_idx, float* topk_w,
+                                  int32_t* counts, int32_t* offsets, int32_t* sorted_pair,
+                                  int32_t* pair_pos, int32_t* n_kept, void* h, void* y_perm,
+                                  void* y, void* ws, size_t ws_bytes, void* stream);
+
+/* How moe_forward_fused (and its rerouting, FP8 and TensorList forms) orders its two GEMM
  * phases, for every later call in the process (default MOE_OVERLAP_AUTO):
  *   MOE_OVERLAP_NEVER   a device-wide barrier between them;
  *   MOE_OVERLAP_AUTO    per-expert waits where they measured faster: when

@@ -13,4 +13,5 @@ from .ops import (alloc_plan, alloc_workspace, moe_check_error, moe_combine, moe
                   weight_table, moe_route_reroute, moe_route_reroute_noalloc, moe_ffn_up_train, moe_pack_weights_backward,
                   moe_combine_backward, moe_gate_backward, moe_ffn_down_backward,
                   moe_ffn_up_backward, moe_ffn_wgrad, moe_wgrad_workspace_bytes,
-                  moe_router_backward, moe_router_backward_workspace_bytes, moe_set_fused_overlap)
+                  moe_router_backward, moe_router_backward_workspace_bytes, moe_set_fused_overlap,
+                  moe_forward_fused_list)

@@ -560,7 +560,9 @@ static moe_status forward_fused_impl(const float* logits, const void* x, int T, 
                                      int32_t* pair_pos, int32_t* n_kept, void* h, void* y_perm,
                                      void* y, void* ws, size_t ws_bytes, void* stream,
                                      bool reroute, const float* w13s = nullptr,
-                                     const float* w2s = nullptr) {
+                                     const float* w2s = nullptr,
+                                     const void* const* w13_list = nullptr,
+                                     const void* const* w2_list = nullptr) {
   // w13s / w2s set: FP8 weights (codes in w13_packed / w2_packed, bf16 activations)
   const bool fp8 = w13s != nullptr || w2s != nullptr;
   if (T < 0) return MOE_ERR_INVALID_ARG;
@@ -583,6 +585,9 @@ static moe_status forward_fused_impl(const float* logits, const void* x, int T, 
     // the pipelined FP8 body's depth
     if (d < moe::fp8_pipe_min_k() || f < moe::fp8_pipe_min_k()) return MOE_ERR_UNSUPPORTED;
   } else {
+    // (TensorList form: the tables stand where the packed weights do)
+    if (w13_list != nullptr) w13_packed = w13_list;
+    if (w2_list != nullptr) w2_packed = w2_list;
     st = check_ffn(x, offsets, E_loc, max_rows, d, f, dtype, w13_packed, h);
     if (st != MOE_OK) return st;
     st = check_ffn(h, offsets, E_loc, max_rows, d, f, dtype, w2_packed, y_perm);
@@ -617,8 +622,10 @@ static moe_status forward_fused_impl(const float* logits, const void* x, int T, 
   }
   a.logits = logits;
   a.x = x;
-  a.w13 = w13_packed;
-  a.w2 = w2_packed;
+  a.w13 = w13_list != nullptr ? nullptr : w13_packed;
+  a.w2 = w2_list != nullptr ? nullptr : w2_packed;
+  a.w13_list = w13_list;
+  a.w2_list = w2_list;
   a.w13s = w13s;
   a.w2s = w2s;
   a.T = T;
@@ -709,6 +716,20 @@ moe_status moe_forward_fused_reroute(const float* logits, const void* x, int T, 
   return forward_fused_impl(logits, x, T, E, k, gate, capacity, e_begin, e_end, d, f, dtype,
                             w13_packed, w2_packed, topk_idx, topk_w, counts, offsets, sorted_pair,
                             pair_pos, n_kept, h, y_perm, y, ws, ws_bytes, stream, true);
+}
+
+moe_status moe_forward_fused_list(const float* logits, const void* x, int T, int E, int k,
+                                  int gate, int capacity, int e_begin, int e_end, int d, int f,
+                                  moe_dtype dtype, const void* const* w13_list,
+                                  const void* const* w2_list, int32_t* topk_idx, float* topk_w,
+                                  int32_t* counts, int32_t* offsets, int32_t* sorted_pair,
+                                  int32_t* pair_pos, int32_t* n_kept, void* h, void* y_perm,
+                                  void* y, void* ws, size_t ws_bytes, void* stream) {
+  if (!w13_list || !w2_list) return MOE_ERR_INVALID_ARG;
+  return forward_fused_impl(logits, x, T, E, k, gate, capacity, e_begin, e_end, d, f, dtype,
+                            nullptr, nullptr, topk_idx, topk_w, counts, offsets, sorted_pair,
+                            pair_pos, n_kept, h, y_perm, y, ws, ws_bytes, stream, false, nullptr,
+                            nullptr, w13_list, w2_list);
 }
 
 moe_status moe_forward_fused_fp8(const float* logits, const void* x, int T, int E, int k,

@@ -301,19 +301,21 @@ __global__ __launch_bounds__(fused_threads<BF16>(), 1) void moe_fused_kernel(Fus
   // (the launcher never picks OVERLAP with the FP8 code-streaming body,
   // which does not count its tiles)
   uint32_t* up = OVERLAP ? a.up_ready : nullptr;
+  // (a.w13_list / a.w2_list: the bf16 and fp32 weights as per-expert tables;
+  // never with FP8 codes)
   auto pipe_up = [&](auto cfg, const uint16_t* w, const float* ws) {
     using C = decltype(cfg);
     gemm_pipe_body<true, C::BM, C::BNW, C::STAGES, C::CLASS, 8, false, FP8, 64>(
         static_cast<const uint16_t*>(a.x), a.offsets, E_loc, w, static_cast<uint16_t*>(a.h), a.f,
-        a.d, bid, G, lds, prefix, segs, a.sorted_pair, k, nullptr, nullptr, ws, up, nullptr,
-        a.err);
+        a.d, bid, G, lds, prefix, segs, a.sorted_pair, k,
+        reinterpret_cast<const uint16_t* const*>(a.w13_list), nullptr, ws, up, nullptr, a.err);
   };
   auto pipe_down = [&](auto cfg, const uint16_t* w, const float* ws) {
     using C = decltype(cfg);
     gemm_pipe_body<false, C::BM, C::BNW, C::STAGES, C::CLASS, 8, false, FP8, 64>(
         static_cast<const uint16_t*>(a.h), a.offsets, E_loc, w, static_cast<uint16_t*>(a.y_perm),
-        a.d, a.f, bid, G, lds, prefix, segs, nullptr, 1, nullptr, nullptr, ws, nullptr, up,
-        a.err);
+        a.d, a.f, bid, G, lds, prefix, segs, nullptr, 1,
+        reinterpret_cast<const uint16_t* const*>(a.w2_list), nullptr, ws, nullptr, up, a.err);
   };
   if constexpr (FP8) {
     // the FP8 weights' row splits, as in the separate FP8 calls: few rows per
@@ -389,11 +391,13 @@ __global__ __launch_bounds__(fused_threads<BF16>(), 1) void moe_fused_kernel(Fus
     float* smem = reinterpret_cast<float*>(lds);
     gemm_f32_body<true>(static_cast<const float*>(a.x), a.offsets, E_loc,
                         static_cast<const float*>(a.w13), static_cast<float*>(a.h), a.f, a.d,
-                        bid, G, smem, prefix, a.sorted_pair, k);
+                        bid, G, smem, prefix, a.sorted_pair, k,
+                        reinterpret_cast<const float* const*>(a.w13_list));
     grid_barrier(a, G);
     gemm_f32_body<false>(static_cast<const float*>(a.h), a.offsets, E_loc,
                          static_cast<const float*>(a.w2), static_cast<float*>(a.y_perm), a.d, a.f,
-                         bid, G, smem, prefix);
+                         bid, G, smem, prefix, nullptr, 1,
+                         reinterpret_cast<const float* const*>(a.w2_list));
   }
   grid_barrier(a, G);
 

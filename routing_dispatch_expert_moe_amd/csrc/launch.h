@@ -153,6 +153,8 @@ struct FusedArgs {
   const void* x;
   const void* w13;
   const void* w2;
+  const void* const* w13_list;  // per-expert weight tables (TensorList form), else null
+  const void* const* w2_list;
   const float* w13s;  // FP8 weights: the codes' 128 x 128 block scales (else null)
   const float* w2s;
   int T, E, k, gate, capacity, e_begin, e_end, d, f;

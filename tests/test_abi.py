@@ -35,7 +35,7 @@ def test_header_declares_the_path():
               "moe_forward_fused", "moe_quantize_fp8", "moe_expert_ffn_fp8", "moe_ffn_up_fp8",
               "moe_ffn_down_fp8", "moe_expert_ffn_list", "moe_ffn_up_list", "moe_ffn_down_list",
               "moe_route_reroute", "moe_forward_fused_reroute", "moe_forward_fused_fp8",
-              "moe_set_fused_overlap"):
+              "moe_set_fused_overlap", "moe_forward_fused_list"):
         assert n in names
 
 
@@ -275,6 +275,22 @@ def test_fused_validation(lib):
     # a workspace sized for the dispatch alone is too small once rerouting needs its scratch
     dispatch_only = ws_ok - (100 * 3 * 4 + 255) // 256 * 256 * 2 - 256
     assert call_r(wsb=dispatch_only) == L.MOE_ERR_WORKSPACE
+    # the TensorList form: the same arguments with weight tables in place of the packed weights
+    t = lib.moe_forward_fused_list
+    assert _call_list(t, ok, w13=None) == L.MOE_ERR_INVALID_ARG
+    assert _call_list(t, ok, w2=None) == L.MOE_ERR_INVALID_ARG
+    assert _call_list(t, ok, w2=MIS) == L.MOE_ERR_MISALIGNED
+    assert _call_list(t, ok, k=9) == L.MOE_ERR_INVALID_TOPK
+    assert _call_list(t, ok, d=100) == L.MOE_ERR_UNSUPPORTED
+    assert _call_list(t, ok, wsb=2047) == L.MOE_ERR_WORKSPACE
+
+
+def _call_list(fn, ok, **kw):
+    a = dict(ok)
+    a.update(kw)
+    return fn(a["lg"], a["x"], a["T"], a["E"], a["k"], a["gate"], a["cap"], a["e0"], a["e1"],
+              a["d"], a["f"], a["dt"], a["w13"], a["w2"], a["idx"], a["w"], a["counts"], a["off"],
+              a["sp"], a["pp"], a["nk"], a["h"], a["yp"], a["y"], a["ws"], a["wsb"], None)
 
 
 def test_package_fails_loudly_without_library(monkeypatch, tmp_path):

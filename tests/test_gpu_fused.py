@@ -63,6 +63,52 @@ def test_fused_layer(kw):
     assert O.rel_err(as64(fl.y, wl.dtype), ref["y"]) <= TOL[wl.dtype]
 
 
+@pytest.mark.parametrize("kw", [
+    dict(name="l1", T=200, d=128, f=192, E=8, k=2, dtype="bf16"),
+    dict(name="l2", T=333, d=128, f=128, E=16, k=2, dtype="bf16", capacity_factor=1.25,
+         e_begin=4, e_end=12, logit_bias="normal"),
+    # 256-row tiles over the full blocks and 128 x 128 remainder tiles (K = 4224)
+    dict(name="l3", T=1200, d=256, f=4224, E=4, k=1, dtype="bf16"),
+    dict(name="l4", T=64, d=128, f=256, E=8, k=2, dtype="f32"),
+])
+def test_fused_layer_list(kw):
+    """moe_forward_fused_list (per-expert weight buffers through pointer
+    tables, the TensorList form) gives the same bits as moe_forward_fused on
+    the packed weights, in both orders of the GEMM phases."""
+    kw = dict(kw)
+    log(f"fused layer, weight tables {kw}")
+    name = kw.pop("name")
+    wl = custom(name, seed=8, **kw)
+    w13, w2p, _ = packed_weights(wl)
+    x = t_in(wl.x, wl.dtype)
+    logits = t_in(wl.logits, "f32")
+    ref = layer_for(wl, w13, w2p)
+    ref.forward_fused(x, logits)
+    assert M.moe_check_error(ref.ws) == 0
+    # every expert in a buffer of its own
+    b13 = [w13[i].clone() for i in range(wl.E_loc)]
+    b2 = [w2p[i].clone() for i in range(wl.E_loc)]
+    t13, t2 = M.weight_table(b13), M.weight_table(b2)
+    fl = layer_for(wl, w13, w2p)
+    a = ref.outputs()
+    n = int(t_out(a["n_kept"])[0])
+    try:
+        for mode in ("auto", "never", "always"):
+            M.moe_set_fused_overlap(mode)
+            fl.y.zero_()
+            M.moe_forward_fused_list(logits, x, wl.k, wl.gate, fl.capacity, wl.e_begin, wl.e_end,
+                                     t13, t2, wl.f, fl.ws, fl.plan, fl.topk_idx, fl.topk_w, fl.h,
+                                     fl.y_perm, fl.y)
+            assert M.moe_check_error(fl.ws) == 0
+            b = fl.outputs()
+            for key in ("topk_idx", "topk_w", "counts", "offsets", "pair_pos", "y"):
+                assert np.array_equal(t_out(a[key]), t_out(b[key])), (mode, key)
+            for key in ("sorted_pair", "h", "y_perm"):
+                assert np.array_equal(t_out(a[key])[:n], t_out(b[key])[:n]), (mode, key)
+    finally:
+        M.moe_set_fused_overlap("auto")
+
+
 def test_fused_all_dropped():
     wl = custom(T=40, d=64, f=64, E=4, k=2, dtype="bf16", seed=2)
     w13, w2p, _ = packed_weights(wl)
