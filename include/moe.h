@@ -300,6 +300,29 @@ moe_status moe_ffn_down_fp8(const void* h, const int32_t* offsets, int E_loc, in
                             int d, int f, const uint8_t* w2_q, const float* w2_s, void* y_perm,
                             void* stream);
 
+/* The FP8 calls over per-expert buffers (DWDP page, key optimisations and
+ * TensorList: the grouped GEMM takes a list of weight buffers, so experts
+ * need not be one packed tensor; NCCL EP page §2.1: FP8 expert compute with
+ * a scale tensor).  *_q_list and *_s_list: device tables of E_loc device
+ * pointers; entry i of a code table points to expert i of moe_quantize_fp8's
+ * codes ([2f][d] for w13, [d][f] for w2, uint8), entry i of a scale table to
+ * expert i of its scales ([2f/128][d/128] resp. [d/128][f/128], fp32); every
+ * buffer and table 16-byte aligned and alive until the call's kernels have
+ * run.  Same kernels and bits as the packed FP8 calls.  A NULL table is
+ * MOE_ERR_INVALID_ARG; other rules and errors as moe_expert_ffn_fp8.  No
+ * workspace. */
+moe_status moe_expert_ffn_fp8_list(const void* x_perm, const int32_t* offsets, int E_loc,
+                                   int64_t max_rows, int d, int f,
+                                   const void* const* w13_q_list, const float* const* w13_s_list,
+                                   const void* const* w2_q_list, const float* const* w2_s_list,
+                                   void* h, void* y_perm, void* stream);
+moe_status moe_ffn_up_fp8_list(const void* x_perm, const int32_t* offsets, int E_loc,
+                               int64_t max_rows, int d, int f, const void* const* w13_q_list,
+                               const float* const* w13_s_list, void* h, void* stream);
+moe_status moe_ffn_down_fp8_list(const void* h, const int32_t* offsets, int E_loc,
+                                 int64_t max_rows, int d, int f, const void* const* w2_q_list,
+                                 const float* const* w2_s_list, void* y_perm, void* stream);
+
 /* Weighted combine (NCCL EP page §2.1, LL combine):
  *   y[t] = sum_{j=0..k-1, pair_pos[t*k+j] >= 0} topk_w[t][j] * y_perm[pair_pos[t*k+j]]
  * accumulated in fp32 in ascending j, rounded once to `dtype`; tokens with no

@@ -67,6 +67,10 @@ SIGNATURES = {
     "moe_expert_ffn_fp8": (_i, [_vp, _i32p, _i, _i64, _i, _i, _vp, _fp, _vp, _fp, _vp, _vp, _vp]),
     "moe_ffn_up_fp8": (_i, [_vp, _i32p, _i, _i64, _i, _i, _vp, _fp, _vp, _vp]),
     "moe_ffn_down_fp8": (_i, [_vp, _i32p, _i, _i64, _i, _i, _vp, _fp, _vp, _vp]),
+    "moe_expert_ffn_fp8_list": (_i, [_vp, _i32p, _i, _i64, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp,
+                                     _vp]),
+    "moe_ffn_up_fp8_list": (_i, [_vp, _i32p, _i, _i64, _i, _i, _vp, _vp, _vp, _vp]),
+    "moe_ffn_down_fp8_list": (_i, [_vp, _i32p, _i, _i64, _i, _i, _vp, _vp, _vp, _vp]),
     "moe_ffn_up_train": (_i, [_vp, _i32p, _i, _i64, _i, _i, _i, _vp, _vp, _vp, _vp]),
     "moe_pack_weights_backward": (_i, [_vp, _vp, _i, _i, _i, _i, _vp, _vp]),
     "moe_combine_backward": (_i, [_vp, _vp, _i32p, _fp, _i, _i, _i, _i, _vp, _fp, _vp]),

@@ -316,6 +316,46 @@ moe_status moe_ffn_down_fp8(const void* h, const int32_t* offsets, int E_loc, in
                                              y_perm, stream));
 }
 
+// the FP8 calls over per-expert code and scale buffers: the tables stand
+// where the packed codes and scales do in the shape and pointer checks
+moe_status moe_ffn_up_fp8_list(const void* x_perm, const int32_t* offsets, int E_loc,
+                               int64_t max_rows, int d, int f, const void* const* w13_q_list,
+                               const float* const* w13_s_list, void* h, void* stream) {
+  moe_status st = check_ffn_fp8(x_perm, offsets, E_loc, max_rows, d, f, w13_q_list,
+                                reinterpret_cast<const float*>(w13_s_list), h);
+  if (st != MOE_OK) return st;
+  return hip_status(moe::launch_ffn_up_fp8(x_perm, offsets, E_loc, max_rows, d, f, nullptr,
+                                           nullptr, h, stream, w13_q_list, w13_s_list));
+}
+
+moe_status moe_ffn_down_fp8_list(const void* h, const int32_t* offsets, int E_loc,
+                                 int64_t max_rows, int d, int f, const void* const* w2_q_list,
+                                 const float* const* w2_s_list, void* y_perm, void* stream) {
+  moe_status st = check_ffn_fp8(h, offsets, E_loc, max_rows, d, f, w2_q_list,
+                                reinterpret_cast<const float*>(w2_s_list), y_perm);
+  if (st != MOE_OK) return st;
+  return hip_status(moe::launch_ffn_down_fp8(h, offsets, E_loc, max_rows, d, f, nullptr, nullptr,
+                                             y_perm, stream, w2_q_list, w2_s_list));
+}
+
+moe_status moe_expert_ffn_fp8_list(const void* x_perm, const int32_t* offsets, int E_loc,
+                                   int64_t max_rows, int d, int f,
+                                   const void* const* w13_q_list, const float* const* w13_s_list,
+                                   const void* const* w2_q_list, const float* const* w2_s_list,
+                                   void* h, void* y_perm, void* stream) {
+  moe_status st = check_ffn_fp8(x_perm, offsets, E_loc, max_rows, d, f, w13_q_list,
+                                reinterpret_cast<const float*>(w13_s_list), h);
+  if (st != MOE_OK) return st;
+  st = check_ffn_fp8(h, offsets, E_loc, max_rows, d, f, w2_q_list,
+                     reinterpret_cast<const float*>(w2_s_list), y_perm);
+  if (st != MOE_OK) return st;
+  st = moe_ffn_up_fp8_list(x_perm, offsets, E_loc, max_rows, d, f, w13_q_list, w13_s_list, h,
+                           stream);
+  if (st != MOE_OK) return st;
+  return moe_ffn_down_fp8_list(h, offsets, E_loc, max_rows, d, f, w2_q_list, w2_s_list, y_perm,
+                               stream);
+}
+
 moe_status moe_expert_ffn_fp8(const void* x_perm, const int32_t* offsets, int E_loc,
                               int64_t max_rows, int d, int f, const uint8_t* w13_q,
                               const float* w13_s, const uint8_t* w2_q, const float* w2_s,

@@ -54,7 +54,7 @@ template <int BM, int BN, int BK, int WM, int WN, bool SWIGLU, int CLASS, bool F
 __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets, int E_loc,
     const void* __restrict__ Wv, const float* __restrict__ Ws, uint16_t* __restrict__ C, int N,
-    int K, const void* const* __restrict__ wlist) {
+    int K, const void* const* __restrict__ wlist, const float* const* __restrict__ slist) {
   constexpr int NTHR = WM * WN * 64;
   constexpr int BNW = SWIGLU ? 2 * BN : BN;  // weight rows per tile
   constexpr int KC = BK / 8;                 // 16-byte chunks per tile row
@@ -245,12 +245,13 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(
       if constexpr (FP8W) {
         if (wave_active && ((kt + 1) * BK) % kFp8Block == 0) {
           const int kb = (kt * BK) / kFp8Block;
+          const float* se = slist != nullptr ? slist[e] : Ws + static_cast<size_t>(e) * RB * KB;
 #pragma unroll
           for (int j = 0; j < FN; ++j) {
             const int rowb = (n0 + wn * TN + j * 32) / kFp8Block;  // W1 (or W2) block row
-            const float sc = Ws[(static_cast<size_t>(e) * RB + rowb) * KB + kb];
+            const float sc = se[static_cast<size_t>(rowb) * KB + kb];
             float scg = 0.f;
-            if constexpr (SWIGLU) scg = Ws[(static_cast<size_t>(e) * RB + N / kFp8Block + rowb) * KB + kb];
+            if constexpr (SWIGLU) scg = se[static_cast<size_t>(N / kFp8Block + rowb) * KB + kb];
 #pragma unroll
             for (int i = 0; i < FM; ++i) {
               acc[i][j] += sc * part[i][j];
@@ -319,7 +320,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(
 template <int BM, int BN, int BK, int WM, int WN, bool SWIGLU, int CLASS, bool FP8W = false>
 static int launch_gemm(const void* A, const int32_t* offsets, int E_loc, int64_t max_rows,
                        const void* W, void* C, int N, int K, hipStream_t s,
-                       const float* Ws = nullptr, const void* const* wlist = nullptr) {
+                       const float* Ws = nullptr, const void* const* wlist = nullptr,
+                       const float* const* slist = nullptr) {
   constexpr int BNW = SWIGLU ? 2 * BN : BN;
   const size_t lds = static_cast<size_t>(2) * (BM + BNW) * BK * sizeof(uint16_t);
   auto kern = gemm_bf16_kernel<BM, BN, BK, WM, WN, SWIGLU, CLASS, FP8W>;
@@ -339,7 +341,7 @@ static int launch_gemm(const void* A, const int32_t* offsets, int E_loc, int64_t
   if (grid < 1) grid = 1;
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(WM * WN * 64), lds, s,
                      static_cast<const uint16_t*>(A), offsets, E_loc, W, Ws,
-                     static_cast<uint16_t*>(C), N, K, wlist);
+                     static_cast<uint16_t*>(C), N, K, wlist, slist);
   return static_cast<int>(hipGetLastError());
 }
 
@@ -450,10 +452,12 @@ namespace moe {
 // the device.
 static int fp8_pipe_pass(bool up, const void* A, const int32_t* offsets, int E_loc,
                          int64_t max_rows, int d, int f, const uint8_t* wq, const float* ws,
-                         void* C, void* stream) {
+                         void* C, const void* const* wlist, const float* const* slist,
+                         void* stream) {
   const int N = up ? f : d, K = up ? d : f;
   auto run = [&](PipeRows r) {
-    return launch_gemm_pipe_fp8(r, up, A, offsets, E_loc, max_rows, wq, ws, C, N, K, stream);
+    return launch_gemm_pipe_fp8(r, up, A, offsets, E_loc, max_rows, wq, ws, C, N, K, wlist, slist,
+                                stream);
   };
   // the bf16 pass's row classes: 256-row tiles then 128-row remainder tiles
   // (long-K passes with few tiles), the ride-along split (many tiles: the
@@ -474,28 +478,32 @@ static int fp8_pipe_pass(bool up, const void* A, const int32_t* offsets, int E_l
 }
 int launch_ffn_up_fp8(const void* x_perm, const int32_t* offsets, int E_loc, int64_t max_rows,
                       int d, int f, const uint8_t* w13q, const float* w13s, void* h,
-                      void* stream) {
+                      void* stream, const void* const* wlist, const float* const* slist) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (max_rows == 0) return 0;
   if (max_rows / E_loc <= kStreamRows)
-    return launch_gemm_fp8w(true, x_perm, offsets, E_loc, max_rows, w13q, w13s, h, f, d, stream);
+    return launch_gemm_fp8w(true, x_perm, offsets, E_loc, max_rows, w13q, w13s, h, f, d, stream,
+                            wlist, slist);
   if (d >= fp8_pipe_min_k() && ffn_operands_fit32(true, max_rows, d, f))
-    return fp8_pipe_pass(true, x_perm, offsets, E_loc, max_rows, d, f, w13q, w13s, h, stream);
+    return fp8_pipe_pass(true, x_perm, offsets, E_loc, max_rows, d, f, w13q, w13s, h, wlist,
+                         slist, stream);
   return launch_gemm<64, 128, 64, 2, 2, true, ROWS_ALL, true>(x_perm, offsets, E_loc, max_rows,
-                                                              w13q, h, f, d, s, w13s);
+                                                              w13q, h, f, d, s, w13s, wlist, slist);
 }
 
 int launch_ffn_down_fp8(const void* h, const int32_t* offsets, int E_loc, int64_t max_rows,
                         int d, int f, const uint8_t* w2q, const float* w2s, void* y,
-                        void* stream) {
+                        void* stream, const void* const* wlist, const float* const* slist) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (max_rows == 0) return 0;
   if (max_rows / E_loc <= kStreamRows)
-    return launch_gemm_fp8w(false, h, offsets, E_loc, max_rows, w2q, w2s, y, d, f, stream);
+    return launch_gemm_fp8w(false, h, offsets, E_loc, max_rows, w2q, w2s, y, d, f, stream, wlist,
+                            slist);
   if (f >= fp8_pipe_min_k() && ffn_operands_fit32(false, max_rows, d, f))
-    return fp8_pipe_pass(false, h, offsets, E_loc, max_rows, d, f, w2q, w2s, y, stream);
+    return fp8_pipe_pass(false, h, offsets, E_loc, max_rows, d, f, w2q, w2s, y, wlist, slist,
+                         stream);
   return launch_gemm<64, 128, 64, 2, 2, false, ROWS_ALL, true>(h, offsets, E_loc, max_rows, w2q,
-                                                               y, d, f, s, w2s);
+                                                               y, d, f, s, w2s, wlist, slist);
 }
 
 }  // namespace moe

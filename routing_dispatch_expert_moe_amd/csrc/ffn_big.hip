@@ -38,13 +38,14 @@ template <bool SWIGLU, int BM, int CLASS>
 __global__ __launch_bounds__(kFp8Waves * 64, 1) void gemm_fp8_pipe(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets, int E_loc,
     const uint8_t* __restrict__ Wq, const float* __restrict__ Ws, uint16_t* __restrict__ C,
-    int N, int K) {
+    int N, int K, const uint16_t* const* __restrict__ wlist,
+    const float* const* __restrict__ slist) {
   extern __shared__ uint4 lds[];
   __shared__ int prefix[MOE_MAX_E + 1];
   __shared__ int segs[MOE_MAX_E + 1];
   gemm_pipe_body<SWIGLU, BM, 256, fp8_stages<BM>(), CLASS, kFp8Waves, false, true, kFp8BK>(
       A, offsets, E_loc, reinterpret_cast<const uint16_t*>(Wq), C, N, K, blockIdx.x, gridDim.x,
-      lds, prefix, segs, nullptr, 1, nullptr, nullptr, Ws);
+      lds, prefix, segs, nullptr, 1, wlist, nullptr, Ws, nullptr, nullptr, nullptr, slist);
 }
 
 int fp8_pipe_min_k() {
@@ -56,7 +57,8 @@ namespace {
 
 template <bool SWIGLU, int BM, int CLASS>
 int launch_fp8(const void* A, const int32_t* offsets, int E_loc, int64_t max_rows,
-               const uint8_t* Wq, const float* Ws, void* C, int N, int K, hipStream_t s) {
+               const uint8_t* Wq, const float* Ws, void* C, int N, int K, const void* const* wlist,
+               const float* const* slist, hipStream_t s) {
   constexpr size_t lds = pipe_lds_bytes(BM, 256, fp8_stages<BM>(), true, kFp8BK);
   static_assert(lds + 2 * (MOE_MAX_E + 1) * 4 <= 160 * 1024, "LDS budget");
   auto kern = gemm_fp8_pipe<SWIGLU, BM, CLASS>;
@@ -72,25 +74,26 @@ int launch_fp8(const void* A, const int32_t* offsets, int E_loc, int64_t max_row
   if (grid < 1) grid = 1;
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(kFp8Waves * 64), lds, s,
                      static_cast<const uint16_t*>(A), offsets, E_loc, Wq, Ws,
-                     static_cast<uint16_t*>(C), N, K);
+                     static_cast<uint16_t*>(C), N, K,
+                     reinterpret_cast<const uint16_t* const*>(wlist), slist);
   return static_cast<int>(hipGetLastError());
 }
 
 template <bool SWIGLU>
 int launch_fp8_kind(PipeRows rows, const void* A, const int32_t* offsets, int E_loc,
                     int64_t max_rows, const uint8_t* Wq, const float* Ws, void* C, int N, int K,
-                    hipStream_t s) {
+                    const void* const* wlist, const float* const* slist, hipStream_t s) {
   switch (rows) {
     case PipeRows::kBigTiles:
-      return launch_fp8<SWIGLU, 256, ROWS_BIG>(A, offsets, E_loc, max_rows, Wq, Ws, C, N, K, s);
+      return launch_fp8<SWIGLU, 256, ROWS_BIG>(A, offsets, E_loc, max_rows, Wq, Ws, C, N, K, wlist, slist, s);
     case PipeRows::kTailTiles:
-      return launch_fp8<SWIGLU, 128, ROWS_TAIL>(A, offsets, E_loc, max_rows, Wq, Ws, C, N, K, s);
+      return launch_fp8<SWIGLU, 128, ROWS_TAIL>(A, offsets, E_loc, max_rows, Wq, Ws, C, N, K, wlist, slist, s);
     case PipeRows::kBigRide:
-      return launch_fp8<SWIGLU, 256, ROWS_BIGR>(A, offsets, E_loc, max_rows, Wq, Ws, C, N, K, s);
+      return launch_fp8<SWIGLU, 256, ROWS_BIGR>(A, offsets, E_loc, max_rows, Wq, Ws, C, N, K, wlist, slist, s);
     case PipeRows::kTailRide:
-      return launch_fp8<SWIGLU, 128, ROWS_TAILR>(A, offsets, E_loc, max_rows, Wq, Ws, C, N, K, s);
+      return launch_fp8<SWIGLU, 128, ROWS_TAILR>(A, offsets, E_loc, max_rows, Wq, Ws, C, N, K, wlist, slist, s);
     default:
-      return launch_fp8<SWIGLU, 256, ROWS_ALL>(A, offsets, E_loc, max_rows, Wq, Ws, C, N, K, s);
+      return launch_fp8<SWIGLU, 256, ROWS_ALL>(A, offsets, E_loc, max_rows, Wq, Ws, C, N, K, wlist, slist, s);
   }
 }
 
@@ -98,10 +101,14 @@ int launch_fp8_kind(PipeRows rows, const void* A, const int32_t* offsets, int E_
 
 int launch_gemm_pipe_fp8(PipeRows rows, bool swiglu, const void* A, const int32_t* offsets,
                          int E_loc, int64_t max_rows, const uint8_t* Wq, const float* Ws, void* C,
-                         int N, int K, void* stream) {
+                         int N, int K, const void* const* wlist, const float* const* slist,
+                         void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (swiglu) return launch_fp8_kind<true>(rows, A, offsets, E_loc, max_rows, Wq, Ws, C, N, K, s);
-  return launch_fp8_kind<false>(rows, A, offsets, E_loc, max_rows, Wq, Ws, C, N, K, s);
+  if (swiglu)
+    return launch_fp8_kind<true>(rows, A, offsets, E_loc, max_rows, Wq, Ws, C, N, K, wlist, slist,
+                                 s);
+  return launch_fp8_kind<false>(rows, A, offsets, E_loc, max_rows, Wq, Ws, C, N, K, wlist, slist,
+                                s);
 }
 
 namespace {

@@ -81,16 +81,18 @@ __global__ __launch_bounds__(256, 2) void gemm_fp8w_kernel(const uint16_t* __res
                                                         const int32_t* __restrict__ offsets,
                                                         int E_loc, const uint8_t* __restrict__ Wq,
                                                         const float* __restrict__ Ws,
-                                                        uint16_t* __restrict__ C, int N, int K) {
+                                                        uint16_t* __restrict__ C, int N, int K,
+                                                        const uint8_t* const* __restrict__ wlist,
+                                                        const float* const* __restrict__ slist) {
   __shared__ uint4 lds[Fp8wTile<BN, SWIGLU>::kLdsU4];
   __shared__ int prefix[MOE_MAX_E + 1];
   gemm_fp8w_body<BN, SWIGLU, 1>(A, offsets, E_loc, Wq, Ws, C, N, K, blockIdx.x, gridDim.x, lds,
-                                prefix);
+                                prefix, nullptr, 1, wlist, slist);
 }
 
 int launch_gemm_fp8w(bool swiglu, const void* A, const int32_t* offsets, int E_loc,
                      int64_t max_rows, const uint8_t* Wq, const float* Ws, void* C, int N, int K,
-                     void* stream) {
+                     void* stream, const void* const* wlist, const float* const* slist) {
   constexpr int BN = 128;
   const void* kern = swiglu ? reinterpret_cast<const void*>(gemm_fp8w_kernel<BN, true>)
                             : reinterpret_cast<const void*>(gemm_fp8w_kernel<BN, false>);
@@ -107,12 +109,13 @@ int launch_gemm_fp8w(bool swiglu, const void* A, const int32_t* offsets, int E_l
   hipStream_t s = static_cast<hipStream_t>(stream);
   const uint16_t* a = static_cast<const uint16_t*>(A);
   uint16_t* c = static_cast<uint16_t*>(C);
+  const uint8_t* const* wl = reinterpret_cast<const uint8_t* const*>(wlist);
   if (swiglu)
     hipLaunchKernelGGL((gemm_fp8w_kernel<BN, true>), dim3(static_cast<unsigned>(grid)), dim3(256),
-                       0, s, a, offsets, E_loc, Wq, Ws, c, N, K);
+                       0, s, a, offsets, E_loc, Wq, Ws, c, N, K, wl, slist);
   else
     hipLaunchKernelGGL((gemm_fp8w_kernel<BN, false>), dim3(static_cast<unsigned>(grid)), dim3(256),
-                       0, s, a, offsets, E_loc, Wq, Ws, c, N, K);
+                       0, s, a, offsets, E_loc, Wq, Ws, c, N, K, wl, slist);
   return static_cast<int>(hipGetLastError());
 }
 

@@ -42,6 +42,9 @@ constexpr size_t fp8w_lds_bytes(int parts) {
 // lds: fp8w_lds_bytes(PARTS) bytes; prefix: MOE_MAX_E + 1 ints of LDS.
 // gather: if not null, activation row r is row gather[r] / gk of A (the fused
 // layer reads the token rows in place).  N and K are multiples of 128.
+// wlist / slist: if not null, expert e's codes start at wlist[e] and its
+// block scales at slist[e] (tables of per-expert buffers) instead of
+// Wq + e * rows * K and Ws + e * (rows / 128) * (K / 128).
 template <int BN, bool SWIGLU, int PARTS>
 __device__ __forceinline__ void gemm_fp8w_body(const uint16_t* __restrict__ A,
                                                const int32_t* __restrict__ offsets, int E_loc,
@@ -50,7 +53,9 @@ __device__ __forceinline__ void gemm_fp8w_body(const uint16_t* __restrict__ A,
                                                uint16_t* __restrict__ C, int N, int K, int bid,
                                                int G, uint4* lds, int* prefix,
                                                const int32_t* __restrict__ gather = nullptr,
-                                               int gk = 1) {
+                                               int gk = 1,
+                                               const uint8_t* const* __restrict__ wlist = nullptr,
+                                               const float* const* __restrict__ slist = nullptr) {
   using P = Fp8wTile<BN, SWIGLU>;
   constexpr int BM = P::BM, BK = P::BK, WN = P::WN, NTHR = P::NTHR;
   constexpr int BNW = P::BNW, AKC = P::AKC, BU = P::BU;
@@ -108,7 +113,8 @@ __device__ __forceinline__ void gemm_fp8w_body(const uint16_t* __restrict__ A,
       const int c = tid + i * NTHR, r = c / BU, u = c % BU;
       const int half = SWIGLU ? r / BN : 0, n = n0 + r % BN;
       b_ok[i] = n < N;
-      b_src[i] = Wq + e * wstride + (static_cast<size_t>(half) * N + (b_ok[i] ? n : 0)) * K + u * 16;
+      b_src[i] = (wlist != nullptr ? wlist[e] : Wq + e * wstride) +
+                 (static_cast<size_t>(half) * N + (b_ok[i] ? n : 0)) * K + u * 16;
       b_dst[i] = r * BU + (u ^ ((r >> 1) & 7));
     }
     uint4 ra[CA], rq[CB];
@@ -149,13 +155,13 @@ __device__ __forceinline__ void gemm_fp8w_body(const uint16_t* __restrict__ A,
     }
     // block scales of step kt (the wave's columns lie in one 128-row block)
     float sc[FN], scg[SWIGLU ? FN : 1];
+    const float* se = slist != nullptr ? slist[e] : Ws + static_cast<size_t>(e) * RB * KT;
     auto sload = [&](int kt) {
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         const int rowb = (n0 + wn * TN + j * 32) / kFp8Block;
-        sc[j] = Ws[(static_cast<size_t>(e) * RB + rowb) * KT + kt];
-        if constexpr (SWIGLU)
-          scg[j] = Ws[(static_cast<size_t>(e) * RB + N / kFp8Block + rowb) * KT + kt];
+        sc[j] = se[static_cast<size_t>(rowb) * KT + kt];
+        if constexpr (SWIGLU) scg[j] = se[static_cast<size_t>(N / kFp8Block + rowb) * KT + kt];
       }
     };
     sload(0);

@@ -138,8 +138,10 @@ constexpr size_t pipe_lds_bytes(int BM, int BNW, int STAGES, bool fp8w = false, 
 // (4 or 8: one or two per SIMD) split the tile 2 x NW/2.
 // gather: if not null, activation row r is row gather[r] / gk of A (A rows
 // read in place through the dispatch permutation instead of a permuted copy).
-// wlist: if not null, expert e's packed weights start at wlist[e] (a table of
-// per-expert buffers) instead of W + e * (weight rows * K).
+// wlist: if not null, expert e's packed weights (FP8W: codes) start at
+// wlist[e] (a table of per-expert buffers) instead of W + e * (weight rows * K);
+// slist (FP8W): if not null, expert e's block scales start at slist[e]
+// instead of Ws + e * (rows / 128) * (K / 128).
 // SAVE (SwiGLU only): the pre-activations are also stored, a = A W1 at
 // AB[row][col] and g = A W3 at AB[row][N + col] (row pitch 2N), rounded to
 // bf16, for the backward pass.
@@ -184,7 +186,8 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
                                                const float* __restrict__ Ws = nullptr,
                                                uint32_t* ready_out = nullptr,
                                                const uint32_t* ready_in = nullptr,
-                                               int* err = nullptr) {
+                                               int* err = nullptr,
+                                               const float* const* __restrict__ slist = nullptr) {
   static_assert(SWIGLU || !SAVE, "pre-activations exist only with SwiGLU");
   static_assert(!FP8W || !SAVE, "FP8 weights have no training forward");
   static_assert(BK == 32 || BK == 64, "step depth");
@@ -271,8 +274,9 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       acq_e = t.e;
     }
-    if constexpr (FP8W)
-      iWb = reinterpret_cast<const char*>(W) + t.e * wstride;  // one byte per code
+    if constexpr (FP8W)  // one byte per code
+      iWb = wlist != nullptr ? reinterpret_cast<const char*>(wlist[t.e])
+                             : reinterpret_cast<const char*>(W) + t.e * wstride;
     else
       iWb = reinterpret_cast<const char*>(wlist != nullptr ? wlist[t.e] : W + t.e * wstride);
     // lane % KC is the LDS chunk position the lane writes; it fetches the
@@ -373,7 +377,8 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
     int wrow = SWIGLU ? (q / (NQ / 2)) * N + ct.n0 + wn * (HALF / WN) + (q % (NQ / 2)) * 32
                       : ct.n0 + wn * (BNW / WN) + q * 32;
     if (!SWIGLU) wrow = min(wrow, N - 1);  // columns past N are computed and dropped
-    return Ws[(static_cast<size_t>(ct.e) * RB + wrow / kScaleBlock) * KB + kb];
+    const float* se = slist != nullptr ? slist[ct.e] : Ws + static_cast<size_t>(ct.e) * RB * KB;
+    return se[(wrow / kScaleBlock) * KB + kb];
   };
   // FP8W: codes of slot `slot` to dequantised bf16 operands, code x sq[q]
   // (the power-of-two scale of tile q's current K block); lanes 0..31 take

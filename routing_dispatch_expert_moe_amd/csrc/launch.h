@@ -86,7 +86,8 @@ int ffn_plan_bf16(bool up, int64_t max_rows, int E_loc, int d, int f, int cu);
 int fp8_pipe_min_k();
 int launch_gemm_pipe_fp8(PipeRows rows, bool swiglu, const void* A, const int32_t* offsets,
                          int E_loc, int64_t max_rows, const uint8_t* Wq, const float* Ws, void* C,
-                         int N, int K, void* stream);
+                         int N, int K, const void* const* wlist, const float* const* slist,
+                         void* stream);
 // ab (SwiGLU only): if not null, the pre-activations are stored there too
 // ([rows][2N]: a then g)
 int launch_gemm_pipe_bf16(PipeRows rows, bool swiglu, const void* A, const int32_t* offsets,
@@ -105,15 +106,20 @@ int launch_ffn_up_train_f32(const float* x_perm, const int32_t* offsets, int E_l
 int launch_quantize_fp8(const void* w, int E_loc, int R, int K, uint8_t* q, float* scales,
                         void* stream);
 // few rows per expert: codes kept in LDS, converted per MFMA operand
+// (FP8 launchers: wlist / slist, if not null, are device tables of E_loc
+// per-expert code and scale buffers used in place of Wq / Ws)
 int launch_gemm_fp8w(bool swiglu, const void* A, const int32_t* offsets, int E_loc,
                      int64_t max_rows, const uint8_t* Wq, const float* Ws, void* C, int N, int K,
-                     void* stream);
+                     void* stream, const void* const* wlist = nullptr,
+                     const float* const* slist = nullptr);
 int launch_ffn_up_fp8(const void* x_perm, const int32_t* offsets, int E_loc, int64_t max_rows,
                       int d, int f, const uint8_t* w13q, const float* w13s, void* h,
-                      void* stream);
+                      void* stream, const void* const* wlist = nullptr,
+                      const float* const* slist = nullptr);
 int launch_ffn_down_fp8(const void* h, const int32_t* offsets, int E_loc, int64_t max_rows,
                         int d, int f, const uint8_t* w2q, const float* w2s, void* y,
-                        void* stream);
+                        void* stream, const void* const* wlist = nullptr,
+                        const float* const* slist = nullptr);
 int launch_ffn_up_f32(const float* x_perm, const int32_t* offsets, int E_loc, int64_t max_rows,
                       int d, int f, const float* w13, float* h, const void* const* wlist,
                       void* stream);

@@ -322,6 +322,46 @@ def moe_expert_ffn_fp8(x_perm, offsets, E_loc, max_rows, w13_q, w13_s, w2_q, w2_
     return h, y_perm
 
 
+def moe_ffn_up_fp8_list(x_perm, offsets, E_loc, max_rows, q_table, s_table, f, h=None,
+                        stream=None):
+    """moe_ffn_up_fp8 over per-expert code and scale buffers (tables from
+    weight_table; each buffer one expert of moe_quantize_fp8's outputs)."""
+    d = x_perm.shape[1]
+    if h is None:
+        h = torch.empty((max(max_rows, 1), f), dtype=x_perm.dtype, device=x_perm.device)
+    check(lib().moe_ffn_up_fp8_list(_ptr(x_perm), _ptr(offsets), E_loc, max_rows, d, f,
+                                    _ptr(q_table), _ptr(s_table), _ptr(h), _stream(stream)),
+          "moe_ffn_up_fp8_list")
+    return h
+
+
+def moe_ffn_down_fp8_list(h, offsets, E_loc, max_rows, q_table, s_table, d, y_perm=None,
+                          stream=None):
+    """moe_ffn_down_fp8 over per-expert code and scale buffers."""
+    f = h.shape[1]
+    if y_perm is None:
+        y_perm = torch.empty((max(max_rows, 1), d), dtype=h.dtype, device=h.device)
+    check(lib().moe_ffn_down_fp8_list(_ptr(h), _ptr(offsets), E_loc, max_rows, d, f,
+                                      _ptr(q_table), _ptr(s_table), _ptr(y_perm),
+                                      _stream(stream)), "moe_ffn_down_fp8_list")
+    return y_perm
+
+
+def moe_expert_ffn_fp8_list(x_perm, offsets, E_loc, max_rows, w13_q_table, w13_s_table,
+                            w2_q_table, w2_s_table, f, h=None, y_perm=None, stream=None):
+    """moe_expert_ffn_fp8 over per-expert code and scale buffers."""
+    d = x_perm.shape[1]
+    if h is None:
+        h = torch.empty((max(max_rows, 1), f), dtype=x_perm.dtype, device=x_perm.device)
+    if y_perm is None:
+        y_perm = torch.empty((max(max_rows, 1), d), dtype=x_perm.dtype, device=x_perm.device)
+    check(lib().moe_expert_ffn_fp8_list(_ptr(x_perm), _ptr(offsets), E_loc, max_rows, d, f,
+                                        _ptr(w13_q_table), _ptr(w13_s_table), _ptr(w2_q_table),
+                                        _ptr(w2_s_table), _ptr(h), _ptr(y_perm),
+                                        _stream(stream)), "moe_expert_ffn_fp8_list")
+    return h, y_perm
+
+
 def moe_combine(y_perm, pair_pos, topk_w, y=None, stream=None, T=None, k=None):
     """y [T, d]; topk_w None: unit weights (then pass T and k)."""
     if topk_w is not None:

@@ -35,7 +35,8 @@ def test_header_declares_the_path():
               "moe_forward_fused", "moe_quantize_fp8", "moe_expert_ffn_fp8", "moe_ffn_up_fp8",
               "moe_ffn_down_fp8", "moe_expert_ffn_list", "moe_ffn_up_list", "moe_ffn_down_list",
               "moe_route_reroute", "moe_forward_fused_reroute", "moe_forward_fused_fp8",
-              "moe_set_fused_overlap", "moe_forward_fused_list"):
+              "moe_set_fused_overlap", "moe_forward_fused_list", "moe_expert_ffn_fp8_list",
+              "moe_ffn_up_fp8_list", "moe_ffn_down_fp8_list"):
         assert n in names
 
 
@@ -196,6 +197,19 @@ def test_fp8_validation(lib):
     assert f(*bad) == L.MOE_ERR_INVALID_ARG
     assert lib.moe_ffn_up_fp8(FAKE, FAKE, 8, 100, 4096, 1024, FAKE, None, FAKE, None) == L.MOE_ERR_INVALID_ARG
     assert lib.moe_ffn_down_fp8(FAKE, FAKE, 8, 100, 4096, 1024, FAKE, MIS, FAKE, None) == L.MOE_ERR_MISALIGNED
+    # the TensorList form: the tables stand where the codes and scales do
+    fl = lib.moe_expert_ffn_fp8_list
+    for i, code in ((6, L.MOE_ERR_INVALID_ARG), (7, L.MOE_ERR_INVALID_ARG),
+                    (8, L.MOE_ERR_INVALID_ARG), (9, L.MOE_ERR_INVALID_ARG)):
+        bad = list(ok); bad[i] = None          # a missing code or scale table
+        assert fl(*bad) == code
+    bad = list(ok); bad[8] = MIS
+    assert fl(*bad) == L.MOE_ERR_MISALIGNED
+    bad = list(ok); bad[5] = 960
+    assert fl(*bad) == L.MOE_ERR_UNSUPPORTED
+    assert lib.moe_ffn_up_fp8_list(FAKE, FAKE, 8, 100, 4096, 1024, FAKE, None, FAKE, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_ffn_down_fp8_list(FAKE, FAKE, 8, 100, 4096, 1024, MIS, FAKE, FAKE, None) == L.MOE_ERR_MISALIGNED
+    assert lib.moe_ffn_down_fp8_list(FAKE, FAKE, 0, 100, 4096, 1024, FAKE, FAKE, FAKE, None) == L.MOE_ERR_INVALID_ARG
 
 
 def test_combine_router_pack_validation(lib):

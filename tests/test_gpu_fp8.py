@@ -124,6 +124,21 @@ def test_expert_ffn_fp8(d, f, rows):
     y1 = t_out(y).copy()
     M.moe_expert_ffn_fp8(xt, off_t, E_loc, max_rows, q13, s13, q2, s2, h, y)
     assert np.array_equal(t_out(y), y1)
+    # the TensorList form: every expert's codes and scales in buffers of their
+    # own (allocated in reverse order), same bits as the packed tensors
+    bufs = [None] * E_loc
+    for i in reversed(range(E_loc)):
+        bufs[i] = (q13[i].clone(), s13[i].clone(), q2[i].clone(), s2[i].clone())
+    tabs = [M.weight_table([b[j] for b in bufs]) for j in range(4)]
+    hl, yl = M.moe_expert_ffn_fp8_list(xt, off_t, E_loc, max_rows, *tabs, f)
+    assert np.array_equal(t_out(hl)[:n], t_out(h)[:n])
+    assert np.array_equal(t_out(yl)[:n], y1[:n])
+    # and the halves on their own
+    hl.zero_()
+    M.moe_ffn_up_fp8_list(xt, off_t, E_loc, max_rows, tabs[0], tabs[1], f, hl)
+    yl2 = M.moe_ffn_down_fp8_list(hl, off_t, E_loc, max_rows, tabs[2], tabs[3], d)
+    assert np.array_equal(t_out(hl)[:n], t_out(h)[:n])
+    assert np.array_equal(t_out(yl2)[:n], y1[:n])
 
 
 @pytest.mark.timeout(600)
