@@ -444,6 +444,24 @@ moe_status moe_forward_fused_fp8(const float* logits, const void* x, int T, int 
                                  int32_t* pair_pos, int32_t* n_kept, void* h, void* y_perm,
                                  void* y, void* ws, size_t ws_bytes, void* stream);
 
+/* moe_forward_fused_fp8 with the codes and block scales as per-expert
+ * buffers (DWDP page, key optimisations and TensorList; the tables as in
+ * moe_expert_ffn_fp8_list: entry i of w13_q_list / w13_s_list / w2_q_list /
+ * w2_s_list points to expert i of moe_quantize_fp8's codes or scales, each
+ * 16-byte aligned).  Same bits as moe_forward_fused_fp8 on the packed codes
+ * and scales; a NULL table is MOE_ERR_INVALID_ARG, other rules and errors as
+ * moe_forward_fused_fp8. */
+moe_status moe_forward_fused_fp8_list(const float* logits, const void* x, int T, int E, int k,
+                                      int gate, int capacity, int e_begin, int e_end, int d,
+                                      int f, const void* const* w13_q_list,
+                                      const float* const* w13_s_list,
+                                      const void* const* w2_q_list,
+                                      const float* const* w2_s_list, int32_t* topk_idx,
+                                      float* topk_w, int32_t* counts, int32_t* offsets,
+                                      int32_t* sorted_pair, int32_t* pair_pos, int32_t* n_kept,
+                                      void* h, void* y_perm, void* y, void* ws, size_t ws_bytes,
+                                      void* stream);
+
 /* ------------------------------------------------------------------------
  * Backward pass (NCCL EP page §3.2, training adaptation: the backward step
  * reuses the forward's routing handle, sends the output gradient to the

@@ -15,4 +15,4 @@ from .ops import (alloc_plan, alloc_workspace, moe_check_error, moe_combine, moe
                   moe_ffn_up_backward, moe_ffn_wgrad, moe_wgrad_workspace_bytes,
                   moe_router_backward, moe_router_backward_workspace_bytes, moe_set_fused_overlap,
                   moe_forward_fused_list, moe_expert_ffn_fp8_list, moe_ffn_up_fp8_list,
-                  moe_ffn_down_fp8_list)
+                  moe_ffn_down_fp8_list, moe_forward_fused_fp8_list)

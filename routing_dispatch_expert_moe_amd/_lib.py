@@ -91,6 +91,9 @@ SIGNATURES = {
     "moe_forward_fused_fp8": (_i, [_fp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i, _vp, _fp, _vp,
                                    _fp, _i32p, _fp, _i32p, _i32p, _i32p, _i32p, _i32p, _vp, _vp,
                                    _vp, _vp, _sz, _vp]),
+    "moe_forward_fused_fp8_list": (_i, [_fp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i, _vp, _vp,
+                                        _vp, _vp, _i32p, _fp, _i32p, _i32p, _i32p, _i32p, _i32p,
+                                        _vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_set_fused_overlap": (_i, [_i]),
     "moe_forward_fused_list": (_i, [_fp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _vp, _vp,
                                     _i32p, _fp, _i32p, _i32p, _i32p, _i32p, _i32p, _vp, _vp, _vp,

@@ -602,9 +602,13 @@ static moe_status forward_fused_impl(const float* logits, const void* x, int T, 
                                      bool reroute, const float* w13s = nullptr,
                                      const float* w2s = nullptr,
                                      const void* const* w13_list = nullptr,
-                                     const void* const* w2_list = nullptr) {
-  // w13s / w2s set: FP8 weights (codes in w13_packed / w2_packed, bf16 activations)
-  const bool fp8 = w13s != nullptr || w2s != nullptr;
+                                     const void* const* w2_list = nullptr,
+                                     const float* const* w13s_list = nullptr,
+                                     const float* const* w2s_list = nullptr) {
+  // w13s / w2s (or their tables) set: FP8 weights (codes in w13_packed /
+  // w2_packed or the code tables, bf16 activations)
+  const bool fp8 = w13s != nullptr || w2s != nullptr || w13s_list != nullptr ||
+                   w2s_list != nullptr;
   if (T < 0) return MOE_ERR_INVALID_ARG;
   moe_status st = check_topk(E, k);
   if (st != MOE_OK) return st;
@@ -618,9 +622,14 @@ static moe_status forward_fused_impl(const float* logits, const void* x, int T, 
   // GEMM1 reads x in place (rows gathered through sorted_pair)
   if (fp8) {
     if (dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
-    st = check_ffn_fp8(x, offsets, E_loc, max_rows, d, f, w13_packed, w13s, h);
+    // (TensorList form: the code and scale tables stand where the packed ones do)
+    const bool tables = w13s_list != nullptr || w2s_list != nullptr;
+    if (tables && (!w13_list || !w2_list || !w13s_list || !w2s_list)) return MOE_ERR_INVALID_ARG;
+    st = check_ffn_fp8(x, offsets, E_loc, max_rows, d, f, tables ? w13_list : w13_packed,
+                       tables ? reinterpret_cast<const float*>(w13s_list) : w13s, h);
     if (st != MOE_OK) return st;
-    st = check_ffn_fp8(h, offsets, E_loc, max_rows, d, f, w2_packed, w2s, y_perm);
+    st = check_ffn_fp8(h, offsets, E_loc, max_rows, d, f, tables ? w2_list : w2_packed,
+                       tables ? reinterpret_cast<const float*>(w2s_list) : w2s, y_perm);
     if (st != MOE_OK) return st;
     // the pipelined FP8 body's depth
     if (d < moe::fp8_pipe_min_k() || f < moe::fp8_pipe_min_k()) return MOE_ERR_UNSUPPORTED;
@@ -668,6 +677,8 @@ static moe_status forward_fused_impl(const float* logits, const void* x, int T, 
   a.w2_list = w2_list;
   a.w13s = w13s;
   a.w2s = w2s;
+  a.w13s_list = w13s_list;
+  a.w2s_list = w2s_list;
   a.T = T;
   a.E = E;
   a.k = k;
@@ -783,6 +794,23 @@ moe_status moe_forward_fused_fp8(const float* logits, const void* x, int T, int 
   return forward_fused_impl(logits, x, T, E, k, gate, capacity, e_begin, e_end, d, f, MOE_BF16,
                             w13_q, w2_q, topk_idx, topk_w, counts, offsets, sorted_pair, pair_pos,
                             n_kept, h, y_perm, y, ws, ws_bytes, stream, false, w13_s, w2_s);
+}
+
+moe_status moe_forward_fused_fp8_list(const float* logits, const void* x, int T, int E, int k,
+                                      int gate, int capacity, int e_begin, int e_end, int d,
+                                      int f, const void* const* w13_q_list,
+                                      const float* const* w13_s_list,
+                                      const void* const* w2_q_list,
+                                      const float* const* w2_s_list, int32_t* topk_idx,
+                                      float* topk_w, int32_t* counts, int32_t* offsets,
+                                      int32_t* sorted_pair, int32_t* pair_pos, int32_t* n_kept,
+                                      void* h, void* y_perm, void* y, void* ws, size_t ws_bytes,
+                                      void* stream) {
+  if (!w13_q_list || !w13_s_list || !w2_q_list || !w2_s_list) return MOE_ERR_INVALID_ARG;
+  return forward_fused_impl(logits, x, T, E, k, gate, capacity, e_begin, e_end, d, f, MOE_BF16,
+                            nullptr, nullptr, topk_idx, topk_w, counts, offsets, sorted_pair,
+                            pair_pos, n_kept, h, y_perm, y, ws, ws_bytes, stream, false, nullptr,
+                            nullptr, w13_q_list, w2_q_list, w13_s_list, w2_s_list);
 }
 
 }  // extern "C"

@@ -301,21 +301,23 @@ __global__ __launch_bounds__(fused_threads<BF16>(), 1) void moe_fused_kernel(Fus
   // (the launcher never picks OVERLAP with the FP8 code-streaming body,
   // which does not count its tiles)
   uint32_t* up = OVERLAP ? a.up_ready : nullptr;
-  // (a.w13_list / a.w2_list: the bf16 and fp32 weights as per-expert tables;
-  // never with FP8 codes)
+  // (a.w13_list / a.w2_list: the weights or FP8 codes as per-expert tables;
+  // a.w13s_list / a.w2s_list: the FP8 block scales as per-expert tables)
   auto pipe_up = [&](auto cfg, const uint16_t* w, const float* ws) {
     using C = decltype(cfg);
     gemm_pipe_body<true, C::BM, C::BNW, C::STAGES, C::CLASS, 8, false, FP8, 64>(
         static_cast<const uint16_t*>(a.x), a.offsets, E_loc, w, static_cast<uint16_t*>(a.h), a.f,
         a.d, bid, G, lds, prefix, segs, a.sorted_pair, k,
-        reinterpret_cast<const uint16_t* const*>(a.w13_list), nullptr, ws, up, nullptr, a.err);
+        reinterpret_cast<const uint16_t* const*>(a.w13_list), nullptr, ws, up, nullptr, a.err,
+        a.w13s_list);
   };
   auto pipe_down = [&](auto cfg, const uint16_t* w, const float* ws) {
     using C = decltype(cfg);
     gemm_pipe_body<false, C::BM, C::BNW, C::STAGES, C::CLASS, 8, false, FP8, 64>(
         static_cast<const uint16_t*>(a.h), a.offsets, E_loc, w, static_cast<uint16_t*>(a.y_perm),
         a.d, a.f, bid, G, lds, prefix, segs, nullptr, 1,
-        reinterpret_cast<const uint16_t* const*>(a.w2_list), nullptr, ws, nullptr, up, a.err);
+        reinterpret_cast<const uint16_t* const*>(a.w2_list), nullptr, ws, nullptr, up, a.err,
+        a.w2s_list);
   };
   if constexpr (FP8) {
     // the FP8 weights' row splits, as in the separate FP8 calls: few rows per
@@ -331,7 +333,9 @@ __global__ __launch_bounds__(fused_threads<BF16>(), 1) void moe_fused_kernel(Fus
       gemm_fp8w_body<128, true, kParts>(static_cast<const uint16_t*>(a.x), a.offsets, E_loc,
                                         static_cast<const uint8_t*>(a.w13), a.w13s,
                                         static_cast<uint16_t*>(a.h), a.f, a.d, bid, G, lds, prefix,
-                                        a.sorted_pair, k);
+                                        a.sorted_pair, k,
+                                        reinterpret_cast<const uint8_t* const*>(a.w13_list),
+                                        a.w13s_list);
     } else if (a.rows_up == kFusedWide) {
       pipe_up(TileCfg<128, 256, 4, ROWS_ALL>{}, w13, a.w13s);
     } else if (a.rows_up == kFusedBigTail) {
@@ -349,7 +353,9 @@ __global__ __launch_bounds__(fused_threads<BF16>(), 1) void moe_fused_kernel(Fus
       gemm_fp8w_body<128, false, kParts>(static_cast<const uint16_t*>(a.h), a.offsets, E_loc,
                                          static_cast<const uint8_t*>(a.w2), a.w2s,
                                          static_cast<uint16_t*>(a.y_perm), a.d, a.f, bid, G, lds,
-                                         prefix);
+                                         prefix, nullptr, 1,
+                                         reinterpret_cast<const uint8_t* const*>(a.w2_list),
+                                         a.w2s_list);
     } else if (a.rows_down == kFusedBigTail) {
       pipe_down(TileCfg<256, 256, 3, ROWS_BIG>{}, w2, a.w2s);
       pipe_down(TileCfg<128, 256, 4, ROWS_TAIL>{}, w2, a.w2s);

@@ -163,6 +163,8 @@ struct FusedArgs {
   const void* const* w2_list;
   const float* w13s;  // FP8 weights: the codes' 128 x 128 block scales (else null)
   const float* w2s;
+  const float* const* w13s_list;  // FP8 per-expert scale tables (TensorList form), else null
+  const float* const* w2s_list;
   int T, E, k, gate, capacity, e_begin, e_end, d, f;
   int ffn_all_rows;  // bf16: 1 = every row in 128-row tiles (few rows per expert)
   int rows_up, rows_down;  // bf16 GEMM phases (unless ffn_all_rows): a FusedRows value

@@ -427,6 +427,22 @@ def moe_forward_fused_list(logits, x, k, gate, capacity, e_begin, e_end, w13_tab
     return y
 
 
+def moe_forward_fused_fp8_list(logits, x, k, gate, capacity, e_begin, e_end, w13_q_table,
+                               w13_s_table, w2_q_table, w2_s_table, f, ws, plan: DispatchPlan,
+                               topk_idx, topk_w, h, y_perm, y, stream=None):
+    """moe_forward_fused_fp8 over per-expert code and scale buffers (tables
+    from weight_table; each buffer one expert of moe_quantize_fp8's outputs)."""
+    T, E = logits.shape
+    d = x.shape[1]
+    check(lib().moe_forward_fused_fp8_list(
+        _ptr(logits), _ptr(x), T, E, k, _gate_code(gate), capacity, e_begin, e_end, d, f,
+        _ptr(w13_q_table), _ptr(w13_s_table), _ptr(w2_q_table), _ptr(w2_s_table), _ptr(topk_idx),
+        _ptr(topk_w), _ptr(plan.counts), _ptr(plan.offsets), _ptr(plan.sorted_pair),
+        _ptr(plan.pair_pos), _ptr(plan.n_kept), _ptr(h), _ptr(y_perm), _ptr(y), _ptr(ws),
+        ws.numel(), _stream(stream)), "moe_forward_fused_fp8_list")
+    return y
+
+
 def moe_forward_fused_fp8(logits, x, k, gate, capacity, e_begin, e_end, w13_q, w13_s, w2_q, w2_s,
                           ws, plan: DispatchPlan, topk_idx, topk_w, h, y_perm, y, stream=None):
     """moe_forward_fused with FP8 expert weights (codes and block scales from

@@ -36,7 +36,7 @@ def test_header_declares_the_path():
               "moe_ffn_down_fp8", "moe_expert_ffn_list", "moe_ffn_up_list", "moe_ffn_down_list",
               "moe_route_reroute", "moe_forward_fused_reroute", "moe_forward_fused_fp8",
               "moe_set_fused_overlap", "moe_forward_fused_list", "moe_expert_ffn_fp8_list",
-              "moe_ffn_up_fp8_list", "moe_ffn_down_fp8_list"):
+              "moe_ffn_up_fp8_list", "moe_ffn_down_fp8_list", "moe_forward_fused_fp8_list"):
         assert n in names
 
 
@@ -283,6 +283,24 @@ def test_fused_validation(lib):
     assert call_8(k=9) == L.MOE_ERR_INVALID_TOPK
     assert call_8(s13=MIS) == L.MOE_ERR_MISALIGNED
     assert call_8(wsb=2047) == L.MOE_ERR_WORKSPACE
+    # the fused FP8 layer on per-expert tables: the same checks on the tables
+    h8l = lib.moe_forward_fused_fp8_list
+
+    def call_8l(**kw):
+        a = dict(ok, d=256, f=512, s13=FAKE, s2=FAKE)
+        a.update(kw)
+        return h8l(a["lg"], a["x"], a["T"], a["E"], a["k"], a["gate"], a["cap"], a["e0"],
+                   a["e1"], a["d"], a["f"], a["w13"], a["s13"], a["w2"], a["s2"], a["idx"], a["w"],
+                   a["counts"], a["off"], a["sp"], a["pp"], a["nk"], a["h"], a["yp"], a["y"],
+                   a["ws"], a["wsb"], None)
+
+    for key in ("w13", "s13", "w2", "s2"):
+        assert call_8l(**{key: None}) == L.MOE_ERR_INVALID_ARG, key
+    assert call_8l(s2=MIS) == L.MOE_ERR_MISALIGNED
+    assert call_8l(d=192) == L.MOE_ERR_UNSUPPORTED
+    assert call_8l(f=128) == L.MOE_ERR_UNSUPPORTED
+    assert call_8l(k=9) == L.MOE_ERR_INVALID_TOPK
+    assert call_8l(wsb=2047) == L.MOE_ERR_WORKSPACE
     assert call_r(k=9) == L.MOE_ERR_INVALID_TOPK
     assert call_r(gate=5) == L.MOE_ERR_INVALID_ARG
     assert call_r(y=MIS) == L.MOE_ERR_MISALIGNED

@@ -270,3 +270,24 @@ def test_fused_layer_fp8(kw):
     assert np.array_equal(t_out(fl.y), y1)
     # the GEMM phases separated by a barrier instead of the per-expert waits
     barrier_order_matches(fl, x, lg, y1)
+    # the TensorList form: every expert's codes and scales in buffers of
+    # their own, same bits in each order of the GEMM phases
+    bufs = [None] * wl.E_loc
+    for i in reversed(range(wl.E_loc)):
+        bufs[i] = (q13[i].clone(), s13[i].clone(), q2[i].clone(), s2[i].clone())
+    tabs = [M.weight_table([bb[j] for bb in bufs]) for j in range(4)]
+    tl = layer()
+    try:
+        for mode in ("auto", "never", "always"):
+            M.moe_set_fused_overlap(mode)
+            tl.y.zero_()
+            M.moe_forward_fused_fp8_list(lg, x, wl.k, wl.gate, tl.capacity, wl.e_begin, wl.e_end,
+                                         *tabs, wl.f, tl.ws, tl.plan, tl.topk_idx, tl.topk_w,
+                                         tl.h, tl.y_perm, tl.y)
+            assert M.moe_check_error(tl.ws) == 0
+            c = tl.outputs()
+            assert np.array_equal(t_out(c["y"]), y1), mode
+            for key in ("h", "y_perm"):
+                assert np.array_equal(t_out(c[key])[:n], t_out(b[key])[:n]), (mode, key)
+    finally:
+        M.moe_set_fused_overlap("auto")
