@@ -34,7 +34,10 @@ constexpr int kFp8BK = 64, kFp8Waves = 8;
 template <int BM>
 constexpr int fp8_stages() { return BM == 256 ? 3 : 4; }
 
-template <bool SWIGLU, int BM, int CLASS>
+// LIST: codes and scales through per-expert tables (wlist, slist); the packed
+// kernels (LIST false) take null tables at compile time, so their code has no
+// table lookups at all.
+template <bool SWIGLU, int BM, int CLASS, bool LIST>
 __global__ __launch_bounds__(kFp8Waves * 64, 1) void gemm_fp8_pipe(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets, int E_loc,
     const uint8_t* __restrict__ Wq, const float* __restrict__ Ws, uint16_t* __restrict__ C,
@@ -45,7 +48,8 @@ __global__ __launch_bounds__(kFp8Waves * 64, 1) void gemm_fp8_pipe(
   __shared__ int segs[MOE_MAX_E + 1];
   gemm_pipe_body<SWIGLU, BM, 256, fp8_stages<BM>(), CLASS, kFp8Waves, false, true, kFp8BK>(
       A, offsets, E_loc, reinterpret_cast<const uint16_t*>(Wq), C, N, K, blockIdx.x, gridDim.x,
-      lds, prefix, segs, nullptr, 1, wlist, nullptr, Ws, nullptr, nullptr, nullptr, slist);
+      lds, prefix, segs, nullptr, 1, LIST ? wlist : nullptr, nullptr, Ws, nullptr, nullptr,
+      nullptr, LIST ? slist : nullptr);
 }
 
 int fp8_pipe_min_k() {
@@ -55,13 +59,13 @@ int fp8_pipe_min_k() {
 
 namespace {
 
-template <bool SWIGLU, int BM, int CLASS>
+template <bool SWIGLU, int BM, int CLASS, bool LIST>
 int launch_fp8(const void* A, const int32_t* offsets, int E_loc, int64_t max_rows,
                const uint8_t* Wq, const float* Ws, void* C, int N, int K, const void* const* wlist,
                const float* const* slist, hipStream_t s) {
   constexpr size_t lds = pipe_lds_bytes(BM, 256, fp8_stages<BM>(), true, kFp8BK);
   static_assert(lds + 2 * (MOE_MAX_E + 1) * 4 <= 160 * 1024, "LDS budget");
-  auto kern = gemm_fp8_pipe<SWIGLU, BM, CLASS>;
+  auto kern = gemm_fp8_pipe<SWIGLU, BM, CLASS, LIST>;
   static LdsAttr attr;
   if (int rc = set_dynamic_lds_once(reinterpret_cast<const void*>(kern), lds, attr)) return rc;
   const int BN = SWIGLU ? 128 : 256;
@@ -79,21 +83,21 @@ int launch_fp8(const void* A, const int32_t* offsets, int E_loc, int64_t max_row
   return static_cast<int>(hipGetLastError());
 }
 
-template <bool SWIGLU>
+template <bool SWIGLU, bool LIST>
 int launch_fp8_kind(PipeRows rows, const void* A, const int32_t* offsets, int E_loc,
                     int64_t max_rows, const uint8_t* Wq, const float* Ws, void* C, int N, int K,
                     const void* const* wlist, const float* const* slist, hipStream_t s) {
   switch (rows) {
     case PipeRows::kBigTiles:
-      return launch_fp8<SWIGLU, 256, ROWS_BIG>(A, offsets, E_loc, max_rows, Wq, Ws, C, N, K, wlist, slist, s);
+      return launch_fp8<SWIGLU, 256, ROWS_BIG, LIST>(A, offsets, E_loc, max_rows, Wq, Ws, C, N, K, wlist, slist, s);
     case PipeRows::kTailTiles:
-      return launch_fp8<SWIGLU, 128, ROWS_TAIL>(A, offsets, E_loc, max_rows, Wq, Ws, C, N, K, wlist, slist, s);
+      return launch_fp8<SWIGLU, 128, ROWS_TAIL, LIST>(A, offsets, E_loc, max_rows, Wq, Ws, C, N, K, wlist, slist, s);
     case PipeRows::kBigRide:
-      return launch_fp8<SWIGLU, 256, ROWS_BIGR>(A, offsets, E_loc, max_rows, Wq, Ws, C, N, K, wlist, slist, s);
+      return launch_fp8<SWIGLU, 256, ROWS_BIGR, LIST>(A, offsets, E_loc, max_rows, Wq, Ws, C, N, K, wlist, slist, s);
     case PipeRows::kTailRide:
-      return launch_fp8<SWIGLU, 128, ROWS_TAILR>(A, offsets, E_loc, max_rows, Wq, Ws, C, N, K, wlist, slist, s);
+      return launch_fp8<SWIGLU, 128, ROWS_TAILR, LIST>(A, offsets, E_loc, max_rows, Wq, Ws, C, N, K, wlist, slist, s);
     default:
-      return launch_fp8<SWIGLU, 256, ROWS_ALL>(A, offsets, E_loc, max_rows, Wq, Ws, C, N, K, wlist, slist, s);
+      return launch_fp8<SWIGLU, 256, ROWS_ALL, LIST>(A, offsets, E_loc, max_rows, Wq, Ws, C, N, K, wlist, slist, s);
   }
 }
 
@@ -104,11 +108,16 @@ int launch_gemm_pipe_fp8(PipeRows rows, bool swiglu, const void* A, const int32_
                          int N, int K, const void* const* wlist, const float* const* slist,
                          void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool list = wlist != nullptr || slist != nullptr;
   if (swiglu)
-    return launch_fp8_kind<true>(rows, A, offsets, E_loc, max_rows, Wq, Ws, C, N, K, wlist, slist,
-                                 s);
-  return launch_fp8_kind<false>(rows, A, offsets, E_loc, max_rows, Wq, Ws, C, N, K, wlist, slist,
-                                s);
+    return list ? launch_fp8_kind<true, true>(rows, A, offsets, E_loc, max_rows, Wq, Ws, C, N, K,
+                                              wlist, slist, s)
+                : launch_fp8_kind<true, false>(rows, A, offsets, E_loc, max_rows, Wq, Ws, C, N, K,
+                                               wlist, slist, s);
+  return list ? launch_fp8_kind<false, true>(rows, A, offsets, E_loc, max_rows, Wq, Ws, C, N, K,
+                                             wlist, slist, s)
+              : launch_fp8_kind<false, false>(rows, A, offsets, E_loc, max_rows, Wq, Ws, C, N, K,
+                                              wlist, slist, s);
 }
 
 namespace {

@@ -373,12 +373,14 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
   // block) in K block kb
   constexpr int kScaleBlock = 128;
   const int RB = (SWIGLU ? 2 * N : N) / kScaleBlock, KB = K / kScaleBlock;
-  auto frag_scale = [&](const Tile& ct, int q, int kb) -> float {
+  // (se: the tile's expert's scales from slist, looked up once per tile; null
+  // for the packed scales)
+  auto frag_scale = [&](const float* se, const Tile& ct, int q, int kb) -> float {
     int wrow = SWIGLU ? (q / (NQ / 2)) * N + ct.n0 + wn * (HALF / WN) + (q % (NQ / 2)) * 32
                       : ct.n0 + wn * (BNW / WN) + q * 32;
     if (!SWIGLU) wrow = min(wrow, N - 1);  // columns past N are computed and dropped
-    const float* se = slist != nullptr ? slist[ct.e] : Ws + static_cast<size_t>(ct.e) * RB * KB;
-    return se[(wrow / kScaleBlock) * KB + kb];
+    if (se != nullptr) return se[(wrow / kScaleBlock) * KB + kb];
+    return Ws[(static_cast<size_t>(ct.e) * RB + wrow / kScaleBlock) * KB + kb];
   };
   // FP8W: codes of slot `slot` to dequantised bf16 operands, code x sq[q]
   // (the power-of-two scale of tile q's current K block); lanes 0..31 take
@@ -439,11 +441,11 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
   // kb + 1's scales.  sc holds the scales of blocks kb and kb + 1 of each
   // tile; those of block kb + 2 are loaded here, a whole block before they
   // are used.
-  auto next_block_scales = [&](const Tile& ct, int kb, float (&sc)[2][NQ]) {
+  auto next_block_scales = [&](const float* se, const Tile& ct, int kb, float (&sc)[2][NQ]) {
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       sc[0][q] = sc[1][q];
-      sc[1][q] = kb + 2 < KB ? frag_scale(ct, q, kb + 2) : 1.f;
+      sc[1][q] = kb + 2 < KB ? frag_scale(se, ct, q, kb + 2) : 1.f;
     }
   };
   // (na: the wave's first NA 32-row blocks; the others hold no row of the
@@ -570,11 +572,13 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
         for (int q = 0; q < NQ; ++q) acc[i][q] = f32x16_t{};
       // FP8W: the block scales of K blocks 0 and 1 of this tile's MFMA tiles
       float sc[2][NQ];
+      const float* se = nullptr;
       if constexpr (FP8W) {
+        if (slist != nullptr) se = slist[ct.e];
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
-          sc[0][q] = frag_scale(ct, q, 0);
-          sc[1][q] = KB > 1 ? frag_scale(ct, q, 1) : 1.f;
+          sc[0][q] = frag_scale(se, ct, q, 0);
+          sc[1][q] = KB > 1 ? frag_scale(se, ct, q, 1) : 1.f;
         }
       }
       // The K loop of one tile.  NA = the wave's 32-row blocks that hold rows
@@ -638,7 +642,7 @@ __device__ __forceinline__ void gemm_pipe_body(const uint16_t* __restrict__ A,
           if constexpr (ACT && FP8W) {
             const int kt = s % KT;
             if ((kt + 1) % (kScaleBlock / BK) == 0)
-              next_block_scales(ct, kt / (kScaleBlock / BK), sc);
+              next_block_scales(se, ct, kt / (kScaleBlock / BK), sc);
           }
         };
         const int s0 = j * KT;
