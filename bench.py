@@ -91,6 +91,11 @@ def parse(argv=None):
                    help="also time a training step: the forward with the SwiGLU pre-activations "
                         "kept, then the whole backward pass (gradients of x, the gate logits "
                         "or router, and the expert weights); reported under 'training'")
+    p.add_argument("--arrivals", type=int, default=0, metavar="S",
+                   help="(a workload with a local expert range) also time the local expert FFN "
+                        "on the rows that S source batches (seeds 0..S-1, each routed and "
+                        "dispatched here) would send this rank: what one rank of an S-rank "
+                        "expert-parallel layer computes; reported under 'arrivals'")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-tokens", type=int, default=64)
     p.add_argument("--copy-calibration", action="store_true",
@@ -905,6 +910,81 @@ def fused_orders_out(r):
                            "library's automatic choice"}
 
 
+def arrivals_bench(args, name, weights, dev):
+    """The local expert FFN at the load one rank of an S-rank expert-parallel
+    layer receives: S seeded source batches of the workload (its x and logits
+    from seeds 0..S-1; the rank's local experts' weights from seed 0) are each
+    routed and dispatched here with the workload's capacity and local range,
+    and their kept rows are joined expert by expert, source by source (what
+    the receive side of the exchange would hold).  The join runs once,
+    untimed; K steps of the two FFN halves on the joined rows are timed with
+    HIP events."""
+    import torch
+    import routing_dispatch_expert_moe_amd as M
+    from workloads import make
+
+    S = args.arrivals
+    wl0 = make(name)
+    if wl0.E_loc == wl0.E:
+        raise SystemExit("--arrivals needs a workload with a local expert range")
+    w13, w2p, _, _, _ = weights.get(wl0)
+    C = M.moe_capacity(wl0.T, wl0.k, wl0.E, wl0.capacity_factor)
+    parts = []
+    for src in range(S):
+        ws_ = make(name, seed=src)
+        layer = M.MoELayer(w13, w2p, E=ws_.E, k=ws_.k, gate=ws_.gate, T=ws_.T, capacity=C,
+                           e_begin=ws_.e_begin, e_end=ws_.e_end)
+        layer.route(torch.from_numpy(ws_.logits).to(dev))
+        layer.dispatch(bf16_dev(ws_.x, dev))
+        torch.cuda.synchronize()
+        if M.moe_check_error(layer.ws) != 0:
+            raise RuntimeError("device error in an arrivals source batch")
+        off = layer.plan.offsets.cpu().tolist()
+        parts.append((layer.plan.x_perm, off))
+        del layer
+    E_loc = wl0.E_loc
+    segs, offsets = [], [0]
+    for i in range(E_loc):
+        for xp, off in parts:
+            if off[i + 1] > off[i]:
+                segs.append(xp[off[i]:off[i + 1]])
+        offsets.append(offsets[-1] + sum(off[i + 1] - off[i] for _, off in parts))
+    n = offsets[-1]
+    x_perm = torch.cat(segs) if segs else torch.zeros((1, wl0.d), dtype=torch.bfloat16, device=dev)
+    del parts, segs
+    off_t = torch.tensor(offsets, dtype=torch.int32, device=dev)
+    rows = max(n, 1)
+    h = torch.empty((rows, wl0.f), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((rows, wl0.d), dtype=torch.bfloat16, device=dev)
+    for _ in range(args.warmup):
+        M.moe_ffn_up(x_perm, off_t, E_loc, n, w13, h)
+        M.moe_ffn_down(h, off_t, E_loc, n, w2p, y)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for e3 in ev:
+        e3[0].record()
+        M.moe_ffn_up(x_perm, off_t, E_loc, n, w13, h)
+        e3[1].record()
+        M.moe_ffn_down(h, off_t, E_loc, n, w2p, y)
+        e3[2].record()
+    torch.cuda.synchronize()
+    up = sum(e3[0].elapsed_time(e3[1]) for e3 in ev) / len(ev)
+    down = sum(e3[1].elapsed_time(e3[2]) for e3 in ev) / len(ev)
+    per = [offsets[i + 1] - offsets[i] for i in range(E_loc)]
+    touched = sum(1 for r in per if r > 0)
+    m = work_model(wl0, n, touched, 0)
+    out = {"sources": S, "rows": n, "rows_per_expert_min_max": [min(per), max(per)],
+           "capacity_per_source": C, "ms_ffn": round(up + down, 4),
+           "rows_per_s": round(n / ((up + down) * 1e-3), 1)}
+    for key, ms in (("ffn_up", up), ("ffn_down", down)):
+        fl, by = m[key]
+        out[key] = {"ms": round(ms, 5), "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
+                    "gbs": round(by / (ms * 1e-3) / 1e9, 1), "roofline": roofline_of(fl, by, ms)}
+    out["note"] = ("x and logits of seeds 0..S-1 routed and dispatched on this GPU, kept local "
+                   "rows joined per expert (untimed); HIP events around each FFN half")
+    return out
+
+
 def main(argv=None):
     args = parse(argv)
     if args.traffic_from:
@@ -1025,6 +1105,9 @@ def main(argv=None):
             run_fp8(name)
     line["others"] = others_out or None
     line["fp8_weights"] = fp8_out or None
+    if args.arrivals > 0:
+        log(f"arrivals: {args.arrivals} source batches of {args.workload}")
+        line["arrivals"] = arrivals_bench(args, args.workload, weights, dev)
     print(json.dumps(line), flush=True)
 
 
