@@ -910,6 +910,24 @@ def fused_orders_out(r):
                            "library's automatic choice"}
 
 
+def join_arrivals(parts, E_loc):
+    """The rows one rank receives from several sources, as its FFN takes them:
+    parts[s] = (x_perm of source s, its local offsets list); the result holds
+    expert 0's rows of source 0, then of source 1, ..., then expert 1's, and
+    the joined offsets (E_loc + 1 ints)."""
+    import torch
+    segs, offsets = [], [0]
+    for i in range(E_loc):
+        for xp, off in parts:
+            if off[i + 1] > off[i]:
+                segs.append(xp[off[i]:off[i + 1]])
+        offsets.append(offsets[-1] + sum(off[i + 1] - off[i] for _, off in parts))
+    xp0 = parts[0][0]
+    x_perm = torch.cat(segs) if segs else torch.zeros((1, xp0.shape[1]), dtype=xp0.dtype,
+                                                      device=xp0.device)
+    return x_perm, offsets
+
+
 def arrivals_bench(args, name, weights, dev):
     """The local expert FFN at the load one rank of an S-rank expert-parallel
     layer receives: S seeded source batches of the workload (its x and logits
@@ -943,15 +961,9 @@ def arrivals_bench(args, name, weights, dev):
         parts.append((layer.plan.x_perm, off))
         del layer
     E_loc = wl0.E_loc
-    segs, offsets = [], [0]
-    for i in range(E_loc):
-        for xp, off in parts:
-            if off[i + 1] > off[i]:
-                segs.append(xp[off[i]:off[i + 1]])
-        offsets.append(offsets[-1] + sum(off[i + 1] - off[i] for _, off in parts))
+    x_perm, offsets = join_arrivals(parts, E_loc)
     n = offsets[-1]
-    x_perm = torch.cat(segs) if segs else torch.zeros((1, wl0.d), dtype=torch.bfloat16, device=dev)
-    del parts, segs
+    del parts
     off_t = torch.tensor(offsets, dtype=torch.int32, device=dev)
     rows = max(n, 1)
     h = torch.empty((rows, wl0.f), dtype=torch.bfloat16, device=dev)

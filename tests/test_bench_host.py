@@ -157,3 +157,23 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     line = json.loads(r.stdout.strip().splitlines()[-1])
     assert "one GPU" in line["error"]
+
+
+def test_arrivals_join_is_expert_major_then_source_order():
+    """The rows a rank receives from several sources are joined expert by
+    expert, each expert's rows in source order, with matching offsets; a
+    source with no row for an expert adds nothing."""
+    import torch
+    d = 3
+    # source 0: experts 0, 1, 2 hold 2, 0, 1 rows; source 1: 1, 2, 0 rows
+    x0 = torch.tensor([[0., 0, 0], [0, 0, 1], [0, 2, 0]])
+    x1 = torch.tensor([[1., 0, 0], [1, 1, 0], [1, 1, 1]])
+    xp, off = bench.join_arrivals([(x0, [0, 2, 2, 3]), (x1, [0, 1, 3, 3])], 3)
+    assert off == [0, 3, 5, 6]
+    want = torch.stack([x0[0], x0[1], x1[0],      # expert 0: source 0, then source 1
+                        x1[1], x1[2],             # expert 1: source 1 only
+                        x0[2]])                   # expert 2: source 0 only
+    assert torch.equal(xp, want) and xp.shape == (6, d)
+    # no rows at all: one zero row keeps the buffer non-empty, offsets all zero
+    xe, oe = bench.join_arrivals([(x0[:0], [0, 0]), (x1[:0], [0, 0])], 1)
+    assert oe == [0, 0] and xe.shape == (1, d)
